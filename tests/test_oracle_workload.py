@@ -1,0 +1,101 @@
+"""Statistical and whole-step pins of the oracle on the seeded workloads.
+
+Planted recovery: on the tiny 4K workload (8 hot blocks per KV head whose keys
+are shifted by two standard deviations along the true query, lookahead query =
+true query + N(0, 0.3^2) noise) the oracle's top-32 selection must recover the
+planted blocks; a dropped term, a wrong sign or a transposed operand anywhere in
+score or select destroys that.  Recovery is a property of the workload, so the
+threshold (per-block recall >= 0.99 over 1,000 rows) sits below the value the
+recipe gives (about 0.997)."""
+import numpy as np
+import pytest
+import torch
+
+from lookahead_sparse_kv_amd import workload as wlm
+
+
+def test_planted_blocks_recovered_tiny(orc):
+    wl = wlm.WORKLOADS["tiny_4k"]
+    hits = total = 0
+    for i in range(500):                     # 500 seeds x 2 KV heads = 1,000 rows
+        d = wlm.make_layer(wl, seed=10_000 + i, pools=False)
+        s = orc.score(d["q_look32"], d["K32"], d["ctx_len"], wl.block_size, wl.table_width)
+        sel = orc.select(s, d["ctx_len"], wl.block_size, wl.k_blocks)
+        for g in range(wl.num_kv_heads):
+            hot = set(d["hot"][0, g].tolist())
+            hits += len(hot & set(sel[0, g].tolist()))
+            total += len(hot)
+    recall = hits / total
+    assert recall >= 0.99, recall
+
+
+def test_planted_blocks_point_along_the_true_query(orc):
+    # with the TRUE query the planted blocks are the top of the ranking even more often
+    wl = wlm.WORKLOADS["tiny_4k"]
+    hits = total = 0
+    for i in range(100):
+        d = wlm.make_layer(wl, seed=20_000 + i, pools=False)
+        s = orc.score(d["q32"].unsqueeze(1), d["K32"], d["ctx_len"], wl.block_size, wl.table_width)
+        sel = orc.select(s, d["ctx_len"], wl.block_size, wl.k_blocks)
+        for g in range(wl.num_kv_heads):
+            hot = set(d["hot"][0, g].tolist())
+            hits += len(hot & set(sel[0, g].tolist()))
+            total += len(hot)
+    assert hits / total >= 0.99
+
+
+def test_budget_equal_to_context_gives_dense_attention(orc):
+    # budget = whole context: every block is selected, the working set is
+    # everything, and the step's attention equals dense attention (torch, fp64)
+    wl = wlm.small_workload(batch=1, q_heads=4, kv_heads=2, head_dim=32, ctx=(256,), budget=256,
+                            n_hot=2, ratio=1.0, seed=3)
+    d = wlm.make_layer(wl, pools=False)
+    sb, lu = wlm.empty_state(wl)
+    r = orc.decode_step(d["q_look"], d["q"], d["K"], d["V"], d["ctx_len"], 16, wl.table_width,
+                        wl.k_blocks, wl.k_blocks, 0, sb, lu)
+    assert np.all(np.sort(r["slot_block"], axis=-1) == np.arange(16))
+    q = d["q"].double()
+    for g in range(2):
+        for h in range(2):
+            qh = q[0, 2 * g + h].view(1, 1, 1, -1)
+            k = d["K"][0, g].double().view(1, 1, 256, -1)
+            v = d["V"][0, g].double().view(1, 1, 256, -1)
+            want = torch.nn.functional.scaled_dot_product_attention(qh, k, v).view(-1).numpy()
+            np.testing.assert_allclose(r["out"][0, 2 * g + h], want, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_step_is_the_composition_of_the_stages(orc):
+    wl = wlm.small_workload(seed=5)
+    d = wlm.make_layer(wl, pools=False)
+    sb, lu = wlm.empty_state(wl)
+    cap = wl.cap()
+    r = orc.decode_step(d["q_look"], d["q"], d["K"], d["V"], d["ctx_len"], 16, wl.table_width,
+                        wl.k_blocks, cap, 3, sb, lu)
+    s = orc.score(d["q_look"], d["K"], d["ctx_len"], 16, wl.table_width)
+    sel = orc.select(s, d["ctx_len"], 16, wl.k_blocks)
+    fb, fs, cnt, sb2, lu2 = orc.plan(sel, s, sb, lu, cap, 3)
+    out = orc.attn(d["q"], d["K"], d["V"], d["ctx_len"], 16, sb2)
+    np.testing.assert_array_equal(r["scores"], s)
+    np.testing.assert_array_equal(r["sel"], sel)
+    np.testing.assert_array_equal(r["fetch_block"], fb)
+    np.testing.assert_array_equal(r["fetch_slot"], fs)
+    np.testing.assert_array_equal(r["fetch_count"], cnt)
+    np.testing.assert_array_equal(r["slot_block"], sb2)
+    np.testing.assert_array_equal(r["out"], out)
+    assert np.all(cnt <= cap)
+
+
+def test_generator_is_seeded_and_poisons_the_tail():
+    wl = wlm.small_workload(ctx=(100, 60), seed=9)
+    a = wlm.make_layer(wl)
+    b = wlm.make_layer(wl)
+    for key in ("q", "q_look", "K", "V", "block_table", "k_pool", "v_pool"):
+        assert torch.equal(a[key], b[key])
+    assert torch.all(a["K"][1, :, 60:] == wlm.POISON)
+    # the pools hold the logical values at the permuted pages
+    bt = a["block_table"]
+    for b_ in range(2):
+        for n in range(wl.table_width):
+            p = int(bt[b_, n])
+            assert torch.equal(a["k_pool"][p, 1], a["K"][b_, 1, 16 * n:16 * n + 16])
+            assert torch.equal(a["v_pool"][p, 0], a["V"][b_, 0, 16 * n:16 * n + 16].T)
