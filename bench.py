@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the OasisKV decode hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload qwen3_8b_32k] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path of one layer over one batch: block
+scoring with the lookahead query, top-K selection, the resident-diff / fetch
+cap / LRU plan, and sparse decode attention over the working set the plan
+leaves.  Inputs (seeded synthetic Gaussian KV with planted hot blocks) are
+resident in HBM before the timed region.  The resident set starts from the
+previous step's selection (an independent lookahead draw of the same true
+query, planned into empty slots), and every step draws a fresh lookahead
+query, so the fetch cap binds the way it does in steady-state decode.
+
+Prints ONE JSON line: seq-decode-steps/s (sequences x steps / s), per-stage
+times, the scoring kernel's HBM roofline fraction, and the CPU oracle timed
+on a bounded sample of the same workload.
+
+    python bench.py --copy-calibration   # plain 1 GiB device copies, for PMC scaling
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+N_LOOK_DRAWS = 4               # distinct lookahead draws cycled through the steps
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_blocks_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "lookahead_sparse_kv_amd", "csrc", "score_blocks.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="qwen3_8b_32k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-seqs", type=int, default=2,
+                   help="sequences (all KV heads) of the workload the oracle runs")
+    p.add_argument("--copy-calibration", action="store_true")
+    return p.parse_args()
+
+
+def score_bytes(wl):
+    keys = sum(c for c in wl.ctx) * wl.num_kv_heads * wl.head_dim * 2
+    q = wl.batch * wl.n_look * wl.num_q_heads * wl.head_dim * 2
+    table = wl.batch * wl.table_width * 4
+    out = wl.batch * wl.num_kv_heads * wl.table_width * 4
+    return keys + q + table + out + wl.batch * 4
+
+
+def attn_bytes(wl):
+    rows = wl.batch * wl.num_kv_heads
+    kv = rows * wl.k_blocks * 16 * wl.head_dim * 2 * 2
+    q = wl.batch * wl.num_q_heads * wl.head_dim * 2
+    out = q
+    lists = rows * wl.k_blocks * 4 * 2          # block list + the page-table entries it names
+    return kv + q + out + lists
+
+
+def select_bytes(wl):
+    return wl.batch * wl.num_kv_heads * (wl.table_width * 4 + wl.k_blocks * 4)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for name in ("score_blocks.hip", "oasis_device.h", "oasis_launch.h"):
+        with open(os.path.join(ROOT, "lookahead_sparse_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(wl_name):
+    """HBM bytes per scoring launch from the committed PMC summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash() or t.get("workload") != wl_name:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
+
+
+def cpu_baseline(wl, d, n_seqs, cap):
+    """Time the oracle's whole decode step on the first n_seqs sequences (every
+    KV head), starting from the same seeded resident state as the GPU."""
+    from lookahead_sparse_kv_amd import workload as wlm
+    from oracle import oasis_oracle as orc
+    import numpy as np
+    import torch
+    n = min(n_seqs, wl.batch)
+    K = d["K"][:n].double().numpy()
+    V = d["V"][:n].double().numpy()
+    q_look = d["q_look"][:n]
+    q = d["q"][:n]
+    ctx = d["ctx_len"][:n]
+    sb, lu = wlm.empty_state(wl)
+    sb, lu = sb[:n].numpy(), lu[:n].numpy()
+    prev = wlm.draw_lookahead(wl, d["q32"], wl.seed + 1).to(torch.bfloat16)[:n]
+    seed_run = orc.decode_step(prev, q, K, V, ctx, 16, wl.table_width, wl.k_blocks, wl.k_blocks,
+                               -1, sb, lu)
+    t0 = time.perf_counter()
+    orc.decode_step(q_look, q, K, V, ctx, 16, wl.table_width, wl.k_blocks, cap, 0,
+                    seed_run["slot_block"], seed_run["last_use"])
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "seq-decode-steps/s", "cores": orc.max_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {wl.batch} sequences x {wl.num_kv_heads} KV heads, one full "
+                      f"score+select+plan+attention step in fp64 ({dt:.2f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path shards per (sequence, KV head) row; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    from lookahead_sparse_kv_amd import ops
+    from lookahead_sparse_kv_amd import workload as wlm
+    from lookahead_sparse_kv_amd.pipeline import DecodeLayer
+
+    ops.lib()          # fail loudly before any work if the HIP library is missing
+    wl = wlm.WORKLOADS[args.workload]
+    cap = wl.cap()
+    t_gen = time.perf_counter()
+    d = wlm.make_layer(wl)
+    gen_s = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    g = {k: d[k].to(dev) for k in ("k_pool", "v_pool", "block_table", "ctx_len")}
+    q = d["q"].unsqueeze(1).to(dev)
+    looks = [d["q_look"].to(dev)] + [
+        wlm.draw_lookahead(wl, d["q32"], wl.seed + 100 + i).to(torch.bfloat16).to(dev)
+        for i in range(N_LOOK_DRAWS - 1)]
+    prev = wlm.draw_lookahead(wl, d["q32"], wl.seed + 1).to(torch.bfloat16).to(dev)
+
+    layer = DecodeLayer(k_pool=g["k_pool"], v_pool=g["v_pool"], block_table=g["block_table"],
+                        ctx_len=g["ctx_len"], num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks,
+                        cap=wl.k_blocks, n_look=wl.n_look)
+    layer.score(prev)                      # previous step: fill the working set
+    layer.select()
+    layer.plan(-1)
+    layer.cap = cap
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        layer.step(looks[i % N_LOOK_DRAWS], q, i)
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        layer.step(looks[i % N_LOOK_DRAWS], q, args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # per-stage timing, events on the stream the kernels run on (torch's current stream)
+    stages = ("score", "select", "plan", "attn")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    base = args.warmup + args.steps
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record()
+        layer.score(looks[i % N_LOOK_DRAWS])
+        e[1].record()
+        layer.select()
+        e[2].record()
+        layer.plan(base + i)
+        e[3].record()
+        layer.attend(q)
+        e[4].record()
+    torch.cuda.synchronize()
+    per = {s: sorted(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps))
+           for j, s in enumerate(stages)}
+    mean_ms = {s: sum(v) / len(v) for s, v in per.items()}
+    med_us = {s: round(v[len(v) // 2] * 1e3, 2) for s, v in per.items()}
+    fetched = int(layer.fetch_count.sum().item())
+
+    sb = score_bytes(wl)
+    achieved = sb / (mean_ms["score"] * 1e-3) / 1e9
+    ab = attn_bytes(wl)
+    attn_gbs = ab / (mean_ms["attn"] * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, d, args.cpu_sample_seqs, cap)
+
+    value = wl.batch / (ms_per_step * 1e-3)
+    line = {
+        "metric": "seq-decode-steps/s, score+select+sparse attn, Qwen3-8B shape 32K; % HBM peak",
+        "value": round(value, 1),
+        "unit": "seq-decode-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "num_q_heads": wl.num_q_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "context": wl.ctx_max, "block_size": 16, "budget_tokens": wl.budget,
+                   "k_blocks": wl.k_blocks, "fetch_ratio": wl.ratios[0], "cap": cap,
+                   "n_look": wl.n_look, "step": "score+select+plan+attn, one layer",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "score_blocks",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": sb},
+        "stages_us_median": med_us,
+        "stages_us_mean": {s: round(v * 1e3, 2) for s, v in mean_ms.items()},
+        "attn_roofline": {"achieved": round(attn_gbs, 1), "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                          "algorithmic_bytes": ab},
+        "score_select_attn_us": round((mean_ms["score"] + mean_ms["select"] + mean_ms["attn"]) * 1e3, 2),
+        "fetched_blocks_last_step": fetched,
+        "wall_ms_timed_region": round(wall_ms, 2),
+        "input_generation_s": round(gen_s, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * oasis.h -- C ABI of the OasisKV decode hot path for MI355X (gfx950).
+ *
+ * The method ("OasisKV: Scaling In-Decode KV Cache Beyond HBM with Lookahead
+ * Sparse Prefetching", arXiv 2608.08097): a lookahead (draft) query predicts,
+ * one decode step ahead, which KV blocks the next step will attend to; only
+ * those blocks are kept in a bounded HBM working set under a token budget,
+ * and the missing ones are fetched under a per-step cap.  One decode step of
+ * one layer is four calls, each a hand-written HIP kernel:
+ *
+ *   oasis_score_blocks       lookahead-query block scores over the paged keys
+ *   oasis_select_topk        top-K blocks per KV head under the budget
+ *   oasis_plan_fetch         resident diff + fetch cap + LRU eviction, which
+ *                            updates the per-head working-set table
+ *   oasis_sparse_decode_attn split-K decode attention over the working set
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers are DEVICE pointers unless a comment says otherwise.  Every
+ *    buffer is caller-owned; no call allocates device memory.
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *    only enqueue work and never synchronise.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    failing call enqueues nothing and returns a non-zero status, with detail
+ *    text from oasis_last_error() (thread-local).  Device-side faults surface
+ *    at the caller's next synchronisation.
+ *  - Device-resident indices (block tables, context lengths, block lists) are
+ *    bounds-checked inside the kernels: a page id outside [0, num_pages) or a
+ *    negative list entry makes that block count as absent (score -inf, not
+ *    attended) instead of being dereferenced; a context longer than
+ *    table_width * block_size is clamped to it.
+ *  - Calls are reentrant; the library keeps no state besides the error text.
+ *
+ * Layouts (row-major, innermost last):
+ *  - lookahead queries  q_look  [B][n_look][Hq][D]    bf16
+ *  - true queries       q       [B][n_q][Hq][D]       bf16
+ *  - key pool           k_pool  [num_pages][Hkv][bs][D]  bf16 (token-major tile)
+ *  - value pool         v_pool  [num_pages][Hkv][D][bs]  bf16 (dim-major tile)
+ *  - block table        [B][table_width]  int32, logical block -> page
+ *  - context lengths    ctx_len [B]       int32, tokens
+ *  - scores             [B][Hkv][table_width]  fp32
+ *  - selection          sel     [B][Hkv][K]     int32, ascending, -1 padded
+ *  - working-set table  slot_block, last_use [B][Hkv][K] int32
+ *  - fetch list         fetch_block, fetch_slot [B][Hkv][cap] int32, -1 padded;
+ *                       fetch_count [B][Hkv] int32
+ *  - output             out     [B][n_q][Hq][D]       bf16
+ * Query head h belongs to KV head h / G, G = Hq / Hkv (grouped-query attention).
+ */
+#ifndef OASIS_H
+#define OASIS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum oasis_status {
+    OASIS_OK = 0,
+    OASIS_ERR_INVALID = 1,      /* null pointer, negative size, inconsistent shape   */
+    OASIS_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement     */
+    OASIS_ERR_NOMEM = 3,        /* workspace too small / host pool allocation failed */
+    OASIS_ERR_HIP = 4           /* the HIP runtime reported an error                 */
+};
+
+typedef struct oasis_shape {
+    int32_t batch;          /* B, sequences (0 allowed: the call does nothing)          */
+    int32_t num_q_heads;    /* Hq                                                        */
+    int32_t num_kv_heads;   /* Hkv; Hq must be a multiple of Hkv                         */
+    int32_t head_dim;       /* D: 64 or 128                                              */
+    int32_t block_size;     /* tokens per KV block: 16                                   */
+    int32_t table_width;    /* W, entries per block-table row (blocks per sequence max)  */
+    int32_t num_pages;      /* pages in k_pool / v_pool                                  */
+} oasis_shape;
+
+/*
+ * Lookahead block scoring.  Figure 7 caption of the pages (metalmedia.ai
+ * summary of OasisKV): the draft query scans the keys to predict the next
+ * step's top-K blocks.  The pages leave the score open; this library fixes it:
+ *
+ *   scores[b][g][n] = max over drafts j < n_look, query heads h of KV head g,
+ *                     and tokens t of block n with 16n + t < ctx_len[b] of
+ *                     scale * (q_look[b][j][h] . k_t)
+ *   scores[b][g][n] = -inf for n >= ceil(ctx_len[b] / bs) (up to table_width).
+ *
+ * bf16 inputs, fp32 accumulation.  Requires D in {64, 128}, bs = 16,
+ * 1 <= n_look and n_look * G <= 16.  scale is normally 1/sqrt(D) and must be > 0.
+ */
+int oasis_score_blocks(const oasis_shape *s, const uint16_t *q_look, int32_t n_look,
+                       const uint16_t *k_pool, const int32_t *block_table,
+                       const int32_t *ctx_len, float scale, float *scores, void *stream);
+
+/*
+ * Per-KV-head top-K.  Figure 7 caption ("top-K blocks"); abstract (a
+ * 2,048-token KV budget, i.e. K = budget / bs blocks per KV head).
+ * Among blocks n < ceil(ctx_len[b] / bs), the k_blocks largest scores win;
+ * equal scores go to the lower block index (-0.0 equals +0.0).  sel is written
+ * in ascending block order, padded with -1 when fewer blocks exist.
+ * Requires 1 <= k_blocks <= 1024 and table_width <= 15360.  Scores must not be NaN.
+ */
+int oasis_select_topk(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                      int32_t k_blocks, int32_t *sel, void *stream);
+
+/*
+ * Resident diff + fetch cap + capped LRU eviction, one row per (sequence,
+ * KV head).  Pages: five-step flow step 3 (compare the prediction with the
+ * blocks already on the GPU and pull only the missing ones, with a per-step
+ * bound); Figure 9 caption (per-KV-head table from working-set block to CPU
+ * logical block); Table 2 caption (the cap is a fetch ratio; LRU eviction).
+ *
+ * slot_block[b][g][j] is the logical block held by working-set slot j (-1 =
+ * empty) and last_use[b][g][j] the step it was last used; both are read and
+ * updated in place.  For each row:
+ *   1. resident selected blocks (hits) get last_use = step;
+ *   2. the selected blocks that are not resident (misses) are ranked by score
+ *      (descending, ties to the lower index); the first min(#misses, cap) are
+ *      fetched and listed in ascending block order;
+ *   3. their destinations are the empty slots in ascending order, then -- if
+ *      more are needed -- exactly that many resident blocks that are not
+ *      selected, least recently used first (ties to the lower block index);
+ *      a selected block is never evicted;
+ *   4. slot_block / last_use of each destination become (block, step).
+ * fetch_block[i] / fetch_slot[i] (i < fetch_count) list the fetched blocks and
+ * their slots, -1 padded up to cap.  `scores` is the scoring output [B][Hkv][W].
+ * Requires 1 <= k_blocks <= 1024, 0 <= cap <= k_blocks; when cap == 0 the
+ * fetch_block / fetch_slot pointers may be NULL.  Precondition: no row of
+ * slot_block holds a block twice.
+ */
+int oasis_plan_fetch(const oasis_shape *s, const int32_t *sel, const float *scores,
+                     int32_t k_blocks, int32_t cap, int32_t step, int32_t *slot_block,
+                     int32_t *last_use, int32_t *fetch_block, int32_t *fetch_slot,
+                     int32_t *fetch_count, void *stream);
+
+/*
+ * Bytes of device workspace oasis_sparse_decode_attn needs for this shape
+ * (split-K partial results).  Returns 0 for an invalid shape.
+ */
+size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk);
+
+/*
+ * Sparse paged decode attention over the working set.  Figure 7 caption:
+ * attention runs over the sparse KV working set.  For each sequence b, query
+ * row i < n_q and head h of KV head g:
+ *
+ *   out[b][i][h] = sum_t softmax_t(scale * q[b][i][h] . k_t) v_t
+ *
+ * over every valid token t of the row's listed blocks.  Entry e of row
+ * (b, g) names the block
+ *   blk[b][g][e]  -- an index into page_table row b (-1 = empty entry);
+ *                    blk == NULL means entry e is index e itself;
+ *   blk_logical[b][g][e] -- its logical block number (token 16*l + t is valid
+ *                    while < ctx_len[b]; -1 = empty entry);
+ * full-pool mode passes the block table as page_table and the selected (or
+ * resident) logical blocks as both blk and blk_logical; working-set mode
+ * passes the slot -> page table and blk = NULL, blk_logical = slot_block.
+ * A row with no valid token outputs zeros.  bf16 in and out, fp32 softmax and
+ * accumulation.  Requires D in {64, 128}, bs = 16, 1 <= n_q, n_q * G <= 16,
+ * n_blk >= 1, scale > 0, and workspace_bytes >= oasis_attn_workspace_bytes().
+ */
+int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_q,
+                             const uint16_t *k_pool, const uint16_t *v_pool,
+                             const int32_t *page_table, const int32_t *blk, int32_t n_blk,
+                             const int32_t *blk_logical, const int32_t *ctx_len, float scale,
+                             uint16_t *out, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *oasis_status_string(int status);
+
+/* Detail text of the calling thread's last failed call ("" if none). */
+const char *oasis_last_error(void);
+
+/* Library version string (static storage). */
+const char *oasis_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OASIS_H */

@@ -1,0 +1,185 @@
+// oasis_abi.hip -- the extern "C" entry points declared in include/oasis.h:
+// host-side argument validation, then one launch per call on the caller's
+// stream.  No allocation, no synchronisation, no printing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "oasis.h"
+#include "oasis_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return OASIS_OK;
+}
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_hip(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(OASIS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Shape checks shared by every call.
+int check_shape(const oasis_shape *s, const char *fn) {
+    if (!s) return fail(OASIS_ERR_INVALID, "%s: shape is NULL", fn);
+    if (s->batch < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->head_dim <= 0 ||
+        s->block_size <= 0 || s->table_width < 0 || s->num_pages < 0)
+        return fail(OASIS_ERR_INVALID, "%s: negative or zero dimension in shape", fn);
+    if (s->num_q_heads % s->num_kv_heads)
+        return fail(OASIS_ERR_INVALID, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", fn,
+                    s->num_q_heads, s->num_kv_heads);
+    if (s->block_size != oasis::kBlockTokens)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is implemented)", fn,
+                    s->block_size);
+    if (s->head_dim != 64 && s->head_dim != 128)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 are implemented)", fn,
+                    s->head_dim);
+    if ((long long)s->batch * s->num_kv_heads > 65535)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: batch * num_kv_heads above 65535", fn);
+    return OASIS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *oasis_status_string(int status) {
+    switch (status) {
+        case OASIS_OK: return "OASIS_OK";
+        case OASIS_ERR_INVALID: return "OASIS_ERR_INVALID";
+        case OASIS_ERR_UNSUPPORTED: return "OASIS_ERR_UNSUPPORTED";
+        case OASIS_ERR_NOMEM: return "OASIS_ERR_NOMEM";
+        case OASIS_ERR_HIP: return "OASIS_ERR_HIP";
+        default: return "OASIS_ERR_UNKNOWN";
+    }
+}
+
+const char *oasis_last_error(void) { return g_err; }
+
+const char *oasis_version(void) { return "oasis-mi355x 0.1 (gfx950)"; }
+
+int oasis_score_blocks(const oasis_shape *s, const uint16_t *q_look, int32_t n_look,
+                       const uint16_t *k_pool, const int32_t *block_table, const int32_t *ctx_len,
+                       float scale, float *scores, void *stream) {
+    const char *fn = "oasis_score_blocks";
+    if (int e = check_shape(s, fn)) return e;
+    if (n_look < 1) return fail(OASIS_ERR_INVALID, "%s: n_look %d < 1", fn, n_look);
+    const int G = s->num_q_heads / s->num_kv_heads;
+    if ((long long)n_look * G > oasis::kMaxRowsQ)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: n_look * group = %lld above %d", fn,
+                    (long long)n_look * G, oasis::kMaxRowsQ);
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(OASIS_ERR_INVALID, "%s: scale must be finite and > 0", fn);
+    if (s->batch == 0 || s->table_width == 0) return ok();
+    if (!q_look || !k_pool || !block_table || !ctx_len || !scores)
+        return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    oasis::ScoreArgs a{q_look, k_pool, block_table, ctx_len, scores, scale,
+                       s->batch, s->num_q_heads, s->num_kv_heads, G, s->table_width,
+                       s->num_pages, n_look, n_look * G};
+    return check_hip(oasis::launch_score_blocks(a, s->head_dim, as_stream(stream)), fn);
+}
+
+int oasis_select_topk(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                      int32_t k_blocks, int32_t *sel, void *stream) {
+    const char *fn = "oasis_select_topk";
+    if (int e = check_shape(s, fn)) return e;
+    if (k_blocks < 1) return fail(OASIS_ERR_INVALID, "%s: k_blocks %d < 1", fn, k_blocks);
+    if (k_blocks > oasis::kMaxKBlocks)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: k_blocks %d above %d", fn, k_blocks,
+                    oasis::kMaxKBlocks);
+    if (s->table_width > oasis::kMaxSelectWidth)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: table_width %d above %d", fn, s->table_width,
+                    oasis::kMaxSelectWidth);
+    if (s->batch == 0) return ok();
+    if (!scores || !ctx_len || !sel) return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    oasis::SelectArgs a{scores, ctx_len, sel, s->batch * s->num_kv_heads, s->num_kv_heads,
+                        s->table_width, k_blocks};
+    return check_hip(oasis::launch_select_topk(a, as_stream(stream)), fn);
+}
+
+int oasis_plan_fetch(const oasis_shape *s, const int32_t *sel, const float *scores,
+                     int32_t k_blocks, int32_t cap, int32_t step, int32_t *slot_block,
+                     int32_t *last_use, int32_t *fetch_block, int32_t *fetch_slot,
+                     int32_t *fetch_count, void *stream) {
+    const char *fn = "oasis_plan_fetch";
+    if (int e = check_shape(s, fn)) return e;
+    if (k_blocks < 1) return fail(OASIS_ERR_INVALID, "%s: k_blocks %d < 1", fn, k_blocks);
+    if (k_blocks > oasis::kMaxKBlocks)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: k_blocks %d above %d", fn, k_blocks,
+                    oasis::kMaxKBlocks);
+    if (cap < 0 || cap > k_blocks)
+        return fail(OASIS_ERR_INVALID, "%s: cap %d outside [0, k_blocks = %d]", fn, cap, k_blocks);
+    if (s->batch == 0) return ok();
+    if (!sel || !scores || !slot_block || !last_use || !fetch_count)
+        return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    if (cap > 0 && (!fetch_block || !fetch_slot))
+        return fail(OASIS_ERR_INVALID, "%s: NULL fetch list with cap %d", fn, cap);
+    oasis::PlanArgs a{sel, scores, slot_block, last_use, fetch_block, fetch_slot, fetch_count,
+                      s->batch * s->num_kv_heads, s->table_width, k_blocks, cap, step};
+    return check_hip(oasis::launch_plan_fetch(a, as_stream(stream)), fn);
+}
+
+size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk) {
+    if (!s || s->batch < 0 || s->num_kv_heads <= 0 || s->num_q_heads <= 0 || s->head_dim <= 0 ||
+        n_q < 1 || n_blk < 1 || s->num_q_heads % s->num_kv_heads)
+        return 0;
+    const int rows = s->batch * s->num_kv_heads;
+    const int nrq = n_q * (s->num_q_heads / s->num_kv_heads);
+    int splits = 1, per = 1;
+    oasis::attn_split_plan(rows, n_blk, &splits, &per);
+    return (size_t)rows * splits * nrq * (s->head_dim + 2) * sizeof(float);
+}
+
+int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_q,
+                             const uint16_t *k_pool, const uint16_t *v_pool,
+                             const int32_t *page_table, const int32_t *blk, int32_t n_blk,
+                             const int32_t *blk_logical, const int32_t *ctx_len, float scale,
+                             uint16_t *out, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    const char *fn = "oasis_sparse_decode_attn";
+    if (int e = check_shape(s, fn)) return e;
+    if (n_q < 1) return fail(OASIS_ERR_INVALID, "%s: n_q %d < 1", fn, n_q);
+    if (n_blk < 1) return fail(OASIS_ERR_INVALID, "%s: n_blk %d < 1", fn, n_blk);
+    const int G = s->num_q_heads / s->num_kv_heads;
+    if ((long long)n_q * G > oasis::kMaxRowsQ)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: n_q * group = %lld above %d", fn,
+                    (long long)n_q * G, oasis::kMaxRowsQ);
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(OASIS_ERR_INVALID, "%s: scale must be finite and > 0", fn);
+    if (s->batch == 0) return ok();
+    if (!q || !k_pool || !v_pool || !page_table || !ctx_len || !out)
+        return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    if (!blk && !blk_logical)
+        return fail(OASIS_ERR_INVALID, "%s: blk and blk_logical are both NULL", fn);
+    const size_t need = oasis_attn_workspace_bytes(s, n_q, n_blk);
+    if (!workspace || workspace_bytes < need)
+        return fail(OASIS_ERR_NOMEM, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16)
+        return fail(OASIS_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+    const int rows = s->batch * s->num_kv_heads;
+    int splits = 1, per = 1;
+    oasis::attn_split_plan(rows, n_blk, &splits, &per);
+    const int nrq = n_q * G;
+    float *part_o = static_cast<float *>(workspace);
+    float *part_ml = part_o + (size_t)rows * splits * nrq * s->head_dim;
+    oasis::AttnArgs a{q, k_pool, v_pool, page_table, blk, blk_logical, ctx_len, out,
+                      part_o, part_ml, scale * 1.4426950408889634f,
+                      s->batch, s->num_q_heads, s->num_kv_heads, G, s->table_width,
+                      s->num_pages, n_q, nrq, n_blk, splits, per};
+    return check_hip(oasis::launch_sparse_decode_attn(a, s->head_dim, as_stream(stream)), fn);
+}
+
+}  // extern "C"

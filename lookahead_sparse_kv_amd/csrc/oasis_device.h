@@ -1,0 +1,77 @@
+// oasis_device.h -- device-side helpers shared by the gfx950 kernels:
+// vector types for MFMA operands, bf16 bit conversions, wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oasis {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 with round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return float_to_bf16_bits(lo) | (float_to_bf16_bits(hi) << 16);
+}
+
+// 16-byte and 8-byte global loads (non-temporal hint off: keys are streamed
+// once per step, but the working set may be re-read by attention next step).
+__device__ __forceinline__ u32x4 load_u32x4(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ u32x2 load_u32x2(const void *p) {
+    return *reinterpret_cast<const u32x2 *>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ s16x4 as_s16x4(u32x2 v) { return __builtin_bit_cast(s16x4, v); }
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
+// Lane l supplies A row (l % 16), B column (l % 16), and the same eight
+// reduction indices in both (lane group l / 16); it receives D rows
+// 4 * (l / 16) + i, i < 4, of column l % 16.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16, fp32) += A(16x16, bf16) * B(16x16, bf16), four reduction indices
+// per lane, same lane roles as above.
+__device__ __forceinline__ f32x4 mfma16x16x16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+__device__ __forceinline__ int shfl_xor_i(int v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
+    return v;
+}
+
+__device__ __forceinline__ int readlane_i(int v, int lane) {
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+}  // namespace oasis

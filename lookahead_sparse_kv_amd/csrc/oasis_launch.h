@@ -1,0 +1,68 @@
+// oasis_launch.h -- argument blocks and launchers of the gfx950 kernels.
+// Host-side validation lives in oasis_abi.hip; the launchers assume valid
+// arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oasis {
+
+struct ScoreArgs {
+    const uint16_t *q_look;
+    const uint16_t *k_pool;
+    const int32_t *block_table;
+    const int32_t *ctx_len;
+    float *scores;
+    float scale;
+    int batch, hq, hkv, group, width, num_pages, n_look, n_rows_q;
+};
+
+struct SelectArgs {
+    const float *scores;
+    const int32_t *ctx_len;
+    int32_t *sel;
+    int rows, hkv, width, k;
+};
+
+struct PlanArgs {
+    const int32_t *sel;
+    const float *scores;
+    int32_t *slot_block;
+    int32_t *last_use;
+    int32_t *fetch_block;
+    int32_t *fetch_slot;
+    int32_t *fetch_count;
+    int rows, width, k, cap, step;
+};
+
+struct AttnArgs {
+    const uint16_t *q;
+    const uint16_t *k_pool;
+    const uint16_t *v_pool;
+    const int32_t *page_table;
+    const int32_t *blk;
+    const int32_t *blk_logical;
+    const int32_t *ctx_len;
+    uint16_t *out;
+    float *part_o;    // [rows][splits][n_rows_q][D]
+    float *part_ml;   // [rows][splits][n_rows_q][2]
+    float scale_log2;
+    int batch, hq, hkv, group, width, num_pages, n_q, n_rows_q, n_blk, splits, per_split;
+};
+
+hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t stream);
+hipError_t launch_select_topk(const SelectArgs &a, hipStream_t stream);
+hipError_t launch_plan_fetch(const PlanArgs &a, hipStream_t stream);
+hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_t stream);
+
+// Split-K plan of the attention kernel: how many splits per row and entries per split.
+void attn_split_plan(int rows, int n_blk, int *splits, int *per_split);
+
+constexpr int kBlockTokens = 16;   // tokens per KV block
+constexpr int kMaxRowsQ = 16;     // lookahead / query rows per KV head in one MFMA tile
+constexpr int kMaxKBlocks = 1024; // K limit of select / plan
+constexpr int kMaxSelectWidth = 15360;   // keys of a row staged in LDS (60 KiB)
+
+}  // namespace oasis

@@ -1,0 +1,139 @@
+// score_blocks.hip -- lookahead-query block scoring over the paged key pool.
+//
+// OasisKV (metalmedia.ai summary), Figure 7 caption: the draft query scans
+// the keys to predict the next step's top-K blocks.  Score of block n of KV
+// head g: the max over its valid tokens t and over every lookahead row
+// (draft j, query head h of the group) of scale * q_jh . k_t.
+//
+// Design (gfx950): the scan is a skinny dense contraction (16 tokens x D
+// against at most 16 lookahead rows per block), so each 16-token block is one
+// 16x16 MFMA output tile: A = the block's key tile (token = M, head dim = K),
+// B = the group's lookahead rows (head dim = K, row = N), D / 32 MFMAs of
+// 16x16x32 bf16 with fp32 accumulation.  The kernel is bound by streaming the
+// keys from HBM: every key byte is read exactly once, 16 bytes per lane per
+// load, the whole 4 KiB (D = 128) tile of a block by one wave.  A wave owns a
+// chunk of 16 consecutive blocks of one (sequence, KV head) row and keeps four
+// blocks of loads in flight; the max over the tile is reduced across lanes
+// four blocks at a time so that each lane exchange serves several blocks.
+#include "oasis_device.h"
+#include "oasis_launch.h"
+
+namespace oasis {
+
+constexpr int kScoreChunk = 16;      // blocks per wave
+constexpr int kScoreUnroll = 4;      // blocks loaded together
+constexpr int kScoreWaves = 4;       // waves per workgroup
+
+template <int D>
+__global__ __launch_bounds__(kScoreWaves * kWave) void score_blocks_kernel(ScoreArgs a) {
+    constexpr int KK = D / 32;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int row = blockIdx.y;                       // b * hkv + g
+    const int b = row / a.hkv;
+    const int g = row - b * a.hkv;
+    const int n0 = (blockIdx.x * kScoreWaves + wave) * kScoreChunk;
+    if (n0 >= a.width) return;
+    const int r16 = lane & 15;
+    const int j4 = lane >> 4;
+
+    int ctx = a.ctx_len[b];
+    ctx = ctx < 0 ? 0 : (ctx > a.width * kBlockTokens ? a.width * kBlockTokens : ctx);
+    const int nb = (ctx + kBlockTokens - 1) / kBlockTokens;
+
+    // B operand: lookahead row r16 (draft r16 / G, head g*G + r16 % G), head-dim
+    // slice 32*kk + 8*j4 .. +8.  Rows past n_rows_q are zero and masked below.
+    bf16x8 qv[KK];
+    const bool col_ok = r16 < a.n_rows_q;
+    if (col_ok) {
+        const int jd = r16 / a.group;
+        const int hr = r16 - jd * a.group;
+        const uint16_t *qp = a.q_look +
+            (((size_t)b * a.n_look + jd) * a.hq + (size_t)g * a.group + hr) * D + 8 * j4;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qv[kk] = as_bf16x8(load_u32x4(qp + 32 * kk));
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qv[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
+
+    // Page of block n0 + lane (lanes < chunk); -1 when past the context or out of range.
+    int pg = -1;
+    if (lane < kScoreChunk) {
+        const int n = n0 + lane;
+        if (n < nb) {
+            const int p = a.block_table[(size_t)b * a.width + n];
+            if (p >= 0 && p < a.num_pages) pg = p;
+        }
+    }
+
+    const size_t page_stride = (size_t)a.hkv * kBlockTokens * D;
+    // A operand: token r16 of the tile, head-dim slice 32*kk + 8*j4 .. +8.
+    const uint16_t *kbase = a.k_pool + (size_t)g * kBlockTokens * D + (size_t)r16 * D + 8 * j4;
+    float *out = a.scores + (size_t)row * a.width;
+    const float NEG_INF = -__builtin_inff();
+
+#pragma unroll 1
+    for (int c = 0; c < kScoreChunk; c += kScoreUnroll) {
+        int pgs[kScoreUnroll];
+        u32x4 kv[kScoreUnroll][KK];
+#pragma unroll
+        for (int u = 0; u < kScoreUnroll; ++u) {
+            pgs[u] = readlane_i(pg, c + u);
+            if (pgs[u] >= 0) {
+                const uint16_t *kp = kbase + (size_t)pgs[u] * page_stride;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) kv[u][kk] = load_u32x4(kp + 32 * kk);
+            }
+        }
+        float v[kScoreUnroll];
+#pragma unroll
+        for (int u = 0; u < kScoreUnroll; ++u) {
+            v[u] = NEG_INF;
+            if (pgs[u] >= 0) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) acc = mfma16x16x32(as_bf16x8(kv[u][kk]), qv[kk], acc);
+                // rows 4*j4 + i of the tile are tokens; keep the valid ones
+                const int valid = ctx - (n0 + c + u) * kBlockTokens - 4 * j4;
+                float m = NEG_INF;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m = (i < valid) ? fmaxf(m, acc[i]) : m;
+                v[u] = col_ok ? m : NEG_INF;
+            }
+        }
+        // Reduce four blocks across the wave: halve the block set per exchange
+        // (lane bit 5, then bit 4), then finish within 16-lane groups.
+        float a0 = (lane & 32) ? v[2] : v[0];
+        float a1 = (lane & 32) ? v[3] : v[1];
+        const float s0 = (lane & 32) ? v[0] : v[2];
+        const float s1 = (lane & 32) ? v[1] : v[3];
+        a0 = fmaxf(a0, shfl_xor_f(s0, 32));
+        a1 = fmaxf(a1, shfl_xor_f(s1, 32));
+        float x = (lane & 16) ? a1 : a0;
+        const float y = (lane & 16) ? a0 : a1;
+        x = fmaxf(x, shfl_xor_f(y, 16));
+        x = fmaxf(x, shfl_xor_f(x, 8));
+        x = fmaxf(x, shfl_xor_f(x, 4));
+        x = fmaxf(x, shfl_xor_f(x, 2));
+        x = fmaxf(x, shfl_xor_f(x, 1));
+        const int u_mine = ((lane >> 5) << 1) | ((lane >> 4) & 1);
+        const int n = n0 + c + u_mine;
+        if (r16 == 0 && n < a.width) out[n] = x * a.scale;
+    }
+}
+
+hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t stream) {
+    const int rows = a.batch * a.hkv;
+    if (rows == 0 || a.width == 0) return hipSuccess;
+    const int per_wg = kScoreWaves * kScoreChunk;
+    dim3 grid((a.width + per_wg - 1) / per_wg, rows);
+    dim3 block(kScoreWaves * kWave);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(score_blocks_kernel<128>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(score_blocks_kernel<64>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace oasis

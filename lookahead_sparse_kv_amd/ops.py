@@ -1,0 +1,148 @@
+"""Thin ctypes binding of liboasis.so (include/oasis.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, builds the oasis_shape, passes raw pointers and torch's
+current HIP stream, and raises on a non-zero status.  All arithmetic runs in
+the library's HIP kernels; there is no CPU path.  The library must have been
+built (python -m lookahead_sparse_kv_amd.build); loading fails loudly if not.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboasis.so")
+BLOCK_SIZE = 16
+
+OASIS_OK, OASIS_ERR_INVALID, OASIS_ERR_UNSUPPORTED, OASIS_ERR_NOMEM, OASIS_ERR_HIP = range(5)
+
+# Every symbol include/oasis.h declares.
+EXPORTS = ("oasis_score_blocks", "oasis_select_topk", "oasis_plan_fetch",
+           "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_status_string",
+           "oasis_last_error", "oasis_version")
+
+
+class OasisShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("table_width", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
+
+
+class OasisError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liboasis.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m lookahead_sparse_kv_amd.build` (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        S = ctypes.POINTER(OasisShape)
+        L.oasis_score_blocks.argtypes = [S, p, i32, p, p, p, f32, p, p]
+        L.oasis_select_topk.argtypes = [S, p, p, i32, p, p]
+        L.oasis_plan_fetch.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p]
+        L.oasis_attn_workspace_bytes.argtypes = [S, i32, i32]
+        L.oasis_attn_workspace_bytes.restype = sz
+        L.oasis_sparse_decode_attn.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz, p]
+        for fn in ("oasis_score_blocks", "oasis_select_topk", "oasis_plan_fetch",
+                   "oasis_sparse_decode_attn"):
+            getattr(L, fn).restype = ctypes.c_int
+        L.oasis_status_string.argtypes = [ctypes.c_int]
+        L.oasis_status_string.restype = ctypes.c_char_p
+        L.oasis_last_error.argtypes = []
+        L.oasis_last_error.restype = ctypes.c_char_p
+        L.oasis_version.argtypes = []
+        L.oasis_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().oasis_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().oasis_last_error().decode()
+
+
+def _check(status: int):
+    if status != OASIS_OK:
+        raise OasisError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_shape(batch, num_q_heads, num_kv_heads, head_dim, table_width, num_pages,
+               block_size=BLOCK_SIZE) -> OasisShape:
+    return OasisShape(batch, num_q_heads, num_kv_heads, head_dim, block_size, table_width,
+                      num_pages)
+
+
+def _pool_shape(q: torch.Tensor, k_pool: torch.Tensor, table: torch.Tensor) -> OasisShape:
+    return make_shape(table.shape[0], q.shape[-2], k_pool.shape[1], k_pool.shape[-1],
+                      table.shape[1], k_pool.shape[0])
+
+
+def score_blocks(q_look, k_pool, block_table, ctx_len, scores, scale=None, stream=None):
+    """q_look [B][n_look][Hq][D] bf16, k_pool [P][Hkv][16][D] bf16, block_table [B][W] i32,
+    ctx_len [B] i32 -> scores [B][Hkv][W] f32 (written in place)."""
+    s = _pool_shape(q_look, k_pool, block_table)
+    scale = float(s.head_dim) ** -0.5 if scale is None else scale
+    _check(lib().oasis_score_blocks(ctypes.byref(s), _ptr(q_look), q_look.shape[1], _ptr(k_pool),
+                                    _ptr(block_table), _ptr(ctx_len), scale, _ptr(scores),
+                                    _stream(stream)))
+    return scores
+
+
+def select_topk(shape: OasisShape, scores, ctx_len, k_blocks, sel, stream=None):
+    """scores [B][Hkv][W] f32 -> sel [B][Hkv][K] i32 (ascending, -1 padded)."""
+    _check(lib().oasis_select_topk(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks,
+                                   _ptr(sel), _stream(stream)))
+    return sel
+
+
+def plan_fetch(shape: OasisShape, sel, scores, k_blocks, cap, step, slot_block, last_use,
+               fetch_block, fetch_slot, fetch_count, stream=None):
+    """Updates slot_block / last_use [B][Hkv][K] in place; writes the capped fetch list."""
+    _check(lib().oasis_plan_fetch(ctypes.byref(shape), _ptr(sel), _ptr(scores), k_blocks, cap,
+                                  step, _ptr(slot_block), _ptr(last_use), _ptr(fetch_block),
+                                  _ptr(fetch_slot), _ptr(fetch_count), _stream(stream)))
+
+
+def attn_workspace_bytes(shape: OasisShape, n_q: int, n_blk: int) -> int:
+    return int(lib().oasis_attn_workspace_bytes(ctypes.byref(shape), n_q, n_blk))
+
+
+def sparse_decode_attn(shape: OasisShape, q, k_pool, v_pool, page_table, blk, blk_logical,
+                       ctx_len, out, workspace, scale=None, stream=None):
+    """q [B][n_q][Hq][D] bf16 -> out [B][n_q][Hq][D] bf16 over the listed blocks.
+    blk / blk_logical [B][Hkv][n_blk] i32 (blk may be None: entry e is index e)."""
+    n_blk = (blk if blk is not None else blk_logical).shape[-1]
+    scale = float(shape.head_dim) ** -0.5 if scale is None else scale
+    _check(lib().oasis_sparse_decode_attn(
+        ctypes.byref(shape), _ptr(q), q.shape[1], _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+        _ptr(blk), n_blk, _ptr(blk_logical), _ptr(ctx_len), scale, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

@@ -1,0 +1,131 @@
+"""The C-ABI library loads, exports every symbol include/oasis.h declares, and
+rejects bad arguments on the host before anything reaches the GPU.  No call
+here passes validation with work to do, so nothing is launched: these run on
+a machine without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lookahead_sparse_kv_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oasis.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oasis_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared_functions()
+    for fn in ("oasis_score_blocks", "oasis_select_topk", "oasis_plan_fetch",
+               "oasis_sparse_decode_attn"):
+        assert fn in names
+    assert set(names) == set(ops.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ops.lib()
+    for fn in _declared_functions():
+        assert hasattr(L, fn), fn
+    assert ops.lib().oasis_version().decode().startswith("oasis")
+
+
+def test_status_strings():
+    assert ops.status_string(0) == "OASIS_OK"
+    assert ops.status_string(1) == "OASIS_ERR_INVALID"
+    assert ops.status_string(2) == "OASIS_ERR_UNSUPPORTED"
+    assert ops.status_string(3) == "OASIS_ERR_NOMEM"
+    assert ops.status_string(4) == "OASIS_ERR_HIP"
+    assert ops.status_string(77) == "OASIS_ERR_UNKNOWN"
+
+
+def _shape(**kw):
+    d = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, table_width=64, num_pages=128)
+    d.update(kw)
+    return ops.make_shape(**d)
+
+
+P = ctypes.c_void_p(16)   # a non-null dummy; never dereferenced (validation fails first)
+
+
+def _score(s, n_look=1, scale=0.1, q=P):
+    return ops.lib().oasis_score_blocks(ctypes.byref(s), q, n_look, P, P, P, scale, P, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), ops.OASIS_ERR_UNSUPPORTED),
+    (dict(block_size=32), ops.OASIS_ERR_UNSUPPORTED),
+    (dict(num_q_heads=7), ops.OASIS_ERR_INVALID),
+    (dict(batch=-1), ops.OASIS_ERR_INVALID),
+    (dict(num_kv_heads=0), ops.OASIS_ERR_INVALID),
+])
+def test_score_rejects_bad_shapes(kw, status):
+    assert _score(_shape(**kw)) == status
+    assert ops.last_error()
+
+
+def test_score_rejects_bad_arguments():
+    assert _score(_shape(), n_look=0) == ops.OASIS_ERR_INVALID
+    assert _score(_shape(), n_look=5) == ops.OASIS_ERR_UNSUPPORTED      # 5 * 4 rows > 16
+    assert _score(_shape(), scale=0.0) == ops.OASIS_ERR_INVALID
+    assert _score(_shape(), scale=float("nan")) == ops.OASIS_ERR_INVALID
+    assert _score(_shape(), q=None) == ops.OASIS_ERR_INVALID
+    assert "NULL" in ops.last_error()
+    assert ops.lib().oasis_score_blocks(None, P, 1, P, P, P, 0.1, P, None) == ops.OASIS_ERR_INVALID
+
+
+def test_empty_batch_is_a_no_op():
+    s = _shape(batch=0)
+    assert _score(s, q=None) == ops.OASIS_OK
+    L = ops.lib()
+    assert L.oasis_select_topk(ctypes.byref(s), None, None, 8, None, None) == ops.OASIS_OK
+    assert L.oasis_plan_fetch(ctypes.byref(s), None, None, 8, 2, 0, None, None, None, None, None,
+                              None) == ops.OASIS_OK
+    assert L.oasis_sparse_decode_attn(ctypes.byref(s), None, 1, None, None, None, None, 8, None,
+                                      None, 0.1, None, None, 0, None) == ops.OASIS_OK
+
+
+def test_select_and_plan_reject_bad_arguments():
+    L = ops.lib()
+    s = _shape()
+    assert L.oasis_select_topk(ctypes.byref(s), P, P, 0, P, None) == ops.OASIS_ERR_INVALID
+    assert L.oasis_select_topk(ctypes.byref(s), P, P, 2048, P, None) == ops.OASIS_ERR_UNSUPPORTED
+    wide = _shape(table_width=20000)
+    assert L.oasis_select_topk(ctypes.byref(wide), P, P, 8, P, None) == ops.OASIS_ERR_UNSUPPORTED
+    assert L.oasis_select_topk(ctypes.byref(s), None, P, 8, P, None) == ops.OASIS_ERR_INVALID
+    plan = lambda k, cap, fb=P: L.oasis_plan_fetch(ctypes.byref(s), P, P, k, cap, 0, P, P, fb, P,
+                                                   P, None)
+    assert plan(8, 9) == ops.OASIS_ERR_INVALID          # cap > K
+    assert plan(8, -1) == ops.OASIS_ERR_INVALID
+    assert plan(0, 0) == ops.OASIS_ERR_INVALID
+    assert plan(8, 2, fb=None) == ops.OASIS_ERR_INVALID
+
+
+def test_attn_workspace_and_argument_checks():
+    L = ops.lib()
+    s = _shape(batch=16, num_q_heads=32, num_kv_heads=8, table_width=2048, num_pages=32768)
+    ws = ops.attn_workspace_bytes(s, 1, 128)
+    # 128 rows x 16 splits x 4 query rows x (128 + 2) floats
+    assert ws == 128 * 16 * 4 * 130 * 4
+    assert ops.attn_workspace_bytes(s, 0, 128) == 0
+    assert ops.attn_workspace_bytes(s, 1, 0) == 0
+    att = lambda n_q=1, n_blk=128, wsb=ws, wsp=P, blk=P: L.oasis_sparse_decode_attn(
+        ctypes.byref(s), P, n_q, P, P, P, blk, n_blk, blk, P, 0.088, P, wsp, wsb, None)
+    assert att(wsb=ws - 4) == ops.OASIS_ERR_NOMEM
+    assert att(wsp=None) == ops.OASIS_ERR_NOMEM
+    assert att(n_q=5) == ops.OASIS_ERR_UNSUPPORTED      # 5 * 4 rows > 16
+    assert att(n_blk=0) == ops.OASIS_ERR_INVALID
+    assert att(blk=None) == ops.OASIS_ERR_INVALID       # blk and blk_logical both NULL
+    assert att(wsp=ctypes.c_void_p(24)) == ops.OASIS_ERR_INVALID  # misaligned workspace
+
+
+def test_library_is_required():
+    # the binding never falls back to a CPU path
+    src = open(os.path.join(ROOT, "lookahead_sparse_kv_amd", "ops.py")).read()
+    assert "oracle" not in src
+    assert "no CPU fallback" in src

@@ -1,0 +1,412 @@
+"""GPU parity of the four HIP kernels against the CPU oracle, called through
+the C ABI (liboasis.so via lookahead_sparse_kv_amd.ops).
+
+Stage tests feed both sides the same inputs (for select and plan the same
+fp32 scores, so the integer results must match bit for bit); the step tests
+chain the four stages and apply the near-tie exemption where the fp32 kernel
+scores and the fp64 oracle scores may legitimately order a boundary pair
+differently.  Sizes span several tiles with ragged tails, plus edge cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from lookahead_sparse_kv_amd import ops
+from lookahead_sparse_kv_amd import workload as wlm
+from lookahead_sparse_kv_amd.pipeline import DecodeLayer
+from oracle import oasis_oracle as orc
+from parity_utils import (ATTN_ATOL, check_plan_row, check_scores, check_selection_row,
+                          score_tolerance)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NEG = -(2 ** 31)
+
+
+def dev(t):
+    return t.to(DEV).contiguous()
+
+
+def group_rows(q_look, b, g, G):
+    """[n_look * G][D] lookahead rows of KV head g (draft-major)."""
+    n_look = q_look.shape[1]
+    return torch.cat([q_look[b, j, g * G:(g + 1) * G] for j in range(n_look)]).double().numpy()
+
+
+# ---------------------------------------------------------------- score
+SCORE_CASES = {
+    "tiny_4k_d64_g4": wlm.WORKLOADS["tiny_4k"],
+    "ragged_d64_g4": wlm.small_workload(ctx=(1000, 777), head_dim=64, seed=11),
+    "short_ctx_d128": wlm.small_workload(batch=4, ctx=(2000, 33, 16, 5), head_dim=128, n_hot=0,
+                                         seed=12),
+    "g8_two_drafts_d128": wlm.small_workload(batch=2, q_heads=16, kv_heads=2, head_dim=128,
+                                             ctx=(3000, 1601), n_look=2, seed=13),
+    "g1_d128": wlm.small_workload(batch=1, q_heads=4, kv_heads=4, head_dim=128, ctx=(777,),
+                                  seed=14),
+    "four_drafts_d128": wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128,
+                                           ctx=(4096, 2500), n_look=4, seed=15),
+}
+
+
+@pytest.mark.parametrize("name", list(SCORE_CASES))
+def test_score_blocks_matches_oracle(name):
+    wl = SCORE_CASES[name]
+    d = wlm.make_layer(wl)
+    scores = torch.full((wl.batch, wl.num_kv_heads, wl.table_width), 7.0, device=DEV)
+    ops.score_blocks(dev(d["q_look"]), dev(d["k_pool"]), dev(d["block_table"]), dev(d["ctx_len"]),
+                     scores)
+    torch.cuda.synchronize()
+    got = scores.cpu().double().numpy()
+    want = orc.score(d["q_look"], d["K"], d["ctx_len"], 16, wl.table_width)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            tol = score_tolerance(group_rows(d["q_look"], b, g, wl.group),
+                                  d["K"][b, g].double().numpy(), wl.ctx[b], 16, wl.table_width)
+            check_scores(got[b, g], want[b, g], tol, f"{name} b{b} g{g}")
+
+
+def test_score_blocks_skips_out_of_range_pages():
+    wl = wlm.small_workload(batch=1, ctx=(640,), seed=16)
+    d = wlm.make_layer(wl)
+    bt = d["block_table"].clone()
+    bt[0, 3] = -5
+    bt[0, 7] = wl.num_pages + 100          # both must count as absent, not be read
+    scores = torch.empty((1, 2, wl.table_width), device=DEV)
+    ops.score_blocks(dev(d["q_look"]), dev(d["k_pool"]), dev(bt), dev(d["ctx_len"]), scores)
+    got = scores.cpu().numpy()
+    assert np.all(np.isneginf(got[0, :, [3, 7]]))
+    assert np.all(np.isfinite(np.delete(got[0], [3, 7], axis=1)))
+
+
+# ---------------------------------------------------------------- select
+def _random_scores(rng, B, Hkv, W, mode):
+    s = rng.standard_normal((B, Hkv, W)).astype(np.float32)
+    if mode == "ties":
+        s = (np.round(s * 4) / 4).astype(np.float32)
+    elif mode == "zeros":
+        s = rng.choice(np.array([0.0, -0.0, 1.0, -1.0], dtype=np.float32), size=(B, Hkv, W))
+    elif mode == "inf":
+        s[rng.random(s.shape) < 0.3] = -np.inf
+    return s
+
+
+SELECT_CASES = [
+    # B, Hkv, ctx list, K, mode
+    (1, 2, [4096], 32, "normal"),
+    (2, 8, [32768, 20000], 128, "normal"),
+    (3, 4, [5000, 2048, 300], 128, "ties"),
+    (2, 2, [16 * 128, 16 * 127], 128, "normal"),      # nb == K and nb == K - 1
+    (2, 3, [8192 * 16, 8192 * 16], 128, "ties"),      # 131K context
+    (1, 2, [15360 * 16], 1000, "normal"),             # the widest table supported
+    (2, 2, [4000, 900], 1, "zeros"),
+    (2, 2, [3000, 6000], 64, "inf"),
+    (1, 1, [0], 8, "normal"),                         # empty context
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=lambda c: f"B{c[0]}H{c[1]}K{c[3]}{c[4]}")
+def test_select_topk_bit_exact(case):
+    B, Hkv, ctx, K, mode = case
+    rng = np.random.default_rng(hash(str(case)) % 2 ** 32)
+    W = max(1, (max(ctx) + 15) // 16)
+    s = _random_scores(rng, B, Hkv, W, mode)
+    ctx_len = np.array(ctx, dtype=np.int32)
+    shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
+    sel = torch.full((B, Hkv, K), -7, dtype=torch.int32, device=DEV)
+    ops.select_topk(shape, dev(torch.from_numpy(s)), dev(torch.from_numpy(ctx_len)), K, sel)
+    got = sel.cpu().numpy()
+    want = orc.select(s.astype(np.float64), ctx_len, 16, K)
+    np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------- plan
+def _random_state(rng, B, Hkv, K, nb, fill):
+    sb = np.full((B, Hkv, K), -1, np.int32)
+    lu = np.full((B, Hkv, K), NEG, np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            n = int(rng.integers(0, K + 1)) if fill is None else fill
+            blocks = rng.choice(nb, size=min(n, nb), replace=False)
+            slots = rng.choice(K, size=len(blocks), replace=False)
+            sb[b, g, slots] = blocks
+            lu[b, g, slots] = rng.integers(0, 4, size=len(blocks))
+    return sb, lu
+
+
+PLAN_CASES = [
+    # B, Hkv, nb, K, cap, mode, initial fill (None = random)
+    (2, 2, 256, 32, 32, "normal", 0),
+    (4, 8, 2048, 128, 2, "normal", 128),
+    (2, 4, 2048, 128, 6, "ties", None),
+    (3, 2, 300, 128, 25, "ties", None),
+    (2, 2, 100, 128, 128, "normal", None),      # fewer blocks than K
+    (2, 2, 64, 5, 0, "normal", 5),              # cap 0: nothing moves but the hits
+    (1, 3, 40, 1, 1, "zeros", None),
+]
+
+
+@pytest.mark.parametrize("case", PLAN_CASES, ids=lambda c: f"nb{c[2]}K{c[3]}cap{c[4]}{c[5]}")
+def test_plan_fetch_bit_exact_over_steps(case):
+    B, Hkv, nb, K, cap, mode, fill = case
+    rng = np.random.default_rng(hash(str(case)) % 2 ** 32)
+    W = nb
+    ctx_len = np.full(B, nb * 16, np.int32)
+    sb, lu = _random_state(rng, B, Hkv, K, nb, fill)
+    shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
+    g_sb, g_lu = dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))
+    fb = torch.empty((B, Hkv, max(cap, 1)), dtype=torch.int32, device=DEV)
+    fs = torch.empty_like(fb)
+    fc = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    for step in range(10, 22):
+        s = _random_scores(rng, B, Hkv, W, mode)
+        sel = orc.select(s.astype(np.float64), ctx_len, 16, K)
+        ofb, ofs, ocnt, sb, lu = orc.plan(sel, s.astype(np.float64), sb, lu, cap, step)
+        ops.plan_fetch(shape, dev(torch.from_numpy(sel)), dev(torch.from_numpy(s)), K, cap, step,
+                       g_sb, g_lu, fb if cap else None, fs if cap else None, fc)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(fc.cpu().numpy(), ocnt)
+        if cap:
+            np.testing.assert_array_equal(fb.cpu().numpy()[:, :, :cap], ofb)
+            np.testing.assert_array_equal(fs.cpu().numpy()[:, :, :cap], ofs)
+        np.testing.assert_array_equal(g_sb.cpu().numpy(), sb)
+        np.testing.assert_array_equal(g_lu.cpu().numpy(), lu)
+        assert np.all(ocnt <= cap)
+
+
+# ---------------------------------------------------------------- attention
+ATTN_CASES = {
+    # name: (workload kwargs, n_q, n_blk, fraction of -1 entries)
+    "d128_g4_k128": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 3000)), 1, 128, 0.0),
+    "d64_g4_ragged": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=64, ctx=(1000, 777)), 1, 32, 0.2),
+    "d128_g8_nq2": (dict(batch=2, q_heads=16, kv_heads=2, head_dim=128, ctx=(2000, 1601)), 2, 40, 0.1),
+    "d128_g1": (dict(batch=1, q_heads=4, kv_heads=4, head_dim=128, ctx=(999,)), 1, 7, 0.0),
+    "d128_g4_nq4": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 300)), 4, 19, 0.3),
+    "d128_one_block": (dict(batch=3, q_heads=8, kv_heads=2, head_dim=128, ctx=(16, 5, 4096)), 1, 1, 0.0),
+    "d128_all_empty_rows": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(600, 600)), 1, 9, 1.0),
+}
+
+
+def _random_lists(rng, wl, n_blk, frac_empty):
+    lists = np.full((wl.batch, wl.num_kv_heads, n_blk), -1, np.int32)
+    for b in range(wl.batch):
+        nb = (wl.ctx[b] + 15) // 16
+        for g in range(wl.num_kv_heads):
+            picks = rng.choice(nb, size=min(n_blk, nb), replace=False)
+            lists[b, g, :len(picks)] = picks
+            lists[b, g, rng.random(n_blk) < frac_empty] = -1
+            rng.shuffle(lists[b, g])
+    return lists
+
+
+@pytest.mark.parametrize("name", list(ATTN_CASES))
+def test_sparse_attention_matches_oracle(name):
+    kw, n_q, n_blk, frac = ATTN_CASES[name]
+    wl = wlm.small_workload(n_hot=0, seed=21, **kw)
+    d = wlm.make_layer(wl)
+    rng = np.random.default_rng(22)
+    q = torch.randn((wl.batch, n_q, wl.num_q_heads, wl.head_dim), generator=torch.Generator().manual_seed(5))
+    q = (q * 2.0).to(torch.bfloat16)
+    lists = _random_lists(rng, wl, n_blk, frac)
+    shape = ops.make_shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.table_width,
+                           wl.num_pages)
+    ws = torch.empty(ops.attn_workspace_bytes(shape, n_q, n_blk) // 4 + 4, device=DEV)
+    out = torch.empty((wl.batch, n_q, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device=DEV)
+    g_lists = dev(torch.from_numpy(lists))
+    ops.sparse_decode_attn(shape, dev(q), dev(d["k_pool"]), dev(d["v_pool"]), dev(d["block_table"]),
+                           g_lists, g_lists, dev(d["ctx_len"]), out, ws)
+    got = out.float().cpu().numpy()
+    for i in range(n_q):
+        want = orc.attn(q[:, i], d["K"], d["V"], d["ctx_len"], 16, lists)
+        err = np.abs(got[:, i] - want)
+        assert err.max() <= ATTN_ATOL, (name, i, err.max())
+    assert np.all(np.isfinite(got))
+
+
+def test_sparse_attention_working_set_mode():
+    # slots -> pages of a separate working-set pool; blk = NULL, blk_logical = slot table
+    wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(3000, 2000), n_hot=0,
+                            seed=23)
+    d = wlm.make_layer(wl)
+    K = 24
+    rng = np.random.default_rng(24)
+    slot_block = _random_lists(rng, wl, K, 0.25)
+    # working-set pool: page = b * K + slot, holding (for every head) that head's slot block
+    ws_k = torch.zeros((wl.batch * K, 2, 16, 128), dtype=torch.bfloat16)
+    ws_v = torch.zeros((wl.batch * K, 2, 128, 16), dtype=torch.bfloat16)
+    for b in range(wl.batch):
+        for g in range(2):
+            for j in range(K):
+                n = slot_block[b, g, j]
+                if n >= 0:
+                    p = int(d["block_table"][b, n])
+                    ws_k[b * K + j, g] = d["k_pool"][p, g]
+                    ws_v[b * K + j, g] = d["v_pool"][p, g]
+    page_table = torch.arange(wl.batch * K, dtype=torch.int32).view(wl.batch, K)
+    shape = ops.make_shape(wl.batch, 8, 2, 128, K, wl.batch * K)
+    q = torch.randn((wl.batch, 1, 8, 128), generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
+    ws = torch.empty(ops.attn_workspace_bytes(shape, 1, K) // 4 + 4, device=DEV)
+    out = torch.empty((wl.batch, 1, 8, 128), dtype=torch.bfloat16, device=DEV)
+    ops.sparse_decode_attn(shape, dev(q), dev(ws_k), dev(ws_v), dev(page_table), None,
+                           dev(torch.from_numpy(slot_block)), dev(d["ctx_len"]), out, ws)
+    want = orc.attn(q[:, 0], d["K"], d["V"], d["ctx_len"], 16, slot_block)
+    assert np.abs(out[:, 0].float().cpu().numpy() - want).max() <= ATTN_ATOL
+
+
+def test_sparse_attention_large_logits_stay_finite():
+    wl = wlm.small_workload(batch=1, q_heads=8, kv_heads=2, head_dim=128, ctx=(2048,), n_hot=0, seed=25)
+    d = wlm.make_layer(wl)
+    q = (torch.randn((1, 1, 8, 128), generator=torch.Generator().manual_seed(7)) * 12).to(torch.bfloat16)
+    lists = np.tile(np.arange(0, 128, 2, dtype=np.int32), (1, 2, 1))
+    shape = ops.make_shape(1, 8, 2, 128, wl.table_width, wl.num_pages)
+    ws = torch.empty(ops.attn_workspace_bytes(shape, 1, 64) // 4 + 4, device=DEV)
+    out = torch.empty((1, 1, 8, 128), dtype=torch.bfloat16, device=DEV)
+    g_lists = dev(torch.from_numpy(lists))
+    ops.sparse_decode_attn(shape, dev(q), dev(d["k_pool"]), dev(d["v_pool"]), dev(d["block_table"]),
+                           g_lists, g_lists, dev(d["ctx_len"]), out, ws)
+    want = orc.attn(q[:, 0], d["K"], d["V"], d["ctx_len"], 16, lists)
+    got = out[:, 0].float().cpu().numpy()
+    assert np.all(np.isfinite(got)) and np.abs(got - want).max() <= ATTN_ATOL
+
+
+# ---------------------------------------------------------------- whole step
+def _oracle_seed_state(wl, d, seed, rows=None):
+    """Resident set = the oracle's top-K under an independent lookahead draw,
+    filled into empty slots at step -1 (the workload's 'previous step')."""
+    q_prev = wlm.draw_lookahead(wl, d["q32"], seed).to(torch.bfloat16)
+    sb, lu = wlm.empty_state(wl)
+    sb, lu = sb.numpy(), lu.numpy()
+    rows = rows or [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    for b, g in rows:
+        s = orc.score_row(group_rows(q_prev, b, g, wl.group), d["K"][b, g], wl.ctx[b], 16,
+                          wl.table_width)
+        sel = orc.select_row(s, (wl.ctx[b] + 15) // 16, wl.k_blocks)
+        _, _, _, sb[b, g], lu[b, g] = orc.plan_row(sel, s, sb[b, g], lu[b, g], wl.k_blocks, -1)
+    return sb, lu
+
+
+def _check_step_rows(wl, d, layer, q_look, q, sb0, lu0, cap, step, rows, name):
+    """Compare one GPU step with the oracle on the given rows (with resync)."""
+    scores = layer.scores.cpu().double().numpy()
+    sel = layer.sel.cpu().numpy()
+    g_state = dict(fetch_block=layer.fetch_block.cpu().numpy()[..., :cap],
+                   fetch_slot=layer.fetch_slot.cpu().numpy()[..., :cap],
+                   fetch_count=layer.fetch_count.cpu().numpy(),
+                   slot_block=layer.slot_block.cpu().numpy(), last_use=layer.last_use.cpu().numpy())
+    out = layer.out.float().cpu().numpy()
+    n_exempt = 0
+    for b, g in rows:
+        where = f"{name} step {step} b{b} g{g}"
+        nb = (wl.ctx[b] + 15) // 16
+        qr = group_rows(q_look, b, g, wl.group)
+        o_s = orc.score_row(qr, d["K"][b, g], wl.ctx[b], 16, wl.table_width)
+        check_scores(scores[b, g], o_s, score_tolerance(qr, d["K"][b, g].double().numpy(), wl.ctx[b],
+                                                        16, wl.table_width), where)
+        o_sel = orc.select_row(o_s, nb, wl.k_blocks)
+        ex = check_selection_row(sel[b, g], o_sel, o_s, nb, wl.k_blocks, where)
+        use_sel = sel[b, g] if ex else o_sel          # resync on an exempt row
+        fb, fs, cnt, sb1, lu1 = orc.plan_row(use_sel, o_s, sb0[b, g], lu0[b, g], cap, step)
+        o_plan = dict(fetch_block=fb, fetch_slot=fs, fetch_count=cnt, slot_block=sb1, last_use=lu1)
+        g_plan = {k: v[b, g] for k, v in g_state.items()}
+        ex |= check_plan_row(g_plan, o_plan, use_sel, sb0[b, g], o_s, cap, step, where)
+        n_exempt += ex
+        # attention over the GPU's working set (equal to the oracle's unless exempt)
+        blocks = g_state["slot_block"][b, g]
+        o_out = orc.attn_row(q[b, 0, g * wl.group:(g + 1) * wl.group], d["K"][b, g], d["V"][b, g],
+                             wl.ctx[b], 16, blocks)
+        err = np.abs(out[b, 0, g * wl.group:(g + 1) * wl.group] - o_out).max()
+        assert err <= ATTN_ATOL, (where, err)
+    return n_exempt
+
+
+def _gpu_layer(wl, d, cap, sb, lu):
+    return DecodeLayer(k_pool=dev(d["k_pool"]), v_pool=dev(d["v_pool"]),
+                       block_table=dev(d["block_table"]), ctx_len=dev(d["ctx_len"]),
+                       num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks, cap=cap, n_look=wl.n_look,
+                       slot_block=torch.from_numpy(sb), last_use=torch.from_numpy(lu))
+
+
+def test_decode_step_tiny_4k_empty_start():
+    wl = wlm.WORKLOADS["tiny_4k"]
+    d = wlm.make_layer(wl)
+    sb0, lu0 = (x.numpy() for x in wlm.empty_state(wl))
+    cap = wl.cap()                                    # ratio 1.0 -> cap = K = 32
+    layer = _gpu_layer(wl, d, cap, sb0, lu0)
+    layer.step(dev(d["q_look"]), dev(d["q"].unsqueeze(1)), 0)
+    torch.cuda.synchronize()
+    rows = [(0, 0), (0, 1)]
+    _check_step_rows(wl, d, layer, d["q_look"], d["q"].unsqueeze(1), sb0, lu0, cap, 0, rows, "tiny")
+    # ratio 1.0 from an empty start: the working set is exactly the selection
+    sel = np.sort(layer.sel.cpu().numpy(), axis=-1)
+    assert np.array_equal(np.sort(layer.slot_block.cpu().numpy(), axis=-1), sel)
+    assert np.all(layer.fetch_count.cpu().numpy() == 32)
+
+
+@pytest.mark.parametrize("n_look", [1, 4])
+def test_decode_steps_mid_size_with_lru(n_look):
+    wl = wlm.small_workload(batch=3, q_heads=8, kv_heads=2, head_dim=128, ctx=(6000, 4096, 2333),
+                            budget=512, n_hot=12, ratio=0.1, n_look=n_look, seed=31)
+    d = wlm.make_layer(wl)
+    sb, lu = _oracle_seed_state(wl, d, seed=wl.seed + 1)
+    cap = wl.cap()
+    layer = _gpu_layer(wl, d, cap, sb, lu)
+    rows = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    exempt = 0
+    q = d["q"].unsqueeze(1)
+    for step in range(6):
+        q_look = wlm.draw_lookahead(wl, d["q32"], 100 + step).to(torch.bfloat16)
+        sb0, lu0 = layer.slot_block.cpu().numpy(), layer.last_use.cpu().numpy()
+        layer.step(dev(q_look), dev(q), step)
+        torch.cuda.synchronize()
+        exempt += _check_step_rows(wl, d, layer, q_look, q, sb0, lu0, cap, step, rows, "mid")
+        assert np.all(layer.fetch_count.cpu().numpy() <= cap)
+    assert exempt <= len(rows) * 6 // 4
+
+
+def test_step_is_deterministic():
+    wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(8000, 5000),
+                            budget=1024, n_hot=20, ratio=0.05, seed=41)
+    d = wlm.make_layer(wl)
+    outs = []
+    for _ in range(2):
+        sb, lu = (x.numpy() for x in wlm.empty_state(wl))
+        layer = _gpu_layer(wl, d, wl.cap(), sb, lu)
+        for step in range(3):
+            layer.step(dev(d["q_look"]), dev(d["q"].unsqueeze(1)), step)
+        torch.cuda.synchronize()
+        outs.append([layer.scores.cpu(), layer.sel.cpu(), layer.slot_block.cpu(),
+                     layer.last_use.cpu(), layer.out.cpu()])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_32k"])
+def test_full_size_sampled_rows(name):
+    """The metric workload at its full size, launched as the benchmark launches
+    it; the oracle checks a sample of rows one by one."""
+    wl = wlm.WORKLOADS[name]
+    d = wlm.make_layer(wl)
+    rows = [(0, 0), (5, 3), (11, 6), (15, 7)]
+    sb, lu = _oracle_seed_state(wl, d, seed=wl.seed + 1, rows=rows)
+    # rows outside the sample start from any valid state: a random one
+    rng = np.random.default_rng(3)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            if (b, g) not in rows:
+                sb[b, g] = rng.choice(wl.table_width, size=wl.k_blocks, replace=False)
+                lu[b, g] = -1
+    cap = wl.cap()
+    layer = _gpu_layer(wl, d, cap, sb, lu)
+    q = d["q"].unsqueeze(1)
+    layer.step(dev(d["q_look"]), dev(q), 0)
+    torch.cuda.synchronize()
+    _check_step_rows(wl, d, layer, d["q_look"], q, sb, lu, cap, 0, rows, name)
+    # properties that hold at any size, on every row
+    fc = layer.fetch_count.cpu().numpy()
+    assert np.all(fc <= cap)
+    sbg = layer.slot_block.cpu().numpy()
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            r = sbg[b, g][sbg[b, g] >= 0]
+            assert len(np.unique(r)) == len(r)
+    assert np.all(np.isfinite(layer.out.float().cpu().numpy()))
