@@ -134,6 +134,18 @@ int oasis_plan_fetch(const oasis_shape *s, const int32_t *sel, const float *scor
                      int32_t *fetch_count, void *stream);
 
 /*
+ * oasis_select_topk followed by oasis_plan_fetch on the same row, as one
+ * launch when k_blocks <= 256 and table_width <= 2048 (one wave per row; the
+ * selection never leaves the chip between the two), else as the two calls.
+ * Results are identical to the two calls; `sel` receives the selection.
+ * Same arguments, requirements and errors as the two calls together.
+ */
+int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                      int32_t k_blocks, int32_t cap, int32_t step, int32_t *sel,
+                      int32_t *slot_block, int32_t *last_use, int32_t *fetch_block,
+                      int32_t *fetch_slot, int32_t *fetch_count, void *stream);
+
+/*
  * Bytes of device workspace oasis_sparse_decode_attn needs for this shape
  * (split-K partial results).  Returns 0 for an invalid shape.
  */

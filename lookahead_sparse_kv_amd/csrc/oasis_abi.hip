@@ -105,8 +105,13 @@ int oasis_select_topk(const oasis_shape *s, const float *scores, const int32_t *
                     oasis::kMaxSelectWidth);
     if (s->batch == 0) return ok();
     if (!scores || !ctx_len || !sel) return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
-    oasis::SelectArgs a{scores, ctx_len, sel, s->batch * s->num_kv_heads, s->num_kv_heads,
-                        s->table_width, k_blocks};
+    const int rows = s->batch * s->num_kv_heads;
+    if (oasis::wave_select_plan_fits(s->table_width, k_blocks, true)) {
+        oasis::SelectPlanArgs a{scores, ctx_len, sel, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                rows, s->num_kv_heads, s->table_width, k_blocks, 0, 0};
+        return check_hip(oasis::launch_wave_select_plan(a, 1, as_stream(stream)), fn);
+    }
+    oasis::SelectArgs a{scores, ctx_len, sel, rows, s->num_kv_heads, s->table_width, k_blocks};
     return check_hip(oasis::launch_select_topk(a, as_stream(stream)), fn);
 }
 
@@ -127,9 +132,50 @@ int oasis_plan_fetch(const oasis_shape *s, const int32_t *sel, const float *scor
         return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
     if (cap > 0 && (!fetch_block || !fetch_slot))
         return fail(OASIS_ERR_INVALID, "%s: NULL fetch list with cap %d", fn, cap);
+    const int rows = s->batch * s->num_kv_heads;
+    if (oasis::wave_select_plan_fits(s->table_width, k_blocks, false)) {
+        oasis::SelectPlanArgs a{scores, nullptr, const_cast<int32_t *>(sel), slot_block, last_use,
+                                fetch_block, fetch_slot, fetch_count, rows, s->num_kv_heads,
+                                s->table_width, k_blocks, cap, step};
+        return check_hip(oasis::launch_wave_select_plan(a, 2, as_stream(stream)), fn);
+    }
     oasis::PlanArgs a{sel, scores, slot_block, last_use, fetch_block, fetch_slot, fetch_count,
-                      s->batch * s->num_kv_heads, s->table_width, k_blocks, cap, step};
+                      rows, s->table_width, k_blocks, cap, step};
     return check_hip(oasis::launch_plan_fetch(a, as_stream(stream)), fn);
+}
+
+int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                      int32_t k_blocks, int32_t cap, int32_t step, int32_t *sel,
+                      int32_t *slot_block, int32_t *last_use, int32_t *fetch_block,
+                      int32_t *fetch_slot, int32_t *fetch_count, void *stream) {
+    const char *fn = "oasis_select_plan";
+    if (int e = check_shape(s, fn)) return e;
+    if (k_blocks < 1) return fail(OASIS_ERR_INVALID, "%s: k_blocks %d < 1", fn, k_blocks);
+    if (k_blocks > oasis::kMaxKBlocks)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: k_blocks %d above %d", fn, k_blocks,
+                    oasis::kMaxKBlocks);
+    if (s->table_width > oasis::kMaxSelectWidth)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: table_width %d above %d", fn, s->table_width,
+                    oasis::kMaxSelectWidth);
+    if (cap < 0 || cap > k_blocks)
+        return fail(OASIS_ERR_INVALID, "%s: cap %d outside [0, k_blocks = %d]", fn, cap, k_blocks);
+    if (s->batch == 0) return ok();
+    if (!scores || !ctx_len || !sel || !slot_block || !last_use || !fetch_count)
+        return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    if (cap > 0 && (!fetch_block || !fetch_slot))
+        return fail(OASIS_ERR_INVALID, "%s: NULL fetch list with cap %d", fn, cap);
+    const int rows = s->batch * s->num_kv_heads;
+    if (oasis::wave_select_plan_fits(s->table_width, k_blocks, true)) {
+        oasis::SelectPlanArgs a{scores, ctx_len, sel, slot_block, last_use, fetch_block, fetch_slot,
+                                fetch_count, rows, s->num_kv_heads, s->table_width, k_blocks, cap,
+                                step};
+        return check_hip(oasis::launch_wave_select_plan(a, 3, as_stream(stream)), fn);
+    }
+    oasis::SelectArgs sa{scores, ctx_len, sel, rows, s->num_kv_heads, s->table_width, k_blocks};
+    if (int e = check_hip(oasis::launch_select_topk(sa, as_stream(stream)), fn)) return e;
+    oasis::PlanArgs pa{sel, scores, slot_block, last_use, fetch_block, fetch_slot, fetch_count,
+                       rows, s->table_width, k_blocks, cap, step};
+    return check_hip(oasis::launch_plan_fetch(pa, as_stream(stream)), fn);
 }
 
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk) {

@@ -40,6 +40,24 @@ __device__ __forceinline__ u32x2 load_u32x2(const void *p) {
     return *reinterpret_cast<const u32x2 *>(p);
 }
 
+// Buffer resource over one tile: loads at byte offsets >= `bytes` return zero
+// and touch no memory, so a block that is absent is "loaded" with bytes = 0
+// without a branch around the load instruction.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) 32-bit data, gfx9 family
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+// byte offset = lane part (VGPR) + constant part (scalar offset, no extra VGPR)
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t lane_off, int const_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, const_off, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t lane_off, int const_off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, const_off, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ s16x4 as_s16x4(u32x2 v) { return __builtin_bit_cast(s16x4, v); }
 

@@ -12,23 +12,39 @@
 // 16x16x32 bf16 with fp32 accumulation.  The kernel is bound by streaming the
 // keys from HBM: every key byte is read exactly once, 16 bytes per lane per
 // load, the whole 4 KiB (D = 128) tile of a block by one wave.  A wave owns a
-// chunk of 16 consecutive blocks of one (sequence, KV head) row and keeps four
-// blocks of loads in flight; the max over the tile is reduced across lanes
-// four blocks at a time so that each lane exchange serves several blocks.
+// chunk of consecutive blocks of one (sequence, KV head) row and streams it in
+// groups: the next group's loads are issued (as buffer loads that can never
+// fault) before the current group is reduced.  The max over a tile is reduced
+// across lanes four blocks at a time so that each lane exchange serves
+// several blocks.
 #include "oasis_device.h"
 #include "oasis_launch.h"
 
 namespace oasis {
 
-constexpr int kScoreChunk = 16;      // blocks per wave
-constexpr int kScoreUnroll = 4;      // blocks loaded together
+#ifndef OASIS_SCORE_CHUNK
+#define OASIS_SCORE_CHUNK 16         // blocks per wave
+#endif
+#ifndef OASIS_SCORE_GROUP
+#define OASIS_SCORE_GROUP 4          // blocks loaded together (a multiple of 4)
+#endif
+constexpr int kScoreChunk = OASIS_SCORE_CHUNK;
+constexpr int kScoreGroup = OASIS_SCORE_GROUP;
 constexpr int kScoreWaves = 4;       // waves per workgroup
+static_assert(kScoreChunk % kScoreGroup == 0 && kScoreGroup % 4 == 0 && kScoreChunk <= kWave,
+              "chunk must split into groups of four-block reductions");
+
+template <int D>
+struct KeyGroup {
+    u32x4 k[kScoreGroup][D / 32];
+};
 
 template <int D>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_blocks_kernel(ScoreArgs a) {
     constexpr int KK = D / 32;
+    constexpr uint32_t kTileBytes = kBlockTokens * D * 2;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps row indices scalar
     const int row = blockIdx.y;                       // b * hkv + g
     const int b = row / a.hkv;
     const int g = row - b * a.hkv;
@@ -68,58 +84,65 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_blocks_kernel(Score
     }
 
     const size_t page_stride = (size_t)a.hkv * kBlockTokens * D;
+    const uint16_t *head_base = a.k_pool + (size_t)g * kBlockTokens * D;
     // A operand: token r16 of the tile, head-dim slice 32*kk + 8*j4 .. +8.
-    const uint16_t *kbase = a.k_pool + (size_t)g * kBlockTokens * D + (size_t)r16 * D + 8 * j4;
+    const uint32_t koff = (uint32_t)(r16 * D + 8 * j4) * 2;
     float *out = a.scores + (size_t)row * a.width;
     const float NEG_INF = -__builtin_inff();
 
-#pragma unroll 1
-    for (int c = 0; c < kScoreChunk; c += kScoreUnroll) {
-        int pgs[kScoreUnroll];
-        u32x4 kv[kScoreUnroll][KK];
+    // Absent blocks get a zero-byte resource: their loads return zeros without
+    // touching memory, so every load is issued and the next group streams in
+    // while the current one is reduced.
+    auto load_group = [&](KeyGroup<D> &kg, int c) {
 #pragma unroll
-        for (int u = 0; u < kScoreUnroll; ++u) {
-            pgs[u] = readlane_i(pg, c + u);
-            if (pgs[u] >= 0) {
-                const uint16_t *kp = kbase + (size_t)pgs[u] * page_stride;
+        for (int u = 0; u < kScoreGroup; ++u) {
+            const int p = readlane_i(pg, c + u);
+            const rsrc_t r = p >= 0 ? make_rsrc(head_base + (size_t)p * page_stride, kTileBytes)
+                                    : make_rsrc(a.k_pool, 0u);
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) kv[u][kk] = load_u32x4(kp + 32 * kk);
-            }
+            for (int kk = 0; kk < KK; ++kk) kg.k[u][kk] = buf_load16(r, koff, 64 * kk);
         }
-        float v[kScoreUnroll];
+    };
+
+    KeyGroup<D> cur, nxt;
+    load_group(cur, 0);
 #pragma unroll
-        for (int u = 0; u < kScoreUnroll; ++u) {
-            v[u] = NEG_INF;
-            if (pgs[u] >= 0) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < kScoreChunk; c += kScoreGroup) {
+        if (c + kScoreGroup < kScoreChunk) load_group(nxt, c + kScoreGroup);
+        float v[kScoreGroup];
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) acc = mfma16x16x32(as_bf16x8(kv[u][kk]), qv[kk], acc);
-                // rows 4*j4 + i of the tile are tokens; keep the valid ones
-                const int valid = ctx - (n0 + c + u) * kBlockTokens - 4 * j4;
-                float m = NEG_INF;
+        for (int u = 0; u < kScoreGroup; ++u) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) m = (i < valid) ? fmaxf(m, acc[i]) : m;
-                v[u] = col_ok ? m : NEG_INF;
-            }
+            for (int kk = 0; kk < KK; ++kk) acc = mfma16x16x32(as_bf16x8(cur.k[u][kk]), qv[kk], acc);
+            // rows 4*j4 + i of the tile are tokens; keep the valid ones
+            const int valid = ctx - (n0 + c + u) * kBlockTokens - 4 * j4;
+            float m = NEG_INF;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = (i < valid) ? fmaxf(m, acc[i]) : m;
+            v[u] = (col_ok && readlane_i(pg, c + u) >= 0) ? m : NEG_INF;
         }
-        // Reduce four blocks across the wave: halve the block set per exchange
-        // (lane bit 5, then bit 4), then finish within 16-lane groups.
-        float a0 = (lane & 32) ? v[2] : v[0];
-        float a1 = (lane & 32) ? v[3] : v[1];
-        const float s0 = (lane & 32) ? v[0] : v[2];
-        const float s1 = (lane & 32) ? v[1] : v[3];
-        a0 = fmaxf(a0, shfl_xor_f(s0, 32));
-        a1 = fmaxf(a1, shfl_xor_f(s1, 32));
-        float x = (lane & 16) ? a1 : a0;
-        const float y = (lane & 16) ? a0 : a1;
-        x = fmaxf(x, shfl_xor_f(y, 16));
-        x = fmaxf(x, shfl_xor_f(x, 8));
-        x = fmaxf(x, shfl_xor_f(x, 4));
-        x = fmaxf(x, shfl_xor_f(x, 2));
-        x = fmaxf(x, shfl_xor_f(x, 1));
-        const int u_mine = ((lane >> 5) << 1) | ((lane >> 4) & 1);
-        const int n = n0 + c + u_mine;
-        if (r16 == 0 && n < a.width) out[n] = x * a.scale;
+        // Reduce four blocks at a time across the wave: halve the block set per
+        // exchange (lane bit 5, then bit 4), then finish within 16-lane groups.
+#pragma unroll
+        for (int q = 0; q < kScoreGroup; q += 4) {
+            float a0 = (lane & 32) ? v[q + 2] : v[q + 0];
+            float a1 = (lane & 32) ? v[q + 3] : v[q + 1];
+            const float s0 = (lane & 32) ? v[q + 0] : v[q + 2];
+            const float s1 = (lane & 32) ? v[q + 1] : v[q + 3];
+            a0 = fmaxf(a0, shfl_xor_f(s0, 32));
+            a1 = fmaxf(a1, shfl_xor_f(s1, 32));
+            float x = (lane & 16) ? a1 : a0;
+            const float y = (lane & 16) ? a0 : a1;
+            x = fmaxf(x, shfl_xor_f(y, 16));
+            x = fmaxf(x, shfl_xor_f(x, 8));
+            x = fmaxf(x, shfl_xor_f(x, 4));
+            x = fmaxf(x, shfl_xor_f(x, 2));
+            x = fmaxf(x, shfl_xor_f(x, 1));
+            const int n = n0 + c + q + (((lane >> 5) << 1) | ((lane >> 4) & 1));
+            if (r16 == 0 && n < a.width) out[n] = x * a.scale;
+        }
+        if (c + kScoreGroup < kScoreChunk) cur = nxt;
     }
 }
 

@@ -4,51 +4,45 @@
 // blocks; abstract: a 2,048-token KV budget, K = budget / 16 blocks per KV
 // head.  Ties go to the lower block index; the set is written ascending.
 //
-// Design: one workgroup per (sequence, KV head) row.  Scores become
-// order-preserving 32-bit keys in LDS; four 8-bit radix passes (LDS histogram
-// + workgroup scan) find the K-th largest key tau exactly.  Every key above
-// tau is taken, and of the keys equal to tau the lowest-index ones fill the
-// rest; an ordered workgroup scan over index-contiguous chunks writes the
-// winners in ascending order.  The result is exact and deterministic (no
-// floating-point arithmetic, no atomics whose order matters).
+// Design: one 1024-thread workgroup per (sequence, KV head) row.  Thread t
+// holds the order-preserving 32-bit keys of blocks t, t + 1024, ... in
+// registers (at most 15 per thread).  The K-th largest key tau is found bit
+// by bit from the top: a candidate prefix survives when at least K keys are
+// >= it; each count is a wavefront ballot + popcount per register slot (on
+// the scalar unit) summed over the 16 waves through LDS, one barrier a step.
+// Every key above tau is taken, and of the keys equal to tau the lowest-index
+// ones fill the rest; register slot i of thread t is block 1024 i + t, so a
+// ballot prefix per slot followed by a scan over the waves walks the blocks
+// in ascending order and writes the winners in place.  Exact and
+// deterministic: integer compares only, no atomics.
 #include "oasis_device.h"
 #include "oasis_launch.h"
 
 namespace oasis {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelPerThread = (kMaxSelectWidth + kSelThreads - 1) / kSelThreads;
 
 // Larger float -> larger key; -0.0 maps to +0.0 so that the two compare equal.
+// Every non-NaN float maps to a key >= 0x007fffff, so 0 marks "no block".
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
     if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive scan of one int per thread over a 256-thread workgroup.
-__device__ __forceinline__ int block_inclusive_scan(int v, int *wave_sums) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int t = __shfl_up(v, d, kWave);
-        if (lane >= d) v += t;
-    }
-    if (lane == kWave - 1) wave_sums[wave] = v;
-    __syncthreads();
-    int off = 0;
-    for (int w = 0; w < wave; ++w) off += wave_sums[w];
-    __syncthreads();
-    return v + off;
+__device__ __forceinline__ int popc_lt(uint64_t mask, int lane) {
+    return __popcll(mask & ((1ull << lane) - 1ull));
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectArgs a) {
-    extern __shared__ uint32_t keys[];           // [width]
-    __shared__ int hist[256];
-    __shared__ int wave_sums[kSelThreads / kWave];
-    __shared__ int s_digit, s_above;
+    __shared__ int counts[2][kSelWaves];
+    __shared__ int wsum_a[kSelWaves], wsum_b[kSelWaves];
 
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const int row = blockIdx.x;
     const int b = row / a.hkv;
     int ctx = a.ctx_len[b];
@@ -62,59 +56,81 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectArgs a) 
         for (int i = tid; i < a.k; i += kSelThreads) out[i] = i < nb ? i : -1;
         return;
     }
-    for (int n = tid; n < nb; n += kSelThreads) keys[n] = order_key(srow[n]);
+    const int E = (nb + kSelThreads - 1) / kSelThreads;   // register slots in use (uniform)
+    uint32_t key[kSelPerThread];
+#pragma unroll
+    for (int i = 0; i < kSelPerThread; ++i) {
+        const int n = i * kSelThreads + tid;
+        key[i] = (i < E && n < nb) ? order_key(srow[n]) : 0u;
+    }
+
+    // tau = the largest key value with at least K keys >= tau (the K-th largest key)
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < kSelPerThread; ++i)
+            if (i < E) c += __popcll(__ballot(key[i] >= cand));
+        if (lane == 0) counts[bit & 1][wave] = c;
+        __syncthreads();
+        int total = 0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) total += counts[bit & 1][w];
+        if (total >= a.k) tau = cand;
+    }
+
+    // How many keys lie strictly above tau; the rest of K are copies of tau.
+    int c_gt = 0;
+#pragma unroll
+    for (int i = 0; i < kSelPerThread; ++i)
+        if (i < E) c_gt += __popcll(__ballot(key[i] > tau));
+    if (lane == 0) counts[1][wave] = c_gt;       // counts[1] is free again after the last step's barrier
     __syncthreads();
+    int gt_total = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) gt_total += counts[1][w];
+    const int krem = a.k - gt_total;
 
-    uint32_t prefix = 0, mask = 0;
-    int krem = a.k;                               // how many still to take at/below the prefix
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[tid] = 0;
+    // Walk the blocks in ascending order, one register slot (1024 blocks) at a time.
+    int eq_base = 0, out_base = 0;
+#pragma unroll
+    for (int i = 0; i < kSelPerThread; ++i) {
+        if (i >= E) break;                        // uniform across the workgroup
+        const uint32_t u = key[i];
+        const uint64_t eqm = __ballot(u == tau);
+        if (lane == 0) wsum_a[wave] = __popcll(eqm);
         __syncthreads();
-        for (int n = tid; n < nb; n += kSelThreads) {
-            const uint32_t u = keys[n];
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+        int eq_before = eq_base, eq_slab = 0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) {
+            const int c = wsum_a[w];
+            eq_before += (w < wave) ? c : 0;
+            eq_slab += c;
         }
+        eq_before += popc_lt(eqm, lane);
+        const bool take = (u > tau) || (u == tau && eq_before < krem);
+        const uint64_t tm = __ballot(take);
+        if (lane == 0) wsum_b[wave] = __popcll(tm);
         __syncthreads();
-        // thread t looks at digit 255 - t: inclusive scan = keys with digit >= 255 - t
-        const int c = hist[255 - tid];
-        const int incl = block_inclusive_scan(c, wave_sums);
-        const int excl = incl - c;
-        if (excl < krem && krem <= incl) { s_digit = 255 - tid; s_above = excl; }
-        __syncthreads();
-        prefix |= (uint32_t)s_digit << shift;
-        mask |= 255u << shift;
-        krem -= s_above;
-        __syncthreads();
-    }
-    const uint32_t tau = prefix;                  // the K-th largest key; krem of its copies are taken
-
-    const int E = (nb + kSelThreads - 1) / kSelThreads;
-    const int lo = tid * E;
-    const int hi = lo + E < nb ? lo + E : nb;
-    int c_gt = 0, c_eq = 0;
-    for (int n = lo; n < hi; ++n) {
-        const uint32_t u = keys[n];
-        c_gt += u > tau;
-        c_eq += u == tau;
-    }
-    const int eq_before = block_inclusive_scan(c_eq, wave_sums) - c_eq;
-    int take_eq = krem - eq_before;
-    take_eq = take_eq < 0 ? 0 : (take_eq > c_eq ? c_eq : take_eq);
-    const int c_sel = c_gt + take_eq;
-    int pos = block_inclusive_scan(c_sel, wave_sums) - c_sel;
-    int er = eq_before;
-    for (int n = lo; n < hi; ++n) {
-        const uint32_t u = keys[n];
-        bool take = u > tau;
-        if (u == tau) { take = er < krem; ++er; }
-        if (take) out[pos++] = n;
+        int pos = out_base, take_slab = 0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) {
+            const int c = wsum_b[w];
+            pos += (w < wave) ? c : 0;
+            take_slab += c;
+        }
+        pos += popc_lt(tm, lane);
+        if (take) out[pos] = i * kSelThreads + tid;
+        eq_base += eq_slab;
+        out_base += take_slab;
+        __syncthreads();                          // wsum_a / wsum_b are reused next slab
     }
 }
 
 hipError_t launch_select_topk(const SelectArgs &a, hipStream_t stream) {
     if (a.rows == 0) return hipSuccess;
-    const size_t shmem = (size_t)(a.width > 0 ? a.width : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL(select_topk_kernel, dim3(a.rows), dim3(kSelThreads), shmem, stream, a);
+    hipLaunchKernelGGL(select_topk_kernel, dim3(a.rows), dim3(kSelThreads), 0, stream, a);
     return hipGetLastError();
 }
 

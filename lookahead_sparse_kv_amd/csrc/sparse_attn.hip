@@ -10,13 +10,14 @@
 //   S (16 tokens x 16 query rows) = 16x16x32 bf16 MFMAs, A = key tile
 //     (token-major, 16 B per lane), B = the group's query rows;
 //   online softmax per query row in fp32 (exp2 with a folded log2(e));
-//   O^T (D x 16 query rows) += V^T (D x 16 tokens) * P (16 tokens x 16 rows):
-//     16x16x16 bf16 MFMAs whose B operand is P exactly as the S tile left it
-//     in registers, and whose A operand is read straight from the dim-major
-//     value tile (8 B per lane, 512 contiguous bytes per load).
+//   O^T (D x 16 query rows) += V^T (D x 32 tokens) * P (32 tokens x 16 rows)
+//     for two blocks at a time: 16x16x32 bf16 MFMAs whose B operand is P
+//     exactly as the two S tiles left it in registers, and whose A operand is
+//     read straight from the dim-major value tiles (8 B per lane per block,
+//     512 contiguous bytes per load).
 // The gather is HBM-bound (each selected K and V byte is read once); split-K
-// spreads rows over enough waves to fill 256 CUs, and the next block's loads
-// are issued before the current block is computed.  A second kernel merges
+// spreads rows over enough waves to fill 256 CUs, and the next pair of
+// blocks is loaded before the current pair is computed.  A second kernel merges
 // the (max, sum, O) partials of the splits.
 #include "oasis_device.h"
 #include "oasis_launch.h"
@@ -24,7 +25,10 @@
 namespace oasis {
 
 constexpr int kAttnWaves = 4;
-constexpr int kAttnTargetWaves = 2048;   // enough to give every CU several waves
+#ifndef OASIS_ATTN_TARGET_WAVES
+#define OASIS_ATTN_TARGET_WAVES 1024
+#endif
+constexpr int kAttnTargetWaves = OASIS_ATTN_TARGET_WAVES;   // enough to give every CU several waves
 constexpr int kAttnMinPerSplit = 4;
 constexpr int kAttnMaxPerSplit = 64;     // one list entry per lane
 
@@ -42,24 +46,34 @@ void attn_split_plan(int rows, int n_blk, int *splits, int *per_split) {
 
 template <int D>
 struct BlockRegs {
-    u32x4 k[D / 32];
-    u32x2 v[D / 16];
+    u32x4 k[D / 32];   // key tile: token r16, dims 32*kk + 8*j4 .. +8
+    u32x2 v[D / 16];   // value tile (dim-major): dim 16*mt + r16, tokens 4*j4 .. +4
 };
 
+// Load one block's key and value tiles.  An absent block has zero-byte
+// resources: every lane reads zeros and no memory is touched, so the load
+// instructions are issued unconditionally and the compiler can count the
+// loads in flight exactly.
 template <int D>
-__device__ __forceinline__ void load_block(BlockRegs<D> &r, const uint16_t *kp, const uint16_t *vp) {
+__device__ __forceinline__ void load_block(BlockRegs<D> &r, rsrc_t kr, rsrc_t vr, uint32_t koff,
+                                           uint32_t voff) {
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) r.k[kk] = load_u32x4(kp + 32 * kk);
+    for (int kk = 0; kk < D / 32; ++kk) r.k[kk] = buf_load16(kr, koff, 64 * kk);
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) r.v[mt] = load_u32x2(vp + 16 * kBlockTokens * mt);
+    for (int mt = 0; mt < D / 16; ++mt) r.v[mt] = buf_load8(vr, voff, 16 * kBlockTokens * 2 * mt);
+}
+
+// Masks of the two bf16 values of tokens (t0, t0 + 1) that are valid (< nt).
+__device__ __forceinline__ uint32_t pair_mask(int t0, int nt) {
+    return (t0 < nt ? 0x0000ffffu : 0u) | (t0 + 1 < nt ? 0xffff0000u : 0u);
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * kWave, 2) void attn_partial_kernel(AttnArgs a) {
     constexpr int KK = D / 32;
     constexpr int MT = D / 16;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps row indices scalar
     const int gw = blockIdx.x * kAttnWaves + wave;
     const int rows = a.batch * a.hkv;
     const int row = gw / a.splits;
@@ -90,7 +104,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial_kernel(AttnAr
         for (int kk = 0; kk < KK; ++kk) qv[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
     }
 
-    // Entry e0 + lane: its page and number of valid tokens (0 = skip).
+    // Entry e0 + lane: its page and number of valid tokens (page -1 = skip).
     int my_page = -1, my_ntok = 0;
     if (lane < ne) {
         const size_t e = (size_t)row * a.n_blk + e0 + lane;
@@ -105,8 +119,15 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial_kernel(AttnAr
     }
 
     const size_t page_stride = (size_t)a.hkv * kBlockTokens * D;
-    const uint16_t *kbase = a.k_pool + (size_t)g * kBlockTokens * D + (size_t)r16 * D + 8 * j4;
-    const uint16_t *vbase = a.v_pool + (size_t)g * D * kBlockTokens + (size_t)r16 * kBlockTokens + 4 * j4;
+    const size_t head_off = (size_t)g * kBlockTokens * D;       // same for K and V tiles
+    constexpr uint32_t kTileBytes = kBlockTokens * D * 2;
+    const uint32_t koff = (uint32_t)(r16 * D + 8 * j4) * 2;             // + 64 B per kk
+    const uint32_t voff = (uint32_t)(r16 * kBlockTokens + 4 * j4) * 2;  // + 512 B per mt
+    auto tile = [&](const uint16_t *pool, int e) {
+        const int p = e < ne ? readlane_i(my_page, e) : -1;
+        return p >= 0 ? make_rsrc(pool + (size_t)p * page_stride + head_off, kTileBytes)
+                      : make_rsrc(pool, 0u);
+    };
 
     float m_run = NEG_INF;      // running max of column r16 (log2 units)
     float l_run = 0.f;          // this lane's share of the column's running sum
@@ -114,61 +135,68 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial_kernel(AttnAr
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Find the first valid entry and prefetch it.
-    int i = 0;
-    while (i < ne && readlane_i(my_page, i) < 0) ++i;
-    BlockRegs<D> cur;
-    if (i < ne) {
-        const size_t off = (size_t)readlane_i(my_page, i) * page_stride;
-        load_block<D>(cur, kbase + off, vbase + off);
-    }
-    while (i < ne) {
-        const int nt = readlane_i(my_ntok, i);
-        int nx = i + 1;
-        while (nx < ne && readlane_i(my_page, nx) < 0) ++nx;
-        BlockRegs<D> nxt;
-        if (nx < ne) {
-            const size_t off = (size_t)readlane_i(my_page, nx) * page_stride;
-            load_block<D>(nxt, kbase + off, vbase + off);
-        }
-
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    // Entries go in pairs: the pair after the current one is loaded before
+    // the current one is computed, so up to four blocks are in flight.
+    BlockRegs<D> cur[2], nxt[2];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) s = mfma16x16x32(as_bf16x8(cur.k[kk]), qv[kk], s);
-        float x[4];
-        float mb = NEG_INF;
+    for (int u = 0; u < 2; ++u) load_block<D>(cur[u], tile(a.k_pool, u), tile(a.v_pool, u), koff, voff);
+    for (int i = 0; i < ne; i += 2) {
+        int nt[2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            x[t] = (4 * j4 + t < nt) ? s[t] * a.scale_log2 : NEG_INF;
-            mb = fmaxf(mb, x[t]);
+        for (int u = 0; u < 2; ++u) {
+            nt[u] = (i + u < ne && readlane_i(my_page, i + u) >= 0) ? readlane_i(my_ntok, i + u) : 0;
+            load_block<D>(nxt[u], tile(a.k_pool, i + 2 + u), tile(a.v_pool, i + 2 + u), koff, voff);
         }
-        mb = fmaxf(mb, shfl_xor_f(mb, 16));
-        mb = fmaxf(mb, shfl_xor_f(mb, 32));
-        const float m_new = fmaxf(m_run, mb);    // finite: every block has a valid token
-        const float alpha = exp2f(m_run - m_new);
-        const uint32_t p01 = pack_bf16x2(exp2f(x[0] - m_new), exp2f(x[1] - m_new));
-        const uint32_t p23 = pack_bf16x2(exp2f(x[2] - m_new), exp2f(x[3] - m_new));
-        // the normaliser sums the same bf16-rounded weights the MFMA uses
-        const float psum = bf16_bits_to_float(p01 & 0xffffu) + bf16_bits_to_float(p01 >> 16) +
-                           bf16_bits_to_float(p23 & 0xffffu) + bf16_bits_to_float(p23 >> 16);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (nt < kBlockTokens) {
-            // zero the values of masked tokens so that garbage cannot reach O
-            const int base_t = 4 * j4;
-            const uint32_t k01 = (base_t + 0 < nt ? 0x0000ffffu : 0u) | (base_t + 1 < nt ? 0xffff0000u : 0u);
-            const uint32_t k23 = (base_t + 2 < nt ? 0x0000ffffu : 0u) | (base_t + 3 < nt ? 0xffff0000u : 0u);
+        if (nt[0] + nt[1] > 0) {
+            float x[2][4];
+            float mb = NEG_INF;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) { cur.v[mt].x &= k01; cur.v[mt].y &= k23; }
-        }
-        const s16x4 pb = as_s16x4(u32x2{p01, p23});
+            for (int u = 0; u < 2; ++u) {
+                f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            o[mt] *= alpha;
-            o[mt] = mfma16x16x16(as_s16x4(cur.v[mt]), pb, o[mt]);
+                for (int kk = 0; kk < KK; ++kk) s = mfma16x16x32(as_bf16x8(cur[u].k[kk]), qv[kk], s);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    x[u][t] = (4 * j4 + t < nt[u]) ? s[t] * a.scale_log2 : NEG_INF;
+                    mb = fmaxf(mb, x[u][t]);
+                }
+            }
+            mb = fmaxf(mb, shfl_xor_f(mb, 16));
+            mb = fmaxf(mb, shfl_xor_f(mb, 32));
+            const float m_new = fmaxf(m_run, mb);   // finite: the pair has a valid token
+            const float alpha = exp2f(m_run - m_new);
+            uint32_t pw[2][2];
+            float psum = 0.f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                pw[u][0] = pack_bf16x2(exp2f(x[u][0] - m_new), exp2f(x[u][1] - m_new));
+                pw[u][1] = pack_bf16x2(exp2f(x[u][2] - m_new), exp2f(x[u][3] - m_new));
+                // the normaliser sums the same bf16-rounded weights the MFMA uses
+                psum += bf16_bits_to_float(pw[u][0] & 0xffffu) + bf16_bits_to_float(pw[u][0] >> 16) +
+                        bf16_bits_to_float(pw[u][1] & 0xffffu) + bf16_bits_to_float(pw[u][1] >> 16);
+                if (nt[u] < kBlockTokens) {
+                    // zero the values of tokens past the context so that whatever the
+                    // page holds there cannot reach O (0 * NaN would)
+                    const uint32_t k01 = pair_mask(4 * j4, nt[u]);
+                    const uint32_t k23 = pair_mask(4 * j4 + 2, nt[u]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) { cur[u].v[mt].x &= k01; cur[u].v[mt].y &= k23; }
+                }
+            }
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            // O^T += V^T P over the pair's 32 tokens: reduction index 8*j4 + i is
+            // token 4*j4 + i of the first block (i < 4) or of the second (i >= 4).
+            const bf16x8 pb = as_bf16x8(u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]});
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                o[mt] *= alpha;
+                const u32x4 va = {cur[0].v[mt].x, cur[0].v[mt].y, cur[1].v[mt].x, cur[1].v[mt].y};
+                o[mt] = mfma16x16x32(as_bf16x8(va), pb, o[mt]);
+            }
         }
-        cur = nxt;
-        i = nx;
+        cur[0] = nxt[0];
+        cur[1] = nxt[1];
     }
 
     // Column totals of the normaliser live in lanes r16, r16+16, r16+32, r16+48.
@@ -195,21 +223,20 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
     const int b = row / a.hkv;
     const int g = row - b * a.hkv;
     const int d = threadIdx.x;
-    float M = -__builtin_inff();
-    for (int s = 0; s < a.splits; ++s) {
-        const size_t slot = ((size_t)row * a.splits + s) * a.n_rows_q + c;
-        M = fmaxf(M, a.part_ml[2 * slot]);
-    }
+    const float NEG_INF = -__builtin_inff();
+    const size_t slot0 = (size_t)row * a.splits * a.n_rows_q + c;
+    const size_t sstride = a.n_rows_q;
+    float M = NEG_INF;
+#pragma unroll 8
+    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[2 * (slot0 + s * sstride)]);
     float L = 0.f, O = 0.f;
-    if (M != -__builtin_inff()) {
-        for (int s = 0; s < a.splits; ++s) {
-            const size_t slot = ((size_t)row * a.splits + s) * a.n_rows_q + c;
-            const float m = a.part_ml[2 * slot];
-            if (m == -__builtin_inff()) continue;
-            const float w = exp2f(m - M);
-            L += w * a.part_ml[2 * slot + 1];
-            O += w * a.part_o[slot * D + d];
-        }
+#pragma unroll 8
+    for (int s = 0; s < a.splits; ++s) {
+        const size_t slot = slot0 + s * sstride;
+        const float m = a.part_ml[2 * slot];
+        const float w = (m == NEG_INF) ? 0.f : exp2f(m - M);
+        L += w * a.part_ml[2 * slot + 1];
+        O += w * a.part_o[slot * D + d];
     }
     const float res = L > 0.f ? O / L : 0.f;
     const int iq = c / a.group;

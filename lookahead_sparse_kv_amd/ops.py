@@ -21,7 +21,7 @@ BLOCK_SIZE = 16
 OASIS_OK, OASIS_ERR_INVALID, OASIS_ERR_UNSUPPORTED, OASIS_ERR_NOMEM, OASIS_ERR_HIP = range(5)
 
 # Every symbol include/oasis.h declares.
-EXPORTS = ("oasis_score_blocks", "oasis_select_topk", "oasis_plan_fetch",
+EXPORTS = ("oasis_score_blocks", "oasis_select_topk", "oasis_plan_fetch", "oasis_select_plan",
            "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_status_string",
            "oasis_last_error", "oasis_version")
 
@@ -55,11 +55,12 @@ def lib() -> ctypes.CDLL:
         L.oasis_score_blocks.argtypes = [S, p, i32, p, p, p, f32, p, p]
         L.oasis_select_topk.argtypes = [S, p, p, i32, p, p]
         L.oasis_plan_fetch.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p]
+        L.oasis_select_plan.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p, p]
         L.oasis_attn_workspace_bytes.argtypes = [S, i32, i32]
         L.oasis_attn_workspace_bytes.restype = sz
         L.oasis_sparse_decode_attn.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz, p]
         for fn in ("oasis_score_blocks", "oasis_select_topk", "oasis_plan_fetch",
-                   "oasis_sparse_decode_attn"):
+                   "oasis_select_plan", "oasis_sparse_decode_attn"):
             getattr(L, fn).restype = ctypes.c_int
         L.oasis_status_string.argtypes = [ctypes.c_int]
         L.oasis_status_string.restype = ctypes.c_char_p
@@ -129,6 +130,15 @@ def plan_fetch(shape: OasisShape, sel, scores, k_blocks, cap, step, slot_block, 
     _check(lib().oasis_plan_fetch(ctypes.byref(shape), _ptr(sel), _ptr(scores), k_blocks, cap,
                                   step, _ptr(slot_block), _ptr(last_use), _ptr(fetch_block),
                                   _ptr(fetch_slot), _ptr(fetch_count), _stream(stream)))
+
+
+def select_plan(shape: OasisShape, scores, ctx_len, k_blocks, cap, step, sel, slot_block,
+                last_use, fetch_block, fetch_slot, fetch_count, stream=None):
+    """select_topk then plan_fetch in one launch where the shape allows (same results)."""
+    _check(lib().oasis_select_plan(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks, cap,
+                                   step, _ptr(sel), _ptr(slot_block), _ptr(last_use),
+                                   _ptr(fetch_block), _ptr(fetch_slot), _ptr(fetch_count),
+                                   _stream(stream)))
 
 
 def attn_workspace_bytes(shape: OasisShape, n_q: int, n_blk: int) -> int:

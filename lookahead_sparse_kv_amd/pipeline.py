@@ -54,6 +54,11 @@ class DecodeLayer:
                        self.slot_block, self.last_use, self.fetch_block, self.fetch_slot,
                        self.fetch_count, stream)
 
+    def select_plan(self, step, stream=None):
+        ops.select_plan(self.shape, self.scores, self.ctx_len, self.k_blocks, self.cap, step,
+                        self.sel, self.slot_block, self.last_use, self.fetch_block,
+                        self.fetch_slot, self.fetch_count, stream)
+
     def attend(self, q, blocks=None, stream=None):
         blocks = self.slot_block if blocks is None else blocks
         ops.sparse_decode_attn(self.shape, q, self.k_pool, self.v_pool, self.block_table, blocks,
@@ -61,7 +66,6 @@ class DecodeLayer:
 
     def step(self, q_look, q, step, stream=None):
         self.score(q_look, stream)
-        self.select(stream)
-        self.plan(step, stream)
+        self.select_plan(step, stream)
         self.attend(q, stream=stream)
         return self.out

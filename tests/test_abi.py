@@ -110,8 +110,8 @@ def test_attn_workspace_and_argument_checks():
     L = ops.lib()
     s = _shape(batch=16, num_q_heads=32, num_kv_heads=8, table_width=2048, num_pages=32768)
     ws = ops.attn_workspace_bytes(s, 1, 128)
-    # 128 rows x 16 splits x 4 query rows x (128 + 2) floats
-    assert ws == 128 * 16 * 4 * 130 * 4
+    # 128 rows x 8 splits x 4 query rows x (128 + 2) floats
+    assert ws == 128 * 8 * 4 * 130 * 4
     assert ops.attn_workspace_bytes(s, 0, 128) == 0
     assert ops.attn_workspace_bytes(s, 1, 0) == 0
     att = lambda n_q=1, n_blk=128, wsb=ws, wsp=P, blk=P: L.oasis_sparse_decode_attn(
@@ -129,3 +129,16 @@ def test_library_is_required():
     src = open(os.path.join(ROOT, "lookahead_sparse_kv_amd", "ops.py")).read()
     assert "oracle" not in src
     assert "no CPU fallback" in src
+
+
+def test_select_plan_rejects_bad_arguments():
+    L = ops.lib()
+    s = _shape()
+    sp = lambda k=8, cap=2, fb=P, shape=s: L.oasis_select_plan(
+        ctypes.byref(shape), P, P, k, cap, 0, P, P, P, fb, P, P, None)
+    assert sp(k=0) == ops.OASIS_ERR_INVALID
+    assert sp(k=2048) == ops.OASIS_ERR_UNSUPPORTED
+    assert sp(cap=9) == ops.OASIS_ERR_INVALID
+    assert sp(fb=None) == ops.OASIS_ERR_INVALID
+    assert sp(shape=_shape(table_width=20000)) == ops.OASIS_ERR_UNSUPPORTED
+    assert sp(shape=_shape(batch=0)) == ops.OASIS_OK

@@ -102,6 +102,8 @@ SELECT_CASES = [
     (2, 2, [4000, 900], 1, "zeros"),
     (2, 2, [3000, 6000], 64, "inf"),
     (1, 1, [0], 8, "normal"),                         # empty context
+    (2, 2, [2048 * 16, 1900 * 16], 300, "ties"),      # K above the one-wave limit
+    (2, 2, [2049 * 16, 3000 * 16], 128, "normal"),    # table wider than the one-wave limit
 ]
 
 
@@ -143,6 +145,7 @@ PLAN_CASES = [
     (2, 2, 100, 128, 128, "normal", None),      # fewer blocks than K
     (2, 2, 64, 5, 0, "normal", 5),              # cap 0: nothing moves but the hits
     (1, 3, 40, 1, 1, "zeros", None),
+    (2, 2, 1000, 300, 7, "ties", None),         # K above the one-wave limit (generic kernel)
 ]
 
 
@@ -172,6 +175,44 @@ def test_plan_fetch_bit_exact_over_steps(case):
         np.testing.assert_array_equal(g_sb.cpu().numpy(), sb)
         np.testing.assert_array_equal(g_lu.cpu().numpy(), lu)
         assert np.all(ocnt <= cap)
+
+
+@pytest.mark.parametrize("case", [
+    # B, Hkv, nb (= W), K, cap, mode
+    (4, 8, 2048, 128, 2, "normal"),
+    (2, 4, 2048, 128, 6, "ties"),
+    (3, 2, 300, 32, 32, "zeros"),
+    (2, 2, 100, 128, 25, "normal"),             # fewer blocks than K
+    (2, 2, 4000, 128, 2, "normal"),             # wider than the one-wave select: two launches
+    (2, 2, 1000, 300, 7, "ties"),               # K above the one-wave limit: two launches
+], ids=lambda c: f"nb{c[2]}K{c[3]}cap{c[4]}{c[5]}")
+def test_select_plan_fused_bit_exact_over_steps(case):
+    B, Hkv, nb, K, cap, mode = case
+    rng = np.random.default_rng(hash(str(case)) % 2 ** 32)
+    W = nb
+    ctx_len = np.full(B, nb * 16, np.int32)
+    ctx_len[-1] -= 5 * 16 + 3                   # a ragged last sequence
+    sb, lu = _random_state(rng, B, Hkv, K, nb - 6, None)
+    shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
+    g_sb, g_lu = dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))
+    g_ctx = dev(torch.from_numpy(ctx_len))
+    sel = torch.empty((B, Hkv, K), dtype=torch.int32, device=DEV)
+    fb = torch.empty((B, Hkv, cap), dtype=torch.int32, device=DEV)
+    fs = torch.empty_like(fb)
+    fc = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    for step in range(3, 11):
+        s = _random_scores(rng, B, Hkv, W, mode)
+        osel = orc.select(s.astype(np.float64), ctx_len, 16, K)
+        ofb, ofs, ocnt, sb, lu = orc.plan(osel, s.astype(np.float64), sb, lu, cap, step)
+        ops.select_plan(shape, dev(torch.from_numpy(s)), g_ctx, K, cap, step, sel, g_sb, g_lu,
+                        fb, fs, fc)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(sel.cpu().numpy(), osel)
+        np.testing.assert_array_equal(fc.cpu().numpy(), ocnt)
+        np.testing.assert_array_equal(fb.cpu().numpy(), ofb)
+        np.testing.assert_array_equal(fs.cpu().numpy(), ofs)
+        np.testing.assert_array_equal(g_sb.cpu().numpy(), sb)
+        np.testing.assert_array_equal(g_lu.cpu().numpy(), lu)
 
 
 # ---------------------------------------------------------------- attention
