@@ -106,10 +106,10 @@ int oasis_select_topk(const oasis_shape *s, const float *scores, const int32_t *
     if (s->batch == 0) return ok();
     if (!scores || !ctx_len || !sel) return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
     const int rows = s->batch * s->num_kv_heads;
-    if (oasis::wave_select_plan_fits(s->table_width, k_blocks, true)) {
+    if (oasis::row_select_plan_fits(s->table_width, k_blocks, 1)) {
         oasis::SelectPlanArgs a{scores, ctx_len, sel, nullptr, nullptr, nullptr, nullptr, nullptr,
                                 rows, s->num_kv_heads, s->table_width, k_blocks, 0, 0};
-        return check_hip(oasis::launch_wave_select_plan(a, 1, as_stream(stream)), fn);
+        return check_hip(oasis::launch_row_select_plan(a, 1, as_stream(stream)), fn);
     }
     oasis::SelectArgs a{scores, ctx_len, sel, rows, s->num_kv_heads, s->table_width, k_blocks};
     return check_hip(oasis::launch_select_topk(a, as_stream(stream)), fn);
@@ -133,15 +133,10 @@ int oasis_plan_fetch(const oasis_shape *s, const int32_t *sel, const float *scor
     if (cap > 0 && (!fetch_block || !fetch_slot))
         return fail(OASIS_ERR_INVALID, "%s: NULL fetch list with cap %d", fn, cap);
     const int rows = s->batch * s->num_kv_heads;
-    if (oasis::wave_select_plan_fits(s->table_width, k_blocks, false)) {
-        oasis::SelectPlanArgs a{scores, nullptr, const_cast<int32_t *>(sel), slot_block, last_use,
-                                fetch_block, fetch_slot, fetch_count, rows, s->num_kv_heads,
-                                s->table_width, k_blocks, cap, step};
-        return check_hip(oasis::launch_wave_select_plan(a, 2, as_stream(stream)), fn);
-    }
-    oasis::PlanArgs a{sel, scores, slot_block, last_use, fetch_block, fetch_slot, fetch_count,
-                      rows, s->table_width, k_blocks, cap, step};
-    return check_hip(oasis::launch_plan_fetch(a, as_stream(stream)), fn);
+    oasis::SelectPlanArgs a{scores, nullptr, const_cast<int32_t *>(sel), slot_block, last_use,
+                            fetch_block, fetch_slot, fetch_count, rows, s->num_kv_heads,
+                            s->table_width, k_blocks, cap, step};
+    return check_hip(oasis::launch_row_select_plan(a, 2, as_stream(stream)), fn);
 }
 
 int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
@@ -165,17 +160,18 @@ int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *
     if (cap > 0 && (!fetch_block || !fetch_slot))
         return fail(OASIS_ERR_INVALID, "%s: NULL fetch list with cap %d", fn, cap);
     const int rows = s->batch * s->num_kv_heads;
-    if (oasis::wave_select_plan_fits(s->table_width, k_blocks, true)) {
-        oasis::SelectPlanArgs a{scores, ctx_len, sel, slot_block, last_use, fetch_block, fetch_slot,
-                                fetch_count, rows, s->num_kv_heads, s->table_width, k_blocks, cap,
-                                step};
-        return check_hip(oasis::launch_wave_select_plan(a, 3, as_stream(stream)), fn);
+    oasis::SelectPlanArgs a{scores, ctx_len, sel, slot_block, last_use, fetch_block, fetch_slot,
+                            fetch_count, rows, s->num_kv_heads, s->table_width, k_blocks, cap,
+                            step};
+    if (oasis::row_select_plan_fits(s->table_width, k_blocks, 3))
+        return check_hip(oasis::launch_row_select_plan(a, 3, as_stream(stream)), fn);
+    if (oasis::row_select_plan_fits(s->table_width, k_blocks, 1)) {
+        if (int e = check_hip(oasis::launch_row_select_plan(a, 1, as_stream(stream)), fn)) return e;
+    } else {
+        oasis::SelectArgs sa{scores, ctx_len, sel, rows, s->num_kv_heads, s->table_width, k_blocks};
+        if (int e = check_hip(oasis::launch_select_topk(sa, as_stream(stream)), fn)) return e;
     }
-    oasis::SelectArgs sa{scores, ctx_len, sel, rows, s->num_kv_heads, s->table_width, k_blocks};
-    if (int e = check_hip(oasis::launch_select_topk(sa, as_stream(stream)), fn)) return e;
-    oasis::PlanArgs pa{sel, scores, slot_block, last_use, fetch_block, fetch_slot, fetch_count,
-                       rows, s->table_width, k_blocks, cap, step};
-    return check_hip(oasis::launch_plan_fetch(pa, as_stream(stream)), fn);
+    return check_hip(oasis::launch_row_select_plan(a, 2, as_stream(stream)), fn);
 }
 
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk) {

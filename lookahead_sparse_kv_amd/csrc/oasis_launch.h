@@ -26,17 +26,6 @@ struct SelectArgs {
     int rows, hkv, width, k;
 };
 
-struct PlanArgs {
-    const int32_t *sel;
-    const float *scores;
-    int32_t *slot_block;
-    int32_t *last_use;
-    int32_t *fetch_block;
-    int32_t *fetch_slot;
-    int32_t *fetch_count;
-    int rows, width, k, cap, step;
-};
-
 struct SelectPlanArgs {
     const float *scores;
     const int32_t *ctx_len;
@@ -66,10 +55,9 @@ struct AttnArgs {
 
 hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_select_topk(const SelectArgs &a, hipStream_t stream);
-hipError_t launch_plan_fetch(const PlanArgs &a, hipStream_t stream);
-// One wave per row, no workgroup barriers; mode 1 = select, 2 = plan, 3 = both.
-bool wave_select_plan_fits(int width, int k, bool needs_select);
-hipError_t launch_wave_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
+// One 256-thread workgroup per row; mode 1 = select, 2 = plan, 3 = select then plan.
+bool row_select_plan_fits(int width, int k, int mode);
+hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
 hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_t stream);
 
 // Split-K plan of the attention kernel: how many splits per row and entries per split.
@@ -78,8 +66,9 @@ void attn_split_plan(int rows, int n_blk, int *splits, int *per_split);
 constexpr int kBlockTokens = 16;   // tokens per KV block
 constexpr int kMaxRowsQ = 16;     // lookahead / query rows per KV head in one MFMA tile
 constexpr int kMaxKBlocks = 1024; // K limit of select / plan
-constexpr int kWaveMaxK = 256;    // K limit of the one-wave-per-row select / plan
-constexpr int kWaveMaxWidth = 2048;   // table width limit of the one-wave select (32 keys per lane)
+constexpr int kRowSelectMaxWidth = 8192;  // widest table the 256-thread select keeps in LDS
+constexpr int kFusedMaxWidth = 4096;      // fused select + plan: table width limit
+constexpr int kFusedMaxK = 512;           // fused select + plan: K limit
 constexpr int kMaxSelectWidth = 15360;   // keys of a row staged in LDS (60 KiB)
 
 }  // namespace oasis

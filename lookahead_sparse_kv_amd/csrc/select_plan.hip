@@ -1,0 +1,86 @@
+// select_plan.hip -- the select, plan and fused select + plan kernels: one
+// 256-thread workgroup per (sequence, KV head) row (row_select_plan.h).
+//
+// The fused kernel keeps the row's keys, its selection and its slot table in
+// LDS from start to end: the selection never goes back to HBM before it is
+// planned, the slot table is read while the selection runs, and the launch
+// between the two steps disappears.
+#include "row_select_plan.h"
+
+namespace oasis {
+
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+__device__ __forceinline__ int row_valid_blocks(const int32_t *ctx_len, int b, int width) {
+    int ctx = ctx_len[b];
+    ctx = ctx < 0 ? 0 : ctx;
+    const int nb = (ctx + kBlockTokens - 1) / kBlockTokens;
+    return nb > width ? width : nb;
+}
+
+// MODE 1 = select, 2 = plan (selection read from a.sel), 3 = select then plan.
+template <int MODE>
+__global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlanArgs a) {
+    extern __shared__ int dyn[];
+    __shared__ RowShared sh;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const int K = a.k;
+    const int Kp = plan_pad(K);
+    int *sel = dyn;                                               // Kp
+    int *pl = sel + Kp;                                           // 9 Kp (plan)
+    uint32_t *keys = reinterpret_cast<uint32_t *>(MODE & 2 ? pl + 9 * Kp : pl);   // width
+    const float *srow = a.scores + (size_t)row * a.width;
+    const size_t rk = (size_t)row * K;
+
+    if (MODE & 1) {
+        const int nb = row_valid_blocks(a.ctx_len, row / a.hkv, a.width);
+        for (int n = tid; n < nb; n += kRowThreads) keys[n] = score_key(srow[n]);
+        __syncthreads();
+        row_select(keys, nb, K, sel, sh);
+        if (a.sel)
+            for (int i = tid; i < K; i += kRowThreads) a.sel[rk + i] = sel[i];
+    } else {
+        for (int i = tid; i < K; i += kRowThreads) {
+            const int s = a.sel[rk + i];
+            sel[i] = (s >= 0 && s < a.width) ? s : -1;
+        }
+        __syncthreads();
+    }
+    if (MODE & 2) {
+        int32_t *fb = a.fetch_block + (size_t)row * a.cap;
+        int32_t *fs = a.fetch_slot + (size_t)row * a.cap;
+        if (MODE & 1)
+            row_plan(sel, [&](int s) { return key_to_score(keys[s]); }, K, a.cap, a.step,
+                     a.slot_block + rk, a.last_use + rk, fb, fs, a.fetch_count + row, pl, sh);
+        else
+            row_plan(sel, [&](int s) { return srow[s]; }, K, a.cap, a.step, a.slot_block + rk,
+                     a.last_use + rk, fb, fs, a.fetch_count + row, pl, sh);
+    }
+}
+
+bool row_select_plan_fits(int width, int k, int mode) {
+    if (k > kMaxKBlocks) return false;
+    if (mode == 1) return width <= kRowSelectMaxWidth;
+    if (mode == 2) return true;
+    return width <= kFusedMaxWidth && k <= kFusedMaxK;
+}
+
+hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream) {
+    if (a.rows == 0) return hipSuccess;
+    const int Kp = plan_pad(a.k);
+    const size_t w = (size_t)(a.width > 0 ? a.width : 1);
+    const dim3 grid(a.rows), block(kRowThreads);
+    if (mode == 1) {
+        hipLaunchKernelGGL(row_select_plan_kernel<1>, grid, block, (Kp + w) * 4, stream, a);
+    } else if (mode == 2) {
+        hipLaunchKernelGGL(row_select_plan_kernel<2>, grid, block, (size_t)10 * Kp * 4, stream, a);
+    } else {
+        hipLaunchKernelGGL(row_select_plan_kernel<3>, grid, block, (10 * Kp + w) * 4, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace oasis

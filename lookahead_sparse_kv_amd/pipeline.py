@@ -42,22 +42,23 @@ class DecodeLayer:
         self.workspace = torch.empty((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
 
     # individual stages -------------------------------------------------
-    def score(self, q_look, stream=None):
-        ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len, self.scores,
-                         stream=stream)
+    def score(self, q_look, stream=None, scores=None):
+        ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len,
+                         self.scores if scores is None else scores, stream=stream)
 
-    def select(self, stream=None):
-        ops.select_topk(self.shape, self.scores, self.ctx_len, self.k_blocks, self.sel, stream)
+    def select(self, stream=None, scores=None):
+        ops.select_topk(self.shape, self.scores if scores is None else scores, self.ctx_len,
+                        self.k_blocks, self.sel, stream)
 
-    def plan(self, step, stream=None):
-        ops.plan_fetch(self.shape, self.sel, self.scores, self.k_blocks, self.cap, step,
-                       self.slot_block, self.last_use, self.fetch_block, self.fetch_slot,
-                       self.fetch_count, stream)
+    def plan(self, step, stream=None, scores=None):
+        ops.plan_fetch(self.shape, self.sel, self.scores if scores is None else scores,
+                       self.k_blocks, self.cap, step, self.slot_block, self.last_use,
+                       self.fetch_block, self.fetch_slot, self.fetch_count, stream)
 
-    def select_plan(self, step, stream=None):
-        ops.select_plan(self.shape, self.scores, self.ctx_len, self.k_blocks, self.cap, step,
-                        self.sel, self.slot_block, self.last_use, self.fetch_block,
-                        self.fetch_slot, self.fetch_count, stream)
+    def select_plan(self, step, stream=None, scores=None):
+        ops.select_plan(self.shape, self.scores if scores is None else scores, self.ctx_len,
+                        self.k_blocks, self.cap, step, self.sel, self.slot_block, self.last_use,
+                        self.fetch_block, self.fetch_slot, self.fetch_count, stream)
 
     def attend(self, q, blocks=None, stream=None):
         blocks = self.slot_block if blocks is None else blocks
@@ -69,3 +70,70 @@ class DecodeLayer:
         self.select_plan(step, stream)
         self.attend(q, stream=stream)
         return self.out
+
+
+class PipelinedDecode:
+    """Steady-state decode of one layer with the next step's scoring overlapped.
+
+    The pages' prefetch pipeline (Figure 8 of the metalmedia.ai summary) lets
+    the draft query of step t drive top-K prediction and KV selection before
+    that layer's attention at step t + 1.  Here attention of step t, which
+    reads the working set left by the previous plan, runs on the caller's
+    stream while the block scoring of the lookahead query for step t + 1 runs
+    on a side stream; select + plan for step t + 1 then waits for both (it
+    rewrites the working set attention reads).  The score buffer is doubled so
+    that scoring can run a step ahead.  Every stage sees exactly the inputs it
+    sees in DecodeLayer.step order (score -> select/plan -> attention), so the
+    results are identical.
+
+        pipe = PipelinedDecode(layer)
+        pipe.prime(q_look_0, step=0)          # score + select/plan of step 0
+        for t in range(T):
+            pipe.step(q_t, q_look_{t+1}, t)   # attention(t) || score(t+1); select/plan(t+1)
+        pipe.drain()
+    """
+
+    def __init__(self, layer: DecodeLayer):
+        self.L = layer
+        self.buf = [layer.scores, torch.empty_like(layer.scores)]
+        self.side = torch.cuda.Stream(device=layer.scores.device)       # default priority
+        self.ev_scored = [torch.cuda.Event(), torch.cuda.Event()]
+        self.ev_planned = [torch.cuda.Event(), torch.cuda.Event()]
+        self.used = [False, False]
+        self.i = 0
+
+    def _score_next(self, q_look, main):
+        b = self.i % 2
+        if self.used[b]:
+            self.side.wait_event(self.ev_planned[b])    # the plan that last read buf[b]
+        else:
+            self.side.wait_stream(main)                 # inputs written on the caller's stream
+        self.L.score(q_look, stream=self.side, scores=self.buf[b])
+        self.ev_scored[b].record(self.side)
+        return b
+
+    def _plan(self, b, step, main):
+        main.wait_event(self.ev_scored[b])
+        self.L.select_plan(step, stream=main, scores=self.buf[b])
+        self.ev_planned[b].record(main)
+        self.used[b] = True
+        self.i += 1
+
+    def prime(self, q_look, step):
+        main = torch.cuda.current_stream()
+        b = self._score_next(q_look, main)
+        self._plan(b, step, main)
+
+    def step(self, q, q_look_next, step, copy_out=True):
+        """Attention of `step` (true query q), overlapped with the scoring of
+        q_look_next; then select + plan of step + 1.  Returns a copy of the
+        output of `step` (or None), valid on the caller's stream."""
+        main = torch.cuda.current_stream()
+        b = self._score_next(q_look_next, main)
+        self.L.attend(q, stream=main)
+        out = self.L.out.clone() if copy_out else None
+        self._plan(b, step + 1, main)
+        return out
+
+    def drain(self):
+        torch.cuda.current_stream().wait_stream(self.side)

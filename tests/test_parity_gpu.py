@@ -14,7 +14,7 @@ import torch
 
 from lookahead_sparse_kv_amd import ops
 from lookahead_sparse_kv_amd import workload as wlm
-from lookahead_sparse_kv_amd.pipeline import DecodeLayer
+from lookahead_sparse_kv_amd.pipeline import DecodeLayer, PipelinedDecode
 from oracle import oasis_oracle as orc
 from parity_utils import (ATTN_ATOL, check_plan_row, check_scores, check_selection_row,
                           score_tolerance)
@@ -402,6 +402,36 @@ def test_decode_steps_mid_size_with_lru(n_look):
         exempt += _check_step_rows(wl, d, layer, q_look, q, sb0, lu0, cap, step, rows, "mid")
         assert np.all(layer.fetch_count.cpu().numpy() <= cap)
     assert exempt <= len(rows) * 6 // 4
+
+
+def test_pipelined_decode_matches_sequential_steps():
+    """Scoring of step t + 1 on a side stream, overlapped with attention of
+    step t, gives bit-identical outputs and state to the plain step order."""
+    wl = wlm.small_workload(batch=4, q_heads=32, kv_heads=8, head_dim=128,
+                            ctx=(8192, 6000, 4096, 7000), budget=1024, n_hot=24, ratio=0.05, seed=43)
+    d = wlm.make_layer(wl)
+    T = 6
+    looks = [dev(wlm.draw_lookahead(wl, d["q32"], 300 + t).to(torch.bfloat16)) for t in range(T + 1)]
+    q = dev(d["q"].unsqueeze(1))
+    sb, lu = (x.numpy() for x in wlm.empty_state(wl))
+    seq = _gpu_layer(wl, d, wl.cap(), sb, lu)
+    want = []
+    for t in range(T):
+        seq.step(looks[t], q, t)
+        want.append(seq.out.clone())
+    seq.score(looks[T])
+    seq.select_plan(T)
+    pipe_layer = _gpu_layer(wl, d, wl.cap(), sb, lu)
+    pipe = PipelinedDecode(pipe_layer)
+    pipe.prime(looks[0], 0)
+    got = [pipe.step(q, looks[t + 1], t) for t in range(T)]
+    pipe.drain()
+    torch.cuda.synchronize()
+    for t in range(T):
+        assert torch.equal(got[t], want[t]), t
+    assert torch.equal(pipe_layer.slot_block, seq.slot_block)
+    assert torch.equal(pipe_layer.last_use, seq.last_use)
+    assert torch.equal(pipe_layer.sel, seq.sel)
 
 
 def test_step_is_deterministic():
