@@ -50,9 +50,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              kRsrcWord3);
 }
-// byte offset = lane part (VGPR) + constant part (scalar offset, no extra VGPR)
+// byte offset = lane part (VGPR) + constant part (scalar offset, no extra VGPR);
+// CPOL is the cache-policy operand of the load.
+template <int CPOL = 0>
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t lane_off, int const_off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, const_off, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, const_off, CPOL);
 }
 __device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t lane_off, int const_off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, const_off, 0);

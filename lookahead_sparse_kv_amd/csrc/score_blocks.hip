@@ -25,6 +25,9 @@ namespace oasis {
 #ifndef OASIS_SCORE_CHUNK
 #define OASIS_SCORE_CHUNK 16         // blocks per wave
 #endif
+#ifndef OASIS_SCORE_CPOL
+#define OASIS_SCORE_CPOL 2           // keys are streamed once per step: non-temporal loads
+#endif
 #ifndef OASIS_SCORE_GROUP
 #define OASIS_SCORE_GROUP 4          // blocks loaded together (a multiple of 4)
 #endif
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_blocks_kernel(Score
             const rsrc_t r = p >= 0 ? make_rsrc(head_base + (size_t)p * page_stride, kTileBytes)
                                     : make_rsrc(a.k_pool, 0u);
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) kg.k[u][kk] = buf_load16(r, koff, 64 * kk);
+            for (int kk = 0; kk < KK; ++kk) kg.k[u][kk] = buf_load16<OASIS_SCORE_CPOL>(r, koff, 64 * kk);
         }
     };
 

@@ -102,13 +102,17 @@ class PipelinedDecode:
         self.used = [False, False]
         self.i = 0
 
-    def _score_next(self, q_look, main):
+    def _score_next(self, q_look, main, ev=None):
         b = self.i % 2
         if self.used[b]:
             self.side.wait_event(self.ev_planned[b])    # the plan that last read buf[b]
         else:
             self.side.wait_stream(main)                 # inputs written on the caller's stream
+        if ev:
+            ev[0].record(self.side)
         self.L.score(q_look, stream=self.side, scores=self.buf[b])
+        if ev:
+            ev[1].record(self.side)
         self.ev_scored[b].record(self.side)
         return b
 
@@ -124,12 +128,14 @@ class PipelinedDecode:
         b = self._score_next(q_look, main)
         self._plan(b, step, main)
 
-    def step(self, q, q_look_next, step, copy_out=True):
+    def step(self, q, q_look_next, step, copy_out=True, score_events=None):
         """Attention of `step` (true query q), overlapped with the scoring of
         q_look_next; then select + plan of step + 1.  Returns a copy of the
-        output of `step` (or None), valid on the caller's stream."""
+        output of `step` (or None), valid on the caller's stream.
+        `score_events`, if given, are two timing events recorded around the
+        scoring kernel on the side stream."""
         main = torch.cuda.current_stream()
-        b = self._score_next(q_look_next, main)
+        b = self._score_next(q_look_next, main, score_events)
         self.L.attend(q, stream=main)
         out = self.L.out.clone() if copy_out else None
         self._plan(b, step + 1, main)
