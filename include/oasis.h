@@ -178,6 +178,43 @@ int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_
                              uint16_t *out, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/*
+ * Pinned host KV pool, the tier the working set is fetched from.  The pages
+ * keep the full KV cache in CPU memory and hold only a bounded working set in
+ * HBM (abstract; Figure 7 caption).  oasis_hostpool_create allocates `bytes`
+ * of page-locked host memory mapped into the device address space (host
+ * pointer in *host_ptr; OASIS_ERR_NOMEM if the allocation fails);
+ * oasis_hostpool_device_pointer gives the address kernels use for it;
+ * oasis_hostpool_destroy frees it (after all work that reads it is done).
+ * The caller fills the pool from the host.
+ */
+int oasis_hostpool_create(size_t bytes, void **host_ptr);
+int oasis_hostpool_device_pointer(void *host_ptr, void **device_ptr);
+int oasis_hostpool_destroy(void *host_ptr);
+
+/*
+ * Capped fetch host -> HBM.  Five-step flow step 3 (pull only the missing
+ * blocks, bounded per step), Figure 8 caption (the transfer runs in the
+ * background before that layer's attention at the next step), Figure 9
+ * caption (working-set slots of each KV head).  For every row (b, g) and
+ * i < fetch_count[b][g] (clamped to [0, cap]), copies logical block
+ * fetch_block[b][g][i] of the host pool into working-set slot
+ * fetch_slot[b][g][i], i.e. into page ws_page_table[b][slot] of the working-set
+ * pools, for KV head g.  Layouts: host_k [B][Hkv][host_blocks][bs][D] and
+ * host_v [B][Hkv][host_blocks][D][bs] (device-mapped pointers from
+ * oasis_hostpool_device_pointer); ws_page_table [B][table_width];
+ * ws_k_pool [num_pages][Hkv][bs][D], ws_v_pool [num_pages][Hkv][D][bs].  Here
+ * s->table_width is the number of slots K and s->num_pages the working-set
+ * pages.  Entries with a block outside [0, host_blocks), a slot outside
+ * [0, K) or a page outside [0, num_pages) are skipped.  The fetch lists are
+ * those oasis_plan_fetch writes; the call reads them on the device, so no host
+ * synchronisation is needed.  Requires 0 <= cap <= K.
+ */
+int oasis_fetch_blocks(const oasis_shape *s, const uint16_t *host_k, const uint16_t *host_v,
+                       int32_t host_blocks, const int32_t *fetch_block, const int32_t *fetch_slot,
+                       const int32_t *fetch_count, int32_t cap, const int32_t *ws_page_table,
+                       uint16_t *ws_k_pool, uint16_t *ws_v_pool, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *oasis_status_string(int status);
 

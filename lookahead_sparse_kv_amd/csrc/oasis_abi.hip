@@ -224,4 +224,53 @@ int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_
     return check_hip(oasis::launch_sparse_decode_attn(a, s->head_dim, as_stream(stream)), fn);
 }
 
+int oasis_hostpool_create(size_t bytes, void **host_ptr) {
+    const char *fn = "oasis_hostpool_create";
+    if (!host_ptr) return fail(OASIS_ERR_INVALID, "%s: host_ptr is NULL", fn);
+    *host_ptr = nullptr;
+    if (bytes == 0) return fail(OASIS_ERR_INVALID, "%s: zero bytes", fn);
+    void *p = nullptr;
+    const hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocPortable);
+    if (e != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return fail(OASIS_ERR_NOMEM, "%s: hipHostMalloc of %zu bytes failed: %s", fn, bytes,
+                    hipGetErrorString(e));
+    }
+    *host_ptr = p;
+    return ok();
+}
+
+int oasis_hostpool_device_pointer(void *host_ptr, void **device_ptr) {
+    const char *fn = "oasis_hostpool_device_pointer";
+    if (!host_ptr || !device_ptr) return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    *device_ptr = nullptr;
+    return check_hip(hipHostGetDevicePointer(device_ptr, host_ptr, 0), fn);
+}
+
+int oasis_hostpool_destroy(void *host_ptr) {
+    const char *fn = "oasis_hostpool_destroy";
+    if (!host_ptr) return ok();
+    return check_hip(hipHostFree(host_ptr), fn);
+}
+
+int oasis_fetch_blocks(const oasis_shape *s, const uint16_t *host_k, const uint16_t *host_v,
+                       int32_t host_blocks, const int32_t *fetch_block, const int32_t *fetch_slot,
+                       const int32_t *fetch_count, int32_t cap, const int32_t *ws_page_table,
+                       uint16_t *ws_k_pool, uint16_t *ws_v_pool, void *stream) {
+    const char *fn = "oasis_fetch_blocks";
+    if (int e = check_shape(s, fn)) return e;
+    if (host_blocks < 1) return fail(OASIS_ERR_INVALID, "%s: host_blocks %d < 1", fn, host_blocks);
+    if (cap < 0 || cap > s->table_width)
+        return fail(OASIS_ERR_INVALID, "%s: cap %d outside [0, table_width = %d]", fn, cap,
+                    s->table_width);
+    if (s->batch == 0 || cap == 0) return ok();
+    if (!host_k || !host_v || !fetch_block || !fetch_slot || !fetch_count || !ws_page_table ||
+        !ws_k_pool || !ws_v_pool)
+        return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    oasis::FetchArgs a{host_k, host_v, fetch_block, fetch_slot, fetch_count, ws_page_table,
+                       ws_k_pool, ws_v_pool, s->batch, s->num_kv_heads, host_blocks,
+                       s->table_width, cap, s->num_pages};
+    return check_hip(oasis::launch_fetch_blocks(a, s->head_dim, as_stream(stream)), fn);
+}
+
 }  // extern "C"

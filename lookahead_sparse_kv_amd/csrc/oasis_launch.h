@@ -38,6 +38,18 @@ struct SelectPlanArgs {
     int rows, hkv, width, k, cap, step;
 };
 
+struct FetchArgs {
+    const uint16_t *host_k;       // device-mapped pinned host pool, [B][Hkv][host_blocks][bs][D]
+    const uint16_t *host_v;       // [B][Hkv][host_blocks][D][bs]
+    const int32_t *fetch_block;
+    const int32_t *fetch_slot;
+    const int32_t *fetch_count;
+    const int32_t *ws_page_table; // [B][k_slots] slot -> working-set page
+    uint16_t *ws_k;               // [ws_pages][Hkv][bs][D]
+    uint16_t *ws_v;               // [ws_pages][Hkv][D][bs]
+    int batch, hkv, host_blocks, k_slots, cap, ws_pages;
+};
+
 struct AttnArgs {
     const uint16_t *q;
     const uint16_t *k_pool;
@@ -58,6 +70,7 @@ hipError_t launch_select_topk(const SelectArgs &a, hipStream_t stream);
 // One 256-thread workgroup per row; mode 1 = select, 2 = plan, 3 = select then plan.
 bool row_select_plan_fits(int width, int k, int mode);
 hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
+hipError_t launch_fetch_blocks(const FetchArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_t stream);
 
 // Split-K plan of the attention kernel: how many splits per row and entries per split.

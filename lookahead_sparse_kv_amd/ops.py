@@ -22,8 +22,9 @@ OASIS_OK, OASIS_ERR_INVALID, OASIS_ERR_UNSUPPORTED, OASIS_ERR_NOMEM, OASIS_ERR_H
 
 # Every symbol include/oasis.h declares.
 EXPORTS = ("oasis_score_blocks", "oasis_select_topk", "oasis_plan_fetch", "oasis_select_plan",
-           "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_status_string",
-           "oasis_last_error", "oasis_version")
+           "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_hostpool_create",
+           "oasis_hostpool_device_pointer", "oasis_hostpool_destroy", "oasis_fetch_blocks",
+           "oasis_status_string", "oasis_last_error", "oasis_version")
 
 
 class OasisShape(ctypes.Structure):
@@ -59,8 +60,14 @@ def lib() -> ctypes.CDLL:
         L.oasis_attn_workspace_bytes.argtypes = [S, i32, i32]
         L.oasis_attn_workspace_bytes.restype = sz
         L.oasis_sparse_decode_attn.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz, p]
+        L.oasis_hostpool_create.argtypes = [sz, ctypes.POINTER(ctypes.c_void_p)]
+        L.oasis_hostpool_device_pointer.argtypes = [p, ctypes.POINTER(ctypes.c_void_p)]
+        L.oasis_hostpool_destroy.argtypes = [p]
+        L.oasis_fetch_blocks.argtypes = [S, p, p, i32, p, p, p, i32, p, p, p, p]
         for fn in ("oasis_score_blocks", "oasis_select_topk", "oasis_plan_fetch",
-                   "oasis_select_plan", "oasis_sparse_decode_attn"):
+                   "oasis_select_plan", "oasis_sparse_decode_attn", "oasis_hostpool_create",
+                   "oasis_hostpool_device_pointer", "oasis_hostpool_destroy",
+                   "oasis_fetch_blocks"):
             getattr(L, fn).restype = ctypes.c_int
         L.oasis_status_string.argtypes = [ctypes.c_int]
         L.oasis_status_string.restype = ctypes.c_char_p
@@ -156,3 +163,55 @@ def sparse_decode_attn(shape: OasisShape, q, k_pool, v_pool, page_table, blk, bl
         _ptr(blk), n_blk, _ptr(blk_logical), _ptr(ctx_len), scale, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+class HostPool:
+    """Page-locked, device-mapped host memory from oasis_hostpool_create.
+
+    `tensor(shape, dtype)` views (a prefix of) it as a CPU tensor for filling
+    from the host; `device_ptr` is the address kernels read it through."""
+
+    def __init__(self, nbytes: int):
+        host = ctypes.c_void_p()
+        _check(lib().oasis_hostpool_create(nbytes, ctypes.byref(host)))
+        self.host_ptr = host.value
+        dev = ctypes.c_void_p()
+        try:
+            _check(lib().oasis_hostpool_device_pointer(ctypes.c_void_p(self.host_ptr),
+                                                       ctypes.byref(dev)))
+        except Exception:
+            lib().oasis_hostpool_destroy(ctypes.c_void_p(self.host_ptr))
+            raise
+        self.device_ptr = dev.value
+        self.nbytes = nbytes
+
+    def tensor(self, shape, dtype, offset_bytes=0):
+        import numpy as np
+        n = 1
+        for x in shape:
+            n *= x
+        esize = torch.tensor([], dtype=dtype).element_size()
+        assert offset_bytes + n * esize <= self.nbytes
+        buf = (ctypes.c_uint8 * (n * esize)).from_address(self.host_ptr + offset_bytes)
+        return torch.from_numpy(np.frombuffer(buf, dtype=np.uint8)).view(dtype).view(*shape)
+
+    def close(self):
+        if self.host_ptr:
+            lib().oasis_hostpool_destroy(ctypes.c_void_p(self.host_ptr))
+            self.host_ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def fetch_blocks(ws_shape: OasisShape, host_k_dev: int, host_v_dev: int, host_blocks: int,
+                 fetch_block, fetch_slot, fetch_count, cap, ws_page_table, ws_k_pool, ws_v_pool,
+                 stream=None):
+    """Copy the listed blocks from the pinned host pool into working-set slots (device side)."""
+    _check(lib().oasis_fetch_blocks(ctypes.byref(ws_shape), ctypes.c_void_p(host_k_dev),
+                                    ctypes.c_void_p(host_v_dev), host_blocks, _ptr(fetch_block),
+                                    _ptr(fetch_slot), _ptr(fetch_count), cap, _ptr(ws_page_table),
+                                    _ptr(ws_k_pool), _ptr(ws_v_pool), _stream(stream)))

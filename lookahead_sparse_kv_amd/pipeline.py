@@ -143,3 +143,116 @@ class PipelinedDecode:
 
     def drain(self):
         torch.cuda.current_stream().wait_stream(self.side)
+
+
+class HostTierLayer:
+    """One layer whose full K and V live in a pinned host pool.
+
+    HBM holds the keys for scoring (exact scoring reads every key, so they stay
+    on the device) and, for attention, a bounded working set: K slots per
+    (sequence, KV head), in working-set pools addressed through a slot -> page
+    table.  The plan's capped fetch list is pulled from the host pool into the
+    slots by oasis_fetch_blocks (abstract: only the most relevant KV stays in
+    HBM; Figure 7 caption: CPU full KV cache and the GPU sparse working set;
+    Figure 9 caption: per-head working-set table).
+    """
+
+    def __init__(self, *, k_pool, block_table, ctx_len, host_pool_k_dev, host_pool_v_dev,
+                 host_blocks, ws_page_table, num_q_heads, k_blocks, cap, n_look=1, n_q=1):
+        dev = k_pool.device
+        B, W = block_table.shape
+        Hkv, D = k_pool.shape[1], k_pool.shape[-1]
+        self.k_pool, self.block_table, self.ctx_len = k_pool, block_table, ctx_len
+        self.host_k, self.host_v, self.host_blocks = host_pool_k_dev, host_pool_v_dev, host_blocks
+        self.ws_page_table = ws_page_table
+        ws_pages = int(ws_page_table.numel())
+        self.shape = ops.make_shape(B, num_q_heads, Hkv, D, W, k_pool.shape[0])
+        self.ws_shape = ops.make_shape(B, num_q_heads, Hkv, D, k_blocks, ws_pages)
+        self.k_blocks, self.cap, self.n_look, self.n_q = k_blocks, cap, n_look, n_q
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.ws_k = torch.zeros((ws_pages, Hkv, 16, D), dtype=torch.bfloat16, device=dev)
+        self.ws_v = torch.zeros((ws_pages, Hkv, D, 16), dtype=torch.bfloat16, device=dev)
+        self.scores = torch.empty((B, Hkv, W), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((B, Hkv, k_blocks), **i32)
+        self.slot_block = torch.full((B, Hkv, k_blocks), -1, **i32)
+        self.last_use = torch.full((B, Hkv, k_blocks), -(2 ** 31), **i32)
+        # fetch lists sized for cap = K (the fill); a step uses the first cap per row
+        self.fetch_block = torch.empty((B * Hkv * k_blocks,), **i32)
+        self.fetch_slot = torch.empty((B * Hkv * k_blocks,), **i32)
+        self.fetch_count = torch.zeros((B, Hkv), **i32)
+        self.out = torch.empty((B, n_q, num_q_heads, D), dtype=torch.bfloat16, device=dev)
+        ws = ops.attn_workspace_bytes(self.ws_shape, n_q, k_blocks)
+        self.workspace = torch.empty((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
+
+    def score(self, q_look, stream=None):
+        ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len, self.scores,
+                         stream=stream)
+
+    def select_plan(self, step, cap=None, stream=None):
+        cap = self.cap if cap is None else cap
+        ops.select_plan(self.shape, self.scores, self.ctx_len, self.k_blocks, cap, step, self.sel,
+                        self.slot_block, self.last_use, self.fetch_block, self.fetch_slot,
+                        self.fetch_count, stream)
+        self._last_cap = cap
+
+    def fetch(self, stream=None):
+        ops.fetch_blocks(self.ws_shape, self.host_k, self.host_v, self.host_blocks,
+                         self.fetch_block, self.fetch_slot, self.fetch_count, self._last_cap,
+                         self.ws_page_table, self.ws_k, self.ws_v, stream)
+
+    def attend(self, q, stream=None):
+        ops.sparse_decode_attn(self.ws_shape, q, self.ws_k, self.ws_v, self.ws_page_table, None,
+                               self.slot_block, self.ctx_len, self.out, self.workspace,
+                               stream=stream)
+
+
+class HostTierDecode:
+    """Decode steps over several layers with the fetch overlapped across layers.
+
+    Per step and layer, on the caller's stream: attention over the layer's
+    working set (after that layer's previous fetch has landed), scoring with the
+    lookahead query, select + plan.  The fetch of the planned blocks runs on a
+    side stream and overlaps the following layers; the next step's attention of
+    the same layer waits for it (Figure 8 caption: one layer's chain runs from
+    the draft query at step t through top-K prediction, KV selection and KV
+    transfer to that layer's attention at step t + 1; flow step 4: the stages
+    overlap across layers).
+    """
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        dev = self.layers[0].scores.device
+        self.side = torch.cuda.Stream(device=dev)                       # default priority
+        self.ev_planned = [torch.cuda.Event() for _ in self.layers]
+        self.ev_fetched = [torch.cuda.Event() for _ in self.layers]
+        self.pending = [False for _ in self.layers]
+
+    def fill(self, q_looks_prev, step=-1):
+        """The previous step: select the top K under q_looks_prev, plan them into
+        the empty slots (cap = K) and fetch them all."""
+        main = torch.cuda.current_stream()
+        for L, ql in zip(self.layers, q_looks_prev):
+            L.score(ql, main)
+            L.select_plan(step, cap=L.k_blocks, stream=main)
+            L.fetch(main)
+
+    def step(self, qs, q_looks, step, copy_out=False):
+        main = torch.cuda.current_stream()
+        outs = []
+        for li, L in enumerate(self.layers):
+            if self.pending[li]:
+                main.wait_event(self.ev_fetched[li])
+            L.attend(qs[li], main)
+            if copy_out:
+                outs.append(L.out.clone())
+            L.score(q_looks[li], main)
+            L.select_plan(step, stream=main)
+            self.ev_planned[li].record(main)
+            self.side.wait_event(self.ev_planned[li])
+            L.fetch(self.side)
+            self.ev_fetched[li].record(self.side)
+            self.pending[li] = True
+        return outs
+
+    def drain(self):
+        torch.cuda.current_stream().wait_stream(self.side)

@@ -481,3 +481,108 @@ def test_full_size_sampled_rows(name):
             r = sbg[b, g][sbg[b, g] >= 0]
             assert len(np.unique(r)) == len(r)
     assert np.all(np.isfinite(layer.out.float().cpu().numpy()))
+
+
+# ---------------------------------------------------------------- host tier
+def _host_pool_for(d, wl):
+    """Pinned host pool holding a layer's K ([B][Hkv][W][16][D]) then V ([B][Hkv][W][D][16])."""
+    B, Hkv, W, D = wl.batch, wl.num_kv_heads, wl.table_width, wl.head_dim
+    n = B * Hkv * W * 16 * D
+    pool = ops.HostPool(4 * n)
+    pool.tensor((B, Hkv, W, 16, D), torch.bfloat16).copy_(d["K"].view(B, Hkv, W, 16, D))
+    pool.tensor((B, Hkv, W, D, 16), torch.bfloat16, offset_bytes=2 * n).copy_(
+        d["V"].view(B, Hkv, W, 16, D).transpose(-1, -2))
+    return pool, pool.device_ptr, pool.device_ptr + 2 * n
+
+
+def test_fetch_blocks_copies_listed_tiles_and_skips_bad_entries():
+    wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(2000, 1500), n_hot=0,
+                            seed=52)
+    d = wlm.make_layer(wl, pools=False)
+    B, Hkv, W, K, cap = 2, 2, wl.table_width, 16, 6
+    pool, hk, hv = _host_pool_for(d, wl)
+    pt = torch.randperm(B * K, generator=torch.Generator().manual_seed(3)).to(torch.int32).view(B, K)
+    fb = torch.randint(0, 94, (B, Hkv, cap), generator=torch.Generator().manual_seed(4), dtype=torch.int32)
+    fs = torch.stack([torch.stack([torch.randperm(K)[:cap] for _ in range(Hkv)]) for _ in range(B)]).to(torch.int32)
+    fb[0, 1, 2] = W + 5          # block past the host pool: skipped
+    fs[1, 0, 1] = K + 3          # slot past the working set: skipped
+    fc = torch.tensor([[6, 4], [5, 6]], dtype=torch.int32)
+    ws_k = torch.zeros((B * K, Hkv, 16, 128), dtype=torch.bfloat16, device=DEV)
+    ws_v = torch.zeros((B * K, Hkv, 128, 16), dtype=torch.bfloat16, device=DEV)
+    shape = ops.make_shape(B, 8, Hkv, 128, K, B * K)
+    ops.fetch_blocks(shape, hk, hv, W, dev(fb), dev(fs), dev(fc), cap, dev(pt), ws_k, ws_v)
+    torch.cuda.synchronize()
+    gk, gv = ws_k.cpu(), ws_v.cpu()
+    expect_k = torch.zeros_like(gk)
+    expect_v = torch.zeros_like(gv)
+    for b in range(B):
+        for g in range(Hkv):
+            for i in range(int(fc[b, g])):
+                blk, slot = int(fb[b, g, i]), int(fs[b, g, i])
+                if not (0 <= blk < W and 0 <= slot < K):
+                    continue
+                page = int(pt[b, slot])
+                expect_k[page, g] = d["K"][b, g, 16 * blk:16 * blk + 16]
+                expect_v[page, g] = d["V"][b, g, 16 * blk:16 * blk + 16].T
+    assert torch.equal(gk, expect_k) and torch.equal(gv, expect_v)
+    del pool
+
+
+def test_host_tier_matches_full_pool_over_layers_and_steps():
+    """Four steps of two layers with the full KV in pinned host pools, the
+    capped fetch on a side stream overlapped with the next layer: outputs and
+    plans are bit-identical to the full-pool path, and every resident slot
+    holds its block's K and V."""
+    from lookahead_sparse_kv_amd.pipeline import HostTierDecode, HostTierLayer
+    wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 3000),
+                            budget=512, n_hot=10, ratio=0.125, seed=51)
+    K, cap, W, B, Hkv = wl.k_blocks, wl.cap(), wl.table_width, wl.batch, wl.num_kv_heads
+    n_layers, T = 2, 4
+    datas = [wlm.make_layer(wl, seed=51 + 7 * l) for l in range(n_layers)]
+    pools, host_layers, ref_layers = [], [], []
+    for l, d in enumerate(datas):
+        pool, hk, hv = _host_pool_for(d, wl)
+        pools.append(pool)
+        pt = torch.randperm(B * K, generator=torch.Generator().manual_seed(10 + l)).to(torch.int32).view(B, K)
+        host_layers.append(HostTierLayer(k_pool=dev(d["k_pool"]), block_table=dev(d["block_table"]),
+                                         ctx_len=dev(d["ctx_len"]), host_pool_k_dev=hk,
+                                         host_pool_v_dev=hv, host_blocks=W, ws_page_table=dev(pt),
+                                         num_q_heads=wl.num_q_heads, k_blocks=K, cap=cap))
+        sb, lu = (x.numpy() for x in wlm.empty_state(wl))
+        ref_layers.append(_gpu_layer(wl, d, cap, sb, lu))
+    prev = [dev(wlm.draw_lookahead(wl, d["q32"], 900 + l).to(torch.bfloat16)) for l, d in enumerate(datas)]
+    looks = [[dev(wlm.draw_lookahead(wl, d["q32"], 1000 + 10 * t + l).to(torch.bfloat16))
+              for l, d in enumerate(datas)] for t in range(T)]
+    qs = [dev(d["q"].unsqueeze(1)) for d in datas]
+    pipe = HostTierDecode(host_layers)
+    pipe.fill(prev)
+    for R, p in zip(ref_layers, prev):
+        R.score(p)
+        R.cap = K
+        R.select_plan(-1)
+        R.cap = cap
+    for t in range(T):
+        outs = pipe.step(qs, looks[t], t, copy_out=True)
+        for l, R in enumerate(ref_layers):
+            R.attend(qs[l])
+            assert torch.equal(outs[l], R.out), (t, l)
+            R.score(looks[t][l])
+            R.select_plan(t)
+    pipe.drain()
+    torch.cuda.synchronize()
+    for l, (H, R) in enumerate(zip(host_layers, ref_layers)):
+        assert torch.equal(H.slot_block, R.slot_block) and torch.equal(H.last_use, R.last_use)
+        assert int(H.fetch_count.max()) <= cap
+        sbk, ptb = H.slot_block.cpu(), H.ws_page_table.cpu()
+        wk, wv = H.ws_k.cpu(), H.ws_v.cpu()
+        d = datas[l]
+        for b in range(B):
+            for g in range(Hkv):
+                for j in range(K):
+                    blk = int(sbk[b, g, j])
+                    if blk < 0:
+                        continue
+                    page = int(ptb[b, j])
+                    assert torch.equal(wk[page, g], d["K"][b, g, 16 * blk:16 * blk + 16])
+                    assert torch.equal(wv[page, g], d["V"][b, g, 16 * blk:16 * blk + 16].T)
+    del pools
