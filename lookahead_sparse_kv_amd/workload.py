@@ -20,6 +20,9 @@ Recipe (draw order fixed; torch CPU generator):
      uniform without replacement; every key of a hot block is shifted by
      hot_shift * sum over the group's query heads of q_h / |q_h|, which raises
      each head's logit on those keys by about hot_shift standard deviations.
+     (Drifting workloads apply the shift to the bf16-rounded keys, so that a
+     block that stops being hot gets its exact unshifted keys back; each step
+     every hot block moves by a uniform integer in [-drift, drift].)
   6. page permutation: one shared pool of B * W pages, a random permutation
      of it gives every sequence's block table.
 Values are drawn in fp32 and rounded to bf16 (round to nearest even) for the
@@ -192,14 +195,22 @@ def make_layer(wl: Workload, seed: Optional[int] = None, *, pools: bool = True) 
             hot[b, h] = torch.randperm(nb[b], generator=g)[: wl.n_hot]
     pages = torch.randperm(B * W, generator=g).to(torch.int32).view(B, W)           # 6
 
-    if wl.n_hot:
-        _plant(wl, K32, hot, hot_direction(wl, q32))
     _poison_tail(wl, K32)
     _poison_tail(wl, V32)
-
     out = dict(q=_bf16(q32), q_look=_bf16(q_look32), hot=hot, block_table=pages.contiguous(),
                ctx_len=torch.tensor(wl.ctx, dtype=torch.int32), seed=seed)
-    out["K"] = _bf16(K32)
+    if wl.drift:
+        # drifting hot blocks are planted on the bf16 keys so that a move can
+        # restore the old position exactly: K = bf16(K0 + shift) on hot blocks
+        out["K0"] = _bf16(K32)
+        out["hot_dir"] = hot_direction(wl, q32)
+        out["K"] = out["K0"].clone()
+        _replant(wl, out, torch.zeros_like(hot_mask(wl, hot)), hot_mask(wl, hot))
+    else:
+        if wl.n_hot:
+            _plant(wl, K32, hot, hot_direction(wl, q32))
+            _poison_tail(wl, K32)                # a partial last block may be hot
+        out["K"] = _bf16(K32)
     out["V"] = _bf16(V32)
     if wl.kv_fp32:
         out.update(K32=K32, V32=V32, q32=q32, q_look32=q_look32)
@@ -234,6 +245,47 @@ def empty_state(wl: Workload):
     shape = (wl.batch, wl.num_kv_heads, wl.k_blocks)
     return (torch.full(shape, -1, dtype=torch.int32),
             torch.full(shape, -(2 ** 31), dtype=torch.int32))
+
+
+def hot_mask(wl: Workload, hot: torch.Tensor) -> torch.Tensor:
+    """[B][Hkv][W] bool: blocks that at least one hot entry points at."""
+    m = torch.zeros((wl.batch, wl.num_kv_heads, wl.table_width), dtype=torch.bool)
+    m.scatter_(2, hot, True)
+    return m
+
+
+def _replant(wl: Workload, d: dict, old_mask: torch.Tensor, new_mask: torch.Tensor):
+    """Rewrite the key tiles whose hot status changed (drifting workloads):
+    hot -> bf16(K0 + hot_shift * direction), not hot -> K0.  Updates d["K"] and,
+    if present, d["k_pool"]; returns the (page, head) pairs of the changed tiles."""
+    bs, D = wl.block_size, wl.head_dim
+    changed = (old_mask != new_mask).nonzero()            # rows of (b, g, blk)
+    if changed.numel() == 0:
+        return torch.empty((0,), dtype=torch.int64), torch.empty((0,), dtype=torch.int64)
+    b, g, blk = changed[:, 0], changed[:, 1], changed[:, 2]
+    tok = (blk.unsqueeze(1) * bs + torch.arange(bs)).reshape(-1)
+    bb = b.repeat_interleave(bs)
+    gg = g.repeat_interleave(bs)
+    base = d["K0"][bb, gg, tok]                           # [n * bs][D] bf16
+    shift = (wl.hot_shift * d["hot_dir"][bb, gg]).float()
+    ctx = torch.tensor(wl.ctx, dtype=torch.int64)
+    hot_now = (new_mask[b, g, blk].repeat_interleave(bs) & (tok < ctx[bb])).unsqueeze(1)
+    d["K"][bb, gg, tok] = torch.where(hot_now, (base.float() + shift).to(torch.bfloat16), base)
+    pages = d["block_table"][b, blk].to(torch.int64)
+    if "k_pool" in d:
+        d["k_pool"][pages, g] = d["K"][b.unsqueeze(1), g.unsqueeze(1),
+                                       (blk.unsqueeze(1) * bs + torch.arange(bs))]
+    return pages, g
+
+
+def drift_step(wl: Workload, d: dict, seed: int):
+    """One decode step of drift: every hot block moves by a uniform integer in
+    [-drift, +drift] (reflected at the ends), and the keys are re-planted
+    (old positions revert, new positions are shifted).  Updates d in place and
+    returns the (page, head) pairs of the key tiles that changed."""
+    old = hot_mask(wl, d["hot"])
+    d["hot"] = drift_hot(wl, d["hot"], seed)
+    return _replant(wl, d, old, hot_mask(wl, d["hot"]))
 
 
 def drift_hot(wl: Workload, hot: torch.Tensor, seed: int) -> torch.Tensor:

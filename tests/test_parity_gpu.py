@@ -586,3 +586,64 @@ def test_host_tier_matches_full_pool_over_layers_and_steps():
                     assert torch.equal(wk[page, g], d["K"][b, g, 16 * blk:16 * blk + 16])
                     assert torch.equal(wv[page, g], d["V"][b, g, 16 * blk:16 * blk + 16].T)
     del pools
+
+
+# ---------------------------------------------------------------- multi-step workloads at full size
+def _random_other_rows(wl, sb, lu, rows, seed):
+    rng = np.random.default_rng(seed)
+    for b in range(wl.batch):
+        nb = (wl.ctx[b] + 15) // 16
+        for g in range(wl.num_kv_heads):
+            if (b, g) not in rows:
+                sb[b, g] = rng.choice(nb, size=wl.k_blocks, replace=False)
+                lu[b, g] = -1
+    return sb, lu
+
+
+def test_drifting_hot_blocks_131k_sampled_rows():
+    """Llama-3.1-8B-shaped 131K context (8,192 blocks per row) with hot blocks
+    drifting by up to 4 blocks per step: sampled rows match the oracle at every
+    step (scores, selection, capped plan with LRU, attention), continuing from
+    the GPU's state; the fetch count never exceeds the cap on any row."""
+    wl = wlm.WORKLOADS["llama31_8b_128k_drift"]
+    d = wlm.make_layer(wl)
+    rows = [(0, 0), (1, 5), (3, 7)]
+    sb, lu = _oracle_seed_state(wl, d, seed=wl.seed + 1, rows=rows)
+    sb, lu = _random_other_rows(wl, sb, lu, rows, 5)
+    cap = wl.cap()
+    layer = _gpu_layer(wl, d, cap, sb, lu)
+    q = d["q"].unsqueeze(1)
+    counts = []
+    for step in range(6):
+        pages, heads = wlm.drift_step(wl, d, 7000 + step)
+        if pages.numel():
+            layer.k_pool[pages.to(DEV), heads.to(DEV)] = d["k_pool"][pages, heads].to(DEV)
+        q_look = wlm.draw_lookahead(wl, d["q32"], 8000 + step).to(torch.bfloat16)
+        sb0, lu0 = layer.slot_block.cpu().numpy(), layer.last_use.cpu().numpy()
+        layer.step(dev(q_look), dev(q), step)
+        torch.cuda.synchronize()
+        _check_step_rows(wl, d, layer, q_look, q, sb0, lu0, cap, step, rows, "drift131k")
+        fc = layer.fetch_count.cpu().numpy()
+        assert np.all(fc <= cap)
+        counts.append(int(fc.sum()))
+    assert max(counts) > 0
+
+
+def test_four_draft_queries_sampled_rows():
+    """Qwen3-8B shape with 4 draft lookahead queries (16 lookahead rows per KV
+    head, max over drafts) at fetch ratio 0.05: sampled rows match the oracle."""
+    wl = wlm.WORKLOADS["qwen3_8b_32k_spec4"].replace(ratios=(0.05,))
+    d = wlm.make_layer(wl)
+    rows = [(0, 1), (9, 4), (15, 7)]
+    sb, lu = _oracle_seed_state(wl, d, seed=wl.seed + 1, rows=rows)
+    sb, lu = _random_other_rows(wl, sb, lu, rows, 6)
+    cap = wl.cap()
+    assert cap == 6
+    layer = _gpu_layer(wl, d, cap, sb, lu)
+    q = d["q"].unsqueeze(1)
+    for step in range(3):
+        q_look = wlm.draw_lookahead(wl, d["q32"], 6000 + step).to(torch.bfloat16)
+        sb0, lu0 = layer.slot_block.cpu().numpy(), layer.last_use.cpu().numpy()
+        layer.step(dev(q_look), dev(q), step)
+        torch.cuda.synchronize()
+        _check_step_rows(wl, d, layer, q_look, q, sb0, lu0, cap, step, rows, "spec4")
