@@ -17,6 +17,11 @@ times, the scoring kernel's HBM roofline fraction, and the CPU oracle timed
 on a bounded sample of the same workload.
 
     python bench.py --copy-calibration   # plain 1 GiB device copies, for PMC scaling
+
+Other workloads (one JSON line each; not the headline metric):
+    --workload qwen3_32b_32k_hostpool    4 layers, full K/V in pinned host pools, capped fetch
+    --workload qwen3_8b_32k_spec4        4 draft queries, fetch-ratio sweep (host-pool tier)
+    --workload llama31_8b_128k_drift     131K context, hot blocks drifting over 64 steps
 """
 import argparse
 import hashlib
@@ -131,6 +136,183 @@ def cpu_baseline(wl, d, n_seqs, cap):
                       f"score+select+plan+attention step in fp64 ({dt:.2f} s)"}
 
 
+def _ev():
+    import torch
+    return torch.cuda.Event(enable_timing=True)
+
+
+def host_tier_layers(wl, ratio, n_layers, dev):
+    """Per layer: seeded inputs, a pinned host pool with the full K and V, the
+    device key copy for scoring, and the working set; returns (layers, pools,
+    true queries, lookahead draws per layer, previous-step lookahead per layer)."""
+    import torch
+    from lookahead_sparse_kv_amd import ops
+    from lookahead_sparse_kv_amd import workload as wlm
+    from lookahead_sparse_kv_amd.pipeline import HostTierLayer
+    B, Hkv, W, D, K = wl.batch, wl.num_kv_heads, wl.table_width, wl.head_dim, wl.k_blocks
+    layers, pools, qs, looks, prevs = [], [], [], [], []
+    for l in range(n_layers):
+        d = wlm.make_layer(wl, seed=wl.seed + 101 * l)
+        n = B * Hkv * W * 16 * D
+        pool = ops.HostPool(4 * n)
+        pool.tensor((B, Hkv, W, 16, D), torch.bfloat16).copy_(d["K"].view(B, Hkv, W, 16, D))
+        pool.tensor((B, Hkv, W, D, 16), torch.bfloat16, offset_bytes=2 * n).copy_(
+            d["V"].view(B, Hkv, W, 16, D).transpose(-1, -2))
+        pt = torch.randperm(B * K, generator=torch.Generator().manual_seed(wl.seed + l))
+        layers.append(HostTierLayer(
+            k_pool=d["k_pool"].to(dev), block_table=d["block_table"].to(dev),
+            ctx_len=d["ctx_len"].to(dev), host_pool_k_dev=pool.device_ptr,
+            host_pool_v_dev=pool.device_ptr + 2 * n, host_blocks=W,
+            ws_page_table=pt.to(torch.int32).view(B, K).to(dev), num_q_heads=wl.num_q_heads,
+            k_blocks=K, cap=wl.cap(ratio), n_look=wl.n_look))
+        pools.append(pool)
+        qs.append(d["q"].unsqueeze(1).to(dev))
+        looks.append([wlm.draw_lookahead(wl, d["q32"], wl.seed + 100 + i).to(torch.bfloat16).to(dev)
+                      for i in range(N_LOOK_DRAWS)])
+        prevs.append(wlm.draw_lookahead(wl, d["q32"], wl.seed + 1).to(torch.bfloat16).to(dev))
+        del d
+    return layers, pools, qs, looks, prevs
+
+
+def run_host_tier(layers, qs, looks, prevs, steps, warmup):
+    """Fill, warm up, then time `steps` overlapped steps; then a counting pass."""
+    import torch
+    from lookahead_sparse_kv_amd.pipeline import HostTierDecode
+    pipe = HostTierDecode(layers)
+    pipe.fill(prevs)
+    for i in range(warmup):
+        pipe.step(qs, [lk[i % N_LOOK_DRAWS] for lk in looks], i)
+    pipe.drain()
+    torch.cuda.synchronize()
+    fev = [[(_ev(), _ev()) for _ in layers] for _ in range(steps)]
+    e0, e1 = _ev(), _ev()
+    e0.record()
+    for i in range(steps):
+        s = warmup + i
+        pipe.step(qs, [lk[s % N_LOOK_DRAWS] for lk in looks], s, fetch_events=fev[i])
+    pipe.drain()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    fetch_ms = sum(a.elapsed_time(b) for row in fev for a, b in row) / steps
+    counts = []                          # fetched blocks per step (all layers), separate pass
+    for i in range(min(steps, 8)):
+        s = warmup + steps + i
+        pipe.step(qs, [lk[s % N_LOOK_DRAWS] for lk in looks], s)
+        torch.cuda.synchronize()
+        counts.append(sum(int(L.fetch_count.sum()) for L in layers))
+    pipe.drain()
+    torch.cuda.synchronize()
+    return ms_step, fetch_ms, counts
+
+
+def bench_hostpool(args, wl):
+    """Full K/V of several layers in pinned host pools; per step and layer:
+    attention over the working set, scoring, select/plan, and the capped fetch
+    on a side stream overlapped with the following layers."""
+    import torch
+    dev = torch.device("cuda:0")
+    n_layers = wl.layers
+    t0 = time.perf_counter()
+    layers, pools, qs, looks, prevs = host_tier_layers(wl, wl.ratios[0], n_layers, dev)
+    gen_s = time.perf_counter() - t0
+    ms_step, fetch_ms, counts = run_host_tier(layers, qs, looks, prevs, args.steps, args.warmup)
+    tile = 16 * wl.head_dim * 2 * 2                       # K + V of one block, one head
+    blocks = sum(counts) / len(counts)
+    gb_step = blocks * tile / 1e9
+    return {
+        "metric": "seq-decode-steps/s over all layers, host-pool KV tier with capped fetch",
+        "value": round(wl.batch / (ms_step * 1e-3), 1), "unit": "seq-decode-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": n_layers, "batch": wl.batch,
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "context": wl.ctx_max, "k_blocks": wl.k_blocks,
+                   "fetch_ratio": wl.ratios[0], "cap": wl.cap(),
+                   "host_pool_GiB": round(sum(p.nbytes for p in pools) / 2 ** 30, 2)},
+        "ms_per_layer": round(ms_step / n_layers, 4),
+        "fetched_blocks_per_step": blocks, "fetched_GB_per_step": round(gb_step, 5),
+        "fetch_kernel_ms_per_step": round(fetch_ms, 4),
+        "fetch_GBps": round(gb_step / (fetch_ms * 1e-3), 2) if fetch_ms > 0 else None,
+        "input_generation_s": round(gen_s, 1),
+    }
+
+
+def bench_ratio_sweep(args, wl):
+    """The fetch-ratio sweep (the pages' Table 2 analogue) on one layer with the
+    full K/V in a pinned host pool: steps/s and fetched GB/step per ratio."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = {}
+    layers, pools, qs, looks, prevs = host_tier_layers(wl, wl.ratios[0], 1, dev)
+    L = layers[0]
+    tile = 16 * wl.head_dim * 2 * 2
+    for ratio in wl.ratios:
+        L.cap = wl.cap(ratio)
+        L.slot_block.fill_(-1)
+        L.last_use.fill_(-(2 ** 31))
+        ms_step, fetch_ms, counts = run_host_tier(layers, qs, looks, prevs, args.steps, args.warmup)
+        blocks = sum(counts) / len(counts)
+        gb = blocks * tile / 1e9
+        out[str(ratio)] = {"cap": L.cap, "seq_steps_per_s": round(wl.batch / (ms_step * 1e-3), 1),
+                           "ms_per_step": round(ms_step, 4), "fetched_GB_per_step": round(gb, 5),
+                           "fetch_GBps": round(gb / (fetch_ms * 1e-3), 2) if fetch_ms > 0 else None}
+    best = max(v["seq_steps_per_s"] for v in out.values())
+    return {
+        "metric": "seq-decode-steps/s per fetch ratio, 4 draft lookahead queries, host-pool tier",
+        "value": best, "unit": "seq-decode-steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "n_look": wl.n_look,
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "context": wl.ctx_max, "k_blocks": wl.k_blocks},
+        "per_ratio": out,
+    }
+
+
+def bench_drift(args, wl):
+    """Long context with hot blocks drifting every step (full KV in HBM):
+    per-step time and fetched-block counts over wl.steps steps."""
+    import torch
+    from lookahead_sparse_kv_amd import workload as wlm
+    from lookahead_sparse_kv_amd.pipeline import DecodeLayer
+    dev = torch.device("cuda:0")
+    d = wlm.make_layer(wl)
+    layer = DecodeLayer(k_pool=d["k_pool"].to(dev), v_pool=d["v_pool"].to(dev),
+                        block_table=d["block_table"].to(dev), ctx_len=d["ctx_len"].to(dev),
+                        num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks, cap=wl.k_blocks)
+    q = d["q"].unsqueeze(1).to(dev)
+    layer.score(wlm.draw_lookahead(wl, d["q32"], wl.seed + 1).to(torch.bfloat16).to(dev))
+    layer.select_plan(-1)
+    layer.cap = wl.cap()
+    times, counts = [], []
+    for t in range(wl.steps):
+        pages, heads = wlm.drift_step(wl, d, wl.seed + 10_000 + t)
+        if pages.numel():
+            layer.k_pool[pages.to(dev), heads.to(dev)] = d["k_pool"][pages, heads].to(dev)
+        look = wlm.draw_lookahead(wl, d["q32"], wl.seed + 20_000 + t).to(torch.bfloat16).to(dev)
+        torch.cuda.synchronize()
+        a, b = _ev(), _ev()
+        a.record()
+        layer.step(look, q, t)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+        counts.append(int(layer.fetch_count.sum()))
+    steady = sorted(times[2:])
+    ms = steady[len(steady) // 2]
+    return {
+        "metric": "seq-decode-steps/s, long context with drifting hot blocks",
+        "value": round(wl.batch / (ms * 1e-3), 1), "unit": "seq-decode-steps/s", "n_gpus": 1,
+        "steps": wl.steps, "warmup": 2, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.ctx_max,
+                   "k_blocks": wl.k_blocks, "cap": wl.cap(), "drift": wl.drift},
+        "fetched_blocks_per_step": counts,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -148,6 +330,11 @@ def main():
 
     ops.lib()          # fail loudly before any work if the HIP library is missing
     wl = wlm.WORKLOADS[args.workload]
+    other = {"qwen3_32b_32k_hostpool": bench_hostpool, "qwen3_8b_32k_spec4": bench_ratio_sweep,
+             "llama31_8b_128k_drift": bench_drift}
+    if wl.name in other:
+        print(json.dumps(other[wl.name](args, wl)), flush=True)
+        return
     cap = wl.cap()
     t_gen = time.perf_counter()
     d = wlm.make_layer(wl)

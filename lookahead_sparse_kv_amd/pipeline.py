@@ -236,7 +236,10 @@ class HostTierDecode:
             L.select_plan(step, cap=L.k_blocks, stream=main)
             L.fetch(main)
 
-    def step(self, qs, q_looks, step, copy_out=False):
+    def step(self, qs, q_looks, step, copy_out=False, fetch_events=None):
+        """One decode step over every layer.  `fetch_events`, if given, holds a
+        (start, end) pair of timing events per layer, recorded around the
+        fetch on the side stream."""
         main = torch.cuda.current_stream()
         outs = []
         for li, L in enumerate(self.layers):
@@ -249,7 +252,11 @@ class HostTierDecode:
             L.select_plan(step, stream=main)
             self.ev_planned[li].record(main)
             self.side.wait_event(self.ev_planned[li])
+            if fetch_events:
+                fetch_events[li][0].record(self.side)
             L.fetch(self.side)
+            if fetch_events:
+                fetch_events[li][1].record(self.side)
             self.ev_fetched[li].record(self.side)
             self.pending[li] = True
         return outs
