@@ -49,6 +49,11 @@ def parse():
     p.add_argument("--cpu-sample-seqs", type=int, default=16,
                    help="sequences (all KV heads) of the workload the oracle runs")
     p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--replicas", type=int, default=4,
+                   help="device copies of the layer's K/V and state, taken in turn by "
+                        "successive steps, so that no step finds the previous one's "
+                        "working set in the 256 MB last-level cache (as in a model, "
+                        "where consecutive layers hold different KV)")
     p.add_argument("--detail", action="store_true",
                    help="also time the steps without overlap and each stage alone")
     return p.parse_args()
@@ -139,6 +144,13 @@ def cpu_baseline(wl, d, n_seqs, cap):
 def _ev():
     import torch
     return torch.cuda.Event(enable_timing=True)
+
+
+def percentiles_us(sorted_ms):
+    """p10 / median / p90 of a sorted list of milliseconds, in microseconds."""
+    n = len(sorted_ms)
+    pick = lambda f: round(sorted_ms[min(n - 1, int(f * n))] * 1e3, 2)
+    return {"p10": pick(0.1), "median": pick(0.5), "p90": pick(0.9)}
 
 
 def host_tier_layers(wl, ratio, n_layers, dev):
@@ -347,58 +359,87 @@ def main():
         for i in range(N_LOOK_DRAWS - 1)]
     prev = wlm.draw_lookahead(wl, d["q32"], wl.seed + 1).to(torch.bfloat16).to(dev)
 
-    layer = DecodeLayer(k_pool=g["k_pool"], v_pool=g["v_pool"], block_table=g["block_table"],
-                        ctx_len=g["ctx_len"], num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks,
-                        cap=wl.k_blocks, n_look=wl.n_look)
-    layer.score(prev)                      # previous step: fill the working set
-    layer.select()
-    layer.plan(-1)
-    layer.cap = cap
+    # Replica r holds its own copy of the pools (distinct HBM pages) and its own
+    # resident-set state; the contents, and so every selection, are the same.
+    n_rep = max(1, args.replicas)
+    layers = []
+    for r in range(n_rep):
+        kp = g["k_pool"] if r == 0 else g["k_pool"].clone()
+        vp = g["v_pool"] if r == 0 else g["v_pool"].clone()
+        L = DecodeLayer(k_pool=kp, v_pool=vp, block_table=g["block_table"], ctx_len=g["ctx_len"],
+                        num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks, cap=wl.k_blocks,
+                        n_look=wl.n_look)
+        L.score(prev)                      # previous step: fill the working set
+        L.select()
+        L.plan(-1)
+        L.cap = cap
+        layers.append(L)
+    layer = layers[0]
     torch.cuda.synchronize()
 
     # Whole-step timing.  Steady-state decode overlaps the scoring of step t+1
     # (side stream) with attention of step t; select/plan of t+1 waits for both.
-    # Each kernel is also bracketed by events on the stream it runs on.
-    pipe = PipelinedDecode(layer)
-    pipe.prime(looks[0], 0)
+    # Successive steps take the replicas in turn (one scoring stream, layer
+    # after layer, as in a model's decode step).  Only the scoring kernel is
+    # bracketed by events inside the timed loop, on the stream it runs on.
+    side = torch.cuda.Stream(device=dev)                                # default priority
+    pipes = [PipelinedDecode(L, side=side) for L in layers]
+    for P in pipes:
+        P.prime(looks[0], 0)
     for i in range(args.warmup):
-        pipe.step(q, looks[(i + 1) % N_LOOK_DRAWS], i, copy_out=False)
-    pipe.drain()
+        pipes[i % n_rep].step(q, looks[(i // n_rep + 1) % N_LOOK_DRAWS], 1 + i // n_rep,
+                              copy_out=False)
+    for P in pipes:
+        P.drain()
     torch.cuda.synchronize()
-    # only the scoring kernel (side stream) is bracketed inside the timed loop
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for i in range(args.steps):
         s = args.warmup + i
-        pipe.step(q, looks[(s + 1) % N_LOOK_DRAWS], s, copy_out=False, score_events=ev[i])
-    pipe.drain()
+        pipes[s % n_rep].step(q, looks[(s // n_rep + 1) % N_LOOK_DRAWS], 1 + s // n_rep,
+                              copy_out=False, score_events=ev[i])
+    for P in pipes:
+        P.drain()
     ev1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     score_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
     mean_ms = {"score": sum(score_ms) / len(score_ms)}
-    med_us = {"score": round(score_ms[len(score_ms) // 2] * 1e3, 2)}
 
-    # each stage alone, back to back on one stream (select/plan and attention
-    # are latency-bound and would otherwise share the GPU with scoring)
+    # each stage alone, back to back on one stream, replicas in turn
+    # (select/plan and attention are latency-bound and would otherwise share
+    # the GPU with scoring)
     iso = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         e = iso[i]
+        L = layers[i % n_rep]
         e[0].record()
-        layer.score(looks[i % N_LOOK_DRAWS])
+        L.score(looks[i % N_LOOK_DRAWS])
         e[1].record()
-        layer.select_plan(2000 + i)
+        L.select_plan(2000 + i)
         e[2].record()
-        layer.attend(q)
+        L.attend(q)
         e[3].record()
     torch.cuda.synchronize()
     alone = {}
     for j, k in enumerate(("score", "select_plan", "attn")):
-        v = sorted(e[j].elapsed_time(e[j + 1]) for e in iso)
-        alone[k] = (v[len(v) // 2], sum(v) / len(v))
+        alone[k] = sorted(e[j].elapsed_time(e[j + 1]) for e in iso)
+    # each stage back to back (events around the whole loop, replicas in
+    # turn): the per-call cost without an event and a launch gap per call
+    b2b = {}
+    for k, fn in (("score", lambda i, L: L.score(looks[i % N_LOOK_DRAWS])),
+                  ("select_plan", lambda i, L: L.select_plan(3000 + i)),
+                  ("attn", lambda i, L: L.attend(q))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            fn(i, layers[i % n_rep])
+        e1.record()
+        torch.cuda.synchronize()
+        b2b[k] = e0.elapsed_time(e1) / args.steps
 
     detail = {}
     if args.detail:
@@ -406,7 +447,7 @@ def main():
         e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e2.record()
         for i in range(args.steps):
-            layer.step(looks[i % N_LOOK_DRAWS], q, 1000 + i)
+            layers[i % n_rep].step(looks[i % N_LOOK_DRAWS], q, 1000 + i)
         e3.record()
         torch.cuda.synchronize()
         detail["ms_per_step_no_overlap"] = round(e2.elapsed_time(e3) / args.steps, 4)
@@ -416,7 +457,7 @@ def main():
     sb = score_bytes(wl)
     achieved = sb / (mean_ms["score"] * 1e-3) / 1e9
     ab = attn_bytes(wl)
-    attn_gbs = ab / (alone["attn"][1] * 1e-3) / 1e9
+    attn_gbs = ab / (b2b["attn"] * 1e-3) / 1e9
     traffic = measured_traffic(wl.name)
 
     cpu = None
@@ -442,14 +483,17 @@ def main():
                    "context": wl.ctx_max, "block_size": 16, "budget_tokens": wl.budget,
                    "k_blocks": wl.k_blocks, "fetch_ratio": wl.ratios[0], "cap": cap,
                    "n_look": wl.n_look, "step": "score + select/plan + attn, one layer",
+                   "replicas": n_rep,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "score_blocks",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": sb},
-        "score_us_in_loop": {"median": med_us["score"], "mean": round(mean_ms["score"] * 1e3, 2)},
-        "stages_alone_us_median": {k: round(v[0] * 1e3, 2) for k, v in alone.items()},
-        "attn_roofline": {"achieved": round(attn_gbs, 1), "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+        "score_us_in_loop": dict(percentiles_us(score_ms), mean=round(mean_ms["score"] * 1e3, 2)),
+        "stages_alone_us": {k: percentiles_us(v) for k, v in alone.items()},
+        "stages_back_to_back_us": {k: round(v * 1e3, 2) for k, v in b2b.items()},
+        "attn_roofline": {"kernels": "attn_partial + attn_merge", "timing": "back-to-back mean",
+                          "achieved": round(attn_gbs, 1), "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                           "algorithmic_bytes": ab},
         "detail": detail or None,
         "fetched_blocks_last_step": fetched,

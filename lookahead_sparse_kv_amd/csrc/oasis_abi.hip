@@ -8,6 +8,10 @@
 #include "oasis.h"
 #include "oasis_launch.h"
 
+#ifndef OASIS_HOSTPOOL_FLAGS
+#define OASIS_HOSTPOOL_FLAGS (hipHostMallocMapped | hipHostMallocPortable)
+#endif
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -230,7 +234,7 @@ int oasis_hostpool_create(size_t bytes, void **host_ptr) {
     *host_ptr = nullptr;
     if (bytes == 0) return fail(OASIS_ERR_INVALID, "%s: zero bytes", fn);
     void *p = nullptr;
-    const hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocPortable);
+    const hipError_t e = hipHostMalloc(&p, bytes, OASIS_HOSTPOOL_FLAGS);
     if (e != hipSuccess || !p) {
         (void)hipGetLastError();
         return fail(OASIS_ERR_NOMEM, "%s: hipHostMalloc of %zu bytes failed: %s", fn, bytes,

@@ -25,6 +25,9 @@
 namespace oasis {
 
 constexpr int kAttnWaves = 4;
+#ifndef OASIS_ATTN_CPOL
+#define OASIS_ATTN_CPOL 2        // K/V tile loads: non-temporal (each byte is read once)
+#endif
 #ifndef OASIS_ATTN_TARGET_WAVES
 #define OASIS_ATTN_TARGET_WAVES 1024
 #endif
@@ -58,9 +61,10 @@ template <int D>
 __device__ __forceinline__ void load_block(BlockRegs<D> &r, rsrc_t kr, rsrc_t vr, uint32_t koff,
                                            uint32_t voff) {
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) r.k[kk] = buf_load16(kr, koff, 64 * kk);
+    for (int kk = 0; kk < D / 32; ++kk) r.k[kk] = buf_load16<OASIS_ATTN_CPOL>(kr, koff, 64 * kk);
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) r.v[mt] = buf_load8(vr, voff, 16 * kBlockTokens * 2 * mt);
+    for (int mt = 0; mt < D / 16; ++mt)
+        r.v[mt] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff, 16 * kBlockTokens * 2 * mt, OASIS_ATTN_CPOL);
 }
 
 // Masks of the two bf16 values of tokens (t0, t0 + 1) that are valid (< nt).
@@ -69,40 +73,46 @@ __device__ __forceinline__ uint32_t pair_mask(int t0, int nt) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttnWaves * kWave, 2) void attn_partial_kernel(AttnArgs a) {
-    constexpr int KK = D / 32;
-    constexpr int MT = D / 16;
+struct WaveAcc {
+    float m_run;          // running max of column r16 (log2 units)
+    float l_run;          // this lane's share of the column's running sum
+    f32x4 o[D / 16];      // O^T rows 16*mt + 4*j4 + i of column r16
+};
+
+// B operand of QK^T: query row r16 = (query i, head g*G + hr), dims 32*kk + 8*j4 .. +8.
+template <int D>
+__device__ __forceinline__ void load_query(const AttnArgs &a, int b, int g, bf16x8 (&qv)[D / 32]) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps row indices scalar
-    const int gw = blockIdx.x * kAttnWaves + wave;
-    const int rows = a.batch * a.hkv;
-    const int row = gw / a.splits;
-    if (row >= rows) return;
-    const int split = gw - row * a.splits;
-    const int b = row / a.hkv;
-    const int g = row - b * a.hkv;
     const int r16 = lane & 15;
     const int j4 = lane >> 4;
-    const int e0 = split * a.per_split;
-    int ne = a.n_blk - e0;
-    ne = ne < a.per_split ? ne : a.per_split;
-    const int ctx = a.ctx_len[b];
-    const float NEG_INF = -__builtin_inff();
-
-    // B operand of QK^T: query row r16 = (query i, head g*G + hr), dims 32*kk + 8*j4 .. +8.
-    bf16x8 qv[KK];
-    const bool col_ok = r16 < a.n_rows_q;
-    if (col_ok) {
+    if (r16 < a.n_rows_q) {
         const int iq = r16 / a.group;
         const int hr = r16 - iq * a.group;
         const uint16_t *qp =
             a.q + (((size_t)b * a.n_q + iq) * a.hq + (size_t)g * a.group + hr) * D + 8 * j4;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qv[kk] = as_bf16x8(load_u32x4(qp + 32 * kk));
+        for (int kk = 0; kk < D / 32; ++kk) qv[kk] = as_bf16x8(load_u32x4(qp + 32 * kk));
     } else {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qv[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        for (int kk = 0; kk < D / 32; ++kk) qv[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
     }
+}
+
+// Accumulate list entries [e0, e0 + ne) (ne <= 64) of row (b, g) into acc.
+template <int D>
+__device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int b, int g,
+                                                int e0, int ne, const bf16x8 (&qv)[D / 32],
+                                                WaveAcc<D> &acc) {
+    constexpr int KK = D / 32;
+    constexpr int MT = D / 16;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r16 = lane & 15;
+    const int j4 = lane >> 4;
+    const int ctx = a.ctx_len[b];
+    const float NEG_INF = -__builtin_inff();
+    float &m_run = acc.m_run;
+    float &l_run = acc.l_run;
+    f32x4 (&o)[MT] = acc.o;
 
     // Entry e0 + lane: its page and number of valid tokens (page -1 = skip).
     int my_page = -1, my_ntok = 0;
@@ -128,12 +138,6 @@ __global__ __launch_bounds__(kAttnWaves * kWave, 2) void attn_partial_kernel(Att
         return p >= 0 ? make_rsrc(pool + (size_t)p * page_stride + head_off, kTileBytes)
                       : make_rsrc(pool, 0u);
     };
-
-    float m_run = NEG_INF;      // running max of column r16 (log2 units)
-    float l_run = 0.f;          // this lane's share of the column's running sum
-    f32x4 o[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Entries go in pairs: the pair after the current one is loaded before
     // the current one is computed, so up to four blocks are in flight.
@@ -199,6 +203,82 @@ __global__ __launch_bounds__(kAttnWaves * kWave, 2) void attn_partial_kernel(Att
         cur[1] = nxt[1];
     }
 
+}
+
+// Output element (c, d) of row `row` from the partials of its splits, taken
+// eight splits at a time: the loads of a chunk are unconditional (indices past
+// the last split repeat it, with weight 0), so they are all in flight at once.
+template <int D>
+__device__ __forceinline__ void merge_one(const AttnArgs &a, int row, int c, int d) {
+    constexpr int kChunk = 8;
+    const int b = row / a.hkv;
+    const int g = row - b * a.hkv;
+    const float NEG_INF = -__builtin_inff();
+    const size_t slot0 = (size_t)row * a.splits * a.n_rows_q + c;
+    float M = NEG_INF, L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < a.splits; s0 += kChunk) {
+        float m[kChunk], l[kChunk], o[kChunk];
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const int s = s0 + u < a.splits ? s0 + u : a.splits - 1;
+            const size_t slot = slot0 + (size_t)s * a.n_rows_q;
+            m[u] = a.part_ml[2 * slot];
+            l[u] = a.part_ml[2 * slot + 1];
+            o[u] = a.part_o[slot * D + d];
+        }
+        float mc = NEG_INF;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u)
+            if (s0 + u < a.splits) mc = fmaxf(mc, m[u]);
+        const float Mn = fmaxf(M, mc);
+        if (Mn == NEG_INF) continue;              // no valid token so far
+        const float r = M == NEG_INF ? 0.f : exp2f(M - Mn);
+        L *= r;
+        O *= r;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const float w = (s0 + u < a.splits && m[u] != NEG_INF) ? exp2f(m[u] - Mn) : 0.f;
+            L += w * l[u];
+            O += w * o[u];
+        }
+        M = Mn;
+    }
+    const float res = L > 0.f ? O / L : 0.f;
+    const int iq = c / a.group;
+    const int hr = c - iq * a.group;
+    a.out[(((size_t)b * a.n_q + iq) * a.hq + (size_t)g * a.group + hr) * D + d] =
+        (uint16_t)float_to_bf16_bits(res);
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnWaves * kWave, 2) void attn_partial_kernel(AttnArgs a) {
+    constexpr int MT = D / 16;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps row indices scalar
+    const int gw = blockIdx.x * kAttnWaves + wave;
+    const int rows = a.batch * a.hkv;
+    const int row = gw / a.splits;
+    if (row >= rows) return;
+    const int split = gw - row * a.splits;
+    const int b = row / a.hkv;
+    const int g = row - b * a.hkv;
+    const int r16 = lane & 15;
+    const int j4 = lane >> 4;
+    const int e0 = split * a.per_split;
+    int ne = a.n_blk - e0;
+    ne = ne < a.per_split ? ne : a.per_split;
+    const bool col_ok = r16 < a.n_rows_q;
+    bf16x8 qv[D / 32];
+    load_query<D>(a, b, g, qv);
+    WaveAcc<D> acc;
+    acc.m_run = -__builtin_inff();
+    acc.l_run = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    attn_wave_range<D>(a, row, b, g, e0, ne, qv, acc);
+    float m_run = acc.m_run, l_run = acc.l_run;
+    f32x4 (&o)[MT] = acc.o;
+
     // Column totals of the normaliser live in lanes r16, r16+16, r16+32, r16+48.
     l_run += shfl_xor_f(l_run, 16);
     l_run += shfl_xor_f(l_run, 32);
@@ -219,30 +299,7 @@ template <int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
     const int pair = blockIdx.x;                 // row * n_rows_q + c
     const int row = pair / a.n_rows_q;
-    const int c = pair - row * a.n_rows_q;
-    const int b = row / a.hkv;
-    const int g = row - b * a.hkv;
-    const int d = threadIdx.x;
-    const float NEG_INF = -__builtin_inff();
-    const size_t slot0 = (size_t)row * a.splits * a.n_rows_q + c;
-    const size_t sstride = a.n_rows_q;
-    float M = NEG_INF;
-#pragma unroll 8
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[2 * (slot0 + s * sstride)]);
-    float L = 0.f, O = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < a.splits; ++s) {
-        const size_t slot = slot0 + s * sstride;
-        const float m = a.part_ml[2 * slot];
-        const float w = (m == NEG_INF) ? 0.f : exp2f(m - M);
-        L += w * a.part_ml[2 * slot + 1];
-        O += w * a.part_o[slot * D + d];
-    }
-    const float res = L > 0.f ? O / L : 0.f;
-    const int iq = c / a.group;
-    const int hr = c - iq * a.group;
-    a.out[(((size_t)b * a.n_q + iq) * a.hq + (size_t)g * a.group + hr) * D + d] =
-        (uint16_t)float_to_bf16_bits(res);
+    merge_one<D>(a, row, pair - row * a.n_rows_q, threadIdx.x);
 }
 
 hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_t stream) {

@@ -39,7 +39,7 @@ class DecodeLayer:
         self.fetch_count = torch.empty((B, Hkv), **i32)
         self.out = torch.empty((B, n_q, num_q_heads, D), dtype=torch.bfloat16, device=dev)
         ws = ops.attn_workspace_bytes(self.shape, n_q, k_blocks)
-        self.workspace = torch.empty((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        self.workspace = torch.zeros((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
 
     # individual stages -------------------------------------------------
     def score(self, q_look, stream=None, scores=None):
@@ -93,10 +93,14 @@ class PipelinedDecode:
         pipe.drain()
     """
 
-    def __init__(self, layer: DecodeLayer):
+    def __init__(self, layer: DecodeLayer, side=None):
+        """`side`: the stream the scoring runs on; several pipelines (one per
+        layer) may share one, so that scoring runs layer after layer."""
         self.L = layer
         self.buf = [layer.scores, torch.empty_like(layer.scores)]
-        self.side = torch.cuda.Stream(device=layer.scores.device)       # default priority
+        if side is None:
+            side = torch.cuda.Stream(device=layer.scores.device)          # default priority
+        self.side = side
         self.ev_scored = [torch.cuda.Event(), torch.cuda.Event()]
         self.ev_planned = [torch.cuda.Event(), torch.cuda.Event()]
         self.used = [False, False]
@@ -182,7 +186,7 @@ class HostTierLayer:
         self.fetch_count = torch.zeros((B, Hkv), **i32)
         self.out = torch.empty((B, n_q, num_q_heads, D), dtype=torch.bfloat16, device=dev)
         ws = ops.attn_workspace_bytes(self.ws_shape, n_q, k_blocks)
-        self.workspace = torch.empty((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        self.workspace = torch.zeros((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
 
     def score(self, q_look, stream=None):
         ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len, self.scores,

@@ -251,7 +251,7 @@ def test_sparse_attention_matches_oracle(name):
     lists = _random_lists(rng, wl, n_blk, frac)
     shape = ops.make_shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.table_width,
                            wl.num_pages)
-    ws = torch.empty(ops.attn_workspace_bytes(shape, n_q, n_blk) // 4 + 4, device=DEV)
+    ws = torch.zeros(ops.attn_workspace_bytes(shape, n_q, n_blk) // 4 + 4, device=DEV)
     out = torch.empty((wl.batch, n_q, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device=DEV)
     g_lists = dev(torch.from_numpy(lists))
     ops.sparse_decode_attn(shape, dev(q), dev(d["k_pool"]), dev(d["v_pool"]), dev(d["block_table"]),
@@ -286,7 +286,7 @@ def test_sparse_attention_working_set_mode():
     page_table = torch.arange(wl.batch * K, dtype=torch.int32).view(wl.batch, K)
     shape = ops.make_shape(wl.batch, 8, 2, 128, K, wl.batch * K)
     q = torch.randn((wl.batch, 1, 8, 128), generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
-    ws = torch.empty(ops.attn_workspace_bytes(shape, 1, K) // 4 + 4, device=DEV)
+    ws = torch.zeros(ops.attn_workspace_bytes(shape, 1, K) // 4 + 4, device=DEV)
     out = torch.empty((wl.batch, 1, 8, 128), dtype=torch.bfloat16, device=DEV)
     ops.sparse_decode_attn(shape, dev(q), dev(ws_k), dev(ws_v), dev(page_table), None,
                            dev(torch.from_numpy(slot_block)), dev(d["ctx_len"]), out, ws)
@@ -300,7 +300,7 @@ def test_sparse_attention_large_logits_stay_finite():
     q = (torch.randn((1, 1, 8, 128), generator=torch.Generator().manual_seed(7)) * 12).to(torch.bfloat16)
     lists = np.tile(np.arange(0, 128, 2, dtype=np.int32), (1, 2, 1))
     shape = ops.make_shape(1, 8, 2, 128, wl.table_width, wl.num_pages)
-    ws = torch.empty(ops.attn_workspace_bytes(shape, 1, 64) // 4 + 4, device=DEV)
+    ws = torch.zeros(ops.attn_workspace_bytes(shape, 1, 64) // 4 + 4, device=DEV)
     out = torch.empty((1, 1, 8, 128), dtype=torch.bfloat16, device=DEV)
     g_lists = dev(torch.from_numpy(lists))
     ops.sparse_decode_attn(shape, dev(q), dev(d["k_pool"]), dev(d["v_pool"]), dev(d["block_table"]),
