@@ -264,6 +264,76 @@ int oracle_attn_row(int G, int D, int bs, int ctx, const double *q, const double
 }
 
 /* ------------------------------------------------------------------------ */
+/* ------------------------------------------------------------------------ */
+/* Compressed keys (Figure 7 caption: beside the sparse working set, the GPU
+ * holds the keys compressed by per-block min/max pooling, and the draft query
+ * scans those to predict the next step's top-K blocks).
+ *
+ * Reading of "min/max pooling": per block and per dimension d, the smallest
+ * and the largest k[t][d] over the block's valid tokens t < ctx.
+ *
+ * ck: [W][2][D]; ck[n][0][d] = min, ck[n][1][d] = max for n < nb.  Blocks
+ * n >= nb are not written.                                                  */
+int oracle_pool_keys_row(int ctx, int D, int bs, const double *k, int W, double *ck)
+{
+    if (ctx < 0 || D <= 0 || bs <= 0 || W < 0) return ORC_EINVAL;
+    int nb = (ctx + bs - 1) / bs;
+    if (nb > W) return ORC_EINVAL;
+    for (int n = 0; n < nb; ++n) {
+        int t_end = (n + 1) * bs < ctx ? (n + 1) * bs : ctx;
+        double *mn = ck + (size_t)n * 2 * D;
+        double *mx = mn + D;
+        for (int d = 0; d < D; ++d) {
+            double lo = k[(size_t)(n * bs) * D + d], hi = lo;
+            for (int t = n * bs + 1; t < t_end; ++t) {
+                double x = k[(size_t)t * D + d];
+                if (x < lo) lo = x;
+                if (x > hi) hi = x;
+            }
+            mn[d] = lo;
+            mx[d] = hi;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Block score from the compressed keys (Figure 7 caption).  The pages name
+ * the pooling but not the score; the reading taken here is the largest value
+ * q.x / sqrt(D) can reach for a key x inside the block's box
+ * min <= x <= max: per dimension the larger of q_d * min_d and q_d * max_d,
+ * summed over d.  Every valid token of the block lies in the box, so this is
+ * an upper bound of the exact block score, equal to it when the block has
+ * one token.  Maximised over the lookahead rows j < n_q, as the exact score.
+ *
+ * q: [n_q][D]; ck: [W][2][D] as written by oracle_pool_keys_row.
+ * scores[n] = -inf for nb <= n < W.                                         */
+int oracle_score_minmax_row(int ctx, int D, int bs, int n_q, const double *q,
+                            const double *ck, int W, double *scores)
+{
+    if (ctx < 0 || D <= 0 || bs <= 0 || n_q <= 0 || W < 0) return ORC_EINVAL;
+    int nb = (ctx + bs - 1) / bs;
+    if (nb > W) return ORC_EINVAL;
+    double inv_sqrt_d = 1.0 / sqrt((double)D);
+    for (int n = 0; n < W; ++n) {
+        if (n >= nb) { scores[n] = -INFINITY; continue; }
+        const double *mn = ck + (size_t)n * 2 * D;
+        const double *mx = mn + D;
+        double best = -INFINITY;
+        for (int j = 0; j < n_q; ++j) {
+            double sum = 0.0;
+            for (int d = 0; d < D; ++d) {
+                double a = q[(size_t)j * D + d] * mn[d];
+                double b = q[(size_t)j * D + d] * mx[d];
+                sum += a > b ? a : b;
+            }
+            double bound = sum * inv_sqrt_d;
+            if (bound > best) best = bound;
+        }
+        scores[n] = best;
+    }
+    return ORC_OK;
+}
+
 /* Whole-batch drivers: the same per-row functions over every (sequence, KV
  * head) row, rows in parallel with OpenMP (rows are independent).
  *
@@ -301,6 +371,53 @@ int oracle_score(int B, int Hq, int Hkv, int D, int bs, int ctx_max, int W,
             e = oracle_score_row(ctx_len[b], D, bs, n_look * G, qg,
                                  K + ((size_t)b * Hkv + g) * ctx_max * D, W,
                                  scores + ((size_t)b * Hkv + g) * W);
+            free(qg);
+        }
+        if (e) {
+#pragma omp atomic write
+            err = e;
+        }
+    }
+    return err;
+}
+
+/* Compressed keys of every row: K [B][Hkv][ctx_max][D] -> ck [B][Hkv][W][2][D]. */
+int oracle_pool_keys(int B, int Hkv, int D, int bs, int ctx_max, int W, const int *ctx_len,
+                     const double *K, double *ck)
+{
+    if (B < 0 || Hkv <= 0) return ORC_EINVAL;
+    int rows = B * Hkv, err = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < rows; ++r) {
+        int b = r / Hkv;
+        int e = ctx_len[b] > ctx_max ? ORC_EINVAL
+              : oracle_pool_keys_row(ctx_len[b], D, bs, K + (size_t)r * ctx_max * D, W,
+                                     ck + (size_t)r * W * 2 * D);
+        if (e) {
+#pragma omp atomic write
+            err = e;
+        }
+    }
+    return err;
+}
+
+/* Compressed-key scores of every row: q_look [B][n_look][Hq][D],
+ * ck [B][Hkv][W][2][D] -> scores [B][Hkv][W]. */
+int oracle_score_minmax(int B, int Hq, int Hkv, int D, int bs, int W, const int *ctx_len,
+                        int n_look, const double *q_look, const double *ck, double *scores)
+{
+    if (B < 0 || Hkv <= 0 || Hq % Hkv) return ORC_EINVAL;
+    int G = Hq / Hkv;
+    int rows = B * Hkv, err = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < rows; ++r) {
+        int b = r / Hkv, g = r % Hkv;
+        double *qg = (double *)malloc(sizeof(double) * (size_t)n_look * G * D);
+        int e = ORC_ENOMEM;
+        if (qg) {
+            gather_group_queries(q_look, n_look, Hq, D, b, g, G, qg);
+            e = oracle_score_minmax_row(ctx_len[b], D, bs, n_look * G, qg,
+                                        ck + (size_t)r * W * 2 * D, W, scores + (size_t)r * W);
             free(qg);
         }
         if (e) {

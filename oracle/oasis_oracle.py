@@ -8,7 +8,9 @@ Functions mirror the C entry points (see the C file for the passage each one
 follows and the readings it takes where the pages are silent):
 
     score_row / select_row / plan_row / attn_row     -- one (sequence, KV head) row
+    pool_keys_row / score_minmax_row                 -- compressed keys of one row
     score / select / plan / attn / decode_step       -- every row of a batch
+    pool_keys / score_minmax                         -- compressed keys, every row
 """
 import ctypes
 import os
@@ -42,9 +44,15 @@ def _load():
         lib.oracle_decode_step.argtypes = [i, i, i, i, i, i, i, p_i, i, p_d, p_d, p_d, p_d,
                                            i, i, i, p_d, p_i, p_i, p_i, p_i, p_i, p_i, p_d]
         lib.oracle_max_threads.argtypes = []
+        lib.oracle_pool_keys_row.argtypes = [i, i, i, p_d, i, p_d]
+        lib.oracle_score_minmax_row.argtypes = [i, i, i, i, p_d, p_d, i, p_d]
+        lib.oracle_pool_keys.argtypes = [i, i, i, i, i, i, p_i, p_d, p_d]
+        lib.oracle_score_minmax.argtypes = [i, i, i, i, i, i, p_i, i, p_d, p_d, p_d]
         for name in ("oracle_score_row", "oracle_select_row", "oracle_plan_row",
                      "oracle_attn_row", "oracle_score", "oracle_select", "oracle_plan",
-                     "oracle_attn", "oracle_decode_step", "oracle_max_threads"):
+                     "oracle_attn", "oracle_decode_step", "oracle_max_threads",
+                     "oracle_pool_keys_row", "oracle_score_minmax_row", "oracle_pool_keys",
+                     "oracle_score_minmax"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -124,6 +132,28 @@ def attn_row(q_heads, k, v, ctx, bs, blocks):
     return out
 
 
+def pool_keys_row(k, ctx, bs, W):
+    """k [>=ctx][D] -> ck [W][2][D] (min, max per block and dim; blocks >= nb zero)."""
+    k = _f64(k)
+    D = k.shape[1]
+    assert k.shape[0] >= ctx
+    ck = np.zeros((W, 2, D), dtype=np.float64)
+    _check(_load().oracle_pool_keys_row(ctx, D, bs, _pd(k), W, _pd(ck)), "pool_keys_row")
+    return ck
+
+
+def score_minmax_row(q_rows, ck, ctx, bs):
+    """q_rows [n_q][D]; ck [W][2][D] -> bound scores [W]."""
+    q_rows, ck = _f64(q_rows), _f64(ck)
+    n_q, D = q_rows.shape
+    W = ck.shape[0]
+    assert ck.shape == (W, 2, D)
+    out = np.empty(W, dtype=np.float64)
+    _check(_load().oracle_score_minmax_row(ctx, D, bs, n_q, _pd(q_rows), _pd(ck), W, _pd(out)),
+           "score_minmax_row")
+    return out
+
+
 # ---------------------------------------------------------------- whole batch
 def score(q_look, K, ctx_len, bs, W):
     """q_look [B][n_look][Hq][D]; K [B][Hkv][ctx_max][D] -> scores [B][Hkv][W]."""
@@ -193,3 +223,24 @@ def decode_step(q_look, q, K, V, ctx_len, bs, W, K_blocks, cap, step, slot_block
                                       _pi(fs_c), _pi(cnt), _pd(out)), "decode_step")
     return dict(scores=scores, sel=sel, fetch_block=fb_c[:, :, :cap], fetch_slot=fs_c[:, :, :cap],
                 fetch_count=cnt, slot_block=sb, last_use=lu, out=out)
+
+
+def pool_keys(K, ctx_len, bs, W):
+    """K [B][Hkv][ctx_max][D] -> ck [B][Hkv][W][2][D] (blocks past the context zero)."""
+    K, ctx_len = _f64(K), _i32(ctx_len)
+    B, Hkv, ctx_max, D = K.shape
+    ck = np.zeros((B, Hkv, W, 2, D), dtype=np.float64)
+    _check(_load().oracle_pool_keys(B, Hkv, D, bs, ctx_max, W, _pi(ctx_len), _pd(K), _pd(ck)),
+           "pool_keys")
+    return ck
+
+
+def score_minmax(q_look, ck, ctx_len, bs):
+    """q_look [B][n_look][Hq][D]; ck [B][Hkv][W][2][D] -> scores [B][Hkv][W]."""
+    q_look, ck, ctx_len = _f64(q_look), _f64(ck), _i32(ctx_len)
+    B, n_look, Hq, D = q_look.shape
+    _, Hkv, W, _, _ = ck.shape
+    out = np.empty((B, Hkv, W), dtype=np.float64)
+    _check(_load().oracle_score_minmax(B, Hq, Hkv, D, bs, W, _pi(ctx_len), n_look, _pd(q_look),
+                                       _pd(ck), _pd(out)), "score_minmax")
+    return out
