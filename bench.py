@@ -35,7 +35,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 N_LOOK_DRAWS = 4               # distinct lookahead draws cycled through the steps
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_blocks_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "lookahead_sparse_kv_amd", "csrc", "score_blocks.hip")
 
 
@@ -60,10 +59,16 @@ def parse():
 
 
 def score_bytes(wl):
-    keys = sum(c for c in wl.ctx) * wl.num_kv_heads * wl.head_dim * 2
+    """Algorithmic bytes of one scoring launch: every valid key (exact) or
+    every valid block's min and max rows (compressed), the lookahead queries,
+    the block table (exact only), the scores and the context lengths."""
     q = wl.batch * wl.n_look * wl.num_q_heads * wl.head_dim * 2
-    table = wl.batch * wl.table_width * 4
     out = wl.batch * wl.num_kv_heads * wl.table_width * 4
+    if wl.scorer == "minmax":
+        blocks = sum((c + 15) // 16 for c in wl.ctx)
+        return blocks * wl.num_kv_heads * 2 * wl.head_dim * 2 + q + out + wl.batch * 4
+    keys = sum(c for c in wl.ctx) * wl.num_kv_heads * wl.head_dim * 2
+    table = wl.batch * wl.table_width * 4
     return keys + q + table + out + wl.batch * 4
 
 
@@ -80,23 +85,30 @@ def select_bytes(wl):
     return wl.batch * wl.num_kv_heads * (wl.table_width * 4 + wl.k_blocks * 4)
 
 
-def kernel_hash():
+# scorer -> (kernel, committed PMC summary, sources the summary's hash covers)
+SCORE_KERNELS = {
+    "exact": ("score_blocks", "score_blocks_traffic.json", ("score_blocks.hip", "oasis_device.h")),
+    "minmax": ("score_minmax", "score_minmax_traffic.json", ("score_minmax.hip", "oasis_device.h")),
+}
+
+
+def kernel_hash(scorer="exact"):
     h = hashlib.sha256()
-    for name in ("score_blocks.hip", "oasis_device.h"):
+    for name in SCORE_KERNELS[scorer][2]:
         with open(os.path.join(ROOT, "lookahead_sparse_kv_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(wl_name):
+def measured_traffic(wl_name, scorer="exact"):
     """HBM bytes per scoring launch from the committed PMC summary, if it was
     taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", SCORE_KERNELS[scorer][1])) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_hash() or t.get("workload") != wl_name:
+    if t.get("kernel_hash") != kernel_hash(scorer) or t.get("workload") != wl_name:
         return None
     return t.get("bytes_per_launch")
 
@@ -129,16 +141,35 @@ def cpu_baseline(wl, d, n_seqs, cap):
     sb, lu = wlm.empty_state(wl)
     sb, lu = sb[:n].numpy(), lu[:n].numpy()
     prev = wlm.draw_lookahead(wl, d["q32"], wl.seed + 1).to(torch.bfloat16)[:n]
-    seed_run = orc.decode_step(prev, q, K, V, ctx, 16, wl.table_width, wl.k_blocks, wl.k_blocks,
-                               -1, sb, lu)
-    t0 = time.perf_counter()
-    orc.decode_step(q_look, q, K, V, ctx, 16, wl.table_width, wl.k_blocks, cap, 0,
-                    seed_run["slot_block"], seed_run["last_use"])
-    dt = time.perf_counter() - t0
+    if wl.scorer == "minmax":
+        # the compressed keys are built once (prefill work, untimed); a step is
+        # compressed scoring, select, plan and attention, each over every row
+        ck = orc.pool_keys(K, ctx, 16, wl.table_width)
+
+        def step(ql, cap_, t, sb_, lu_):
+            sc = orc.score_minmax(ql, ck, ctx, 16)
+            sel = orc.select(sc, ctx, 16, wl.k_blocks)
+            _, _, _, sb2, lu2 = orc.plan(sel, sc, sb_, lu_, cap_, t)
+            orc.attn(q, K, V, ctx, 16, sb2)
+            return sb2, lu2
+
+        sb, lu = step(prev, wl.k_blocks, -1, sb, lu)
+        t0 = time.perf_counter()
+        step(q_look, cap, 0, sb, lu)
+        dt = time.perf_counter() - t0
+        what = "compressed-key score+select+plan+attention step"
+    else:
+        seed_run = orc.decode_step(prev, q, K, V, ctx, 16, wl.table_width, wl.k_blocks,
+                                   wl.k_blocks, -1, sb, lu)
+        t0 = time.perf_counter()
+        orc.decode_step(q_look, q, K, V, ctx, 16, wl.table_width, wl.k_blocks, cap, 0,
+                        seed_run["slot_block"], seed_run["last_use"])
+        dt = time.perf_counter() - t0
+        what = "score+select+plan+attention step"
     return {"value": n / dt, "unit": "seq-decode-steps/s", "cores": orc.max_threads(),
             "kind": "oracle",
             "sample": f"{n} of {wl.batch} sequences x {wl.num_kv_heads} KV heads, one full "
-                      f"score+select+plan+attention step in fp64 ({dt:.2f} s)"}
+                      f"{what} in fp64 ({dt:.2f} s)"}
 
 
 def _ev():
@@ -368,7 +399,7 @@ def main():
         vp = g["v_pool"] if r == 0 else g["v_pool"].clone()
         L = DecodeLayer(k_pool=kp, v_pool=vp, block_table=g["block_table"], ctx_len=g["ctx_len"],
                         num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks, cap=wl.k_blocks,
-                        n_look=wl.n_look)
+                        n_look=wl.n_look, scorer=wl.scorer)
         L.score(prev)                      # previous step: fill the working set
         L.select()
         L.plan(-1)
@@ -386,9 +417,12 @@ def main():
     pipes = [PipelinedDecode(L, side=side) for L in layers]
     for P in pipes:
         P.prime(looks[0], 0)
+    # compressed scorer: each step also refreshes the compressed keys of the
+    # block a decode step appends to (the pool itself is not written here)
+    append = wl.scorer == "minmax"
     for i in range(args.warmup):
         pipes[i % n_rep].step(q, looks[(i // n_rep + 1) % N_LOOK_DRAWS], 1 + i // n_rep,
-                              copy_out=False)
+                              copy_out=False, append=append)
     for P in pipes:
         P.drain()
     torch.cuda.synchronize()
@@ -399,7 +433,7 @@ def main():
     for i in range(args.steps):
         s = args.warmup + i
         pipes[s % n_rep].step(q, looks[(s // n_rep + 1) % N_LOOK_DRAWS], 1 + s // n_rep,
-                              copy_out=False, score_events=ev[i])
+                              copy_out=False, score_events=ev[i], append=append)
     for P in pipes:
         P.drain()
     ev1.record()
@@ -430,9 +464,12 @@ def main():
     # each stage back to back (events around the whole loop, replicas in
     # turn): the per-call cost without an event and a launch gap per call
     b2b = {}
-    for k, fn in (("score", lambda i, L: L.score(looks[i % N_LOOK_DRAWS])),
-                  ("select_plan", lambda i, L: L.select_plan(3000 + i)),
-                  ("attn", lambda i, L: L.attend(q))):
+    stages = [("score", lambda i, L: L.score(looks[i % N_LOOK_DRAWS])),
+              ("select_plan", lambda i, L: L.select_plan(3000 + i)),
+              ("attn", lambda i, L: L.attend(q))]
+    if append:
+        stages.append(("append", lambda i, L: L.append()))
+    for k, fn in stages:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(args.steps):
@@ -447,6 +484,8 @@ def main():
         e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e2.record()
         for i in range(args.steps):
+            if append:
+                layers[i % n_rep].append()
             layers[i % n_rep].step(looks[i % N_LOOK_DRAWS], q, 1000 + i)
         e3.record()
         torch.cuda.synchronize()
@@ -458,15 +497,19 @@ def main():
     achieved = sb / (mean_ms["score"] * 1e-3) / 1e9
     ab = attn_bytes(wl)
     attn_gbs = ab / (b2b["attn"] * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name, wl.scorer)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, d, args.cpu_sample_seqs, cap)
 
     value = wl.batch / (ms_per_step * 1e-3)
+    metric = ("seq-decode-steps/s, score+select+sparse attn, Qwen3-8B shape 32K; % HBM peak"
+              if wl.scorer == "exact" else
+              "seq-decode-steps/s, min/max compressed-key score+select+sparse attn, "
+              "Qwen3-8B shape 32K; % HBM peak")
     line = {
-        "metric": "seq-decode-steps/s, score+select+sparse attn, Qwen3-8B shape 32K; % HBM peak",
+        "metric": metric,
         "value": round(value, 1),
         "unit": "seq-decode-steps/s",
         "n_gpus": 1,
@@ -482,10 +525,11 @@ def main():
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "context": wl.ctx_max, "block_size": 16, "budget_tokens": wl.budget,
                    "k_blocks": wl.k_blocks, "fetch_ratio": wl.ratios[0], "cap": cap,
-                   "n_look": wl.n_look, "step": "score + select/plan + attn, one layer",
+                   "n_look": wl.n_look, "scorer": wl.scorer,
+                   "step": "score + select/plan + attn, one layer",
                    "replicas": n_rep,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "score_blocks",
+        "roofline": {"bound": "hbm", "kernel": SCORE_KERNELS[wl.scorer][0],
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": sb},

@@ -14,6 +14,9 @@
  *                            updates the per-head working-set table
  *   oasis_sparse_decode_attn split-K decode attention over the working set
  *
+ * and, for the pages' own compressed-key scorer, oasis_pool_keys (min/max
+ * pooling of the keys) and oasis_score_blocks_minmax (scores from them).
+ *
  * Conventions shared by every call
  * --------------------------------
  *  - Pointers are DEVICE pointers unless a comment says otherwise.  Every
@@ -40,6 +43,7 @@
  *  - block table        [B][table_width]  int32, logical block -> page
  *  - context lengths    ctx_len [B]       int32, tokens
  *  - scores             [B][Hkv][table_width]  fp32
+ *  - compressed keys    ck      [B][Hkv][table_width][2][D]  bf16 (min, max)
  *  - selection          sel     [B][Hkv][K]     int32, ascending, -1 padded
  *  - working-set table  slot_block, last_use [B][Hkv][K] int32
  *  - fetch list         fetch_block, fetch_slot [B][Hkv][cap] int32, -1 padded;
@@ -91,6 +95,48 @@ typedef struct oasis_shape {
 int oasis_score_blocks(const oasis_shape *s, const uint16_t *q_look, int32_t n_look,
                        const uint16_t *k_pool, const int32_t *block_table,
                        const int32_t *ctx_len, float scale, float *scores, void *stream);
+
+/*
+ * Compressed keys by per-block min/max pooling.  Figure 7 caption: beside the
+ * sparse KV working set the GPU keeps the keys compressed by per-block min/max
+ * pooling, for the draft query to scan.
+ *
+ *   ck[b][g][n][0][d] = min, ck[b][g][n][1][d] = max of k_t[d] over the tokens
+ *   t of block n with 16n + t < ctx_len[b]          (ck: [B][Hkv][W][2][D] bf16)
+ *
+ * last_only = 0 writes every block n < ceil(ctx_len[b] / bs); last_only = 1
+ * only block ceil(ctx_len[b] / bs) - 1 of each sequence (the one a decode step
+ * appends its token to; it is recomputed from the pool, so the call may be
+ * repeated).  Blocks at or past the context are not written.  A page id
+ * outside [0, num_pages) is not read: that block is written as an empty box
+ * (min = +inf, max = -inf), which oasis_score_blocks_minmax scores -inf.  The
+ * values are bf16 keys themselves, so the pooling is exact.
+ * Requires D in {64, 128}, bs = 16, k_pool and ck 16-byte aligned;
+ * last_only must be 0 or 1.
+ */
+int oasis_pool_keys(const oasis_shape *s, const uint16_t *k_pool, const int32_t *block_table,
+                    const int32_t *ctx_len, int32_t last_only, uint16_t *ck, void *stream);
+
+/*
+ * Lookahead block scoring from the compressed keys (Figure 7 caption: the
+ * draft query scans the compressed keys to predict the next step's top-K
+ * blocks).  The pages name the pooling, not the score; this library takes the
+ * largest value q . x can reach inside the block's box min <= x <= max:
+ *
+ *   scores[b][g][n] = max over drafts j < n_look and query heads h of KV head g
+ *                     of scale * sum_d max(q_d * min_d, q_d * max_d),
+ *                     q = q_look[b][j][h], (min, max) = ck[b][g][n]
+ *   scores[b][g][n] = -inf for n >= ceil(ctx_len[b] / bs) and for empty boxes.
+ *
+ * An upper bound of oasis_score_blocks' exact score, equal to it for a block
+ * of one token; it reads 2D values per block instead of 16D.  bf16 inputs,
+ * fp32 accumulation.  Requires D in {64, 128}, bs = 16, 1 <= n_look,
+ * n_look * G <= 16, scale > 0, ck 16-byte aligned.  The output feeds
+ * oasis_select_topk / oasis_select_plan unchanged.
+ */
+int oasis_score_blocks_minmax(const oasis_shape *s, const uint16_t *q_look, int32_t n_look,
+                              const uint16_t *ck, const int32_t *ctx_len, float scale,
+                              float *scores, void *stream);
 
 /*
  * Per-KV-head top-K.  Figure 7 caption ("top-K blocks"); abstract (a

@@ -96,6 +96,44 @@ int oasis_score_blocks(const oasis_shape *s, const uint16_t *q_look, int32_t n_l
     return check_hip(oasis::launch_score_blocks(a, s->head_dim, as_stream(stream)), fn);
 }
 
+int oasis_pool_keys(const oasis_shape *s, const uint16_t *k_pool, const int32_t *block_table,
+                    const int32_t *ctx_len, int32_t last_only, uint16_t *ck, void *stream) {
+    const char *fn = "oasis_pool_keys";
+    if (int e = check_shape(s, fn)) return e;
+    if (last_only != 0 && last_only != 1)
+        return fail(OASIS_ERR_INVALID, "%s: last_only must be 0 or 1, got %d", fn, last_only);
+    if (s->batch == 0 || s->table_width == 0) return ok();
+    if (!k_pool || !block_table || !ctx_len || !ck)
+        return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    if (reinterpret_cast<uintptr_t>(ck) % 16 || reinterpret_cast<uintptr_t>(k_pool) % 16)
+        return fail(OASIS_ERR_INVALID, "%s: k_pool and ck must be 16-byte aligned", fn);
+    oasis::PoolArgs a{k_pool, block_table, ctx_len, ck, s->batch, s->num_kv_heads, s->table_width,
+                      s->num_pages, last_only};
+    return check_hip(oasis::launch_pool_keys(a, s->head_dim, as_stream(stream)), fn);
+}
+
+int oasis_score_blocks_minmax(const oasis_shape *s, const uint16_t *q_look, int32_t n_look,
+                              const uint16_t *ck, const int32_t *ctx_len, float scale,
+                              float *scores, void *stream) {
+    const char *fn = "oasis_score_blocks_minmax";
+    if (int e = check_shape(s, fn)) return e;
+    if (n_look < 1) return fail(OASIS_ERR_INVALID, "%s: n_look %d < 1", fn, n_look);
+    const int G = s->num_q_heads / s->num_kv_heads;
+    if ((long long)n_look * G > oasis::kMaxRowsQ)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: n_look * group = %lld above %d", fn,
+                    (long long)n_look * G, oasis::kMaxRowsQ);
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(OASIS_ERR_INVALID, "%s: scale must be finite and > 0", fn);
+    if (s->batch == 0 || s->table_width == 0) return ok();
+    if (!q_look || !ck || !ctx_len || !scores)
+        return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    if (reinterpret_cast<uintptr_t>(ck) % 16)
+        return fail(OASIS_ERR_INVALID, "%s: ck must be 16-byte aligned", fn);
+    oasis::MinmaxArgs a{q_look, ck, ctx_len, scores, scale, s->batch, s->num_q_heads,
+                        s->num_kv_heads, G, s->table_width, n_look, n_look * G};
+    return check_hip(oasis::launch_score_minmax(a, s->head_dim, as_stream(stream)), fn);
+}
+
 int oasis_select_topk(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
                       int32_t k_blocks, int32_t *sel, void *stream) {
     const char *fn = "oasis_select_topk";

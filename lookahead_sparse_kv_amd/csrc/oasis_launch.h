@@ -65,7 +65,29 @@ struct AttnArgs {
     int batch, hq, hkv, group, width, num_pages, n_q, n_rows_q, n_blk, splits, per_split;
 };
 
+// Min/max pooling of the paged keys into ck [B][Hkv][W][2][D] (all blocks, or
+// only the last block of each sequence).
+struct PoolArgs {
+    const uint16_t *k_pool;
+    const int32_t *block_table;
+    const int32_t *ctx_len;
+    uint16_t *ck;
+    int batch, hkv, width, num_pages, last_only;
+};
+
+// Block scores from the compressed keys.
+struct MinmaxArgs {
+    const uint16_t *q_look;
+    const uint16_t *ck;
+    const int32_t *ctx_len;
+    float *scores;
+    float scale;
+    int batch, hq, hkv, group, width, n_look, n_rows_q;
+};
+
 hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t stream);
+hipError_t launch_pool_keys(const PoolArgs &a, int head_dim, hipStream_t stream);
+hipError_t launch_score_minmax(const MinmaxArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_select_topk(const SelectArgs &a, hipStream_t stream);
 // One 256-thread workgroup per row; mode 1 = select, 2 = plan, 3 = select then plan.
 bool row_select_plan_fits(int width, int k, int mode);

@@ -1,0 +1,135 @@
+// score_minmax.hip -- lookahead block scores from the min/max-pooled keys.
+//
+// OasisKV (metalmedia.ai summary), Figure 7 caption: the draft query scans the
+// compressed keys (per-block min/max pooling) to predict the next step's top-K
+// blocks.  The score of block n for one lookahead row q is the largest value
+// q . x can reach for x in the block's box min <= x <= max:
+//   sum_d max(q_d * min_d, q_d * max_d) = q- . min + q+ . max,
+// where q+ keeps the non-negative and q- the negative components of q.  It is
+// maximised over the KV head's lookahead rows and scaled, as the exact score.
+//
+// Design (gfx950): the right-hand form is one dot product of length 2D, so a
+// 16 x 16 MFMA tile covers 16 lookahead rows (A = [q- | q+], bf16, split by
+// sign bit once per wave) against 16 blocks (B = the compressed rows
+// [min | max], 512 contiguous bytes per block at D = 128); D/16
+// v_mfma_f32_16x16x32_bf16 per tile.  A wave takes 64 consecutive blocks of
+// one row, issues all their loads (raw buffer loads bounded to the row's valid
+// blocks, non-temporal: each compressed key is read once per step), then
+// reduces each tile's columns over the lookahead rows with two lane exchanges.
+// A block written as an empty box (min > max, for a page outside the pool)
+// scores -inf.  The bytes are 1/8 of the exact scorer's at bs = 16.
+#include "oasis_device.h"
+#include "oasis_launch.h"
+
+#ifndef OASIS_MINMAX_CPOL
+#define OASIS_MINMAX_CPOL 2      // non-temporal: each compressed key is read once per step
+#endif
+
+namespace oasis {
+
+constexpr int kMmWaves = 4;
+constexpr int kMmTiles = 4;            // 16-block tiles per wave
+constexpr int kMmBlocksPerWave = kMmTiles * kBlockTokens;
+
+template <int D>
+__global__ __launch_bounds__(kMmWaves * kWave) void score_minmax_kernel(MinmaxArgs a) {
+    constexpr int QK = D / 32;         // 32-wide k-steps of one half (q- or q+)
+    constexpr int KK = 2 * QK;         // k-steps of a tile
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int r16 = lane & 15;
+    const int j4 = lane >> 4;
+    const long long gw = (long long)blockIdx.x * kMmWaves + wave;
+    const int chunks = (a.width + kMmBlocksPerWave - 1) / kMmBlocksPerWave;
+    const int rows = a.batch * a.hkv;
+    const int row = (int)(gw / chunks);
+    if (row >= rows) return;
+    const int n0 = (int)(gw - (long long)row * chunks) * kMmBlocksPerWave;
+    const int b = row / a.hkv;
+    const int g = row - b * a.hkv;
+    long long ctx = a.ctx_len[b];
+    const long long cmax = (long long)a.width * kBlockTokens;
+    ctx = ctx < 0 ? 0 : (ctx > cmax ? cmax : ctx);
+    const int nb = (int)((ctx + kBlockTokens - 1) / kBlockTokens);
+
+    // Compressed rows of blocks n0 .. n0 + 63; the resource ends at the last
+    // valid block, so loads past it return zeros without touching memory.
+    constexpr uint32_t kRowBytes = 2 * D * 2;
+    const int valid_here = nb - n0 > 0 ? nb - n0 : 0;
+    const uint16_t *base = a.ck + ((size_t)row * a.width + n0) * 2 * D;
+    const rsrc_t r = make_rsrc(base, (uint32_t)(valid_here < kMmBlocksPerWave ? valid_here
+                                                                                : kMmBlocksPerWave) * kRowBytes);
+    // The block index sits in the per-lane offset, so the range check cuts at
+    // whole blocks; the k-step offset (< 512 B) stays inside the block's row.
+    u32x4 kb[kMmTiles][KK];
+#pragma unroll
+    for (int t = 0; t < kMmTiles; ++t) {
+        const uint32_t boff = (uint32_t)((t * kBlockTokens + r16) * 2 * D + 8 * j4) * 2;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kb[t][kk] = buf_load16<OASIS_MINMAX_CPOL>(r, boff, 64 * kk);
+    }
+
+    // A operand: lookahead row r16 (draft r16 / G, head g*G + r16 % G), dims
+    // 32*kk + 8*j4 .. +8, split by sign: k-steps 0 .. QK-1 carry q-, the rest q+.
+    bf16x8 qa[KK];
+    if (r16 < a.n_rows_q) {
+        const int jd = r16 / a.group;
+        const int hr = r16 - jd * a.group;
+        const uint16_t *qp = a.q_look +
+            (((size_t)b * a.n_look + jd) * a.hq + (size_t)g * a.group + hr) * D + 8 * j4;
+#pragma unroll
+        for (int kk = 0; kk < QK; ++kk) {
+            const u32x4 w = load_u32x4(qp + 32 * kk);
+            u32x4 neg, pos;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t m = ((w[e] & 0x80008000u) >> 15) * 0xffffu;   // sign of each half
+                neg[e] = w[e] & m;
+                pos[e] = w[e] & ~m;
+            }
+            qa[kk] = as_bf16x8(neg);
+            qa[QK + kk] = as_bf16x8(pos);
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qa[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
+
+    const float NEG_INF = -__builtin_inff();
+    float *out = a.scores + (size_t)row * a.width;
+#pragma unroll
+    for (int t = 0; t < kMmTiles; ++t) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s = mfma16x16x32(qa[kk], as_bf16x8(kb[t][kk]), s);
+        // s[i] = bound of lookahead row 4*j4 + i on block r16 of the tile
+        float m = NEG_INF;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = (4 * j4 + i < a.n_rows_q) ? fmaxf(m, s[i]) : m;
+        m = fmaxf(m, shfl_xor_f(m, 16));
+        m = fmaxf(m, shfl_xor_f(m, 32));
+        const int n = n0 + t * kBlockTokens + r16;
+        if (j4 == 0 && n < a.width) {
+            // lanes j4 = 0 hold min[0..7] (k-step 0) and max[0..7] (k-step QK) of block r16
+            const float mn0 = bf16_bits_to_float(kb[t][0][0] & 0xffffu);
+            const float mx0 = bf16_bits_to_float(kb[t][QK][0] & 0xffffu);
+            out[n] = (n < nb && !(mn0 > mx0)) ? m * a.scale : NEG_INF;
+        }
+    }
+}
+
+hipError_t launch_score_minmax(const MinmaxArgs &a, int head_dim, hipStream_t stream) {
+    const long long rows = (long long)a.batch * a.hkv;
+    const long long chunks = (a.width + kMmBlocksPerWave - 1) / kMmBlocksPerWave;
+    const long long waves = rows * chunks;
+    if (waves == 0) return hipSuccess;
+    const dim3 grid((unsigned)((waves + kMmWaves - 1) / kMmWaves));
+    const dim3 block(kMmWaves * kWave);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(score_minmax_kernel<128>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(score_minmax_kernel<64>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace oasis

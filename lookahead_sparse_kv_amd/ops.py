@@ -21,7 +21,7 @@ BLOCK_SIZE = 16
 OASIS_OK, OASIS_ERR_INVALID, OASIS_ERR_UNSUPPORTED, OASIS_ERR_NOMEM, OASIS_ERR_HIP = range(5)
 
 # Every symbol include/oasis.h declares.
-EXPORTS = ("oasis_score_blocks", "oasis_select_topk", "oasis_plan_fetch", "oasis_select_plan",
+EXPORTS = ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax", "oasis_select_topk", "oasis_plan_fetch", "oasis_select_plan",
            "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_hostpool_create",
            "oasis_hostpool_device_pointer", "oasis_hostpool_destroy", "oasis_fetch_blocks",
            "oasis_status_string", "oasis_last_error", "oasis_version")
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         S = ctypes.POINTER(OasisShape)
         L.oasis_score_blocks.argtypes = [S, p, i32, p, p, p, f32, p, p]
         L.oasis_select_topk.argtypes = [S, p, p, i32, p, p]
+        L.oasis_pool_keys.argtypes = [S, p, p, p, i32, p, p]
+        L.oasis_score_blocks_minmax.argtypes = [S, p, i32, p, p, f32, p, p]
         L.oasis_plan_fetch.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p]
         L.oasis_select_plan.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p, p]
         L.oasis_attn_workspace_bytes.argtypes = [S, i32, i32]
@@ -64,7 +66,8 @@ def lib() -> ctypes.CDLL:
         L.oasis_hostpool_device_pointer.argtypes = [p, ctypes.POINTER(ctypes.c_void_p)]
         L.oasis_hostpool_destroy.argtypes = [p]
         L.oasis_fetch_blocks.argtypes = [S, p, p, i32, p, p, p, i32, p, p, p, p]
-        for fn in ("oasis_score_blocks", "oasis_select_topk", "oasis_plan_fetch",
+        for fn in ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax",
+                   "oasis_select_topk", "oasis_plan_fetch",
                    "oasis_select_plan", "oasis_sparse_decode_attn", "oasis_hostpool_create",
                    "oasis_hostpool_device_pointer", "oasis_hostpool_destroy",
                    "oasis_fetch_blocks"):
@@ -121,6 +124,29 @@ def score_blocks(q_look, k_pool, block_table, ctx_len, scores, scale=None, strea
     _check(lib().oasis_score_blocks(ctypes.byref(s), _ptr(q_look), q_look.shape[1], _ptr(k_pool),
                                     _ptr(block_table), _ptr(ctx_len), scale, _ptr(scores),
                                     _stream(stream)))
+    return scores
+
+
+def pool_keys(k_pool, block_table, ctx_len, ck, num_q_heads=None, last_only=False, stream=None):
+    """k_pool [P][Hkv][16][D] bf16, block_table [B][W] i32, ctx_len [B] i32 ->
+    ck [B][Hkv][W][2][D] bf16 (per-block min, max; written in place)."""
+    Hkv = k_pool.shape[1]
+    s = make_shape(block_table.shape[0], num_q_heads or Hkv, Hkv, k_pool.shape[-1],
+                   block_table.shape[1], k_pool.shape[0])
+    _check(lib().oasis_pool_keys(ctypes.byref(s), _ptr(k_pool), _ptr(block_table), _ptr(ctx_len),
+                                 1 if last_only else 0, _ptr(ck), _stream(stream)))
+    return ck
+
+
+def score_blocks_minmax(q_look, ck, ctx_len, scores, scale=None, stream=None):
+    """q_look [B][n_look][Hq][D] bf16, ck [B][Hkv][W][2][D] bf16, ctx_len [B] i32 ->
+    scores [B][Hkv][W] f32 (written in place)."""
+    B, Hkv, W, _, D = ck.shape
+    s = make_shape(B, q_look.shape[-2], Hkv, D, W, 0)
+    scale = float(D) ** -0.5 if scale is None else scale
+    _check(lib().oasis_score_blocks_minmax(ctypes.byref(s), _ptr(q_look), q_look.shape[1],
+                                           _ptr(ck), _ptr(ctx_len), scale, _ptr(scores),
+                                           _stream(stream)))
     return scores
 
 

@@ -18,9 +18,18 @@ from . import ops
 
 
 class DecodeLayer:
+    """scorer="exact" scores every key of the pool (oasis_score_blocks);
+    scorer="minmax" keeps the keys' per-block min/max (Figure 7 caption:
+    compressed keys by min/max pooling), built from the pool at construction
+    and refreshed with `append()` after a decode step writes a token, and
+    scores from those (oasis_score_blocks_minmax)."""
+
     def __init__(self, *, k_pool, v_pool, block_table, ctx_len, num_q_heads, k_blocks, cap,
-                 n_look=1, n_q=1, slot_block=None, last_use=None):
+                 n_look=1, n_q=1, slot_block=None, last_use=None, scorer="exact"):
+        if scorer not in ("exact", "minmax"):
+            raise ValueError(f"scorer must be 'exact' or 'minmax', not {scorer!r}")
         dev = k_pool.device
+        self.scorer = scorer
         self.k_pool, self.v_pool = k_pool, v_pool
         self.block_table, self.ctx_len = block_table, ctx_len
         B, W = block_table.shape
@@ -40,11 +49,27 @@ class DecodeLayer:
         self.out = torch.empty((B, n_q, num_q_heads, D), dtype=torch.bfloat16, device=dev)
         ws = ops.attn_workspace_bytes(self.shape, n_q, k_blocks)
         self.workspace = torch.zeros((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        self.ck = None
+        if scorer == "minmax":
+            self.ck = torch.empty((B, Hkv, W, 2, D), dtype=torch.bfloat16, device=dev)
+            ops.pool_keys(k_pool, block_table, ctx_len, self.ck, num_q_heads=num_q_heads)
 
     # individual stages -------------------------------------------------
     def score(self, q_look, stream=None, scores=None):
-        ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len,
-                         self.scores if scores is None else scores, stream=stream)
+        out = self.scores if scores is None else scores
+        if self.ck is not None:
+            ops.score_blocks_minmax(q_look, self.ck, self.ctx_len, out, stream=stream)
+        else:
+            ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len, out,
+                             stream=stream)
+
+    def append(self, stream=None):
+        """After the caller has written each sequence's new token into the key
+        pool and advanced ctx_len: refresh the compressed keys of the block it
+        went to (no-op for the exact scorer)."""
+        if self.ck is not None:
+            ops.pool_keys(self.k_pool, self.block_table, self.ctx_len, self.ck,
+                          num_q_heads=self.shape.num_q_heads, last_only=True, stream=stream)
 
     def select(self, stream=None, scores=None):
         ops.select_topk(self.shape, self.scores if scores is None else scores, self.ctx_len,
@@ -106,12 +131,14 @@ class PipelinedDecode:
         self.used = [False, False]
         self.i = 0
 
-    def _score_next(self, q_look, main, ev=None):
+    def _score_next(self, q_look, main, ev=None, append=False):
         b = self.i % 2
         if self.used[b]:
             self.side.wait_event(self.ev_planned[b])    # the plan that last read buf[b]
         else:
             self.side.wait_stream(main)                 # inputs written on the caller's stream
+        if append:
+            self.L.append(stream=self.side)             # compressed keys of the last blocks
         if ev:
             ev[0].record(self.side)
         self.L.score(q_look, stream=self.side, scores=self.buf[b])
@@ -132,14 +159,17 @@ class PipelinedDecode:
         b = self._score_next(q_look, main)
         self._plan(b, step, main)
 
-    def step(self, q, q_look_next, step, copy_out=True, score_events=None):
+    def step(self, q, q_look_next, step, copy_out=True, score_events=None, append=False):
         """Attention of `step` (true query q), overlapped with the scoring of
         q_look_next; then select + plan of step + 1.  Returns a copy of the
         output of `step` (or None), valid on the caller's stream.
         `score_events`, if given, are two timing events recorded around the
-        scoring kernel on the side stream."""
+        scoring kernel on the side stream.  `append` (compressed scorer)
+        first refreshes, on the scoring stream, the compressed keys of each
+        sequence's last block: the token of this step must already be in the
+        key pool as that stream sees it."""
         main = torch.cuda.current_stream()
-        b = self._score_next(q_look_next, main, score_events)
+        b = self._score_next(q_look_next, main, score_events, append)
         self.L.attend(q, stream=main)
         out = self.L.out.clone() if copy_out else None
         self._plan(b, step + 1, main)

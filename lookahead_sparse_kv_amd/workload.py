@@ -62,6 +62,7 @@ class Workload:
     drift: int = 0                # hot blocks random-walk by up to +-drift blocks per step
     seed: int = 0
     block_size: int = BLOCK_SIZE
+    scorer: str = "exact"         # "exact" keys, or "minmax" compressed keys
 
     @property
     def group(self) -> int:
@@ -103,6 +104,10 @@ WORKLOADS = {
     # Qwen3-8B-shaped layer: 16 x 32K, 32 / 8 heads, D 128, budget 2048 (128 blocks)
     "qwen3_8b_32k": Workload("qwen3_8b_32k", 16, 32, 8, 128, (32768,) * 16, 2048, n_hot=102,
                              rhos=(0.9,), ratios=(0.02,), seed=2000),
+    # the same layer and inputs, scored from min/max-pooled keys (Figure 7 caption)
+    "qwen3_8b_32k_minmax": Workload("qwen3_8b_32k_minmax", 16, 32, 8, 128, (32768,) * 16, 2048,
+                                    n_hot=102, rhos=(0.9,), ratios=(0.02,), seed=2000,
+                                    scorer="minmax"),
     # Qwen3-32B-shaped layer, full KV in a pinned host pool, 4 pipelined layers
     "qwen3_32b_32k_hostpool": Workload("qwen3_32b_32k_hostpool", 32, 64, 8, 128, (32768,) * 32,
                                        2048, n_hot=102, rhos=(0.9,), ratios=(0.05,), layers=4,

@@ -39,6 +39,25 @@ def score_tolerance(q_rows, k_row, ctx, bs, W):
     return tol + 1e-30
 
 
+def minmax_tolerance(q_rows, ck_row, ctx, bs):
+    """Per-block bound of |fp32 kernel bound score - fp64 bound score|.  The
+    kernel sums, per lookahead row, 2D exact bf16 products of which at most D
+    are non-zero ([q- | q+] . [min | max]); the same recursive-summation bound
+    as for the exact score applies with gamma_2D, on sum_d |q_d| * the larger
+    of |min_d| and |max_d|."""
+    q = np.abs(np.asarray(q_rows, dtype=np.float64))
+    ck = np.asarray(ck_row, dtype=np.float64)
+    W, _, D = ck.shape
+    scale = 1.0 / math.sqrt(D)
+    gamma = 2 * D * U32 / (1 - 2 * D * U32)
+    big = np.maximum(np.abs(ck[:, 0]), np.abs(ck[:, 1]))     # [W][D]
+    a = (big @ q.T).max(axis=1) * scale                       # [W]
+    nb = (ctx + bs - 1) // bs
+    tol = np.zeros(W)
+    tol[:nb] = 2.0 * (gamma * a[:nb] + 2 * U32 * a[:nb])
+    return tol + 1e-30
+
+
 def check_scores(gpu, orc, tol, where=""):
     gpu = np.asarray(gpu, dtype=np.float64)
     inf_o = np.isneginf(orc)

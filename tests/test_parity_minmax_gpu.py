@@ -1,0 +1,265 @@
+"""GPU parity of the compressed-key path (min/max pooling of the keys and the
+block score from them; OasisKV summary page, Figure 7 caption) against the
+CPU oracle, through the C ABI.  The pooled keys are bf16 values of the keys
+themselves, so they must match the oracle exactly; the scores within the
+fp32 accumulation bound; selections on them bit for bit outside near ties."""
+import numpy as np
+import pytest
+import torch
+
+from lookahead_sparse_kv_amd import ops
+from lookahead_sparse_kv_amd import workload as wlm
+from oracle import oasis_oracle as orc
+from parity_utils import check_scores, check_selection_row, minmax_tolerance
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SENTINEL = 0x4049        # bf16 bits of 3.140625: marks compressed rows that must stay untouched
+
+
+def dev(t):
+    return t.to(DEV).contiguous()
+
+
+def group_rows(q_look, b, g, G):
+    n_look = q_look.shape[1]
+    return torch.cat([q_look[b, j, g * G:(g + 1) * G] for j in range(n_look)]).double().numpy()
+
+
+def gpu_pool(d, wl, last_only=False, ck=None):
+    if ck is None:
+        ck = torch.full((wl.batch, wl.num_kv_heads, wl.table_width, 2, wl.head_dim), SENTINEL,
+                        dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ops.pool_keys(dev(d["k_pool"]), dev(d["block_table"]), dev(d["ctx_len"]), ck,
+                  num_q_heads=wl.num_q_heads, last_only=last_only)
+    torch.cuda.synchronize()
+    return ck
+
+
+def check_pooled(ck_gpu, K, ctx_len, W, where):
+    want = orc.pool_keys(K, ctx_len, 16, W)
+    got = ck_gpu.float().cpu().double().numpy()
+    untouched = ck_gpu.view(torch.int16).cpu().numpy() == SENTINEL
+    for b, ctx in enumerate(np.asarray(ctx_len)):
+        nb = (int(ctx) + 15) // 16
+        assert np.array_equal(got[b, :, :nb], want[b, :, :nb]), f"{where}: pooled keys differ (b{b})"
+        assert untouched[b, :, nb:].all(), f"{where}: blocks past the context were written (b{b})"
+
+
+POOL_CASES = {
+    "tiny_4k_d64": wlm.WORKLOADS["tiny_4k"],
+    "ragged_d64": wlm.small_workload(ctx=(1000, 777), head_dim=64, seed=41),
+    "short_ctx_d128": wlm.small_workload(batch=4, ctx=(2000, 33, 16, 5), head_dim=128, n_hot=0,
+                                         seed=42),
+    "empty_and_one_token_d128": wlm.small_workload(batch=3, ctx=(300, 0, 1), head_dim=128,
+                                                   n_hot=0, seed=43),
+}
+
+
+@pytest.mark.parametrize("name", list(POOL_CASES))
+def test_pool_keys_exact(name):
+    wl = POOL_CASES[name]
+    d = wlm.make_layer(wl)
+    ck = gpu_pool(d, wl)
+    check_pooled(ck, d["K"], d["ctx_len"], wl.table_width, name)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_pool_keys_last_block_after_append(head_dim):
+    # 1000 -> 1001 appends inside a partial block; 768 -> 769 opens a new block
+    wl = wlm.small_workload(ctx=(1000, 768), head_dim=head_dim, seed=44)
+    d = wlm.make_layer(wl)
+    ck = gpu_pool(d, wl)
+    rng = torch.Generator().manual_seed(45)
+    K = d["K"].clone()
+    k_pool = d["k_pool"].clone()
+    new_ctx = d["ctx_len"].clone() + 1
+    for b in range(wl.batch):
+        t = int(d["ctx_len"][b])
+        tok = torch.randn((wl.num_kv_heads, head_dim), generator=rng).to(torch.bfloat16) * 3
+        K[b, :, t] = tok
+        k_pool[int(d["block_table"][b, t // 16]), :, t % 16] = tok
+    d2 = dict(d, K=K, k_pool=k_pool, ctx_len=new_ctx)
+    ck = gpu_pool(d2, wl, last_only=True, ck=ck)
+    check_pooled(ck, K, new_ctx, wl.table_width, f"append D{head_dim}")
+    before = ck.clone()
+    gpu_pool(d2, wl, last_only=True, ck=ck)                  # idempotent
+    assert torch.equal(before.view(torch.int16), ck.view(torch.int16))
+
+
+def test_pool_keys_out_of_range_page_is_an_empty_box():
+    wl = wlm.small_workload(batch=1, ctx=(640,), seed=46)
+    d = wlm.make_layer(wl)
+    bt = d["block_table"].clone()
+    bt[0, 3] = -5
+    bt[0, 7] = wl.num_pages + 100
+    ck = gpu_pool(dict(d, block_table=bt), wl)
+    f = ck.float().cpu()
+    for n in (3, 7):
+        assert torch.all(f[0, :, n, 0] == float("inf")) and torch.all(f[0, :, n, 1] == -float("inf"))
+    scores = torch.empty((1, wl.num_kv_heads, wl.table_width), device=DEV)
+    ops.score_blocks_minmax(dev(d["q_look"]), ck, dev(d["ctx_len"]), scores)
+    got = scores.cpu().numpy()
+    assert np.all(np.isneginf(got[0, :, [3, 7]]))
+    assert np.all(np.isfinite(np.delete(got[0], [3, 7], axis=1)))
+
+
+SCORE_CASES = {
+    "tiny_4k_d64_g4": wlm.WORKLOADS["tiny_4k"],
+    "ragged_d64_g4": wlm.small_workload(ctx=(1000, 777), head_dim=64, seed=51),
+    "short_ctx_d128": wlm.small_workload(batch=4, ctx=(2000, 33, 16, 5), head_dim=128, n_hot=0,
+                                         seed=52),
+    "g8_two_drafts_d128": wlm.small_workload(batch=2, q_heads=16, kv_heads=2, head_dim=128,
+                                             ctx=(3000, 1601), n_look=2, seed=53),
+    "g1_d128": wlm.small_workload(batch=1, q_heads=4, kv_heads=4, head_dim=128, ctx=(777,),
+                                  seed=54),
+    "four_drafts_d128": wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128,
+                                           ctx=(4096, 2500), n_look=4, seed=55),
+    "width_not_multiple_of_64_d128": wlm.small_workload(batch=2, ctx=(16 * 70 + 3, 16 * 65),
+                                                        head_dim=128, seed=56),
+}
+
+
+@pytest.mark.parametrize("name", list(SCORE_CASES))
+def test_score_minmax_matches_oracle(name):
+    wl = SCORE_CASES[name]
+    d = wlm.make_layer(wl)
+    ck = gpu_pool(d, wl)
+    scores = torch.full((wl.batch, wl.num_kv_heads, wl.table_width), 7.0, device=DEV)
+    ops.score_blocks_minmax(dev(d["q_look"]), ck, dev(d["ctx_len"]), scores)
+    torch.cuda.synchronize()
+    got = scores.cpu().double().numpy()
+    ck_o = orc.pool_keys(d["K"], d["ctx_len"], 16, wl.table_width)
+    want = orc.score_minmax(d["q_look"], ck_o, d["ctx_len"], 16)
+    exact = orc.score(d["q_look"], d["K"], d["ctx_len"], 16, wl.table_width)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            tol = minmax_tolerance(group_rows(d["q_look"], b, g, wl.group), ck_o[b, g], wl.ctx[b], 16)
+            check_scores(got[b, g], want[b, g], tol, f"{name} b{b} g{g}")
+    fin = np.isfinite(want)
+    assert np.all(want[fin] >= exact[fin] - 1e-9)             # the bound holds on these inputs
+
+
+@pytest.mark.parametrize("name", ["ragged_d64_g4", "four_drafts_d128"])
+def test_select_on_minmax_scores(name):
+    wl = SCORE_CASES[name]
+    d = wlm.make_layer(wl)
+    ck = gpu_pool(d, wl)
+    scores = torch.empty((wl.batch, wl.num_kv_heads, wl.table_width), device=DEV)
+    ops.score_blocks_minmax(dev(d["q_look"]), ck, dev(d["ctx_len"]), scores)
+    K = wl.k_blocks
+    sel = torch.empty((wl.batch, wl.num_kv_heads, K), dtype=torch.int32, device=DEV)
+    shape = ops.make_shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.table_width,
+                           wl.num_pages)
+    ops.select_topk(shape, scores, dev(d["ctx_len"]), K, sel)
+    got = sel.cpu().numpy()
+    ck_o = orc.pool_keys(d["K"], d["ctx_len"], 16, wl.table_width)
+    want_s = orc.score_minmax(d["q_look"], ck_o, d["ctx_len"], 16)
+    want = orc.select(want_s, d["ctx_len"], 16, K)
+    for b in range(wl.batch):
+        nb = (wl.ctx[b] + 15) // 16
+        for g in range(wl.num_kv_heads):
+            check_selection_row(got[b, g], want[b, g], want_s[b, g], nb, K, f"{name} b{b} g{g}")
+
+
+def test_minmax_full_size_sampled_rows():
+    # 16 x 32K, Qwen3-8B shape: pool every block, score, select; sampled rows
+    # against the oracle row by row.
+    wl = wlm.WORKLOADS["qwen3_8b_32k"]
+    d = wlm.make_layer(wl)
+    ck = gpu_pool(d, wl)
+    scores = torch.empty((wl.batch, wl.num_kv_heads, wl.table_width), device=DEV)
+    ops.score_blocks_minmax(dev(d["q_look"]), ck, dev(d["ctx_len"]), scores)
+    sel = torch.empty((wl.batch, wl.num_kv_heads, wl.k_blocks), dtype=torch.int32, device=DEV)
+    shape = ops.make_shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.table_width,
+                           wl.num_pages)
+    ops.select_topk(shape, scores, dev(d["ctx_len"]), wl.k_blocks, sel)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(57)
+    exempt = 0
+    for b, g in [(0, 0), (15, 7)] + [tuple(x) for x in rng.integers(0, [16, 8], size=(4, 2))]:
+        ctx = wl.ctx[b]
+        ck_row = orc.pool_keys_row(d["K"][b, g], ctx, 16, wl.table_width)
+        got_ck = ck[b, g].float().cpu().double().numpy()
+        nb = (ctx + 15) // 16
+        assert np.array_equal(got_ck[:nb], ck_row[:nb]), f"b{b} g{g}: pooled keys differ"
+        rows = group_rows(d["q_look"], b, g, wl.group)
+        want = orc.score_minmax_row(rows, ck_row, ctx, 16)
+        got = scores[b, g].cpu().double().numpy()
+        check_scores(got, want, minmax_tolerance(rows, ck_row, ctx, 16), f"b{b} g{g}")
+        want_sel = orc.select_row(want, nb, wl.k_blocks)
+        exempt += check_selection_row(sel[b, g].cpu().numpy(), want_sel, want, nb, wl.k_blocks,
+                                      f"b{b} g{g}")
+    assert exempt <= 2
+
+
+def test_minmax_decode_steps_with_appends():
+    """Steps of the whole layer with the compressed scorer (score -> select +
+    plan -> attention); after each step every sequence appends one token to
+    its keys and values and the compressed keys of its last block are
+    refreshed.  Each step is checked against the oracle on the grown context,
+    with the near-tie exemption and resync on the planner's state."""
+    from lookahead_sparse_kv_amd.pipeline import DecodeLayer
+    from parity_utils import ATTN_ATOL, check_plan_row
+    wl = wlm.small_workload(batch=3, q_heads=8, kv_heads=2, head_dim=128, ctx=(3000, 2047, 1024),
+                            budget=512, n_hot=12, ratio=0.1, seed=61)
+    d = wlm.make_layer(wl)
+    K, V = d["K"].clone(), d["V"].clone()
+    k_pool, v_pool = dev(d["k_pool"]), dev(d["v_pool"])
+    ctx = d["ctx_len"].clone()
+    ctx_dev = dev(ctx)
+    cap = wl.cap()
+    layer = DecodeLayer(k_pool=k_pool, v_pool=v_pool, block_table=dev(d["block_table"]),
+                        ctx_len=ctx_dev, num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks,
+                        cap=cap, scorer="minmax")
+    q = d["q"].unsqueeze(1)
+    gen = torch.Generator().manual_seed(62)
+    rows = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    exempt = 0
+    for step in range(5):
+        q_look = wlm.draw_lookahead(wl, d["q32"], 200 + step).to(torch.bfloat16)
+        sb0, lu0 = layer.slot_block.cpu().numpy(), layer.last_use.cpu().numpy()
+        layer.step(dev(q_look), dev(q), step)
+        torch.cuda.synchronize()
+        scores = layer.scores.cpu().double().numpy()
+        sel = layer.sel.cpu().numpy()
+        g_state = dict(fetch_block=layer.fetch_block.cpu().numpy()[..., :cap],
+                       fetch_slot=layer.fetch_slot.cpu().numpy()[..., :cap],
+                       fetch_count=layer.fetch_count.cpu().numpy(),
+                       slot_block=layer.slot_block.cpu().numpy(),
+                       last_use=layer.last_use.cpu().numpy())
+        out = layer.out.float().cpu().numpy()
+        for b, g in rows:
+            where = f"minmax step {step} b{b} g{g}"
+            c = int(ctx[b])
+            nb = (c + 15) // 16
+            qr = group_rows(q_look, b, g, wl.group)
+            ck_row = orc.pool_keys_row(K[b, g], c, 16, wl.table_width)
+            o_s = orc.score_minmax_row(qr, ck_row, c, 16)
+            check_scores(scores[b, g], o_s, minmax_tolerance(qr, ck_row, c, 16), where)
+            o_sel = orc.select_row(o_s, nb, wl.k_blocks)
+            ex = check_selection_row(sel[b, g], o_sel, o_s, nb, wl.k_blocks, where)
+            use_sel = sel[b, g] if ex else o_sel
+            fb, fs, cnt, sb1, lu1 = orc.plan_row(use_sel, o_s, sb0[b, g], lu0[b, g], cap, step)
+            o_plan = dict(fetch_block=fb, fetch_slot=fs, fetch_count=cnt, slot_block=sb1,
+                          last_use=lu1)
+            ex |= check_plan_row({k: v[b, g] for k, v in g_state.items()}, o_plan, use_sel,
+                                 sb0[b, g], o_s, cap, step, where)
+            exempt += ex
+            o_out = orc.attn_row(q[b, 0, g * wl.group:(g + 1) * wl.group], K[b, g], V[b, g], c, 16,
+                                 g_state["slot_block"][b, g])
+            err = np.abs(out[b, 0, g * wl.group:(g + 1) * wl.group] - o_out).max()
+            assert err <= ATTN_ATOL, (where, err)
+        # every sequence appends one token (the block table has a page for it)
+        for b in range(wl.batch):
+            t = int(ctx[b])
+            page = int(d["block_table"][b, t // 16])
+            kt = torch.randn((wl.num_kv_heads, wl.head_dim), generator=gen).to(torch.bfloat16)
+            vt = torch.randn((wl.num_kv_heads, wl.head_dim), generator=gen).to(torch.bfloat16)
+            K[b, :, t], V[b, :, t] = kt, vt
+            k_pool[page, :, t % 16] = dev(kt)
+            v_pool[page, :, :, t % 16] = dev(vt)
+        ctx += 1
+        ctx_dev.copy_(dev(ctx))
+        layer.append()
+    assert exempt <= len(rows) * 5 // 4
