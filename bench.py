@@ -414,32 +414,53 @@ def main():
     # after layer, as in a model's decode step).  Only the scoring kernel is
     # bracketed by events inside the timed loop, on the stream it runs on.
     side = torch.cuda.Stream(device=dev)                                # default priority
-    pipes = [PipelinedDecode(L, side=side) for L in layers]
-    for P in pipes:
-        P.prime(looks[0], 0)
-    # compressed scorer: each step also refreshes the compressed keys of the
-    # block a decode step appends to (the pool itself is not written here)
+    # Compressed scorer: select/plan on a third stream, so that a layer's plan
+    # for t + 1 overlaps the next layers' attention (measured faster); exact
+    # scorer: scoring bounds the step and select/plan stays on the caller's
+    # stream (a third stream measured slower there).
+    plan_stream = torch.cuda.Stream(device=dev) if wl.scorer == "minmax" else None
+    pipes = [PipelinedDecode(L, side=side, plan_stream=plan_stream) for L in layers]
+    # compressed scorer: each scoring launch also re-pools the block a decode
+    # step appends to (the pool itself is not written here)
     append = wl.scorer == "minmax"
+    for P in pipes:
+        P.prime(looks[0], 0, append=append)
     for i in range(args.warmup):
         pipes[i % n_rep].step(q, looks[(i // n_rep + 1) % N_LOOK_DRAWS], 1 + i // n_rep,
                               copy_out=False, append=append)
     for P in pipes:
         P.drain()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+
+    def run_steps(first, events=None):
+        for i in range(args.steps):
+            s = first + i
+            pipes[s % n_rep].step(q, looks[(s // n_rep + 1) % N_LOOK_DRAWS], 1 + s // n_rep,
+                                  copy_out=False, append=append,
+                                  score_events=None if events is None else events[i])
+        for P in pipes:
+            P.drain()
+
+    # The timed region: K steps, no events inside (an event pair per launch
+    # perturbs the three-stream schedule of the compressed scorer by up to 2x).
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
-    for i in range(args.steps):
-        s = args.warmup + i
-        pipes[s % n_rep].step(q, looks[(s // n_rep + 1) % N_LOOK_DRAWS], 1 + s // n_rep,
-                              copy_out=False, score_events=ev[i], append=append)
-    for P in pipes:
-        P.drain()
+    run_steps(args.warmup)
     ev1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    # The same K steps again with the scoring launches bracketed by events on
+    # the scoring stream: the roofline of the scoring kernel as it runs in the
+    # pipeline (sharing the GPU with attention and select/plan).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_a.record()
+    run_steps(args.warmup + args.steps, ev)
+    e_b.record()
+    torch.cuda.synchronize()
+    ms_per_step_with_events = e_a.elapsed_time(e_b) / args.steps
     score_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
     mean_ms = {"score": sum(score_ms) / len(score_ms)}
 
@@ -451,7 +472,7 @@ def main():
         e = iso[i]
         L = layers[i % n_rep]
         e[0].record()
-        L.score(looks[i % N_LOOK_DRAWS])
+        L.score(looks[i % N_LOOK_DRAWS], refresh=append)
         e[1].record()
         L.select_plan(2000 + i)
         e[2].record()
@@ -464,11 +485,9 @@ def main():
     # each stage back to back (events around the whole loop, replicas in
     # turn): the per-call cost without an event and a launch gap per call
     b2b = {}
-    stages = [("score", lambda i, L: L.score(looks[i % N_LOOK_DRAWS])),
+    stages = [("score", lambda i, L: L.score(looks[i % N_LOOK_DRAWS], refresh=append)),
               ("select_plan", lambda i, L: L.select_plan(3000 + i)),
               ("attn", lambda i, L: L.attend(q))]
-    if append:
-        stages.append(("append", lambda i, L: L.append()))
     for k, fn in stages:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -484,9 +503,10 @@ def main():
         e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e2.record()
         for i in range(args.steps):
-            if append:
-                layers[i % n_rep].append()
-            layers[i % n_rep].step(looks[i % N_LOOK_DRAWS], q, 1000 + i)
+            L = layers[i % n_rep]
+            L.score(looks[i % N_LOOK_DRAWS], refresh=append)
+            L.select_plan(1000 + i)
+            L.attend(q)
         e3.record()
         torch.cuda.synchronize()
         detail["ms_per_step_no_overlap"] = round(e2.elapsed_time(e3) / args.steps, 4)
@@ -533,7 +553,8 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": sb},
-        "score_us_in_loop": dict(percentiles_us(score_ms), mean=round(mean_ms["score"] * 1e3, 2)),
+        "score_us_in_loop": dict(percentiles_us(score_ms), mean=round(mean_ms["score"] * 1e3, 2),
+                                 ms_per_step_of_that_loop=round(ms_per_step_with_events, 4)),
         "stages_alone_us": {k: percentiles_us(v) for k, v in alone.items()},
         "stages_back_to_back_us": {k: round(v * 1e3, 2) for k, v in b2b.items()},
         "attn_roofline": {"kernels": "attn_partial + attn_merge", "timing": "back-to-back mean",

@@ -130,13 +130,22 @@ int oasis_pool_keys(const oasis_shape *s, const uint16_t *k_pool, const int32_t 
  *
  * An upper bound of oasis_score_blocks' exact score, equal to it for a block
  * of one token; it reads 2D values per block instead of 16D.  bf16 inputs,
- * fp32 accumulation.  Requires D in {64, 128}, bs = 16, 1 <= n_look,
- * n_look * G <= 16, scale > 0, ck 16-byte aligned.  The output feeds
- * oasis_select_topk / oasis_select_plan unchanged.
+ * fp32 accumulation.  The output feeds oasis_select_topk / oasis_select_plan
+ * unchanged.
+ *
+ * k_pool and block_table (both set, or both NULL): in the same launch, the
+ * last block of each sequence (ceil(ctx_len[b] / bs) - 1, the one a decode
+ * step appends its token to) is first re-pooled from the key pool exactly as
+ * oasis_pool_keys(last_only = 1) would, its row of ck is written, and it is
+ * scored from the fresh values.  This keeps ck current for decode without a
+ * separate launch.  ck is only read when both are NULL.
+ *
+ * Requires D in {64, 128}, bs = 16, 1 <= n_look, n_look * G <= 16, scale > 0;
+ * q_look, ck and k_pool 16-byte aligned.
  */
 int oasis_score_blocks_minmax(const oasis_shape *s, const uint16_t *q_look, int32_t n_look,
-                              const uint16_t *ck, const int32_t *ctx_len, float scale,
-                              float *scores, void *stream);
+                              uint16_t *ck, const uint16_t *k_pool, const int32_t *block_table,
+                              const int32_t *ctx_len, float scale, float *scores, void *stream);
 
 /*
  * Per-KV-head top-K.  Figure 7 caption ("top-K blocks"); abstract (a

@@ -113,8 +113,8 @@ int oasis_pool_keys(const oasis_shape *s, const uint16_t *k_pool, const int32_t 
 }
 
 int oasis_score_blocks_minmax(const oasis_shape *s, const uint16_t *q_look, int32_t n_look,
-                              const uint16_t *ck, const int32_t *ctx_len, float scale,
-                              float *scores, void *stream) {
+                              uint16_t *ck, const uint16_t *k_pool, const int32_t *block_table,
+                              const int32_t *ctx_len, float scale, float *scores, void *stream) {
     const char *fn = "oasis_score_blocks_minmax";
     if (int e = check_shape(s, fn)) return e;
     if (n_look < 1) return fail(OASIS_ERR_INVALID, "%s: n_look %d < 1", fn, n_look);
@@ -127,10 +127,15 @@ int oasis_score_blocks_minmax(const oasis_shape *s, const uint16_t *q_look, int3
     if (s->batch == 0 || s->table_width == 0) return ok();
     if (!q_look || !ck || !ctx_len || !scores)
         return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
-    if (reinterpret_cast<uintptr_t>(ck) % 16)
-        return fail(OASIS_ERR_INVALID, "%s: ck must be 16-byte aligned", fn);
-    oasis::MinmaxArgs a{q_look, ck, ctx_len, scores, scale, s->batch, s->num_q_heads,
-                        s->num_kv_heads, G, s->table_width, n_look, n_look * G};
+    if (!k_pool != !block_table)
+        return fail(OASIS_ERR_INVALID, "%s: k_pool and block_table must both be set or both NULL",
+                    fn);
+    if (reinterpret_cast<uintptr_t>(ck) % 16 || reinterpret_cast<uintptr_t>(k_pool) % 16 ||
+        reinterpret_cast<uintptr_t>(q_look) % 16)
+        return fail(OASIS_ERR_INVALID, "%s: q_look, ck and k_pool must be 16-byte aligned", fn);
+    oasis::MinmaxArgs a{q_look, ck, k_pool, block_table, ctx_len, scores, scale, s->batch,
+                        s->num_q_heads, s->num_kv_heads, G, s->table_width, s->num_pages, n_look,
+                        n_look * G};
     return check_hip(oasis::launch_score_minmax(a, s->head_dim, as_stream(stream)), fn);
 }
 

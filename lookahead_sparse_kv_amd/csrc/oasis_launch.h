@@ -76,13 +76,18 @@ struct PoolArgs {
 };
 
 // Block scores from the compressed keys.
+// Block scores from the compressed keys; with k_pool set, the last block of
+// each sequence is first re-pooled from the key pool (ck written) and scored
+// from the fresh values.
 struct MinmaxArgs {
     const uint16_t *q_look;
-    const uint16_t *ck;
+    uint16_t *ck;
+    const uint16_t *k_pool;        // NULL: no refresh
+    const int32_t *block_table;
     const int32_t *ctx_len;
     float *scores;
     float scale;
-    int batch, hq, hkv, group, width, n_look, n_rows_q;
+    int batch, hq, hkv, group, width, num_pages, n_look, n_rows_q;
 };
 
 hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t stream);

@@ -38,6 +38,26 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Scores of one row into LDS as keys.  A thread's loads (8 per round) are all
+// issued before the first is used, so the row costs one memory latency per
+// 2,048 blocks instead of one per 256.
+__device__ __forceinline__ void load_row_keys(const float *srow, int nb, uint32_t *keys) {
+    constexpr int U = 8;
+    for (int n0 = 0; n0 < nb; n0 += kRowThreads * U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int n = n0 + u * kRowThreads + (int)threadIdx.x;
+            v[u] = n < nb ? srow[n] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int n = n0 + u * kRowThreads + (int)threadIdx.x;
+            if (n < nb) keys[n] = score_key(v[u]);
+        }
+    }
+}
+
 // Inclusive scan of one int per thread over the workgroup (two barriers).
 __device__ __forceinline__ int row_inclusive_scan(int v, int *wave_sums) {
     const int lane = threadIdx.x & (kWave - 1);

@@ -18,6 +18,11 @@
 // reduces each tile's columns over the lookahead rows with two lane exchanges.
 // A block written as an empty box (min > max, for a page outside the pool)
 // scores -inf.  The bytes are 1/8 of the exact scorer's at bs = 16.
+//
+// With the key pool given, one more wave per row re-pools the row's last
+// block (the one a decode step appends to) from the pool, writes it, and
+// scores it itself; the tile waves leave that block's score to it, so no
+// wave reads compressed keys another wave writes.
 #include "oasis_device.h"
 #include "oasis_launch.h"
 
@@ -31,6 +36,110 @@ constexpr int kMmWaves = 4;
 constexpr int kMmTiles = 4;            // 16-block tiles per wave
 constexpr int kMmBlocksPerWave = kMmTiles * kBlockTokens;
 
+// Refresh wave of one row: pool the last block (ceil(ctx / 16) - 1) from the
+// key pool as oasis_pool_keys does, write its compressed row, and score it
+// from the fresh values: lane (c, tg) holds dims 8c .. 8c + 7 and takes the
+// lookahead rows tg, tg + TPL, ...; the row sums are folded over the CH lanes
+// of a token group and the max over the groups.
+template <int D>
+__device__ __forceinline__ void refresh_last_block(const MinmaxArgs &a, int row) {
+    constexpr int CH = D / 8;
+    constexpr int TPL = kWave / CH;
+    constexpr int NL = kBlockTokens / TPL;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int b = row / a.hkv;
+    const int g = row - b * a.hkv;
+    long long ctx = a.ctx_len[b];
+    const long long cmax = (long long)a.width * kBlockTokens;
+    ctx = ctx < 0 ? 0 : (ctx > cmax ? cmax : ctx);
+    const int nb = (int)((ctx + kBlockTokens - 1) / kBlockTokens);
+    if (nb == 0) return;
+    const int n = nb - 1;
+    const int nt = (int)(ctx - (long long)n * kBlockTokens);
+    const int c = lane % CH;
+    const int tg = lane / CH;
+    uint16_t *crow = a.ck + ((size_t)row * a.width + n) * 2 * D;
+    float *out = a.scores + (size_t)row * a.width;
+    const int page = a.block_table[(size_t)b * a.width + n];
+    if (page < 0 || page >= a.num_pages) {
+        if (tg == 0) {
+            const u32x4 pinf = {0x7f807f80u, 0x7f807f80u, 0x7f807f80u, 0x7f807f80u};
+            const u32x4 ninf = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+            *reinterpret_cast<u32x4 *>(crow + 8 * c) = pinf;
+            *reinterpret_cast<u32x4 *>(crow + D + 8 * c) = ninf;
+        }
+        if (lane == 0) out[n] = -__builtin_inff();
+        return;
+    }
+    const uint16_t *tile = a.k_pool + ((size_t)page * a.hkv + g) * kBlockTokens * D;
+    float mn[8], mx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { mn[e] = __builtin_inff(); mx[e] = -__builtin_inff(); }
+    u32x4 v[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int t = tg + TPL * i;
+        v[i] = t < nt ? *reinterpret_cast<const u32x4 *>(tile + (size_t)t * D + 8 * c)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        if (tg + TPL * i < nt) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float lo = bf16_bits_to_float(v[i][w] & 0xffffu);
+                const float hi = bf16_bits_to_float(v[i][w] >> 16);
+                mn[2 * w] = fminf(mn[2 * w], lo);
+                mx[2 * w] = fmaxf(mx[2 * w], lo);
+                mn[2 * w + 1] = fminf(mn[2 * w + 1], hi);
+                mx[2 * w + 1] = fmaxf(mx[2 * w + 1], hi);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = CH; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            mn[e] = fminf(mn[e], shfl_xor_f(mn[e], off));
+            mx[e] = fmaxf(mx[e], shfl_xor_f(mx[e], off));
+        }
+    }
+    if (tg == 0) {
+        u32x4 pmn, pmx;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            pmn[w] = (__builtin_bit_cast(uint32_t, mn[2 * w]) >> 16) |
+                     (__builtin_bit_cast(uint32_t, mn[2 * w + 1]) & 0xffff0000u);
+            pmx[w] = (__builtin_bit_cast(uint32_t, mx[2 * w]) >> 16) |
+                     (__builtin_bit_cast(uint32_t, mx[2 * w + 1]) & 0xffff0000u);
+        }
+        *reinterpret_cast<u32x4 *>(crow + 8 * c) = pmn;
+        *reinterpret_cast<u32x4 *>(crow + D + 8 * c) = pmx;
+    }
+    // the bound of every lookahead row this lane takes, then the max
+    float best = -__builtin_inff();
+    for (int r = tg; r < a.n_rows_q; r += TPL) {
+        const int jd = r / a.group;
+        const int hr = r - jd * a.group;
+        const u32x4 qw = load_u32x4(a.q_look +
+            (((size_t)b * a.n_look + jd) * a.hq + (size_t)g * a.group + hr) * D + 8 * c);
+        float part = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float q0 = bf16_bits_to_float(qw[w] & 0xffffu);
+            const float q1 = bf16_bits_to_float(qw[w] >> 16);
+            part += q0 < 0.f ? q0 * mn[2 * w] : q0 * mx[2 * w];
+            part += q1 < 0.f ? q1 * mn[2 * w + 1] : q1 * mx[2 * w + 1];
+        }
+#pragma unroll
+        for (int off = 1; off < CH; off <<= 1) part += shfl_xor_f(part, off);
+        best = fmaxf(best, part);
+    }
+#pragma unroll
+    for (int off = CH; off < kWave; off <<= 1) best = fmaxf(best, shfl_xor_f(best, off));
+    if (lane == 0) out[n] = best * a.scale;
+}
+
 template <int D>
 __global__ __launch_bounds__(kMmWaves * kWave) void score_minmax_kernel(MinmaxArgs a) {
     constexpr int QK = D / 32;         // 32-wide k-steps of one half (q- or q+)
@@ -42,8 +151,13 @@ __global__ __launch_bounds__(kMmWaves * kWave) void score_minmax_kernel(MinmaxAr
     const long long gw = (long long)blockIdx.x * kMmWaves + wave;
     const int chunks = (a.width + kMmBlocksPerWave - 1) / kMmBlocksPerWave;
     const int rows = a.batch * a.hkv;
+    const bool refresh = a.k_pool != nullptr;
+    if (gw >= (long long)rows * chunks) {         // the refresh waves, one per row
+        const long long r = gw - (long long)rows * chunks;
+        if (refresh && r < rows) refresh_last_block<D>(a, (int)r);
+        return;
+    }
     const int row = (int)(gw / chunks);
-    if (row >= rows) return;
     const int n0 = (int)(gw - (long long)row * chunks) * kMmBlocksPerWave;
     const int b = row / a.hkv;
     const int g = row - b * a.hkv;
@@ -109,7 +223,7 @@ __global__ __launch_bounds__(kMmWaves * kWave) void score_minmax_kernel(MinmaxAr
         m = fmaxf(m, shfl_xor_f(m, 16));
         m = fmaxf(m, shfl_xor_f(m, 32));
         const int n = n0 + t * kBlockTokens + r16;
-        if (j4 == 0 && n < a.width) {
+        if (j4 == 0 && n < a.width && !(refresh && n == nb - 1)) {   // the refresh wave scores nb - 1
             // lanes j4 = 0 hold min[0..7] (k-step 0) and max[0..7] (k-step QK) of block r16
             const float mn0 = bf16_bits_to_float(kb[t][0][0] & 0xffffu);
             const float mx0 = bf16_bits_to_float(kb[t][QK][0] & 0xffffu);
@@ -121,7 +235,7 @@ __global__ __launch_bounds__(kMmWaves * kWave) void score_minmax_kernel(MinmaxAr
 hipError_t launch_score_minmax(const MinmaxArgs &a, int head_dim, hipStream_t stream) {
     const long long rows = (long long)a.batch * a.hkv;
     const long long chunks = (a.width + kMmBlocksPerWave - 1) / kMmBlocksPerWave;
-    const long long waves = rows * chunks;
+    const long long waves = rows * chunks + (a.k_pool ? rows : 0);
     if (waves == 0) return hipSuccess;
     const dim3 grid((unsigned)((waves + kMmWaves - 1) / kMmWaves));
     const dim3 block(kMmWaves * kWave);

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
 
     if (MODE & 1) {
         const int nb = row_valid_blocks(a.ctx_len, row / a.hkv, a.width);
-        for (int n = tid; n < nb; n += kRowThreads) keys[n] = score_key(srow[n]);
+        load_row_keys(srow, nb, keys);
         __syncthreads();
         row_select(keys, nb, K, sel, sh);
         if (a.sel)

@@ -56,7 +56,7 @@ def lib() -> ctypes.CDLL:
         L.oasis_score_blocks.argtypes = [S, p, i32, p, p, p, f32, p, p]
         L.oasis_select_topk.argtypes = [S, p, p, i32, p, p]
         L.oasis_pool_keys.argtypes = [S, p, p, p, i32, p, p]
-        L.oasis_score_blocks_minmax.argtypes = [S, p, i32, p, p, f32, p, p]
+        L.oasis_score_blocks_minmax.argtypes = [S, p, i32, p, p, p, p, f32, p, p]
         L.oasis_plan_fetch.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p]
         L.oasis_select_plan.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p, p]
         L.oasis_attn_workspace_bytes.argtypes = [S, i32, i32]
@@ -138,15 +138,17 @@ def pool_keys(k_pool, block_table, ctx_len, ck, num_q_heads=None, last_only=Fals
     return ck
 
 
-def score_blocks_minmax(q_look, ck, ctx_len, scores, scale=None, stream=None):
+def score_blocks_minmax(q_look, ck, ctx_len, scores, scale=None, k_pool=None, block_table=None,
+                        stream=None):
     """q_look [B][n_look][Hq][D] bf16, ck [B][Hkv][W][2][D] bf16, ctx_len [B] i32 ->
-    scores [B][Hkv][W] f32 (written in place)."""
+    scores [B][Hkv][W] f32 (written in place).  With k_pool [P][Hkv][16][D] and
+    block_table [B][W], each sequence's last block is re-pooled into ck first."""
     B, Hkv, W, _, D = ck.shape
-    s = make_shape(B, q_look.shape[-2], Hkv, D, W, 0)
+    s = make_shape(B, q_look.shape[-2], Hkv, D, W, 0 if k_pool is None else k_pool.shape[0])
     scale = float(D) ** -0.5 if scale is None else scale
     _check(lib().oasis_score_blocks_minmax(ctypes.byref(s), _ptr(q_look), q_look.shape[1],
-                                           _ptr(ck), _ptr(ctx_len), scale, _ptr(scores),
-                                           _stream(stream)))
+                                           _ptr(ck), _ptr(k_pool), _ptr(block_table),
+                                           _ptr(ctx_len), scale, _ptr(scores), _stream(stream)))
     return scores
 
 

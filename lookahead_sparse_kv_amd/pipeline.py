@@ -55,10 +55,15 @@ class DecodeLayer:
             ops.pool_keys(k_pool, block_table, ctx_len, self.ck, num_q_heads=num_q_heads)
 
     # individual stages -------------------------------------------------
-    def score(self, q_look, stream=None, scores=None):
+    def score(self, q_look, stream=None, scores=None, refresh=False):
+        """refresh (compressed scorer): in the same launch, first re-pool each
+        sequence's last block from the key pool (see append())."""
         out = self.scores if scores is None else scores
         if self.ck is not None:
-            ops.score_blocks_minmax(q_look, self.ck, self.ctx_len, out, stream=stream)
+            ops.score_blocks_minmax(q_look, self.ck, self.ctx_len, out,
+                                    k_pool=self.k_pool if refresh else None,
+                                    block_table=self.block_table if refresh else None,
+                                    stream=stream)
         else:
             ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len, out,
                              stream=stream)
@@ -98,18 +103,24 @@ class DecodeLayer:
 
 
 class PipelinedDecode:
-    """Steady-state decode of one layer with the next step's scoring overlapped.
+    """Steady-state decode of one layer with the next step's prediction in the
+    background.
 
     The pages' prefetch pipeline (Figure 8 of the metalmedia.ai summary) lets
     the draft query of step t drive top-K prediction and KV selection before
     that layer's attention at step t + 1.  Here attention of step t, which
     reads the working set left by the previous plan, runs on the caller's
     stream while the block scoring of the lookahead query for step t + 1 runs
-    on a side stream; select + plan for step t + 1 then waits for both (it
+    on a side stream; select + plan for step t + 1 waits for both (it
     rewrites the working set attention reads).  The score buffer is doubled so
     that scoring can run a step ahead.  Every stage sees exactly the inputs it
     sees in DecodeLayer.step order (score -> select/plan -> attention), so the
     results are identical.
+
+    With `plan_stream`, select + plan runs on that stream instead of the
+    caller's: the caller's stream then carries only attention, which waits for
+    its own layer's plan.  When several layers (one pipeline each) take turns,
+    a layer's plan for t + 1 overlaps the attention of the layers after it.
 
         pipe = PipelinedDecode(layer)
         pipe.prime(q_look_0, step=0)          # score + select/plan of step 0
@@ -118,16 +129,20 @@ class PipelinedDecode:
         pipe.drain()
     """
 
-    def __init__(self, layer: DecodeLayer, side=None):
-        """`side`: the stream the scoring runs on; several pipelines (one per
-        layer) may share one, so that scoring runs layer after layer."""
+    def __init__(self, layer: DecodeLayer, side=None, plan_stream=None):
+        """`side`: the stream the scoring runs on; `plan_stream`: the stream
+        select + plan runs on (None: the caller's).  Several pipelines (one per
+        layer) may share them, so that each runs layer after layer."""
         self.L = layer
         self.buf = [layer.scores, torch.empty_like(layer.scores)]
         if side is None:
             side = torch.cuda.Stream(device=layer.scores.device)          # default priority
         self.side = side
+        self.plan_stream = plan_stream
         self.ev_scored = [torch.cuda.Event(), torch.cuda.Event()]
         self.ev_planned = [torch.cuda.Event(), torch.cuda.Event()]
+        self.ev_attended = torch.cuda.Event()
+        self.last_plan = None            # event of the latest plan (plan_stream mode)
         self.used = [False, False]
         self.i = 0
 
@@ -137,26 +152,33 @@ class PipelinedDecode:
             self.side.wait_event(self.ev_planned[b])    # the plan that last read buf[b]
         else:
             self.side.wait_stream(main)                 # inputs written on the caller's stream
-        if append:
-            self.L.append(stream=self.side)             # compressed keys of the last blocks
         if ev:
             ev[0].record(self.side)
-        self.L.score(q_look, stream=self.side, scores=self.buf[b])
+        # append: the compressed keys of the last blocks are refreshed in the launch
+        self.L.score(q_look, stream=self.side, scores=self.buf[b], refresh=append)
         if ev:
             ev[1].record(self.side)
         self.ev_scored[b].record(self.side)
         return b
 
-    def _plan(self, b, step, main):
-        main.wait_event(self.ev_scored[b])
-        self.L.select_plan(step, stream=main, scores=self.buf[b])
-        self.ev_planned[b].record(main)
+    def _plan(self, b, step, main, after_attention=False):
+        ps = main if self.plan_stream is None else self.plan_stream
+        if ps is not main:
+            if after_attention:
+                self.ev_attended.record(main)            # the plan rewrites what it read
+                ps.wait_event(self.ev_attended)
+            else:
+                ps.wait_stream(main)                    # inputs written on the caller's stream
+        ps.wait_event(self.ev_scored[b])
+        self.L.select_plan(step, stream=ps, scores=self.buf[b])
+        self.ev_planned[b].record(ps)
+        self.last_plan = self.ev_planned[b]
         self.used[b] = True
         self.i += 1
 
-    def prime(self, q_look, step):
+    def prime(self, q_look, step, append=False):
         main = torch.cuda.current_stream()
-        b = self._score_next(q_look, main)
+        b = self._score_next(q_look, main, append=append)
         self._plan(b, step, main)
 
     def step(self, q, q_look_next, step, copy_out=True, score_events=None, append=False):
@@ -169,14 +191,19 @@ class PipelinedDecode:
         sequence's last block: the token of this step must already be in the
         key pool as that stream sees it."""
         main = torch.cuda.current_stream()
+        if self.plan_stream is not None and self.last_plan is not None:
+            main.wait_event(self.last_plan)             # the working set of `step`
         b = self._score_next(q_look_next, main, score_events, append)
         self.L.attend(q, stream=main)
         out = self.L.out.clone() if copy_out else None
-        self._plan(b, step + 1, main)
+        self._plan(b, step + 1, main, after_attention=True)
         return out
 
     def drain(self):
-        torch.cuda.current_stream().wait_stream(self.side)
+        main = torch.cuda.current_stream()
+        main.wait_stream(self.side)
+        if self.plan_stream is not None:
+            main.wait_stream(self.plan_stream)
 
 
 class HostTierLayer:

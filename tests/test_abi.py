@@ -142,3 +142,25 @@ def test_select_plan_rejects_bad_arguments():
     assert sp(fb=None) == ops.OASIS_ERR_INVALID
     assert sp(shape=_shape(table_width=20000)) == ops.OASIS_ERR_UNSUPPORTED
     assert sp(shape=_shape(batch=0)) == ops.OASIS_OK
+
+
+def test_minmax_calls_reject_bad_arguments():
+    L = ops.lib()
+    s = _shape()
+    mm = lambda n_look=1, ck=P, kp=None, bt=None, scale=0.1, shape=s: L.oasis_score_blocks_minmax(
+        ctypes.byref(shape), P, n_look, ck, kp, bt, P, scale, P, None)
+    assert mm(n_look=0) == ops.OASIS_ERR_INVALID
+    assert mm(n_look=5) == ops.OASIS_ERR_UNSUPPORTED        # 5 * 4 rows > 16
+    assert mm(ck=None) == ops.OASIS_ERR_INVALID
+    assert mm(kp=P) == ops.OASIS_ERR_INVALID                  # k_pool without block_table
+    assert mm(bt=P) == ops.OASIS_ERR_INVALID
+    assert mm(ck=ctypes.c_void_p(24)) == ops.OASIS_ERR_INVALID   # misaligned
+    assert mm(scale=-1.0) == ops.OASIS_ERR_INVALID
+    assert mm(shape=_shape(head_dim=96)) == ops.OASIS_ERR_UNSUPPORTED
+    assert mm(shape=_shape(batch=0)) == ops.OASIS_OK
+    pk = lambda last=0, ck=P, shape=s: L.oasis_pool_keys(ctypes.byref(shape), P, P, P, last, ck, None)
+    assert pk(last=2) == ops.OASIS_ERR_INVALID
+    assert pk(ck=None) == ops.OASIS_ERR_INVALID
+    assert pk(ck=ctypes.c_void_p(24)) == ops.OASIS_ERR_INVALID
+    assert pk(shape=_shape(block_size=8)) == ops.OASIS_ERR_UNSUPPORTED
+    assert pk(shape=_shape(batch=0)) == ops.OASIS_OK

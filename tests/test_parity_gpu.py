@@ -404,9 +404,11 @@ def test_decode_steps_mid_size_with_lru(n_look):
     assert exempt <= len(rows) * 6 // 4
 
 
-def test_pipelined_decode_matches_sequential_steps():
+@pytest.mark.parametrize("plan_stream", [False, True])
+def test_pipelined_decode_matches_sequential_steps(plan_stream):
     """Scoring of step t + 1 on a side stream, overlapped with attention of
-    step t, gives bit-identical outputs and state to the plain step order."""
+    step t (and, with plan_stream, select + plan on a third stream), gives
+    bit-identical outputs and state to the plain step order."""
     wl = wlm.small_workload(batch=4, q_heads=32, kv_heads=8, head_dim=128,
                             ctx=(8192, 6000, 4096, 7000), budget=1024, n_hot=24, ratio=0.05, seed=43)
     d = wlm.make_layer(wl)
@@ -422,7 +424,7 @@ def test_pipelined_decode_matches_sequential_steps():
     seq.score(looks[T])
     seq.select_plan(T)
     pipe_layer = _gpu_layer(wl, d, wl.cap(), sb, lu)
-    pipe = PipelinedDecode(pipe_layer)
+    pipe = PipelinedDecode(pipe_layer, plan_stream=torch.cuda.Stream() if plan_stream else None)
     pipe.prime(looks[0], 0)
     got = [pipe.step(q, looks[t + 1], t) for t in range(T)]
     pipe.drain()

@@ -65,6 +65,53 @@ def test_pool_keys_exact(name):
 
 
 @pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("n_look", [1, 3])
+def test_score_with_refresh_after_append(head_dim, n_look):
+    # the scorer's own refresh of the last block: the compressed keys it
+    # leaves and the scores it writes equal pooling everything afresh
+    wl = wlm.small_workload(batch=3, ctx=(1000, 768, 47), head_dim=head_dim, n_look=n_look,
+                            n_hot=2, seed=47)
+    d = wlm.make_layer(wl)
+    ck = gpu_pool(d, wl)
+    gen = torch.Generator().manual_seed(48)
+    K, k_pool = d["K"].clone(), d["k_pool"].clone()
+    new_ctx = d["ctx_len"].clone() + 1
+    for b in range(wl.batch):
+        t = int(d["ctx_len"][b])
+        tok = torch.randn((wl.num_kv_heads, head_dim), generator=gen).to(torch.bfloat16) * 3
+        K[b, :, t] = tok
+        k_pool[int(d["block_table"][b, t // 16]), :, t % 16] = tok
+    scores = torch.full((wl.batch, wl.num_kv_heads, wl.table_width), 7.0, device=DEV)
+    ops.score_blocks_minmax(dev(d["q_look"]), ck, dev(new_ctx), scores, k_pool=dev(k_pool),
+                            block_table=dev(d["block_table"]))
+    torch.cuda.synchronize()
+    check_pooled(ck, K, new_ctx, wl.table_width, f"refresh D{head_dim}")
+    ck_o = orc.pool_keys(K, new_ctx, 16, wl.table_width)
+    want = orc.score_minmax(d["q_look"], ck_o, new_ctx, 16)
+    got = scores.cpu().double().numpy()
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            tol = minmax_tolerance(group_rows(d["q_look"], b, g, wl.group), ck_o[b, g],
+                                   int(new_ctx[b]), 16)
+            check_scores(got[b, g], want[b, g], tol, f"refresh b{b} g{g}")
+
+
+def test_score_refresh_of_out_of_range_page():
+    wl = wlm.small_workload(batch=1, ctx=(645,), seed=49)
+    d = wlm.make_layer(wl)
+    ck = gpu_pool(d, wl)
+    bt = d["block_table"].clone()
+    bt[0, 40] = -3                                # block 40 is the last one (ctx 645)
+    scores = torch.empty((1, wl.num_kv_heads, wl.table_width), device=DEV)
+    ops.score_blocks_minmax(dev(d["q_look"]), ck, dev(d["ctx_len"]), scores, k_pool=dev(d["k_pool"]),
+                            block_table=dev(bt))
+    got = scores.cpu().numpy()
+    assert np.all(np.isneginf(got[0, :, 40])) and np.all(np.isfinite(got[0, :, :40]))
+    f = ck.float().cpu()
+    assert torch.all(f[0, :, 40, 0] == float("inf")) and torch.all(f[0, :, 40, 1] == -float("inf"))
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
 def test_pool_keys_last_block_after_append(head_dim):
     # 1000 -> 1001 appends inside a partial block; 768 -> 769 opens a new block
     wl = wlm.small_workload(ctx=(1000, 768), head_dim=head_dim, seed=44)
@@ -261,5 +308,56 @@ def test_minmax_decode_steps_with_appends():
             v_pool[page, :, :, t % 16] = dev(vt)
         ctx += 1
         ctx_dev.copy_(dev(ctx))
-        layer.append()
+        if step % 2:
+            layer.append()                                    # a separate refresh launch
+        else:
+            layer.score(dev(q_look), refresh=True)            # the scorer's own refresh
     assert exempt <= len(rows) * 5 // 4
+
+
+def test_layers_with_plan_stream_match_sequential_steps():
+    """Two layers taking turns through pipelines that share a scoring stream
+    and a select + plan stream, with the compressed scorer refreshing the last
+    block in each scoring launch: outputs and state equal the plain order."""
+    from lookahead_sparse_kv_amd.pipeline import DecodeLayer, PipelinedDecode
+    wl = wlm.small_workload(batch=2, q_heads=16, kv_heads=4, head_dim=128, ctx=(5000, 3333),
+                            budget=512, n_hot=12, ratio=0.1, seed=63)
+    ds = [wlm.make_layer(wl, seed=wl.seed + 7 * i) for i in range(2)]
+    T = 5
+
+    def make(d):
+        return DecodeLayer(k_pool=dev(d["k_pool"]), v_pool=dev(d["v_pool"]),
+                           block_table=dev(d["block_table"]), ctx_len=dev(d["ctx_len"]),
+                           num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks, cap=wl.cap(),
+                           scorer="minmax")
+    looks = [[dev(wlm.draw_lookahead(wl, d["q32"], 400 + t).to(torch.bfloat16)) for t in range(T + 1)]
+             for d in ds]
+    qs = [dev(d["q"].unsqueeze(1)) for d in ds]
+    seq = [make(d) for d in ds]
+    want = [[], []]
+    for t in range(T):
+        for i, L in enumerate(seq):
+            L.score(looks[i][t], refresh=True)
+            L.select_plan(t)
+            L.attend(qs[i])
+            want[i].append(L.out.clone())
+    for i, L in enumerate(seq):              # the pipeline has also planned step T
+        L.score(looks[i][T], refresh=True)
+        L.select_plan(T)
+    side, ps = torch.cuda.Stream(), torch.cuda.Stream()
+    layers = [make(d) for d in ds]
+    pipes = [PipelinedDecode(L, side=side, plan_stream=ps) for L in layers]
+    for i, P in enumerate(pipes):
+        P.prime(looks[i][0], 0, append=True)
+    got = [[], []]
+    for t in range(T):
+        for i, P in enumerate(pipes):
+            got[i].append(P.step(qs[i], looks[i][t + 1], t, append=True))
+    for P in pipes:
+        P.drain()
+    torch.cuda.synchronize()
+    for i in range(2):
+        for t in range(T):
+            assert torch.equal(got[i][t], want[i][t]), (i, t)
+        assert torch.equal(layers[i].slot_block, seq[i].slot_block)
+        assert torch.equal(layers[i].last_use, seq[i].last_use)
