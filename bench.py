@@ -184,7 +184,7 @@ def percentiles_us(sorted_ms):
     return {"p10": pick(0.1), "median": pick(0.5), "p90": pick(0.9)}
 
 
-def host_tier_layers(wl, ratio, n_layers, dev):
+def host_tier_layers(wl, ratio, n_layers, dev, n_q=1):
     """Per layer: seeded inputs, a pinned host pool with the full K and V, the
     device key copy for scoring, and the working set; returns (layers, pools,
     true queries, lookahead draws per layer, previous-step lookahead per layer)."""
@@ -207,9 +207,10 @@ def host_tier_layers(wl, ratio, n_layers, dev):
             ctx_len=d["ctx_len"].to(dev), host_pool_k_dev=pool.device_ptr,
             host_pool_v_dev=pool.device_ptr + 2 * n, host_blocks=W,
             ws_page_table=pt.to(torch.int32).view(B, K).to(dev), num_q_heads=wl.num_q_heads,
-            k_blocks=K, cap=wl.cap(ratio), n_look=wl.n_look))
+            k_blocks=K, cap=wl.cap(ratio), n_look=wl.n_look, n_q=n_q))
         pools.append(pool)
-        qs.append(d["q"].unsqueeze(1).to(dev))
+        # n_q > 1: the normal query followed by the draft queries, attended together
+        qs.append(torch.cat([d["q"].unsqueeze(1), d["q_look"]], dim=1)[:, :n_q].to(dev))
         looks.append([wlm.draw_lookahead(wl, d["q32"], wl.seed + 100 + i).to(torch.bfloat16).to(dev)
                       for i in range(N_LOOK_DRAWS)])
         prevs.append(wlm.draw_lookahead(wl, d["q32"], wl.seed + 1).to(torch.bfloat16).to(dev))
@@ -288,7 +289,9 @@ def bench_ratio_sweep(args, wl):
     import torch
     dev = torch.device("cuda:0")
     out = {}
-    layers, pools, qs, looks, prevs = host_tier_layers(wl, wl.ratios[0], 1, dev)
+    # attention takes the normal query and the draft queries together (one pass)
+    n_q = 1 + wl.n_look
+    layers, pools, qs, looks, prevs = host_tier_layers(wl, wl.ratios[0], 1, dev, n_q=n_q)
     L = layers[0]
     tile = 16 * wl.head_dim * 2 * 2
     for ratio in wl.ratios:
@@ -302,6 +305,20 @@ def bench_ratio_sweep(args, wl):
                            "ms_per_step": round(ms_step, 4), "fetched_GB_per_step": round(gb, 5),
                            "fetch_GBps": round(gb / (fetch_ms * 1e-3), 2) if fetch_ms > 0 else None}
     best = max(v["seq_steps_per_s"] for v in out.values())
+    # attention alone over the same working set: the normal query only, and
+    # the normal query with the draft queries in one pass
+    attn_us = {}
+    for k, qq in (("normal only (n_q=1)", qs[0][:, :1].contiguous()),
+                  (f"normal + {wl.n_look} drafts (n_q={n_q})", qs[0])):
+        for _ in range(3):
+            L.attend(qq)
+        e0, e1 = _ev(), _ev()
+        e0.record()
+        for _ in range(args.steps):
+            L.attend(qq)
+        e1.record()
+        torch.cuda.synchronize()
+        attn_us[k] = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
     return {
         "metric": "seq-decode-steps/s per fetch ratio, 4 draft lookahead queries, host-pool tier",
         "value": best, "unit": "seq-decode-steps/s", "n_gpus": 1, "steps": args.steps,
@@ -309,8 +326,10 @@ def bench_ratio_sweep(args, wl):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "n_look": wl.n_look,
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
-                   "context": wl.ctx_max, "k_blocks": wl.k_blocks},
+                   "context": wl.ctx_max, "k_blocks": wl.k_blocks,
+                   "attention_query_rows": f"normal + {wl.n_look} drafts"},
         "per_ratio": out,
+        "attention_back_to_back_us": attn_us,
     }
 
 

@@ -222,8 +222,13 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
  * full-pool mode passes the block table as page_table and the selected (or
  * resident) logical blocks as both blk and blk_logical; working-set mode
  * passes the slot -> page table and blk = NULL, blk_logical = slot_block.
+ * The n_q query rows of a sequence are independent: with the normal query
+ * and the draft queries of a speculative step as rows i = 0 .. n_q - 1, one
+ * call attends them all in a single pass over the sparse KV (Figure 7
+ * caption: the attention kernel takes the normal and the draft queries
+ * together).
  * A row with no valid token outputs zeros.  bf16 in and out, fp32 softmax and
- * accumulation.  Requires D in {64, 128}, bs = 16, 1 <= n_q, n_q * G <= 16,
+ * accumulation.  Requires D in {64, 128}, bs = 16, 1 <= n_q, n_q * G <= 32,
  * n_blk >= 1, scale > 0, and workspace_bytes >= oasis_attn_workspace_bytes().
  */
 int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_q,

@@ -243,9 +243,9 @@ int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_
     if (n_q < 1) return fail(OASIS_ERR_INVALID, "%s: n_q %d < 1", fn, n_q);
     if (n_blk < 1) return fail(OASIS_ERR_INVALID, "%s: n_blk %d < 1", fn, n_blk);
     const int G = s->num_q_heads / s->num_kv_heads;
-    if ((long long)n_q * G > oasis::kMaxRowsQ)
+    if ((long long)n_q * G > oasis::kMaxAttnRowsQ)
         return fail(OASIS_ERR_UNSUPPORTED, "%s: n_q * group = %lld above %d", fn,
-                    (long long)n_q * G, oasis::kMaxRowsQ);
+                    (long long)n_q * G, oasis::kMaxAttnRowsQ);
     if (!(scale > 0.f) || !isfinite(scale))
         return fail(OASIS_ERR_INVALID, "%s: scale must be finite and > 0", fn);
     if (s->batch == 0) return ok();

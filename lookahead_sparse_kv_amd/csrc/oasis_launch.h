@@ -104,7 +104,8 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_
 void attn_split_plan(int rows, int n_blk, int *splits, int *per_split);
 
 constexpr int kBlockTokens = 16;   // tokens per KV block
-constexpr int kMaxRowsQ = 16;     // lookahead / query rows per KV head in one MFMA tile
+constexpr int kMaxRowsQ = 16;     // lookahead rows per KV head in one MFMA tile (scoring)
+constexpr int kMaxAttnRowsQ = 32; // query rows per KV head in attention (two MFMA tiles)
 constexpr int kMaxKBlocks = 1024; // K limit of select / plan
 constexpr int kRowSelectMaxWidth = 8192;  // widest table the 256-thread select keeps in LDS
 constexpr int kFusedMaxWidth = 4096;      // fused select + plan: table width limit

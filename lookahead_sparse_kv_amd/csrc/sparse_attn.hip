@@ -72,37 +72,44 @@ __device__ __forceinline__ uint32_t pair_mask(int t0, int nt) {
     return (t0 < nt ? 0x0000ffffu : 0u) | (t0 + 1 < nt ? 0xffff0000u : 0u);
 }
 
-template <int D>
+// Running softmax state of a wave, per 16-column tile nt of query rows.
+template <int D, int NT>
 struct WaveAcc {
-    float m_run;          // running max of column r16 (log2 units)
-    float l_run;          // this lane's share of the column's running sum
-    f32x4 o[D / 16];      // O^T rows 16*mt + 4*j4 + i of column r16
+    float m_run[NT];          // running max of column r16 (log2 units)
+    float l_run[NT];          // this lane's share of the column's running sum
+    f32x4 o[NT][D / 16];      // O^T rows 16*mt + 4*j4 + i of column r16
 };
 
-// B operand of QK^T: query row r16 = (query i, head g*G + hr), dims 32*kk + 8*j4 .. +8.
-template <int D>
-__device__ __forceinline__ void load_query(const AttnArgs &a, int b, int g, bf16x8 (&qv)[D / 32]) {
+// B operand of QK^T, tile nt: query row c = 16*nt + r16 = (query i, head
+// g*G + hr), dims 32*kk + 8*j4 .. +8; rows past n_rows_q are zero.
+template <int D, int NT>
+__device__ __forceinline__ void load_query(const AttnArgs &a, int b, int g,
+                                           bf16x8 (&qv)[NT][D / 32]) {
     const int lane = threadIdx.x & (kWave - 1);
     const int r16 = lane & 15;
     const int j4 = lane >> 4;
-    if (r16 < a.n_rows_q) {
-        const int iq = r16 / a.group;
-        const int hr = r16 - iq * a.group;
-        const uint16_t *qp =
-            a.q + (((size_t)b * a.n_q + iq) * a.hq + (size_t)g * a.group + hr) * D + 8 * j4;
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) qv[kk] = as_bf16x8(load_u32x4(qp + 32 * kk));
-    } else {
+    for (int nt = 0; nt < NT; ++nt) {
+        const int c = 16 * nt + r16;
+        if (c < a.n_rows_q) {
+            const int iq = c / a.group;
+            const int hr = c - iq * a.group;
+            const uint16_t *qp =
+                a.q + (((size_t)b * a.n_q + iq) * a.hq + (size_t)g * a.group + hr) * D + 8 * j4;
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) qv[kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+            for (int kk = 0; kk < D / 32; ++kk) qv[nt][kk] = as_bf16x8(load_u32x4(qp + 32 * kk));
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) qv[nt][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        }
     }
 }
 
 // Accumulate list entries [e0, e0 + ne) (ne <= 64) of row (b, g) into acc.
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int b, int g,
-                                                int e0, int ne, const bf16x8 (&qv)[D / 32],
-                                                WaveAcc<D> &acc) {
+                                                int e0, int ne, const bf16x8 (&qv)[NT][D / 32],
+                                                WaveAcc<D, NT> &acc) {
     constexpr int KK = D / 32;
     constexpr int MT = D / 16;
     const int lane = threadIdx.x & (kWave - 1);
@@ -110,9 +117,6 @@ __device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int 
     const int j4 = lane >> 4;
     const int ctx = a.ctx_len[b];
     const float NEG_INF = -__builtin_inff();
-    float &m_run = acc.m_run;
-    float &l_run = acc.l_run;
-    f32x4 (&o)[MT] = acc.o;
 
     // Entry e0 + lane: its page and number of valid tokens (page -1 = skip).
     int my_page = -1, my_ntok = 0;
@@ -145,64 +149,69 @@ __device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int 
 #pragma unroll
     for (int u = 0; u < 2; ++u) load_block<D>(cur[u], tile(a.k_pool, u), tile(a.v_pool, u), koff, voff);
     for (int i = 0; i < ne; i += 2) {
-        int nt[2];
+        int ntok[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            nt[u] = (i + u < ne && readlane_i(my_page, i + u) >= 0) ? readlane_i(my_ntok, i + u) : 0;
+            ntok[u] = (i + u < ne && readlane_i(my_page, i + u) >= 0) ? readlane_i(my_ntok, i + u) : 0;
             load_block<D>(nxt[u], tile(a.k_pool, i + 2 + u), tile(a.v_pool, i + 2 + u), koff, voff);
         }
-        if (nt[0] + nt[1] > 0) {
-            float x[2][4];
-            float mb = NEG_INF;
+        if (ntok[0] + ntok[1] > 0) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) s = mfma16x16x32(as_bf16x8(cur[u].k[kk]), qv[kk], s);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    x[u][t] = (4 * j4 + t < nt[u]) ? s[t] * a.scale_log2 : NEG_INF;
-                    mb = fmaxf(mb, x[u][t]);
-                }
-            }
-            mb = fmaxf(mb, shfl_xor_f(mb, 16));
-            mb = fmaxf(mb, shfl_xor_f(mb, 32));
-            const float m_new = fmaxf(m_run, mb);   // finite: the pair has a valid token
-            const float alpha = exp2f(m_run - m_new);
-            uint32_t pw[2][2];
-            float psum = 0.f;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                pw[u][0] = pack_bf16x2(exp2f(x[u][0] - m_new), exp2f(x[u][1] - m_new));
-                pw[u][1] = pack_bf16x2(exp2f(x[u][2] - m_new), exp2f(x[u][3] - m_new));
-                // the normaliser sums the same bf16-rounded weights the MFMA uses
-                psum += bf16_bits_to_float(pw[u][0] & 0xffffu) + bf16_bits_to_float(pw[u][0] >> 16) +
-                        bf16_bits_to_float(pw[u][1] & 0xffffu) + bf16_bits_to_float(pw[u][1] >> 16);
-                if (nt[u] < kBlockTokens) {
+                if (ntok[u] < kBlockTokens) {
                     // zero the values of tokens past the context so that whatever the
                     // page holds there cannot reach O (0 * NaN would)
-                    const uint32_t k01 = pair_mask(4 * j4, nt[u]);
-                    const uint32_t k23 = pair_mask(4 * j4 + 2, nt[u]);
+                    const uint32_t k01 = pair_mask(4 * j4, ntok[u]);
+                    const uint32_t k23 = pair_mask(4 * j4 + 2, ntok[u]);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) { cur[u].v[mt].x &= k01; cur[u].v[mt].y &= k23; }
                 }
             }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            // O^T += V^T P over the pair's 32 tokens: reduction index 8*j4 + i is
-            // token 4*j4 + i of the first block (i < 4) or of the second (i >= 4).
-            const bf16x8 pb = as_bf16x8(u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]});
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                o[mt] *= alpha;
-                const u32x4 va = {cur[0].v[mt].x, cur[0].v[mt].y, cur[1].v[mt].x, cur[1].v[mt].y};
-                o[mt] = mfma16x16x32(as_bf16x8(va), pb, o[mt]);
+            for (int t = 0; t < NT; ++t) {
+                float x[2][4];
+                float mb = NEG_INF;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk) s = mfma16x16x32(as_bf16x8(cur[u].k[kk]), qv[t][kk], s);
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        x[u][q4] = (4 * j4 + q4 < ntok[u]) ? s[q4] * a.scale_log2 : NEG_INF;
+                        mb = fmaxf(mb, x[u][q4]);
+                    }
+                }
+                mb = fmaxf(mb, shfl_xor_f(mb, 16));
+                mb = fmaxf(mb, shfl_xor_f(mb, 32));
+                const float m_new = fmaxf(acc.m_run[t], mb);   // finite: the pair has a valid token
+                const float alpha = exp2f(acc.m_run[t] - m_new);
+                uint32_t pw[2][2];
+                float psum = 0.f;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    pw[u][0] = pack_bf16x2(exp2f(x[u][0] - m_new), exp2f(x[u][1] - m_new));
+                    pw[u][1] = pack_bf16x2(exp2f(x[u][2] - m_new), exp2f(x[u][3] - m_new));
+                    // the normaliser sums the same bf16-rounded weights the MFMA uses
+                    psum += bf16_bits_to_float(pw[u][0] & 0xffffu) + bf16_bits_to_float(pw[u][0] >> 16) +
+                            bf16_bits_to_float(pw[u][1] & 0xffffu) + bf16_bits_to_float(pw[u][1] >> 16);
+                }
+                acc.l_run[t] = acc.l_run[t] * alpha + psum;
+                acc.m_run[t] = m_new;
+                // O^T += V^T P over the pair's 32 tokens: reduction index 8*j4 + i is
+                // token 4*j4 + i of the first block (i < 4) or of the second (i >= 4).
+                const bf16x8 pb = as_bf16x8(u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]});
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc.o[t][mt] *= alpha;
+                    const u32x4 va = {cur[0].v[mt].x, cur[0].v[mt].y, cur[1].v[mt].x, cur[1].v[mt].y};
+                    acc.o[t][mt] = mfma16x16x32(as_bf16x8(va), pb, acc.o[t][mt]);
+                }
             }
         }
         cur[0] = nxt[0];
         cur[1] = nxt[1];
     }
-
 }
 
 // Output element (c, d) of row `row` from the partials of its splits, taken
@@ -250,8 +259,10 @@ __device__ __forceinline__ void merge_one(const AttnArgs &a, int row, int c, int
         (uint16_t)float_to_bf16_bits(res);
 }
 
-template <int D>
-__global__ __launch_bounds__(kAttnWaves * kWave, 2) void attn_partial_kernel(AttnArgs a) {
+// NT = 1: up to 16 query rows per KV head; NT = 2: up to 32 (the normal and
+// the draft queries together), at one wave per SIMD for the registers.
+template <int D, int NT>
+__global__ __launch_bounds__(kAttnWaves * kWave, NT == 1 ? 2 : 1) void attn_partial_kernel(AttnArgs a) {
     constexpr int MT = D / 16;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps row indices scalar
@@ -267,29 +278,34 @@ __global__ __launch_bounds__(kAttnWaves * kWave, 2) void attn_partial_kernel(Att
     const int e0 = split * a.per_split;
     int ne = a.n_blk - e0;
     ne = ne < a.per_split ? ne : a.per_split;
-    const bool col_ok = r16 < a.n_rows_q;
-    bf16x8 qv[D / 32];
-    load_query<D>(a, b, g, qv);
-    WaveAcc<D> acc;
-    acc.m_run = -__builtin_inff();
-    acc.l_run = 0.f;
+    bf16x8 qv[NT][D / 32];
+    load_query<D, NT>(a, b, g, qv);
+    WaveAcc<D, NT> acc;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    attn_wave_range<D>(a, row, b, g, e0, ne, qv, acc);
-    float m_run = acc.m_run, l_run = acc.l_run;
-    f32x4 (&o)[MT] = acc.o;
+    for (int t = 0; t < NT; ++t) {
+        acc.m_run[t] = -__builtin_inff();
+        acc.l_run[t] = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc.o[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    attn_wave_range<D, NT>(a, row, b, g, e0, ne, qv, acc);
 
-    // Column totals of the normaliser live in lanes r16, r16+16, r16+32, r16+48.
-    l_run += shfl_xor_f(l_run, 16);
-    l_run += shfl_xor_f(l_run, 32);
-    if (col_ok) {
-        const size_t slot = ((size_t)row * a.splits + split) * a.n_rows_q + r16;
-        float *po = a.part_o + slot * D + 4 * j4;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4 *>(po + 16 * mt) = o[mt];
-        if (j4 == 0) {
-            a.part_ml[2 * slot] = m_run;
-            a.part_ml[2 * slot + 1] = l_run;
+    for (int t = 0; t < NT; ++t) {
+        // Column totals of the normaliser live in lanes r16, r16+16, r16+32, r16+48.
+        float l_run = acc.l_run[t];
+        l_run += shfl_xor_f(l_run, 16);
+        l_run += shfl_xor_f(l_run, 32);
+        const int c = 16 * t + r16;
+        if (c < a.n_rows_q) {
+            const size_t slot = ((size_t)row * a.splits + split) * a.n_rows_q + c;
+            float *po = a.part_o + slot * D + 4 * j4;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4 *>(po + 16 * mt) = acc.o[t][mt];
+            if (j4 == 0) {
+                a.part_ml[2 * slot] = acc.m_run[t];
+                a.part_ml[2 * slot + 1] = l_run;
+            }
         }
     }
 }
@@ -308,11 +324,14 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_
     const long long waves = (long long)rows * a.splits;
     dim3 grid((unsigned)((waves + kAttnWaves - 1) / kAttnWaves));
     dim3 block(kAttnWaves * kWave);
+    const bool two = a.n_rows_q > 16;
     if (head_dim == 128) {
-        hipLaunchKernelGGL(attn_partial_kernel<128>, grid, block, 0, stream, a);
+        if (two) hipLaunchKernelGGL((attn_partial_kernel<128, 2>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_partial_kernel<128, 1>), grid, block, 0, stream, a);
         hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(rows * a.n_rows_q), dim3(128), 0, stream, a);
     } else {
-        hipLaunchKernelGGL(attn_partial_kernel<64>, grid, block, 0, stream, a);
+        if (two) hipLaunchKernelGGL((attn_partial_kernel<64, 2>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_partial_kernel<64, 1>), grid, block, 0, stream, a);
         hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(rows * a.n_rows_q), dim3(64), 0, stream, a);
     }
     return hipGetLastError();

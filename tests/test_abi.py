@@ -118,7 +118,7 @@ def test_attn_workspace_and_argument_checks():
         ctypes.byref(s), P, n_q, P, P, P, blk, n_blk, blk, P, 0.088, P, wsp, wsb, None)
     assert att(wsb=ws - 4) == ops.OASIS_ERR_NOMEM
     assert att(wsp=None) == ops.OASIS_ERR_NOMEM
-    assert att(n_q=5) == ops.OASIS_ERR_UNSUPPORTED      # 5 * 4 rows > 16
+    assert att(n_q=9) == ops.OASIS_ERR_UNSUPPORTED      # 9 * 4 rows > 32
     assert att(n_blk=0) == ops.OASIS_ERR_INVALID
     assert att(blk=None) == ops.OASIS_ERR_INVALID       # blk and blk_logical both NULL
     assert att(wsp=ctypes.c_void_p(24)) == ops.OASIS_ERR_INVALID  # misaligned workspace

@@ -225,6 +225,15 @@ ATTN_CASES = {
     "d128_g4_nq4": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 300)), 4, 19, 0.3),
     "d128_one_block": (dict(batch=3, q_heads=8, kv_heads=2, head_dim=128, ctx=(16, 5, 4096)), 1, 1, 0.0),
     "d128_all_empty_rows": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(600, 600)), 1, 9, 1.0),
+    # normal + draft queries together: more than 16 query rows per KV head (two MFMA tiles)
+    "d128_g4_nq5_normal_and_4_drafts": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128,
+                                             ctx=(4096, 3000)), 5, 128, 0.1),
+    "d64_g16_nq2_32_rows": (dict(batch=2, q_heads=32, kv_heads=2, head_dim=64, ctx=(1000, 777)),
+                            2, 33, 0.2),
+    "d128_g8_nq3_24_rows": (dict(batch=2, q_heads=16, kv_heads=2, head_dim=128, ctx=(2000, 161)),
+                            3, 40, 0.0),
+    "d128_g4_nq8_32_rows_short": (dict(batch=3, q_heads=8, kv_heads=2, head_dim=128,
+                                       ctx=(16, 5, 700)), 8, 3, 0.0),
 }
 
 
@@ -649,3 +658,30 @@ def test_four_draft_queries_sampled_rows():
         layer.step(dev(q_look), dev(q), step)
         torch.cuda.synchronize()
         _check_step_rows(wl, d, layer, q_look, q, sb0, lu0, cap, step, rows, "spec4")
+
+
+def test_normal_and_draft_queries_full_size_sampled_rows():
+    """16 x 32K, Qwen3-8B shape: the normal query and four draft queries of
+    each sequence (20 query rows per KV head) attended in one call over
+    128-block working sets; sampled rows against the oracle query by query."""
+    wl = wlm.WORKLOADS["qwen3_8b_32k_spec4"]
+    d = wlm.make_layer(wl)
+    q_all = torch.cat([d["q"].unsqueeze(1), d["q_look"]], dim=1)        # [B][5][Hq][D]
+    n_q = q_all.shape[1]
+    rng = np.random.default_rng(71)
+    lists = _random_lists(rng, wl, wl.k_blocks, 0.0)
+    shape = ops.make_shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.table_width,
+                           wl.num_pages)
+    ws = torch.zeros(ops.attn_workspace_bytes(shape, n_q, wl.k_blocks) // 4 + 4, device=DEV)
+    out = torch.empty((wl.batch, n_q, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device=DEV)
+    g_lists = dev(torch.from_numpy(lists))
+    ops.sparse_decode_attn(shape, dev(q_all), dev(d["k_pool"]), dev(d["v_pool"]), dev(d["block_table"]),
+                           g_lists, g_lists, dev(d["ctx_len"]), out, ws)
+    got = out.float().cpu().numpy()
+    G = wl.group
+    for b, g in [(0, 0), (15, 7), (7, 3), (11, 5)]:
+        for i in range(n_q):
+            want = orc.attn_row(q_all[b, i, g * G:(g + 1) * G], d["K"][b, g], d["V"][b, g], wl.ctx[b],
+                                16, lists[b, g])
+            err = np.abs(got[b, i, g * G:(g + 1) * G] - want).max()
+            assert err <= ATTN_ATOL, (b, g, i, err)
