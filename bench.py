@@ -202,9 +202,18 @@ def host_tier_layers(wl, ratio, n_layers, dev, n_q=1):
         pool.tensor((B, Hkv, W, D, 16), torch.bfloat16, offset_bytes=2 * n).copy_(
             d["V"].view(B, Hkv, W, 16, D).transpose(-1, -2))
         pt = torch.randperm(B * K, generator=torch.Generator().manual_seed(wl.seed + l))
+        k_dev, ck = d["k_pool"].to(dev), None
+        bt_dev, ctx_dev = d["block_table"].to(dev), d["ctx_len"].to(dev)
+        if wl.scorer == "minmax":
+            # the compressed keys are pooled once from a temporary device copy
+            # of the keys (prefill work), which is then released
+            ck = torch.empty((B, Hkv, W, 2, D), dtype=torch.bfloat16, device=dev)
+            ops.pool_keys(k_dev, bt_dev, ctx_dev, ck, num_q_heads=wl.num_q_heads)
+            torch.cuda.synchronize()
+            k_dev = None
         layers.append(HostTierLayer(
-            k_pool=d["k_pool"].to(dev), block_table=d["block_table"].to(dev),
-            ctx_len=d["ctx_len"].to(dev), host_pool_k_dev=pool.device_ptr,
+            k_pool=k_dev, ck=ck, block_table=bt_dev,
+            ctx_len=ctx_dev, host_pool_k_dev=pool.device_ptr,
             host_pool_v_dev=pool.device_ptr + 2 * n, host_blocks=W,
             ws_page_table=pt.to(torch.int32).view(B, K).to(dev), num_q_heads=wl.num_q_heads,
             k_blocks=K, cap=wl.cap(ratio), n_look=wl.n_look, n_q=n_q))
@@ -264,8 +273,13 @@ def bench_hostpool(args, wl):
     tile = 16 * wl.head_dim * 2 * 2                       # K + V of one block, one head
     blocks = sum(counts) / len(counts)
     gb_step = blocks * tile / 1e9
+    # HBM held per layer by what scoring reads and by the working set
+    L0 = layers[0]
+    scoring_bytes = (L0.ck.numel() * 2 if L0.ck is not None else L0.k_pool.numel() * 2)
+    ws_bytes = (L0.ws_k.numel() + L0.ws_v.numel()) * 2
     return {
-        "metric": "seq-decode-steps/s over all layers, host-pool KV tier with capped fetch",
+        "metric": ("seq-decode-steps/s over all layers, host-pool KV tier with capped fetch"
+                   + (", compressed-key scoring" if wl.scorer == "minmax" else "")),
         "value": round(wl.batch / (ms_step * 1e-3), 1), "unit": "seq-decode-steps/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -273,8 +287,10 @@ def bench_hostpool(args, wl):
         "config": {"workload": wl.name, "layers": n_layers, "batch": wl.batch,
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "context": wl.ctx_max, "k_blocks": wl.k_blocks,
-                   "fetch_ratio": wl.ratios[0], "cap": wl.cap(),
+                   "fetch_ratio": wl.ratios[0], "cap": wl.cap(), "scorer": wl.scorer,
                    "host_pool_GiB": round(sum(p.nbytes for p in pools) / 2 ** 30, 2)},
+        "hbm_per_layer_GiB": {"scoring": round(scoring_bytes / 2 ** 30, 3),
+                              "working_set": round(ws_bytes / 2 ** 30, 3)},
         "ms_per_layer": round(ms_step / n_layers, 4),
         "fetched_blocks_per_step": blocks, "fetched_GB_per_step": round(gb_step, 5),
         "fetch_kernel_ms_per_step": round(fetch_ms, 4),
@@ -392,7 +408,9 @@ def main():
 
     ops.lib()          # fail loudly before any work if the HIP library is missing
     wl = wlm.WORKLOADS[args.workload]
-    other = {"qwen3_32b_32k_hostpool": bench_hostpool, "qwen3_8b_32k_spec4": bench_ratio_sweep,
+    other = {"qwen3_32b_32k_hostpool": bench_hostpool,
+             "qwen3_32b_32k_hostpool_minmax": bench_hostpool,
+             "qwen3_8b_32k_spec4": bench_ratio_sweep,
              "llama31_8b_128k_drift": bench_drift}
     if wl.name in other:
         print(json.dumps(other[wl.name](args, wl)), flush=True)

@@ -209,25 +209,37 @@ class PipelinedDecode:
 class HostTierLayer:
     """One layer whose full K and V live in a pinned host pool.
 
-    HBM holds the keys for scoring (exact scoring reads every key, so they stay
-    on the device) and, for attention, a bounded working set: K slots per
-    (sequence, KV head), in working-set pools addressed through a slot -> page
-    table.  The plan's capped fetch list is pulled from the host pool into the
-    slots by oasis_fetch_blocks (abstract: only the most relevant KV stays in
-    HBM; Figure 7 caption: CPU full KV cache and the GPU sparse working set;
-    Figure 9 caption: per-head working-set table).
+    HBM holds what scoring reads and, for attention, a bounded working set: K
+    slots per (sequence, KV head), in working-set pools addressed through a
+    slot -> page table.  The plan's capped fetch list is pulled from the host
+    pool into the slots by oasis_fetch_blocks (abstract: only the most
+    relevant KV stays in HBM; Figure 7 caption: CPU full KV cache and two GPU
+    caches, the compressed keys and the sparse working set; Figure 9 caption:
+    per-head working-set table).
+
+    What scoring reads: with the exact scorer (k_pool given) a device copy of
+    every key; with the compressed scorer (ck given, k_pool None) only the
+    min/max-pooled keys, 1/8 of that.
     """
 
-    def __init__(self, *, k_pool, block_table, ctx_len, host_pool_k_dev, host_pool_v_dev,
-                 host_blocks, ws_page_table, num_q_heads, k_blocks, cap, n_look=1, n_q=1):
-        dev = k_pool.device
+    def __init__(self, *, k_pool=None, ck=None, block_table, ctx_len, host_pool_k_dev,
+                 host_pool_v_dev, host_blocks, ws_page_table, num_q_heads, k_blocks, cap,
+                 n_look=1, n_q=1):
+        if (k_pool is None) == (ck is None):
+            raise ValueError("give k_pool (exact scorer) or ck (compressed scorer), not both")
+        dev = (k_pool if k_pool is not None else ck).device
         B, W = block_table.shape
-        Hkv, D = k_pool.shape[1], k_pool.shape[-1]
-        self.k_pool, self.block_table, self.ctx_len = k_pool, block_table, ctx_len
+        if k_pool is not None:
+            Hkv, D = k_pool.shape[1], k_pool.shape[-1]
+        else:
+            Hkv, D = ck.shape[1], ck.shape[-1]
+        self.k_pool, self.ck = k_pool, ck
+        self.block_table, self.ctx_len = block_table, ctx_len
         self.host_k, self.host_v, self.host_blocks = host_pool_k_dev, host_pool_v_dev, host_blocks
         self.ws_page_table = ws_page_table
         ws_pages = int(ws_page_table.numel())
-        self.shape = ops.make_shape(B, num_q_heads, Hkv, D, W, k_pool.shape[0])
+        self.shape = ops.make_shape(B, num_q_heads, Hkv, D, W,
+                                    k_pool.shape[0] if k_pool is not None else 0)
         self.ws_shape = ops.make_shape(B, num_q_heads, Hkv, D, k_blocks, ws_pages)
         self.k_blocks, self.cap, self.n_look, self.n_q = k_blocks, cap, n_look, n_q
         i32 = dict(dtype=torch.int32, device=dev)
@@ -246,8 +258,11 @@ class HostTierLayer:
         self.workspace = torch.zeros((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
 
     def score(self, q_look, stream=None):
-        ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len, self.scores,
-                         stream=stream)
+        if self.ck is not None:
+            ops.score_blocks_minmax(q_look, self.ck, self.ctx_len, self.scores, stream=stream)
+        else:
+            ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len, self.scores,
+                             stream=stream)
 
     def select_plan(self, step, cap=None, stream=None):
         cap = self.cap if cap is None else cap

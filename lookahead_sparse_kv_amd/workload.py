@@ -112,6 +112,11 @@ WORKLOADS = {
     "qwen3_32b_32k_hostpool": Workload("qwen3_32b_32k_hostpool", 32, 64, 8, 128, (32768,) * 32,
                                        2048, n_hot=102, rhos=(0.9,), ratios=(0.05,), layers=4,
                                        seed=3000),
+    # the same, scored from min/max-pooled keys: no device copy of the keys
+    "qwen3_32b_32k_hostpool_minmax": Workload("qwen3_32b_32k_hostpool_minmax", 32, 64, 8, 128,
+                                              (32768,) * 32, 2048, n_hot=102, rhos=(0.9,),
+                                              ratios=(0.05,), layers=4, seed=3000,
+                                              scorer="minmax"),
     # Llama-3.1-8B-shaped long context with drifting hot blocks over 64 steps
     "llama31_8b_128k_drift": Workload("llama31_8b_128k_drift", 4, 32, 8, 128, (131072,) * 4,
                                       2048, n_hot=102, rhos=(0.9,), ratios=(0.02,), steps=64,

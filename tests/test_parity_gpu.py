@@ -369,11 +369,12 @@ def _check_step_rows(wl, d, layer, q_look, q, sb0, lu0, cap, step, rows, name):
     return n_exempt
 
 
-def _gpu_layer(wl, d, cap, sb, lu):
+def _gpu_layer(wl, d, cap, sb, lu, scorer="exact"):
     return DecodeLayer(k_pool=dev(d["k_pool"]), v_pool=dev(d["v_pool"]),
                        block_table=dev(d["block_table"]), ctx_len=dev(d["ctx_len"]),
                        num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks, cap=cap, n_look=wl.n_look,
-                       slot_block=torch.from_numpy(sb), last_use=torch.from_numpy(lu))
+                       slot_block=torch.from_numpy(sb), last_use=torch.from_numpy(lu),
+                       scorer=scorer)
 
 
 def test_decode_step_tiny_4k_empty_start():
@@ -539,11 +540,13 @@ def test_fetch_blocks_copies_listed_tiles_and_skips_bad_entries():
     del pool
 
 
-def test_host_tier_matches_full_pool_over_layers_and_steps():
+@pytest.mark.parametrize("scorer", ["exact", "minmax"])
+def test_host_tier_matches_full_pool_over_layers_and_steps(scorer):
     """Four steps of two layers with the full KV in pinned host pools, the
     capped fetch on a side stream overlapped with the next layer: outputs and
     plans are bit-identical to the full-pool path, and every resident slot
-    holds its block's K and V."""
+    holds its block's K and V.  With the compressed scorer the host-tier
+    layers hold no device copy of the keys, only the pooled ones."""
     from lookahead_sparse_kv_amd.pipeline import HostTierDecode, HostTierLayer
     wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 3000),
                             budget=512, n_hot=10, ratio=0.125, seed=51)
@@ -555,12 +558,16 @@ def test_host_tier_matches_full_pool_over_layers_and_steps():
         pool, hk, hv = _host_pool_for(d, wl)
         pools.append(pool)
         pt = torch.randperm(B * K, generator=torch.Generator().manual_seed(10 + l)).to(torch.int32).view(B, K)
-        host_layers.append(HostTierLayer(k_pool=dev(d["k_pool"]), block_table=dev(d["block_table"]),
+        sb, lu = (x.numpy() for x in wlm.empty_state(wl))
+        ref = _gpu_layer(wl, d, cap, sb, lu, scorer=scorer)
+        ref_layers.append(ref)
+        scoring = (dict(k_pool=dev(d["k_pool"])) if scorer == "exact"
+                   else dict(ck=ref.ck.clone()))      # pooled on the device from the key pool
+        host_layers.append(HostTierLayer(block_table=dev(d["block_table"]),
                                          ctx_len=dev(d["ctx_len"]), host_pool_k_dev=hk,
                                          host_pool_v_dev=hv, host_blocks=W, ws_page_table=dev(pt),
-                                         num_q_heads=wl.num_q_heads, k_blocks=K, cap=cap))
-        sb, lu = (x.numpy() for x in wlm.empty_state(wl))
-        ref_layers.append(_gpu_layer(wl, d, cap, sb, lu))
+                                         num_q_heads=wl.num_q_heads, k_blocks=K, cap=cap,
+                                         **scoring))
     prev = [dev(wlm.draw_lookahead(wl, d["q32"], 900 + l).to(torch.bfloat16)) for l, d in enumerate(datas)]
     looks = [[dev(wlm.draw_lookahead(wl, d["q32"], 1000 + 10 * t + l).to(torch.bfloat16))
               for l, d in enumerate(datas)] for t in range(T)]
