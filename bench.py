@@ -349,6 +349,66 @@ def bench_ratio_sweep(args, wl):
     }
 
 
+def bench_predictors(args, wl):
+    """Predictor study (Figure 4 caption's comparison; the compensatory fetch a
+    misprediction costs): over wl.steps steps of a drifting true query, the
+    previous token's query and the lookahead query each predict the next
+    step's top-K; the prefetch is capped, the true top-K's missing blocks are
+    then fetched on demand."""
+    import torch
+    from lookahead_sparse_kv_amd import study
+    from lookahead_sparse_kv_amd import workload as wlm
+    from lookahead_sparse_kv_amd.pipeline import DecodeLayer
+    dev = torch.device("cuda:0")
+    d = wlm.make_layer(wl)
+    g = {k: d[k].to(dev) for k in ("k_pool", "v_pool", "block_table", "ctx_len")}
+    T, K = wl.steps, wl.k_blocks
+    bf = torch.bfloat16
+    q32 = wlm.query_walk(wl, d["q32"], T, wl.seed + 50_000)            # q_0 .. q_T
+    true_q = [q32[t + 1].to(bf).unsqueeze(1).to(dev) for t in range(T)]
+    predictors = {
+        "previous_token": [q32[t].to(bf).unsqueeze(1).to(dev) for t in range(T)],
+        "lookahead": [wlm.draw_lookahead(wl, q32[t + 1], wl.seed + 60_000 + t).to(bf).to(dev)
+                      for t in range(T)],
+    }
+    tile = 16 * wl.head_dim * 2 * 2
+    out = {}
+    # each predictor with the workload's cap, and with no cap (every predicted
+    # miss prefetched): the second isolates the prediction from the cap
+    for cap_name, cap in (("cap", wl.cap()), ("no_cap", K)):
+        for name, pq in predictors.items():
+            L = DecodeLayer(k_pool=g["k_pool"], v_pool=g["v_pool"], block_table=g["block_table"],
+                            ctx_len=g["ctx_len"], num_q_heads=wl.num_q_heads, k_blocks=K, cap=K)
+            L.score(q32[0].to(bf).unsqueeze(1).to(dev))                  # step 0's working set
+            L.select_plan(-1)
+            torch.cuda.synchronize()
+            e0, e1 = _ev(), _ev()
+            e0.record()
+            res = study.run_predictor(L, pq, true_q, cap)
+            e1.record()
+            torch.cuda.synchronize()
+            key = name if cap_name == "cap" else f"{name}_{cap_name}"
+            out[key] = study.summarize(res, K, tile)
+            out[key]["cap"] = cap
+            out[key]["ms_per_step"] = round(e0.elapsed_time(e1) / T, 4)
+    return {
+        "metric": "top-K block prediction accuracy of the lookahead query (previous-token query "
+                  "beside it), with compensatory fetches, drifting query",
+        "value": out["lookahead"]["top_k_accuracy"], "unit": "fraction of the true top-K",
+        "n_gpus": 1, "steps": T, "warmup": 0, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.ctx_max,
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "k_blocks": K, "cap": wl.cap(),
+                   "query_persistent_share": wl.query_persist,
+                   "query_drift_step_correlation": wl.query_corr,
+                   "query_step_correlation": round(wl.query_persist
+                                                   + (1 - wl.query_persist) * wl.query_corr, 4),
+                   "lookahead_correlation": wl.rhos[0]},
+        "predictors": out,
+    }
+
+
 def bench_drift(args, wl):
     """Long context with hot blocks drifting every step (full KV in HBM):
     per-step time and fetched-block counts over wl.steps steps."""
@@ -411,6 +471,7 @@ def main():
     other = {"qwen3_32b_32k_hostpool": bench_hostpool,
              "qwen3_32b_32k_hostpool_minmax": bench_hostpool,
              "qwen3_8b_32k_spec4": bench_ratio_sweep,
+             "llama31_8b_128k_predictors": bench_predictors,
              "llama31_8b_128k_drift": bench_drift}
     if wl.name in other:
         print(json.dumps(other[wl.name](args, wl)), flush=True)

@@ -63,6 +63,8 @@ class Workload:
     seed: int = 0
     block_size: int = BLOCK_SIZE
     scorer: str = "exact"         # "exact" keys, or "minmax" compressed keys
+    query_corr: float = 1.0       # step-to-step correlation of the query's drifting part
+    query_persist: float = 0.0    # share of the query's variance that stays on the base query
 
     @property
     def group(self) -> int:
@@ -121,6 +123,13 @@ WORKLOADS = {
     "llama31_8b_128k_drift": Workload("llama31_8b_128k_drift", 4, 32, 8, 128, (131072,) * 4,
                                       2048, n_hot=102, rhos=(0.9,), ratios=(0.02,), steps=64,
                                       drift=4, seed=4000),
+    # predictor study on the 131K shape: half of the true query's variance stays
+    # on the base query, the rest drifts (0.6 per step), so consecutive queries
+    # correlate 0.8; previous-token query against the lookahead query (0.9)
+    "llama31_8b_128k_predictors": Workload("llama31_8b_128k_predictors", 4, 32, 8, 128,
+                                           (131072,) * 4, 2048, n_hot=102, rhos=(0.9,),
+                                           ratios=(0.02,), steps=64, query_corr=0.6,
+                                           query_persist=0.5, seed=6000),
     # Qwen3-8B shape with 4 draft lookahead queries, fetch ratio sweep
     "qwen3_8b_32k_spec4": Workload("qwen3_8b_32k_spec4", 16, 32, 8, 128, (32768,) * 16, 2048,
                                    n_hot=102, rhos=(0.95, 0.9, 0.85, 0.8),
@@ -307,6 +316,23 @@ def drift_hot(wl: Workload, hot: torch.Tensor, seed: int) -> torch.Tensor:
     new = torch.where(new < 0, -new, new)
     new = torch.where(new >= nb, 2 * (nb - 1) - new, new)
     return new
+
+
+def query_walk(wl: Workload, q32: torch.Tensor, steps: int, seed: int) -> list:
+    """True queries of consecutive decode steps, fp32 [B][Hq][D] each:
+    q_t = sqrt(p) * q32 + sqrt(1 - p) * r_t with p = wl.query_persist, where r is
+    a random walk with N(0, 1) marginals: r_{t+1} = a * r_t + sqrt(1 - a^2) * z_t,
+    a = wl.query_corr (r_0 = q32 when p = 0, else a fresh draw).  Consecutive
+    queries are correlated p + (1 - p) * a; the persistent part keeps the
+    blocks planted along q32 relevant."""
+    a, p = float(wl.query_corr), float(wl.query_persist)
+    r = q32 if p == 0.0 else torch.randn(q32.shape, generator=_gen(seed - 1), dtype=torch.float32)
+    qs = [p ** 0.5 * q32 + (1.0 - p) ** 0.5 * r]
+    for t in range(steps):
+        z = torch.randn(q32.shape, generator=_gen(seed + t), dtype=torch.float32)
+        r = a * r + (1.0 - a * a) ** 0.5 * z
+        qs.append(p ** 0.5 * q32 + (1.0 - p) ** 0.5 * r)
+    return qs
 
 
 def small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=64, ctx: Sequence[int] = (1000, 777),
