@@ -198,7 +198,8 @@ def host_tier_layers(wl, ratio, n_layers, dev, n_q=1):
         d = wlm.make_layer(wl, seed=wl.seed + 101 * l)
         n = B * Hkv * W * 16 * D
         pool = ops.HostPool(4 * n)
-        pool.tensor((B, Hkv, W, 16, D), torch.bfloat16).copy_(d["K"].view(B, Hkv, W, 16, D))
+        pool.tensor((B, Hkv, W, 16, D), torch.bfloat16).copy_(
+            wlm.key_tiles(d["K"].view(B, Hkv, W, 16, D)))
         pool.tensor((B, Hkv, W, D, 16), torch.bfloat16, offset_bytes=2 * n).copy_(
             d["V"].view(B, Hkv, W, 16, D).transpose(-1, -2))
         pt = torch.randperm(B * K, generator=torch.Generator().manual_seed(wl.seed + l))

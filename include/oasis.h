@@ -38,7 +38,11 @@
  * Layouts (row-major, innermost last):
  *  - lookahead queries  q_look  [B][n_look][Hq][D]    bf16
  *  - true queries       q       [B][n_q][Hq][D]       bf16
- *  - key pool           k_pool  [num_pages][Hkv][bs][D]  bf16 (token-major tile)
+ *  - key pool           k_pool  [num_pages][Hkv][bs*D]   bf16; each (page, head)
+ *                       tile in 8-dimension slices [D/8][bs][8]: element
+ *                       (token t, dim d) at ((d / 8) * bs + t) * 8 + d % 8, so a
+ *                       16-byte-per-lane load of an MFMA operand reads 1 KiB of
+ *                       contiguous memory
  *  - value pool         v_pool  [num_pages][Hkv][D][bs]  bf16 (dim-major tile)
  *  - block table        [B][table_width]  int32, logical block -> page
  *  - context lengths    ctx_len [B]       int32, tokens
@@ -260,10 +264,11 @@ int oasis_hostpool_destroy(void *host_ptr);
  * i < fetch_count[b][g] (clamped to [0, cap]), copies logical block
  * fetch_block[b][g][i] of the host pool into working-set slot
  * fetch_slot[b][g][i], i.e. into page ws_page_table[b][slot] of the working-set
- * pools, for KV head g.  Layouts: host_k [B][Hkv][host_blocks][bs][D] and
+ * pools, for KV head g.  Layouts: host_k [B][Hkv][host_blocks][bs*D] (tiles in
+ * the key pool's slice order) and
  * host_v [B][Hkv][host_blocks][D][bs] (device-mapped pointers from
  * oasis_hostpool_device_pointer); ws_page_table [B][table_width];
- * ws_k_pool [num_pages][Hkv][bs][D], ws_v_pool [num_pages][Hkv][D][bs].  Here
+ * ws_k_pool [num_pages][Hkv][bs*D], ws_v_pool [num_pages][Hkv][D][bs].  Here
  * s->table_width is the number of slots K and s->num_pages the working-set
  * pages.  Entries with a block outside [0, host_blocks), a slot outside
  * [0, K) or a page outside [0, num_pages) are skipped.  The fetch lists are

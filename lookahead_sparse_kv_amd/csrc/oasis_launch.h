@@ -39,13 +39,13 @@ struct SelectPlanArgs {
 };
 
 struct FetchArgs {
-    const uint16_t *host_k;       // device-mapped pinned host pool, [B][Hkv][host_blocks][bs][D]
+    const uint16_t *host_k;       // device-mapped pinned host pool, [B][Hkv][host_blocks][bs*D], key tiles in slices
     const uint16_t *host_v;       // [B][Hkv][host_blocks][D][bs]
     const int32_t *fetch_block;
     const int32_t *fetch_slot;
     const int32_t *fetch_count;
     const int32_t *ws_page_table; // [B][k_slots] slot -> working-set page
-    uint16_t *ws_k;               // [ws_pages][Hkv][bs][D]
+    uint16_t *ws_k;               // [ws_pages][Hkv][bs*D], key tiles in slices
     uint16_t *ws_v;               // [ws_pages][Hkv][D][bs]
     int batch, hkv, host_blocks, k_slots, cap, ws_pages;
 };

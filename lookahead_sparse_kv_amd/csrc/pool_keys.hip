@@ -8,13 +8,12 @@
 //   (16n + t < ctx_len[b]) of the block.
 // Both are bf16 values of the keys themselves, so the pooling is exact.
 //
-// Design: one wave per block.  The 4 KiB key tile (token-major) is read 16 B
-// per lane, so one load instruction covers 64 lanes x 16 B = 4 tokens at
-// D = 128 (8 at D = 64), contiguous in memory; each lane keeps the running
-// min and max of its 8 dimensions and the token groups are folded by lane
-// exchanges.  A page outside the pool is not read: the block is written as an
-// empty box (min = +inf, max = -inf), which the compressed scorer turns into
-// -inf.  The last-block mode refreshes only block ceil(ctx / 16) - 1 of each
+// Design: one wave per block.  The 4 KiB key tile, stored in 8-dimension
+// slices ([D/8][16][8]), is read 16 B per lane, so one load instruction covers
+// four slices (1 KiB contiguous): lane l holds 8 dimensions of token l % 16,
+// and the 16 tokens of each slice are folded by lane exchanges.  A page
+// outside the pool is not read: the block is written as an empty box
+// (min = +inf, max = -inf), which the compressed scorer turns into -inf.  The last-block mode refreshes only block ceil(ctx / 16) - 1 of each
 // sequence: the one a decode step appends its token to.
 #include "oasis_device.h"
 #include "oasis_launch.h"
@@ -25,9 +24,7 @@ constexpr int kPoolWaves = 4;
 
 template <int D>
 __global__ __launch_bounds__(kPoolWaves * kWave) void pool_keys_kernel(PoolArgs a) {
-    constexpr int CH = D / 8;                    // 16-byte chunks per token
-    constexpr int TPL = kWave / CH;              // tokens per load instruction
-    constexpr int NL = kBlockTokens / TPL;       // loads per lane
+    constexpr int NI = D / 32;                   // load instructions: 4 slices of 8 dims each
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const long long gw = (long long)blockIdx.x * kPoolWaves + wave;
@@ -53,65 +50,70 @@ __global__ __launch_bounds__(kPoolWaves * kWave) void pool_keys_kernel(PoolArgs 
     long long nt = ctx - (long long)n * kBlockTokens;
     nt = nt > kBlockTokens ? kBlockTokens : nt;
 
-    const int c = lane % CH;         // dims 8c .. 8c + 7
-    const int tg = lane / CH;        // tokens tg, tg + TPL, ...
+    // The tile is stored in 8-dimension slices ([D/8][16][8]): load i, lane l
+    // reads token t = l % 16 of slice 4i + l / 16 (1 KiB contiguous per load).
+    const int t = lane & 15;
+    const int g4 = lane >> 4;
     uint16_t *out = a.ck + ((size_t)row * a.width + n) * 2 * D;
     const int page = a.block_table[(size_t)b * a.width + n];
     if (page < 0 || page >= a.num_pages) {
-        if (tg == 0) {
+        if (t == 0) {
             const u32x4 pinf = {0x7f807f80u, 0x7f807f80u, 0x7f807f80u, 0x7f807f80u};
             const u32x4 ninf = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
-            *reinterpret_cast<u32x4 *>(out + 8 * c) = pinf;
-            *reinterpret_cast<u32x4 *>(out + D + 8 * c) = ninf;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                *reinterpret_cast<u32x4 *>(out + 8 * (4 * i + g4)) = pinf;
+                *reinterpret_cast<u32x4 *>(out + D + 8 * (4 * i + g4)) = ninf;
+            }
         }
         return;
     }
     const uint16_t *tile = a.k_pool + ((size_t)page * a.hkv + g) * kBlockTokens * D;
-    float mn[8], mx[8];
+    u32x4 v[NI];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { mn[e] = __builtin_inff(); mx[e] = -__builtin_inff(); }
-    u32x4 v[NL];
+    for (int i = 0; i < NI; ++i)
+        v[i] = *reinterpret_cast<const u32x4 *>(tile + (size_t)i * 512 + lane * 8);
+    float mn[NI][8], mx[NI][8];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        const int t = tg + TPL * i;
-        v[i] = t < nt ? *reinterpret_cast<const u32x4 *>(tile + (size_t)t * D + 8 * c)
-                      : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const bool ok = t < nt;
+            const float lo = bf16_bits_to_float(v[i][w] & 0xffffu);
+            const float hi = bf16_bits_to_float(v[i][w] >> 16);
+            mn[i][2 * w] = ok ? lo : __builtin_inff();
+            mx[i][2 * w] = ok ? lo : -__builtin_inff();
+            mn[i][2 * w + 1] = ok ? hi : __builtin_inff();
+            mx[i][2 * w + 1] = ok ? hi : -__builtin_inff();
+        }
     }
+    // fold the 16 tokens of each slice (lanes of one 16-lane group)
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        if (tg + TPL * i < nt) {
+    for (int off = 1; off < 16; off <<= 1) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float lo = bf16_bits_to_float(v[i][w] & 0xffffu);
-                const float hi = bf16_bits_to_float(v[i][w] >> 16);
-                mn[2 * w] = fminf(mn[2 * w], lo);
-                mx[2 * w] = fmaxf(mx[2 * w], lo);
-                mn[2 * w + 1] = fminf(mn[2 * w + 1], hi);
-                mx[2 * w + 1] = fmaxf(mx[2 * w + 1], hi);
+        for (int i = 0; i < NI; ++i) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                mn[i][e] = fminf(mn[i][e], shfl_xor_f(mn[i][e], off));
+                mx[i][e] = fmaxf(mx[i][e], shfl_xor_f(mx[i][e], off));
             }
         }
     }
-    // fold the token groups (lanes c, c + CH, c + 2 CH, ...)
+    if (t == 0) {
 #pragma unroll
-    for (int off = CH; off < kWave; off <<= 1) {
+        for (int i = 0; i < NI; ++i) {
+            u32x4 pmn, pmx;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            mn[e] = fminf(mn[e], shfl_xor_f(mn[e], off));
-            mx[e] = fmaxf(mx[e], shfl_xor_f(mx[e], off));
+            for (int w = 0; w < 4; ++w) {
+                // exact: every value is a bf16 key element
+                pmn[w] = (__builtin_bit_cast(uint32_t, mn[i][2 * w]) >> 16) |
+                         (__builtin_bit_cast(uint32_t, mn[i][2 * w + 1]) & 0xffff0000u);
+                pmx[w] = (__builtin_bit_cast(uint32_t, mx[i][2 * w]) >> 16) |
+                         (__builtin_bit_cast(uint32_t, mx[i][2 * w + 1]) & 0xffff0000u);
+            }
+            *reinterpret_cast<u32x4 *>(out + 8 * (4 * i + g4)) = pmn;
+            *reinterpret_cast<u32x4 *>(out + D + 8 * (4 * i + g4)) = pmx;
         }
-    }
-    if (tg == 0) {
-        u32x4 pmn, pmx;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // exact: every value is a bf16 key element
-            pmn[w] = (__builtin_bit_cast(uint32_t, mn[2 * w]) >> 16) |
-                     (__builtin_bit_cast(uint32_t, mn[2 * w + 1]) & 0xffff0000u);
-            pmx[w] = (__builtin_bit_cast(uint32_t, mx[2 * w]) >> 16) |
-                     (__builtin_bit_cast(uint32_t, mx[2 * w + 1]) & 0xffff0000u);
-        }
-        *reinterpret_cast<u32x4 *>(out + 8 * c) = pmn;
-        *reinterpret_cast<u32x4 *>(out + D + 8 * c) = pmx;
     }
 }
 

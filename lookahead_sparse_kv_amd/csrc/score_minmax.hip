@@ -37,15 +37,14 @@ constexpr int kMmTiles = 4;            // 16-block tiles per wave
 constexpr int kMmBlocksPerWave = kMmTiles * kBlockTokens;
 
 // Refresh wave of one row: pool the last block (ceil(ctx / 16) - 1) from the
-// key pool as oasis_pool_keys does, write its compressed row, and score it
-// from the fresh values: lane (c, tg) holds dims 8c .. 8c + 7 and takes the
-// lookahead rows tg, tg + TPL, ...; the row sums are folded over the CH lanes
-// of a token group and the max over the groups.
+// key pool as oasis_pool_keys does (load i, lane l: token l % 16 of the
+// 8-dimension slice 4i + l / 16), write its compressed row, and score it from
+// the fresh values: after the fold every lane of 16-lane group g4 holds the
+// min and max of slices 4i + g4; lane l takes lookahead row l % 16, sums over
+// its group's slices, and the sums are folded over the four groups.
 template <int D>
 __device__ __forceinline__ void refresh_last_block(const MinmaxArgs &a, int row) {
-    constexpr int CH = D / 8;
-    constexpr int TPL = kWave / CH;
-    constexpr int NL = kBlockTokens / TPL;
+    constexpr int NI = D / 32;
     const int lane = threadIdx.x & (kWave - 1);
     const int b = row / a.hkv;
     const int g = row - b * a.hkv;
@@ -56,87 +55,94 @@ __device__ __forceinline__ void refresh_last_block(const MinmaxArgs &a, int row)
     if (nb == 0) return;
     const int n = nb - 1;
     const int nt = (int)(ctx - (long long)n * kBlockTokens);
-    const int c = lane % CH;
-    const int tg = lane / CH;
+    const int t = lane & 15;
+    const int g4 = lane >> 4;
     uint16_t *crow = a.ck + ((size_t)row * a.width + n) * 2 * D;
     float *out = a.scores + (size_t)row * a.width;
     const int page = a.block_table[(size_t)b * a.width + n];
     if (page < 0 || page >= a.num_pages) {
-        if (tg == 0) {
+        if (t == 0) {
             const u32x4 pinf = {0x7f807f80u, 0x7f807f80u, 0x7f807f80u, 0x7f807f80u};
             const u32x4 ninf = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
-            *reinterpret_cast<u32x4 *>(crow + 8 * c) = pinf;
-            *reinterpret_cast<u32x4 *>(crow + D + 8 * c) = ninf;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                *reinterpret_cast<u32x4 *>(crow + 8 * (4 * i + g4)) = pinf;
+                *reinterpret_cast<u32x4 *>(crow + D + 8 * (4 * i + g4)) = ninf;
+            }
         }
         if (lane == 0) out[n] = -__builtin_inff();
         return;
     }
     const uint16_t *tile = a.k_pool + ((size_t)page * a.hkv + g) * kBlockTokens * D;
-    float mn[8], mx[8];
+    u32x4 v[NI];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { mn[e] = __builtin_inff(); mx[e] = -__builtin_inff(); }
-    u32x4 v[NL];
+    for (int i = 0; i < NI; ++i)
+        v[i] = *reinterpret_cast<const u32x4 *>(tile + (size_t)i * 512 + lane * 8);
+    float mn[NI][8], mx[NI][8];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        const int t = tg + TPL * i;
-        v[i] = t < nt ? *reinterpret_cast<const u32x4 *>(tile + (size_t)t * D + 8 * c)
-                      : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const bool ok = t < nt;
+            const float lo = bf16_bits_to_float(v[i][w] & 0xffffu);
+            const float hi = bf16_bits_to_float(v[i][w] >> 16);
+            mn[i][2 * w] = ok ? lo : __builtin_inff();
+            mx[i][2 * w] = ok ? lo : -__builtin_inff();
+            mn[i][2 * w + 1] = ok ? hi : __builtin_inff();
+            mx[i][2 * w + 1] = ok ? hi : -__builtin_inff();
+        }
     }
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        if (tg + TPL * i < nt) {
+    for (int off = 1; off < 16; off <<= 1) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float lo = bf16_bits_to_float(v[i][w] & 0xffffu);
-                const float hi = bf16_bits_to_float(v[i][w] >> 16);
-                mn[2 * w] = fminf(mn[2 * w], lo);
-                mx[2 * w] = fmaxf(mx[2 * w], lo);
-                mn[2 * w + 1] = fminf(mn[2 * w + 1], hi);
-                mx[2 * w + 1] = fmaxf(mx[2 * w + 1], hi);
+        for (int i = 0; i < NI; ++i) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                mn[i][e] = fminf(mn[i][e], shfl_xor_f(mn[i][e], off));
+                mx[i][e] = fmaxf(mx[i][e], shfl_xor_f(mx[i][e], off));
             }
         }
     }
+    if (t == 0) {
 #pragma unroll
-    for (int off = CH; off < kWave; off <<= 1) {
+        for (int i = 0; i < NI; ++i) {
+            u32x4 pmn, pmx;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            mn[e] = fminf(mn[e], shfl_xor_f(mn[e], off));
-            mx[e] = fmaxf(mx[e], shfl_xor_f(mx[e], off));
+            for (int w = 0; w < 4; ++w) {
+                pmn[w] = (__builtin_bit_cast(uint32_t, mn[i][2 * w]) >> 16) |
+                         (__builtin_bit_cast(uint32_t, mn[i][2 * w + 1]) & 0xffff0000u);
+                pmx[w] = (__builtin_bit_cast(uint32_t, mx[i][2 * w]) >> 16) |
+                         (__builtin_bit_cast(uint32_t, mx[i][2 * w + 1]) & 0xffff0000u);
+            }
+            *reinterpret_cast<u32x4 *>(crow + 8 * (4 * i + g4)) = pmn;
+            *reinterpret_cast<u32x4 *>(crow + D + 8 * (4 * i + g4)) = pmx;
         }
     }
-    if (tg == 0) {
-        u32x4 pmn, pmx;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            pmn[w] = (__builtin_bit_cast(uint32_t, mn[2 * w]) >> 16) |
-                     (__builtin_bit_cast(uint32_t, mn[2 * w + 1]) & 0xffff0000u);
-            pmx[w] = (__builtin_bit_cast(uint32_t, mx[2 * w]) >> 16) |
-                     (__builtin_bit_cast(uint32_t, mx[2 * w + 1]) & 0xffff0000u);
-        }
-        *reinterpret_cast<u32x4 *>(crow + 8 * c) = pmn;
-        *reinterpret_cast<u32x4 *>(crow + D + 8 * c) = pmx;
-    }
-    // the bound of every lookahead row this lane takes, then the max
-    float best = -__builtin_inff();
-    for (int r = tg; r < a.n_rows_q; r += TPL) {
+    // lookahead row r = lane % 16 over this group's slices, then the other groups
+    const int r = t;
+    float part = 0.f;
+    if (r < a.n_rows_q) {
         const int jd = r / a.group;
         const int hr = r - jd * a.group;
-        const u32x4 qw = load_u32x4(a.q_look +
-            (((size_t)b * a.n_look + jd) * a.hq + (size_t)g * a.group + hr) * D + 8 * c);
-        float part = 0.f;
+        const uint16_t *qrow = a.q_look +
+            (((size_t)b * a.n_look + jd) * a.hq + (size_t)g * a.group + hr) * D;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float q0 = bf16_bits_to_float(qw[w] & 0xffffu);
-            const float q1 = bf16_bits_to_float(qw[w] >> 16);
-            part += q0 < 0.f ? q0 * mn[2 * w] : q0 * mx[2 * w];
-            part += q1 < 0.f ? q1 * mn[2 * w + 1] : q1 * mx[2 * w + 1];
+        for (int i = 0; i < NI; ++i) {
+            const u32x4 qw = load_u32x4(qrow + 8 * (4 * i + g4));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float q0 = bf16_bits_to_float(qw[w] & 0xffffu);
+                const float q1 = bf16_bits_to_float(qw[w] >> 16);
+                part += q0 < 0.f ? q0 * mn[i][2 * w] : q0 * mx[i][2 * w];
+                part += q1 < 0.f ? q1 * mn[i][2 * w + 1] : q1 * mx[i][2 * w + 1];
+            }
         }
-#pragma unroll
-        for (int off = 1; off < CH; off <<= 1) part += shfl_xor_f(part, off);
-        best = fmaxf(best, part);
     }
+    part += shfl_xor_f(part, 16);
+    part += shfl_xor_f(part, 32);
+    float best = r < a.n_rows_q ? part : -__builtin_inff();
 #pragma unroll
-    for (int off = CH; off < kWave; off <<= 1) best = fmaxf(best, shfl_xor_f(best, off));
+    for (int off = 1; off < 16; off <<= 1) best = fmaxf(best, shfl_xor_f(best, off));
     if (lane == 0) out[n] = best * a.scale;
 }
 

@@ -8,7 +8,8 @@
 // Design (gfx950): one wave per (sequence, KV head, split) walks its share of
 // the row's block list.  Per 16-token block:
 //   S (16 tokens x 16 query rows) = 16x16x32 bf16 MFMAs, A = key tile
-//     (token-major, 16 B per lane), B = the group's query rows;
+//     (stored in 8-dimension slices: 16 B per lane, 1 KiB contiguous per
+//     load), B = the group's query rows;
 //   online softmax per query row in fp32 (exp2 with a folded log2(e));
 //   O^T (D x 16 query rows) += V^T (D x 32 tokens) * P (32 tokens x 16 rows)
 //     for two blocks at a time: 16x16x32 bf16 MFMAs whose B operand is P
@@ -61,7 +62,7 @@ template <int D>
 __device__ __forceinline__ void load_block(BlockRegs<D> &r, rsrc_t kr, rsrc_t vr, uint32_t koff,
                                            uint32_t voff) {
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) r.k[kk] = buf_load16<OASIS_ATTN_CPOL>(kr, koff, 64 * kk);
+    for (int kk = 0; kk < D / 32; ++kk) r.k[kk] = buf_load16<OASIS_ATTN_CPOL>(kr, koff, 1024 * kk);
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt)
         r.v[mt] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff, 16 * kBlockTokens * 2 * mt, OASIS_ATTN_CPOL);
@@ -135,7 +136,9 @@ __device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int 
     const size_t page_stride = (size_t)a.hkv * kBlockTokens * D;
     const size_t head_off = (size_t)g * kBlockTokens * D;       // same for K and V tiles
     constexpr uint32_t kTileBytes = kBlockTokens * D * 2;
-    const uint32_t koff = (uint32_t)(r16 * D + 8 * j4) * 2;             // + 64 B per kk
+    // key tiles in 8-dimension slices: token r16, dims 32*kk + 8*j4 .. +8 at
+    // lane * 16 + kk * 1 KiB (1 KiB contiguous per load)
+    const uint32_t koff = (uint32_t)lane * 16;
     const uint32_t voff = (uint32_t)(r16 * kBlockTokens + 4 * j4) * 2;  // + 512 B per mt
     auto tile = [&](const uint16_t *pool, int e) {
         const int p = e < ne ? readlane_i(my_page, e) : -1;

@@ -117,7 +117,8 @@ def _pool_shape(q: torch.Tensor, k_pool: torch.Tensor, table: torch.Tensor) -> O
 
 
 def score_blocks(q_look, k_pool, block_table, ctx_len, scores, scale=None, stream=None):
-    """q_look [B][n_look][Hq][D] bf16, k_pool [P][Hkv][16][D] bf16, block_table [B][W] i32,
+    """q_look [B][n_look][Hq][D] bf16, k_pool [P][Hkv][16][D] bf16 (tiles in 8-dim slices),
+    block_table [B][W] i32,
     ctx_len [B] i32 -> scores [B][Hkv][W] f32 (written in place)."""
     s = _pool_shape(q_look, k_pool, block_table)
     scale = float(s.head_dim) ** -0.5 if scale is None else scale
@@ -128,7 +129,7 @@ def score_blocks(q_look, k_pool, block_table, ctx_len, scores, scale=None, strea
 
 
 def pool_keys(k_pool, block_table, ctx_len, ck, num_q_heads=None, last_only=False, stream=None):
-    """k_pool [P][Hkv][16][D] bf16, block_table [B][W] i32, ctx_len [B] i32 ->
+    """k_pool [P][Hkv][16][D] bf16 (tiles in 8-dim slices), block_table [B][W] i32, ctx_len [B] i32 ->
     ck [B][Hkv][W][2][D] bf16 (per-block min, max; written in place)."""
     Hkv = k_pool.shape[1]
     s = make_shape(block_table.shape[0], num_q_heads or Hkv, Hkv, k_pool.shape[-1],

@@ -187,7 +187,8 @@ def make_layer(wl: Workload, seed: Optional[int] = None, *, pools: bool = True) 
     q [B][Hq][D] bf16, q_look [B][n_look][Hq][D] bf16, K and V [B][Hkv][ctx_pad][D] bf16
     (ctx_pad = W * bs, tokens past each context poisoned), hot [B][Hkv][n_hot] int64,
     block_table [B][W] int32, ctx_len [B] int32, plus (pools=True) k_pool
-    [num_pages][Hkv][bs][D] and v_pool [num_pages][Hkv][D][bs] bf16.  The tiny fp32
+    [num_pages][Hkv][bs][D] (tiles in key_tiles order) and v_pool [num_pages][Hkv][D][bs]
+    bf16.  The tiny fp32
     workload also returns K32 / V32 / q32 / q_look32 in fp32.
     """
     seed = wl.seed if seed is None else seed
@@ -241,10 +242,32 @@ def make_layer(wl: Workload, seed: Optional[int] = None, *, pools: bool = True) 
     return out
 
 
+def key_tiles(x: torch.Tensor) -> torch.Tensor:
+    """Key tiles [..][bs][D] (token-major) -> the pool's byte order, returned with
+    the same shape: each tile is stored in 8-dimension slices, [D/8][bs][8]
+    (slice s holds dims 8s .. 8s+7 of every token of the block)."""
+    *lead, bs, D = x.shape
+    return x.reshape(*lead, bs, D // 8, 8).transpose(-3, -2).reshape(*lead, bs, D).contiguous()
+
+
+def key_tiles_logical(x: torch.Tensor) -> torch.Tensor:
+    """Inverse of key_tiles: pool-order tiles [..][bs][D] -> token-major [..][bs][D]."""
+    *lead, bs, D = x.shape
+    return x.reshape(*lead, D // 8, bs, 8).transpose(-3, -2).reshape(*lead, bs, D).contiguous()
+
+
+def set_key_token(k_pool: torch.Tensor, page: int, t: int, tok: torch.Tensor) -> None:
+    """In place: token t (< bs) of page `page`, every head, tok [Hkv][D]."""
+    P, Hkv, bs, D = k_pool.shape
+    k_pool.view(P, Hkv, D // 8, bs, 8)[page, :, :, t, :] = tok.reshape(Hkv, D // 8, 8)
+
+
 def build_pools(wl: Workload, K: torch.Tensor, V: torch.Tensor, block_table: torch.Tensor):
     """Scatter logical K, V [B][Hkv][W*bs][D] into the paged pools.
 
-    k_pool [num_pages][Hkv][bs][D]: one (page, head) key tile is bs x D, token-major.
+    k_pool [num_pages][Hkv][bs][D]: one (page, head) key tile of bs x D, stored in
+    8-dimension slices (key_tiles), so that each 16-byte-per-lane load of the
+    score and QK MFMA operands reads 1 KiB of contiguous memory.
     v_pool [num_pages][Hkv][D][bs]: one (page, head) value tile is D x bs, dim-major.
     """
     B, Hkv, ctx_pad, D = K.shape
@@ -254,7 +277,8 @@ def build_pools(wl: Workload, K: torch.Tensor, V: torch.Tensor, block_table: tor
     k_pool = torch.empty((n_pages, Hkv, bs, D), dtype=K.dtype)
     v_pool = torch.empty((n_pages, Hkv, D, bs), dtype=V.dtype)
     flat = block_table.reshape(-1).to(torch.int64)
-    k_pool[flat] = K.view(B, Hkv, W, bs, D).permute(0, 2, 1, 3, 4).reshape(B * W, Hkv, bs, D)
+    k_pool[flat] = key_tiles(K.view(B, Hkv, W, bs, D).permute(0, 2, 1, 3, 4)
+                             .reshape(B * W, Hkv, bs, D))
     v_pool[flat] = V.view(B, Hkv, W, bs, D).permute(0, 2, 1, 4, 3).reshape(B * W, Hkv, D, bs)
     return k_pool, v_pool
 
@@ -292,8 +316,8 @@ def _replant(wl: Workload, d: dict, old_mask: torch.Tensor, new_mask: torch.Tens
     d["K"][bb, gg, tok] = torch.where(hot_now, (base.float() + shift).to(torch.bfloat16), base)
     pages = d["block_table"][b, blk].to(torch.int64)
     if "k_pool" in d:
-        d["k_pool"][pages, g] = d["K"][b.unsqueeze(1), g.unsqueeze(1),
-                                       (blk.unsqueeze(1) * bs + torch.arange(bs))]
+        d["k_pool"][pages, g] = key_tiles(d["K"][b.unsqueeze(1), g.unsqueeze(1),
+                                                 (blk.unsqueeze(1) * bs + torch.arange(bs))])
     return pages, g
 
 

@@ -92,10 +92,15 @@ def test_generator_is_seeded_and_poisons_the_tail():
     for key in ("q", "q_look", "K", "V", "block_table", "k_pool", "v_pool"):
         assert torch.equal(a[key], b[key])
     assert torch.all(a["K"][1, :, 60:] == wlm.POISON)
-    # the pools hold the logical values at the permuted pages
+    # the pools hold the logical values at the permuted pages (key tiles in
+    # 8-dimension slices: element (t, d) at ((d // 8) * 16 + t) * 8 + d % 8)
     bt = a["block_table"]
     for b_ in range(2):
         for n in range(wl.table_width):
             p = int(bt[b_, n])
-            assert torch.equal(a["k_pool"][p, 1], a["K"][b_, 1, 16 * n:16 * n + 16])
+            assert torch.equal(wlm.key_tiles_logical(a["k_pool"][p, 1]),
+                               a["K"][b_, 1, 16 * n:16 * n + 16])
+            flat = a["k_pool"][p, 1].reshape(-1)
+            for t, d in ((0, 0), (5, 37), (15, 63), (3, 8)):
+                assert flat[((d // 8) * 16 + t) * 8 + d % 8] == a["K"][b_, 1, 16 * n + t, d]
             assert torch.equal(a["v_pool"][p, 0], a["V"][b_, 0, 16 * n:16 * n + 16].T)

@@ -501,7 +501,7 @@ def _host_pool_for(d, wl):
     B, Hkv, W, D = wl.batch, wl.num_kv_heads, wl.table_width, wl.head_dim
     n = B * Hkv * W * 16 * D
     pool = ops.HostPool(4 * n)
-    pool.tensor((B, Hkv, W, 16, D), torch.bfloat16).copy_(d["K"].view(B, Hkv, W, 16, D))
+    pool.tensor((B, Hkv, W, 16, D), torch.bfloat16).copy_(wlm.key_tiles(d["K"].view(B, Hkv, W, 16, D)))
     pool.tensor((B, Hkv, W, D, 16), torch.bfloat16, offset_bytes=2 * n).copy_(
         d["V"].view(B, Hkv, W, 16, D).transpose(-1, -2))
     return pool, pool.device_ptr, pool.device_ptr + 2 * n
@@ -534,7 +534,7 @@ def test_fetch_blocks_copies_listed_tiles_and_skips_bad_entries():
                 if not (0 <= blk < W and 0 <= slot < K):
                     continue
                 page = int(pt[b, slot])
-                expect_k[page, g] = d["K"][b, g, 16 * blk:16 * blk + 16]
+                expect_k[page, g] = wlm.key_tiles(d["K"][b, g, 16 * blk:16 * blk + 16])
                 expect_v[page, g] = d["V"][b, g, 16 * blk:16 * blk + 16].T
     assert torch.equal(gk, expect_k) and torch.equal(gv, expect_v)
     del pool
@@ -601,7 +601,7 @@ def test_host_tier_matches_full_pool_over_layers_and_steps(scorer):
                     if blk < 0:
                         continue
                     page = int(ptb[b, j])
-                    assert torch.equal(wk[page, g], d["K"][b, g, 16 * blk:16 * blk + 16])
+                    assert torch.equal(wk[page, g], wlm.key_tiles(d["K"][b, g, 16 * blk:16 * blk + 16]))
                     assert torch.equal(wv[page, g], d["V"][b, g, 16 * blk:16 * blk + 16].T)
     del pools
 

@@ -80,7 +80,7 @@ def test_score_with_refresh_after_append(head_dim, n_look):
         t = int(d["ctx_len"][b])
         tok = torch.randn((wl.num_kv_heads, head_dim), generator=gen).to(torch.bfloat16) * 3
         K[b, :, t] = tok
-        k_pool[int(d["block_table"][b, t // 16]), :, t % 16] = tok
+        wlm.set_key_token(k_pool, int(d["block_table"][b, t // 16]), t % 16, tok)
     scores = torch.full((wl.batch, wl.num_kv_heads, wl.table_width), 7.0, device=DEV)
     ops.score_blocks_minmax(dev(d["q_look"]), ck, dev(new_ctx), scores, k_pool=dev(k_pool),
                             block_table=dev(d["block_table"]))
@@ -125,7 +125,7 @@ def test_pool_keys_last_block_after_append(head_dim):
         t = int(d["ctx_len"][b])
         tok = torch.randn((wl.num_kv_heads, head_dim), generator=rng).to(torch.bfloat16) * 3
         K[b, :, t] = tok
-        k_pool[int(d["block_table"][b, t // 16]), :, t % 16] = tok
+        wlm.set_key_token(k_pool, int(d["block_table"][b, t // 16]), t % 16, tok)
     d2 = dict(d, K=K, k_pool=k_pool, ctx_len=new_ctx)
     ck = gpu_pool(d2, wl, last_only=True, ck=ck)
     check_pooled(ck, K, new_ctx, wl.table_width, f"append D{head_dim}")
@@ -304,7 +304,7 @@ def test_minmax_decode_steps_with_appends():
             kt = torch.randn((wl.num_kv_heads, wl.head_dim), generator=gen).to(torch.bfloat16)
             vt = torch.randn((wl.num_kv_heads, wl.head_dim), generator=gen).to(torch.bfloat16)
             K[b, :, t], V[b, :, t] = kt, vt
-            k_pool[page, :, t % 16] = dev(kt)
+            wlm.set_key_token(k_pool, page, t % 16, dev(kt))
             v_pool[page, :, :, t % 16] = dev(vt)
         ctx += 1
         ctx_dev.copy_(dev(ctx))
