@@ -26,6 +26,10 @@
 namespace oasis {
 
 constexpr int kAttnWaves = 4;
+#ifndef OASIS_ATTN_STAGES
+#define OASIS_ATTN_STAGES 2          // block pairs in flight per wave
+#endif
+constexpr int kAttnStages = OASIS_ATTN_STAGES;
 #ifndef OASIS_ATTN_CPOL
 #define OASIS_ATTN_CPOL 2        // K/V tile loads: non-temporal (each byte is read once)
 #endif
@@ -146,18 +150,24 @@ __device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int 
                       : make_rsrc(pool, 0u);
     };
 
-    // Entries go in pairs: the pair after the current one is loaded before
-    // the current one is computed, so up to four blocks are in flight.
-    BlockRegs<D> cur[2], nxt[2];
+    // Entries go in pairs, kStages pairs in flight: the pair kStages - 1 ahead
+    // of the current one is loaded before the current one is computed.
+    constexpr int S = kAttnStages;
+    BlockRegs<D> stage[S][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) load_block<D>(cur[u], tile(a.k_pool, u), tile(a.v_pool, u), koff, voff);
+    for (int st = 0; st < S - 1; ++st)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            load_block<D>(stage[st][u], tile(a.k_pool, 2 * st + u), tile(a.v_pool, 2 * st + u), koff, voff);
     for (int i = 0; i < ne; i += 2) {
         int ntok[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             ntok[u] = (i + u < ne && readlane_i(my_page, i + u) >= 0) ? readlane_i(my_ntok, i + u) : 0;
-            load_block<D>(nxt[u], tile(a.k_pool, i + 2 + u), tile(a.v_pool, i + 2 + u), koff, voff);
+            const int e = i + 2 * (S - 1) + u;
+            load_block<D>(stage[S - 1][u], tile(a.k_pool, e), tile(a.v_pool, e), koff, voff);
         }
+        BlockRegs<D> (&cur)[2] = stage[0];
         if (ntok[0] + ntok[1] > 0) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -212,8 +222,11 @@ __device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int 
                 }
             }
         }
-        cur[0] = nxt[0];
-        cur[1] = nxt[1];
+#pragma unroll
+        for (int st = 0; st < S - 1; ++st) {
+            stage[st][0] = stage[st + 1][0];
+            stage[st][1] = stage[st + 1][1];
+        }
     }
 }
 
@@ -265,7 +278,7 @@ __device__ __forceinline__ void merge_one(const AttnArgs &a, int row, int c, int
 // NT = 1: up to 16 query rows per KV head; NT = 2: up to 32 (the normal and
 // the draft queries together), at one wave per SIMD for the registers.
 template <int D, int NT>
-__global__ __launch_bounds__(kAttnWaves * kWave, NT == 1 ? 2 : 1) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * kWave, NT == 1 && kAttnStages == 2 ? 2 : 1) void attn_partial_kernel(AttnArgs a) {
     constexpr int MT = D / 16;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps row indices scalar
