@@ -208,7 +208,8 @@ def host_tier_layers(wl, ratio, n_layers, dev, n_q=1):
         if wl.scorer == "minmax":
             # the compressed keys are pooled once from a temporary device copy
             # of the keys (prefill work), which is then released
-            ck = torch.empty((B, Hkv, W, 2, D), dtype=torch.bfloat16, device=dev)
+            ck = torch.empty(ops.compressed_keys_shape(B, Hkv, W, D), dtype=torch.bfloat16,
+                             device=dev)
             ops.pool_keys(k_dev, bt_dev, ctx_dev, ck, num_q_heads=wl.num_q_heads)
             torch.cuda.synchronize()
             k_dev = None

@@ -47,7 +47,11 @@
  *  - block table        [B][table_width]  int32, logical block -> page
  *  - context lengths    ctx_len [B]       int32, tokens
  *  - scores             [B][Hkv][table_width]  fp32
- *  - compressed keys    ck      [B][Hkv][table_width][2][D]  bf16 (min, max)
+ *  - compressed keys    ck      [B][Hkv][ceil(W/16)][2D/8][16][8] bf16: per row,
+ *                       tiles of 16 blocks; in a tile, slice s holds elements
+ *                       8s .. 8s+7 of every block's [min(D) | max(D)] vector, so
+ *                       (block n, element e) is at tile n/16, slice e/8,
+ *                       position (n % 16) * 8 + e % 8
  *  - selection          sel     [B][Hkv][K]     int32, ascending, -1 padded
  *  - working-set table  slot_block, last_use [B][Hkv][K] int32
  *  - fetch list         fetch_block, fetch_slot [B][Hkv][cap] int32, -1 padded;
@@ -105,8 +109,8 @@ int oasis_score_blocks(const oasis_shape *s, const uint16_t *q_look, int32_t n_l
  * sparse KV working set the GPU keeps the keys compressed by per-block min/max
  * pooling, for the draft query to scan.
  *
- *   ck[b][g][n][0][d] = min, ck[b][g][n][1][d] = max of k_t[d] over the tokens
- *   t of block n with 16n + t < ctx_len[b]          (ck: [B][Hkv][W][2][D] bf16)
+ *   min[b][g][n][d], max[b][g][n][d] = min and max of k_t[d] over the tokens
+ *   t of block n with 16n + t < ctx_len[b]      (ck layout: see "Layouts" above)
  *
  * last_only = 0 writes every block n < ceil(ctx_len[b] / bs); last_only = 1
  * only block ceil(ctx_len[b] / bs) - 1 of each sequence (the one a decode step
@@ -129,7 +133,7 @@ int oasis_pool_keys(const oasis_shape *s, const uint16_t *k_pool, const int32_t 
  *
  *   scores[b][g][n] = max over drafts j < n_look and query heads h of KV head g
  *                     of scale * sum_d max(q_d * min_d, q_d * max_d),
- *                     q = q_look[b][j][h], (min, max) = ck[b][g][n]
+ *                     q = q_look[b][j][h], (min, max) = block n of row (b, g) in ck
  *   scores[b][g][n] = -inf for n >= ceil(ctx_len[b] / bs) and for empty boxes.
  *
  * An upper bound of oasis_score_blocks' exact score, equal to it for a block

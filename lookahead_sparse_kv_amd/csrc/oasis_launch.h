@@ -90,6 +90,14 @@ struct MinmaxArgs {
     int batch, hq, hkv, group, width, num_pages, n_look, n_rows_q;
 };
 
+// Compressed keys: each row's blocks in tiles of 16, a tile stored as
+// [2D/8 slices][16 blocks][8]: slice s holds elements 8s .. 8s+7 of every
+// block's [min | max] vector.  Element offset of slice s of block n of `row`:
+__host__ __device__ inline size_t ck_slice_offset(int row, int width, int n, int s, int D) {
+    const size_t tiles = (size_t)(width + 15) / 16;
+    return (((size_t)row * tiles + n / 16) * (size_t)(2 * D / 8) + s) * 128 + (size_t)(n % 16) * 8;
+}
+
 hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_pool_keys(const PoolArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_score_minmax(const MinmaxArgs &a, int head_dim, hipStream_t stream);

@@ -54,7 +54,6 @@ __global__ __launch_bounds__(kPoolWaves * kWave) void pool_keys_kernel(PoolArgs 
     // reads token t = l % 16 of slice 4i + l / 16 (1 KiB contiguous per load).
     const int t = lane & 15;
     const int g4 = lane >> 4;
-    uint16_t *out = a.ck + ((size_t)row * a.width + n) * 2 * D;
     const int page = a.block_table[(size_t)b * a.width + n];
     if (page < 0 || page >= a.num_pages) {
         if (t == 0) {
@@ -62,8 +61,8 @@ __global__ __launch_bounds__(kPoolWaves * kWave) void pool_keys_kernel(PoolArgs 
             const u32x4 ninf = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                *reinterpret_cast<u32x4 *>(out + 8 * (4 * i + g4)) = pinf;
-                *reinterpret_cast<u32x4 *>(out + D + 8 * (4 * i + g4)) = ninf;
+                *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, 4 * i + g4, D)) = pinf;
+                *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, D / 8 + 4 * i + g4, D)) = ninf;
             }
         }
         return;
@@ -111,8 +110,8 @@ __global__ __launch_bounds__(kPoolWaves * kWave) void pool_keys_kernel(PoolArgs 
                 pmx[w] = (__builtin_bit_cast(uint32_t, mx[i][2 * w]) >> 16) |
                          (__builtin_bit_cast(uint32_t, mx[i][2 * w + 1]) & 0xffff0000u);
             }
-            *reinterpret_cast<u32x4 *>(out + 8 * (4 * i + g4)) = pmn;
-            *reinterpret_cast<u32x4 *>(out + D + 8 * (4 * i + g4)) = pmx;
+            *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, 4 * i + g4, D)) = pmn;
+            *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, D / 8 + 4 * i + g4, D)) = pmx;
         }
     }
 }

@@ -11,8 +11,8 @@
 // Design (gfx950): the right-hand form is one dot product of length 2D, so a
 // 16 x 16 MFMA tile covers 16 lookahead rows (A = [q- | q+], bf16, split by
 // sign bit once per wave) against 16 blocks (B = the compressed rows
-// [min | max], 512 contiguous bytes per block at D = 128); D/16
-// v_mfma_f32_16x16x32_bf16 per tile.  A wave takes 64 consecutive blocks of
+// [min | max], stored by tiles of 16 blocks in 8-element slices, 8 KiB per
+// tile at D = 128); D/16 v_mfma_f32_16x16x32_bf16 per tile.  A wave takes 64 consecutive blocks of
 // one row, issues all their loads (raw buffer loads bounded to the row's valid
 // blocks, non-temporal: each compressed key is read once per step), then
 // reduces each tile's columns over the lookahead rows with two lane exchanges.
@@ -57,7 +57,6 @@ __device__ __forceinline__ void refresh_last_block(const MinmaxArgs &a, int row)
     const int nt = (int)(ctx - (long long)n * kBlockTokens);
     const int t = lane & 15;
     const int g4 = lane >> 4;
-    uint16_t *crow = a.ck + ((size_t)row * a.width + n) * 2 * D;
     float *out = a.scores + (size_t)row * a.width;
     const int page = a.block_table[(size_t)b * a.width + n];
     if (page < 0 || page >= a.num_pages) {
@@ -66,8 +65,8 @@ __device__ __forceinline__ void refresh_last_block(const MinmaxArgs &a, int row)
             const u32x4 ninf = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                *reinterpret_cast<u32x4 *>(crow + 8 * (4 * i + g4)) = pinf;
-                *reinterpret_cast<u32x4 *>(crow + D + 8 * (4 * i + g4)) = ninf;
+                *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, 4 * i + g4, D)) = pinf;
+                *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, D / 8 + 4 * i + g4, D)) = ninf;
             }
         }
         if (lane == 0) out[n] = -__builtin_inff();
@@ -114,8 +113,8 @@ __device__ __forceinline__ void refresh_last_block(const MinmaxArgs &a, int row)
                 pmx[w] = (__builtin_bit_cast(uint32_t, mx[i][2 * w]) >> 16) |
                          (__builtin_bit_cast(uint32_t, mx[i][2 * w + 1]) & 0xffff0000u);
             }
-            *reinterpret_cast<u32x4 *>(crow + 8 * (4 * i + g4)) = pmn;
-            *reinterpret_cast<u32x4 *>(crow + D + 8 * (4 * i + g4)) = pmx;
+            *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, 4 * i + g4, D)) = pmn;
+            *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, D / 8 + 4 * i + g4, D)) = pmx;
         }
     }
     // lookahead row r = lane % 16 over this group's slices, then the other groups
@@ -172,21 +171,26 @@ __global__ __launch_bounds__(kMmWaves * kWave) void score_minmax_kernel(MinmaxAr
     ctx = ctx < 0 ? 0 : (ctx > cmax ? cmax : ctx);
     const int nb = (int)((ctx + kBlockTokens - 1) / kBlockTokens);
 
-    // Compressed rows of blocks n0 .. n0 + 63; the resource ends at the last
-    // valid block, so loads past it return zeros without touching memory.
-    constexpr uint32_t kRowBytes = 2 * D * 2;
-    const int valid_here = nb - n0 > 0 ? nb - n0 : 0;
-    const uint16_t *base = a.ck + ((size_t)row * a.width + n0) * 2 * D;
-    const rsrc_t r = make_rsrc(base, (uint32_t)(valid_here < kMmBlocksPerWave ? valid_here
-                                                                                : kMmBlocksPerWave) * kRowBytes);
-    // The block index sits in the per-lane offset, so the range check cuts at
-    // whole blocks; the k-step offset (< 512 B) stays inside the block's row.
+    // Compressed tiles n0/16 .. n0/16 + 3 (16 blocks each, in 8-element slices):
+    // the B operand of k-step kk (block r16, elements 32*kk + 8*j4 .. +8) is
+    // slice 4*kk + j4, at lane * 16 + kk * 1 KiB of the tile, so each load
+    // reads 1 KiB of contiguous memory.  The resource ends at the last tile
+    // holding a valid block; blocks past the context inside that tile are
+    // read but their scores are -inf (a column of the MFMA output depends on
+    // its own block only).
+    constexpr uint32_t kTileBytes = kBlockTokens * 2 * D * 2;
+    const int valid_tiles = nb > n0 ? (nb - n0 + kBlockTokens - 1) / kBlockTokens : 0;
+    const uint16_t *base = a.ck + ck_slice_offset(row, a.width, n0, 0, D);
+    const rsrc_t r = make_rsrc(base, (uint32_t)(valid_tiles < kMmTiles ? valid_tiles : kMmTiles) *
+                                         kTileBytes);
+    // The tile index sits in the per-lane offset, so the range check cuts at
+    // whole tiles; the k-step offset (< 8 KiB) stays inside the tile.
     u32x4 kb[kMmTiles][KK];
 #pragma unroll
     for (int t = 0; t < kMmTiles; ++t) {
-        const uint32_t boff = (uint32_t)((t * kBlockTokens + r16) * 2 * D + 8 * j4) * 2;
+        const uint32_t boff = (uint32_t)t * kTileBytes + (uint32_t)lane * 16;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kb[t][kk] = buf_load16<OASIS_MINMAX_CPOL>(r, boff, 64 * kk);
+        for (int kk = 0; kk < KK; ++kk) kb[t][kk] = buf_load16<OASIS_MINMAX_CPOL>(r, boff, 1024 * kk);
     }
 
     // A operand: lookahead row r16 (draft r16 / G, head g*G + r16 % G), dims

@@ -128,9 +128,17 @@ def score_blocks(q_look, k_pool, block_table, ctx_len, scores, scale=None, strea
     return scores
 
 
+def compressed_keys_shape(batch, num_kv_heads, table_width, head_dim):
+    """Shape of the compressed-key buffer: [B][Hkv][ceil(W/16)][2D/8][16][8] bf16
+    (tiles of 16 blocks; slice s holds elements 8s .. 8s+7 of each block's
+    [min | max] vector)."""
+    return (batch, num_kv_heads, (table_width + 15) // 16, 2 * head_dim // 8, 16, 8)
+
+
 def pool_keys(k_pool, block_table, ctx_len, ck, num_q_heads=None, last_only=False, stream=None):
-    """k_pool [P][Hkv][16][D] bf16 (tiles in 8-dim slices), block_table [B][W] i32, ctx_len [B] i32 ->
-    ck [B][Hkv][W][2][D] bf16 (per-block min, max; written in place)."""
+    """k_pool [P][Hkv][16][D] bf16 (tiles in 8-dim slices), block_table [B][W] i32,
+    ctx_len [B] i32 -> ck (compressed_keys_shape) bf16: per-block min, max, written
+    in place."""
     Hkv = k_pool.shape[1]
     s = make_shape(block_table.shape[0], num_q_heads or Hkv, Hkv, k_pool.shape[-1],
                    block_table.shape[1], k_pool.shape[0])
@@ -141,10 +149,12 @@ def pool_keys(k_pool, block_table, ctx_len, ck, num_q_heads=None, last_only=Fals
 
 def score_blocks_minmax(q_look, ck, ctx_len, scores, scale=None, k_pool=None, block_table=None,
                         stream=None):
-    """q_look [B][n_look][Hq][D] bf16, ck [B][Hkv][W][2][D] bf16, ctx_len [B] i32 ->
+    """q_look [B][n_look][Hq][D] bf16, ck (compressed_keys_shape) bf16, ctx_len [B] i32 ->
     scores [B][Hkv][W] f32 (written in place).  With k_pool [P][Hkv][16][D] and
     block_table [B][W], each sequence's last block is re-pooled into ck first."""
-    B, Hkv, W, _, D = ck.shape
+    B, Hkv, W = scores.shape
+    D = ck.shape[3] * 4
+    assert tuple(ck.shape) == compressed_keys_shape(B, Hkv, W, D)
     s = make_shape(B, q_look.shape[-2], Hkv, D, W, 0 if k_pool is None else k_pool.shape[0])
     scale = float(D) ** -0.5 if scale is None else scale
     _check(lib().oasis_score_blocks_minmax(ctypes.byref(s), _ptr(q_look), q_look.shape[1],

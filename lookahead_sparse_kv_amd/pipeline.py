@@ -51,7 +51,8 @@ class DecodeLayer:
         self.workspace = torch.zeros((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
         self.ck = None
         if scorer == "minmax":
-            self.ck = torch.empty((B, Hkv, W, 2, D), dtype=torch.bfloat16, device=dev)
+            self.ck = torch.empty(ops.compressed_keys_shape(B, Hkv, W, D), dtype=torch.bfloat16,
+                                  device=dev)
             ops.pool_keys(k_pool, block_table, ctx_len, self.ck, num_q_heads=num_q_heads)
 
     # individual stages -------------------------------------------------
@@ -232,7 +233,7 @@ class HostTierLayer:
         if k_pool is not None:
             Hkv, D = k_pool.shape[1], k_pool.shape[-1]
         else:
-            Hkv, D = ck.shape[1], ck.shape[-1]
+            Hkv, D = ck.shape[1], ck.shape[3] * 4
         self.k_pool, self.ck = k_pool, ck
         self.block_table, self.ctx_len = block_table, ctx_len
         self.host_k, self.host_v, self.host_blocks = host_pool_k_dev, host_pool_v_dev, host_blocks

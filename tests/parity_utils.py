@@ -126,3 +126,11 @@ def check_plan_row(gpu, orc, sel, slot_block_before, orc_scores, cap, step, wher
     R2 = set(np.asarray(gpu["slot_block"]).tolist()) - {-1}
     assert (R & T) <= R2 and F <= R2
     return True
+
+
+def ck_logical(ck):
+    """The compressed-key buffer [B][Hkv][ceil(W/16)][2D/8][16][8] as logical
+    [B][Hkv][16*ceil(W/16)][2][D] (block n: min row, max row)."""
+    B, Hkv, T, S, _, _ = ck.shape
+    D = S * 4
+    return ck.permute(0, 1, 2, 4, 3, 5).reshape(B, Hkv, T * 16, 2, D)

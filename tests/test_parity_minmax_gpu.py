@@ -10,7 +10,7 @@ import torch
 from lookahead_sparse_kv_amd import ops
 from lookahead_sparse_kv_amd import workload as wlm
 from oracle import oasis_oracle as orc
-from parity_utils import check_scores, check_selection_row, minmax_tolerance
+from parity_utils import check_scores, check_selection_row, ck_logical, minmax_tolerance
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -28,7 +28,8 @@ def group_rows(q_look, b, g, G):
 
 def gpu_pool(d, wl, last_only=False, ck=None):
     if ck is None:
-        ck = torch.full((wl.batch, wl.num_kv_heads, wl.table_width, 2, wl.head_dim), SENTINEL,
+        ck = torch.full(ops.compressed_keys_shape(wl.batch, wl.num_kv_heads, wl.table_width,
+                                                  wl.head_dim), SENTINEL,
                         dtype=torch.int16, device=DEV).view(torch.bfloat16)
     ops.pool_keys(dev(d["k_pool"]), dev(d["block_table"]), dev(d["ctx_len"]), ck,
                   num_q_heads=wl.num_q_heads, last_only=last_only)
@@ -38,8 +39,8 @@ def gpu_pool(d, wl, last_only=False, ck=None):
 
 def check_pooled(ck_gpu, K, ctx_len, W, where):
     want = orc.pool_keys(K, ctx_len, 16, W)
-    got = ck_gpu.float().cpu().double().numpy()
-    untouched = ck_gpu.view(torch.int16).cpu().numpy() == SENTINEL
+    got = ck_logical(ck_gpu).float().cpu().double().numpy()[:, :, :W]
+    untouched = ck_logical(ck_gpu.view(torch.int16)).cpu().numpy()[:, :, :W] == SENTINEL
     for b, ctx in enumerate(np.asarray(ctx_len)):
         nb = (int(ctx) + 15) // 16
         assert np.array_equal(got[b, :, :nb], want[b, :, :nb]), f"{where}: pooled keys differ (b{b})"
@@ -107,7 +108,7 @@ def test_score_refresh_of_out_of_range_page():
                             block_table=dev(bt))
     got = scores.cpu().numpy()
     assert np.all(np.isneginf(got[0, :, 40])) and np.all(np.isfinite(got[0, :, :40]))
-    f = ck.float().cpu()
+    f = ck_logical(ck).float().cpu()
     assert torch.all(f[0, :, 40, 0] == float("inf")) and torch.all(f[0, :, 40, 1] == -float("inf"))
 
 
@@ -141,7 +142,7 @@ def test_pool_keys_out_of_range_page_is_an_empty_box():
     bt[0, 3] = -5
     bt[0, 7] = wl.num_pages + 100
     ck = gpu_pool(dict(d, block_table=bt), wl)
-    f = ck.float().cpu()
+    f = ck_logical(ck).float().cpu()
     for n in (3, 7):
         assert torch.all(f[0, :, n, 0] == float("inf")) and torch.all(f[0, :, n, 1] == -float("inf"))
     scores = torch.empty((1, wl.num_kv_heads, wl.table_width), device=DEV)
@@ -227,7 +228,7 @@ def test_minmax_full_size_sampled_rows():
     for b, g in [(0, 0), (15, 7)] + [tuple(x) for x in rng.integers(0, [16, 8], size=(4, 2))]:
         ctx = wl.ctx[b]
         ck_row = orc.pool_keys_row(d["K"][b, g], ctx, 16, wl.table_width)
-        got_ck = ck[b, g].float().cpu().double().numpy()
+        got_ck = ck_logical(ck)[b, g].float().cpu().double().numpy()
         nb = (ctx + 15) // 16
         assert np.array_equal(got_ck[:nb], ck_row[:nb]), f"b{b} g{g}: pooled keys differ"
         rows = group_rows(d["q_look"], b, g, wl.group)
