@@ -657,7 +657,10 @@ def main():
                                  ms_per_step_of_that_loop=round(ms_per_step_with_events, 4)),
         "stages_alone_us": {k: percentiles_us(v) for k, v in alone.items()},
         "stages_back_to_back_us": {k: round(v * 1e3, 2) for k, v in b2b.items()},
-        "attn_roofline": {"kernels": "attn_partial + attn_merge", "timing": "back-to-back mean",
+        "attn_roofline": {"kernels": ("attn_row_kernel (one workgroup per row, merged in LDS)"
+                                      if wl.batch * wl.num_kv_heads >= 128 else
+                                      "attn_partial + attn_merge (split-K)"),
+                          "timing": "back-to-back mean",
                           "achieved": round(attn_gbs, 1), "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                           "algorithmic_bytes": ab},
         "detail": detail or None,

@@ -16,10 +16,12 @@
 //     exactly as the two S tiles left it in registers, and whose A operand is
 //     read straight from the dim-major value tiles (8 B per lane per block,
 //     512 contiguous bytes per load).
-// The gather is HBM-bound (each selected K and V byte is read once); split-K
-// spreads rows over enough waves to fill 256 CUs, and the next pair of
-// blocks is loaded before the current pair is computed.  A second kernel merges
-// the (max, sum, O) partials of the splits.
+// The gather is HBM-bound (each selected K and V byte is read once), and the
+// next pair of blocks is loaded before the current pair is computed.  With
+// 128 rows or more (and at most 16 query rows) one 8-wave workgroup per row
+// walks the list and merges its waves in LDS; with fewer rows split-K spreads
+// rows over enough waves to fill 256 CUs and a second kernel merges the
+// (max, sum, O) partials of the splits.
 #include "oasis_device.h"
 #include "oasis_launch.h"
 
@@ -326,6 +328,86 @@ __global__ __launch_bounds__(kAttnWaves * kWave, NT == 1 && kAttnStages == 2 ? 2
     }
 }
 
+// Rows from which attention runs as one 8-wave workgroup per row, merged in
+// LDS (no second launch); below it, split-K over more waves fills the CUs.
+#ifndef OASIS_ATTN_ROW_MIN_ROWS
+#define OASIS_ATTN_ROW_MIN_ROWS 128
+#endif
+constexpr int kRowAttnWaves = 8;
+
+__host__ __device__ inline int row_attn_wave_floats(int n_rows_q, int head_dim) {
+    return (n_rows_q * (head_dim + 2) + 3) & ~3;
+}
+
+// One workgroup per row: wave w walks a contiguous eighth of the row's list,
+// 64 entries at a time; the waves' (max, sum, O) are merged in LDS.  With
+// 128 rows it runs at the speed of split-K alone, and beside a concurrent
+// scoring launch the step is faster: it occupies one CU per row and needs no
+// merge launch.
+template <int D>
+__global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArgs a) {
+    constexpr int MT = D / 16;
+    extern __shared__ float red[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int row = blockIdx.x;
+    const int b = row / a.hkv;
+    const int g = row - b * a.hkv;
+    const int r16 = lane & 15;
+    const int j4 = lane >> 4;
+    const int nrq = a.n_rows_q;
+    const int per = (a.n_blk + kRowAttnWaves - 1) / kRowAttnWaves;
+    const int e_begin = wave * per;
+    const int e_end = e_begin + per < a.n_blk ? e_begin + per : a.n_blk;
+    bf16x8 qv[1][D / 32];
+    load_query<D, 1>(a, b, g, qv);
+    WaveAcc<D, 1> acc;
+    acc.m_run[0] = -__builtin_inff();
+    acc.l_run[0] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc.o[0][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e0 = e_begin; e0 < e_end; e0 += kWave) {
+        const int ne = e_end - e0 < kWave ? e_end - e0 : kWave;
+        attn_wave_range<D, 1>(a, row, b, g, e0, ne, qv, acc);
+    }
+    float l_run = acc.l_run[0];
+    l_run += shfl_xor_f(l_run, 16);
+    l_run += shfl_xor_f(l_run, 32);
+    const int wstride = row_attn_wave_floats(nrq, D);
+    float *wo = red + (size_t)wave * wstride;
+    float *wm = wo + (size_t)nrq * D;
+    float *wl = wm + nrq;
+    if (r16 < nrq) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            *reinterpret_cast<f32x4 *>(wo + (size_t)r16 * D + 16 * mt + 4 * j4) = acc.o[0][mt];
+        if (j4 == 0) { wm[r16] = acc.m_run[0]; wl[r16] = l_run; }
+    }
+    __syncthreads();
+    const float NEG_INF = -__builtin_inff();
+    for (int idx = threadIdx.x; idx < nrq * D; idx += kRowAttnWaves * kWave) {
+        const int c = idx / D;
+        const int d = idx - c * D;
+        float M = NEG_INF;
+#pragma unroll
+        for (int w = 0; w < kRowAttnWaves; ++w) M = fmaxf(M, red[(size_t)w * wstride + (size_t)nrq * D + c]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < kRowAttnWaves; ++w) {
+            const float *base = red + (size_t)w * wstride;
+            const float m = base[(size_t)nrq * D + c];
+            const float wgt = (m == NEG_INF) ? 0.f : exp2f(m - M);
+            L += wgt * base[(size_t)nrq * D + nrq + c];
+            O += wgt * base[(size_t)c * D + d];
+        }
+        const float res = L > 0.f ? O / L : 0.f;
+        const int iq = c / a.group;
+        const int hr = c - iq * a.group;
+        a.out[(((size_t)b * a.n_q + iq) * a.hq + (size_t)g * a.group + hr) * D + d] =
+            (uint16_t)float_to_bf16_bits(res);
+    }
+}
+
 // Merge the splits of one (row, query row) pair: thread d owns head dim d.
 template <int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
@@ -340,6 +422,15 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_
     const long long waves = (long long)rows * a.splits;
     dim3 grid((unsigned)((waves + kAttnWaves - 1) / kAttnWaves));
     dim3 block(kAttnWaves * kWave);
+    const size_t row_lds = (size_t)kRowAttnWaves * row_attn_wave_floats(a.n_rows_q, head_dim) * 4;
+    if (rows >= OASIS_ATTN_ROW_MIN_ROWS && a.n_rows_q <= 16 && row_lds <= 65536) {
+        const size_t lds = row_lds;
+        if (head_dim == 128)
+            hipLaunchKernelGGL(attn_row_kernel<128>, dim3(rows), dim3(kRowAttnWaves * kWave), lds, stream, a);
+        else
+            hipLaunchKernelGGL(attn_row_kernel<64>, dim3(rows), dim3(kRowAttnWaves * kWave), lds, stream, a);
+        return hipGetLastError();
+    }
     const bool two = a.n_rows_q > 16;
     if (head_dim == 128) {
         if (two) hipLaunchKernelGGL((attn_partial_kernel<128, 2>), grid, block, 0, stream, a);

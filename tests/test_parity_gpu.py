@@ -234,6 +234,13 @@ ATTN_CASES = {
                             3, 40, 0.0),
     "d128_g4_nq8_32_rows_short": (dict(batch=3, q_heads=8, kv_heads=2, head_dim=128,
                                        ctx=(16, 5, 700)), 8, 3, 0.0),
+    # 128 rows or more: one workgroup per row, merged in LDS
+    "d128_g4_128_rows_ragged": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128,
+                                     ctx=(700, 1601, 16, 5, 999, 1200, 33, 640)), 1, 40, 0.2),
+    "d64_g8_nq2_128_rows": (dict(batch=32, q_heads=32, kv_heads=4, head_dim=64,
+                                 ctx=(500, 777, 64, 1000)), 2, 70, 0.1),
+    "d128_g4_nq4_256_rows_long_lists": (dict(batch=32, q_heads=64, kv_heads=8, head_dim=128,
+                                             ctx=(4096, 3000)), 4, 200, 0.05),
 }
 
 
