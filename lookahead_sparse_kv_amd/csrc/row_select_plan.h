@@ -16,10 +16,10 @@
 // scans over index-contiguous chunks), so ties go to the lower index and the
 // set comes out ascending.
 //
-// Plan: every ranking is a count of the elements that beat an element
-// (integer compares, plus fp32 score compares between misses), each thread
-// deciding its own element; LDS is read 16 bytes at a time.  Exact and
-// deterministic; O(K^2) compares per row.
+// Plan: each thread owns contiguous chunks of the selection and of the slot
+// table, so positions are exclusive scans; hits are binary searches in the
+// ascending selection; only misses (among misses) and eviction candidates
+// (among candidates) are ranked by counting.  Exact and deterministic.
 #pragma once
 
 #include "oasis_device.h"
@@ -154,146 +154,266 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
 __device__ __forceinline__ int4 ld_i4(const int *p) { return *reinterpret_cast<const int4 *>(p); }
 __device__ __forceinline__ float4 ld_f4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
-// LDS of the plan: 9 arrays of Kp = roundup(K, 16) ints after `sel` (Kp ints).
+// LDS of the plan: 8 arrays of Kp = roundup(K, 16) ints after `sel` (Kp ints);
+// 9 are reserved.
 __host__ __device__ __forceinline__ int plan_pad(int K) {
     return (K + kPlanPadding - 1) / kPlanPadding * kPlanPadding;
 }
 
-// The plan of one row.  sel[0..K) (LDS) holds the selection; sel_score(i) gives
-// the fp32 score of sel[i]; slot_block / last_use / fetch_* point at this
-// row's part of the global arrays.  `pl` is 9 * Kp ints of LDS.
+// Exclusive scan of one int per thread; `total` gets the workgroup sum.
+__device__ __forceinline__ int row_exclusive_scan(int v, int *wave_sums, int &total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_up(x, d, kWave);
+        if (lane >= d) x += t;
+    }
+    if (lane == kWave - 1) wave_sums[wave] = x;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+        const int ws = wave_sums[w];
+        off += (w < wave) ? ws : 0;
+        tot += ws;
+    }
+    __syncthreads();
+    total = tot;
+    return x - v + off;
+}
+
+constexpr int kPlanMaxPer = kMaxKBlocks / kRowThreads;   // entries per thread, at most
+
+// Entries of the row's slot table this thread plans: [tid * E, tid * E + E),
+// E = ceil(K / kRowThreads), read before the selection runs.
+struct PlanPrefetch {
+    int sb[kPlanMaxPer];
+    int lu[kPlanMaxPer];
+};
+
+__device__ __forceinline__ void plan_prefetch(const int32_t *slot_block, const int32_t *last_use,
+                                              int K, PlanPrefetch &pf) {
+    const int E = (K + kRowThreads - 1) / kRowThreads;
+    const int lo = threadIdx.x * E;
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        const int j = lo + u;
+        const bool ok = u < E && j < K;
+        pf.sb[u] = ok ? slot_block[j] : -2;
+        pf.lu[u] = ok ? last_use[j] : 0;
+    }
+}
+
+// The plan of one row.  sel[0..K) (LDS) holds the selection; sel_score_of(s)
+// gives the fp32 score of block s; pf holds this thread's part of the slot
+// table (plan_prefetch); slot_block / last_use / fetch_* point at this row's
+// part of the global arrays.  `pl` is 9 * Kp ints of LDS.
+//
+// Each thread owns a contiguous chunk of selection entries and of slots, so
+// every position (the p-th fetched block in ascending order, the p-th free
+// slot) is an exclusive scan.  Hits are found by binary search in the
+// ascending selection (a selection that is not ascending is sorted first);
+// only the misses are ranked against each other by (score desc, block asc),
+// and only the eviction candidates by (last use asc, block asc).
 template <class ScoreOf>
 __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, int cap, int step,
+                                         const PlanPrefetch &pf,
                                          int32_t *slot_block, int32_t *last_use,
                                          int32_t *fetch_block, int32_t *fetch_slot,
                                          int32_t *fetch_count, int *pl, RowShared &sh) {
     const int tid = threadIdx.x;
     const int Kp = plan_pad(K);
+    const int E = (K + kRowThreads - 1) / kRowThreads;
+    const int lo = tid * E;
     float *sel_score = reinterpret_cast<float *>(pl);
-    int *miss = pl + Kp;
-    int *fetched = pl + 2 * Kp;
-    int *sb = pl + 3 * Kp;         // slot -> block as read (-1 = empty; pad -2)
-    int *lu = pl + 4 * Kp;
-    int *cand = pl + 5 * Kp;       // resident and not selected: may be evicted
-    int *sb_new = pl + 6 * Kp;
-    int *lu_new = pl + 7 * Kp;
-    int *dest = pl + 8 * Kp;       // destination slot of the p-th fetched block
+    int *sb = pl + Kp;             // slot -> block as read (-1 = empty)
+    int *lu = pl + 2 * Kp;
+    int *hit_sel = pl + 3 * Kp;    // per selection entry: resident
+    int *fill = pl + 4 * Kp;       // per slot: block fetched into it, -1
+    int *dest = pl + 5 * Kp;       // destination slot of the p-th fetched block
+    float *m_score = reinterpret_cast<float *>(pl + 6 * Kp);   // misses; later candidates' last use
+    int *m_block = pl + 7 * Kp;                                 // misses; later candidates' block
 
-    if (tid == 0) { sh.digit = 0; sh.above = 0; }    // reused as counters: free slots, fetches
     for (int i = tid; i < Kp; i += kRowThreads) {
-        if (i < K) {
-            const int s = sel[i];
-            sel_score[i] = s >= 0 ? sel_score_of(s) : 0.f;
-            const int blk = slot_block[i];
-            sb[i] = blk < 0 ? -1 : blk;
-            lu[i] = last_use[i];
-        } else {
-            sel[i] = -1;
-            sel_score[i] = 0.f;
-            sb[i] = -2;
-            lu[i] = 0;
-        }
-        miss[i] = 0;
-        fetched[i] = 0;
-        cand[i] = 0;
+        if (i >= K) sel[i] = -1;
+        hit_sel[i] = 0;
+        fill[i] = -1;
         dest[i] = -1;
     }
-    __syncthreads();
-
-    for (int j = tid; j < K; j += kRowThreads) {      // hits and eviction candidates
-        const int blk = sb[j];
-        bool hit = false;
-        if (blk >= 0) {
-#pragma unroll 4
-            for (int i = 0; i < Kp; i += 4) {
-                const int4 v = ld_i4(sel + i);
-                hit |= (v.x == blk) | (v.y == blk) | (v.z == blk) | (v.w == blk);
+    bool unsorted = false;
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        const int j = lo + u;
+        if (u < E && j < K) {
+            sb[j] = pf.sb[u] < 0 ? -1 : pf.sb[u];
+            lu[j] = pf.lu[u];
+            if (j + 1 < K) {
+                const int x = sel[j], y = sel[j + 1];
+                unsorted |= (x < 0 && y >= 0) || (x >= 0 && y >= 0 && x >= y);
             }
         }
-        cand[j] = (blk >= 0 && !hit) ? 1 : 0;
-        sb_new[j] = blk;
-        lu_new[j] = hit ? step : lu[j];
-        if (blk == -1) atomicAdd(&sh.digit, 1);
     }
-    for (int i = tid; i < K; i += kRowThreads) {      // misses
-        const int blk = sel[i];
-        bool resident = false;
-        if (blk >= 0) {
-#pragma unroll 4
-            for (int j = 0; j < Kp; j += 4) {
-                const int4 v = ld_i4(sb + j);
-                resident |= (v.x == blk) | (v.y == blk) | (v.z == blk) | (v.w == blk);
+    if (__syncthreads_or(unsorted)) {
+        // not ascending: order by (valid first, block, entry) into fill / dest, then back
+        int key_s[kPlanMaxPer];
+#pragma unroll
+        for (int u = 0; u < kPlanMaxPer; ++u) {
+            const int i = lo + u;
+            key_s[u] = -1;
+            if (u < E && i < K) {
+                const int x = sel[i];
+                // valid entries by (block, entry), then the invalid ones (blocks < 2^31,
+                // entries < 2^11)
+                const long long kx = x < 0 ? (1LL << 50) + i : ((long long)x << 11) + i;
+                int r = 0;
+                for (int j = 0; j < K; ++j) {
+                    const int y = sel[j];
+                    const long long ky = y < 0 ? (1LL << 50) + j : ((long long)y << 11) + j;
+                    r += ky < kx;
+                }
+                key_s[u] = r;
             }
         }
-        miss[i] = (blk >= 0 && !resident) ? 1 : 0;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kPlanMaxPer; ++u)
+            if (key_s[u] >= 0) fill[key_s[u]] = sel[lo + u];
+        __syncthreads();
+        for (int i = tid; i < K; i += kRowThreads) { sel[i] = fill[i]; fill[i] = -1; }
+        __syncthreads();
     }
-    __syncthreads();
-
-    for (int i = tid; i < K; i += kRowThreads) {      // rank misses: (score desc, block asc)
-        if (!miss[i]) continue;
-        const int blk = sel[i];
-        const float s = sel_score[i];
-        int rank = 0;
-#pragma unroll 4
-        for (int i2 = 0; i2 < Kp; i2 += 4) {
-            const int4 m = ld_i4(miss + i2);
-            const int4 b2 = ld_i4(sel + i2);
-            const float4 s2 = ld_f4(sel_score + i2);
-            rank += m.x & ((s2.x > s) | ((s2.x == s) & (b2.x < blk)));
-            rank += m.y & ((s2.y > s) | ((s2.y == s) & (b2.y < blk)));
-            rank += m.z & ((s2.z > s) | ((s2.z == s) & (b2.z < blk)));
-            rank += m.w & ((s2.w > s) | ((s2.w == s) & (b2.w < blk)));
-        }
-        if (rank < cap) { fetched[i] = 1; atomicAdd(&sh.above, 1); }
+    for (int i = tid; i < Kp; i += kRowThreads) {
+        const int x = sel[i];
+        sel_score[i] = (i < K && x >= 0) ? sel_score_of(x) : 0.f;
     }
-    __syncthreads();
-    const int nfree = sh.digit;
-    const int nF = sh.above;
+    // valid selection entries: an ascending prefix
+    int my_valid = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u)
+        my_valid += (u < E && lo + u < K && sel[lo + u] >= 0) ? 1 : 0;
+    int m_valid;
+    row_exclusive_scan(my_valid, sh.wave_sums, m_valid);   // ends with a barrier: sb, lu visible
 
-    for (int j = tid; j < K; j += kRowThreads) {      // free slots, then LRU victims
-        if (sb[j] == -1) {
-            int pos = 0;
-#pragma unroll 4
-            for (int j2 = 0; j2 < Kp; j2 += 4) {
-                const int4 v = ld_i4(sb + j2);
-                pos += (v.x == -1) & (j2 < j);
-                pos += (v.y == -1) & (j2 + 1 < j);
-                pos += (v.z == -1) & (j2 + 2 < j);
-                pos += (v.w == -1) & (j2 + 3 < j);
+    // hits: every resident block is looked up in the selection
+    bool hit[kPlanMaxPer], empty[kPlanMaxPer], cand[kPlanMaxPer];
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        const int j = lo + u;
+        hit[u] = empty[u] = cand[u] = false;
+        if (u < E && j < K) {
+            const int blk = sb[j];
+            if (blk >= 0) {
+                int l = 0, h = m_valid;                    // first entry >= blk
+                while (l < h) {
+                    const int mid = (l + h) >> 1;
+                    if (sel[mid] < blk) l = mid + 1; else h = mid;
+                }
+                if (l < m_valid && sel[l] == blk) { hit[u] = true; hit_sel[l] = 1; }
+                cand[u] = !hit[u];
+            } else {
+                empty[u] = true;
             }
-            if (pos < nF) dest[pos] = j;
-        } else if (cand[j] && nF > nfree) {
-            const int l0 = lu[j], b0 = sb[j];
-            int rank = 0;
-#pragma unroll 4
-            for (int j2 = 0; j2 < Kp; j2 += 4) {
-                const int4 c = ld_i4(cand + j2);
-                const int4 l2 = ld_i4(lu + j2);
-                const int4 b2 = ld_i4(sb + j2);
-                rank += c.x & ((l2.x < l0) | ((l2.x == l0) & (b2.x < b0)));
-                rank += c.y & ((l2.y < l0) | ((l2.y == l0) & (b2.y < b0)));
-                rank += c.z & ((l2.z < l0) | ((l2.z == l0) & (b2.z < b0)));
-                rank += c.w & ((l2.w < l0) | ((l2.w == l0) & (b2.w < b0)));
-            }
-            if (rank < nF - nfree) dest[nfree + rank] = j;
         }
     }
     __syncthreads();
-
-    for (int i = tid; i < K; i += kRowThreads) {      // p-th fetched block (ascending) -> dest[p]
-        if (!fetched[i]) continue;
-        const int blk = sel[i];
-        int p = 0;
-#pragma unroll 4
-        for (int i2 = 0; i2 < Kp; i2 += 4) {
-            const int4 f = ld_i4(fetched + i2);
-            const int4 b2 = ld_i4(sel + i2);
-            p += (f.x & (b2.x < blk)) + (f.y & (b2.y < blk)) + (f.z & (b2.z < blk)) + (f.w & (b2.w < blk));
+    // misses, compacted in ascending block order
+    bool miss[kPlanMaxPer];
+    int my_miss = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        const int i = lo + u;
+        miss[u] = u < E && i < K && sel[i] >= 0 && !hit_sel[i];
+        my_miss += miss[u];
+    }
+    int M;
+    int mpos = row_exclusive_scan(my_miss, sh.wave_sums, M);
+    int mp[kPlanMaxPer];
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        mp[u] = -1;
+        if (miss[u]) {
+            mp[u] = mpos;
+            m_score[mpos] = sel_score[lo + u];
+            m_block[mpos] = sel[lo + u];
+            ++mpos;
         }
-        const int d = dest[p];
-        fetch_block[p] = blk;
-        fetch_slot[p] = d;
-        if (d >= 0) { sb_new[d] = blk; lu_new[d] = step; }
+    }
+    __syncthreads();
+    // the first min(M, cap) misses by (score desc, block asc) are fetched
+    bool fetched[kPlanMaxPer];
+    int my_f = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        fetched[u] = false;
+        if (miss[u]) {
+            if (M <= cap) {
+                fetched[u] = true;
+            } else {
+                const float sc = m_score[mp[u]];
+                const int blk = m_block[mp[u]];
+                int rank = 0;
+                for (int q = 0; q < M; ++q) {
+                    const float s2 = m_score[q];
+                    rank += (s2 > sc) | ((s2 == sc) & (m_block[q] < blk));
+                }
+                fetched[u] = rank < cap;
+            }
+        }
+        my_f += fetched[u];
+    }
+    int nF;
+    int fpos = row_exclusive_scan(my_f, sh.wave_sums, nF);
+    // destinations: the empty slots in ascending order, then LRU victims
+    int my_empty = 0, my_cand = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) { my_empty += empty[u]; my_cand += cand[u]; }
+    int nfree;
+    int epos = row_exclusive_scan(my_empty, sh.wave_sums, nfree);
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u)
+        if (empty[u]) {
+            if (epos < nF) dest[epos] = lo + u;
+            ++epos;
+        }
+    if (nF > nfree) {                                   // uniform across the workgroup
+        int C;
+        int cpos = row_exclusive_scan(my_cand, sh.wave_sums, C);
+#pragma unroll
+        for (int u = 0; u < kPlanMaxPer; ++u) {
+            if (cand[u]) {
+                m_score[cpos] = __int_as_float(lu[lo + u]);
+                m_block[cpos] = sb[lo + u];
+                ++cpos;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kPlanMaxPer; ++u) {
+            if (cand[u]) {
+                const int l0 = lu[lo + u], b0 = sb[lo + u];
+                int rank = 0;
+                for (int q = 0; q < C; ++q) {
+                    const int l2 = __float_as_int(m_score[q]);
+                    rank += (l2 < l0) | ((l2 == l0) & (m_block[q] < b0));
+                }
+                if (rank < nF - nfree) dest[nfree + rank] = lo + u;
+            }
+        }
+    }
+    __syncthreads();
+    // the p-th fetched block (ascending) goes to dest[p]
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        if (fetched[u]) {
+            const int blk = sel[lo + u];
+            const int d = dest[fpos];
+            fetch_block[fpos] = blk;
+            fetch_slot[fpos] = d;
+            if (d >= 0) fill[d] = blk;
+            ++fpos;
+        }
     }
     for (int p = nF + tid; p < cap; p += kRowThreads) {
         fetch_block[p] = -1;
@@ -301,9 +421,14 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
     }
     if (tid == 0) *fetch_count = nF;
     __syncthreads();
-    for (int j = tid; j < K; j += kRowThreads) {
-        slot_block[j] = sb_new[j];
-        last_use[j] = lu_new[j];
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        const int j = lo + u;
+        if (u < E && j < K) {
+            const int f = fill[j];
+            slot_block[j] = f >= 0 ? f : sb[j];
+            last_use[j] = (f >= 0 || hit[u]) ? step : lu[j];
+        }
     }
 }
 

@@ -35,6 +35,8 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
     const float *srow = a.scores + (size_t)row * a.width;
     const size_t rk = (size_t)row * K;
 
+    PlanPrefetch pf;
+    if (MODE & 2) plan_prefetch(a.slot_block + rk, a.last_use + rk, K, pf);   // in flight during the select
     if (MODE & 1) {
         const int nb = row_valid_blocks(a.ctx_len, row / a.hkv, a.width);
         load_row_keys(srow, nb, keys);
@@ -53,10 +55,10 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
         int32_t *fb = a.fetch_block + (size_t)row * a.cap;
         int32_t *fs = a.fetch_slot + (size_t)row * a.cap;
         if (MODE & 1)
-            row_plan(sel, [&](int s) { return key_to_score(keys[s]); }, K, a.cap, a.step,
+            row_plan(sel, [&](int s) { return key_to_score(keys[s]); }, K, a.cap, a.step, pf,
                      a.slot_block + rk, a.last_use + rk, fb, fs, a.fetch_count + row, pl, sh);
         else
-            row_plan(sel, [&](int s) { return srow[s]; }, K, a.cap, a.step, a.slot_block + rk,
+            row_plan(sel, [&](int s) { return srow[s]; }, K, a.cap, a.step, pf, a.slot_block + rk,
                      a.last_use + rk, fb, fs, a.fetch_count + row, pl, sh);
     }
 }

@@ -146,6 +146,8 @@ PLAN_CASES = [
     (2, 2, 64, 5, 0, "normal", 5),              # cap 0: nothing moves but the hits
     (1, 3, 40, 1, 1, "zeros", None),
     (2, 2, 1000, 300, 7, "ties", None),         # K above the one-wave limit (generic kernel)
+    (1, 2, 2000, 1000, 30, "normal", None),     # the largest K: four entries per thread
+    (2, 2, 600, 128, 9, "shuffled", None),      # a selection not in ascending order
 ]
 
 
@@ -162,8 +164,10 @@ def test_plan_fetch_bit_exact_over_steps(case):
     fs = torch.empty_like(fb)
     fc = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
     for step in range(10, 22):
-        s = _random_scores(rng, B, Hkv, W, mode)
+        s = _random_scores(rng, B, Hkv, W, "normal" if mode == "shuffled" else mode)
         sel = orc.select(s.astype(np.float64), ctx_len, 16, K)
+        if mode == "shuffled":          # the plan does not depend on the order of the selection
+            sel = np.ascontiguousarray(rng.permuted(sel, axis=-1))
         ofb, ofs, ocnt, sb, lu = orc.plan(sel, s.astype(np.float64), sb, lu, cap, step)
         ops.plan_fetch(shape, dev(torch.from_numpy(sel)), dev(torch.from_numpy(s)), K, cap, step,
                        g_sb, g_lu, fb if cap else None, fs if cap else None, fc)
