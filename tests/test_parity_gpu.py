@@ -284,19 +284,20 @@ def test_sparse_attention_matches_oracle(name):
     assert np.all(np.isfinite(got))
 
 
-def test_sparse_attention_working_set_mode():
+@pytest.mark.parametrize("batch,kv_heads", [(2, 2), (32, 4)])     # split-K; one workgroup per row
+def test_sparse_attention_working_set_mode(batch, kv_heads):
     # slots -> pages of a separate working-set pool; blk = NULL, blk_logical = slot table
-    wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(3000, 2000), n_hot=0,
-                            seed=23)
+    wl = wlm.small_workload(batch=batch, q_heads=4 * kv_heads, kv_heads=kv_heads, head_dim=128,
+                            ctx=(3000, 2000), n_hot=0, seed=23)
     d = wlm.make_layer(wl)
-    K = 24
+    K, Hkv, Hq = 24, kv_heads, 4 * kv_heads
     rng = np.random.default_rng(24)
     slot_block = _random_lists(rng, wl, K, 0.25)
     # working-set pool: page = b * K + slot, holding (for every head) that head's slot block
-    ws_k = torch.zeros((wl.batch * K, 2, 16, 128), dtype=torch.bfloat16)
-    ws_v = torch.zeros((wl.batch * K, 2, 128, 16), dtype=torch.bfloat16)
+    ws_k = torch.zeros((wl.batch * K, Hkv, 16, 128), dtype=torch.bfloat16)
+    ws_v = torch.zeros((wl.batch * K, Hkv, 128, 16), dtype=torch.bfloat16)
     for b in range(wl.batch):
-        for g in range(2):
+        for g in range(Hkv):
             for j in range(K):
                 n = slot_block[b, g, j]
                 if n >= 0:
@@ -304,10 +305,10 @@ def test_sparse_attention_working_set_mode():
                     ws_k[b * K + j, g] = d["k_pool"][p, g]
                     ws_v[b * K + j, g] = d["v_pool"][p, g]
     page_table = torch.arange(wl.batch * K, dtype=torch.int32).view(wl.batch, K)
-    shape = ops.make_shape(wl.batch, 8, 2, 128, K, wl.batch * K)
-    q = torch.randn((wl.batch, 1, 8, 128), generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
+    shape = ops.make_shape(wl.batch, Hq, Hkv, 128, K, wl.batch * K)
+    q = torch.randn((wl.batch, 1, Hq, 128), generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
     ws = torch.zeros(ops.attn_workspace_bytes(shape, 1, K) // 4 + 4, device=DEV)
-    out = torch.empty((wl.batch, 1, 8, 128), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((wl.batch, 1, Hq, 128), dtype=torch.bfloat16, device=DEV)
     ops.sparse_decode_attn(shape, dev(q), dev(ws_k), dev(ws_v), dev(page_table), None,
                            dev(torch.from_numpy(slot_block)), dev(d["ctx_len"]), out, ws)
     want = orc.attn(q[:, 0], d["K"], d["V"], d["ctx_len"], 16, slot_block)
