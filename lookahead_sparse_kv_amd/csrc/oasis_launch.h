@@ -75,7 +75,6 @@ struct PoolArgs {
     int batch, hkv, width, num_pages, last_only;
 };
 
-// Block scores from the compressed keys.
 // Block scores from the compressed keys; with k_pool set, the last block of
 // each sequence is first re-pooled from the key pool (ck written) and scored
 // from the fresh values.

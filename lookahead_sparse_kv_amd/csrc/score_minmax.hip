@@ -25,6 +25,7 @@
 // wave reads compressed keys another wave writes.
 #include "oasis_device.h"
 #include "oasis_launch.h"
+#include "pool_block.h"
 
 #ifndef OASIS_MINMAX_CPOL
 #define OASIS_MINMAX_CPOL 2      // non-temporal: each compressed key is read once per step
@@ -37,14 +38,14 @@ constexpr int kMmTiles = 4;            // 16-block tiles per wave
 constexpr int kMmBlocksPerWave = kMmTiles * kBlockTokens;
 
 // Refresh wave of one row: pool the last block (ceil(ctx / 16) - 1) from the
-// key pool as oasis_pool_keys does (load i, lane l: token l % 16 of the
-// 8-dimension slice 4i + l / 16), write its compressed row, and score it from
-// the fresh values: after the fold every lane of 16-lane group g4 holds the
-// min and max of slices 4i + g4; lane l takes lookahead row l % 16, sums over
-// its group's slices, and the sums are folded over the four groups.
+// key pool with the same helper as oasis_pool_keys (a group of lanes per
+// 8-dimension slice), write its compressed slices, and score the block from
+// the fresh values.
 template <int D>
 __device__ __forceinline__ void refresh_last_block(const MinmaxArgs &a, int row) {
-    constexpr int NI = D / 32;
+    using G = PoolGeom<D>;
+    constexpr int kRowsPerLane = kMaxRowsQ / G::kLanes;   // lookahead rows per lane
+    constexpr uint32_t kTileBytes = kBlockTokens * D * 2;
     const int lane = threadIdx.x & (kWave - 1);
     const int b = row / a.hkv;
     const int g = row - b * a.hkv;
@@ -55,93 +56,62 @@ __device__ __forceinline__ void refresh_last_block(const MinmaxArgs &a, int row)
     if (nb == 0) return;
     const int n = nb - 1;
     const int nt = (int)(ctx - (long long)n * kBlockTokens);
-    const int t = lane & 15;
-    const int g4 = lane >> 4;
+    const int s = lane / G::kLanes;          // the slice this lane pools and scores
+    const int t0 = lane % G::kLanes;
     float *out = a.scores + (size_t)row * a.width;
+    uint16_t *ck_min = a.ck + ck_slice_offset(row, a.width, n, s, D);
+    uint16_t *ck_max = a.ck + ck_slice_offset(row, a.width, n, G::kSlices + s, D);
     const int page = a.block_table[(size_t)b * a.width + n];
     if (page < 0 || page >= a.num_pages) {
-        if (t == 0) {
-            const u32x4 pinf = {0x7f807f80u, 0x7f807f80u, 0x7f807f80u, 0x7f807f80u};
-            const u32x4 ninf = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, 4 * i + g4, D)) = pinf;
-                *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, D / 8 + 4 * i + g4, D)) = ninf;
-            }
+        if (t0 == 0) {
+            *reinterpret_cast<u32x4 *>(ck_min) =
+                u32x4{kBf16PosInfPair, kBf16PosInfPair, kBf16PosInfPair, kBf16PosInfPair};
+            *reinterpret_cast<u32x4 *>(ck_max) =
+                u32x4{kBf16NegInfPair, kBf16NegInfPair, kBf16NegInfPair, kBf16NegInfPair};
         }
         if (lane == 0) out[n] = -__builtin_inff();
         return;
     }
-    const uint16_t *tile = a.k_pool + ((size_t)page * a.hkv + g) * kBlockTokens * D;
-    u32x4 v[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-        v[i] = *reinterpret_cast<const u32x4 *>(tile + (size_t)i * 512 + lane * 8);
-    float mn[NI][8], mx[NI][8];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const bool ok = t < nt;
-            const float lo = bf16_bits_to_float(v[i][w] & 0xffffu);
-            const float hi = bf16_bits_to_float(v[i][w] >> 16);
-            mn[i][2 * w] = ok ? lo : __builtin_inff();
-            mx[i][2 * w] = ok ? lo : -__builtin_inff();
-            mn[i][2 * w + 1] = ok ? hi : __builtin_inff();
-            mx[i][2 * w + 1] = ok ? hi : -__builtin_inff();
-        }
+    u32x4 v[G::kLoads];
+    pool_load<D, 0>(make_rsrc(a.k_pool + ((size_t)page * a.hkv + g) * kBlockTokens * D, kTileBytes),
+                    pool_lane_offset<D>(lane), v);
+    float mn[8], mx[8];
+    pool_slice<D>(v, nt, lane, mn, mx);
+    if (t0 == 0) {
+        *reinterpret_cast<u32x4 *>(ck_min) = pack_exact_bf16x8(mn);
+        *reinterpret_cast<u32x4 *>(ck_max) = pack_exact_bf16x8(mx);
     }
+    // Lane (s, t0) bounds slice s for lookahead rows t0 + kLanes * k; the
+    // slices are then summed (lanes of equal t0) and the rows maximised.
+    float part[kRowsPerLane];
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                mn[i][e] = fminf(mn[i][e], shfl_xor_f(mn[i][e], off));
-                mx[i][e] = fmaxf(mx[i][e], shfl_xor_f(mx[i][e], off));
-            }
-        }
-    }
-    if (t == 0) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            u32x4 pmn, pmx;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                pmn[w] = (__builtin_bit_cast(uint32_t, mn[i][2 * w]) >> 16) |
-                         (__builtin_bit_cast(uint32_t, mn[i][2 * w + 1]) & 0xffff0000u);
-                pmx[w] = (__builtin_bit_cast(uint32_t, mx[i][2 * w]) >> 16) |
-                         (__builtin_bit_cast(uint32_t, mx[i][2 * w + 1]) & 0xffff0000u);
-            }
-            *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, 4 * i + g4, D)) = pmn;
-            *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, D / 8 + 4 * i + g4, D)) = pmx;
-        }
-    }
-    // lookahead row r = lane % 16 over this group's slices, then the other groups
-    const int r = t;
-    float part = 0.f;
-    if (r < a.n_rows_q) {
-        const int jd = r / a.group;
-        const int hr = r - jd * a.group;
-        const uint16_t *qrow = a.q_look +
-            (((size_t)b * a.n_look + jd) * a.hq + (size_t)g * a.group + hr) * D;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const u32x4 qw = load_u32x4(qrow + 8 * (4 * i + g4));
+    for (int k = 0; k < kRowsPerLane; ++k) {
+        const int r = t0 + G::kLanes * k;
+        part[k] = 0.f;
+        if (r < a.n_rows_q) {
+            const int jd = r / a.group;
+            const int hr = r - jd * a.group;
+            const u32x4 qw = load_u32x4(a.q_look +
+                (((size_t)b * a.n_look + jd) * a.hq + (size_t)g * a.group + hr) * D + 8 * s);
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const float q0 = bf16_bits_to_float(qw[w] & 0xffffu);
                 const float q1 = bf16_bits_to_float(qw[w] >> 16);
-                part += q0 < 0.f ? q0 * mn[i][2 * w] : q0 * mx[i][2 * w];
-                part += q1 < 0.f ? q1 * mn[i][2 * w + 1] : q1 * mx[i][2 * w + 1];
+                part[k] += q0 < 0.f ? q0 * mn[2 * w] : q0 * mx[2 * w];
+                part[k] += q1 < 0.f ? q1 * mn[2 * w + 1] : q1 * mx[2 * w + 1];
             }
         }
     }
-    part += shfl_xor_f(part, 16);
-    part += shfl_xor_f(part, 32);
-    float best = r < a.n_rows_q ? part : -__builtin_inff();
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) best = fmaxf(best, shfl_xor_f(best, off));
+    for (int off = G::kLanes; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < kRowsPerLane; ++k) part[k] += shfl_xor_f(part[k], off);
+    float best = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < kRowsPerLane; ++k)
+        if (t0 + G::kLanes * k < a.n_rows_q) best = fmaxf(best, part[k]);
+#pragma unroll
+    for (int off = 1; off < G::kLanes; off <<= 1) best = fmaxf(best, shfl_xor_f(best, off));
     if (lane == 0) out[n] = best * a.scale;
 }
 
