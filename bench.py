@@ -125,12 +125,24 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
 
 
-def cpu_baseline(wl, d, n_seqs, cap):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, d, n_seqs, cap, cpu_work_s=16.0, max_steps=400):
     """Time the oracle's whole decode step on the first n_seqs sequences (every
-    KV head), starting from the same seeded resident state as the GPU."""
+    KV head), starting from the same seeded resident state as the GPU: on all of
+    the host's threads, consecutive steps until about cpu_work_s core-seconds of
+    work, and one step on a single thread."""
     from lookahead_sparse_kv_amd import workload as wlm
     from oracle import oasis_oracle as orc
-    import numpy as np
     import torch
     n = min(n_seqs, wl.batch)
     K = d["K"][:n].double().numpy()
@@ -152,24 +164,57 @@ def cpu_baseline(wl, d, n_seqs, cap):
             _, _, _, sb2, lu2 = orc.plan(sel, sc, sb_, lu_, cap_, t)
             orc.attn(q, K, V, ctx, 16, sb2)
             return sb2, lu2
-
-        sb, lu = step(prev, wl.k_blocks, -1, sb, lu)
-        t0 = time.perf_counter()
-        step(q_look, cap, 0, sb, lu)
-        dt = time.perf_counter() - t0
-        what = "compressed-key score+select+plan+attention step"
+        what = "compressed-key score+select+plan+attention steps"
     else:
-        seed_run = orc.decode_step(prev, q, K, V, ctx, 16, wl.table_width, wl.k_blocks,
-                                   wl.k_blocks, -1, sb, lu)
-        t0 = time.perf_counter()
-        orc.decode_step(q_look, q, K, V, ctx, 16, wl.table_width, wl.k_blocks, cap, 0,
-                        seed_run["slot_block"], seed_run["last_use"])
-        dt = time.perf_counter() - t0
-        what = "score+select+plan+attention step"
-    return {"value": n / dt, "unit": "seq-decode-steps/s", "cores": orc.max_threads(),
+        def step(ql, cap_, t, sb_, lu_):
+            r = orc.decode_step(ql, q, K, V, ctx, 16, wl.table_width, wl.k_blocks, cap_, t, sb_, lu_)
+            return r["slot_block"], r["last_use"]
+        what = "score+select+plan+attention steps"
+    sb, lu = step(prev, wl.k_blocks, -1, sb, lu)
+    cores = orc.max_threads()
+    target = max(1.0, cpu_work_s / cores)
+    steps, t = 0, 0
+    t0 = time.perf_counter()
+    while steps < max_steps:
+        sb, lu = step(q_look, cap, t, sb, lu)
+        steps, t = steps + 1, t + 1
+        if time.perf_counter() - t0 >= target:
+            break
+    dt = time.perf_counter() - t0
+    orc.set_threads(1)
+    try:
+        t1 = time.perf_counter()
+        step(q_look, cap, t, sb, lu)
+        dt1 = time.perf_counter() - t1
+    finally:
+        orc.set_threads(cores)
+    return {"value": n * steps / dt, "unit": "seq-decode-steps/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{n} of {wl.batch} sequences x {wl.num_kv_heads} KV heads, one full "
-                      f"{what} in fp64 ({dt:.2f} s)"}
+            "single_thread": {"value": float(f"{n / dt1:.4g}"), "seconds_per_step": float(f"{dt1:.4g}")},
+            "cpu_model": cpu_model(),
+            "sample": f"{n} of {wl.batch} sequences x {wl.num_kv_heads} KV heads, {steps} consecutive "
+                      f"{what} in fp64 on {cores} threads ({dt:.2f} s wall, about {dt * cores:.0f} "
+                      f"core-seconds), then one step on one thread ({dt1:.3g} s)"}
+
+
+def topk_agreement(layer, looks, q):
+    """Mean over lookahead draws and rows of |top-K(lookahead) & top-K(true query)| / K,
+    both selected by the layer's own scorer (the Figure 4 comparison, synthetic)."""
+    import torch
+    from lookahead_sparse_kv_amd import study
+    K = layer.k_blocks
+    layer.score(q)
+    layer.select()
+    torch.cuda.synchronize()
+    sel_true = layer.sel.cpu().numpy()
+    fr = []
+    for ql in looks:
+        layer.score(ql)
+        layer.select()
+        torch.cuda.synchronize()
+        fr.append(study.overlap_fraction(layer.sel.cpu().numpy(), sel_true, K).mean())
+    return {"lookahead_vs_true_query": round(float(sum(fr) / len(fr)), 4), "draws": len(looks),
+            "rows": int(sel_true.shape[0] * sel_true.shape[1]), "k_blocks": K}
 
 
 def _ev():
@@ -597,6 +642,25 @@ def main():
         torch.cuda.synchronize()
         b2b[k] = e0.elapsed_time(e1) / args.steps
 
+    pool_build = None
+    if wl.scorer == "minmax":
+        # the compressed-key build (prefill-time work, not in the step): every
+        # block of every row pooled again, replicas in turn
+        n_pool = max(4, n_rep)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_pool):
+            L = layers[i % n_rep]
+            ops.pool_keys(L.k_pool, L.block_table, L.ctx_len, L.ck, num_q_heads=wl.num_q_heads)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / n_pool * 1e3
+        kb = wl.batch * wl.num_kv_heads * wl.ctx_max * wl.head_dim * 2
+        ckb = wl.batch * wl.num_kv_heads * wl.table_width * 2 * wl.head_dim * 2
+        pool_build = {"us": round(us, 2), "key_bytes": kb, "compressed_bytes": ckb,
+                      "GBps": round((kb + ckb) / us / 1e3, 1),
+                      "frac_of_8TBps": round((kb + ckb) / us / 8e6, 3)}
+
     detail = {}
     if args.detail:
         # the same steps without the overlap
@@ -612,6 +676,7 @@ def main():
         detail["ms_per_step_no_overlap"] = round(e2.elapsed_time(e3) / args.steps, 4)
 
     fetched = int(layer.fetch_count.sum().item())
+    agreement = topk_agreement(layer, looks, q)
 
     sb = score_bytes(wl)
     achieved = sb / (mean_ms["score"] * 1e-3) / 1e9
@@ -665,6 +730,8 @@ def main():
                           "algorithmic_bytes": ab},
         "detail": detail or None,
         "fetched_blocks_last_step": fetched,
+        "topk_agreement": agreement,
+        "pool_keys_build": pool_build,
         "wall_ms_timed_region": round(wall_ms, 2),
         "input_generation_s": round(gen_s, 1),
         "cpu_baseline": cpu,

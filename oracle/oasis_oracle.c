@@ -540,3 +540,18 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* Threads of the following parallel regions (for timing the oracle on one core
+ * or on all of them); returns the count now in effect. */
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    extern int omp_get_max_threads(void);
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}

@@ -44,13 +44,14 @@ def _load():
         lib.oracle_decode_step.argtypes = [i, i, i, i, i, i, i, p_i, i, p_d, p_d, p_d, p_d,
                                            i, i, i, p_d, p_i, p_i, p_i, p_i, p_i, p_i, p_d]
         lib.oracle_max_threads.argtypes = []
+        lib.oracle_set_threads.argtypes = [i]
         lib.oracle_pool_keys_row.argtypes = [i, i, i, p_d, i, p_d]
         lib.oracle_score_minmax_row.argtypes = [i, i, i, i, p_d, p_d, i, p_d]
         lib.oracle_pool_keys.argtypes = [i, i, i, i, i, i, p_i, p_d, p_d]
         lib.oracle_score_minmax.argtypes = [i, i, i, i, i, i, p_i, i, p_d, p_d, p_d]
         for name in ("oracle_score_row", "oracle_select_row", "oracle_plan_row",
                      "oracle_attn_row", "oracle_score", "oracle_select", "oracle_plan",
-                     "oracle_attn", "oracle_decode_step", "oracle_max_threads",
+                     "oracle_attn", "oracle_decode_step", "oracle_max_threads", "oracle_set_threads",
                      "oracle_pool_keys_row", "oracle_score_minmax_row", "oracle_pool_keys",
                      "oracle_score_minmax"):
             getattr(lib, name).restype = ctypes.c_int
@@ -87,6 +88,11 @@ def _check(rc, what):
 
 def max_threads() -> int:
     return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> int:
+    """Threads of the oracle's later parallel loops; returns the count in effect."""
+    return int(_load().oracle_set_threads(int(n)))
 
 
 # ---------------------------------------------------------------- per row
