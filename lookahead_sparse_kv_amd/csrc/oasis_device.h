@@ -94,4 +94,64 @@ __device__ __forceinline__ int readlane_i(int v, int lane) {
     return __builtin_amdgcn_readlane(v, lane);
 }
 
+// DPP lane moves (register-only, no LDS traffic).  mov_dpp<CTRL>(v) is v of
+// the lane that CTRL selects, 0 where that lane is outside the row.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowShr1 = 0x111;     // row_shr:k = 0x110 + k
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowMirror = 0x140;   // lane i <- lane 15 - i within each 16 lanes
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i within each 8 lanes
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row into the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 into rows 2 and 3
+
+template <int CTRL>
+__device__ __forceinline__ int mov_dpp(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, mov_dpp<CTRL>(__builtin_bit_cast(int, v)));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele within each
+// 16-lane row (row shifts by 1, 2, 4, 8 with zero fill), then the row totals
+// carried across rows by the two row broadcasts.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += mov_dpp<kDppRowShr1>(x);
+    x += mov_dpp<kDppRowShr2>(x);
+    x += mov_dpp<kDppRowShr4>(x);
+    x += mov_dpp<kDppRowShr8>(x);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xa, 0xf, false);   // rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xc, 0xf, false);   // rows 2, 3
+    return x;
+}
+
+// Minimum / maximum over the wave (every lane gets it): a fold within each
+// 16-lane row by quad exchanges and mirrors, then the four rows' results.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    uint32_t t;
+    t = (uint32_t)mov_dpp<kDppQuadXor1>((int)v); v = t < v ? t : v;
+    t = (uint32_t)mov_dpp<kDppQuadXor2>((int)v); v = t < v ? t : v;
+    t = (uint32_t)mov_dpp<kDppHalfMirror>((int)v); v = t < v ? t : v;
+    t = (uint32_t)mov_dpp<kDppRowMirror>((int)v); v = t < v ? t : v;
+    const uint32_t a = (uint32_t)readlane_i((int)v, 0), b = (uint32_t)readlane_i((int)v, 16);
+    const uint32_t c = (uint32_t)readlane_i((int)v, 32), d = (uint32_t)readlane_i((int)v, 48);
+    const uint32_t ab = a < b ? a : b, cd = c < d ? c : d;
+    return ab < cd ? ab : cd;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    uint32_t t;
+    t = (uint32_t)mov_dpp<kDppQuadXor1>((int)v); v = t > v ? t : v;
+    t = (uint32_t)mov_dpp<kDppQuadXor2>((int)v); v = t > v ? t : v;
+    t = (uint32_t)mov_dpp<kDppHalfMirror>((int)v); v = t > v ? t : v;
+    t = (uint32_t)mov_dpp<kDppRowMirror>((int)v); v = t > v ? t : v;
+    const uint32_t a = (uint32_t)readlane_i((int)v, 0), b = (uint32_t)readlane_i((int)v, 16);
+    const uint32_t c = (uint32_t)readlane_i((int)v, 32), d = (uint32_t)readlane_i((int)v, 48);
+    const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
+}
+
 }  // namespace oasis

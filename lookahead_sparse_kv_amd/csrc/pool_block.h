@@ -41,15 +41,6 @@ __device__ __forceinline__ void pool_load(rsrc_t r, uint32_t lane_off,
         v[i] = buf_load16<CPOL>(r, lane_off, i * PoolGeom<D>::kLanes * 16);
 }
 
-// v from the lane `CTRL` selects (a DPP control: quad permutation or mirror).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
-}
-constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
-constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i within each 8 lanes
-
 template <int D, bool FULL>
 __device__ __forceinline__ void pool_slice_tokens(const u32x4 (&v)[PoolGeom<D>::kLoads], int nt,
                                                   int t0, float (&mn)[8], float (&mx)[8]) {

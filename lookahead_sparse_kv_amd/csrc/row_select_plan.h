@@ -9,12 +9,12 @@
 //
 // Selection (kRowThreads threads, keys in LDS): scores become order-preserving
 // 32-bit keys (-0.0 equals +0.0).  The K-th largest key tau is found exactly by
-// a radix select over three digits (11, 11 and 10 bits): an LDS histogram of
-// the keys that still match the prefix, a workgroup scan over the bins from the
-// top, and the bin where the count crosses the remaining K.  Keys above tau are
-// taken, and copies of tau fill the rest in ascending block order (ordered
-// scans over index-contiguous chunks), so ties go to the lower index and the
-// set comes out ascending.
+// a radix select over digits of at most 11 bits of u - kmin (the row's own key
+// range): an LDS histogram of the keys that still match the prefix, a
+// workgroup scan over the bins from the top, and the bin where the count
+// crosses the remaining K.  Keys above tau are taken, and copies of tau fill
+// the rest in ascending block order (ordered scans over index-contiguous
+// chunks), so ties go to the lower index and the set comes out ascending.
 //
 // Plan: each thread owns contiguous chunks of the selection and of the slot
 // table, so positions are exclusive scans; hits are binary searches in the
@@ -38,17 +38,38 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Scores of one row into LDS as keys.  A thread's loads (8 per round) are all
-// issued before the first is used, so the row costs one memory latency per
-// 2,048 blocks instead of one per 256.
-__device__ __forceinline__ void load_row_keys(const float *srow, int nb, uint32_t *keys) {
+// Scores of one row into LDS as keys, for the row's valid blocks n < nb;
+// returns nb.  A thread's loads (8 per round of 2,048 blocks) are all issued
+// before the first is used, from indices clamped into the row (always in
+// bounds of the [B][Hkv][W] scores, with no branch around the loads), so the
+// first round does not wait for the context length, which is loaded beside it
+// and applied when the keys are written.
+__device__ __forceinline__ int load_row_keys(const float *srow, int width, const int32_t *ctx_p,
+                                             uint32_t *keys) {
     constexpr int U = 8;
-    for (int n0 = 0; n0 < nb; n0 += kRowThreads * U) {
-        float v[U];
+    constexpr int kRound = kRowThreads * U;
+    if (width <= 0) return 0;
+    const int ctx_raw = *ctx_p;
+    const int last = width - 1;
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int n = u * kRowThreads + (int)threadIdx.x;
+        v[u] = srow[n < width ? n : last];
+    }
+    const int ctx = ctx_raw < 0 ? 0 : ctx_raw;
+    const int c = (ctx + kBlockTokens - 1) / kBlockTokens;
+    const int nb = c > width ? width : c;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int n = u * kRowThreads + (int)threadIdx.x;
+        if (n < nb) keys[n] = score_key(v[u]);
+    }
+    for (int n0 = kRound; n0 < nb; n0 += kRound) {      // rows of more than 2,048 blocks
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int n = n0 + u * kRowThreads + (int)threadIdx.x;
-            v[u] = n < nb ? srow[n] : 0.f;
+            v[u] = srow[n < width ? n : last];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -56,17 +77,14 @@ __device__ __forceinline__ void load_row_keys(const float *srow, int nb, uint32_
             if (n < nb) keys[n] = score_key(v[u]);
         }
     }
+    return nb;
 }
 
 // Inclusive scan of one int per thread over the workgroup (two barriers).
 __device__ __forceinline__ int row_inclusive_scan(int v, int *wave_sums) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int t = __shfl_up(v, d, kWave);
-        if (lane >= d) v += t;
-    }
+    v = wave_inclusive_scan(v);
     if (lane == kWave - 1) wave_sums[wave] = v;
     __syncthreads();
     int off = 0;
@@ -79,43 +97,89 @@ __device__ __forceinline__ int row_inclusive_scan(int v, int *wave_sums) {
 struct RowShared {
     int hist[kHistBins];
     int wave_sums[kRowWaves];
-    int digit, above, total;
+    uint32_t wave_min[kRowWaves], wave_max[kRowWaves];
+    int digit, above, count;
 };
 
 // Top-K of `nb` keys (keys[0..nb), already in LDS) into sel[0..K): ascending,
 // -1 padded.  Ends with a barrier; sel may then be read by every thread.
+//
+// The radix digits are taken from u - kmin over the row's own key range
+// [kmin, kmax], the first one being the top 11 bits of that span: block scores
+// share one or two exponents, so digits taken from the raw keys would put
+// nearly every key in a handful of bins and serialise the LDS atomics.  A pass
+// that finds the threshold bin holding exactly the keys still to take ends the
+// search: every key from that bin's base up is taken, with no tie to split.
 __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, int *sel,
                                            RowShared &sh) {
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     if (nb <= K) {
         for (int i = tid; i < K; i += kRowThreads) sel[i] = i < nb ? i : -1;
         __syncthreads();
         return;
     }
-    uint32_t prefix = 0, pmask = 0;
+    // the row's key range (and the first histogram cleared)
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    for (int n = tid; n < nb; n += kRowThreads) {
+        const uint32_t u = keys[n];
+        kmn = u < kmn ? u : kmn;
+        kmx = u > kmx ? u : kmx;
+    }
+    kmn = wave_min_u32(kmn);
+    kmx = wave_max_u32(kmx);
+    if (lane == 0) { sh.wave_min[wave] = kmn; sh.wave_max[wave] = kmx; }
+    for (int i = tid; i < kHistBins; i += kRowThreads) sh.hist[i] = 0;
+    __syncthreads();
+    uint32_t kmin = sh.wave_min[0], kmax = sh.wave_max[0];
+#pragma unroll
+    for (int w = 1; w < kRowWaves; ++w) {
+        kmin = sh.wave_min[w] < kmin ? sh.wave_min[w] : kmin;
+        kmax = sh.wave_max[w] > kmax ? sh.wave_max[w] : kmax;
+    }
+    const uint32_t span = kmax - kmin;
+    const int span_bits = span ? 32 - __builtin_clz(span) : 0;
+    int width = span_bits < 11 ? (span_bits > 0 ? span_bits : 1) : 11;   // bits of this digit
+    int shift = span_bits > 11 ? span_bits - 11 : 0;                     // its lowest bit
+    uint32_t prefix = 0, pmask = 0;               // over u - kmin
     int krem = K;                                 // still to take among keys matching the prefix
+    bool whole = false;                           // the threshold bin is taken whole
 #pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const int nbins = pass == 2 ? 1024 : 2048;
-        for (int i = tid; i < nbins; i += kRowThreads) sh.hist[i] = 0;
-        __syncthreads();
+    for (int pass = 0;; ++pass) {
+        const int nbins = 1 << width;
+        const int sbins = nbins > kRowThreads ? nbins : kRowThreads;   // bins scanned (rest zero)
+        if (pass > 0) {
+            for (int i = tid; i < sbins; i += kRowThreads) sh.hist[i] = 0;
+            __syncthreads();
+        }
         for (int n = tid; n < nb; n += kRowThreads) {
-            const uint32_t u = keys[n];
-            if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1);
+            const uint32_t d = keys[n] - kmin;
+            if ((d & pmask) == prefix) atomicAdd(&sh.hist[(d >> shift) & (uint32_t)(nbins - 1)], 1);
         }
         __syncthreads();
         // thread t owns `per` bins counted from the top: bins hi, hi-1, .., lo
-        const int per = nbins / kRowThreads;
-        const int hi = nbins - 1 - tid * per;
+        // (its counts held in registers for the search below)
+        const int per = sbins / kRowThreads;
+        const int hi = sbins - 1 - tid * per;
+        int h[kHistBins / kRowThreads];
         int local = 0;
-        for (int j = 0; j < per; ++j) local += sh.hist[hi - j];
+#pragma unroll
+        for (int j = 0; j < kHistBins / kRowThreads; ++j) {
+            h[j] = j < per ? sh.hist[hi - j >= 0 ? hi - j : 0] : 0;
+            local += h[j];
+        }
         const int incl = row_inclusive_scan(local, sh.wave_sums);
         int acc = incl - local;                   // keys in bins above hi
         if (acc < krem && krem <= incl) {
-            for (int j = 0; j < per; ++j) {
-                const int c = sh.hist[hi - j];
-                if (acc + c >= krem) { sh.digit = hi - j; sh.above = acc; break; }
+            bool found = false;
+#pragma unroll
+            for (int j = 0; j < kHistBins / kRowThreads; ++j) {
+                const int c = h[j];
+                if (!found && j < per && acc + c >= krem) {
+                    sh.digit = hi - j; sh.above = acc; sh.count = c;
+                    found = true;
+                }
                 acc += c;
             }
         }
@@ -123,9 +187,15 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
         prefix |= (uint32_t)sh.digit << shift;
         pmask |= (uint32_t)(nbins - 1) << shift;
         krem -= sh.above;
-        __syncthreads();                          // digit / above are rewritten next pass
+        whole = sh.count == krem;
+        __syncthreads();                          // digit / above / count are rewritten next pass
+        if (whole || shift == 0) break;
+        width = shift < 11 ? shift : 11;
+        shift -= width;
     }
-    const uint32_t tau = prefix;                  // the K-th largest key; krem copies of it are taken
+    // whole: every key >= tau is taken (exactly K); otherwise tau is the K-th
+    // largest key, and keys above it plus its first krem copies are taken.
+    const uint32_t tau = kmin + prefix;
 
     const int E = (nb + kRowThreads - 1) / kRowThreads;
     const int lo = tid * E;
@@ -133,8 +203,8 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
     int c_gt = 0, c_eq = 0;
     for (int n = lo; n < hi; ++n) {
         const uint32_t u = keys[n];
-        c_gt += u > tau;
-        c_eq += u == tau;
+        c_gt += whole ? u >= tau : u > tau;
+        c_eq += !whole && u == tau;
     }
     const int eq_before = row_inclusive_scan(c_eq, sh.wave_sums) - c_eq;
     int take_eq = krem - eq_before;
@@ -144,8 +214,8 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
     int er = eq_before;
     for (int n = lo; n < hi; ++n) {
         const uint32_t u = keys[n];
-        bool take = u > tau;
-        if (u == tau) { take = er < krem; ++er; }
+        bool take = whole ? u >= tau : u > tau;
+        if (!whole && u == tau) { take = er < krem; ++er; }
         if (take) sel[pos++] = n;
     }
     __syncthreads();
@@ -164,12 +234,7 @@ __host__ __device__ __forceinline__ int plan_pad(int K) {
 __device__ __forceinline__ int row_exclusive_scan(int v, int *wave_sums, int &total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    int x = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int t = __shfl_up(x, d, kWave);
-        if (lane >= d) x += t;
-    }
+    const int x = wave_inclusive_scan(v);
     if (lane == kWave - 1) wave_sums[wave] = x;
     __syncthreads();
     int off = 0, tot = 0;
@@ -187,7 +252,10 @@ __device__ __forceinline__ int row_exclusive_scan(int v, int *wave_sums, int &to
 constexpr int kPlanMaxPer = kMaxKBlocks / kRowThreads;   // entries per thread, at most
 
 // Entries of the row's slot table this thread plans: [tid * E, tid * E + E),
-// E = ceil(K / kRowThreads), read before the selection runs.
+// E = ceil(K / kRowThreads), read before the selection runs.  The loads are
+// unconditional, from indices clamped into the row (K >= 1), and nothing here
+// uses them, so they stay in flight through the selection; the plan reads
+// only the entries with u < E and tid * E + u < K.
 struct PlanPrefetch {
     int sb[kPlanMaxPer];
     int lu[kPlanMaxPer];
@@ -200,9 +268,9 @@ __device__ __forceinline__ void plan_prefetch(const int32_t *slot_block, const i
 #pragma unroll
     for (int u = 0; u < kPlanMaxPer; ++u) {
         const int j = lo + u;
-        const bool ok = u < E && j < K;
-        pf.sb[u] = ok ? slot_block[j] : -2;
-        pf.lu[u] = ok ? last_use[j] : 0;
+        const int jc = j < K ? j : K - 1;
+        pf.sb[u] = slot_block[jc];
+        pf.lu[u] = last_use[jc];
     }
 }
 

@@ -13,13 +13,6 @@ __device__ __forceinline__ float key_to_score(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
-__device__ __forceinline__ int row_valid_blocks(const int32_t *ctx_len, int b, int width) {
-    int ctx = ctx_len[b];
-    ctx = ctx < 0 ? 0 : ctx;
-    const int nb = (ctx + kBlockTokens - 1) / kBlockTokens;
-    return nb > width ? width : nb;
-}
-
 // MODE 1 = select, 2 = plan (selection read from a.sel), 3 = select then plan.
 template <int MODE>
 __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlanArgs a) {
@@ -38,8 +31,7 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
     PlanPrefetch pf;
     if (MODE & 2) plan_prefetch(a.slot_block + rk, a.last_use + rk, K, pf);   // in flight during the select
     if (MODE & 1) {
-        const int nb = row_valid_blocks(a.ctx_len, row / a.hkv, a.width);
-        load_row_keys(srow, nb, keys);
+        const int nb = load_row_keys(srow, a.width, a.ctx_len + row / a.hkv, keys);
         __syncthreads();
         row_select(keys, nb, K, sel, sh);
         if (a.sel)
