@@ -116,6 +116,31 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, mov_dpp<CTRL>(__builtin_bit_cast(int, v)));
 }
 
+// v combined (max or sum) with v of lane ^ 16 / lane ^ 32, through the gfx950
+// row swaps (v_permlane16_swap / v_permlane32_swap on two copies of v): the
+// two results hold v and its partner's v in every lane, so a commutative
+// combine of them is the exchange-and-combine, with no LDS traffic.
+__device__ __forceinline__ float max_xor16(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float add_xor16(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele within each
 // 16-lane row (row shifts by 1, 2, 4, 8 with zero fill), then the row totals
 // carried across rows by the two row broadcasts.

@@ -200,8 +200,7 @@ __global__ __launch_bounds__(kMmWaves * kWave) void score_minmax_kernel(MinmaxAr
         float m = NEG_INF;
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = (4 * j4 + i < a.n_rows_q) ? fmaxf(m, s[i]) : m;
-        m = fmaxf(m, shfl_xor_f(m, 16));
-        m = fmaxf(m, shfl_xor_f(m, 32));
+        m = max_xor32(max_xor16(m));
         const int n = n0 + t * kBlockTokens + r16;
         if (j4 == 0 && n < a.width && !(refresh && n == nb - 1)) {   // the refresh wave scores nb - 1
             // lanes j4 = 0 hold min[0..7] (k-step 0) and max[0..7] (k-step QK) of block r16

@@ -197,8 +197,7 @@ __device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int 
                         mb = fmaxf(mb, x[u][q4]);
                     }
                 }
-                mb = fmaxf(mb, shfl_xor_f(mb, 16));
-                mb = fmaxf(mb, shfl_xor_f(mb, 32));
+                mb = max_xor32(max_xor16(mb));
                 const float m_new = fmaxf(acc.m_run[t], mb);   // finite: the pair has a valid token
                 const float alpha = exp2f(acc.m_run[t] - m_new);
                 uint32_t pw[2][2];
@@ -312,8 +311,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave, NT == 1 && kAttnStages == 2 ? 2
     for (int t = 0; t < NT; ++t) {
         // Column totals of the normaliser live in lanes r16, r16+16, r16+32, r16+48.
         float l_run = acc.l_run[t];
-        l_run += shfl_xor_f(l_run, 16);
-        l_run += shfl_xor_f(l_run, 32);
+        l_run = add_xor32(add_xor16(l_run));
         const int c = 16 * t + r16;
         if (c < a.n_rows_q) {
             const size_t slot = ((size_t)row * a.splits + split) * a.n_rows_q + c;
@@ -371,8 +369,7 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArg
         attn_wave_range<D, 1>(a, row, b, g, e0, ne, qv, acc);
     }
     float l_run = acc.l_run[0];
-    l_run += shfl_xor_f(l_run, 16);
-    l_run += shfl_xor_f(l_run, 32);
+    l_run = add_xor32(add_xor16(l_run));
     const int wstride = row_attn_wave_floats(nrq, D);
     float *wo = red + (size_t)wave * wstride;
     float *wm = wo + (size_t)nrq * D;
