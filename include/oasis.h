@@ -12,7 +12,7 @@
  *   oasis_select_topk        top-K blocks per KV head under the budget
  *   oasis_plan_fetch         resident diff + fetch cap + LRU eviction, which
  *                            updates the per-head working-set table
- *   oasis_sparse_decode_attn split-K decode attention over the working set
+ *   oasis_sparse_decode_attn sparse paged decode attention over the working set
  *
  * and, for the pages' own compressed-key scorer, oasis_pool_keys (min/max
  * pooling of the keys) and oasis_score_blocks_minmax (scores from them).
@@ -209,8 +209,12 @@ int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *
                       int32_t *fetch_slot, int32_t *fetch_count, void *stream);
 
 /*
- * Bytes of device workspace oasis_sparse_decode_attn needs for this shape
- * (split-K partial results).  Returns 0 for an invalid shape.
+ * Bytes of device workspace oasis_sparse_decode_attn needs for this shape:
+ * room for the split-K partial results (per row and split: max, sum and the
+ * D-wide output of each query row).  With 128 rows or more and at most 16
+ * query rows per KV head (whose eight per-wave partials fit in 64 KiB of LDS)
+ * the call runs one workgroup per row and leaves the workspace untouched; the
+ * size asked for covers either way.  Returns 0 for an invalid shape.
  */
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk);
 
