@@ -88,6 +88,14 @@ def _random_scores(rng, B, Hkv, W, mode):
         s = rng.choice(np.array([0.0, -0.0, 1.0, -1.0], dtype=np.float32), size=(B, Hkv, W))
     elif mode == "inf":
         s[rng.random(s.shape) < 0.3] = -np.inf
+    elif mode == "equal":                       # one key value: an empty key range
+        s = np.full((B, Hkv, W), 1.5, dtype=np.float32)
+    elif mode == "narrow":                      # a key range of a few ulps, many repeats
+        s = (np.float32(2.5) + np.float32(1e-6) * s).astype(np.float32)
+    elif mode == "outliers":                    # a narrow bulk and a few large hot blocks
+        s = (np.float32(2.5) + np.float32(0.01) * s).astype(np.float32)
+        hot = rng.random(s.shape) < 0.05
+        s[hot] = (10.0 + rng.random(int(hot.sum()))).astype(np.float32)
     return s
 
 
@@ -104,6 +112,10 @@ SELECT_CASES = [
     (1, 1, [0], 8, "normal"),                         # empty context
     (2, 2, [2048 * 16, 1900 * 16], 300, "ties"),      # K above the one-wave limit
     (2, 2, [2049 * 16, 3000 * 16], 128, "normal"),    # table wider than the one-wave limit
+    (2, 4, [32768, 30000], 128, "equal"),             # every key equal: lowest indices win
+    (2, 4, [32768, 7000], 128, "narrow"),
+    (2, 4, [32768, 32768], 128, "outliers"),          # digits over a range the outliers set
+    (1, 2, [8192 * 16], 1000, "narrow"),              # several rounds of loads, large K
 ]
 
 
@@ -189,6 +201,9 @@ def test_plan_fetch_bit_exact_over_steps(case):
     (2, 2, 100, 128, 25, "normal"),             # fewer blocks than K
     (2, 2, 4000, 128, 2, "normal"),             # wider than the one-wave select: two launches
     (2, 2, 1000, 300, 7, "ties"),               # K above the one-wave limit: two launches
+    (2, 4, 2048, 128, 6, "outliers"),
+    (2, 2, 2048, 128, 2, "equal"),
+    (2, 2, 1500, 64, 3, "narrow"),
 ], ids=lambda c: f"nb{c[2]}K{c[3]}cap{c[4]}{c[5]}")
 def test_select_plan_fused_bit_exact_over_steps(case):
     B, Hkv, nb, K, cap, mode = case
