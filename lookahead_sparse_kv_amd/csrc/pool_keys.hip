@@ -8,15 +8,16 @@
 //   (16n + t < ctx_len[b]) of the block.
 // Both are bf16 values of the keys themselves, so the pooling is exact.
 //
-// Design: a wave pools four consecutive blocks of one (sequence, KV head)
-// row.  The loads of all four key tiles are issued first (non-temporal: the
-// whole pool is streamed once), then each tile is reduced as the shared
-// pooling helper describes: a group of lanes per 8-dimension slice, min/max in
-// registers over the lane's tokens, DPP folds over the group.  A page outside
-// the pool is not read: the block is written as an empty box (min = +inf,
-// max = -inf), which the compressed scorer turns into -inf.  The last-block
-// mode re-pools only block ceil(ctx / 16) - 1 of each sequence: the one a
-// decode step appends its token to.
+// Design: the whole-pool build gives a wave one compressed tile (16
+// consecutive blocks of a row); the loads of four blocks are in flight while
+// the previous four are reduced, as the shared pooling helper describes (a
+// group of lanes per 8-dimension slice, min/max in registers over the lane's
+// tokens, DPP folds over the group); the tile is staged in LDS and written in
+// 1 KiB contiguous stores.  A page outside the pool is not read: the block is
+// written as an empty box (min = +inf, max = -inf), which the compressed
+// scorer turns into -inf.  The last-block mode re-pools only block
+// ceil(ctx / 16) - 1 of each sequence: the one a decode step appends its
+// token to.
 #include "oasis_device.h"
 #include "oasis_launch.h"
 #include "pool_block.h"
@@ -24,11 +25,11 @@
 namespace oasis {
 
 constexpr int kPoolWaves = 4;
-constexpr int kPoolChunk = 4;           // blocks per wave
 #ifndef OASIS_POOL_CPOL
 #define OASIS_POOL_CPOL 2               // key tiles: non-temporal (each is read once)
 #endif
 
+// Last-block mode: one wave per row re-pools block ceil(ctx / 16) - 1.
 template <int D>
 __global__ __launch_bounds__(kPoolWaves * kWave) void pool_keys_kernel(PoolArgs a) {
     using G = PoolGeom<D>;
@@ -37,72 +38,144 @@ __global__ __launch_bounds__(kPoolWaves * kWave) void pool_keys_kernel(PoolArgs 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const long long gw = (long long)blockIdx.x * kPoolWaves + wave;
     const int rows = a.batch * a.hkv;
-    const int chunks = (a.width + kPoolChunk - 1) / kPoolChunk;
-    int row, n0 = 0;
-    if (a.last_only) {
-        if (gw >= rows) return;
-        row = (int)gw;
-    } else {
-        row = (int)(gw / chunks);
-        if (row >= rows) return;
-        n0 = (int)(gw - (long long)row * chunks) * kPoolChunk;
-    }
+    if (gw >= rows) return;
+    const int row = (int)gw;
     const int b = row / a.hkv;
     const int g = row - b * a.hkv;
     long long ctx = a.ctx_len[b];
     const long long cmax = (long long)a.width * kBlockTokens;
     ctx = ctx < 0 ? 0 : (ctx > cmax ? cmax : ctx);
     const int nb = (int)((ctx + kBlockTokens - 1) / kBlockTokens);
-    int count;
-    if (a.last_only) {
-        n0 = nb - 1;
-        count = nb > 0 ? 1 : 0;
-    } else {
-        count = nb - n0 < kPoolChunk ? nb - n0 : kPoolChunk;
+    if (nb <= 0) return;
+    const int n = nb - 1;
+    const int page = a.block_table[(size_t)b * a.width + n];
+    const bool present = page >= 0 && page < a.num_pages;
+    const int s = lane / G::kLanes;
+    u32x4 pmn = {kBf16PosInfPair, kBf16PosInfPair, kBf16PosInfPair, kBf16PosInfPair};
+    u32x4 pmx = {kBf16NegInfPair, kBf16NegInfPair, kBf16NegInfPair, kBf16NegInfPair};
+    if (present) {
+        u32x4 v[G::kLoads];
+        pool_load<D, 0>(make_rsrc(a.k_pool + ((size_t)page * a.hkv + g) * kBlockTokens * D, kTileBytes),
+                        pool_lane_offset<D>(lane), v);
+        long long nt = ctx - (long long)n * kBlockTokens;
+        nt = nt > kBlockTokens ? kBlockTokens : nt;
+        float mn[8], mx[8];
+        pool_slice<D>(v, (int)nt, lane, mn, mx);
+        pmn = pack_exact_bf16x8(mn);
+        pmx = pack_exact_bf16x8(mx);
     }
+    if (lane % G::kLanes == 0) {
+        *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, s, D)) = pmn;
+        *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, G::kSlices + s, D)) = pmx;
+    }
+}
+
+// The whole-pool build: a wave pools one compressed tile (16 consecutive
+// blocks of a row), four blocks at a time with the next four loading, and
+// stages the results in its own LDS region laid out as the tile is in memory
+// ([2D/8 slices][16 blocks][8 elements], a slice padded to 17 entries so
+// that the 16 writer lanes hit different banks).  The tile then leaves in
+// 1 KiB contiguous non-temporal stores instead of 16-byte slices 256 bytes
+// apart (which cost a third of the kernel's time).  Blocks past the context
+// are not written, as in the per-block kernel.
+constexpr int kPoolTileBlocks = 16;      // blocks per compressed tile
+constexpr int kPoolGroup = 4;            // blocks loaded together
+
+template <int D>
+__global__ __launch_bounds__(kPoolWaves * kWave) void pool_tiles_kernel(PoolArgs a) {
+    using G = PoolGeom<D>;
+    constexpr uint32_t kTileBytes = kBlockTokens * D * 2;
+    constexpr int kSlots = 2 * G::kSlices;                      // min slices, then max slices
+    constexpr int kPad = kPoolTileBlocks + 1;
+    constexpr int kEntries = kSlots * kPoolTileBlocks;          // 16-byte entries of a tile
+    __shared__ u32x4 stage[kPoolWaves][kSlots * kPad];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const long long gw = (long long)blockIdx.x * kPoolWaves + wave;
+    const int rows = a.batch * a.hkv;
+    const int tiles = (a.width + kPoolTileBlocks - 1) / kPoolTileBlocks;
+    const int row = (int)(gw / tiles);
+    if (row >= rows) return;
+    const int n0 = (int)(gw - (long long)row * tiles) * kPoolTileBlocks;
+    const int b = row / a.hkv;
+    const int g = row - b * a.hkv;
+    long long ctx = a.ctx_len[b];
+    const long long cmax = (long long)a.width * kBlockTokens;
+    ctx = ctx < 0 ? 0 : (ctx > cmax ? cmax : ctx);
+    const int nb = (int)((ctx + kBlockTokens - 1) / kBlockTokens);
+    const int count = nb - n0 < kPoolTileBlocks ? nb - n0 : kPoolTileBlocks;
     if (count <= 0) return;
 
     const uint32_t off = pool_lane_offset<D>(lane);
-    u32x4 v[kPoolChunk][G::kLoads];
-    bool present[kPoolChunk];
-#pragma unroll
-    for (int u = 0; u < kPoolChunk; ++u) {
-        const int page = u < count ? a.block_table[(size_t)b * a.width + n0 + u] : -1;
-        present[u] = page >= 0 && page < a.num_pages;
-        const rsrc_t r = present[u]
-            ? make_rsrc(a.k_pool + ((size_t)page * a.hkv + g) * kBlockTokens * D, kTileBytes)
-            : make_rsrc(a.k_pool, 0u);
-        pool_load<D, OASIS_POOL_CPOL>(r, off, v[u]);
-    }
     const int s = lane / G::kLanes;
     const bool writer = lane % G::kLanes == 0;
+    u32x4 *st = stage[wave];
+    u32x4 v[2][kPoolGroup][G::kLoads];
+    bool present[kPoolTileBlocks];
+    auto issue = [&](int buf, int grp) {
 #pragma unroll
-    for (int u = 0; u < kPoolChunk; ++u) {
-        if (u >= count) break;
-        const int n = n0 + u;
-        u32x4 pmn = {kBf16PosInfPair, kBf16PosInfPair, kBf16PosInfPair, kBf16PosInfPair};
-        u32x4 pmx = {kBf16NegInfPair, kBf16NegInfPair, kBf16NegInfPair, kBf16NegInfPair};
-        if (present[u]) {
-            long long nt = ctx - (long long)n * kBlockTokens;
-            nt = nt > kBlockTokens ? kBlockTokens : nt;
-            float mn[8], mx[8];
-            pool_slice<D>(v[u], (int)nt, lane, mn, mx);
-            pmn = pack_exact_bf16x8(mn);
-            pmx = pack_exact_bf16x8(mx);
+        for (int u = 0; u < kPoolGroup; ++u) {
+            const int j = grp * kPoolGroup + u;
+            const int page = j < count ? a.block_table[(size_t)b * a.width + n0 + j] : -1;
+            present[j] = page >= 0 && page < a.num_pages;
+            const rsrc_t r = present[j]
+                ? make_rsrc(a.k_pool + ((size_t)page * a.hkv + g) * kBlockTokens * D, kTileBytes)
+                : make_rsrc(a.k_pool, 0u);
+            pool_load<D, OASIS_POOL_CPOL>(r, off, v[buf][u]);
         }
-        if (writer) {
-            *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, s, D)) = pmn;
-            *reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n, G::kSlices + s, D)) = pmx;
+    };
+    issue(0, 0);
+#pragma unroll
+    for (int grp = 0; grp < kPoolTileBlocks / kPoolGroup; ++grp) {
+        if (grp + 1 < kPoolTileBlocks / kPoolGroup) issue((grp + 1) & 1, grp + 1);
+#pragma unroll
+        for (int u = 0; u < kPoolGroup; ++u) {
+            const int j = grp * kPoolGroup + u;
+            if (j >= count) break;
+            u32x4 pmn = {kBf16PosInfPair, kBf16PosInfPair, kBf16PosInfPair, kBf16PosInfPair};
+            u32x4 pmx = {kBf16NegInfPair, kBf16NegInfPair, kBf16NegInfPair, kBf16NegInfPair};
+            if (present[j]) {
+                long long nt = ctx - (long long)(n0 + j) * kBlockTokens;
+                nt = nt > kBlockTokens ? kBlockTokens : nt;
+                float mn[8], mx[8];
+                pool_slice<D>(v[grp & 1][u], (int)nt, lane, mn, mx);
+                pmn = pack_exact_bf16x8(mn);
+                pmx = pack_exact_bf16x8(mx);
+            }
+            if (writer) {
+                st[s * kPad + j] = pmn;
+                st[(G::kSlices + s) * kPad + j] = pmx;
+            }
         }
+    }
+    // the wave reads back what its own lanes staged
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    u32x4 *tile = reinterpret_cast<u32x4 *>(a.ck + ck_slice_offset(row, a.width, n0, 0, D));
+#pragma unroll
+    for (int i = 0; i < kEntries / kWave; ++i) {
+        const int e = i * kWave + lane;                 // slot e / 16, block e % 16
+        const int j = e % kPoolTileBlocks;
+        if (j < count) __builtin_nontemporal_store(st[(e / kPoolTileBlocks) * kPad + j], &tile[e]);
     }
 }
 
 hipError_t launch_pool_keys(const PoolArgs &a, int head_dim, hipStream_t stream) {
     const long long rows = (long long)a.batch * a.hkv;
-    const long long waves = a.last_only ? rows : rows * ((a.width + kPoolChunk - 1) / kPoolChunk);
-    if (waves == 0) return hipSuccess;
-    const dim3 grid((unsigned)((waves + kPoolWaves - 1) / kPoolWaves));
     const dim3 block(kPoolWaves * kWave);
+    if (!a.last_only) {
+        const long long waves = rows * ((a.width + kPoolTileBlocks - 1) / kPoolTileBlocks);
+        if (waves == 0) return hipSuccess;
+        const dim3 grid((unsigned)((waves + kPoolWaves - 1) / kPoolWaves));
+        if (head_dim == 128)
+            hipLaunchKernelGGL(pool_tiles_kernel<128>, grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL(pool_tiles_kernel<64>, grid, block, 0, stream, a);
+        return hipGetLastError();
+    }
+    if (rows == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + kPoolWaves - 1) / kPoolWaves));
     if (head_dim == 128)
         hipLaunchKernelGGL(pool_keys_kernel<128>, grid, block, 0, stream, a);
     else
