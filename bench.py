@@ -53,6 +53,8 @@ def parse():
                         "successive steps, so that no step finds the previous one's "
                         "working set in the 256 MB last-level cache (as in a model, "
                         "where consecutive layers hold different KV)")
+    p.add_argument("--plan-stream", choices=("auto", "on", "off"), default="auto",
+                   help="select + plan on a third stream (auto: with the compressed scorer)")
     p.add_argument("--detail", action="store_true",
                    help="also time the steps without overlap and each stage alone")
     return p.parse_args()
@@ -563,7 +565,8 @@ def main():
     # for t + 1 overlaps the next layers' attention (measured faster); exact
     # scorer: scoring bounds the step and select/plan stays on the caller's
     # stream (a third stream measured slower there).
-    plan_stream = torch.cuda.Stream(device=dev) if wl.scorer == "minmax" else None
+    use_plan_stream = (wl.scorer == "minmax") if args.plan_stream == "auto" else args.plan_stream == "on"
+    plan_stream = torch.cuda.Stream(device=dev) if use_plan_stream else None
     pipes = [PipelinedDecode(L, side=side, plan_stream=plan_stream) for L in layers]
     # compressed scorer: each scoring launch also re-pools the block a decode
     # step appends to (the pool itself is not written here)
@@ -712,6 +715,7 @@ def main():
                    "k_blocks": wl.k_blocks, "fetch_ratio": wl.ratios[0], "cap": cap,
                    "n_look": wl.n_look, "scorer": wl.scorer,
                    "step": "score + select/plan + attn, one layer",
+                   "streams": 3 if plan_stream is not None else 2,
                    "replicas": n_rep,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": SCORE_KERNELS[wl.scorer][0],
