@@ -94,11 +94,17 @@ __device__ __forceinline__ int row_inclusive_scan(int v, int *wave_sums) {
     return v + off;
 }
 
+constexpr int kRankMax = 64;             // threshold bins this small are ranked directly
+
 struct RowShared {
     int hist[kHistBins];
     int wave_sums[kRowWaves];
     uint32_t wave_min[kRowWaves], wave_max[kRowWaves];
     int digit, above, count;
+    uint32_t gkey[kRankMax];                // keys of a small threshold bin
+    int gidx[kRankMax];
+    int ngather, gt_in_bin;
+    uint32_t tau;
 };
 
 // Top-K of `nb` keys (keys[0..nb), already in LDS) into sel[0..K): ascending,
@@ -110,6 +116,9 @@ struct RowShared {
 // nearly every key in a handful of bins and serialise the LDS atomics.  A pass
 // that finds the threshold bin holding exactly the keys still to take ends the
 // search: every key from that bin's base up is taken, with no tie to split.
+// A threshold bin of at most kRankMax keys ends it too: those keys are
+// gathered and ranked against each other (key descending, then block index
+// ascending), which gives the K-th largest key exactly.
 __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, int *sel,
                                            RowShared &sh) {
     const int tid = threadIdx.x;
@@ -183,13 +192,42 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
                 acc += c;
             }
         }
+        if (tid == 0) sh.ngather = 0;
         __syncthreads();
         prefix |= (uint32_t)sh.digit << shift;
         pmask |= (uint32_t)(nbins - 1) << shift;
         krem -= sh.above;
         whole = sh.count == krem;
+        const int cnt = sh.count;
         __syncthreads();                          // digit / above / count are rewritten next pass
         if (whole || shift == 0) break;
+        if (cnt <= kRankMax) {
+            // the cnt keys left in the threshold bin, ranked directly
+            for (int n = tid; n < nb; n += kRowThreads) {
+                const uint32_t u = keys[n];
+                if (((u - kmin) & pmask) == prefix) {
+                    const int slot = atomicAdd(&sh.ngather, 1);
+                    sh.gkey[slot] = u;
+                    sh.gidx[slot] = n;
+                }
+            }
+            __syncthreads();
+            if (tid < cnt) {
+                const uint32_t kj = sh.gkey[tid];
+                const int ij = sh.gidx[tid];
+                int rank = 0, gt = 0;
+                for (int i = 0; i < cnt; ++i) {
+                    const uint32_t ki = sh.gkey[i];
+                    rank += (ki > kj) | ((ki == kj) & (sh.gidx[i] < ij));
+                    gt += ki > kj;
+                }
+                if (rank == krem - 1) { sh.tau = kj; sh.gt_in_bin = gt; }
+            }
+            __syncthreads();
+            prefix = sh.tau - kmin;                // tau = kmin + prefix, exactly
+            krem -= sh.gt_in_bin;                  // copies of tau still to take
+            break;
+        }
         width = shift < 11 ? shift : 11;
         shift -= width;
     }
@@ -206,11 +244,13 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
         c_gt += whole ? u >= tau : u > tau;
         c_eq += !whole && u == tau;
     }
-    const int eq_before = row_inclusive_scan(c_eq, sh.wave_sums) - c_eq;
-    int take_eq = krem - eq_before;
-    take_eq = take_eq < 0 ? 0 : (take_eq > c_eq ? c_eq : take_eq);
-    const int c_sel = c_gt + take_eq;
-    int pos = row_inclusive_scan(c_sel, sh.wave_sums) - c_sel;
+    // one scan of both counts (each < 2^16): the keys taken before this
+    // thread's chunk are all the larger ones and the first krem copies of tau
+    const int packed = (c_eq << 16) | c_gt;
+    const int before = row_inclusive_scan(packed, sh.wave_sums) - packed;
+    const int gt_before = before & 0xffff;
+    const int eq_before = before >> 16;
+    int pos = gt_before + (eq_before < krem ? eq_before : krem);
     int er = eq_before;
     for (int n = lo; n < hi; ++n) {
         const uint32_t u = keys[n];
