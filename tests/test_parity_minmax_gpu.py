@@ -135,8 +135,10 @@ def test_pool_keys_last_block_after_append(head_dim):
     assert torch.equal(before.view(torch.int16), ck.view(torch.int16))
 
 
-def test_pool_keys_out_of_range_page_is_an_empty_box():
-    wl = wlm.small_workload(batch=1, ctx=(640,), seed=46)
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_pool_keys_out_of_range_page_is_an_empty_box(head_dim):
+    # blocks 3 and 7 sit inside the first 16-block tile, with valid blocks on both sides
+    wl = wlm.small_workload(batch=1, ctx=(640,), head_dim=head_dim, seed=46)
     d = wlm.make_layer(wl)
     bt = d["block_table"].clone()
     bt[0, 3] = -5
@@ -145,6 +147,9 @@ def test_pool_keys_out_of_range_page_is_an_empty_box():
     f = ck_logical(ck).float().cpu()
     for n in (3, 7):
         assert torch.all(f[0, :, n, 0] == float("inf")) and torch.all(f[0, :, n, 1] == -float("inf"))
+    want = orc.pool_keys(d["K"], d["ctx_len"], 16, wl.table_width)
+    keep = [n for n in range(40) if n not in (3, 7)]
+    assert np.array_equal(f.double().numpy()[0, :, keep], want[0, :, keep])
     scores = torch.empty((1, wl.num_kv_heads, wl.table_width), device=DEV)
     ops.score_blocks_minmax(dev(d["q_look"]), ck, dev(d["ctx_len"]), scores)
     got = scores.cpu().numpy()
