@@ -286,20 +286,26 @@ class HostTierLayer:
 class HostTierDecode:
     """Decode steps over several layers with the fetch overlapped across layers.
 
-    Per step and layer, on the caller's stream: attention over the layer's
-    working set (after that layer's previous fetch has landed), scoring with the
-    lookahead query, select + plan.  The fetch of the planned blocks runs on a
-    side stream and overlaps the following layers; the next step's attention of
-    the same layer waits for it (Figure 8 caption: one layer's chain runs from
-    the draft query at step t through top-K prediction, KV selection and KV
-    transfer to that layer's attention at step t + 1; flow step 4: the stages
-    overlap across layers).
+    Per step: the scoring of every layer's lookahead query runs on a scoring
+    stream, layer after layer from the start of the step (it reads only the
+    keys and the query, never the working set).  Per layer, on the caller's
+    stream: attention over the layer's working set (after that layer's
+    previous fetch has landed), then, once that layer's scores are in,
+    select + plan.  The fetch of the planned blocks runs on a side stream and
+    overlaps the following layers; the next step's attention of the same layer
+    waits for it (Figure 8 caption: one layer's chain runs from the draft query
+    at step t through top-K prediction, KV selection and KV transfer to that
+    layer's attention at step t + 1; flow step 4: the stages overlap across
+    layers).  Every stage sees the inputs it sees in the plain order, so the
+    results are identical.
     """
 
     def __init__(self, layers):
         self.layers = list(layers)
         dev = self.layers[0].scores.device
         self.side = torch.cuda.Stream(device=dev)                       # default priority
+        self.scoring = torch.cuda.Stream(device=dev)                    # default priority
+        self.ev_scored = [torch.cuda.Event() for _ in self.layers]
         self.ev_planned = [torch.cuda.Event() for _ in self.layers]
         self.ev_fetched = [torch.cuda.Event() for _ in self.layers]
         self.pending = [False for _ in self.layers]
@@ -319,13 +325,19 @@ class HostTierDecode:
         fetch on the side stream."""
         main = torch.cuda.current_stream()
         outs = []
+        # the queries were written on the caller's stream, and the previous
+        # step's plans (on it too) have read every layer's scores
+        self.scoring.wait_stream(main)
+        for li, L in enumerate(self.layers):
+            L.score(q_looks[li], self.scoring)
+            self.ev_scored[li].record(self.scoring)
         for li, L in enumerate(self.layers):
             if self.pending[li]:
                 main.wait_event(self.ev_fetched[li])
             L.attend(qs[li], main)
             if copy_out:
                 outs.append(L.out.clone())
-            L.score(q_looks[li], main)
+            main.wait_event(self.ev_scored[li])
             L.select_plan(step, stream=main)
             self.ev_planned[li].record(main)
             self.side.wait_event(self.ev_planned[li])
@@ -339,4 +351,5 @@ class HostTierDecode:
         return outs
 
     def drain(self):
+        torch.cuda.current_stream().wait_stream(self.scoring)
         torch.cuda.current_stream().wait_stream(self.side)
