@@ -479,7 +479,9 @@ def bench_drift(args, wl):
         if pages.numel():
             layer.k_pool[pages.to(dev), heads.to(dev)] = d["k_pool"][pages, heads].to(dev)
         look = wlm.draw_lookahead(wl, d["q32"], wl.seed + 20_000 + t).to(torch.bfloat16).to(dev)
-        torch.cuda.synchronize()
+        # no synchronisation here: the key update and the query copy are queued
+        # on the same stream, so the step's kernels queue behind them instead of
+        # the GPU idling while the first launch is submitted inside the region
         a, b = _ev(), _ev()
         a.record()
         layer.step(look, q, t)

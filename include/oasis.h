@@ -198,7 +198,7 @@ int oasis_plan_fetch(const oasis_shape *s, const int32_t *sel, const float *scor
 
 /*
  * oasis_select_topk followed by oasis_plan_fetch on the same row, as one
- * launch when k_blocks <= 512 and table_width <= 4096 (one workgroup per row;
+ * launch when k_blocks <= 512 and table_width <= 8192 (one workgroup per row;
  * the selection never leaves the chip between the two), else as the two calls.
  * Results are identical to the two calls; `sel` receives the selection.
  * Same arguments, requirements and errors as the two calls together.

@@ -115,7 +115,7 @@ constexpr int kMaxRowsQ = 16;     // lookahead rows per KV head in one MFMA tile
 constexpr int kMaxAttnRowsQ = 32; // query rows per KV head in attention (two MFMA tiles)
 constexpr int kMaxKBlocks = 1024; // K limit of select / plan
 constexpr int kRowSelectMaxWidth = 8192;  // widest table the 256-thread select keeps in LDS
-constexpr int kFusedMaxWidth = 4096;      // fused select + plan: table width limit
+constexpr int kFusedMaxWidth = 8192;      // fused select + plan: table width limit (LDS: 61 KiB at K = 512)
 constexpr int kFusedMaxK = 512;           // fused select + plan: K limit
 constexpr int kMaxSelectWidth = 15360;   // keys of a row staged in LDS (60 KiB)
 

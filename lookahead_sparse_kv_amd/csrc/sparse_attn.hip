@@ -238,11 +238,12 @@ __device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int 
 }
 
 // Output element (c, d) of row `row` from the partials of its splits, taken
-// eight splits at a time: the loads of a chunk are unconditional (indices past
-// the last split repeat it, with weight 0), so they are all in flight at once.
-template <int D>
+// kChunk splits at a time: the loads of a chunk are unconditional (indices
+// past the last split repeat it, with weight 0), so they are all in flight at
+// once.  The launcher picks kChunk >= splits where it can (up to 32), so that
+// one round of loads covers the row.
+template <int D, int kChunk>
 __device__ __forceinline__ void merge_one(const AttnArgs &a, int row, int c, int d) {
-    constexpr int kChunk = 8;
     const int b = row / a.hkv;
     const int g = row - b * a.hkv;
     const float NEG_INF = -__builtin_inff();
@@ -419,11 +420,22 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArg
 }
 
 // Merge the splits of one (row, query row) pair: thread d owns head dim d.
-template <int D>
+template <int D, int kChunk>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
     const int pair = blockIdx.x;                 // row * n_rows_q + c
     const int row = pair / a.n_rows_q;
-    merge_one<D>(a, row, pair - row * a.n_rows_q, threadIdx.x);
+    merge_one<D, kChunk>(a, row, pair - row * a.n_rows_q, threadIdx.x);
+}
+
+template <int D>
+void launch_merge(const AttnArgs &a, int rows, hipStream_t stream) {
+    const dim3 grid(rows * a.n_rows_q), block(D);
+    if (a.splits <= 8)
+        hipLaunchKernelGGL((attn_merge_kernel<D, 8>), grid, block, 0, stream, a);
+    else if (a.splits <= 16)
+        hipLaunchKernelGGL((attn_merge_kernel<D, 16>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_merge_kernel<D, 32>), grid, block, 0, stream, a);
 }
 
 hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_t stream) {
@@ -445,11 +457,11 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_
     if (head_dim == 128) {
         if (two) hipLaunchKernelGGL((attn_partial_kernel<128, 2>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_partial_kernel<128, 1>), grid, block, 0, stream, a);
-        hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(rows * a.n_rows_q), dim3(128), 0, stream, a);
+        launch_merge<128>(a, rows, stream);
     } else {
         if (two) hipLaunchKernelGGL((attn_partial_kernel<64, 2>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_partial_kernel<64, 1>), grid, block, 0, stream, a);
-        hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(rows * a.n_rows_q), dim3(64), 0, stream, a);
+        launch_merge<64>(a, rows, stream);
     }
     return hipGetLastError();
 }

@@ -199,8 +199,12 @@ def test_plan_fetch_bit_exact_over_steps(case):
     (2, 4, 2048, 128, 6, "ties"),
     (3, 2, 300, 32, 32, "zeros"),
     (2, 2, 100, 128, 25, "normal"),             # fewer blocks than K
-    (2, 2, 4000, 128, 2, "normal"),             # wider than the one-wave select: two launches
-    (2, 2, 1000, 300, 7, "ties"),               # K above the one-wave limit: two launches
+    (2, 2, 4000, 128, 2, "normal"),
+    (2, 2, 1000, 300, 7, "ties"),
+    (2, 2, 8192, 512, 9, "normal"),             # widest fused table at the largest fused K (61 KiB LDS)
+    (2, 2, 8192, 128, 2, "ties"),               # 131K-context rows, one launch
+    (2, 2, 1000, 600, 7, "ties"),               # K above the fused limit: select, then plan
+    (2, 2, 9000, 128, 3, "normal"),             # wider than the row select: wide select, then plan
     (2, 4, 2048, 128, 6, "outliers"),
     (2, 2, 2048, 128, 2, "equal"),
     (2, 2, 1500, 64, 3, "narrow"),
