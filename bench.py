@@ -611,32 +611,53 @@ def main():
     e_b.record()
     torch.cuda.synchronize()
     ms_per_step_with_events = e_a.elapsed_time(e_b) / args.steps
+    # blocks fetched by the plan of the timed loop's last step (all rows)
+    fetched = int(pipes[(args.warmup + 2 * args.steps - 1) % n_rep].L.fetch_count.sum().item())
     score_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
     mean_ms = {"score": sum(score_ms) / len(score_ms)}
 
     # each stage alone, back to back on one stream, replicas in turn
     # (select/plan and attention are latency-bound and would otherwise share
     # the GPU with scoring)
+    # Every visit of a replica takes the next lookahead draw (as in the timed
+    # loop), so its selection changes from visit to visit and the fetch cap
+    # keeps binding; with one fixed draw per replica the planner would settle
+    # into a working set with nothing left to fetch.
+    draw = lambda i: looks[(i // n_rep + 1) % N_LOOK_DRAWS]
     iso = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    fetched_alone = []
     for i in range(args.steps):
         e = iso[i]
         L = layers[i % n_rep]
         e[0].record()
-        L.score(looks[i % N_LOOK_DRAWS], refresh=append)
+        L.score(draw(i), refresh=append)
         e[1].record()
         L.select_plan(2000 + i)
         e[2].record()
         L.attend(q)
         e[3].record()
+        fetched_alone.append(L.fetch_count.sum())
     torch.cuda.synchronize()
+    fetched_alone = [int(x.item()) for x in fetched_alone]
     alone = {}
     for j, k in enumerate(("score", "select_plan", "attn")):
         alone[k] = sorted(e[j].elapsed_time(e[j + 1]) for e in iso)
     # each stage back to back (events around the whole loop, replicas in
     # turn): the per-call cost without an event and a launch gap per call
+    # Select + plan alternates between two score buffers of different draws
+    # per replica, so that every call has misses to rank and victims to evict.
     b2b = {}
-    stages = [("score", lambda i, L: L.score(looks[i % N_LOOK_DRAWS], refresh=append)),
-              ("select_plan", lambda i, L: L.select_plan(3000 + i)),
+    alt = []
+    for r, L in enumerate(layers):
+        pair = []
+        for j in range(2):
+            buf = torch.empty_like(L.scores)
+            L.score(looks[(r + j) % N_LOOK_DRAWS], scores=buf, refresh=append)
+            pair.append(buf)
+        alt.append(pair)
+    stages = [("score", lambda i, L: L.score(draw(i), refresh=append)),
+              ("select_plan", lambda i, L: L.select_plan(3000 + i,
+                                                         scores=alt[i % n_rep][(i // n_rep) % 2])),
               ("attn", lambda i, L: L.attend(q))]
     for k, fn in stages:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -646,6 +667,8 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         b2b[k] = e0.elapsed_time(e1) / args.steps
+        if k == "select_plan":
+            fetched_b2b = int(sum(L.fetch_count.sum().item() for L in layers[:min(n_rep, args.steps)]))
 
     pool_build = None
     if wl.scorer == "minmax":
@@ -673,14 +696,13 @@ def main():
         e2.record()
         for i in range(args.steps):
             L = layers[i % n_rep]
-            L.score(looks[i % N_LOOK_DRAWS], refresh=append)
+            L.score(draw(i), refresh=append)
             L.select_plan(1000 + i)
             L.attend(q)
         e3.record()
         torch.cuda.synchronize()
         detail["ms_per_step_no_overlap"] = round(e2.elapsed_time(e3) / args.steps, 4)
 
-    fetched = int(layer.fetch_count.sum().item())
     agreement = topk_agreement(layer, looks, q)
 
     sb = score_bytes(wl)
@@ -736,6 +758,9 @@ def main():
                           "algorithmic_bytes": ab},
         "detail": detail or None,
         "fetched_blocks_last_step": fetched,
+        "fetched_blocks_per_call": {"cap_per_row": cap, "rows": wl.batch * wl.num_kv_heads,
+                                    "stages_alone_mean": round(sum(fetched_alone) / len(fetched_alone), 1),
+                                    "select_plan_back_to_back_last_calls": fetched_b2b},
         "topk_agreement": agreement,
         "pool_keys_build": pool_build,
         "wall_ms_timed_region": round(wall_ms, 2),
