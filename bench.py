@@ -83,6 +83,17 @@ def attn_bytes(wl):
     return kv + q + out + lists
 
 
+def attn_kernel_name(wl):
+    """The attention launch shape the library picks for this workload (one query row per head)."""
+    rows = wl.batch * wl.num_kv_heads
+    if rows >= 256:
+        return "attn_row_kernel (one workgroup per row, merged in LDS)"
+    if rows >= 128 and wl.k_blocks >= 32:
+        return ("attn_rowsplit_kernel (two workgroups per row, merged in LDS, then across the "
+                "pair through device-scope stores and a per-row arrival counter)")
+    return "attn_partial + attn_merge (split-K)"
+
+
 def select_bytes(wl):
     return wl.batch * wl.num_kv_heads * (wl.table_width * 4 + wl.k_blocks * 4)
 
@@ -750,9 +761,7 @@ def main():
                                  ms_per_step_of_that_loop=round(ms_per_step_with_events, 4)),
         "stages_alone_us": {k: percentiles_us(v) for k, v in alone.items()},
         "stages_back_to_back_us": {k: round(v * 1e3, 2) for k, v in b2b.items()},
-        "attn_roofline": {"kernels": ("attn_row_kernel (one workgroup per row, merged in LDS)"
-                                      if wl.batch * wl.num_kv_heads >= 128 else
-                                      "attn_partial + attn_merge (split-K)"),
+        "attn_roofline": {"kernels": attn_kernel_name(wl),
                           "timing": "back-to-back mean",
                           "achieved": round(attn_gbs, 1), "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                           "algorithmic_bytes": ab},

@@ -13,6 +13,7 @@
  *   oasis_plan_fetch         resident diff + fetch cap + LRU eviction, which
  *                            updates the per-head working-set table
  *   oasis_sparse_decode_attn sparse paged decode attention over the working set
+ *                            (oasis_sparse_decode_attn_ex: the same with launch hints)
  *
  * and, for the pages' own compressed-key scorer, oasis_pool_keys (min/max
  * pooling of the keys) and oasis_score_blocks_minmax (scores from them).
@@ -210,11 +211,12 @@ int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *
 
 /*
  * Bytes of device workspace oasis_sparse_decode_attn needs for this shape:
- * room for the split-K partial results (per row and split: max, sum and the
- * D-wide output of each query row).  With 128 rows or more and at most 16
- * query rows per KV head (whose eight per-wave partials fit in 64 KiB of LDS)
- * the call runs one workgroup per row and leaves the workspace untouched; the
- * size asked for covers either way.  Returns 0 for an invalid shape.
+ * room for the partial results of a row's shares (per row and share: max,
+ * sum and the D-wide output of each query row), then one 32-bit arrival
+ * counter per row (B * Hkv rows), padded to 16 bytes.  The counters must be
+ * zero before the first call on a workspace (allocate it zero-filled); every
+ * call leaves them zero again.  One workspace serves one call at a time.
+ * Returns 0 for an invalid shape.
  */
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk);
 
@@ -241,7 +243,14 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
  * together).
  * A row with no valid token outputs zeros.  bf16 in and out, fp32 softmax and
  * accumulation.  Requires D in {64, 128}, bs = 16, 1 <= n_q, n_q * G <= 32,
- * n_blk >= 1, scale > 0, and workspace_bytes >= oasis_attn_workspace_bytes().
+ * n_blk >= 1, scale > 0, and workspace_bytes >= oasis_attn_workspace_bytes()
+ * of a workspace whose counters are zero (see there).
+ *
+ * Launch shape (results agree to fp32 rounding whichever is taken): from 256
+ * rows (B * Hkv), one workgroup per row merges its waves in LDS; from 128
+ * rows, two workgroups per row, the last to finish merging both through the
+ * workspace; below that, split-K waves and a second merge launch.  Rows with
+ * more than 16 query rows (n_q * G) take split-K.
  */
 int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_q,
                              const uint16_t *k_pool, const uint16_t *v_pool,
@@ -249,6 +258,21 @@ int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_
                              const int32_t *blk_logical, const int32_t *ctx_len, float scale,
                              uint16_t *out, void *workspace, size_t workspace_bytes,
                              void *stream);
+
+/*
+ * oasis_sparse_decode_attn with launch hints.  flags = 0 is that call.
+ * OASIS_ATTN_SHARE_GPU: another launch (the next step's scoring) runs beside
+ * this one; from 128 rows attention then keeps to one workgroup (one CU) per
+ * row, which leaves CUs to the concurrent launch.  Other bits:
+ * OASIS_ERR_INVALID.
+ */
+#define OASIS_ATTN_SHARE_GPU 1
+int oasis_sparse_decode_attn_ex(const oasis_shape *s, const uint16_t *q, int32_t n_q,
+                                const uint16_t *k_pool, const uint16_t *v_pool,
+                                const int32_t *page_table, const int32_t *blk, int32_t n_blk,
+                                const int32_t *blk_logical, const int32_t *ctx_len, float scale,
+                                uint16_t *out, void *workspace, size_t workspace_bytes,
+                                int32_t flags, void *stream);
 
 /*
  * Pinned host KV pool, the tier the working set is fetched from.  The pages

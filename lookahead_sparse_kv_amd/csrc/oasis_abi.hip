@@ -229,7 +229,9 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
     const int nrq = n_q * (s->num_q_heads / s->num_kv_heads);
     int splits = 1, per = 1;
     oasis::attn_split_plan(rows, n_blk, &splits, &per);
-    return (size_t)rows * splits * nrq * (s->head_dim + 2) * sizeof(float);
+    // partials, then one arrival counter per row (16-byte padded)
+    return (size_t)rows * splits * nrq * (s->head_dim + 2) * sizeof(float) +
+           (((size_t)rows * sizeof(uint32_t) + 15) & ~(size_t)15);
 }
 
 int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_q,
@@ -238,8 +240,20 @@ int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_
                              const int32_t *blk_logical, const int32_t *ctx_len, float scale,
                              uint16_t *out, void *workspace, size_t workspace_bytes,
                              void *stream) {
+    return oasis_sparse_decode_attn_ex(s, q, n_q, k_pool, v_pool, page_table, blk, n_blk,
+                                       blk_logical, ctx_len, scale, out, workspace,
+                                       workspace_bytes, 0, stream);
+}
+
+int oasis_sparse_decode_attn_ex(const oasis_shape *s, const uint16_t *q, int32_t n_q,
+                                const uint16_t *k_pool, const uint16_t *v_pool,
+                                const int32_t *page_table, const int32_t *blk, int32_t n_blk,
+                                const int32_t *blk_logical, const int32_t *ctx_len, float scale,
+                                uint16_t *out, void *workspace, size_t workspace_bytes,
+                                int32_t flags, void *stream) {
     const char *fn = "oasis_sparse_decode_attn";
     if (int e = check_shape(s, fn)) return e;
+    if (flags & ~OASIS_ATTN_SHARE_GPU) return fail(OASIS_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
     if (n_q < 1) return fail(OASIS_ERR_INVALID, "%s: n_q %d < 1", fn, n_q);
     if (n_blk < 1) return fail(OASIS_ERR_INVALID, "%s: n_blk %d < 1", fn, n_blk);
     const int G = s->num_q_heads / s->num_kv_heads;
@@ -264,11 +278,13 @@ int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_
     const int nrq = n_q * G;
     float *part_o = static_cast<float *>(workspace);
     float *part_ml = part_o + (size_t)rows * splits * nrq * s->head_dim;
+    uint32_t *row_count = reinterpret_cast<uint32_t *>(part_ml + (size_t)rows * splits * nrq * 2);
     oasis::AttnArgs a{q, k_pool, v_pool, page_table, blk, blk_logical, ctx_len, out,
-                      part_o, part_ml, scale * 1.4426950408889634f,
+                      part_o, part_ml, row_count, scale * 1.4426950408889634f,
                       s->batch, s->num_q_heads, s->num_kv_heads, G, s->table_width,
                       s->num_pages, n_q, nrq, n_blk, splits, per};
-    return check_hip(oasis::launch_sparse_decode_attn(a, s->head_dim, as_stream(stream)), fn);
+    return check_hip(oasis::launch_sparse_decode_attn(a, s->head_dim, (flags & OASIS_ATTN_SHARE_GPU) != 0,
+                                                      as_stream(stream)), fn);
 }
 
 int oasis_hostpool_create(size_t bytes, void **host_ptr) {

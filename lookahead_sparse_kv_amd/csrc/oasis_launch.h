@@ -61,6 +61,7 @@ struct AttnArgs {
     uint16_t *out;
     float *part_o;    // [rows][splits][n_rows_q][D]
     float *part_ml;   // [rows][splits][n_rows_q][2]
+    uint32_t *row_count;   // [rows] arrivals of a row's workgroups (zero between calls)
     float scale_log2;
     int batch, hq, hkv, group, width, num_pages, n_q, n_rows_q, n_blk, splits, per_split;
 };
@@ -105,7 +106,7 @@ hipError_t launch_select_topk(const SelectArgs &a, hipStream_t stream);
 bool row_select_plan_fits(int width, int k, int mode);
 hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
 hipError_t launch_fetch_blocks(const FetchArgs &a, int head_dim, hipStream_t stream);
-hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_t stream);
+hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share_gpu, hipStream_t stream);
 
 // Split-K plan of the attention kernel: how many splits per row and entries per split.
 void attn_split_plan(int rows, int n_blk, int *splits, int *per_split);

@@ -336,37 +336,54 @@ __global__ __launch_bounds__(kAttnWaves * kWave, NT == 1 && kAttnStages == 2 ? 2
     }
 }
 
-// Rows from which attention runs as one 8-wave workgroup per row, merged in
-// LDS (no second launch); below it, split-K over more waves fills the CUs.
+// From kAttnRowFillRows rows (one per CU) attention runs as one 8-wave
+// workgroup per row, merged in LDS.  From OASIS_ATTN_ROWSPLIT_MIN_ROWS up to
+// that, a row takes several such workgroups (enough to give every CU one) that
+// merge across workgroups through the workspace; below it, split-K over more
+// waves fills the CUs and a second launch merges.
 #ifndef OASIS_ATTN_ROW_MIN_ROWS
-#define OASIS_ATTN_ROW_MIN_ROWS 128
+#define OASIS_ATTN_ROW_MIN_ROWS 256
+#endif
+constexpr int kAttnRowFillRows = OASIS_ATTN_ROW_MIN_ROWS;
+#ifndef OASIS_ATTN_ROWSPLIT_MIN_ROWS
+#define OASIS_ATTN_ROWSPLIT_MIN_ROWS 128
 #endif
 constexpr int kRowAttnWaves = 8;
+
+// Workgroups per row and list entries per workgroup for the row-split
+// kernel; false where it does not apply (too few rows, or fewer than 8
+// entries per workgroup, which would leave waves without a block pair).
+inline bool rowsplit_plan(int rows, int n_blk, int *splits, int *per) {
+    if (rows < OASIS_ATTN_ROWSPLIT_MIN_ROWS || rows >= kAttnRowFillRows || rows < 1) return false;
+    const int s = (kAttnRowFillRows + rows - 1) / rows;
+    const int p = (n_blk + s - 1) / s;
+    if (s < 2 || p < 2 * kRowAttnWaves) return false;
+    *splits = (n_blk + p - 1) / p;
+    *per = p;
+    return *splits >= 2;
+}
 
 __host__ __device__ inline int row_attn_wave_floats(int n_rows_q, int head_dim) {
     return (n_rows_q * (head_dim + 2) + 3) & ~3;
 }
 
-// One workgroup per row: wave w walks a contiguous eighth of the row's list,
-// 64 entries at a time; the waves' (max, sum, O) are merged in LDS.  With
-// 128 rows it runs at the speed of split-K alone, and beside a concurrent
-// scoring launch the step is faster: it occupies one CU per row and needs no
-// merge launch.
-template <int D>
-__global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArgs a) {
+// The 8 waves of a workgroup walk entries [w_begin, w_end) of row `row`,
+// each a contiguous eighth (NE > 0: an eighth of exactly NE entries takes the
+// fully unrolled walk), and leave their (O, max, sum) in the workgroup's LDS.
+template <int D, int NE>
+__device__ __forceinline__ void row_waves_to_lds(const AttnArgs &a, int row, int w_begin, int w_end,
+                                                 float *red) {
     constexpr int MT = D / 16;
-    extern __shared__ float red[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int row = blockIdx.x;
     const int b = row / a.hkv;
     const int g = row - b * a.hkv;
     const int r16 = lane & 15;
     const int j4 = lane >> 4;
     const int nrq = a.n_rows_q;
-    const int per = (a.n_blk + kRowAttnWaves - 1) / kRowAttnWaves;
-    const int e_begin = wave * per;
-    const int e_end = e_begin + per < a.n_blk ? e_begin + per : a.n_blk;
+    const int per = (w_end - w_begin + kRowAttnWaves - 1) / kRowAttnWaves;
+    const int e_begin = w_begin + wave * per < w_end ? w_begin + wave * per : w_end;
+    const int e_end = e_begin + per < w_end ? e_begin + per : w_end;
     bf16x8 qv[1][D / 32];
     load_query<D, 1>(a, b, g, qv);
     WaveAcc<D, 1> acc;
@@ -374,8 +391,8 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArg
     acc.l_run[0] = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc.o[0][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (e_end - e_begin == 16) {
-        attn_wave_range<D, 1, 16>(a, row, b, g, e_begin, 16, qv, acc);
+    if (NE > 0 && e_end - e_begin == NE) {
+        attn_wave_range<D, 1, NE>(a, row, b, g, e_begin, NE, qv, acc);
     } else {
         for (int e0 = e_begin; e0 < e_end; e0 += kWave) {
             const int ne = e_end - e0 < kWave ? e_end - e0 : kWave;
@@ -394,28 +411,123 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArg
             *reinterpret_cast<f32x4 *>(wo + (size_t)r16 * D + 16 * mt + 4 * j4) = acc.o[0][mt];
         if (j4 == 0) { wm[r16] = acc.m_run[0]; wl[r16] = l_run; }
     }
-    __syncthreads();
+}
+
+// (max, sum, O) of query row c, dim d, over the 8 waves' LDS partials.
+template <int D>
+__device__ __forceinline__ void lds_merge_waves(const float *red, int nrq, int c, int d, float &M,
+                                                float &L, float &O) {
     const float NEG_INF = -__builtin_inff();
+    const int wstride = row_attn_wave_floats(nrq, D);
+    M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < kRowAttnWaves; ++w) M = fmaxf(M, red[(size_t)w * wstride + (size_t)nrq * D + c]);
+    L = 0.f;
+    O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRowAttnWaves; ++w) {
+        const float *base = red + (size_t)w * wstride;
+        const float m = base[(size_t)nrq * D + c];
+        const float wgt = (m == NEG_INF) ? 0.f : exp2f(m - M);
+        L += wgt * base[(size_t)nrq * D + nrq + c];
+        O += wgt * base[(size_t)c * D + d];
+    }
+}
+
+__device__ __forceinline__ void store_out(const AttnArgs &a, int row, int c, int d, int D, float res) {
+    const int b = row / a.hkv;
+    const int g = row - b * a.hkv;
+    const int iq = c / a.group;
+    const int hr = c - iq * a.group;
+    a.out[(((size_t)b * a.n_q + iq) * a.hq + (size_t)g * a.group + hr) * D + d] =
+        (uint16_t)float_to_bf16_bits(res);
+}
+
+// One workgroup per row: wave w walks a contiguous eighth of the row's list,
+// 64 entries at a time; the waves' (max, sum, O) are merged in LDS.  With
+// 128 rows it runs at the speed of split-K alone, and beside a concurrent
+// scoring launch the step is faster: it occupies one CU per row and needs no
+// merge launch.
+template <int D>
+__global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArgs a) {
+    extern __shared__ float red[];
+    const int row = blockIdx.x;
+    const int nrq = a.n_rows_q;
+    row_waves_to_lds<D, 16>(a, row, 0, a.n_blk, red);
+    __syncthreads();
     for (int idx = threadIdx.x; idx < nrq * D; idx += kRowAttnWaves * kWave) {
         const int c = idx / D;
         const int d = idx - c * D;
-        float M = NEG_INF;
-#pragma unroll
-        for (int w = 0; w < kRowAttnWaves; ++w) M = fmaxf(M, red[(size_t)w * wstride + (size_t)nrq * D + c]);
-        float L = 0.f, O = 0.f;
-#pragma unroll
-        for (int w = 0; w < kRowAttnWaves; ++w) {
-            const float *base = red + (size_t)w * wstride;
-            const float m = base[(size_t)nrq * D + c];
-            const float wgt = (m == NEG_INF) ? 0.f : exp2f(m - M);
-            L += wgt * base[(size_t)nrq * D + nrq + c];
-            O += wgt * base[(size_t)c * D + d];
+        float M, L, O;
+        lds_merge_waves<D>(red, nrq, c, d, M, L, O);
+        store_out(a, row, c, d, D, L > 0.f ? O / L : 0.f);
+    }
+}
+
+// a.splits workgroups per row (rows too few to fill the CUs one per row):
+// workgroup s walks entries [s * per_split, (s + 1) * per_split) with 8 waves
+// merged in LDS, and publishes its (max, sum, O) partial with device-scope
+// stores, which write through to the point where every XCD's L2 sees them.
+// The per-row counter then takes one device-scope increment per workgroup;
+// the last to arrive reads every partial of the row with device-scope loads,
+// merges them and writes the output, and puts the counter back to zero for
+// the next call.  No L2-wide write-back or invalidate is needed: the only
+// data that crosses workgroups is written and read at device scope, and each
+// workgroup's stores have completed before its increment is issued.
+template <int D, int NE>
+__global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_rowsplit_kernel(AttnArgs a) {
+    extern __shared__ float red[];
+    __shared__ int is_last;
+    const int S = a.splits;
+    const int row = blockIdx.x / S;
+    const int part = blockIdx.x - row * S;
+    const int nrq = a.n_rows_q;
+    const float NEG_INF = -__builtin_inff();
+    const int w_begin = part * a.per_split < a.n_blk ? part * a.per_split : a.n_blk;
+    const int w_end = w_begin + a.per_split < a.n_blk ? w_begin + a.per_split : a.n_blk;
+    row_waves_to_lds<D, NE>(a, row, w_begin, w_end, red);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nrq * D; idx += kRowAttnWaves * kWave) {
+        const int c = idx / D;
+        const int d = idx - c * D;
+        float M, L, O;
+        lds_merge_waves<D>(red, nrq, c, d, M, L, O);
+        const size_t slot = ((size_t)row * S + part) * nrq + c;
+        __hip_atomic_store(a.part_o + slot * D + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+            __hip_atomic_store(a.part_ml + 2 * slot, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.part_ml + 2 * slot + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        const float res = L > 0.f ? O / L : 0.f;
-        const int iq = c / a.group;
-        const int hr = c - iq * a.group;
-        a.out[(((size_t)b * a.n_q + iq) * a.hq + (size_t)g * a.group + hr) * D + d] =
-            (uint16_t)float_to_bf16_bits(res);
+    }
+    __builtin_amdgcn_s_waitcnt(0);          // this thread's partial stores have completed
+    __syncthreads();                        // ... and every thread's
+    if (threadIdx.x == 0) {
+        const uint32_t arrived = __hip_atomic_fetch_add(a.row_count + row, 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+        const int last = arrived == (uint32_t)(S - 1);
+        if (last) __hip_atomic_store(a.row_count + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = last;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    for (int idx = threadIdx.x; idx < nrq * D; idx += kRowAttnWaves * kWave) {
+        const int c = idx / D;
+        const int d = idx - c * D;
+        float M = NEG_INF, L = 0.f, O = 0.f;
+        for (int s = 0; s < S; ++s) {
+            const size_t slot = ((size_t)row * S + s) * nrq + c;
+            const float m = __hip_atomic_load(a.part_ml + 2 * slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float l = __hip_atomic_load(a.part_ml + 2 * slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float o = __hip_atomic_load(a.part_o + slot * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (m == NEG_INF) continue;             // no valid token in that share
+            const float Mn = fmaxf(M, m);
+            const float r_old = M == NEG_INF ? 0.f : exp2f(M - Mn);
+            const float r_new = exp2f(m - Mn);
+            L = L * r_old + l * r_new;
+            O = O * r_old + o * r_new;
+            M = Mn;
+        }
+        store_out(a, row, c, d, D, L > 0.f ? O / L : 0.f);
     }
 }
 
@@ -438,19 +550,40 @@ void launch_merge(const AttnArgs &a, int rows, hipStream_t stream) {
         hipLaunchKernelGGL((attn_merge_kernel<D, 32>), grid, block, 0, stream, a);
 }
 
-hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, hipStream_t stream) {
+hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share_gpu, hipStream_t stream) {
     const int rows = a.batch * a.hkv;
     if (rows == 0) return hipSuccess;
     const long long waves = (long long)rows * a.splits;
     dim3 grid((unsigned)((waves + kAttnWaves - 1) / kAttnWaves));
     dim3 block(kAttnWaves * kWave);
     const size_t row_lds = (size_t)kRowAttnWaves * row_attn_wave_floats(a.n_rows_q, head_dim) * 4;
-    if (rows >= OASIS_ATTN_ROW_MIN_ROWS && a.n_rows_q <= 16 && row_lds <= 65536) {
+    const bool row_fits = a.n_rows_q <= 16 && row_lds <= 65536;
+    // sharing the GPU with a concurrent launch: one CU per row from the
+    // row-split range up, which leaves the other CUs to that launch
+    const int row_min = share_gpu ? OASIS_ATTN_ROWSPLIT_MIN_ROWS : kAttnRowFillRows;
+    if (rows >= row_min && row_fits) {
         const size_t lds = row_lds;
         if (head_dim == 128)
             hipLaunchKernelGGL(attn_row_kernel<128>, dim3(rows), dim3(kRowAttnWaves * kWave), lds, stream, a);
         else
             hipLaunchKernelGGL(attn_row_kernel<64>, dim3(rows), dim3(kRowAttnWaves * kWave), lds, stream, a);
+        return hipGetLastError();
+    }
+    int wg_splits = 0, wg_per = 0;
+    if (row_fits && rowsplit_plan(rows, a.n_blk, &wg_splits, &wg_per) && wg_splits <= a.splits) {
+        // the workspace holds room for a.splits >= wg_splits partials per row
+        AttnArgs r = a;
+        r.splits = wg_splits;
+        r.per_split = wg_per;
+        const dim3 grid2((unsigned)(rows * wg_splits)), block2(kRowAttnWaves * kWave);
+        const bool eighth8 = wg_per == 8 * kRowAttnWaves;
+        if (head_dim == 128) {
+            if (eighth8) hipLaunchKernelGGL((attn_rowsplit_kernel<128, 8>), grid2, block2, row_lds, stream, r);
+            else hipLaunchKernelGGL((attn_rowsplit_kernel<128, 0>), grid2, block2, row_lds, stream, r);
+        } else {
+            if (eighth8) hipLaunchKernelGGL((attn_rowsplit_kernel<64, 8>), grid2, block2, row_lds, stream, r);
+            else hipLaunchKernelGGL((attn_rowsplit_kernel<64, 0>), grid2, block2, row_lds, stream, r);
+        }
         return hipGetLastError();
     }
     const bool two = a.n_rows_q > 16;

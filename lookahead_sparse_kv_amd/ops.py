@@ -22,7 +22,8 @@ OASIS_OK, OASIS_ERR_INVALID, OASIS_ERR_UNSUPPORTED, OASIS_ERR_NOMEM, OASIS_ERR_H
 
 # Every symbol include/oasis.h declares.
 EXPORTS = ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax", "oasis_select_topk", "oasis_plan_fetch", "oasis_select_plan",
-           "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_hostpool_create",
+           "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_sparse_decode_attn_ex",
+           "oasis_hostpool_create",
            "oasis_hostpool_device_pointer", "oasis_hostpool_destroy", "oasis_fetch_blocks",
            "oasis_status_string", "oasis_last_error", "oasis_version")
 
@@ -62,13 +63,16 @@ def lib() -> ctypes.CDLL:
         L.oasis_attn_workspace_bytes.argtypes = [S, i32, i32]
         L.oasis_attn_workspace_bytes.restype = sz
         L.oasis_sparse_decode_attn.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz, p]
+        L.oasis_sparse_decode_attn_ex.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz,
+                                                  i32, p]
         L.oasis_hostpool_create.argtypes = [sz, ctypes.POINTER(ctypes.c_void_p)]
         L.oasis_hostpool_device_pointer.argtypes = [p, ctypes.POINTER(ctypes.c_void_p)]
         L.oasis_hostpool_destroy.argtypes = [p]
         L.oasis_fetch_blocks.argtypes = [S, p, p, i32, p, p, p, i32, p, p, p, p]
         for fn in ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax",
                    "oasis_select_topk", "oasis_plan_fetch",
-                   "oasis_select_plan", "oasis_sparse_decode_attn", "oasis_hostpool_create",
+                   "oasis_select_plan", "oasis_sparse_decode_attn", "oasis_sparse_decode_attn_ex",
+                   "oasis_hostpool_create",
                    "oasis_hostpool_device_pointer", "oasis_hostpool_destroy",
                    "oasis_fetch_blocks"):
             getattr(L, fn).restype = ctypes.c_int
@@ -191,16 +195,25 @@ def attn_workspace_bytes(shape: OasisShape, n_q: int, n_blk: int) -> int:
     return int(lib().oasis_attn_workspace_bytes(ctypes.byref(shape), n_q, n_blk))
 
 
+OASIS_ATTN_SHARE_GPU = 1
+
+
 def sparse_decode_attn(shape: OasisShape, q, k_pool, v_pool, page_table, blk, blk_logical,
-                       ctx_len, out, workspace, scale=None, stream=None):
+                       ctx_len, out, workspace, scale=None, stream=None, flags=0):
     """q [B][n_q][Hq][D] bf16 -> out [B][n_q][Hq][D] bf16 over the listed blocks.
-    blk / blk_logical [B][Hkv][n_blk] i32 (blk may be None: entry e is index e)."""
+    blk / blk_logical [B][Hkv][n_blk] i32 (blk may be None: entry e is index e).
+    workspace: zero-filled when allocated (its row counters return to zero
+    after every call).  flags: OASIS_ATTN_SHARE_GPU when another launch runs
+    beside this one (oasis_sparse_decode_attn_ex); 0 calls oasis_sparse_decode_attn."""
     n_blk = (blk if blk is not None else blk_logical).shape[-1]
     scale = float(shape.head_dim) ** -0.5 if scale is None else scale
-    _check(lib().oasis_sparse_decode_attn(
-        ctypes.byref(shape), _ptr(q), q.shape[1], _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
-        _ptr(blk), n_blk, _ptr(blk_logical), _ptr(ctx_len), scale, _ptr(out), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (ctypes.byref(shape), _ptr(q), q.shape[1], _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+            _ptr(blk), n_blk, _ptr(blk_logical), _ptr(ctx_len), scale, _ptr(out), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    if flags:
+        _check(lib().oasis_sparse_decode_attn_ex(*args, flags, _stream(stream)))
+    else:
+        _check(lib().oasis_sparse_decode_attn(*args, _stream(stream)))
     return out
 
 

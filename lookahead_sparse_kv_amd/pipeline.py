@@ -91,10 +91,12 @@ class DecodeLayer:
                         self.k_blocks, self.cap, step, self.sel, self.slot_block, self.last_use,
                         self.fetch_block, self.fetch_slot, self.fetch_count, stream)
 
-    def attend(self, q, blocks=None, stream=None):
+    def attend(self, q, blocks=None, stream=None, share_gpu=False):
+        """share_gpu: another launch (the next step's scoring) runs beside this one."""
         blocks = self.slot_block if blocks is None else blocks
         ops.sparse_decode_attn(self.shape, q, self.k_pool, self.v_pool, self.block_table, blocks,
-                               blocks, self.ctx_len, self.out, self.workspace, stream=stream)
+                               blocks, self.ctx_len, self.out, self.workspace, stream=stream,
+                               flags=ops.OASIS_ATTN_SHARE_GPU if share_gpu else 0)
 
     def step(self, q_look, q, step, stream=None):
         self.score(q_look, stream)
@@ -195,7 +197,7 @@ class PipelinedDecode:
         if self.plan_stream is not None and self.last_plan is not None:
             main.wait_event(self.last_plan)             # the working set of `step`
         b = self._score_next(q_look_next, main, score_events, append)
-        self.L.attend(q, stream=main)
+        self.L.attend(q, stream=main, share_gpu=True)
         out = self.L.out.clone() if copy_out else None
         self._plan(b, step + 1, main, after_attention=True)
         return out

@@ -110,8 +110,8 @@ def test_attn_workspace_and_argument_checks():
     L = ops.lib()
     s = _shape(batch=16, num_q_heads=32, num_kv_heads=8, table_width=2048, num_pages=32768)
     ws = ops.attn_workspace_bytes(s, 1, 128)
-    # 128 rows x 8 splits x 4 query rows x (128 + 2) floats
-    assert ws == 128 * 8 * 4 * 130 * 4
+    # 128 rows x 8 splits x 4 query rows x (128 + 2) floats, then 128 row counters
+    assert ws == 128 * 8 * 4 * 130 * 4 + 128 * 4
     assert ops.attn_workspace_bytes(s, 0, 128) == 0
     assert ops.attn_workspace_bytes(s, 1, 0) == 0
     att = lambda n_q=1, n_blk=128, wsb=ws, wsp=P, blk=P: L.oasis_sparse_decode_attn(
@@ -122,6 +122,10 @@ def test_attn_workspace_and_argument_checks():
     assert att(n_blk=0) == ops.OASIS_ERR_INVALID
     assert att(blk=None) == ops.OASIS_ERR_INVALID       # blk and blk_logical both NULL
     assert att(wsp=ctypes.c_void_p(24)) == ops.OASIS_ERR_INVALID  # misaligned workspace
+    att_ex = lambda flags: L.oasis_sparse_decode_attn_ex(
+        ctypes.byref(s), P, 1, P, P, P, P, 128, P, P, 0.088, P, P, ws, flags, None)
+    assert att_ex(2) == ops.OASIS_ERR_INVALID            # unknown launch hint
+    assert att_ex(-1) == ops.OASIS_ERR_INVALID
 
 
 def test_library_is_required():

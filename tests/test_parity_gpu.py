@@ -257,11 +257,18 @@ ATTN_CASES = {
                             3, 40, 0.0),
     "d128_g4_nq8_32_rows_short": (dict(batch=3, q_heads=8, kv_heads=2, head_dim=128,
                                        ctx=(16, 5, 700)), 8, 3, 0.0),
-    # 128 rows or more: one workgroup per row, merged in LDS
+    # 128 to 255 rows: two 8-wave workgroups per row, merged through the workspace
     "d128_g4_128_rows_ragged": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128,
                                      ctx=(700, 1601, 16, 5, 999, 1200, 33, 640)), 1, 40, 0.2),
     "d64_g8_nq2_128_rows": (dict(batch=32, q_heads=32, kv_heads=4, head_dim=64,
                                  ctx=(500, 777, 64, 1000)), 2, 70, 0.1),
+    "d128_g4_128_rows_k128": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128,
+                                   ctx=(4096, 2100, 3000, 2048)), 1, 128, 0.1),
+    "d64_g4_192_rows_k128": (dict(batch=48, q_heads=16, kv_heads=4, head_dim=64,
+                                  ctx=(2048, 3001)), 1, 128, 0.0),
+    "d128_g4_128_rows_all_empty": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128,
+                                        ctx=(600, 2048)), 1, 128, 1.0),
+    # 256 rows or more: one workgroup per row, merged in LDS
     "d128_g4_nq4_256_rows_long_lists": (dict(batch=32, q_heads=64, kv_heads=8, head_dim=128,
                                              ctx=(4096, 3000)), 4, 200, 0.05),
 }
@@ -303,13 +310,15 @@ def test_sparse_attention_matches_oracle(name):
     assert np.all(np.isfinite(got))
 
 
-@pytest.mark.parametrize("batch,kv_heads", [(2, 2), (32, 4)])     # split-K; one workgroup per row
-def test_sparse_attention_working_set_mode(batch, kv_heads):
+# split-K (2 and 128 rows, short lists); two workgroups per row (128 rows);
+# one workgroup per row (256 rows)
+@pytest.mark.parametrize("batch,kv_heads,K", [(2, 2, 24), (32, 4, 24), (32, 4, 128), (64, 4, 24)])
+def test_sparse_attention_working_set_mode(batch, kv_heads, K):
     # slots -> pages of a separate working-set pool; blk = NULL, blk_logical = slot table
     wl = wlm.small_workload(batch=batch, q_heads=4 * kv_heads, kv_heads=kv_heads, head_dim=128,
                             ctx=(3000, 2000), n_hot=0, seed=23)
     d = wlm.make_layer(wl)
-    K, Hkv, Hq = 24, kv_heads, 4 * kv_heads
+    Hkv, Hq = kv_heads, 4 * kv_heads
     rng = np.random.default_rng(24)
     slot_block = _random_lists(rng, wl, K, 0.25)
     # working-set pool: page = b * K + slot, holding (for every head) that head's slot block
@@ -332,6 +341,68 @@ def test_sparse_attention_working_set_mode(batch, kv_heads):
                            dev(torch.from_numpy(slot_block)), dev(d["ctx_len"]), out, ws)
     want = orc.attn(q[:, 0], d["K"], d["V"], d["ctx_len"], 16, slot_block)
     assert np.abs(out[:, 0].float().cpu().numpy() - want).max() <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("name", ["d128_g4_128_rows_k128", "d64_g4_192_rows_k128",
+                                  "d128_g4_128_rows_ragged"])
+def test_sparse_attention_share_gpu_hint(name):
+    """With OASIS_ATTN_SHARE_GPU, 128..255 rows run one workgroup per row: the
+    same attention, within fp32 rounding of the default launch."""
+    kw, n_q, n_blk, frac = ATTN_CASES[name]
+    wl = wlm.small_workload(n_hot=0, seed=21, **kw)
+    d = wlm.make_layer(wl)
+    rng = np.random.default_rng(22)
+    q = torch.randn((wl.batch, n_q, wl.num_q_heads, wl.head_dim), generator=torch.Generator().manual_seed(5))
+    q = (q * 2.0).to(torch.bfloat16)
+    lists = _random_lists(rng, wl, n_blk, frac)
+    shape = ops.make_shape(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.table_width,
+                           wl.num_pages)
+    g_lists = dev(torch.from_numpy(lists))
+    outs = []
+    for flags in (ops.OASIS_ATTN_SHARE_GPU, 0):
+        ws = torch.zeros(ops.attn_workspace_bytes(shape, n_q, n_blk) // 4 + 4, device=DEV)
+        out = torch.empty((wl.batch, n_q, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device=DEV)
+        ops.sparse_decode_attn(shape, dev(q), dev(d["k_pool"]), dev(d["v_pool"]), dev(d["block_table"]),
+                               g_lists, g_lists, dev(d["ctx_len"]), out, ws, flags=flags)
+        outs.append(out.float().cpu().numpy())
+    want = orc.attn(q[:, 0], d["K"], d["V"], d["ctx_len"], 16, lists)
+    assert np.abs(outs[0][:, 0] - want).max() <= ATTN_ATOL
+    # the two launch shapes differ only in the fp32 merge order before bf16 rounding
+    assert np.abs(outs[0] - outs[1]).max() <= 2 ** -7 * max(1.0, np.abs(outs[1]).max())
+
+
+def test_two_workgroups_per_row_halves_empty_and_repeated_calls():
+    """128 rows, 128 entries: each row is split between two workgroups.  Even
+    rows list nothing in the first half, odd rows nothing in the second, one
+    row lists nothing at all.  A second call on the same workspace gives the
+    same bits (the arrival counters are back at zero after each call)."""
+    wl = wlm.small_workload(batch=16, q_heads=32, kv_heads=8, head_dim=128, ctx=(4096, 2500),
+                            n_hot=0, seed=26)
+    d = wlm.make_layer(wl)
+    rng = np.random.default_rng(27)
+    lists = _random_lists(rng, wl, 128, 0.0)
+    lists[0::2, :, :64] = -1
+    lists[1::2, :, 64:] = -1
+    lists[5, 3, :] = -1
+    q = torch.randn((16, 1, 32, 128), generator=torch.Generator().manual_seed(8)).to(torch.bfloat16)
+    shape = ops.make_shape(16, 32, 8, 128, wl.table_width, wl.num_pages)
+    nbytes = ops.attn_workspace_bytes(shape, 1, 128)
+    ws = torch.zeros(nbytes // 4, device=DEV)
+    g_lists = dev(torch.from_numpy(lists))
+    outs = []
+    for _ in range(2):
+        out = torch.empty((16, 1, 32, 128), dtype=torch.bfloat16, device=DEV)
+        ops.sparse_decode_attn(shape, dev(q), dev(d["k_pool"]), dev(d["v_pool"]), dev(d["block_table"]),
+                               g_lists, g_lists, dev(d["ctx_len"]), out, ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+        # the last 128 words are the row counters
+        assert int(ws[-128:].view(torch.int32).abs().sum().item()) == 0
+    assert torch.equal(outs[0], outs[1])
+    want = orc.attn(q[:, 0], d["K"], d["V"], d["ctx_len"], 16, lists)
+    got = outs[0][:, 0].float().cpu().numpy()
+    assert np.abs(got - want).max() <= ATTN_ATOL
+    assert np.all(got[5, 12:16] == 0.0)          # row (5, 3): query heads 12..15, nothing listed
 
 
 def test_sparse_attention_large_logits_stay_finite():
