@@ -672,6 +672,9 @@ def main():
               ("attn", lambda i, L: L.attend(q))]
     for k, fn in stages:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # one untimed call first: the GPU is then busy when e0 is recorded, so
+        # the loop's time does not include the host's latency to its first launch
+        fn(args.steps, layers[args.steps % n_rep])
         e0.record()
         for i in range(args.steps):
             fn(i, layers[i % n_rep])

@@ -586,6 +586,14 @@ def test_full_size_sampled_rows(name):
     layer.step(dev(d["q_look"]), dev(q), 0)
     torch.cuda.synchronize()
     _check_step_rows(wl, d, layer, d["q_look"], q, sb, lu, cap, 0, rows, name)
+    # the launch shape the overlapped step uses (one workgroup per row beside
+    # the concurrent scoring) gives the same attention on every row, up to the
+    # fp32 merge order before bf16 rounding
+    out_default = layer.out.float().cpu().numpy()
+    layer.attend(dev(q), share_gpu=True)
+    torch.cuda.synchronize()
+    out_share = layer.out.float().cpu().numpy()
+    assert np.abs(out_share - out_default).max() <= 2 ** -7 * max(1.0, np.abs(out_default).max())
     # properties that hold at any size, on every row
     fc = layer.fetch_count.cpu().numpy()
     assert np.all(fc <= cap)
