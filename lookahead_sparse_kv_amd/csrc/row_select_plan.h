@@ -264,8 +264,7 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
 __device__ __forceinline__ int4 ld_i4(const int *p) { return *reinterpret_cast<const int4 *>(p); }
 __device__ __forceinline__ float4 ld_f4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
-// LDS of the plan: 8 arrays of Kp = roundup(K, 16) ints after `sel` (Kp ints);
-// 9 are reserved.
+// LDS of the plan: 9 arrays of Kp = roundup(K, 16) ints after `sel` (Kp ints).
 __host__ __device__ __forceinline__ int plan_pad(int K) {
     return (K + kPlanPadding - 1) / kPlanPadding * kPlanPadding;
 }
@@ -320,11 +319,14 @@ __device__ __forceinline__ void plan_prefetch(const int32_t *slot_block, const i
 // part of the global arrays.  `pl` is 9 * Kp ints of LDS.
 //
 // Each thread owns a contiguous chunk of selection entries and of slots, so
-// every position (the p-th fetched block in ascending order, the p-th free
-// slot) is an exclusive scan.  Hits are found by binary search in the
-// ascending selection (a selection that is not ascending is sorted first);
-// only the misses are ranked against each other by (score desc, block asc),
-// and only the eviction candidates by (last use asc, block asc).
+// every position (the p-th miss or fetched block in ascending order, the p-th
+// free slot or eviction candidate) comes from an exclusive scan; counts that
+// do not depend on each other share one scan, packed as two 16-bit fields.
+// Hits are found by binary search in the ascending selection (a selection
+// that is not ascending is sorted first); only the misses are ranked against
+// each other by (score desc, block asc), and only the eviction candidates by
+// (last use asc, block asc).  min(misses, cap) misses are fetched, so the
+// number of victims is known as soon as the misses are counted.
 template <class ScoreOf>
 __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, int cap, int step,
                                          const PlanPrefetch &pf,
@@ -341,8 +343,11 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
     int *hit_sel = pl + 3 * Kp;    // per selection entry: resident
     int *fill = pl + 4 * Kp;       // per slot: block fetched into it, -1
     int *dest = pl + 5 * Kp;       // destination slot of the p-th fetched block
-    float *m_score = reinterpret_cast<float *>(pl + 6 * Kp);   // misses; later candidates' last use
-    int *m_block = pl + 7 * Kp;                                 // misses; later candidates' block
+    float *m_score = reinterpret_cast<float *>(pl + 6 * Kp);   // misses, compacted
+    int *m_block = pl + 7 * Kp;
+    int *c_lu = pl + 8 * Kp;       // eviction candidates, compacted: last use
+    int *c_block = hit_sel;        //   ... and block (hit_sel is dead by then)
+    int *m_rank = reinterpret_cast<int *>(sel_score);   // per miss: rank (sel_score dead by then)
 
     for (int i = tid; i < Kp; i += kRowThreads) {
         if (i >= K) sel[i] = -1;
@@ -396,20 +401,28 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
         const int x = sel[i];
         sel_score[i] = (i < K && x >= 0) ? sel_score_of(x) : 0.f;
     }
-    // valid selection entries: an ascending prefix
-    int my_valid = 0;
-#pragma unroll
-    for (int u = 0; u < kPlanMaxPer; ++u)
-        my_valid += (u < E && lo + u < K && sel[lo + u] >= 0) ? 1 : 0;
-    int m_valid;
-    row_exclusive_scan(my_valid, sh.wave_sums, m_valid);   // ends with a barrier: sb, lu visible
-
-    // hits: every resident block is looked up in the selection
-    bool hit[kPlanMaxPer], empty[kPlanMaxPer], cand[kPlanMaxPer];
+    // one scan: valid selection entries (an ascending prefix) | empty slots
+    bool empty[kPlanMaxPer];
+    int my_valid = 0, my_empty = 0;
 #pragma unroll
     for (int u = 0; u < kPlanMaxPer; ++u) {
         const int j = lo + u;
-        hit[u] = empty[u] = cand[u] = false;
+        my_valid += (u < E && j < K && sel[j] >= 0) ? 1 : 0;
+        empty[u] = u < E && j < K && pf.sb[u] < 0;
+        my_empty += empty[u];
+    }
+    int tot_a;
+    const int pos_a = row_exclusive_scan(my_valid | (my_empty << 16), sh.wave_sums, tot_a);
+    const int m_valid = tot_a & 0xffff;                    // (ends with a barrier: sb, lu visible)
+    const int nfree = tot_a >> 16;
+    int epos = pos_a >> 16;
+
+    // hits: every resident block is looked up in the selection
+    bool hit[kPlanMaxPer], cand[kPlanMaxPer];
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        const int j = lo + u;
+        hit[u] = cand[u] = false;
         if (u < E && j < K) {
             const int blk = sb[j];
             if (blk >= 0) {
@@ -420,23 +433,27 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
                 }
                 if (l < m_valid && sel[l] == blk) { hit[u] = true; hit_sel[l] = 1; }
                 cand[u] = !hit[u];
-            } else {
-                empty[u] = true;
             }
         }
     }
     __syncthreads();
-    // misses, compacted in ascending block order
+    // one scan: misses (in ascending block order) | eviction candidates
     bool miss[kPlanMaxPer];
-    int my_miss = 0;
+    int my_miss = 0, my_cand = 0;
 #pragma unroll
     for (int u = 0; u < kPlanMaxPer; ++u) {
         const int i = lo + u;
         miss[u] = u < E && i < K && sel[i] >= 0 && !hit_sel[i];
         my_miss += miss[u];
+        my_cand += cand[u];
     }
-    int M;
-    int mpos = row_exclusive_scan(my_miss, sh.wave_sums, M);
+    int tot_b;
+    const int pos_b = row_exclusive_scan(my_miss | (my_cand << 16), sh.wave_sums, tot_b);
+    const int M = tot_b & 0xffff;
+    const int C = tot_b >> 16;
+    const int nF = M < cap ? M : cap;                      // the first min(M, cap) misses are fetched
+    const int n_victims = nF > nfree ? nF - nfree : 0;     // (C >= n_victims always)
+    int mpos = pos_b & 0xffff, cpos = pos_b >> 16;
     int mp[kPlanMaxPer];
 #pragma unroll
     for (int u = 0; u < kPlanMaxPer; ++u) {
@@ -447,11 +464,17 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
             m_block[mpos] = sel[lo + u];
             ++mpos;
         }
+        if (cand[u] && n_victims > 0) {
+            c_lu[cpos] = lu[lo + u];
+            c_block[cpos] = sb[lo + u];
+            ++cpos;
+        }
     }
     __syncthreads();
-    // the first min(M, cap) misses by (score desc, block asc) are fetched
+    // ranks: misses by (score desc, block asc); candidates by (last use asc,
+    // block asc), the first n_victims of them evicted in that order, after the
+    // free slots (ascending)
     bool fetched[kPlanMaxPer];
-    int my_f = 0;
 #pragma unroll
     for (int u = 0; u < kPlanMaxPer; ++u) {
         fetched[u] = false;
@@ -467,60 +490,40 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
                     rank += (s2 > sc) | ((s2 == sc) & (m_block[q] < blk));
                 }
                 fetched[u] = rank < cap;
+                m_rank[mp[u]] = rank;
             }
         }
-        my_f += fetched[u];
-    }
-    int nF;
-    int fpos = row_exclusive_scan(my_f, sh.wave_sums, nF);
-    // destinations: the empty slots in ascending order, then LRU victims
-    int my_empty = 0, my_cand = 0;
-#pragma unroll
-    for (int u = 0; u < kPlanMaxPer; ++u) { my_empty += empty[u]; my_cand += cand[u]; }
-    int nfree;
-    int epos = row_exclusive_scan(my_empty, sh.wave_sums, nfree);
-#pragma unroll
-    for (int u = 0; u < kPlanMaxPer; ++u)
         if (empty[u]) {
             if (epos < nF) dest[epos] = lo + u;
             ++epos;
         }
-    if (nF > nfree) {                                   // uniform across the workgroup
-        int C;
-        int cpos = row_exclusive_scan(my_cand, sh.wave_sums, C);
-#pragma unroll
-        for (int u = 0; u < kPlanMaxPer; ++u) {
-            if (cand[u]) {
-                m_score[cpos] = __int_as_float(lu[lo + u]);
-                m_block[cpos] = sb[lo + u];
-                ++cpos;
+        if (cand[u] && n_victims > 0) {
+            const int l0 = lu[lo + u], b0 = sb[lo + u];
+            int rank = 0;
+            for (int q = 0; q < C; ++q) {
+                const int l2 = c_lu[q];
+                rank += (l2 < l0) | ((l2 == l0) & (c_block[q] < b0));
             }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < kPlanMaxPer; ++u) {
-            if (cand[u]) {
-                const int l0 = lu[lo + u], b0 = sb[lo + u];
-                int rank = 0;
-                for (int q = 0; q < C; ++q) {
-                    const int l2 = __float_as_int(m_score[q]);
-                    rank += (l2 < l0) | ((l2 == l0) & (m_block[q] < b0));
-                }
-                if (rank < nF - nfree) dest[nfree + rank] = lo + u;
-            }
+            if (rank < n_victims) dest[nfree + rank] = lo + u;
         }
     }
     __syncthreads();
-    // the p-th fetched block (ascending) goes to dest[p]
+    // the p-th fetched block (ascending) goes to dest[p]; p counts the fetched
+    // misses before this one in block order
 #pragma unroll
     for (int u = 0; u < kPlanMaxPer; ++u) {
         if (fetched[u]) {
+            int fpos = mp[u];
+            if (M > cap) {
+                fpos = 0;
+                for (int q = 0; q < mp[u]; ++q) fpos += m_rank[q] < cap;
+            }
+            if (fpos >= nF) continue;   // only a selection with repeated blocks gets here
             const int blk = sel[lo + u];
             const int d = dest[fpos];
             fetch_block[fpos] = blk;
             fetch_slot[fpos] = d;
             if (d >= 0) fill[d] = blk;
-            ++fpos;
         }
     }
     for (int p = nF + tid; p < cap; p += kRowThreads) {
