@@ -617,6 +617,98 @@ def _host_pool_for(d, wl):
     return pool, pool.device_ptr, pool.device_ptr + 2 * n
 
 
+def test_host_tier_full_size_sampled_rows():
+    """The 32-sequence, 64-query / 8-KV-head, 32K host-pool workload at its full
+    size (4 GiB of pinned host pool per layer, cap 6), two layers launched as the
+    benchmark launches them: every layer's scoring on a scoring stream, the
+    capped fetch on a side stream overlapped with the next layer, one
+    attention workgroup per row (256 rows).  On sampled rows of both layers and
+    two steps the oracle checks the scores, the selection and the plan bit for
+    bit (outside near ties), the attention over the working set the previous
+    step left, and the K and V tiles every resident slot holds."""
+    from lookahead_sparse_kv_amd.pipeline import HostTierDecode, HostTierLayer
+    wl = wlm.WORKLOADS["qwen3_32b_32k_hostpool"]
+    B, Hkv, W, D, K, G = (wl.batch, wl.num_kv_heads, wl.table_width, wl.head_dim, wl.k_blocks,
+                          wl.group)
+    cap = wl.cap()
+    rows = [(0, 0), (11, 3), (31, 7)]
+    n_layers, T = 2, 2
+    layers, pools, keep = [], [], []
+    for l in range(n_layers):
+        d = wlm.make_layer(wl, seed=wl.seed + 101 * l)
+        n = B * Hkv * W * 16 * D
+        pool = ops.HostPool(4 * n)
+        pool.tensor((B, Hkv, W, 16, D), torch.bfloat16).copy_(
+            wlm.key_tiles(d["K"].view(B, Hkv, W, 16, D)))
+        pool.tensor((B, Hkv, W, D, 16), torch.bfloat16, offset_bytes=2 * n).copy_(
+            d["V"].view(B, Hkv, W, 16, D).transpose(-1, -2))
+        pt = torch.randperm(B * K, generator=torch.Generator().manual_seed(wl.seed + l))
+        pt = pt.to(torch.int32).view(B, K)
+        layers.append(HostTierLayer(k_pool=dev(d["k_pool"]), block_table=dev(d["block_table"]),
+                                    ctx_len=dev(d["ctx_len"]), host_pool_k_dev=pool.device_ptr,
+                                    host_pool_v_dev=pool.device_ptr + 2 * n, host_blocks=W,
+                                    ws_page_table=dev(pt), num_q_heads=wl.num_q_heads,
+                                    k_blocks=K, cap=cap))
+        pools.append(pool)
+        keep.append(dict(K={r: d["K"][r].clone() for r in rows}, V={r: d["V"][r].clone() for r in rows},
+                         q=d["q"].unsqueeze(1), pt=pt,
+                         prev=wlm.draw_lookahead(wl, d["q32"], wl.seed + 1).to(torch.bfloat16),
+                         looks=[wlm.draw_lookahead(wl, d["q32"], wl.seed + 100 + t).to(torch.bfloat16)
+                                for t in range(T)]))
+        del d
+    pipe = HostTierDecode(layers)
+    pipe.fill([dev(k["prev"]) for k in keep])
+    torch.cuda.synchronize()
+    n_exempt = 0
+    for t in range(T):
+        before = [(L.slot_block.cpu().numpy(), L.last_use.cpu().numpy()) for L in layers]
+        outs = pipe.step([dev(k["q"]) for k in keep], [dev(k["looks"][t]) for k in keep], t,
+                         copy_out=True)
+        pipe.drain()
+        torch.cuda.synchronize()
+        for l, (L, k) in enumerate(zip(layers, keep)):
+            sb0, lu0 = before[l]
+            scores = L.scores.cpu().double().numpy()
+            sel = L.sel.cpu().numpy()
+            fb = L.fetch_block[:B * Hkv * cap].view(B, Hkv, cap).cpu().numpy()
+            fs = L.fetch_slot[:B * Hkv * cap].view(B, Hkv, cap).cpu().numpy()
+            fc = L.fetch_count.cpu().numpy()
+            sb1, lu1 = L.slot_block.cpu().numpy(), L.last_use.cpu().numpy()
+            out = outs[l].float().cpu().numpy()
+            ws_k, ws_v = L.ws_k.cpu(), L.ws_v.cpu()
+            assert np.all(fc <= cap)
+            for b, g in rows:
+                where = f"host tier layer {l} step {t} b{b} g{g}"
+                Kr, Vr = k["K"][(b, g)], k["V"][(b, g)]
+                qr = group_rows(k["looks"][t], b, g, G)
+                o_s = orc.score_row(qr, Kr, wl.ctx[b], 16, W)
+                check_scores(scores[b, g], o_s, score_tolerance(qr, Kr.double().numpy(), wl.ctx[b], 16, W),
+                             where)
+                o_sel = orc.select_row(o_s, W, K)
+                ex = check_selection_row(sel[b, g], o_sel, o_s, W, K, where)
+                use_sel = sel[b, g] if ex else o_sel
+                p_fb, p_fs, p_cnt, p_sb, p_lu = orc.plan_row(use_sel, o_s, sb0[b, g], lu0[b, g], cap, t)
+                o_plan = dict(fetch_block=p_fb, fetch_slot=p_fs, fetch_count=p_cnt, slot_block=p_sb,
+                              last_use=p_lu)
+                g_plan = dict(fetch_block=fb[b, g], fetch_slot=fs[b, g], fetch_count=fc[b, g],
+                              slot_block=sb1[b, g], last_use=lu1[b, g])
+                n_exempt += check_plan_row(g_plan, o_plan, use_sel, sb0[b, g], o_s, cap, t, where) or ex
+                # attention of this step ran over the working set the previous step left
+                o_out = orc.attn_row(k["q"][b, 0, g * G:(g + 1) * G], Kr, Vr, wl.ctx[b], 16, sb0[b, g])
+                err = np.abs(out[b, 0, g * G:(g + 1) * G] - o_out).max()
+                assert err <= ATTN_ATOL, (where, err)
+                # every resident slot holds its block's K and V tiles
+                for j in range(K):
+                    n_blk = int(sb1[b, g, j])
+                    if n_blk < 0:
+                        continue
+                    page = int(k["pt"][b, j])
+                    tok = slice(16 * n_blk, 16 * n_blk + 16)
+                    assert torch.equal(ws_k[page, g], wlm.key_tiles(Kr[tok])), (where, j)
+                    assert torch.equal(ws_v[page, g], Vr[tok].t()), (where, j)
+    assert n_exempt <= len(rows) * n_layers * T // 2
+
+
 def test_fetch_blocks_copies_listed_tiles_and_skips_bad_entries():
     wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(2000, 1500), n_hot=0,
                             seed=52)
