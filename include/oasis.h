@@ -210,6 +210,20 @@ int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *
                       int32_t *fetch_slot, int32_t *fetch_count, void *stream);
 
 /*
+ * oasis_select_plan with the step number partly in device memory: the plan
+ * uses step + *step_dev (step_dev may be NULL: step alone).  For callers that
+ * capture the decode step in a HIP graph and replay it: kernel arguments are
+ * fixed at capture, so the step number that the LRU order needs comes from a
+ * counter the graph advances on the device.  Same results as
+ * oasis_select_plan called with that sum.
+ */
+int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                         int32_t k_blocks, int32_t cap, int32_t step, const int32_t *step_dev,
+                         int32_t *sel, int32_t *slot_block, int32_t *last_use,
+                         int32_t *fetch_block, int32_t *fetch_slot, int32_t *fetch_count,
+                         void *stream);
+
+/*
  * Bytes of device workspace oasis_sparse_decode_attn needs for this shape:
  * room for the partial results of a row's shares (per row and share: max,
  * sum and the D-wide output of each query row), then one 32-bit arrival

@@ -190,6 +190,15 @@ int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *
                       int32_t k_blocks, int32_t cap, int32_t step, int32_t *sel,
                       int32_t *slot_block, int32_t *last_use, int32_t *fetch_block,
                       int32_t *fetch_slot, int32_t *fetch_count, void *stream) {
+    return oasis_select_plan_ex(s, scores, ctx_len, k_blocks, cap, step, nullptr, sel, slot_block,
+                                last_use, fetch_block, fetch_slot, fetch_count, stream);
+}
+
+int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                         int32_t k_blocks, int32_t cap, int32_t step, const int32_t *step_dev,
+                         int32_t *sel, int32_t *slot_block, int32_t *last_use,
+                         int32_t *fetch_block, int32_t *fetch_slot, int32_t *fetch_count,
+                         void *stream) {
     const char *fn = "oasis_select_plan";
     if (int e = check_shape(s, fn)) return e;
     if (k_blocks < 1) return fail(OASIS_ERR_INVALID, "%s: k_blocks %d < 1", fn, k_blocks);
@@ -209,7 +218,7 @@ int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *
     const int rows = s->batch * s->num_kv_heads;
     oasis::SelectPlanArgs a{scores, ctx_len, sel, slot_block, last_use, fetch_block, fetch_slot,
                             fetch_count, rows, s->num_kv_heads, s->table_width, k_blocks, cap,
-                            step};
+                            step, step_dev};
     if (oasis::row_select_plan_fits(s->table_width, k_blocks, 3))
         return check_hip(oasis::launch_row_select_plan(a, 3, as_stream(stream)), fn);
     if (oasis::row_select_plan_fits(s->table_width, k_blocks, 1)) {

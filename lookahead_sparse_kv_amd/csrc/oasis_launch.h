@@ -36,6 +36,7 @@ struct SelectPlanArgs {
     int32_t *fetch_slot;
     int32_t *fetch_count;
     int rows, hkv, width, k, cap, step;
+    const int32_t *step_dev;   // if set, *step_dev is added to step (read on the device)
 };
 
 struct FetchArgs {

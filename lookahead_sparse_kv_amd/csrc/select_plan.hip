@@ -44,13 +44,14 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
         __syncthreads();
     }
     if (MODE & 2) {
+        const int step = a.step + (a.step_dev ? *a.step_dev : 0);
         int32_t *fb = a.fetch_block + (size_t)row * a.cap;
         int32_t *fs = a.fetch_slot + (size_t)row * a.cap;
         if (MODE & 1)
-            row_plan(sel, [&](int s) { return key_to_score(keys[s]); }, K, a.cap, a.step, pf,
+            row_plan(sel, [&](int s) { return key_to_score(keys[s]); }, K, a.cap, step, pf,
                      a.slot_block + rk, a.last_use + rk, fb, fs, a.fetch_count + row, pl, sh);
         else
-            row_plan(sel, [&](int s) { return srow[s]; }, K, a.cap, a.step, pf, a.slot_block + rk,
+            row_plan(sel, [&](int s) { return srow[s]; }, K, a.cap, step, pf, a.slot_block + rk,
                      a.last_use + rk, fb, fs, a.fetch_count + row, pl, sh);
     }
 }

@@ -349,15 +349,22 @@ constexpr int kAttnRowFillRows = OASIS_ATTN_ROW_MIN_ROWS;
 #define OASIS_ATTN_ROWSPLIT_MIN_ROWS 128
 #endif
 constexpr int kRowAttnWaves = 8;
+#ifndef OASIS_ATTN_ROWSPLIT_WAVES
+#define OASIS_ATTN_ROWSPLIT_WAVES 8
+#endif
+constexpr int kRowSplitWaves = OASIS_ATTN_ROWSPLIT_WAVES;
+#ifndef OASIS_ATTN_ROWSPLIT_WGS
+#define OASIS_ATTN_ROWSPLIT_WGS 256     // workgroups the row-split launch aims for
+#endif
 
 // Workgroups per row and list entries per workgroup for the row-split
-// kernel; false where it does not apply (too few rows, or fewer than 8
-// entries per workgroup, which would leave waves without a block pair).
+// kernel; false where it does not apply (too few rows, or fewer than two
+// entries per wave, which would leave waves without a block pair).
 inline bool rowsplit_plan(int rows, int n_blk, int *splits, int *per) {
     if (rows < OASIS_ATTN_ROWSPLIT_MIN_ROWS || rows >= kAttnRowFillRows || rows < 1) return false;
-    const int s = (kAttnRowFillRows + rows - 1) / rows;
+    const int s = (OASIS_ATTN_ROWSPLIT_WGS + rows - 1) / rows;
     const int p = (n_blk + s - 1) / s;
-    if (s < 2 || p < 2 * kRowAttnWaves) return false;
+    if (s < 2 || p < 2 * kRowSplitWaves) return false;
     *splits = (n_blk + p - 1) / p;
     *per = p;
     return *splits >= 2;
@@ -370,7 +377,7 @@ __host__ __device__ inline int row_attn_wave_floats(int n_rows_q, int head_dim) 
 // The 8 waves of a workgroup walk entries [w_begin, w_end) of row `row`,
 // each a contiguous eighth (NE > 0: an eighth of exactly NE entries takes the
 // fully unrolled walk), and leave their (O, max, sum) in the workgroup's LDS.
-template <int D, int NE>
+template <int D, int NE, int NW = kRowAttnWaves>
 __device__ __forceinline__ void row_waves_to_lds(const AttnArgs &a, int row, int w_begin, int w_end,
                                                  float *red) {
     constexpr int MT = D / 16;
@@ -381,7 +388,7 @@ __device__ __forceinline__ void row_waves_to_lds(const AttnArgs &a, int row, int
     const int r16 = lane & 15;
     const int j4 = lane >> 4;
     const int nrq = a.n_rows_q;
-    const int per = (w_end - w_begin + kRowAttnWaves - 1) / kRowAttnWaves;
+    const int per = (w_end - w_begin + NW - 1) / NW;
     const int e_begin = w_begin + wave * per < w_end ? w_begin + wave * per : w_end;
     const int e_end = e_begin + per < w_end ? e_begin + per : w_end;
     bf16x8 qv[1][D / 32];
@@ -413,19 +420,19 @@ __device__ __forceinline__ void row_waves_to_lds(const AttnArgs &a, int row, int
     }
 }
 
-// (max, sum, O) of query row c, dim d, over the 8 waves' LDS partials.
-template <int D>
+// (max, sum, O) of query row c, dim d, over the NW waves' LDS partials.
+template <int D, int NW = kRowAttnWaves>
 __device__ __forceinline__ void lds_merge_waves(const float *red, int nrq, int c, int d, float &M,
                                                 float &L, float &O) {
     const float NEG_INF = -__builtin_inff();
     const int wstride = row_attn_wave_floats(nrq, D);
     M = NEG_INF;
 #pragma unroll
-    for (int w = 0; w < kRowAttnWaves; ++w) M = fmaxf(M, red[(size_t)w * wstride + (size_t)nrq * D + c]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[(size_t)w * wstride + (size_t)nrq * D + c]);
     L = 0.f;
     O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kRowAttnWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         const float *base = red + (size_t)w * wstride;
         const float m = base[(size_t)nrq * D + c];
         const float wgt = (m == NEG_INF) ? 0.f : exp2f(m - M);
@@ -475,7 +482,8 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArg
 // data that crosses workgroups is written and read at device scope, and each
 // workgroup's stores have completed before its increment is issued.
 template <int D, int NE>
-__global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_rowsplit_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kRowSplitWaves * kWave) void attn_rowsplit_kernel(AttnArgs a) {
+    constexpr int NW = kRowSplitWaves;
     extern __shared__ float red[];
     __shared__ int is_last;
     const int S = a.splits;
@@ -485,13 +493,13 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_rowsplit_kernel(At
     const float NEG_INF = -__builtin_inff();
     const int w_begin = part * a.per_split < a.n_blk ? part * a.per_split : a.n_blk;
     const int w_end = w_begin + a.per_split < a.n_blk ? w_begin + a.per_split : a.n_blk;
-    row_waves_to_lds<D, NE>(a, row, w_begin, w_end, red);
+    row_waves_to_lds<D, NE, NW>(a, row, w_begin, w_end, red);
     __syncthreads();
-    for (int idx = threadIdx.x; idx < nrq * D; idx += kRowAttnWaves * kWave) {
+    for (int idx = threadIdx.x; idx < nrq * D; idx += NW * kWave) {
         const int c = idx / D;
         const int d = idx - c * D;
         float M, L, O;
-        lds_merge_waves<D>(red, nrq, c, d, M, L, O);
+        lds_merge_waves<D, NW>(red, nrq, c, d, M, L, O);
         const size_t slot = ((size_t)row * S + part) * nrq + c;
         __hip_atomic_store(a.part_o + slot * D + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (d == 0) {
@@ -510,7 +518,7 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_rowsplit_kernel(At
     }
     __syncthreads();
     if (!is_last) return;
-    for (int idx = threadIdx.x; idx < nrq * D; idx += kRowAttnWaves * kWave) {
+    for (int idx = threadIdx.x; idx < nrq * D; idx += NW * kWave) {
         const int c = idx / D;
         const int d = idx - c * D;
         float M = NEG_INF, L = 0.f, O = 0.f;
@@ -575,14 +583,18 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share
         AttnArgs r = a;
         r.splits = wg_splits;
         r.per_split = wg_per;
-        const dim3 grid2((unsigned)(rows * wg_splits)), block2(kRowAttnWaves * kWave);
-        const bool eighth8 = wg_per == 8 * kRowAttnWaves;
+        const dim3 grid2((unsigned)(rows * wg_splits)), block2(kRowSplitWaves * kWave);
+        const size_t lds2 = (size_t)kRowSplitWaves * row_attn_wave_floats(a.n_rows_q, head_dim) * 4;
+        // a wave share of exactly 8 or 16 entries takes the fully unrolled walk
+        const int share = wg_per % kRowSplitWaves == 0 ? wg_per / kRowSplitWaves : 0;
         if (head_dim == 128) {
-            if (eighth8) hipLaunchKernelGGL((attn_rowsplit_kernel<128, 8>), grid2, block2, row_lds, stream, r);
-            else hipLaunchKernelGGL((attn_rowsplit_kernel<128, 0>), grid2, block2, row_lds, stream, r);
+            if (share == 8) hipLaunchKernelGGL((attn_rowsplit_kernel<128, 8>), grid2, block2, lds2, stream, r);
+            else if (share == 16) hipLaunchKernelGGL((attn_rowsplit_kernel<128, 16>), grid2, block2, lds2, stream, r);
+            else hipLaunchKernelGGL((attn_rowsplit_kernel<128, 0>), grid2, block2, lds2, stream, r);
         } else {
-            if (eighth8) hipLaunchKernelGGL((attn_rowsplit_kernel<64, 8>), grid2, block2, row_lds, stream, r);
-            else hipLaunchKernelGGL((attn_rowsplit_kernel<64, 0>), grid2, block2, row_lds, stream, r);
+            if (share == 8) hipLaunchKernelGGL((attn_rowsplit_kernel<64, 8>), grid2, block2, lds2, stream, r);
+            else if (share == 16) hipLaunchKernelGGL((attn_rowsplit_kernel<64, 16>), grid2, block2, lds2, stream, r);
+            else hipLaunchKernelGGL((attn_rowsplit_kernel<64, 0>), grid2, block2, lds2, stream, r);
         }
         return hipGetLastError();
     }

@@ -22,6 +22,7 @@ OASIS_OK, OASIS_ERR_INVALID, OASIS_ERR_UNSUPPORTED, OASIS_ERR_NOMEM, OASIS_ERR_H
 
 # Every symbol include/oasis.h declares.
 EXPORTS = ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax", "oasis_select_topk", "oasis_plan_fetch", "oasis_select_plan",
+           "oasis_select_plan_ex",
            "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_sparse_decode_attn_ex",
            "oasis_hostpool_create",
            "oasis_hostpool_device_pointer", "oasis_hostpool_destroy", "oasis_fetch_blocks",
@@ -60,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L.oasis_score_blocks_minmax.argtypes = [S, p, i32, p, p, p, p, f32, p, p]
         L.oasis_plan_fetch.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p]
         L.oasis_select_plan.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p, p]
+        L.oasis_select_plan_ex.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p, p, p]
         L.oasis_attn_workspace_bytes.argtypes = [S, i32, i32]
         L.oasis_attn_workspace_bytes.restype = sz
         L.oasis_sparse_decode_attn.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz, p]
@@ -71,7 +73,8 @@ def lib() -> ctypes.CDLL:
         L.oasis_fetch_blocks.argtypes = [S, p, p, i32, p, p, p, i32, p, p, p, p]
         for fn in ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax",
                    "oasis_select_topk", "oasis_plan_fetch",
-                   "oasis_select_plan", "oasis_sparse_decode_attn", "oasis_sparse_decode_attn_ex",
+                   "oasis_select_plan", "oasis_select_plan_ex", "oasis_sparse_decode_attn",
+                   "oasis_sparse_decode_attn_ex",
                    "oasis_hostpool_create",
                    "oasis_hostpool_device_pointer", "oasis_hostpool_destroy",
                    "oasis_fetch_blocks"):
@@ -183,12 +186,20 @@ def plan_fetch(shape: OasisShape, sel, scores, k_blocks, cap, step, slot_block, 
 
 
 def select_plan(shape: OasisShape, scores, ctx_len, k_blocks, cap, step, sel, slot_block,
-                last_use, fetch_block, fetch_slot, fetch_count, stream=None):
-    """select_topk then plan_fetch in one launch where the shape allows (same results)."""
-    _check(lib().oasis_select_plan(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks, cap,
-                                   step, _ptr(sel), _ptr(slot_block), _ptr(last_use),
-                                   _ptr(fetch_block), _ptr(fetch_slot), _ptr(fetch_count),
-                                   _stream(stream)))
+                last_use, fetch_block, fetch_slot, fetch_count, stream=None, step_dev=None):
+    """select_topk then plan_fetch in one launch where the shape allows (same results).
+    step_dev (int32 device tensor of one element, or None): the plan's step is
+    step + step_dev[0], read on the device (oasis_select_plan_ex)."""
+    if step_dev is None:
+        _check(lib().oasis_select_plan(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks,
+                                       cap, step, _ptr(sel), _ptr(slot_block), _ptr(last_use),
+                                       _ptr(fetch_block), _ptr(fetch_slot), _ptr(fetch_count),
+                                       _stream(stream)))
+    else:
+        _check(lib().oasis_select_plan_ex(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks,
+                                          cap, step, _ptr(step_dev), _ptr(sel), _ptr(slot_block),
+                                          _ptr(last_use), _ptr(fetch_block), _ptr(fetch_slot),
+                                          _ptr(fetch_count), _stream(stream)))
 
 
 def attn_workspace_bytes(shape: OasisShape, n_q: int, n_blk: int) -> int:

@@ -86,10 +86,12 @@ class DecodeLayer:
                        self.k_blocks, self.cap, step, self.slot_block, self.last_use,
                        self.fetch_block, self.fetch_slot, self.fetch_count, stream)
 
-    def select_plan(self, step, stream=None, scores=None):
+    def select_plan(self, step, stream=None, scores=None, step_dev=None):
+        """step_dev: the plan's step is step + step_dev[0], read on the device."""
         ops.select_plan(self.shape, self.scores if scores is None else scores, self.ctx_len,
                         self.k_blocks, self.cap, step, self.sel, self.slot_block, self.last_use,
-                        self.fetch_block, self.fetch_slot, self.fetch_count, stream)
+                        self.fetch_block, self.fetch_slot, self.fetch_count, stream,
+                        step_dev=step_dev)
 
     def attend(self, q, blocks=None, stream=None, share_gpu=False):
         """share_gpu: another launch (the next step's scoring) runs beside this one."""
@@ -207,6 +209,116 @@ class PipelinedDecode:
         main.wait_stream(self.side)
         if self.plan_stream is not None:
             main.wait_stream(self.plan_stream)
+
+
+class GraphedDecode:
+    """PipelinedDecode's schedule for several layers, captured once in a HIP
+    graph and replayed: one replay runs `rounds` decode steps of every layer.
+
+    The host then issues one graph launch per replay instead of a dozen
+    runtime calls per layer and step, which is what bounds the step when the
+    kernels are short (the compressed scorer).  Round k of a replay does, for
+    each layer in turn, what PipelinedDecode.step(q, q_looks[l][k], s) does:
+    scoring of the lookahead query on the scoring stream into one of two score
+    buffers, attention over the working set on the caller's stream (one CU
+    per row: the scoring runs beside it), then select + plan of step s + 1 on
+    the plan stream (or the caller's) once both are done.  The same events
+    order the streams, recorded and waited inside the capture only: replays
+    are serialised on the launching stream, so a replay starts after the
+    previous one has finished.
+
+    A graph fixes every kernel argument at capture, so the inputs are the
+    fixed tensors given here, and the plan's step number is
+    step0 + k + counter[0], with the counter in device memory advanced by
+    `rounds` at the end of each replay: replay n, round k plans step
+    step0 + n * rounds + k, as the eager steps would.
+
+        g = GraphedDecode(layers, q, q_looks, rounds=4, side=..., plan_stream=...)
+        g.prime(q_look_0, step=step0 - 1)     # eager: score + select/plan before the first round
+        g.replay()                            # rounds steps of every layer
+    """
+
+    # Captures of more than this many layer-steps (tried: 4 layers x 4 rounds
+    # at 16 x 32K) crashed the host process inside the end of the capture, in
+    # the runtime's capture_end; the cause is not known, so larger captures
+    # are refused.  Up to 2 layers x 2 rounds the replays are bit-identical to
+    # the eager steps.
+    MAX_LAYER_STEPS = 4
+
+    def __init__(self, layers, q, q_looks, rounds, step0=1, side=None, plan_stream=None,
+                 append=False):
+        if len(layers) * rounds > self.MAX_LAYER_STEPS or rounds > 2:
+            raise NotImplementedError(
+                f"GraphedDecode: {len(layers)} layers x {rounds} rounds; captures beyond "
+                f"2 layers x 2 rounds are switched off (a 4 x 4 capture crashed in capture_end)")
+        self.layers = list(layers)
+        self.q, self.q_looks, self.rounds, self.step0 = q, q_looks, rounds, step0
+        self.append = append
+        dev = self.layers[0].scores.device
+        self.side = side if side is not None else torch.cuda.Stream(device=dev)   # default priority
+        self.plan_stream = plan_stream
+        self.counter = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.buf = [(L.scores, torch.empty_like(L.scores)) for L in self.layers]
+        self.graph = None
+        # The events that order the streams during capture live as long as the
+        # graph: none may be destroyed while a capture that recorded or waited
+        # on it is still open.
+        n = len(self.layers)
+        self.ev_scored = [[torch.cuda.Event(), torch.cuda.Event()] for _ in range(n)]
+        self.ev_planned = [[torch.cuda.Event(), torch.cuda.Event()] for _ in range(n)]
+        self.ev_attended = [torch.cuda.Event() for _ in range(n)]
+
+    def prime(self, q_look, step):
+        """Eager, before capture: score + select/plan of `step` for every layer."""
+        main = torch.cuda.current_stream()
+        for L, (b0, _) in zip(self.layers, self.buf):
+            L.score(q_look, stream=main, scores=b0, refresh=self.append)
+            L.select_plan(step, stream=main, scores=b0)
+
+    def _schedule(self):
+        main = torch.cuda.current_stream()
+        ps = main if self.plan_stream is None else self.plan_stream
+        n = len(self.layers)
+        ev_scored, ev_planned, ev_attended = self.ev_scored, self.ev_planned, self.ev_attended
+        planned = [[False, False] for _ in range(n)]     # recorded in this capture
+        last_plan = [None] * n
+        self.side.wait_stream(main)                         # fork from the capturing stream
+        if ps is not main:
+            ps.wait_stream(main)
+        for k in range(self.rounds):
+            for l, L in enumerate(self.layers):
+                b = (k + 1) % 2                             # buffer 0 holds the primed scores
+                if planned[l][b]:
+                    self.side.wait_event(ev_planned[l][b])  # the plan that last read buf[b]
+                L.score(self.q_looks[l][k], stream=self.side, scores=self.buf[l][b],
+                        refresh=self.append)
+                ev_scored[l][b].record(self.side)
+                if ps is not main and last_plan[l] is not None:
+                    main.wait_event(last_plan[l])           # the working set of this step
+                L.attend(self.q, stream=main, share_gpu=True)
+                if ps is not main:
+                    ev_attended[l].record(main)             # the plan rewrites what it read
+                    ps.wait_event(ev_attended[l])
+                ps.wait_event(ev_scored[l][b])
+                L.select_plan(self.step0 + k, stream=ps, scores=self.buf[l][b],
+                              step_dev=self.counter)
+                ev_planned[l][b].record(ps)
+                planned[l][b] = True
+                last_plan[l] = ev_planned[l][b]
+        main.wait_stream(self.side)                         # join
+        if ps is not main:
+            main.wait_stream(ps)
+        self.counter.add_(self.rounds)
+
+    def capture(self):
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._schedule()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()
 
 
 class HostTierLayer:

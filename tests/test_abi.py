@@ -168,3 +168,14 @@ def test_minmax_calls_reject_bad_arguments():
     assert pk(ck=ctypes.c_void_p(24)) == ops.OASIS_ERR_INVALID
     assert pk(shape=_shape(block_size=8)) == ops.OASIS_ERR_UNSUPPORTED
     assert pk(shape=_shape(batch=0)) == ops.OASIS_OK
+
+
+def test_graphed_decode_refuses_captures_beyond_the_tested_size():
+    # captures of 4 layers x 4 rounds crashed at the end of the capture; the
+    # class refuses anything beyond 2 layers x 2 rounds before touching a GPU
+    import pytest
+    from lookahead_sparse_kv_amd.pipeline import GraphedDecode
+    with pytest.raises(NotImplementedError):
+        GraphedDecode([object()] * 4, None, None, rounds=4)
+    with pytest.raises(NotImplementedError):
+        GraphedDecode([object()] * 1, None, None, rounds=3)
