@@ -55,6 +55,9 @@ def parse():
                         "where consecutive layers hold different KV)")
     p.add_argument("--plan-stream", choices=("auto", "on", "off"), default="auto",
                    help="select + plan on a third stream (auto: with the compressed scorer)")
+    p.add_argument("--native", choices=("on", "off"), default="on",
+                   help="enqueue each pipelined layer-step with one oasis_layer_step call "
+                        "(on) or with the Python sequence of launches and event calls (off)")
     p.add_argument("--graph", choices=("off", "on"), default="off",
                    help="time the steps as replays of a HIP graph (switched off: capturing "
                         "the bench's schedule of 4 replicas x 4 rounds crashed the process "
@@ -584,7 +587,10 @@ def main():
     # stream (a third stream measured slower there).
     use_plan_stream = (wl.scorer == "minmax") if args.plan_stream == "auto" else args.plan_stream == "on"
     plan_stream = torch.cuda.Stream(device=dev) if use_plan_stream else None
-    pipes = [PipelinedDecode(L, side=side, plan_stream=plan_stream) for L in layers]
+    # the timed loop enqueues each layer-step natively; the loop with events
+    # around the scoring launches takes the Python path (same launches)
+    pipes = [PipelinedDecode(L, side=side, plan_stream=plan_stream, native=args.native == "on")
+             for L in layers]
     # compressed scorer: each scoring launch also re-pools the block a decode
     # step appends to (the pool itself is not written here)
     append = wl.scorer == "minmax"
@@ -791,6 +797,7 @@ def main():
                    "n_look": wl.n_look, "scorer": wl.scorer,
                    "step": "score + select/plan + attn, one layer",
                    "streams": 3 if plan_stream is not None else 2,
+                   "enqueue": "oasis_layer_step" if args.native == "on" else "python",
                    "graph": ({"rounds_per_replay": graph.rounds, "replicas": n_rep,
                               "replays_timed": timed_steps // per_replay}
                              if graph is not None else None),

@@ -326,6 +326,55 @@ int oasis_fetch_blocks(const oasis_shape *s, const uint16_t *host_k, const uint1
                        const int32_t *fetch_count, int32_t cap, const int32_t *ws_page_table,
                        uint16_t *ws_k_pool, uint16_t *ws_v_pool, void *stream);
 
+/*
+ * One layer of the overlapped decode step, enqueued by one call: the three
+ * calls of a step and the event waits and records that order them across
+ * streams (flow step 4 and Figure 8 caption: the next step's prediction runs
+ * ahead of, and overlaps, the current step's attention).  For host loops
+ * whose kernels are short enough that a dozen runtime calls per layer and
+ * step would bound the step.
+ *
+ * oasis_layer holds what does not change from step to step (caller-owned
+ * device buffers, as in the calls named below); ck == NULL selects exact
+ * scoring (oasis_score_blocks), else the compressed keys
+ * (oasis_score_blocks_minmax, re-pooling each sequence's last block first
+ * when refresh != 0).  oasis_step_sync holds hipStream_t / hipEvent_t
+ * handles passed as void*; an event that is NULL is skipped.  The call
+ * enqueues, in this order:
+ *
+ *   score_stream: wait score_after; scoring of q_look_next into scores;
+ *                 record scored
+ *   attn_stream:  wait attn_after; oasis_sparse_decode_attn_ex(attn_flags) of
+ *                 q over the working set slot_block (full-pool mode: the block
+ *                 table as page table); record attended if plan_stream differs
+ *   plan_stream:  if it differs from attn_stream, wait attended; wait scored;
+ *                 oasis_select_plan(step) from scores; record planned
+ *
+ * and nothing else: the results are those of the three calls in that order.
+ * Errors: the first failing call's status; the calls before it stay enqueued.
+ */
+typedef struct {
+    oasis_shape shape;                 /* full-pool shape: num_pages = key pool pages */
+    const uint16_t *k_pool, *v_pool;
+    const int32_t *block_table, *ctx_len;
+    uint16_t *ck;                      /* compressed keys, or NULL for exact scoring */
+    int32_t refresh, n_look, n_q, k_blocks, cap, attn_flags;
+    float scale;
+    int32_t *sel, *slot_block, *last_use, *fetch_block, *fetch_slot, *fetch_count;
+    uint16_t *out;
+    void *workspace;
+    size_t workspace_bytes;
+} oasis_layer;
+
+typedef struct {
+    void *score_stream, *attn_stream, *plan_stream;
+    void *score_after, *attn_after;    /* events waited on first (NULL: none) */
+    void *scored, *attended, *planned; /* events recorded */
+} oasis_step_sync;
+
+int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const uint16_t *q,
+                     float *scores, int32_t step, const oasis_step_sync *sync);
+
 /* Human-readable name of a status code (static storage). */
 const char *oasis_status_string(int status);
 

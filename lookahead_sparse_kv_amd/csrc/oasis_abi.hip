@@ -296,6 +296,46 @@ int oasis_sparse_decode_attn_ex(const oasis_shape *s, const uint16_t *q, int32_t
                                                       as_stream(stream)), fn);
 }
 
+int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const uint16_t *q,
+                     float *scores, int32_t step, const oasis_step_sync *sync) {
+    const char *fn = "oasis_layer_step";
+    if (!L || !sync) return fail(OASIS_ERR_INVALID, "%s: NULL layer or sync", fn);
+    if (!sync->scored || (sync->plan_stream != sync->attn_stream && !sync->attended))
+        return fail(OASIS_ERR_INVALID, "%s: the scored / attended events are required", fn);
+    hipStream_t ss = as_stream(sync->score_stream), as = as_stream(sync->attn_stream),
+                ps = as_stream(sync->plan_stream);
+    const auto ev = [](void *e) { return reinterpret_cast<hipEvent_t>(e); };
+    if (sync->score_after)
+        if (int e = check_hip(hipStreamWaitEvent(ss, ev(sync->score_after), 0), fn)) return e;
+    int e = L->ck ? oasis_score_blocks_minmax(&L->shape, q_look_next, L->n_look, L->ck,
+                                              L->refresh ? L->k_pool : nullptr,
+                                              L->refresh ? L->block_table : nullptr, L->ctx_len,
+                                              L->scale, scores, ss)
+                  : oasis_score_blocks(&L->shape, q_look_next, L->n_look, L->k_pool, L->block_table,
+                                       L->ctx_len, L->scale, scores, ss);
+    if (e) return e;
+    if ((e = check_hip(hipEventRecord(ev(sync->scored), ss), fn))) return e;
+    if (sync->attn_after)
+        if ((e = check_hip(hipStreamWaitEvent(as, ev(sync->attn_after), 0), fn))) return e;
+    if ((e = oasis_sparse_decode_attn_ex(&L->shape, q, L->n_q, L->k_pool, L->v_pool, L->block_table,
+                                         L->slot_block, L->k_blocks, L->slot_block, L->ctx_len,
+                                         L->scale, L->out, L->workspace, L->workspace_bytes,
+                                         L->attn_flags, as)))
+        return e;
+    if (ps != as) {
+        if ((e = check_hip(hipEventRecord(ev(sync->attended), as), fn))) return e;
+        if ((e = check_hip(hipStreamWaitEvent(ps, ev(sync->attended), 0), fn))) return e;
+    }
+    if ((e = check_hip(hipStreamWaitEvent(ps, ev(sync->scored), 0), fn))) return e;
+    if ((e = oasis_select_plan(&L->shape, scores, L->ctx_len, L->k_blocks, L->cap, step, L->sel,
+                               L->slot_block, L->last_use, L->fetch_block, L->fetch_slot,
+                               L->fetch_count, ps)))
+        return e;
+    if (sync->planned)
+        if ((e = check_hip(hipEventRecord(ev(sync->planned), ps), fn))) return e;
+    return ok();
+}
+
 int oasis_hostpool_create(size_t bytes, void **host_ptr) {
     const char *fn = "oasis_hostpool_create";
     if (!host_ptr) return fail(OASIS_ERR_INVALID, "%s: host_ptr is NULL", fn);

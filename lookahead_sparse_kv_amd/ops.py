@@ -26,7 +26,7 @@ EXPORTS = ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax",
            "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_sparse_decode_attn_ex",
            "oasis_hostpool_create",
            "oasis_hostpool_device_pointer", "oasis_hostpool_destroy", "oasis_fetch_blocks",
-           "oasis_status_string", "oasis_last_error", "oasis_version")
+           "oasis_layer_step", "oasis_status_string", "oasis_last_error", "oasis_version")
 
 
 class OasisShape(ctypes.Structure):
@@ -34,6 +34,27 @@ class OasisShape(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("table_width", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32)]
+
+
+class OasisLayer(ctypes.Structure):
+    """oasis_layer: one layer's fixed buffers for oasis_layer_step."""
+    _fields_ = [("shape", OasisShape), ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("ctx_len", ctypes.c_void_p),
+                ("ck", ctypes.c_void_p), ("refresh", ctypes.c_int32), ("n_look", ctypes.c_int32),
+                ("n_q", ctypes.c_int32), ("k_blocks", ctypes.c_int32), ("cap", ctypes.c_int32),
+                ("attn_flags", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("sel", ctypes.c_void_p), ("slot_block", ctypes.c_void_p),
+                ("last_use", ctypes.c_void_p), ("fetch_block", ctypes.c_void_p),
+                ("fetch_slot", ctypes.c_void_p), ("fetch_count", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class OasisStepSync(ctypes.Structure):
+    """oasis_step_sync: streams and events (raw handles) of one oasis_layer_step."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("score_stream", "attn_stream", "plan_stream",
+                                                "score_after", "attn_after", "scored",
+                                                "attended", "planned")]
 
 
 class OasisError(RuntimeError):
@@ -65,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.oasis_attn_workspace_bytes.argtypes = [S, i32, i32]
         L.oasis_attn_workspace_bytes.restype = sz
         L.oasis_sparse_decode_attn.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz, p]
+        L.oasis_layer_step.argtypes = [ctypes.POINTER(OasisLayer), p, p, p, i32,
+                                       ctypes.POINTER(OasisStepSync)]
         L.oasis_sparse_decode_attn_ex.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz,
                                                   i32, p]
         L.oasis_hostpool_create.argtypes = [sz, ctypes.POINTER(ctypes.c_void_p)]
@@ -73,7 +96,8 @@ def lib() -> ctypes.CDLL:
         L.oasis_fetch_blocks.argtypes = [S, p, p, i32, p, p, p, i32, p, p, p, p]
         for fn in ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax",
                    "oasis_select_topk", "oasis_plan_fetch",
-                   "oasis_select_plan", "oasis_select_plan_ex", "oasis_sparse_decode_attn",
+                   "oasis_select_plan", "oasis_select_plan_ex", "oasis_layer_step",
+                   "oasis_sparse_decode_attn",
                    "oasis_sparse_decode_attn_ex",
                    "oasis_hostpool_create",
                    "oasis_hostpool_device_pointer", "oasis_hostpool_destroy",
@@ -226,6 +250,13 @@ def sparse_decode_attn(shape: OasisShape, q, k_pool, v_pool, page_table, blk, bl
     else:
         _check(lib().oasis_sparse_decode_attn(*args, _stream(stream)))
     return out
+
+
+def layer_step(layer: OasisLayer, q_look_next, q, scores, step: int, sync: OasisStepSync):
+    """oasis_layer_step: score (q_look_next -> scores), attention (q), select + plan (step),
+    ordered across the streams of `sync` by its events."""
+    _check(lib().oasis_layer_step(ctypes.byref(layer), _ptr(q_look_next), _ptr(q), _ptr(scores),
+                                  step, ctypes.byref(sync)))
 
 
 class HostPool:

@@ -93,6 +93,28 @@ class DecodeLayer:
                         self.fetch_block, self.fetch_slot, self.fetch_count, stream,
                         step_dev=step_dev)
 
+    def native_desc(self, share_gpu=True, refresh=False):
+        """oasis_layer descriptor of this layer for oasis_layer_step (built once per
+        setting; every pointer in it is a buffer this layer holds)."""
+        key = (share_gpu, refresh)
+        cache = self.__dict__.setdefault("_native", {})
+        if key not in cache:
+            D = self.shape.head_dim
+            vp = lambda t: None if t is None else t.data_ptr()
+            cache[key] = ops.OasisLayer(
+                shape=self.shape, k_pool=vp(self.k_pool), v_pool=vp(self.v_pool),
+                block_table=vp(self.block_table), ctx_len=vp(self.ctx_len), ck=vp(self.ck),
+                refresh=int(refresh), n_look=self.n_look, n_q=self.n_q, k_blocks=self.k_blocks,
+                cap=self.cap, attn_flags=ops.OASIS_ATTN_SHARE_GPU if share_gpu else 0,
+                scale=float(D) ** -0.5, sel=vp(self.sel), slot_block=vp(self.slot_block),
+                last_use=vp(self.last_use), fetch_block=vp(self.fetch_block),
+                fetch_slot=vp(self.fetch_slot), fetch_count=vp(self.fetch_count),
+                out=vp(self.out), workspace=vp(self.workspace),
+                workspace_bytes=self.workspace.numel() * self.workspace.element_size())
+        desc = cache[key]
+        desc.cap = self.cap                     # the one field a caller changes between steps
+        return desc
+
     def attend(self, q, blocks=None, stream=None, share_gpu=False):
         """share_gpu: another launch (the next step's scoring) runs beside this one."""
         blocks = self.slot_block if blocks is None else blocks
@@ -134,10 +156,12 @@ class PipelinedDecode:
         pipe.drain()
     """
 
-    def __init__(self, layer: DecodeLayer, side=None, plan_stream=None):
+    def __init__(self, layer: DecodeLayer, side=None, plan_stream=None, native=False):
         """`side`: the stream the scoring runs on; `plan_stream`: the stream
         select + plan runs on (None: the caller's).  Several pipelines (one per
-        layer) may share them, so that each runs layer after layer."""
+        layer) may share them, so that each runs layer after layer.  `native`:
+        each step is one oasis_layer_step call, which enqueues the same three
+        launches and the same event waits and records from native code."""
         self.L = layer
         self.buf = [layer.scores, torch.empty_like(layer.scores)]
         if side is None:
@@ -150,6 +174,13 @@ class PipelinedDecode:
         self.last_plan = None            # event of the latest plan (plan_stream mode)
         self.used = [False, False]
         self.i = 0
+        self.native = native
+        if native:
+            # torch creates an event at its first record: create them now, so
+            # that their handles can be handed to native code
+            cur = torch.cuda.current_stream()
+            for e in (*self.ev_scored, *self.ev_planned, self.ev_attended):
+                e.record(cur)
 
     def _score_next(self, q_look, main, ev=None, append=False):
         b = self.i % 2
@@ -196,6 +227,9 @@ class PipelinedDecode:
         sequence's last block: the token of this step must already be in the
         key pool as that stream sees it."""
         main = torch.cuda.current_stream()
+        if self.native and score_events is None and not copy_out:
+            self._native_step(q, q_look_next, step, main, append)
+            return None
         if self.plan_stream is not None and self.last_plan is not None:
             main.wait_event(self.last_plan)             # the working set of `step`
         b = self._score_next(q_look_next, main, score_events, append)
@@ -203,6 +237,27 @@ class PipelinedDecode:
         out = self.L.out.clone() if copy_out else None
         self._plan(b, step + 1, main, after_attention=True)
         return out
+
+    def _native_step(self, q, q_look_next, step, main, append):
+        """The same step as the Python path below, through oasis_layer_step."""
+        b = self.i % 2
+        score_after = None
+        if self.used[b]:
+            score_after = self.ev_planned[b]            # the plan that last read buf[b]
+        else:
+            self.side.wait_stream(main)                 # inputs written on the caller's stream
+        ps = main if self.plan_stream is None else self.plan_stream
+        attn_after = self.last_plan if self.plan_stream is not None else None
+        h = lambda x: None if x is None else x.cuda_event
+        sync = ops.OasisStepSync(score_stream=self.side.cuda_stream, attn_stream=main.cuda_stream,
+                                 plan_stream=ps.cuda_stream, score_after=h(score_after),
+                                 attn_after=h(attn_after), scored=h(self.ev_scored[b]),
+                                 attended=h(self.ev_attended), planned=h(self.ev_planned[b]))
+        ops.layer_step(self.L.native_desc(share_gpu=True, refresh=append), q_look_next, q,
+                       self.buf[b], step + 1, sync)
+        self.last_plan = self.ev_planned[b]
+        self.used[b] = True
+        self.i += 1
 
     def drain(self):
         main = torch.cuda.current_stream()

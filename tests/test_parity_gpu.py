@@ -548,6 +548,49 @@ def test_pipelined_decode_matches_sequential_steps(plan_stream):
     assert torch.equal(pipe_layer.sel, seq.sel)
 
 
+@pytest.mark.parametrize("scorer,plan_stream,batch", [("exact", False, 4), ("exact", False, 16),
+                                                      ("minmax", True, 16), ("minmax", False, 4)])
+def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch):
+    """oasis_layer_step enqueues the pipelined step (score, attention, select +
+    plan, with the same event waits and records) from native code: per-step
+    outputs and the final state are bit-identical to the Python pipeline's,
+    over several layers taking turns on shared streams.  32 and 128 rows."""
+    wl = wlm.small_workload(batch=batch, q_heads=32, kv_heads=8, head_dim=128,
+                            ctx=(4096, 3000, 2500, 4000), budget=512, n_hot=12, ratio=0.125, seed=44)
+    n_layers, T = 2, 5
+    datas = [wlm.make_layer(wl, seed=44 + 5 * l) for l in range(n_layers)]
+    q = dev(datas[0]["q"].unsqueeze(1))
+    looks = [[dev(wlm.draw_lookahead(wl, d["q32"], 700 + 3 * t + l).to(torch.bfloat16))
+              for t in range(T + 1)] for l, d in enumerate(datas)]
+    append = scorer == "minmax"
+    runs = {}
+    for native in (False, True):
+        sb, lu = (x.numpy() for x in wlm.empty_state(wl))
+        layers = [_gpu_layer(wl, d, wl.cap(), sb, lu, scorer=scorer) for d in datas]
+        side = torch.cuda.Stream()
+        ps = torch.cuda.Stream() if plan_stream else None
+        pipes = [PipelinedDecode(L, side=side, plan_stream=ps, native=native) for L in layers]
+        for l, P in enumerate(pipes):
+            P.prime(looks[l][0], 0, append=append)
+        outs = []
+        for t in range(T):
+            for l, (P, L) in enumerate(zip(pipes, layers)):
+                P.step(q, looks[l][t + 1], t, copy_out=False, append=append)
+                outs.append(L.out.clone())
+        for P in pipes:
+            P.drain()
+        torch.cuda.synchronize()
+        runs[native] = (outs, [{k: getattr(L, k).clone() for k in
+                                ("sel", "slot_block", "last_use", "fetch_count")} for L in layers])
+    (o_py, st_py), (o_nat, st_nat) = runs[False], runs[True]
+    for i, (a, b) in enumerate(zip(o_py, o_nat)):
+        assert torch.equal(a, b), i
+    for a, b in zip(st_py, st_nat):
+        for k in a:
+            assert torch.equal(a[k], b[k]), k
+    assert int(max(x["fetch_count"].max().item() for x in st_nat)) == wl.cap()
+
+
 def test_step_is_deterministic():
     wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(8000, 5000),
                             budget=1024, n_hot=20, ratio=0.05, seed=41)
