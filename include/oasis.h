@@ -17,6 +17,11 @@
  *
  * and, for the pages' own compressed-key scorer, oasis_pool_keys (min/max
  * pooling of the keys) and oasis_score_blocks_minmax (scores from them).
+ * oasis_select_plan runs select and plan as one launch (oasis_select_plan_ex:
+ * with the step number partly in device memory); oasis_layer_step enqueues a
+ * whole overlapped layer-step (score, attention, select + plan and the event
+ * edges between their streams) in one call; oasis_hostpool_* and
+ * oasis_fetch_blocks are the pinned host tier and its capped fetch.
  *
  * Conventions shared by every call
  * --------------------------------

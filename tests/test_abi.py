@@ -179,3 +179,19 @@ def test_graphed_decode_refuses_captures_beyond_the_tested_size():
         GraphedDecode([object()] * 4, None, None, rounds=4)
     with pytest.raises(NotImplementedError):
         GraphedDecode([object()] * 1, None, None, rounds=3)
+
+
+def test_layer_step_argument_checks():
+    # host-side validation only: nothing is enqueued on a failing call
+    L = ops.lib()
+    layer = ops.OasisLayer()
+    sync = ops.OasisStepSync()
+    assert L.oasis_layer_step(None, P, P, P, 0, ctypes.byref(sync)) == ops.OASIS_ERR_INVALID
+    assert L.oasis_layer_step(ctypes.byref(layer), P, P, P, 0, None) == ops.OASIS_ERR_INVALID
+    # the scored event is required, and the attended one when the plan has a stream of its own
+    assert L.oasis_layer_step(ctypes.byref(layer), P, P, P, 0, ctypes.byref(sync)) == \
+        ops.OASIS_ERR_INVALID
+    sync.scored = 8
+    sync.plan_stream = 16
+    assert L.oasis_layer_step(ctypes.byref(layer), P, P, P, 0, ctypes.byref(sync)) == \
+        ops.OASIS_ERR_INVALID
