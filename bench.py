@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--native", choices=("on", "off"), default="on",
                    help="enqueue each pipelined layer-step with one oasis_layer_step call "
                         "(on) or with the Python sequence of launches and event calls (off)")
+    p.add_argument("--attn-share", choices=("auto", "on", "off"), default="auto",
+                   help="attention in the step launched with the share-GPU hint (one CU per "
+                        "row; auto: with exact scoring)")
     p.add_argument("--graph", choices=("off", "on"), default="off",
                    help="time the steps as replays of a HIP graph (switched off: capturing "
                         "the bench's schedule of 4 replicas x 4 rounds crashed the process "
@@ -589,7 +592,12 @@ def main():
     plan_stream = torch.cuda.Stream(device=dev) if use_plan_stream else None
     # the timed loop enqueues each layer-step natively; the loop with events
     # around the scoring launches takes the Python path (same launches)
-    pipes = [PipelinedDecode(L, side=side, plan_stream=plan_stream, native=args.native == "on")
+    # attention beside the scoring of the next step: with exact scoring (the
+    # longer kernel) one CU per row leaves the other CUs to it; with the
+    # compressed scorer attention is the longer kernel and takes every CU
+    share_gpu = (wl.scorer == "exact") if args.attn_share == "auto" else args.attn_share == "on"
+    pipes = [PipelinedDecode(L, side=side, plan_stream=plan_stream, native=args.native == "on",
+                             share_gpu=share_gpu)
              for L in layers]
     # compressed scorer: each scoring launch also re-pools the block a decode
     # step appends to (the pool itself is not written here)
@@ -798,6 +806,8 @@ def main():
                    "step": "score + select/plan + attn, one layer",
                    "streams": 3 if plan_stream is not None else 2,
                    "enqueue": "oasis_layer_step" if args.native == "on" else "python",
+                   "attn_in_step": ("one workgroup per row (share-GPU hint)" if share_gpu else
+                                    "default launch shape"),
                    "graph": ({"rounds_per_replay": graph.rounds, "replicas": n_rep,
                               "replays_timed": timed_steps // per_replay}
                              if graph is not None else None),

@@ -156,12 +156,16 @@ class PipelinedDecode:
         pipe.drain()
     """
 
-    def __init__(self, layer: DecodeLayer, side=None, plan_stream=None, native=False):
+    def __init__(self, layer: DecodeLayer, side=None, plan_stream=None, native=False,
+                 share_gpu=True):
         """`side`: the stream the scoring runs on; `plan_stream`: the stream
         select + plan runs on (None: the caller's).  Several pipelines (one per
         layer) may share them, so that each runs layer after layer.  `native`:
         each step is one oasis_layer_step call, which enqueues the same three
-        launches and the same event waits and records from native code."""
+        launches and the same event waits and records from native code.
+        `share_gpu`: attention launched with the share-GPU hint (one CU per row
+        from 128 rows), which pays when the concurrent scoring is the longer
+        kernel (exact scoring); without it, attention spreads over every CU."""
         self.L = layer
         self.buf = [layer.scores, torch.empty_like(layer.scores)]
         if side is None:
@@ -175,6 +179,7 @@ class PipelinedDecode:
         self.used = [False, False]
         self.i = 0
         self.native = native
+        self.share_gpu = share_gpu
         if native:
             # torch creates an event at its first record: create them now, so
             # that their handles can be handed to native code
@@ -233,7 +238,7 @@ class PipelinedDecode:
         if self.plan_stream is not None and self.last_plan is not None:
             main.wait_event(self.last_plan)             # the working set of `step`
         b = self._score_next(q_look_next, main, score_events, append)
-        self.L.attend(q, stream=main, share_gpu=True)
+        self.L.attend(q, stream=main, share_gpu=self.share_gpu)
         out = self.L.out.clone() if copy_out else None
         self._plan(b, step + 1, main, after_attention=True)
         return out
@@ -253,7 +258,7 @@ class PipelinedDecode:
                                  plan_stream=ps.cuda_stream, score_after=h(score_after),
                                  attn_after=h(attn_after), scored=h(self.ev_scored[b]),
                                  attended=h(self.ev_attended), planned=h(self.ev_planned[b]))
-        ops.layer_step(self.L.native_desc(share_gpu=True, refresh=append), q_look_next, q,
+        ops.layer_step(self.L.native_desc(share_gpu=self.share_gpu, refresh=append), q_look_next, q,
                        self.buf[b], step + 1, sync)
         self.last_plan = self.ev_planned[b]
         self.used[b] = True

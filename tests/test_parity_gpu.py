@@ -548,9 +548,10 @@ def test_pipelined_decode_matches_sequential_steps(plan_stream):
     assert torch.equal(pipe_layer.sel, seq.sel)
 
 
-@pytest.mark.parametrize("scorer,plan_stream,batch", [("exact", False, 4), ("exact", False, 16),
-                                                      ("minmax", True, 16), ("minmax", False, 4)])
-def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch):
+@pytest.mark.parametrize("scorer,plan_stream,batch,share", [
+    ("exact", False, 4, True), ("exact", False, 16, True), ("minmax", True, 16, True),
+    ("minmax", True, 16, False), ("minmax", False, 4, True)])
+def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch, share):
     """oasis_layer_step enqueues the pipelined step (score, attention, select +
     plan, with the same event waits and records) from native code: per-step
     outputs and the final state are bit-identical to the Python pipeline's,
@@ -569,7 +570,8 @@ def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch):
         layers = [_gpu_layer(wl, d, wl.cap(), sb, lu, scorer=scorer) for d in datas]
         side = torch.cuda.Stream()
         ps = torch.cuda.Stream() if plan_stream else None
-        pipes = [PipelinedDecode(L, side=side, plan_stream=ps, native=native) for L in layers]
+        pipes = [PipelinedDecode(L, side=side, plan_stream=ps, native=native, share_gpu=share)
+                 for L in layers]
         for l, P in enumerate(pipes):
             P.prime(looks[l][0], 0, append=append)
         outs = []
