@@ -39,7 +39,8 @@
  *    negative list entry makes that block count as absent (score -inf, not
  *    attended) instead of being dereferenced; a context longer than
  *    table_width * block_size is clamped to it.
- *  - Calls are reentrant; the library keeps no state besides the error text.
+ *  - Calls are reentrant; the library keeps no state besides the error text
+ *    and a count of attention calls (the source of their tokens).
  *
  * Layouts (row-major, innermost last):
  *  - lookahead queries  q_look  [B][n_look][Hq][D]    bf16
@@ -231,11 +232,12 @@ int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_
 /*
  * Bytes of device workspace oasis_sparse_decode_attn needs for this shape:
  * room for the partial results of a row's shares (per row and share: max,
- * sum and the D-wide output of each query row), then one 32-bit arrival
- * counter per row (B * Hkv rows), padded to 16 bytes.  The counters must be
- * zero before the first call on a workspace (allocate it zero-filled); every
- * call leaves them zero again.  One workspace serves one call at a time.
- * Returns 0 for an invalid shape.
+ * sum and the D-wide output of each query row), then one 32-bit hand-over
+ * flag per row (B * Hkv rows), padded to 16 bytes.  The workspace needs no
+ * initialisation: the two workgroups of a row exchange a token that differs
+ * from call to call (never 0) in the row's flag, and the one that receives
+ * the token merges and sets the flag to 0.  One workspace serves one call at
+ * a time.  Returns 0 for an invalid shape.
  */
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk);
 
@@ -262,8 +264,7 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
  * together).
  * A row with no valid token outputs zeros.  bf16 in and out, fp32 softmax and
  * accumulation.  Requires D in {64, 128}, bs = 16, 1 <= n_q, n_q * G <= 32,
- * n_blk >= 1, scale > 0, and workspace_bytes >= oasis_attn_workspace_bytes()
- * of a workspace whose counters are zero (see there).
+ * n_blk >= 1, scale > 0, and workspace_bytes >= oasis_attn_workspace_bytes().
  *
  * Launch shape (results agree to fp32 rounding whichever is taken): from 256
  * rows (B * Hkv), one workgroup per row merges its waves in LDS; from 128

@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "oasis.h"
 #include "oasis_launch.h"
 
@@ -243,6 +245,16 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
            (((size_t)rows * sizeof(uint32_t) + 15) & ~(size_t)15);
 }
 
+// A nonzero token per attention call: the two workgroups of a row exchange it
+// in the row's flag to find which of them merges (the flag need not start at
+// any particular value, and returns to 0 after the call).
+static uint32_t next_attn_token() {
+    static std::atomic<uint32_t> calls{0};
+    uint32_t t = calls.fetch_add(1, std::memory_order_relaxed) + 1;
+    if (t == 0) t = calls.fetch_add(1, std::memory_order_relaxed) + 1;
+    return t;
+}
+
 int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_q,
                              const uint16_t *k_pool, const uint16_t *v_pool,
                              const int32_t *page_table, const int32_t *blk, int32_t n_blk,
@@ -287,9 +299,9 @@ int oasis_sparse_decode_attn_ex(const oasis_shape *s, const uint16_t *q, int32_t
     const int nrq = n_q * G;
     float *part_o = static_cast<float *>(workspace);
     float *part_ml = part_o + (size_t)rows * splits * nrq * s->head_dim;
-    uint32_t *row_count = reinterpret_cast<uint32_t *>(part_ml + (size_t)rows * splits * nrq * 2);
+    uint32_t *row_flag = reinterpret_cast<uint32_t *>(part_ml + (size_t)rows * splits * nrq * 2);
     oasis::AttnArgs a{q, k_pool, v_pool, page_table, blk, blk_logical, ctx_len, out,
-                      part_o, part_ml, row_count, scale * 1.4426950408889634f,
+                      part_o, part_ml, row_flag, next_attn_token(), scale * 1.4426950408889634f,
                       s->batch, s->num_q_heads, s->num_kv_heads, G, s->table_width,
                       s->num_pages, n_q, nrq, n_blk, splits, per};
     return check_hip(oasis::launch_sparse_decode_attn(a, s->head_dim, (flags & OASIS_ATTN_SHARE_GPU) != 0,

@@ -357,17 +357,18 @@ constexpr int kRowSplitWaves = OASIS_ATTN_ROWSPLIT_WAVES;
 #define OASIS_ATTN_ROWSPLIT_WGS 256     // workgroups the row-split launch aims for
 #endif
 
-// Workgroups per row and list entries per workgroup for the row-split
-// kernel; false where it does not apply (too few rows, or fewer than two
-// entries per wave, which would leave waves without a block pair).
+// Workgroups per row (two: the hand-over is a pairwise token exchange) and
+// list entries per workgroup for the row-split kernel; false where it does
+// not apply (too few rows, or fewer than two entries per wave, which would
+// leave waves without a block pair).
 inline bool rowsplit_plan(int rows, int n_blk, int *splits, int *per) {
     if (rows < OASIS_ATTN_ROWSPLIT_MIN_ROWS || rows >= kAttnRowFillRows || rows < 1) return false;
     const int s = (OASIS_ATTN_ROWSPLIT_WGS + rows - 1) / rows;
     const int p = (n_blk + s - 1) / s;
-    if (s < 2 || p < 2 * kRowSplitWaves) return false;
+    if (s != 2 || p < 2 * kRowSplitWaves) return false;
     *splits = (n_blk + p - 1) / p;
     *per = p;
-    return *splits >= 2;
+    return *splits == 2;
 }
 
 __host__ __device__ inline int row_attn_wave_floats(int n_rows_q, int head_dim) {
@@ -471,16 +472,18 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArg
     }
 }
 
-// a.splits workgroups per row (rows too few to fill the CUs one per row):
+// Two workgroups per row (rows too few to fill the CUs one per row):
 // workgroup s walks entries [s * per_split, (s + 1) * per_split) with 8 waves
 // merged in LDS, and publishes its (max, sum, O) partial with device-scope
 // stores, which write through to the point where every XCD's L2 sees them.
-// The per-row counter then takes one device-scope increment per workgroup;
-// the last to arrive reads every partial of the row with device-scope loads,
-// merges them and writes the output, and puts the counter back to zero for
-// the next call.  No L2-wide write-back or invalidate is needed: the only
-// data that crosses workgroups is written and read at device scope, and each
-// workgroup's stores have completed before its increment is issued.
+// Each then swaps the call's token into the row's flag with one device-scope
+// atomic exchange: the first gets back whatever the flag held (0 after any
+// earlier call, or anything in a fresh workspace: never this call's token),
+// the second gets the token, reads both partials with device-scope loads,
+// merges them, writes the output and sets the flag back to 0.  No L2-wide
+// write-back or invalidate is needed: the only data that crosses workgroups
+// is written and read at device scope, and each workgroup's stores have
+// completed before its exchange is issued.
 template <int D, int NE>
 __global__ __launch_bounds__(kRowSplitWaves * kWave) void attn_rowsplit_kernel(AttnArgs a) {
     constexpr int NW = kRowSplitWaves;
@@ -510,10 +513,10 @@ __global__ __launch_bounds__(kRowSplitWaves * kWave) void attn_rowsplit_kernel(A
     __builtin_amdgcn_s_waitcnt(0);          // this thread's partial stores have completed
     __syncthreads();                        // ... and every thread's
     if (threadIdx.x == 0) {
-        const uint32_t arrived = __hip_atomic_fetch_add(a.row_count + row, 1u, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
-        const int last = arrived == (uint32_t)(S - 1);
-        if (last) __hip_atomic_store(a.row_count + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t seen = __hip_atomic_exchange(a.row_flag + row, a.token, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        const int last = seen == a.token;
+        if (last) __hip_atomic_store(a.row_flag + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         is_last = last;
     }
     __syncthreads();

@@ -237,8 +237,7 @@ def sparse_decode_attn(shape: OasisShape, q, k_pool, v_pool, page_table, blk, bl
                        ctx_len, out, workspace, scale=None, stream=None, flags=0):
     """q [B][n_q][Hq][D] bf16 -> out [B][n_q][Hq][D] bf16 over the listed blocks.
     blk / blk_logical [B][Hkv][n_blk] i32 (blk may be None: entry e is index e).
-    workspace: zero-filled when allocated (its row counters return to zero
-    after every call).  flags: OASIS_ATTN_SHARE_GPU when another launch runs
+    workspace: any contents (oasis_attn_workspace_bytes() bytes).  flags: OASIS_ATTN_SHARE_GPU when another launch runs
     beside this one (oasis_sparse_decode_attn_ex); 0 calls oasis_sparse_decode_attn."""
     n_blk = (blk if blk is not None else blk_logical).shape[-1]
     scale = float(shape.head_dim) ** -0.5 if scale is None else scale

@@ -375,7 +375,7 @@ def test_two_workgroups_per_row_halves_empty_and_repeated_calls():
     """128 rows, 128 entries: each row is split between two workgroups.  Even
     rows list nothing in the first half, odd rows nothing in the second, one
     row lists nothing at all.  A second call on the same workspace gives the
-    same bits (the arrival counters are back at zero after each call)."""
+    same bits (the hand-over flags are back at zero after each call)."""
     wl = wlm.small_workload(batch=16, q_heads=32, kv_heads=8, head_dim=128, ctx=(4096, 2500),
                             n_hot=0, seed=26)
     d = wlm.make_layer(wl)
@@ -396,13 +396,42 @@ def test_two_workgroups_per_row_halves_empty_and_repeated_calls():
                                g_lists, g_lists, dev(d["ctx_len"]), out, ws)
         torch.cuda.synchronize()
         outs.append(out)
-        # the last 128 words are the row counters
+        # the last 128 words are the rows' hand-over flags
         assert int(ws[-128:].view(torch.int32).abs().sum().item()) == 0
     assert torch.equal(outs[0], outs[1])
     want = orc.attn(q[:, 0], d["K"], d["V"], d["ctx_len"], 16, lists)
     got = outs[0][:, 0].float().cpu().numpy()
     assert np.abs(got - want).max() <= ATTN_ATOL
     assert np.all(got[5, 12:16] == 0.0)          # row (5, 3): query heads 12..15, nothing listed
+
+
+def test_two_workgroups_per_row_workspace_needs_no_initialisation():
+    """The row-split hand-over needs no zeroed workspace: one workspace filled
+    with random bits, reused for shapes whose flags sit at different offsets
+    (over random bits or bytes an earlier call left), gives the oracle's
+    attention every time."""
+    wl = wlm.small_workload(batch=64, q_heads=16, kv_heads=4, head_dim=64, ctx=(2100, 3000),
+                            n_hot=0, seed=28)
+    d = wlm.make_layer(wl)
+    rng = np.random.default_rng(29)
+    lists = _random_lists(rng, wl, 64, 0.1)
+    q = torch.randn((64, 1, 16, 64), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    batches = (33, 60, 33, 64)                  # 132, 240, 132, 256 rows: the flags move
+    n_big = max(ops.attn_workspace_bytes(ops.make_shape(b, 16, 4, 64, wl.table_width, wl.num_pages),
+                                         1, 64) for b in batches) // 4
+    ws = torch.randint(-2 ** 31, 2 ** 31 - 1, (n_big,), dtype=torch.int32,
+                       generator=torch.Generator().manual_seed(30)).to(DEV).view(torch.float32)
+    for batch in batches:
+        shape = ops.make_shape(batch, 16, 4, 64, wl.table_width, wl.num_pages)
+        assert ops.attn_workspace_bytes(shape, 1, 64) // 4 <= n_big
+        out = torch.empty((batch, 1, 16, 64), dtype=torch.bfloat16, device=DEV)
+        g_lists = dev(torch.from_numpy(lists[:batch]))
+        ops.sparse_decode_attn(shape, dev(q[:batch]), dev(d["k_pool"]), dev(d["v_pool"]),
+                               dev(d["block_table"][:batch]), g_lists, g_lists,
+                               dev(d["ctx_len"][:batch]), out, ws)
+        want = orc.attn(q[:batch, 0], d["K"][:batch], d["V"][:batch], d["ctx_len"][:batch], 16,
+                        lists[:batch])
+        assert np.abs(out[:, 0].float().cpu().numpy() - want).max() <= ATTN_ATOL, batch
 
 
 def test_sparse_attention_large_logits_stay_finite():
