@@ -155,3 +155,20 @@ def test_plan_batch_driver_matches_rows(orc):
             assert fb[b, g].tolist() == r[0].tolist() and fs[b, g].tolist() == r[1].tolist()
             assert cnt[b, g] == r[2] and sb2[b, g].tolist() == r[3].tolist()
             assert lu2[b, g].tolist() == r[4].tolist()
+
+
+def test_plan_never_evicts_a_selected_block_whatever_the_step(orc):
+    # The stored last uses (5, 6) are later than this step (1): a selected
+    # block refreshed to step 1 would then look least recently used.  The
+    # victims still come only from resident blocks that are not selected.
+    slot_block = [4, 7, 9]
+    last_use = [5, 6, 5]
+    sel = [2, 4, 9]
+    scores = np.zeros(12)
+    scores[[2, 4, 9]] = [0.3, 0.2, 0.1]
+    fb, fs, cnt, sb, lu = orc.plan_row(sel, scores, slot_block, last_use, cap=1, step=1)
+    # hits 4 (slot 0) and 9 (slot 2) -> last use 1; miss 2 goes to the only
+    # unselected resident's slot (block 7, slot 1)
+    assert cnt == 1 and fb.tolist() == [2] and fs.tolist() == [1]
+    assert sb.tolist() == [4, 2, 9]
+    assert lu.tolist() == [1, 1, 1]

@@ -193,6 +193,43 @@ def test_plan_fetch_bit_exact_over_steps(case):
         assert np.all(ocnt <= cap)
 
 
+def test_plan_fetch_bit_exact_when_stored_last_use_is_later_than_the_step():
+    """Stored last uses above the step number (a restarted step count): a hit
+    refreshed to the step then looks older than every unselected resident, and
+    still must not be evicted.  GPU plan and fused select + plan against the
+    oracle, bit for bit, over several steps."""
+    B, Hkv, nb, K, cap = 4, 4, 600, 128, 9
+    rng = np.random.default_rng(77)
+    W = nb
+    ctx_len = np.full(B, nb * 16, np.int32)
+    sb, lu = _random_state(rng, B, Hkv, K, nb, None)
+    lu = np.where(sb >= 0, lu + 1000, lu).astype(np.int32)
+    shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
+    for fused in (False, True):
+        g_sb, g_lu = dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))
+        o_sb, o_lu = sb.copy(), lu.copy()
+        fb = torch.empty((B, Hkv, cap), dtype=torch.int32, device=DEV)
+        fs = torch.empty_like(fb)
+        fc = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+        g_sel = torch.empty((B, Hkv, K), dtype=torch.int32, device=DEV)
+        for step in range(4):
+            s = _random_scores(rng, B, Hkv, W, "ties")
+            sel = orc.select(s.astype(np.float64), ctx_len, 16, K)
+            ofb, ofs, ocnt, o_sb, o_lu = orc.plan(sel, s.astype(np.float64), o_sb, o_lu, cap, step)
+            if fused:
+                ops.select_plan(shape, dev(torch.from_numpy(s)), dev(torch.from_numpy(ctx_len)), K,
+                                cap, step, g_sel, g_sb, g_lu, fb, fs, fc)
+            else:
+                ops.plan_fetch(shape, dev(torch.from_numpy(sel)), dev(torch.from_numpy(s)), K, cap,
+                               step, g_sb, g_lu, fb, fs, fc)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(fc.cpu().numpy(), ocnt)
+            np.testing.assert_array_equal(fb.cpu().numpy(), ofb)
+            np.testing.assert_array_equal(fs.cpu().numpy(), ofs)
+            np.testing.assert_array_equal(g_sb.cpu().numpy(), o_sb)
+            np.testing.assert_array_equal(g_lu.cpu().numpy(), o_lu)
+
+
 @pytest.mark.parametrize("case", [
     # B, Hkv, nb (= W), K, cap, mode
     (4, 8, 2048, 128, 2, "normal"),
