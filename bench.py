@@ -821,6 +821,12 @@ def main():
                                  ms_per_step_of_that_loop=round(ms_per_step_with_events, 4)),
         "stages_alone_us": {k: percentiles_us(v) for k, v in alone.items()},
         "stages_back_to_back_us": {k: round(v * 1e3, 2) for k, v in b2b.items()},
+        # the whole step against HBM: algorithmic bytes of scoring, select + plan
+        # and attention per layer-step over the overlapped step time
+        "path_hbm": {"algorithmic_bytes": sb + select_bytes(wl) + ab,
+                     "GBps": round((sb + select_bytes(wl) + ab) / (ms_per_step * 1e-3) / 1e9, 1),
+                     "frac": round((sb + select_bytes(wl) + ab) / (ms_per_step * 1e-3) / 1e9
+                                   / HBM_PEAK_GBS, 4)},
         "attn_roofline": {"kernels": attn_kernel_name(wl),
                           "timing": "back-to-back mean",
                           "achieved": round(attn_gbs, 1), "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
