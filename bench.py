@@ -100,7 +100,7 @@ def attn_kernel_name(wl):
         return "attn_row_kernel (one workgroup per row, merged in LDS)"
     if rows >= 128 and wl.k_blocks >= 32:
         return ("attn_rowsplit_kernel (two workgroups per row, merged in LDS, then across the "
-                "pair through device-scope stores and a per-row arrival counter)")
+                "pair through device-scope stores and a per-call token exchange)")
     return "attn_partial + attn_merge (split-K)"
 
 
