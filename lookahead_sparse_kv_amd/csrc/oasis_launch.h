@@ -107,6 +107,12 @@ hipError_t launch_select_topk(const SelectArgs &a, hipStream_t stream);
 // One 256-thread workgroup per row; mode 1 = select, 2 = plan, 3 = select then plan.
 bool row_select_plan_fits(int width, int k, int mode);
 hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
+// Rows wider than this (in blocks) are selected by a 1024-thread build of the
+// same kernels (select_plan_wide.hip).
+constexpr int kWideRowMinWidth = 2048;
+namespace wide {
+hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
+}
 hipError_t launch_fetch_blocks(const FetchArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share_gpu, hipStream_t stream);
 

@@ -26,8 +26,14 @@
 #include "oasis_launch.h"
 
 namespace oasis {
-
+#ifdef OASIS_ROW_WIDE
+// Compiled a second time for wide rows (select_plan_wide.hip): the same code
+// with four times the threads per row, in a namespace of its own.
+namespace wide {
+constexpr int kRowThreads = 1024;
+#else
 constexpr int kRowThreads = 256;
+#endif
 constexpr int kRowWaves = kRowThreads / kWave;
 constexpr int kHistBins = 2048;          // widest radix digit: 11 bits
 constexpr int kPlanPadding = 16;
@@ -543,4 +549,7 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
     }
 }
 
+#ifdef OASIS_ROW_WIDE
+}  // namespace wide
+#endif
 }  // namespace oasis
