@@ -109,7 +109,10 @@ bool row_select_plan_fits(int width, int k, int mode);
 hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
 // Rows wider than this (in blocks) are selected by a 1024-thread build of the
 // same kernels (select_plan_wide.hip).
-constexpr int kWideRowMinWidth = 2048;
+#ifndef OASIS_WIDE_ROW_MIN_WIDTH
+#define OASIS_WIDE_ROW_MIN_WIDTH 2048
+#endif
+constexpr int kWideRowMinWidth = OASIS_WIDE_ROW_MIN_WIDTH;
 namespace wide {
 hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
 }
