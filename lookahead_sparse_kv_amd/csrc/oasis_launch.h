@@ -104,7 +104,8 @@ hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t str
 hipError_t launch_pool_keys(const PoolArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_score_minmax(const MinmaxArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_select_topk(const SelectArgs &a, hipStream_t stream);
-// One 256-thread workgroup per row; mode 1 = select, 2 = plan, 3 = select then plan.
+// One workgroup per row (256 threads; 1024 for rows wider than kWideRowMinWidth);
+// mode 1 = select, 2 = plan, 3 = select then plan.
 bool row_select_plan_fits(int width, int k, int mode);
 hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
 // Rows wider than this (in blocks) are selected by a 1024-thread build of the
@@ -126,7 +127,7 @@ constexpr int kBlockTokens = 16;   // tokens per KV block
 constexpr int kMaxRowsQ = 16;     // lookahead rows per KV head in one MFMA tile (scoring)
 constexpr int kMaxAttnRowsQ = 32; // query rows per KV head in attention (two MFMA tiles)
 constexpr int kMaxKBlocks = 1024; // K limit of select / plan
-constexpr int kRowSelectMaxWidth = 8192;  // widest table the 256-thread select keeps in LDS
+constexpr int kRowSelectMaxWidth = 8192;  // widest table the row select keeps in LDS
 constexpr int kFusedMaxWidth = 8192;      // fused select + plan: table width limit (LDS: 61 KiB at K = 512)
 constexpr int kFusedMaxK = 512;           // fused select + plan: K limit
 constexpr int kMaxSelectWidth = 15360;   // keys of a row staged in LDS (60 KiB)

@@ -45,7 +45,7 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 }
 
 // Scores of one row into LDS as keys, for the row's valid blocks n < nb;
-// returns nb.  A thread's loads (8 per round of 2,048 blocks) are all issued
+// returns nb.  A thread's loads (8 per round of 8 * kRowThreads blocks) are all issued
 // before the first is used, from indices clamped into the row (always in
 // bounds of the [B][Hkv][W] scores, with no branch around the loads), so the
 // first round does not wait for the context length, which is loaded beside it
@@ -71,7 +71,7 @@ __device__ __forceinline__ int load_row_keys(const float *srow, int width, const
         const int n = u * kRowThreads + (int)threadIdx.x;
         if (n < nb) keys[n] = score_key(v[u]);
     }
-    for (int n0 = kRound; n0 < nb; n0 += kRound) {      // rows of more than 2,048 blocks
+    for (int n0 = kRound; n0 < nb; n0 += kRound) {      // rows longer than one round
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int n = n0 + u * kRowThreads + (int)threadIdx.x;
