@@ -378,7 +378,7 @@ __host__ __device__ inline int row_attn_wave_floats(int n_rows_q, int head_dim) 
 // The 8 waves of a workgroup walk entries [w_begin, w_end) of row `row`,
 // each a contiguous eighth (NE > 0: an eighth of exactly NE entries takes the
 // fully unrolled walk), and leave their (O, max, sum) in the workgroup's LDS.
-template <int D, int NE, int NW = kRowAttnWaves>
+template <int D, int NE, int NW = kRowAttnWaves, int NT = 1>
 __device__ __forceinline__ void row_waves_to_lds(const AttnArgs &a, int row, int w_begin, int w_end,
                                                  float *red) {
     constexpr int MT = D / 16;
@@ -392,32 +392,39 @@ __device__ __forceinline__ void row_waves_to_lds(const AttnArgs &a, int row, int
     const int per = (w_end - w_begin + NW - 1) / NW;
     const int e_begin = w_begin + wave * per < w_end ? w_begin + wave * per : w_end;
     const int e_end = e_begin + per < w_end ? e_begin + per : w_end;
-    bf16x8 qv[1][D / 32];
-    load_query<D, 1>(a, b, g, qv);
-    WaveAcc<D, 1> acc;
-    acc.m_run[0] = -__builtin_inff();
-    acc.l_run[0] = 0.f;
+    bf16x8 qv[NT][D / 32];
+    load_query<D, NT>(a, b, g, qv);
+    WaveAcc<D, NT> acc;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc.o[0][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) {
+        acc.m_run[t] = -__builtin_inff();
+        acc.l_run[t] = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc.o[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     if (NE > 0 && e_end - e_begin == NE) {
-        attn_wave_range<D, 1, NE>(a, row, b, g, e_begin, NE, qv, acc);
+        attn_wave_range<D, NT, NE>(a, row, b, g, e_begin, NE, qv, acc);
     } else {
         for (int e0 = e_begin; e0 < e_end; e0 += kWave) {
             const int ne = e_end - e0 < kWave ? e_end - e0 : kWave;
-            attn_wave_range<D, 1>(a, row, b, g, e0, ne, qv, acc);
+            attn_wave_range<D, NT>(a, row, b, g, e0, ne, qv, acc);
         }
     }
-    float l_run = acc.l_run[0];
-    l_run = add_xor32(add_xor16(l_run));
     const int wstride = row_attn_wave_floats(nrq, D);
     float *wo = red + (size_t)wave * wstride;
     float *wm = wo + (size_t)nrq * D;
     float *wl = wm + nrq;
-    if (r16 < nrq) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            *reinterpret_cast<f32x4 *>(wo + (size_t)r16 * D + 16 * mt + 4 * j4) = acc.o[0][mt];
-        if (j4 == 0) { wm[r16] = acc.m_run[0]; wl[r16] = l_run; }
+    for (int t = 0; t < NT; ++t) {
+        float l_run = acc.l_run[t];
+        l_run = add_xor32(add_xor16(l_run));
+        const int c = 16 * t + r16;                 // query row of this column
+        if (c < nrq) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                *reinterpret_cast<f32x4 *>(wo + (size_t)c * D + 16 * mt + 4 * j4) = acc.o[t][mt];
+            if (j4 == 0) { wm[c] = acc.m_run[t]; wl[c] = l_run; }
+        }
     }
 }
 
@@ -484,9 +491,8 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArg
 // write-back or invalidate is needed: the only data that crosses workgroups
 // is written and read at device scope, and each workgroup's stores have
 // completed before its exchange is issued.
-template <int D, int NE>
-__global__ __launch_bounds__(kRowSplitWaves * kWave) void attn_rowsplit_kernel(AttnArgs a) {
-    constexpr int NW = kRowSplitWaves;
+template <int D, int NE, int NT = 1, int NW = kRowSplitWaves>
+__global__ __launch_bounds__(NW * kWave) void attn_rowsplit_kernel(AttnArgs a) {
     extern __shared__ float red[];
     __shared__ int is_last;
     const int S = a.splits;
@@ -496,7 +502,7 @@ __global__ __launch_bounds__(kRowSplitWaves * kWave) void attn_rowsplit_kernel(A
     const float NEG_INF = -__builtin_inff();
     const int w_begin = part * a.per_split < a.n_blk ? part * a.per_split : a.n_blk;
     const int w_end = w_begin + a.per_split < a.n_blk ? w_begin + a.per_split : a.n_blk;
-    row_waves_to_lds<D, NE, NW>(a, row, w_begin, w_end, red);
+    row_waves_to_lds<D, NE, NW, NT>(a, row, w_begin, w_end, red);
     __syncthreads();
     for (int idx = threadIdx.x; idx < nrq * D; idx += NW * kWave) {
         const int c = idx / D;
@@ -598,6 +604,27 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share
             if (share == 8) hipLaunchKernelGGL((attn_rowsplit_kernel<64, 8>), grid2, block2, lds2, stream, r);
             else if (share == 16) hipLaunchKernelGGL((attn_rowsplit_kernel<64, 16>), grid2, block2, lds2, stream, r);
             else hipLaunchKernelGGL((attn_rowsplit_kernel<64, 0>), grid2, block2, lds2, stream, r);
+        }
+        return hipGetLastError();
+    }
+    // 17..32 query rows (the normal and the draft queries together): the same
+    // two-workgroup split with two 16-column tiles, 4 waves per workgroup (one
+    // per SIMD: the two tiles' accumulators need the registers)
+    constexpr int kSplit2Waves = 4;
+    const size_t lds_t2 = (size_t)kSplit2Waves * row_attn_wave_floats(a.n_rows_q, head_dim) * 4;
+    if (a.n_rows_q > 16 && a.n_rows_q <= 32 && lds_t2 <= 65536 &&
+        rowsplit_plan(rows, a.n_blk, &wg_splits, &wg_per) && wg_splits <= a.splits) {
+        AttnArgs r = a;
+        r.splits = wg_splits;
+        r.per_split = wg_per;
+        const dim3 grid2((unsigned)(rows * wg_splits)), block2(kSplit2Waves * kWave);
+        const bool share16 = wg_per == 16 * kSplit2Waves;     // 16 entries per wave: unrolled
+        if (head_dim == 128) {
+            if (share16) hipLaunchKernelGGL((attn_rowsplit_kernel<128, 16, 2, kSplit2Waves>), grid2, block2, lds_t2, stream, r);
+            else hipLaunchKernelGGL((attn_rowsplit_kernel<128, 0, 2, kSplit2Waves>), grid2, block2, lds_t2, stream, r);
+        } else {
+            if (share16) hipLaunchKernelGGL((attn_rowsplit_kernel<64, 16, 2, kSplit2Waves>), grid2, block2, lds_t2, stream, r);
+            else hipLaunchKernelGGL((attn_rowsplit_kernel<64, 0, 2, kSplit2Waves>), grid2, block2, lds_t2, stream, r);
         }
         return hipGetLastError();
     }

@@ -305,6 +305,15 @@ ATTN_CASES = {
                                   ctx=(2048, 3001)), 1, 128, 0.0),
     "d128_g4_128_rows_all_empty": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128,
                                         ctx=(600, 2048)), 1, 128, 1.0),
+    # 128 to 255 rows with 17..32 query rows per KV head: two 4-wave workgroups
+    # per row, two column tiles (32 query rows at D 128 exceed the LDS bound:
+    # split-K)
+    "d128_g4_nq5_128_rows_normal_and_4_drafts": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128,
+                                                      ctx=(4096, 2100, 3000, 2048)), 5, 128, 0.1),
+    "d64_g8_nq3_160_rows_ragged": (dict(batch=40, q_heads=32, kv_heads=4, head_dim=64,
+                                        ctx=(700, 1601, 5000, 999)), 3, 70, 0.2),
+    "d128_g16_nq2_128_rows_split_k": (dict(batch=16, q_heads=128, kv_heads=8, head_dim=128,
+                                           ctx=(2048, 1000)), 2, 64, 0.0),
     # 256 rows or more: one workgroup per row, merged in LDS
     "d128_g4_nq4_256_rows_long_lists": (dict(batch=32, q_heads=64, kv_heads=8, head_dim=128,
                                              ctx=(4096, 3000)), 4, 200, 0.05),
