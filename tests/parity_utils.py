@@ -134,3 +134,25 @@ def ck_logical(ck):
     B, Hkv, T, S, _, _ = ck.shape
     D = S * 4
     return ck.permute(0, 1, 2, 4, 3, 5).reshape(B, Hkv, T * 16, 2, D)
+
+
+def build_c_step(tmp_path):
+    """Compile tests/c/abi_step.c against include/oasis.h and link liboasis.so."""
+    import os
+    import shutil
+    import subprocess
+
+    import pytest
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.join(ROOT, "lookahead_sparse_kv_amd")
+    exe = os.path.join(str(tmp_path), "abi_step")
+    cmd = ["gcc", "-std=c11", "-O1", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           os.path.join(ROOT, "tests", "c", "abi_step.c"), "-o", exe, "-L", lib_dir, "-loasis",
+           "-L", "/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath," + lib_dir, "-Wl,-rpath,/opt/rocm/lib",
+           "-lm"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return exe

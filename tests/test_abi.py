@@ -195,3 +195,10 @@ def test_layer_step_argument_checks():
     sync.plan_stream = 16
     assert L.oasis_layer_step(ctypes.byref(layer), P, P, P, 0, ctypes.byref(sync)) == \
         ops.OASIS_ERR_INVALID
+
+
+def test_c_program_compiles_and_links_against_the_abi(tmp_path):
+    # the header is valid C and every call the program makes resolves in liboasis.so
+    ops.lib()                                   # the library is built
+    from parity_utils import build_c_step
+    assert os.path.exists(build_c_step(tmp_path))

@@ -480,6 +480,17 @@ def test_two_workgroups_per_row_workspace_needs_no_initialisation():
         assert np.abs(out[:, 0].float().cpu().numpy() - want).max() <= ATTN_ATOL, batch
 
 
+def test_c_program_runs_a_decode_step_through_the_abi(tmp_path):
+    """tests/c/abi_step.c: one decode step (score, select, plan, attention)
+    from plain C through include/oasis.h, checked by the program itself."""
+    import subprocess
+    from parity_utils import build_c_step
+    exe = build_c_step(tmp_path)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi_step ok" in r.stdout
+
+
 def test_sparse_attention_large_logits_stay_finite():
     wl = wlm.small_workload(batch=1, q_heads=8, kv_heads=2, head_dim=128, ctx=(2048,), n_hot=0, seed=25)
     d = wlm.make_layer(wl)
