@@ -306,7 +306,7 @@ class GraphedDecode:
     MAX_LAYER_STEPS = 4
 
     def __init__(self, layers, q, q_looks, rounds, step0=1, side=None, plan_stream=None,
-                 append=False):
+                 append=False, share_gpu=True):
         if len(layers) * rounds > self.MAX_LAYER_STEPS or rounds > 2:
             raise NotImplementedError(
                 f"GraphedDecode: {len(layers)} layers x {rounds} rounds; captures beyond "
@@ -314,6 +314,7 @@ class GraphedDecode:
         self.layers = list(layers)
         self.q, self.q_looks, self.rounds, self.step0 = q, q_looks, rounds, step0
         self.append = append
+        self.share_gpu = share_gpu              # attention's launch hint (see PipelinedDecode)
         dev = self.layers[0].scores.device
         self.side = side if side is not None else torch.cuda.Stream(device=dev)   # default priority
         self.plan_stream = plan_stream
@@ -355,7 +356,7 @@ class GraphedDecode:
                 ev_scored[l][b].record(self.side)
                 if ps is not main and last_plan[l] is not None:
                     main.wait_event(last_plan[l])           # the working set of this step
-                L.attend(self.q, stream=main, share_gpu=True)
+                L.attend(self.q, stream=main, share_gpu=self.share_gpu)
                 if ps is not main:
                     ev_attended[l].record(main)             # the plan rewrites what it read
                     ps.wait_event(ev_attended[l])

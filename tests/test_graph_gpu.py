@@ -18,11 +18,15 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 CASES = {
-    # name: (workload kwargs, scorer, plan on a stream of its own)
-    "rows4_exact": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 3000)), "exact", False),
-    "rows4_minmax": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 3000)), "minmax", True),
-    "rows128_exact": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128, ctx=(2048, 3000)), "exact", False),
-    "rows128_minmax": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128, ctx=(2048, 3000)), "minmax", True),
+    # name: (workload kwargs, scorer, plan on a stream of its own, attention's share-GPU hint)
+    "rows4_exact": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 3000)), "exact", False, True),
+    "rows4_minmax": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 3000)), "minmax", True, True),
+    "rows128_exact": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128, ctx=(2048, 3000)), "exact", False, True),
+    "rows128_minmax": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128, ctx=(2048, 3000)), "minmax", True, True),
+    # two attention workgroups per row: the hand-over token is fixed in the graph,
+    # and each replay must leave the rows' flags ready for the next
+    "rows128_minmax_two_workgroups": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128,
+                                           ctx=(2048, 3000)), "minmax", True, False),
 }
 
 
@@ -40,7 +44,7 @@ def _state(L):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_graph_replays_match_eager_steps(name):
-    kw, scorer, own_plan_stream = CASES[name]
+    kw, scorer, own_plan_stream, share = CASES[name]
     wl = wlm.small_workload(budget=512, ratio=0.125, n_hot=6, seed=61, **kw)   # K = 32, cap 4
     n_layers, rounds, replays = 2, 2, 3
     datas = [wlm.make_layer(wl, seed=61 + 13 * l) for l in range(n_layers)]
@@ -54,7 +58,8 @@ def test_graph_replays_match_eager_steps(name):
     eager = [_layer(wl, d, scorer) for d in datas]
     side = torch.cuda.Stream()
     ps = torch.cuda.Stream() if own_plan_stream else None
-    G = GraphedDecode(graphed, q, looks, rounds, step0=1, side=side, plan_stream=ps, append=append)
+    G = GraphedDecode(graphed, q, looks, rounds, step0=1, side=side, plan_stream=ps, append=append,
+                      share_gpu=share)
     G.prime(look0, step=0)
     for L in eager:
         L.score(look0, refresh=append)
@@ -65,7 +70,7 @@ def test_graph_replays_match_eager_steps(name):
         # the same steps, eagerly, in the plain order on one stream
         for k in range(rounds):
             for l, L in enumerate(eager):
-                L.attend(q, share_gpu=True)        # the launch shape the graph captured
+                L.attend(q, share_gpu=share)       # the launch shape the graph captured
                 L.score(looks[l][k], refresh=append)
                 L.select_plan(1 + n * rounds + k)
         torch.cuda.synchronize()

@@ -315,6 +315,8 @@ ATTN_CASES = {
     "d128_g16_nq2_128_rows_split_k": (dict(batch=16, q_heads=128, kv_heads=8, head_dim=128,
                                            ctx=(2048, 1000)), 2, 64, 0.0),
     # 256 rows or more: one workgroup per row, merged in LDS
+    "d64_g4_256_rows": (dict(batch=64, q_heads=16, kv_heads=4, head_dim=64, ctx=(2048, 1500, 333)),
+                        1, 96, 0.1),
     "d128_g4_nq4_256_rows_long_lists": (dict(batch=32, q_heads=64, kv_heads=8, head_dim=128,
                                              ctx=(4096, 3000)), 4, 200, 0.05),
 }
