@@ -61,10 +61,6 @@ def parse():
     p.add_argument("--attn-share", choices=("auto", "on", "off"), default="auto",
                    help="attention in the step launched with the share-GPU hint (one CU per "
                         "row; auto: with exact scoring)")
-    p.add_argument("--graph", choices=("off", "on"), default="off",
-                   help="time the steps as replays of a HIP graph (switched off: capturing "
-                        "the bench's schedule of 4 replicas x 4 rounds crashed the process "
-                        "at the end of the capture)")
     p.add_argument("--detail", action="store_true",
                    help="also time the steps without overlap and each stage alone")
     return p.parse_args()
@@ -536,7 +532,7 @@ def main():
         return
     from lookahead_sparse_kv_amd import ops
     from lookahead_sparse_kv_amd import workload as wlm
-    from lookahead_sparse_kv_amd.pipeline import DecodeLayer, GraphedDecode, PipelinedDecode
+    from lookahead_sparse_kv_amd.pipeline import DecodeLayer, PipelinedDecode
 
     ops.lib()          # fail loudly before any work if the HIP library is missing
     wl = wlm.WORKLOADS[args.workload]
@@ -602,43 +598,20 @@ def main():
     # compressed scorer: each scoring launch also re-pools the block a decode
     # step appends to (the pool itself is not written here)
     append = wl.scorer == "minmax"
-    use_graph = args.graph == "on"
-    if use_graph:
-        # GraphedDecode refuses captures of this size (see its class notes)
-        raise SystemExit("bench.py --graph on: the capture of 4 replicas x 4 rounds is "
-                         "switched off (it crashed in capture_end); run without --graph")
-    graph = None
-    if use_graph:
-        # one replay: a round of steps per lookahead draw, every replica in
-        # turn in each round, in the pipelined schedule; the plan's step number
-        # advances on the device from replay to replay
-        rounds = N_LOOK_DRAWS
-        graph = GraphedDecode(layers, q, [[looks[(k + 1) % N_LOOK_DRAWS] for k in range(rounds)]
-                                          for _ in layers], rounds, step0=1, side=side,
-                              plan_stream=plan_stream, append=append)
-        graph.prime(looks[0], 0)
-        graph.capture()
-        per_replay = rounds * n_rep
-        for _ in range(max(1, -(-args.warmup // per_replay))):
-            graph.replay()
-    else:
-        for P in pipes:
-            P.prime(looks[0], 0, append=append)
-        for i in range(args.warmup):
-            pipes[i % n_rep].step(q, looks[(i // n_rep + 1) % N_LOOK_DRAWS], 1 + i // n_rep,
-                                  copy_out=False, append=append)
-        for P in pipes:
-            P.drain()
+    for P in pipes:
+        P.prime(looks[0], 0, append=append)
+    for i in range(args.warmup):
+        pipes[i % n_rep].step(q, looks[(i // n_rep + 1) % N_LOOK_DRAWS], 1 + i // n_rep,
+                              copy_out=False, append=append)
+    for P in pipes:
+        P.drain()
     torch.cuda.synchronize()
-
-    # eager steps after graph replays continue the replays' step numbers
-    step_base = 0
 
     def run_steps(first, events=None):
         for i in range(args.steps):
             s = first + i
-            pipes[s % n_rep].step(q, looks[(s // n_rep + 1) % N_LOOK_DRAWS],
-                                  step_base + 1 + s // n_rep, copy_out=False, append=append,
+            pipes[s % n_rep].step(q, looks[(s // n_rep + 1) % N_LOOK_DRAWS], 1 + s // n_rep,
+                                  copy_out=False, append=append,
                                   score_events=None if events is None else events[i])
         for P in pipes:
             P.drain()
@@ -648,21 +621,12 @@ def main():
     timed_steps = args.steps
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if graph is not None:
-        n_replays = max(1, -(-args.steps // per_replay))
-        timed_steps = n_replays * per_replay
-        ev0.record()
-        for _ in range(n_replays):
-            graph.replay()
-    else:
-        ev0.record()
-        run_steps(args.warmup)
+    ev0.record()
+    run_steps(args.warmup)
     ev1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = ev0.elapsed_time(ev1) / timed_steps
-    if graph is not None:
-        step_base = int(graph.counter.item()) + graph.step0
     # The same K steps again with the scoring launches bracketed by events on
     # the scoring stream: the roofline of the scoring kernel as it runs in the
     # pipeline (sharing the GPU with attention and select/plan).
@@ -808,9 +772,6 @@ def main():
                    "enqueue": "oasis_layer_step" if args.native == "on" else "python",
                    "attn_in_step": ("one workgroup per row (share-GPU hint)" if share_gpu else
                                     "default launch shape"),
-                   "graph": ({"rounds_per_replay": graph.rounds, "replicas": n_rep,
-                              "replays_timed": timed_steps // per_replay}
-                             if graph is not None else None),
                    "replicas": n_rep,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": SCORE_KERNELS[wl.scorer][0],
