@@ -234,9 +234,9 @@ int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_
  * room for the partial results of a row's shares (per row and share: max,
  * sum and the D-wide output of each query row), then one 32-bit hand-over
  * flag per row (B * Hkv rows), padded to 16 bytes.  The workspace needs no
- * initialisation: the two workgroups of a row exchange a token that differs
- * from call to call (never 0) in the row's flag, and the one that receives
- * the token merges and sets the flag to 0.  One workspace serves one call at
+ * initialisation: the two workgroups of a row exchange a per-call 32-bit
+ * token (never 0, never a small integer) in the row's flag, and the one that
+ * receives the token merges and sets the flag to 0.  One workspace serves one call at
  * a time.  Returns 0 for an invalid shape.
  */
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk);

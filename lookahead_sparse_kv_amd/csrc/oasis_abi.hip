@@ -245,14 +245,16 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
            (((size_t)rows * sizeof(uint32_t) + 15) & ~(size_t)15);
 }
 
-// A nonzero token per attention call: the two workgroups of a row exchange it
-// in the row's flag to find which of them merges (the flag need not start at
-// any particular value, and returns to 0 after the call).
+// A token per attention call: the two workgroups of a row exchange it in the
+// row's flag to find which of them merges (the flag need not start at any
+// particular value, and returns to 0 after the call).  The call count is
+// spread over the 32 bits by an odd multiplier, and the top and bottom bits
+// are set, so a token is never 0 and never a small integer such as a block
+// index left in a reused allocation.
 static uint32_t next_attn_token() {
     static std::atomic<uint32_t> calls{0};
-    uint32_t t = calls.fetch_add(1, std::memory_order_relaxed) + 1;
-    if (t == 0) t = calls.fetch_add(1, std::memory_order_relaxed) + 1;
-    return t;
+    const uint32_t t = calls.fetch_add(1, std::memory_order_relaxed) + 1;
+    return (t * 0x9E3779B1u) | 0x80000001u;
 }
 
 int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_q,

@@ -455,9 +455,9 @@ def test_two_workgroups_per_row_halves_empty_and_repeated_calls():
 
 def test_two_workgroups_per_row_workspace_needs_no_initialisation():
     """The row-split hand-over needs no zeroed workspace: one workspace filled
-    with random bits, reused for shapes whose flags sit at different offsets
-    (over random bits or bytes an earlier call left), gives the oracle's
-    attention every time."""
+    with random bits, and one filled with small integers (as a reused
+    allocation of block indices would be), each reused for shapes whose flags
+    sit at different offsets, give the oracle's attention every time."""
     wl = wlm.small_workload(batch=64, q_heads=16, kv_heads=4, head_dim=64, ctx=(2100, 3000),
                             n_hot=0, seed=28)
     d = wlm.make_layer(wl)
@@ -467,11 +467,21 @@ def test_two_workgroups_per_row_workspace_needs_no_initialisation():
     batches = (33, 60, 33, 64)                  # 132, 240, 132, 256 rows: the flags move
     n_big = max(ops.attn_workspace_bytes(ops.make_shape(b, 16, 4, 64, wl.table_width, wl.num_pages),
                                          1, 64) for b in batches) // 4
-    ws = torch.randint(-2 ** 31, 2 ** 31 - 1, (n_big,), dtype=torch.int32,
-                       generator=torch.Generator().manual_seed(30)).to(DEV).view(torch.float32)
+    fills = {
+        "random bits": torch.randint(-2 ** 31, 2 ** 31 - 1, (n_big,), dtype=torch.int32,
+                                     generator=torch.Generator().manual_seed(30)),
+        # small integers, as block indices left in a reused allocation would be
+        "small integers": torch.arange(n_big, dtype=torch.int32) % 4096,
+    }
+    for fill, ws_host in fills.items():
+        _attend_shapes_on_one_workspace(wl, d, lists, q, batches, ws_host.to(DEV).view(torch.float32),
+                                        fill)
+
+
+def _attend_shapes_on_one_workspace(wl, d, lists, q, batches, ws, fill):
     for batch in batches:
         shape = ops.make_shape(batch, 16, 4, 64, wl.table_width, wl.num_pages)
-        assert ops.attn_workspace_bytes(shape, 1, 64) // 4 <= n_big
+        assert ops.attn_workspace_bytes(shape, 1, 64) // 4 <= ws.numel()
         out = torch.empty((batch, 1, 16, 64), dtype=torch.bfloat16, device=DEV)
         g_lists = dev(torch.from_numpy(lists[:batch]))
         ops.sparse_decode_attn(shape, dev(q[:batch]), dev(d["k_pool"]), dev(d["v_pool"]),
@@ -479,7 +489,7 @@ def test_two_workgroups_per_row_workspace_needs_no_initialisation():
                                dev(d["ctx_len"][:batch]), out, ws)
         want = orc.attn(q[:batch, 0], d["K"][:batch], d["V"][:batch], d["ctx_len"][:batch], 16,
                         lists[:batch])
-        assert np.abs(out[:, 0].float().cpu().numpy() - want).max() <= ATTN_ATOL, batch
+        assert np.abs(out[:, 0].float().cpu().numpy() - want).max() <= ATTN_ATOL, (fill, batch)
 
 
 def test_c_program_runs_a_decode_step_through_the_abi(tmp_path):
