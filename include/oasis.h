@@ -266,11 +266,15 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
  * accumulation.  Requires D in {64, 128}, bs = 16, 1 <= n_q, n_q * G <= 32,
  * n_blk >= 1, scale > 0, and workspace_bytes >= oasis_attn_workspace_bytes().
  *
- * Launch shape (results agree to fp32 rounding whichever is taken): from 256
- * rows (B * Hkv), one workgroup per row merges its waves in LDS; from 128
- * rows, two workgroups per row, the last to finish merging both through the
- * workspace; below that, split-K waves and a second merge launch.  Rows with
- * more than 16 query rows (n_q * G) take split-K.
+ * Launch shape (results agree to fp32 rounding whichever is taken), by rows
+ * (B * Hkv) and query rows per KV head (n_q * G):
+ *   - 256 rows or more, at most 16 query rows: one workgroup per row merges
+ *     its waves in LDS;
+ *   - 128 to 255 rows, and at least 32 listed entries per row: two
+ *     workgroups per row (8 waves each up to 16 query rows; 4 waves with two
+ *     column tiles for 17..32 query rows while their partials fit in 64 KiB
+ *     of LDS), the second to finish merging both through the workspace;
+ *   - otherwise split-K waves and a second merge launch.
  */
 int oasis_sparse_decode_attn(const oasis_shape *s, const uint16_t *q, int32_t n_q,
                              const uint16_t *k_pool, const uint16_t *v_pool,
