@@ -270,7 +270,7 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
  * (B * Hkv) and query rows per KV head (n_q * G):
  *   - 256 rows or more, at most 16 query rows: one workgroup per row merges
  *     its waves in LDS;
- *   - 128 to 255 rows, and at least 32 listed entries per row: two
+ *   - 128 to 255 rows, and at least 31 listed entries per row: two
  *     workgroups per row (8 waves each up to 16 query rows; 4 waves with two
  *     column tiles for 17..32 query rows while their partials fit in 64 KiB
  *     of LDS), the second to finish merging both through the workspace;
