@@ -100,8 +100,10 @@ def test_plan_brute_force_tiny_rows(orc):
         slot_block = res + [-1] * (K - n_res)
         rng.shuffle(slot_block)
         last_use = [int(rng.integers(0, 3)) if b >= 0 else NEG for b in slot_block]
-        F, dest, sb_w, lu_w = _brute_force_plan(sel, scores, slot_block, last_use, cap, 5)
-        fb, fs, cnt, sb, lu = orc.plan_row(sel, scores, slot_block, last_use, cap, 5)
+        # steps 0..5: some below the stored last uses (a restarted step count)
+        step = int(rng.integers(0, 6))
+        F, dest, sb_w, lu_w = _brute_force_plan(sel, scores, slot_block, last_use, cap, step)
+        fb, fs, cnt, sb, lu = orc.plan_row(sel, scores, slot_block, last_use, cap, step)
         assert cnt == len(F)
         assert fb[:cnt].tolist() == F and fs[:cnt].tolist() == dest
         assert sb.tolist() == sb_w and lu.tolist() == lu_w
