@@ -569,11 +569,11 @@ def _check_step_rows(wl, d, layer, q_look, q, sb0, lu0, cap, step, rows, name):
     return n_exempt
 
 
-def _gpu_layer(wl, d, cap, sb, lu, scorer="exact"):
+def _gpu_layer(wl, d, cap, sb, lu, scorer="exact", n_q=1):
     return DecodeLayer(k_pool=dev(d["k_pool"]), v_pool=dev(d["v_pool"]),
                        block_table=dev(d["block_table"]), ctx_len=dev(d["ctx_len"]),
                        num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks, cap=cap, n_look=wl.n_look,
-                       slot_block=torch.from_numpy(sb), last_use=torch.from_numpy(lu),
+                       n_q=n_q, slot_block=torch.from_numpy(sb), last_use=torch.from_numpy(lu),
                        scorer=scorer)
 
 
@@ -646,26 +646,30 @@ def test_pipelined_decode_matches_sequential_steps(plan_stream):
     assert torch.equal(pipe_layer.sel, seq.sel)
 
 
-@pytest.mark.parametrize("scorer,plan_stream,batch,share", [
-    ("exact", False, 4, True), ("exact", False, 16, True), ("minmax", True, 16, True),
-    ("minmax", True, 16, False), ("minmax", False, 4, True)])
-def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch, share):
+@pytest.mark.parametrize("scorer,plan_stream,batch,share,drafts", [
+    ("exact", False, 4, True, 0), ("exact", False, 16, True, 0), ("minmax", True, 16, True, 0),
+    ("minmax", True, 16, False, 0), ("minmax", False, 4, True, 0),
+    ("exact", True, 16, False, 4)])          # 4 drafts scored, normal + drafts attended
+def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch, share, drafts):
     """oasis_layer_step enqueues the pipelined step (score, attention, select +
     plan, with the same event waits and records) from native code: per-step
     outputs and the final state are bit-identical to the Python pipeline's,
     over several layers taking turns on shared streams.  32 and 128 rows."""
     wl = wlm.small_workload(batch=batch, q_heads=32, kv_heads=8, head_dim=128,
-                            ctx=(4096, 3000, 2500, 4000), budget=512, n_hot=12, ratio=0.125, seed=44)
+                            ctx=(4096, 3000, 2500, 4000), budget=512, n_hot=12, ratio=0.125, seed=44,
+                            n_look=max(1, drafts))
     n_layers, T = 2, 5
+    n_q = 1 + drafts
     datas = [wlm.make_layer(wl, seed=44 + 5 * l) for l in range(n_layers)]
-    q = dev(datas[0]["q"].unsqueeze(1))
+    # attention's query rows: the normal query, then the drafts
+    q = dev(torch.cat([datas[0]["q"].unsqueeze(1), datas[0]["q_look"]], dim=1)[:, :n_q])
     looks = [[dev(wlm.draw_lookahead(wl, d["q32"], 700 + 3 * t + l).to(torch.bfloat16))
               for t in range(T + 1)] for l, d in enumerate(datas)]
     append = scorer == "minmax"
     runs = {}
     for native in (False, True):
         sb, lu = (x.numpy() for x in wlm.empty_state(wl))
-        layers = [_gpu_layer(wl, d, wl.cap(), sb, lu, scorer=scorer) for d in datas]
+        layers = [_gpu_layer(wl, d, wl.cap(), sb, lu, scorer=scorer, n_q=n_q) for d in datas]
         side = torch.cuda.Stream()
         ps = torch.cuda.Stream() if plan_stream else None
         pipes = [PipelinedDecode(L, side=side, plan_stream=ps, native=native, share_gpu=share)
