@@ -30,7 +30,10 @@ namespace oasis {
 // Compiled a second time for wide rows (select_plan_wide.hip): the same code
 // with four times the threads per row, in a namespace of its own.
 namespace wide {
-constexpr int kRowThreads = 1024;
+#ifndef OASIS_ROW_WIDE_THREADS
+#define OASIS_ROW_WIDE_THREADS 1024
+#endif
+constexpr int kRowThreads = OASIS_ROW_WIDE_THREADS;
 #else
 constexpr int kRowThreads = 256;
 #endif
