@@ -105,7 +105,8 @@ typedef struct oasis_shape {
  *   scores[b][g][n] = -inf for n >= ceil(ctx_len[b] / bs) (up to table_width).
  *
  * bf16 inputs, fp32 accumulation.  Requires D in {64, 128}, bs = 16,
- * 1 <= n_look and n_look * G <= 16.  scale is normally 1/sqrt(D) and must be > 0.
+ * 1 <= n_look and n_look * G <= 16, q_look and k_pool 16-byte aligned.  scale
+ * is normally 1/sqrt(D) and must be > 0.
  */
 int oasis_score_blocks(const oasis_shape *s, const uint16_t *q_look, int32_t n_look,
                        const uint16_t *k_pool, const int32_t *block_table,
@@ -264,7 +265,8 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
  * together).
  * A row with no valid token outputs zeros.  bf16 in and out, fp32 softmax and
  * accumulation.  Requires D in {64, 128}, bs = 16, 1 <= n_q, n_q * G <= 32,
- * n_blk >= 1, scale > 0, and workspace_bytes >= oasis_attn_workspace_bytes().
+ * n_blk >= 1, scale > 0, q, k_pool, v_pool and workspace 16-byte aligned, and
+ * workspace_bytes >= oasis_attn_workspace_bytes().
  *
  * Launch shape (results agree to fp32 rounding whichever is taken), by rows
  * (B * Hkv) and query rows per KV head (n_q * G):
@@ -329,7 +331,8 @@ int oasis_hostpool_destroy(void *host_ptr);
  * pages.  Entries with a block outside [0, host_blocks), a slot outside
  * [0, K) or a page outside [0, num_pages) are skipped.  The fetch lists are
  * those oasis_plan_fetch writes; the call reads them on the device, so no host
- * synchronisation is needed.  Requires 0 <= cap <= K.
+ * synchronisation is needed.  Requires 0 <= cap <= K and the four pools
+ * 16-byte aligned.
  */
 int oasis_fetch_blocks(const oasis_shape *s, const uint16_t *host_k, const uint16_t *host_v,
                        int32_t host_blocks, const int32_t *fetch_block, const int32_t *fetch_slot,

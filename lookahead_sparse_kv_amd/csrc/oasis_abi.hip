@@ -58,6 +58,9 @@ int check_shape(const oasis_shape *s, const char *fn) {
     return OASIS_OK;
 }
 
+// The kernels read these buffers 16 bytes per lane.
+bool misaligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
+
 }  // namespace
 
 extern "C" {
@@ -92,6 +95,8 @@ int oasis_score_blocks(const oasis_shape *s, const uint16_t *q_look, int32_t n_l
     if (s->batch == 0 || s->table_width == 0) return ok();
     if (!q_look || !k_pool || !block_table || !ctx_len || !scores)
         return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    if (misaligned16(q_look) || misaligned16(k_pool))
+        return fail(OASIS_ERR_INVALID, "%s: q_look and k_pool must be 16-byte aligned", fn);
     oasis::ScoreArgs a{q_look, k_pool, block_table, ctx_len, scores, scale,
                        s->batch, s->num_q_heads, s->num_kv_heads, G, s->table_width,
                        s->num_pages, n_look, n_look * G};
@@ -107,7 +112,7 @@ int oasis_pool_keys(const oasis_shape *s, const uint16_t *k_pool, const int32_t 
     if (s->batch == 0 || s->table_width == 0) return ok();
     if (!k_pool || !block_table || !ctx_len || !ck)
         return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
-    if (reinterpret_cast<uintptr_t>(ck) % 16 || reinterpret_cast<uintptr_t>(k_pool) % 16)
+    if (misaligned16(ck) || misaligned16(k_pool))
         return fail(OASIS_ERR_INVALID, "%s: k_pool and ck must be 16-byte aligned", fn);
     oasis::PoolArgs a{k_pool, block_table, ctx_len, ck, s->batch, s->num_kv_heads, s->table_width,
                       s->num_pages, last_only};
@@ -132,8 +137,7 @@ int oasis_score_blocks_minmax(const oasis_shape *s, const uint16_t *q_look, int3
     if (!k_pool != !block_table)
         return fail(OASIS_ERR_INVALID, "%s: k_pool and block_table must both be set or both NULL",
                     fn);
-    if (reinterpret_cast<uintptr_t>(ck) % 16 || reinterpret_cast<uintptr_t>(k_pool) % 16 ||
-        reinterpret_cast<uintptr_t>(q_look) % 16)
+    if (misaligned16(ck) || misaligned16(k_pool) || misaligned16(q_look))
         return fail(OASIS_ERR_INVALID, "%s: q_look, ck and k_pool must be 16-byte aligned", fn);
     oasis::MinmaxArgs a{q_look, ck, k_pool, block_table, ctx_len, scores, scale, s->batch,
                         s->num_q_heads, s->num_kv_heads, G, s->table_width, s->num_pages, n_look,
@@ -234,7 +238,9 @@ int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_
 
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk) {
     if (!s || s->batch < 0 || s->num_kv_heads <= 0 || s->num_q_heads <= 0 || s->head_dim <= 0 ||
-        n_q < 1 || n_blk < 1 || s->num_q_heads % s->num_kv_heads)
+        n_q < 1 || n_blk < 1 || s->num_q_heads % s->num_kv_heads ||
+        (long long)s->batch * s->num_kv_heads > 65535 ||
+        (long long)n_q * (s->num_q_heads / s->num_kv_heads) > oasis::kMaxAttnRowsQ)
         return 0;
     const int rows = s->batch * s->num_kv_heads;
     const int nrq = n_q * (s->num_q_heads / s->num_kv_heads);
@@ -290,10 +296,12 @@ int oasis_sparse_decode_attn_ex(const oasis_shape *s, const uint16_t *q, int32_t
         return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
     if (!blk && !blk_logical)
         return fail(OASIS_ERR_INVALID, "%s: blk and blk_logical are both NULL", fn);
+    if (misaligned16(q) || misaligned16(k_pool) || misaligned16(v_pool))
+        return fail(OASIS_ERR_INVALID, "%s: q, k_pool and v_pool must be 16-byte aligned", fn);
     const size_t need = oasis_attn_workspace_bytes(s, n_q, n_blk);
     if (!workspace || workspace_bytes < need)
         return fail(OASIS_ERR_NOMEM, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes, need);
-    if (reinterpret_cast<uintptr_t>(workspace) % 16)
+    if (misaligned16(workspace))
         return fail(OASIS_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
     const int rows = s->batch * s->num_kv_heads;
     int splits = 1, per = 1;
@@ -393,6 +401,9 @@ int oasis_fetch_blocks(const oasis_shape *s, const uint16_t *host_k, const uint1
     if (!host_k || !host_v || !fetch_block || !fetch_slot || !fetch_count || !ws_page_table ||
         !ws_k_pool || !ws_v_pool)
         return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    if (misaligned16(host_k) || misaligned16(host_v) || misaligned16(ws_k_pool) ||
+        misaligned16(ws_v_pool))
+        return fail(OASIS_ERR_INVALID, "%s: host and working-set pools must be 16-byte aligned", fn);
     oasis::FetchArgs a{host_k, host_v, fetch_block, fetch_slot, fetch_count, ws_page_table,
                        ws_k_pool, ws_v_pool, s->batch, s->num_kv_heads, host_blocks,
                        s->table_width, cap, s->num_pages};

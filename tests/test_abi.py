@@ -77,6 +77,8 @@ def test_score_rejects_bad_arguments():
     assert _score(_shape(), q=None) == ops.OASIS_ERR_INVALID
     assert "NULL" in ops.last_error()
     assert ops.lib().oasis_score_blocks(None, P, 1, P, P, P, 0.1, P, None) == ops.OASIS_ERR_INVALID
+    assert _score(_shape(), q=ctypes.c_void_p(18)) == ops.OASIS_ERR_INVALID   # 16 B per lane
+    assert "aligned" in ops.last_error()
 
 
 def test_empty_batch_is_a_no_op():
@@ -122,10 +124,34 @@ def test_attn_workspace_and_argument_checks():
     assert att(n_blk=0) == ops.OASIS_ERR_INVALID
     assert att(blk=None) == ops.OASIS_ERR_INVALID       # blk and blk_logical both NULL
     assert att(wsp=ctypes.c_void_p(24)) == ops.OASIS_ERR_INVALID  # misaligned workspace
+    for i in range(3):   # q, k_pool, v_pool, each read 16 bytes per lane
+        ptrs = [P, P, P]
+        ptrs[i] = ctypes.c_void_p(24)
+        assert L.oasis_sparse_decode_attn(ctypes.byref(s), ptrs[0], 1, ptrs[1], ptrs[2], P, P, 128,
+                                          P, P, 0.088, P, P, ws, None) == ops.OASIS_ERR_INVALID
+    # the workspace size shares the calls' limits: 0 where every call would refuse the shape
+    assert ops.attn_workspace_bytes(s, 9, 128) == 0
+    assert ops.attn_workspace_bytes(_shape(batch=70000, num_q_heads=8, num_kv_heads=1), 1, 128) == 0
     att_ex = lambda flags: L.oasis_sparse_decode_attn_ex(
         ctypes.byref(s), P, 1, P, P, P, P, 128, P, P, 0.088, P, P, ws, flags, None)
     assert att_ex(2) == ops.OASIS_ERR_INVALID            # unknown launch hint
     assert att_ex(-1) == ops.OASIS_ERR_INVALID
+
+
+def test_fetch_rejects_bad_arguments():
+    L = ops.lib()
+    s = _shape(table_width=8, num_pages=64)    # K = 8 slots, 64 working-set pages
+    fetch = lambda host_blocks=256, cap=2, hk=P, wsv=P, shape=s: L.oasis_fetch_blocks(
+        ctypes.byref(shape), hk, P, host_blocks, P, P, P, cap, P, P, wsv, None)
+    assert fetch(host_blocks=0) == ops.OASIS_ERR_INVALID
+    assert fetch(cap=9) == ops.OASIS_ERR_INVALID           # cap > K
+    assert fetch(cap=-1) == ops.OASIS_ERR_INVALID
+    assert fetch(hk=None) == ops.OASIS_ERR_INVALID
+    assert fetch(hk=ctypes.c_void_p(40)) == ops.OASIS_ERR_INVALID    # misaligned host pool
+    assert fetch(wsv=ctypes.c_void_p(8)) == ops.OASIS_ERR_INVALID    # misaligned working set
+    assert fetch(shape=_shape(head_dim=96)) == ops.OASIS_ERR_UNSUPPORTED
+    assert fetch(cap=0) == ops.OASIS_OK                    # nothing to fetch: no launch
+    assert fetch(shape=_shape(batch=0)) == ops.OASIS_OK
 
 
 def test_library_is_required():
