@@ -67,7 +67,7 @@ __device__ __forceinline__ int load_row_keys(const float *srow, int width, const
         v[u] = srow[n < width ? n : last];
     }
     const int ctx = ctx_raw < 0 ? 0 : ctx_raw;
-    const int c = (ctx + kBlockTokens - 1) / kBlockTokens;
+    const int c = ctx / kBlockTokens + (ctx % kBlockTokens != 0);   // ceil, no overflow
     const int nb = c > width ? width : c;
 #pragma unroll
     for (int u = 0; u < U; ++u) {

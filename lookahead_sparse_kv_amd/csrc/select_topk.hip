@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(SelectArgs a) 
     const int b = row / a.hkv;
     int ctx = a.ctx_len[b];
     ctx = ctx < 0 ? 0 : ctx;
-    int nb = (ctx + kBlockTokens - 1) / kBlockTokens;
+    int nb = ctx / kBlockTokens + (ctx % kBlockTokens != 0);   // ceil, no overflow
     nb = nb > a.width ? a.width : nb;
     const float *srow = a.scores + (size_t)row * a.width;
     int32_t *out = a.sel + (size_t)row * a.k;

@@ -275,6 +275,43 @@ def test_select_plan_fused_bit_exact_over_steps(case):
         np.testing.assert_array_equal(g_lu.cpu().numpy(), lu)
 
 
+@pytest.mark.parametrize("W,K", [(300, 32), (3000, 128), (9000, 128), (1000, 600)],
+                         ids=["fused", "fused_1024_threads", "generic_select_then_plan",
+                              "row_select_then_plan"])
+def test_select_with_context_lengths_out_of_range(W, K):
+    # A context length past the table's 16 * W tokens counts as the whole
+    # table, and a negative one as empty (INT32_MAX must not overflow the
+    # round-up to blocks): both select and select + plan see ctx clamped to
+    # [0, 16 * W].
+    B, Hkv, cap = 4, 2, 3
+    rng = np.random.default_rng(W * 7 + K)
+    ctx_len = np.array([2 ** 31 - 1, -5, 16 * W + 7, 16 * W - 9], np.int32)
+    clamped = np.clip(ctx_len.astype(np.int64), 0, 16 * W).astype(np.int32)
+    s = _random_scores(rng, B, Hkv, W, "normal")
+    shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
+    g_s, g_ctx = dev(torch.from_numpy(s)), dev(torch.from_numpy(ctx_len))
+    want = orc.select(s.astype(np.float64), clamped, 16, K)
+    sel = torch.full((B, Hkv, K), -7, dtype=torch.int32, device=DEV)
+    ops.select_topk(shape, g_s, g_ctx, K, sel)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), want)
+    sb, lu = _random_state(rng, B, Hkv, K, W - 6, None)
+    ofb, ofs, ocnt, osb, olu = orc.plan(want, s.astype(np.float64), sb, lu, cap, 5)
+    g_sb, g_lu = dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))
+    fb = torch.empty((B, Hkv, cap), dtype=torch.int32, device=DEV)
+    fs = torch.empty_like(fb)
+    fc = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    sel.fill_(-7)
+    ops.select_plan(shape, g_s, g_ctx, K, cap, 5, sel, g_sb, g_lu, fb, fs, fc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), want)
+    np.testing.assert_array_equal(fc.cpu().numpy(), ocnt)
+    np.testing.assert_array_equal(fb.cpu().numpy(), ofb)
+    np.testing.assert_array_equal(fs.cpu().numpy(), ofs)
+    np.testing.assert_array_equal(g_sb.cpu().numpy(), osb)
+    np.testing.assert_array_equal(g_lu.cpu().numpy(), olu)
+
+
 # ---------------------------------------------------------------- attention
 ATTN_CASES = {
     # name: (workload kwargs, n_q, n_blk, fraction of -1 entries)
