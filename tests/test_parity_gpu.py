@@ -356,6 +356,12 @@ ATTN_CASES = {
                         1, 96, 0.1),
     "d128_g4_nq4_256_rows_long_lists": (dict(batch=32, q_heads=64, kv_heads=8, head_dim=128,
                                              ctx=(4096, 3000)), 4, 200, 0.05),
+    # the largest list (K = 1024): each wave walks its share 64 entries at a time
+    "d64_g4_256_rows_k1024_two_chunks_per_wave": (dict(batch=64, q_heads=16, kv_heads=4,
+                                                       head_dim=64, ctx=(4096, 3000, 777)),
+                                                  1, 1024, 0.0),
+    "d128_g4_nq5_128_rows_k1024_two_tiles": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128,
+                                                  ctx=(4096, 2100, 300)), 5, 1024, 0.0),
 }
 
 
