@@ -12,10 +12,13 @@
 // 16 x 16 MFMA tile covers 16 lookahead rows (A = [q- | q+], bf16, split by
 // sign bit once per wave) against 16 blocks (B = the compressed rows
 // [min | max], stored by tiles of 16 blocks in 8-element slices, 8 KiB per
-// tile at D = 128); D/16 v_mfma_f32_16x16x32_bf16 per tile.  A wave takes 64 consecutive blocks of
-// one row, issues all their loads (raw buffer loads bounded to the row's valid
-// blocks, non-temporal: each compressed key is read once per step), then
-// reduces each tile's columns over the lookahead rows with two lane exchanges.
+// tile at D = 128); D/16 v_mfma_f32_16x16x32_bf16 per tile.  A wave takes one
+// tile (16 consecutive blocks) of one row, issues all its loads (raw buffer
+// loads bounded to the row's valid blocks, non-temporal: each compressed key
+// is read once per step), then reduces the tile's columns over the lookahead
+// rows with two lane exchanges.  One tile per wave (8 KiB) keeps more waves in
+// flight and leaves a shorter tail than four: 22.3 against 23.7 us per launch
+// at 16 x 32K.
 // A block written as an empty box (min > max, for a page outside the pool)
 // scores -inf.  The bytes are 1/8 of the exact scorer's at bs = 16.
 //
@@ -33,8 +36,14 @@
 
 namespace oasis {
 
-constexpr int kMmWaves = 4;
-constexpr int kMmTiles = 4;            // 16-block tiles per wave
+#ifndef OASIS_MM_WAVES
+#define OASIS_MM_WAVES 4
+#endif
+constexpr int kMmWaves = OASIS_MM_WAVES;   // waves per workgroup
+#ifndef OASIS_MM_TILES
+#define OASIS_MM_TILES 1
+#endif
+constexpr int kMmTiles = OASIS_MM_TILES;   // 16-block tiles per wave
 constexpr int kMmBlocksPerWave = kMmTiles * kBlockTokens;
 
 // Refresh wave of one row: pool the last block (ceil(ctx / 16) - 1) from the
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(kMmWaves * kWave) void score_minmax_kernel(MinmaxAr
     ctx = ctx < 0 ? 0 : (ctx > cmax ? cmax : ctx);
     const int nb = (int)((ctx + kBlockTokens - 1) / kBlockTokens);
 
-    // Compressed tiles n0/16 .. n0/16 + 3 (16 blocks each, in 8-element slices):
+    // Compressed tiles n0/16 .. n0/16 + kMmTiles - 1 (16 blocks each, in 8-element slices):
     // the B operand of k-step kk (block r16, elements 32*kk + 8*j4 .. +8) is
     // slice 4*kk + j4, at lane * 16 + kk * 1 KiB of the tile, so each load
     // reads 1 KiB of contiguous memory.  The resource ends at the last tile
