@@ -24,7 +24,10 @@
 
 namespace oasis {
 
-constexpr int kPoolWaves = 4;
+#ifndef OASIS_POOL_WAVES
+#define OASIS_POOL_WAVES 4
+#endif
+constexpr int kPoolWaves = OASIS_POOL_WAVES;   // waves per workgroup
 #ifndef OASIS_POOL_CPOL
 #define OASIS_POOL_CPOL 2               // key tiles: non-temporal (each is read once)
 #endif
@@ -79,7 +82,10 @@ __global__ __launch_bounds__(kPoolWaves * kWave) void pool_keys_kernel(PoolArgs 
 // apart (which cost a third of the kernel's time).  Blocks past the context
 // are not written, as in the per-block kernel.
 constexpr int kPoolTileBlocks = 16;      // blocks per compressed tile
-constexpr int kPoolGroup = 4;            // blocks loaded together
+#ifndef OASIS_POOL_GROUP
+#define OASIS_POOL_GROUP 4
+#endif
+constexpr int kPoolGroup = OASIS_POOL_GROUP;   // blocks loaded together
 
 template <int D>
 __global__ __launch_bounds__(kPoolWaves * kWave) void pool_tiles_kernel(PoolArgs a) {
