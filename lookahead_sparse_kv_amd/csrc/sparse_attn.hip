@@ -348,7 +348,10 @@ constexpr int kAttnRowFillRows = OASIS_ATTN_ROW_MIN_ROWS;
 #ifndef OASIS_ATTN_ROWSPLIT_MIN_ROWS
 #define OASIS_ATTN_ROWSPLIT_MIN_ROWS 128
 #endif
-constexpr int kRowAttnWaves = 8;
+#ifndef OASIS_ATTN_ROW_WAVES
+#define OASIS_ATTN_ROW_WAVES 8
+#endif
+constexpr int kRowAttnWaves = OASIS_ATTN_ROW_WAVES;   // waves of the one-workgroup-per-row kernel
 #ifndef OASIS_ATTN_ROWSPLIT_WAVES
 #define OASIS_ATTN_ROWSPLIT_WAVES 8
 #endif
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArg
     extern __shared__ float red[];
     const int row = blockIdx.x;
     const int nrq = a.n_rows_q;
-    row_waves_to_lds<D, 16>(a, row, 0, a.n_blk, red);
+    row_waves_to_lds<D, 128 / kRowAttnWaves>(a, row, 0, a.n_blk, red);   // 128 listed blocks: unrolled
     __syncthreads();
     for (int idx = threadIdx.x; idx < nrq * D; idx += kRowAttnWaves * kWave) {
         const int c = idx / D;
