@@ -54,7 +54,7 @@ def parse():
                         "working set in the 256 MB last-level cache (as in a model, "
                         "where consecutive layers hold different KV)")
     p.add_argument("--plan-stream", choices=("auto", "on", "off"), default="auto",
-                   help="select + plan on a third stream (auto: with the compressed scorer)")
+                   help="select + plan on a third stream (auto: on)")
     p.add_argument("--native", choices=("on", "off"), default="on",
                    help="enqueue each pipelined layer-step with one oasis_layer_step call "
                         "(on) or with the Python sequence of launches and event calls (off)")
@@ -89,10 +89,11 @@ def attn_bytes(wl):
     return kv + q + out + lists
 
 
-def attn_kernel_name(wl):
-    """The attention launch shape the library picks for this workload (one query row per head)."""
+def attn_kernel_name(wl, share_gpu=False):
+    """The attention launch shape the library picks for this workload (one query row per head;
+    share_gpu: with the share-GPU hint, one workgroup per row from 128 rows)."""
     rows = wl.batch * wl.num_kv_heads
-    if rows >= 256:
+    if rows >= 256 or (share_gpu and rows >= 128):
         return "attn_row_kernel (one workgroup per row, merged in LDS)"
     if rows >= 128 and wl.k_blocks >= 32:
         return ("attn_rowsplit_kernel (two workgroups per row, merged in LDS, then across the "
@@ -580,11 +581,12 @@ def main():
     # after layer, as in a model's decode step).  Only the scoring kernel is
     # bracketed by events inside the timed loop, on the stream it runs on.
     side = torch.cuda.Stream(device=dev)                                # default priority
-    # Compressed scorer: select/plan on a third stream, so that a layer's plan
-    # for t + 1 overlaps the next layers' attention (measured faster); exact
-    # scorer: scoring bounds the step and select/plan stays on the caller's
-    # stream (a third stream measured slower there).
-    use_plan_stream = (wl.scorer == "minmax") if args.plan_stream == "auto" else args.plan_stream == "on"
+    # Select/plan on a third stream: the scoring of step t + 1 waits for the
+    # caller's stream (where a model writes that step's lookahead query), so a
+    # plan on the caller's stream would put its latency between consecutive
+    # scoring launches; on its own stream a layer's plan for t + 1 also
+    # overlaps the next layers' attention.
+    use_plan_stream = True if args.plan_stream == "auto" else args.plan_stream == "on"
     plan_stream = torch.cuda.Stream(device=dev) if use_plan_stream else None
     # the timed loop enqueues each layer-step natively; the loop with events
     # around the scoring launches takes the Python path (same launches)
@@ -685,6 +687,9 @@ def main():
               ("select_plan", lambda i, L: L.select_plan(3000 + i,
                                                          scores=alt[i % n_rep][(i // n_rep) % 2])),
               ("attn", lambda i, L: L.attend(q))]
+    if share_gpu:
+        # the launch shape the timed step uses for attention (one CU per row)
+        stages.append(("attn_in_step_shape", lambda i, L: L.attend(q, share_gpu=True)))
     for k, fn in stages:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         # one untimed call first: the GPU is then busy when e0 is recorded, so
@@ -791,7 +796,13 @@ def main():
         "attn_roofline": {"kernels": attn_kernel_name(wl),
                           "timing": "back-to-back mean",
                           "achieved": round(attn_gbs, 1), "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                          "algorithmic_bytes": ab},
+                          "algorithmic_bytes": ab,
+                          # the launch shape of the timed step, when it differs
+                          "in_step_launch_shape": None if not share_gpu else {
+                              "kernels": attn_kernel_name(wl, share_gpu=True),
+                              "achieved": round(ab / (b2b["attn_in_step_shape"] * 1e-3) / 1e9, 1),
+                              "frac": round(ab / (b2b["attn_in_step_shape"] * 1e-3) / 1e9
+                                            / HBM_PEAK_GBS, 4)}},
         "detail": detail or None,
         "fetched_blocks_last_step": fetched,
         "fetched_blocks_per_call": {"cap_per_row": cap, "rows": wl.batch * wl.num_kv_heads,

@@ -355,8 +355,9 @@ int oasis_fetch_blocks(const oasis_shape *s, const uint16_t *host_k, const uint1
  * handles passed as void*; an event that is NULL is skipped.  The call
  * enqueues, in this order:
  *
- *   score_stream: wait score_after; scoring of q_look_next into scores;
- *                 record scored
+ *   attn_stream:  record inputs (if set)
+ *   score_stream: wait inputs (if set); wait score_after; scoring of
+ *                 q_look_next into scores; record scored
  *   attn_stream:  wait attn_after; oasis_sparse_decode_attn_ex(attn_flags) of
  *                 q over the working set slot_block (full-pool mode: the block
  *                 table as page table); record attended if plan_stream differs
@@ -383,6 +384,11 @@ typedef struct {
     void *score_stream, *attn_stream, *plan_stream;
     void *score_after, *attn_after;    /* events waited on first (NULL: none) */
     void *scored, *attended, *planned; /* events recorded */
+    void *inputs;                      /* recorded on attn_stream and waited on by score_stream
+                                          before scoring, so that scoring sees q_look_next,
+                                          ctx_len and appended keys written on attn_stream
+                                          (the caller's stream) before the call; NULL: the
+                                          caller orders those writes itself */
 } oasis_step_sync;
 
 int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const uint16_t *q,

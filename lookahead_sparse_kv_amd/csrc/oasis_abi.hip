@@ -327,6 +327,10 @@ int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const ui
     hipStream_t ss = as_stream(sync->score_stream), as = as_stream(sync->attn_stream),
                 ps = as_stream(sync->plan_stream);
     const auto ev = [](void *e) { return reinterpret_cast<hipEvent_t>(e); };
+    if (sync->inputs) {
+        if (int e = check_hip(hipEventRecord(ev(sync->inputs), as), fn)) return e;
+        if (int e = check_hip(hipStreamWaitEvent(ss, ev(sync->inputs), 0), fn)) return e;
+    }
     if (sync->score_after)
         if (int e = check_hip(hipStreamWaitEvent(ss, ev(sync->score_after), 0), fn)) return e;
     int e = L->ck ? oasis_score_blocks_minmax(&L->shape, q_look_next, L->n_look, L->ck,

@@ -54,7 +54,7 @@ class OasisStepSync(ctypes.Structure):
     """oasis_step_sync: streams and events (raw handles) of one oasis_layer_step."""
     _fields_ = [(n, ctypes.c_void_p) for n in ("score_stream", "attn_stream", "plan_stream",
                                                 "score_after", "attn_after", "scored",
-                                                "attended", "planned")]
+                                                "attended", "planned", "inputs")]
 
 
 class OasisError(RuntimeError):
@@ -130,6 +130,44 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _numel(*dims) -> int:
+    n = 1
+    for d in dims:
+        n *= int(d)
+    return n
+
+
+def _check_tensors(*specs):
+    """The C ABI receives bare pointers and cannot see a buffer's size, layout
+    or device: reject, before anything is enqueued, a tensor that is not a
+    contiguous tensor of the expected dtype holding at least the elements the
+    call will touch, and then one that is not on the GPU.  Each spec is
+    (tensor, name, dtype, numel) or (tensor, name, dtype, numel, optional)."""
+    present = []
+    for spec in specs:
+        t, name, dtype, numel = spec[:4]
+        optional = len(spec) > 4 and spec[4]
+        if t is None:
+            if optional:
+                continue
+            raise ValueError(f"{name}: a tensor is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous (the kernels index it as a dense array)")
+        if t.numel() < numel:
+            raise ValueError(f"{name}: {t.numel()} elements, at least {numel} needed")
+        present.append((t, name))
+    for t, name in present:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: on {t.device}, expected a GPU tensor")
+
+
+_BF16, _F32, _I32 = torch.bfloat16, torch.float32, torch.int32
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -151,7 +189,16 @@ def score_blocks(q_look, k_pool, block_table, ctx_len, scores, scale=None, strea
     """q_look [B][n_look][Hq][D] bf16, k_pool [P][Hkv][16][D] bf16 (tiles in 8-dim slices),
     block_table [B][W] i32,
     ctx_len [B] i32 -> scores [B][Hkv][W] f32 (written in place)."""
+    if q_look.dim() != 4 or k_pool.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("score_blocks: q_look [B][n_look][Hq][D], k_pool [P][Hkv][16][D], "
+                         "block_table [B][W] expected")
     s = _pool_shape(q_look, k_pool, block_table)
+    B, Hkv, D, W = s.batch, s.num_kv_heads, s.head_dim, s.table_width
+    _check_tensors((q_look, "q_look", _BF16, _numel(B, q_look.shape[1], s.num_q_heads, D)),
+                   (k_pool, "k_pool", _BF16, _numel(s.num_pages, Hkv, BLOCK_SIZE, D)),
+                   (block_table, "block_table", _I32, B * W),
+                   (ctx_len, "ctx_len", _I32, B),
+                   (scores, "scores", _F32, B * Hkv * W))
     scale = float(s.head_dim) ** -0.5 if scale is None else scale
     _check(lib().oasis_score_blocks(ctypes.byref(s), _ptr(q_look), q_look.shape[1], _ptr(k_pool),
                                     _ptr(block_table), _ptr(ctx_len), scale, _ptr(scores),
@@ -173,6 +220,11 @@ def pool_keys(k_pool, block_table, ctx_len, ck, num_q_heads=None, last_only=Fals
     Hkv = k_pool.shape[1]
     s = make_shape(block_table.shape[0], num_q_heads or Hkv, Hkv, k_pool.shape[-1],
                    block_table.shape[1], k_pool.shape[0])
+    B, D, W = s.batch, s.head_dim, s.table_width
+    _check_tensors((k_pool, "k_pool", _BF16, _numel(s.num_pages, Hkv, BLOCK_SIZE, D)),
+                   (block_table, "block_table", _I32, B * W),
+                   (ctx_len, "ctx_len", _I32, B),
+                   (ck, "ck", _BF16, _numel(*compressed_keys_shape(B, Hkv, W, D))))
     _check(lib().oasis_pool_keys(ctypes.byref(s), _ptr(k_pool), _ptr(block_table), _ptr(ctx_len),
                                  1 if last_only else 0, _ptr(ck), _stream(stream)))
     return ck
@@ -187,6 +239,12 @@ def score_blocks_minmax(q_look, ck, ctx_len, scores, scale=None, k_pool=None, bl
     D = ck.shape[3] * 4
     assert tuple(ck.shape) == compressed_keys_shape(B, Hkv, W, D)
     s = make_shape(B, q_look.shape[-2], Hkv, D, W, 0 if k_pool is None else k_pool.shape[0])
+    _check_tensors((q_look, "q_look", _BF16, _numel(B, q_look.shape[1], s.num_q_heads, D)),
+                   (ck, "ck", _BF16, _numel(*compressed_keys_shape(B, Hkv, W, D))),
+                   (ctx_len, "ctx_len", _I32, B),
+                   (scores, "scores", _F32, B * Hkv * W),
+                   (k_pool, "k_pool", _BF16, _numel(s.num_pages, Hkv, BLOCK_SIZE, D), True),
+                   (block_table, "block_table", _I32, B * W, True))
     scale = float(D) ** -0.5 if scale is None else scale
     _check(lib().oasis_score_blocks_minmax(ctypes.byref(s), _ptr(q_look), q_look.shape[1],
                                            _ptr(ck), _ptr(k_pool), _ptr(block_table),
@@ -196,14 +254,34 @@ def score_blocks_minmax(q_look, ck, ctx_len, scores, scale=None, k_pool=None, bl
 
 def select_topk(shape: OasisShape, scores, ctx_len, k_blocks, sel, stream=None):
     """scores [B][Hkv][W] f32 -> sel [B][Hkv][K] i32 (ascending, -1 padded)."""
+    rows = shape.batch * shape.num_kv_heads
+    _check_tensors((scores, "scores", _F32, rows * shape.table_width),
+                   (ctx_len, "ctx_len", _I32, shape.batch),
+                   (sel, "sel", _I32, rows * max(k_blocks, 0)))
     _check(lib().oasis_select_topk(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks,
                                    _ptr(sel), _stream(stream)))
     return sel
 
 
+def _plan_specs(shape, k_blocks, cap, sel, slot_block, last_use, fetch_block, fetch_slot,
+                fetch_count, scores):
+    """Buffers of a plan: the fetch lists get cap entries per row at stride cap."""
+    rows = shape.batch * shape.num_kv_heads
+    K = max(int(k_blocks), 0)
+    specs = [(sel, "sel", _I32, rows * K), (slot_block, "slot_block", _I32, rows * K),
+             (last_use, "last_use", _I32, rows * K), (fetch_count, "fetch_count", _I32, rows),
+             (scores, "scores", _F32, rows * shape.table_width)]
+    if cap > 0:
+        specs += [(fetch_block, "fetch_block", _I32, rows * int(cap)),
+                  (fetch_slot, "fetch_slot", _I32, rows * int(cap))]
+    return specs
+
+
 def plan_fetch(shape: OasisShape, sel, scores, k_blocks, cap, step, slot_block, last_use,
                fetch_block, fetch_slot, fetch_count, stream=None):
     """Updates slot_block / last_use [B][Hkv][K] in place; writes the capped fetch list."""
+    _check_tensors(*_plan_specs(shape, k_blocks, cap, sel, slot_block, last_use, fetch_block,
+                                fetch_slot, fetch_count, scores))
     _check(lib().oasis_plan_fetch(ctypes.byref(shape), _ptr(sel), _ptr(scores), k_blocks, cap,
                                   step, _ptr(slot_block), _ptr(last_use), _ptr(fetch_block),
                                   _ptr(fetch_slot), _ptr(fetch_count), _stream(stream)))
@@ -214,6 +292,10 @@ def select_plan(shape: OasisShape, scores, ctx_len, k_blocks, cap, step, sel, sl
     """select_topk then plan_fetch in one launch where the shape allows (same results).
     step_dev (int32 device tensor of one element, or None): the plan's step is
     step + step_dev[0], read on the device (oasis_select_plan_ex)."""
+    _check_tensors(*_plan_specs(shape, k_blocks, cap, sel, slot_block, last_use, fetch_block,
+                                fetch_slot, fetch_count, scores),
+                   (ctx_len, "ctx_len", _I32, shape.batch),
+                   (step_dev, "step_dev", _I32, 1, True))
     if step_dev is None:
         _check(lib().oasis_select_plan(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks,
                                        cap, step, _ptr(sel), _ptr(slot_block), _ptr(last_use),
@@ -239,7 +321,21 @@ def sparse_decode_attn(shape: OasisShape, q, k_pool, v_pool, page_table, blk, bl
     blk / blk_logical [B][Hkv][n_blk] i32 (blk may be None: entry e is index e).
     workspace: any contents (oasis_attn_workspace_bytes() bytes).  flags: OASIS_ATTN_SHARE_GPU when another launch runs
     beside this one (oasis_sparse_decode_attn_ex); 0 calls oasis_sparse_decode_attn."""
+    if blk is None and blk_logical is None:
+        raise ValueError("blk_logical: blk and blk_logical are both None")
     n_blk = (blk if blk is not None else blk_logical).shape[-1]
+    B, Hkv, D = shape.batch, shape.num_kv_heads, shape.head_dim
+    n_q = q.shape[1]
+    _check_tensors((q, "q", _BF16, _numel(B, n_q, shape.num_q_heads, D)),
+                   (k_pool, "k_pool", _BF16, _numel(shape.num_pages, Hkv, BLOCK_SIZE, D)),
+                   (v_pool, "v_pool", _BF16, _numel(shape.num_pages, Hkv, BLOCK_SIZE, D)),
+                   (page_table, "page_table", _I32, B * shape.table_width),
+                   (blk, "blk", _I32, B * Hkv * n_blk, True),
+                   (blk_logical, "blk_logical", _I32, B * Hkv * n_blk, blk is not None),
+                   (ctx_len, "ctx_len", _I32, B),
+                   (out, "out", _BF16, _numel(B, n_q, shape.num_q_heads, D)),
+                   (workspace, "workspace", workspace.dtype if isinstance(workspace, torch.Tensor)
+                    else None, 0))
     scale = float(shape.head_dim) ** -0.5 if scale is None else scale
     args = (ctypes.byref(shape), _ptr(q), q.shape[1], _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
             _ptr(blk), n_blk, _ptr(blk_logical), _ptr(ctx_len), scale, _ptr(out), _ptr(workspace),
@@ -253,7 +349,14 @@ def sparse_decode_attn(shape: OasisShape, q, k_pool, v_pool, page_table, blk, bl
 
 def layer_step(layer: OasisLayer, q_look_next, q, scores, step: int, sync: OasisStepSync):
     """oasis_layer_step: score (q_look_next -> scores), attention (q), select + plan (step),
-    ordered across the streams of `sync` by its events."""
+    ordered across the streams of `sync` by its events.  The layer's own buffers were
+    checked when its descriptor was built (DecodeLayer)."""
+    s = layer.shape
+    rows = s.batch * s.num_kv_heads
+    _check_tensors((q_look_next, "q_look_next", _BF16,
+                    _numel(s.batch, layer.n_look, s.num_q_heads, s.head_dim)),
+                   (q, "q", _BF16, _numel(s.batch, layer.n_q, s.num_q_heads, s.head_dim)),
+                   (scores, "scores", _F32, rows * s.table_width))
     _check(lib().oasis_layer_step(ctypes.byref(layer), _ptr(q_look_next), _ptr(q), _ptr(scores),
                                   step, ctypes.byref(sync)))
 
@@ -304,6 +407,15 @@ def fetch_blocks(ws_shape: OasisShape, host_k_dev: int, host_v_dev: int, host_bl
                  fetch_block, fetch_slot, fetch_count, cap, ws_page_table, ws_k_pool, ws_v_pool,
                  stream=None):
     """Copy the listed blocks from the pinned host pool into working-set slots (device side)."""
+    rows = ws_shape.batch * ws_shape.num_kv_heads
+    tile = _numel(ws_shape.num_pages, ws_shape.num_kv_heads, BLOCK_SIZE, ws_shape.head_dim)
+    specs = [(fetch_count, "fetch_count", _I32, rows),
+             (ws_page_table, "ws_page_table", _I32, ws_shape.batch * ws_shape.table_width),
+             (ws_k_pool, "ws_k_pool", _BF16, tile), (ws_v_pool, "ws_v_pool", _BF16, tile)]
+    if cap > 0:
+        specs += [(fetch_block, "fetch_block", _I32, rows * int(cap)),
+                  (fetch_slot, "fetch_slot", _I32, rows * int(cap))]
+    _check_tensors(*specs)
     _check(lib().oasis_fetch_blocks(ctypes.byref(ws_shape), ctypes.c_void_p(host_k_dev),
                                     ctypes.c_void_p(host_v_dev), host_blocks, _ptr(fetch_block),
                                     _ptr(fetch_slot), _ptr(fetch_count), cap, _ptr(ws_page_table),

@@ -35,7 +35,7 @@ class DecodeLayer:
         B, W = block_table.shape
         Hkv, D = k_pool.shape[1], k_pool.shape[-1]
         self.shape = ops.make_shape(B, num_q_heads, Hkv, D, W, k_pool.shape[0])
-        self.k_blocks, self.cap, self.n_look, self.n_q = k_blocks, cap, n_look, n_q
+        self.k_blocks, self.n_look, self.n_q = k_blocks, n_look, n_q
         i32 = dict(dtype=torch.int32, device=dev)
         self.scores = torch.empty((B, Hkv, W), dtype=torch.float32, device=dev)
         self.sel = torch.empty((B, Hkv, k_blocks), **i32)
@@ -43,9 +43,14 @@ class DecodeLayer:
                            else slot_block.to(dev, torch.int32).contiguous())
         self.last_use = (torch.full((B, Hkv, k_blocks), -(2 ** 31), **i32) if last_use is None
                          else last_use.to(dev, torch.int32).contiguous())
-        self.fetch_block = torch.empty((B, Hkv, max(cap, 1)), **i32)
-        self.fetch_slot = torch.empty((B, Hkv, max(cap, 1)), **i32)
+        # The fetch lists hold `cap` entries per row at stride cap; the storage
+        # has room for cap = K, the largest cap a step may use, so that a
+        # caller may change cap between steps (the prefetch and the uncapped
+        # compensatory fetch share one layer).
+        self._fetch_block_buf = torch.empty((B * Hkv * k_blocks,), **i32)
+        self._fetch_slot_buf = torch.empty((B * Hkv * k_blocks,), **i32)
         self.fetch_count = torch.empty((B, Hkv), **i32)
+        self.cap = cap
         self.out = torch.empty((B, n_q, num_q_heads, D), dtype=torch.bfloat16, device=dev)
         ws = ops.attn_workspace_bytes(self.shape, n_q, k_blocks)
         self.workspace = torch.zeros((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
@@ -54,6 +59,29 @@ class DecodeLayer:
             self.ck = torch.empty(ops.compressed_keys_shape(B, Hkv, W, D), dtype=torch.bfloat16,
                                   device=dev)
             ops.pool_keys(k_pool, block_table, ctx_len, self.ck, num_q_heads=num_q_heads)
+
+    @property
+    def cap(self) -> int:
+        return self._cap
+
+    @cap.setter
+    def cap(self, value: int):
+        value = int(value)
+        if not 0 <= value <= self.k_blocks:
+            raise ValueError(f"cap {value} outside [0, k_blocks = {self.k_blocks}]: the fetch "
+                             f"lists hold at most k_blocks entries per row")
+        self._cap = value
+
+    @property
+    def fetch_block(self) -> torch.Tensor:
+        """[B][Hkv][cap] view of the fetch list (the plan writes it at stride cap)."""
+        B, Hkv = self.fetch_count.shape
+        return self._fetch_block_buf[:B * Hkv * self._cap].view(B, Hkv, self._cap)
+
+    @property
+    def fetch_slot(self) -> torch.Tensor:
+        B, Hkv = self.fetch_count.shape
+        return self._fetch_slot_buf[:B * Hkv * self._cap].view(B, Hkv, self._cap)
 
     # individual stages -------------------------------------------------
     def score(self, q_look, stream=None, scores=None, refresh=False):
@@ -107,8 +135,8 @@ class DecodeLayer:
                 refresh=int(refresh), n_look=self.n_look, n_q=self.n_q, k_blocks=self.k_blocks,
                 cap=self.cap, attn_flags=ops.OASIS_ATTN_SHARE_GPU if share_gpu else 0,
                 scale=float(D) ** -0.5, sel=vp(self.sel), slot_block=vp(self.slot_block),
-                last_use=vp(self.last_use), fetch_block=vp(self.fetch_block),
-                fetch_slot=vp(self.fetch_slot), fetch_count=vp(self.fetch_count),
+                last_use=vp(self.last_use), fetch_block=vp(self._fetch_block_buf),
+                fetch_slot=vp(self._fetch_slot_buf), fetch_count=vp(self.fetch_count),
                 out=vp(self.out), workspace=vp(self.workspace),
                 workspace_bytes=self.workspace.numel() * self.workspace.element_size())
         desc = cache[key]
@@ -175,6 +203,7 @@ class PipelinedDecode:
         self.ev_scored = [torch.cuda.Event(), torch.cuda.Event()]
         self.ev_planned = [torch.cuda.Event(), torch.cuda.Event()]
         self.ev_attended = torch.cuda.Event()
+        self.ev_inputs = torch.cuda.Event()
         self.last_plan = None            # event of the latest plan (plan_stream mode)
         self.used = [False, False]
         self.i = 0
@@ -184,15 +213,19 @@ class PipelinedDecode:
             # torch creates an event at its first record: create them now, so
             # that their handles can be handed to native code
             cur = torch.cuda.current_stream()
-            for e in (*self.ev_scored, *self.ev_planned, self.ev_attended):
+            for e in (*self.ev_scored, *self.ev_planned, self.ev_attended, self.ev_inputs):
                 e.record(cur)
 
     def _score_next(self, q_look, main, ev=None, append=False):
         b = self.i % 2
-        if self.used[b]:
+        # The caller writes this step's inputs (the lookahead query, ctx_len, an
+        # appended key) on its own stream just before the call: scoring waits
+        # for everything enqueued there so far.  With select + plan on the
+        # caller's stream that includes the plan that last read buf[b];
+        # otherwise that plan is waited for on its own.
+        self.side.wait_stream(main)
+        if self.used[b] and self.plan_stream is not None:
             self.side.wait_event(self.ev_planned[b])    # the plan that last read buf[b]
-        else:
-            self.side.wait_stream(main)                 # inputs written on the caller's stream
         if ev:
             ev[0].record(self.side)
         # append: the compressed keys of the last blocks are refreshed in the launch
@@ -246,18 +279,18 @@ class PipelinedDecode:
     def _native_step(self, q, q_look_next, step, main, append):
         """The same step as the Python path below, through oasis_layer_step."""
         b = self.i % 2
-        score_after = None
-        if self.used[b]:
-            score_after = self.ev_planned[b]            # the plan that last read buf[b]
-        else:
-            self.side.wait_stream(main)                 # inputs written on the caller's stream
+        # as in _score_next: the inputs event orders scoring after the caller's
+        # stream; a plan on another stream that last read buf[b] is waited for
+        score_after = (self.ev_planned[b] if self.used[b] and self.plan_stream is not None
+                       else None)
         ps = main if self.plan_stream is None else self.plan_stream
         attn_after = self.last_plan if self.plan_stream is not None else None
         h = lambda x: None if x is None else x.cuda_event
         sync = ops.OasisStepSync(score_stream=self.side.cuda_stream, attn_stream=main.cuda_stream,
                                  plan_stream=ps.cuda_stream, score_after=h(score_after),
                                  attn_after=h(attn_after), scored=h(self.ev_scored[b]),
-                                 attended=h(self.ev_attended), planned=h(self.ev_planned[b]))
+                                 attended=h(self.ev_attended), planned=h(self.ev_planned[b]),
+                                 inputs=h(self.ev_inputs))
         ops.layer_step(self.L.native_desc(share_gpu=self.share_gpu, refresh=append), q_look_next, q,
                        self.buf[b], step + 1, sync)
         self.last_plan = self.ev_planned[b]
@@ -298,19 +331,22 @@ class GraphedDecode:
         g.replay()                            # rounds steps of every layer
     """
 
-    # Captures of more than this many layer-steps (tried: 4 layers x 4 rounds
-    # at 16 x 32K) crashed the host process inside the end of the capture, in
-    # the runtime's capture_end; the cause is not known, so larger captures
-    # are refused.  Up to 2 layers x 2 rounds the replays are bit-identical to
-    # the eager steps.
-    MAX_LAYER_STEPS = 4
+    # A capture of 4 layers x 4 rounds at 16 x 32K crashed the host process
+    # inside the end of the capture, in the runtime's capture_end; the cause is
+    # not known.  Captures of at most 2 layers and at most 2 rounds have run,
+    # and their replays are bit-identical to the eager steps; anything else is
+    # refused, including shapes such as 3 or 4 layers x 1 round that were
+    # never run.
+    MAX_LAYERS = 2
+    MAX_ROUNDS = 2
 
     def __init__(self, layers, q, q_looks, rounds, step0=1, side=None, plan_stream=None,
                  append=False, share_gpu=True):
-        if len(layers) * rounds > self.MAX_LAYER_STEPS or rounds > 2:
+        if len(layers) > self.MAX_LAYERS or rounds > self.MAX_ROUNDS:
             raise NotImplementedError(
-                f"GraphedDecode: {len(layers)} layers x {rounds} rounds; captures beyond "
-                f"2 layers x 2 rounds are switched off (a 4 x 4 capture crashed in capture_end)")
+                f"GraphedDecode: {len(layers)} layers x {rounds} rounds; only captures of at most "
+                f"{self.MAX_LAYERS} layers and {self.MAX_ROUNDS} rounds have run (a 4 x 4 capture "
+                f"crashed in capture_end)")
         self.layers = list(layers)
         self.q, self.q_looks, self.rounds, self.step0 = q, q_looks, rounds, step0
         self.append = append

@@ -197,14 +197,14 @@ def test_minmax_calls_reject_bad_arguments():
 
 
 def test_graphed_decode_refuses_captures_beyond_the_tested_size():
-    # captures of 4 layers x 4 rounds crashed at the end of the capture; the
-    # class refuses anything beyond 2 layers x 2 rounds before touching a GPU
+    # a capture of 4 layers x 4 rounds crashed at the end of the capture; the
+    # class refuses more than 2 layers or more than 2 rounds before touching a
+    # GPU, so shapes that never ran (3 or 4 layers x 1 round) are refused too
     import pytest
     from lookahead_sparse_kv_amd.pipeline import GraphedDecode
-    with pytest.raises(NotImplementedError):
-        GraphedDecode([object()] * 4, None, None, rounds=4)
-    with pytest.raises(NotImplementedError):
-        GraphedDecode([object()] * 1, None, None, rounds=3)
+    for n_layers, rounds in ((4, 4), (1, 3), (3, 1), (4, 1), (3, 2), (2, 3)):
+        with pytest.raises(NotImplementedError):
+            GraphedDecode([object()] * n_layers, None, None, rounds=rounds)
 
 
 def test_layer_step_argument_checks():

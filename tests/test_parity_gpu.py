@@ -738,6 +738,67 @@ def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch, s
     assert int(max(x["fetch_count"].max().item() for x in st_nat)) == wl.cap()
 
 
+@pytest.mark.parametrize("native,plan_stream", [(False, False), (False, True), (True, False),
+                                                (True, True)])
+def test_pipeline_sees_inputs_written_on_the_callers_stream(native, plan_stream):
+    """A decode loop writes each step's lookahead query and context lengths in
+    place, on its own stream, just before the step (here behind a long chain
+    of matrix products, so that a scoring launch that did not wait for that
+    stream would read the previous step's values).  The pipelined steps give
+    the same bits as the same calls made one after another on one stream."""
+    wl = wlm.small_workload(batch=4, q_heads=32, kv_heads=8, head_dim=128,
+                            ctx=(4096, 3000, 2500, 4000), budget=512, n_hot=12, ratio=0.125, seed=45)
+    d = wlm.make_layer(wl)
+    T = 5
+    looks = [wlm.draw_lookahead(wl, d["q32"], 750 + t).to(torch.bfloat16) for t in range(T + 1)]
+    # context lengths before each call (prime, then steps): growing, ragged
+    ctxs = [torch.tensor([c - 200 + 37 * t for c in wl.ctx], dtype=torch.int32)
+            for t in range(T + 1)]
+    q = dev(d["q"].unsqueeze(1))
+    sb, lu = (x.numpy() for x in wlm.empty_state(wl))
+
+    # the plain order on one stream: write the inputs, then attention of step
+    # t, scoring of the lookahead query for t + 1 and select + plan of t + 1
+    ref = _gpu_layer(wl, d, wl.cap(), sb, lu)
+    q_buf, ctx_buf = dev(looks[0].clone()), ref.ctx_len
+    ctx_buf.copy_(dev(ctxs[0]))
+    ref.score(q_buf)
+    ref.select_plan(0)
+    want = []
+    for t in range(T):
+        ctx_buf.copy_(dev(ctxs[t + 1]))
+        q_buf.copy_(dev(looks[t + 1]))
+        ref.attend(q)
+        want.append(ref.out.clone())
+        ref.score(q_buf)
+        ref.select_plan(t + 1)
+    torch.cuda.synchronize()
+
+    lay = _gpu_layer(wl, d, wl.cap(), sb, lu)
+    q_buf2, ctx_buf2 = dev(looks[0].clone()), lay.ctx_len
+    ctx_buf2.copy_(dev(ctxs[0]))
+    host_looks = [dev(x) for x in looks]
+    host_ctxs = [dev(x) for x in ctxs]
+    pipe = PipelinedDecode(lay, plan_stream=torch.cuda.Stream() if plan_stream else None,
+                           native=native)
+    pipe.prime(q_buf2, 0)
+    x = torch.randn(2048, 2048, device=DEV)
+    got = []
+    for t in range(T):
+        for _ in range(12):                       # delay the writes on the caller's stream
+            x = torch.tanh(x @ x)
+        ctx_buf2.copy_(host_ctxs[t + 1])
+        q_buf2.copy_(host_looks[t + 1])
+        pipe.step(q, q_buf2, t, copy_out=False)
+        got.append(lay.out.clone())
+    pipe.drain()
+    torch.cuda.synchronize()
+    for t in range(T):
+        assert torch.equal(got[t], want[t]), t
+    for k in ("sel", "slot_block", "last_use", "fetch_count"):
+        assert torch.equal(getattr(lay, k), getattr(ref, k)), k
+
+
 def test_step_is_deterministic():
     wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(8000, 5000),
                             budget=1024, n_hot=20, ratio=0.05, seed=41)
