@@ -184,12 +184,31 @@ def check_attention_batch(gpu, want, q, K, V, ctx_len, lists, where="", rows=Non
     Hkv = np.asarray(lists).shape[1]
     G = Hq // Hkv
     ctx_len = np.asarray(ctx_len.cpu() if hasattr(ctx_len, "cpu") else ctx_len)
-    worst = 0.0
-    for b, g in rows or [(b, g) for b in range(B) for g in range(Hkv)]:
+
+    def one(r):
+        b, g = r
         hs = slice(g * G, (g + 1) * G)
-        worst = max(worst, check_attention(gpu[b, hs], want[b, hs], q[b, hs], K[b, g], V[b, g],
-                                           int(ctx_len[b]), lists[b, g], f"{where} b{b} g{g}"))
-    return worst
+        return check_attention(gpu[b, hs], want[b, hs], q[b, hs], K[b, g], V[b, g],
+                               int(ctx_len[b]), lists[b, g], f"{where} b{b} g{g}")
+
+    return max(pool_map(one, rows or [(b, g) for b in range(B) for g in range(Hkv)]))
+
+
+def pool_map(fn, items):
+    """fn over items on a thread pool (numpy's products and the oracle's ctypes
+    calls release the GIL), one BLAS thread per worker; re-raises the first
+    failure."""
+    import concurrent.futures
+    import os
+
+    from threadpoolctl import threadpool_limits
+    items = list(items)
+    workers = max(1, min(16, os.cpu_count() or 1, len(items)))
+    if workers == 1:
+        return [fn(x) for x in items]
+    with threadpool_limits(limits=1), \
+            concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
 
 
 def check_scores(gpu, orc, tol, where=""):

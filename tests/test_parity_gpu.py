@@ -6,9 +6,7 @@ fp32 scores, so the integer results must match bit for bit); the step tests
 chain the four stages and apply the near-tie exemption where the fp32 kernel
 scores and the fp64 oracle scores may legitimately order a boundary pair
 differently.  Sizes span several tiles with ragged tails, plus edge cases."""
-import concurrent.futures
 import math
-import os
 
 import numpy as np
 import pytest
@@ -20,7 +18,7 @@ from lookahead_sparse_kv_amd.pipeline import DecodeLayer, PipelinedDecode
 from oracle import oasis_oracle as orc
 from parity_utils import (check_attention, check_attention_batch, check_plan_row,
                           check_scores, check_selection_row,
-                          score_tolerance, score_tolerance_batch)
+                          pool_map, score_tolerance, score_tolerance_batch)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -571,18 +569,7 @@ def test_sparse_attention_large_logits_stay_finite():
 
 
 # ---------------------------------------------------------------- whole step
-def _pool_map(fn, items):
-    """fn over items on a thread pool (the oracle's ctypes calls and numpy's
-    matrix products release the GIL); re-raises the first failure."""
-    from threadpoolctl import threadpool_limits
-    items = list(items)
-    workers = max(1, min(16, os.cpu_count() or 1, len(items)))
-    if workers == 1:
-        return [fn(x) for x in items]
-    # one BLAS thread per worker: the rows are the parallelism
-    with threadpool_limits(limits=1), \
-            concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
-        return list(ex.map(fn, items))
+_pool_map = pool_map
 
 
 def _all_rows(wl):

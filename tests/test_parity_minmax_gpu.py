@@ -10,7 +10,8 @@ import torch
 from lookahead_sparse_kv_amd import ops
 from lookahead_sparse_kv_amd import workload as wlm
 from oracle import oasis_oracle as orc
-from parity_utils import check_scores, check_selection_row, ck_logical, minmax_tolerance
+from parity_utils import (check_scores, check_selection_row, ck_logical, minmax_tolerance,
+                          pool_map as _pool_map)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -213,17 +214,6 @@ def test_select_on_minmax_scores(name):
         nb = (wl.ctx[b] + 15) // 16
         for g in range(wl.num_kv_heads):
             check_selection_row(got[b, g], want[b, g], want_s[b, g], nb, K, f"{name} b{b} g{g}")
-
-
-def _pool_map(fn, items):
-    import concurrent.futures
-    import os
-    from threadpoolctl import threadpool_limits
-    items = list(items)
-    workers = max(1, min(16, os.cpu_count() or 1, len(items)))
-    with threadpool_limits(limits=1), \
-            concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
-        return list(ex.map(fn, items))
 
 
 def test_minmax_full_size_every_row():
