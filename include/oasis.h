@@ -301,6 +301,30 @@ int oasis_sparse_decode_attn_ex(const oasis_shape *s, const uint16_t *q, int32_t
                                 int32_t flags, void *stream);
 
 /*
+ * oasis_sparse_decode_attn_ex without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split partials and hand-over flags live in a static device array of
+ * OASIS_ATTN_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; its address on the current device is looked up on
+ * the first call there.  Same inputs, outputs, results and launch shapes as
+ * oasis_sparse_decode_attn_ex.
+ * Errors: as oasis_sparse_decode_attn_ex, plus OASIS_ERR_NOMEM when the shape
+ * needs more than OASIS_ATTN_SCRATCH_BYTES (oasis_attn_workspace_bytes tells);
+ * OASIS_ERR_HIP if the array's address cannot be had.  The array keeps the
+ * last call's contents and nothing in it needs clearing (the hand-over flags
+ * need no initial value; the array starts at zero and each call returns its
+ * flags to zero).  Calls that overlap on one GPU (on different streams, or
+ * from different threads) share the array and race: serialise them.
+ */
+#define OASIS_ATTN_SCRATCH_BYTES (16u << 20)
+int oasis_sparse_decode_attn_noalloc(const oasis_shape *s, const uint16_t *q, int32_t n_q,
+                                     const uint16_t *k_pool, const uint16_t *v_pool,
+                                     const int32_t *page_table, const int32_t *blk, int32_t n_blk,
+                                     const int32_t *blk_logical, const int32_t *ctx_len,
+                                     float scale, uint16_t *out, int32_t flags, void *stream);
+
+/*
  * Pinned host KV pool, the tier the working set is fetched from.  The pages
  * keep the full KV cache in CPU memory and hold only a bounded working set in
  * HBM (abstract; Figure 7 caption).  oasis_hostpool_create allocates `bytes`

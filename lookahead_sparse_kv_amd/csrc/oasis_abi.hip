@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "oasis.h"
 #include "oasis_launch.h"
@@ -316,6 +317,71 @@ int oasis_sparse_decode_attn_ex(const oasis_shape *s, const uint16_t *q, int32_t
                       s->num_pages, n_q, nrq, n_blk, splits, per};
     return check_hip(oasis::launch_sparse_decode_attn(a, s->head_dim, (flags & OASIS_ATTN_SHARE_GPU) != 0,
                                                       as_stream(stream)), fn);
+}
+
+}  // extern "C"
+
+// Device-resident workspace of oasis_sparse_decode_attn_noalloc, for callers
+// that cannot allocate.  In host code the name `scratch` is only a host-side
+// stand-in for the array: its device address on each GPU comes from
+// hipGetSymbolAddress (with that GPU current), kept in g_scratch_ptr, and
+// only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[OASIS_ATTN_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void *g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
+// The current device's scratch address (looked up once per device).
+int scratch_for_current_device(void **ptr, const char *fn) {
+    int device = -1;
+    if (int e = check_hip(hipGetDevice(&device), fn)) return e;
+    if (device < 0 || device >= kMaxScratchDevices)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: device %d above the %d this library keeps scratch for",
+                    fn, device, kMaxScratchDevices);
+    std::call_once(g_scratch_once[device], [device] {
+        void *p = nullptr;
+        g_scratch_err[device] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[device] = g_scratch_err[device] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[device] != hipSuccess || !g_scratch_ptr[device])
+        return fail(OASIS_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array on device %d: %s",
+                    fn, device, hipGetErrorString(g_scratch_err[device]));
+    *ptr = g_scratch_ptr[device];
+    return OASIS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oasis_sparse_decode_attn_noalloc(const oasis_shape *s, const uint16_t *q, int32_t n_q,
+                                     const uint16_t *k_pool, const uint16_t *v_pool,
+                                     const int32_t *page_table, const int32_t *blk, int32_t n_blk,
+                                     const int32_t *blk_logical, const int32_t *ctx_len,
+                                     float scale, uint16_t *out, int32_t flags, void *stream) {
+    const char *fn = "oasis_sparse_decode_attn_noalloc";
+    if (int e = check_shape(s, fn)) return e;
+    if (flags & ~OASIS_ATTN_SHARE_GPU) return fail(OASIS_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
+    if (n_q < 1) return fail(OASIS_ERR_INVALID, "%s: n_q %d < 1", fn, n_q);
+    if (n_blk < 1) return fail(OASIS_ERR_INVALID, "%s: n_blk %d < 1", fn, n_blk);
+    const size_t need = oasis_attn_workspace_bytes(s, n_q, n_blk);
+    if (need == 0)       // nothing to do, or a shape the attention call refuses: it says which
+        return oasis_sparse_decode_attn_ex(s, q, n_q, k_pool, v_pool, page_table, blk, n_blk,
+                                           blk_logical, ctx_len, scale, out, nullptr, 0, flags,
+                                           stream);
+    if (need > OASIS_ATTN_SCRATCH_BYTES)
+        return fail(OASIS_ERR_NOMEM, "%s: this shape needs %zu bytes of workspace, above the %u "
+                    "bytes of the static scratch array; call oasis_sparse_decode_attn with a "
+                    "workspace of your own", fn, need, (unsigned)OASIS_ATTN_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (int e = scratch_for_current_device(&ws, fn)) return e;
+    return oasis_sparse_decode_attn_ex(s, q, n_q, k_pool, v_pool, page_table, blk, n_blk,
+                                       blk_logical, ctx_len, scale, out, ws,
+                                       OASIS_ATTN_SCRATCH_BYTES, flags, stream);
 }
 
 int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const uint16_t *q,

@@ -24,6 +24,7 @@ OASIS_OK, OASIS_ERR_INVALID, OASIS_ERR_UNSUPPORTED, OASIS_ERR_NOMEM, OASIS_ERR_H
 EXPORTS = ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax", "oasis_select_topk", "oasis_plan_fetch", "oasis_select_plan",
            "oasis_select_plan_ex",
            "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_sparse_decode_attn_ex",
+           "oasis_sparse_decode_attn_noalloc",
            "oasis_hostpool_create",
            "oasis_hostpool_device_pointer", "oasis_hostpool_destroy", "oasis_fetch_blocks",
            "oasis_layer_step", "oasis_status_string", "oasis_last_error", "oasis_version")
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(OasisStepSync)]
         L.oasis_sparse_decode_attn_ex.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz,
                                                   i32, p]
+        L.oasis_sparse_decode_attn_noalloc.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p,
+                                                       i32, p]
         L.oasis_hostpool_create.argtypes = [sz, ctypes.POINTER(ctypes.c_void_p)]
         L.oasis_hostpool_device_pointer.argtypes = [p, ctypes.POINTER(ctypes.c_void_p)]
         L.oasis_hostpool_destroy.argtypes = [p]
@@ -98,7 +101,7 @@ def lib() -> ctypes.CDLL:
                    "oasis_select_topk", "oasis_plan_fetch",
                    "oasis_select_plan", "oasis_select_plan_ex", "oasis_layer_step",
                    "oasis_sparse_decode_attn",
-                   "oasis_sparse_decode_attn_ex",
+                   "oasis_sparse_decode_attn_ex", "oasis_sparse_decode_attn_noalloc",
                    "oasis_hostpool_create",
                    "oasis_hostpool_device_pointer", "oasis_hostpool_destroy",
                    "oasis_fetch_blocks"):
@@ -344,6 +347,34 @@ def sparse_decode_attn(shape: OasisShape, q, k_pool, v_pool, page_table, blk, bl
         _check(lib().oasis_sparse_decode_attn_ex(*args, flags, _stream(stream)))
     else:
         _check(lib().oasis_sparse_decode_attn(*args, _stream(stream)))
+    return out
+
+
+OASIS_ATTN_SCRATCH_BYTES = 16 << 20
+
+
+def sparse_decode_attn_noalloc(shape: OasisShape, q, k_pool, v_pool, page_table, blk, blk_logical,
+                               ctx_len, out, scale=None, stream=None, flags=0):
+    """sparse_decode_attn without a workspace: the library's static per-GPU
+    scratch array (OASIS_ATTN_SCRATCH_BYTES) holds the partials; nothing is
+    allocated.  Calls that overlap on one GPU race on that array."""
+    if blk is None and blk_logical is None:
+        raise ValueError("blk_logical: blk and blk_logical are both None")
+    n_blk = (blk if blk is not None else blk_logical).shape[-1]
+    B, Hkv, D = shape.batch, shape.num_kv_heads, shape.head_dim
+    n_q = q.shape[1]
+    _check_tensors((q, "q", _BF16, _numel(B, n_q, shape.num_q_heads, D)),
+                   (k_pool, "k_pool", _BF16, _numel(shape.num_pages, Hkv, BLOCK_SIZE, D)),
+                   (v_pool, "v_pool", _BF16, _numel(shape.num_pages, Hkv, BLOCK_SIZE, D)),
+                   (page_table, "page_table", _I32, B * shape.table_width),
+                   (blk, "blk", _I32, B * Hkv * n_blk, True),
+                   (blk_logical, "blk_logical", _I32, B * Hkv * n_blk, blk is not None),
+                   (ctx_len, "ctx_len", _I32, B),
+                   (out, "out", _BF16, _numel(B, n_q, shape.num_q_heads, D)))
+    scale = float(D) ** -0.5 if scale is None else scale
+    _check(lib().oasis_sparse_decode_attn_noalloc(
+        ctypes.byref(shape), _ptr(q), n_q, _ptr(k_pool), _ptr(v_pool), _ptr(page_table), _ptr(blk),
+        n_blk, _ptr(blk_logical), _ptr(ctx_len), scale, _ptr(out), flags, _stream(stream)))
     return out
 
 

@@ -108,6 +108,25 @@ def test_select_and_plan_reject_bad_arguments():
     assert plan(8, 2, fb=None) == ops.OASIS_ERR_INVALID
 
 
+def test_attn_noalloc_argument_checks():
+    # host-side validation only, all before the scratch array is looked up
+    L = ops.lib()
+    na = lambda shape, n_q=1, n_blk=128, flags=0: L.oasis_sparse_decode_attn_noalloc(
+        ctypes.byref(shape), P, n_q, P, P, P, P, n_blk, P, P, 0.088, P, flags, None)
+    s = _shape(batch=16, num_q_heads=32, num_kv_heads=8, table_width=2048, num_pages=32768)
+    assert ops.attn_workspace_bytes(s, 1, 128) <= ops.OASIS_ATTN_SCRATCH_BYTES
+    # 16,384 rows: 68 MB of partials, above the 16 MiB array
+    big = _shape(batch=2048, num_q_heads=32, num_kv_heads=8, table_width=2048, num_pages=32768)
+    assert ops.attn_workspace_bytes(big, 1, 128) > ops.OASIS_ATTN_SCRATCH_BYTES
+    assert na(big) == ops.OASIS_ERR_NOMEM
+    assert "static scratch" in ops.last_error()
+    assert na(s, n_q=9) == ops.OASIS_ERR_UNSUPPORTED        # 9 * 4 query rows > 32
+    assert na(s, n_blk=0) == ops.OASIS_ERR_INVALID
+    assert na(s, flags=4) == ops.OASIS_ERR_INVALID
+    assert na(_shape(block_size=8)) == ops.OASIS_ERR_UNSUPPORTED
+    assert na(_shape(batch=0)) == ops.OASIS_OK
+
+
 def test_attn_workspace_and_argument_checks():
     L = ops.lib()
     s = _shape(batch=16, num_q_heads=32, num_kv_heads=8, table_width=2048, num_pages=32768)
