@@ -265,7 +265,7 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
  * together).
  * A row with no valid token outputs zeros.  bf16 in and out, fp32 softmax and
  * accumulation.  Requires D in {64, 128}, bs = 16, 1 <= n_q, n_q * G <= 32,
- * n_blk >= 1, scale > 0, q, k_pool, v_pool and workspace 16-byte aligned, and
+ * 1 <= n_blk <= 65536, scale > 0, q, k_pool, v_pool and workspace 16-byte aligned, and
  * workspace_bytes >= oasis_attn_workspace_bytes().
  *
  * Launch shape (results agree to fp32 rounding whichever is taken), by rows

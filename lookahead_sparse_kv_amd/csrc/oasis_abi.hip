@@ -239,7 +239,7 @@ int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_
 
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk) {
     if (!s || s->batch < 0 || s->num_kv_heads <= 0 || s->num_q_heads <= 0 || s->head_dim <= 0 ||
-        n_q < 1 || n_blk < 1 || s->num_q_heads % s->num_kv_heads ||
+        n_q < 1 || n_blk < 1 || n_blk > oasis::kMaxAttnBlocks || s->num_q_heads % s->num_kv_heads ||
         (long long)s->batch * s->num_kv_heads > 65535 ||
         (long long)n_q * (s->num_q_heads / s->num_kv_heads) > oasis::kMaxAttnRowsQ)
         return 0;
@@ -286,6 +286,8 @@ int oasis_sparse_decode_attn_ex(const oasis_shape *s, const uint16_t *q, int32_t
     if (flags & ~OASIS_ATTN_SHARE_GPU) return fail(OASIS_ERR_INVALID, "%s: unknown flags 0x%x", fn, flags);
     if (n_q < 1) return fail(OASIS_ERR_INVALID, "%s: n_q %d < 1", fn, n_q);
     if (n_blk < 1) return fail(OASIS_ERR_INVALID, "%s: n_blk %d < 1", fn, n_blk);
+    if (n_blk > oasis::kMaxAttnBlocks)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: n_blk %d above %d", fn, n_blk, oasis::kMaxAttnBlocks);
     const int G = s->num_q_heads / s->num_kv_heads;
     if ((long long)n_q * G > oasis::kMaxAttnRowsQ)
         return fail(OASIS_ERR_UNSUPPORTED, "%s: n_q * group = %lld above %d", fn,

@@ -126,6 +126,7 @@ void attn_split_plan(int rows, int n_blk, int *splits, int *per_split);
 constexpr int kBlockTokens = 16;   // tokens per KV block
 constexpr int kMaxRowsQ = 16;     // lookahead rows per KV head in one MFMA tile (scoring)
 constexpr int kMaxAttnRowsQ = 32; // query rows per KV head in attention (two MFMA tiles)
+constexpr int kMaxAttnBlocks = 65536;  // list entries per row in attention (keeps the split plan's int sums in range)
 constexpr int kMaxKBlocks = 1024; // K limit of select / plan
 constexpr int kRowSelectMaxWidth = 8192;  // widest table the row select keeps in LDS
 constexpr int kFusedMaxWidth = 8192;      // fused select + plan: table width limit (LDS: 61 KiB at K = 512)
