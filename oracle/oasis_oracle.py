@@ -18,7 +18,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboasis_oracle.so")
+# OASIS_ORACLE_LIB: another build of oasis_oracle.c (the CPU tests load planted
+# mistakes this way, to show that the pins catch each of them)
+_LIB_PATH = os.environ.get("OASIS_ORACLE_LIB") or os.path.join(_HERE, "liboasis_oracle.so")
 _lib = None
 
 _D = ctypes.POINTER(ctypes.c_double)
