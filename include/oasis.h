@@ -233,12 +233,18 @@ int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_
 /*
  * Bytes of device workspace oasis_sparse_decode_attn needs for this shape:
  * room for the partial results of a row's shares (per row and share: max,
- * sum and the D-wide output of each query row), then one 32-bit hand-over
- * flag per row (B * Hkv rows), padded to 16 bytes.  The workspace needs no
- * initialisation: the two workgroups of a row exchange a per-call 32-bit
- * token (never 0, never a small integer) in the row's flag, and the one that
- * receives the token merges and sets the flag to 0.  One workspace serves one call at
- * a time.  Returns 0 for an invalid shape.
+ * sum and the D-wide output of each query row), then a 32-bit hand-over flag
+ * and a 32-bit hand-over epoch per row (B * Hkv rows each), padded to 16
+ * bytes.  The workspace needs no initialisation.  Where a row is split
+ * between two workgroups, each publishes its partial as 64-bit words that
+ * carry a tag (the call's token mixed with the row's epoch) beside each
+ * value, then reads its partner's: the one that finds its partner's words
+ * all tagged merges; when neither does, an exchange of the tag in the row's
+ * flag picks the one that waits for its partner's words.  A merging
+ * workgroup advances the row's epoch, so the tag changes from call to call
+ * even where the token does not (a call replayed from a captured graph), and
+ * words left by other calls or shapes do not carry it.  One workspace serves
+ * one call at a time.  Returns 0 for an invalid shape.
  */
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk);
 

@@ -247,9 +247,9 @@ size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_b
     const int nrq = n_q * (s->num_q_heads / s->num_kv_heads);
     int splits = 1, per = 1;
     oasis::attn_split_plan(rows, n_blk, &splits, &per);
-    // partials, then one arrival counter per row (16-byte padded)
+    // partials, then a hand-over flag and an epoch per row (16-byte padded)
     return (size_t)rows * splits * nrq * (s->head_dim + 2) * sizeof(float) +
-           (((size_t)rows * sizeof(uint32_t) + 15) & ~(size_t)15);
+           (((size_t)rows * 2 * sizeof(uint32_t) + 15) & ~(size_t)15);
 }
 
 // A token per attention call: the two workgroups of a row exchange it in the
@@ -313,8 +313,10 @@ int oasis_sparse_decode_attn_ex(const oasis_shape *s, const uint16_t *q, int32_t
     float *part_o = static_cast<float *>(workspace);
     float *part_ml = part_o + (size_t)rows * splits * nrq * s->head_dim;
     uint32_t *row_flag = reinterpret_cast<uint32_t *>(part_ml + (size_t)rows * splits * nrq * 2);
+    uint32_t *row_epoch = row_flag + rows;
     oasis::AttnArgs a{q, k_pool, v_pool, page_table, blk, blk_logical, ctx_len, out,
-                      part_o, part_ml, row_flag, next_attn_token(), scale * 1.4426950408889634f,
+                      part_o, part_ml, row_flag, row_epoch, next_attn_token(),
+                      scale * 1.4426950408889634f,
                       s->batch, s->num_q_heads, s->num_kv_heads, G, s->table_width,
                       s->num_pages, n_q, nrq, n_blk, splits, per};
     return check_hip(oasis::launch_sparse_decode_attn(a, s->head_dim, (flags & OASIS_ATTN_SHARE_GPU) != 0,

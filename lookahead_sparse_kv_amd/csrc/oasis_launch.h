@@ -63,6 +63,7 @@ struct AttnArgs {
     float *part_o;    // [rows][splits][n_rows_q][D]
     float *part_ml;   // [rows][splits][n_rows_q][2]
     uint32_t *row_flag;    // [rows] hand-over flags of a row's two workgroups (any initial value)
+    uint32_t *row_epoch;   // [rows] hand-over epochs, advanced by each call (any initial value)
     uint32_t token;        // nonzero, different from call to call
     float scale_log2;
     int batch, hq, hkv, group, width, num_pages, n_q, n_rows_q, n_blk, splits, per_split;

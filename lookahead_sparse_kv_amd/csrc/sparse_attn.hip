@@ -112,26 +112,18 @@ __device__ __forceinline__ void load_query(const AttnArgs &a, int b, int g,
     }
 }
 
-// Accumulate list entries [e0, e0 + ne) (ne <= 64) of row (b, g) into acc.
-// NE > 0: ne == NE is known at compile time, so the walk over the pairs is
-// fully unrolled and the loads and waits of consecutive pairs are scheduled
-// together (the common case: 128 listed blocks over 8 waves).
-template <int D, int NT, int NE = 0>
-__device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int b, int g,
-                                                int e0, int ne_arg, const bf16x8 (&qv)[NT][D / 32],
-                                                WaveAcc<D, NT> &acc) {
-    const int ne = NE > 0 ? NE : ne_arg;
-    constexpr int KK = D / 32;
-    constexpr int MT = D / 16;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int r16 = lane & 15;
-    const int j4 = lane >> 4;
-    const int ctx = a.ctx_len[b];
-    const float NEG_INF = -__builtin_inff();
+// Entry e0 + lane of row (b, g) (lane < ne <= 64): its page and number of
+// valid tokens (page -1 = skip).
+struct WaveEntries {
+    int page, ntok;
+};
 
-    // Entry e0 + lane: its page and number of valid tokens (page -1 = skip).
-    int my_page = -1, my_ntok = 0;
+__device__ __forceinline__ WaveEntries load_entries(const AttnArgs &a, int row, int b, int e0,
+                                                    int ne) {
+    const int lane = threadIdx.x & (kWave - 1);
+    WaveEntries w{-1, 0};
     if (lane < ne) {
+        const int ctx = a.ctx_len[b];
         const size_t e = (size_t)row * a.n_blk + e0 + lane;
         const int ent = a.blk ? a.blk[e] : e0 + lane;
         const int lg = a.blk_logical ? a.blk_logical[e] : ent;
@@ -139,9 +131,29 @@ __device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int row, int 
             const int p = a.page_table[(size_t)b * a.width + ent];
             long long nt = (long long)ctx - (long long)lg * kBlockTokens;
             nt = nt > kBlockTokens ? kBlockTokens : nt;
-            if (p >= 0 && p < a.num_pages && nt > 0) { my_page = p; my_ntok = (int)nt; }
+            if (p >= 0 && p < a.num_pages && nt > 0) { w.page = p; w.ntok = (int)nt; }
         }
     }
+    return w;
+}
+
+// Accumulate list entries [e0, e0 + ne) (ne <= 64) of row (b, g), whose pages
+// `ent` holds (load_entries), into acc.  NE > 0: ne == NE is known at compile
+// time, so the walk over the pairs is fully unrolled and the loads and waits
+// of consecutive pairs are scheduled together (the common case: 128 listed
+// blocks over 8 waves).
+template <int D, int NT, int NE = 0>
+__device__ __forceinline__ void attn_wave_range(const AttnArgs &a, int g, int ne_arg,
+                                                WaveEntries ent, const bf16x8 (&qv)[NT][D / 32],
+                                                WaveAcc<D, NT> &acc) {
+    const int ne = NE > 0 ? NE : ne_arg;
+    constexpr int KK = D / 32;
+    constexpr int MT = D / 16;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r16 = lane & 15;
+    const int j4 = lane >> 4;
+    const float NEG_INF = -__builtin_inff();
+    const int my_page = ent.page, my_ntok = ent.ntok;
 
     const size_t page_stride = (size_t)a.hkv * kBlockTokens * D;
     const size_t head_off = (size_t)g * kBlockTokens * D;       // same for K and V tiles
@@ -302,6 +314,9 @@ __global__ __launch_bounds__(kAttnWaves * kWave, NT == 1 && kAttnStages == 2 ? 2
     const int e0 = split * a.per_split;
     int ne = a.n_blk - e0;
     ne = ne < a.per_split ? ne : a.per_split;
+    // the list and page-table loads first: a wait for them then does not
+    // wait for the query load behind them
+    const WaveEntries ent = load_entries(a, row, b, e0, ne);
     bf16x8 qv[NT][D / 32];
     load_query<D, NT>(a, b, g, qv);
     WaveAcc<D, NT> acc;
@@ -313,9 +328,9 @@ __global__ __launch_bounds__(kAttnWaves * kWave, NT == 1 && kAttnStages == 2 ? 2
         for (int mt = 0; mt < MT; ++mt) acc.o[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (ne == 16)
-        attn_wave_range<D, NT, 16>(a, row, b, g, e0, 16, qv, acc);
+        attn_wave_range<D, NT, 16>(a, g, 16, ent, qv, acc);
     else
-        attn_wave_range<D, NT>(a, row, b, g, e0, ne, qv, acc);
+        attn_wave_range<D, NT>(a, g, ne, ent, qv, acc);
 
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -395,6 +410,10 @@ __device__ __forceinline__ void row_waves_to_lds(const AttnArgs &a, int row, int
     const int per = (w_end - w_begin + NW - 1) / NW;
     const int e_begin = w_begin + wave * per < w_end ? w_begin + wave * per : w_end;
     const int e_end = e_begin + per < w_end ? e_begin + per : w_end;
+    // the first chunk's list and page-table loads first: a wait for them
+    // then does not wait for the query load behind them
+    const int ne0 = e_end - e_begin < kWave ? e_end - e_begin : kWave;
+    const WaveEntries ent0 = load_entries(a, row, b, e_begin, ne0);
     bf16x8 qv[NT][D / 32];
     load_query<D, NT>(a, b, g, qv);
     WaveAcc<D, NT> acc;
@@ -406,11 +425,12 @@ __device__ __forceinline__ void row_waves_to_lds(const AttnArgs &a, int row, int
         for (int mt = 0; mt < MT; ++mt) acc.o[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (NE > 0 && e_end - e_begin == NE) {
-        attn_wave_range<D, NT, NE>(a, row, b, g, e_begin, NE, qv, acc);
+        attn_wave_range<D, NT, NE>(a, g, NE, ent0, qv, acc);
     } else {
         for (int e0 = e_begin; e0 < e_end; e0 += kWave) {
             const int ne = e_end - e0 < kWave ? e_end - e0 : kWave;
-            attn_wave_range<D, NT>(a, row, b, g, e0, ne, qv, acc);
+            attn_wave_range<D, NT>(a, g, ne, e0 == e_begin ? ent0 : load_entries(a, row, b, e0, ne),
+                                   qv, acc);
         }
     }
     const int wstride = row_attn_wave_floats(nrq, D);
@@ -482,6 +502,129 @@ __global__ __launch_bounds__(kRowAttnWaves * kWave) void attn_row_kernel(AttnArg
     }
 }
 
+#ifndef OASIS_ATTN_TAGGED
+#define OASIS_ATTN_TAGGED 1
+#endif
+
+// A partial value and the call's token in one 64-bit word, written and read
+// with single-copy-atomic device-scope accesses: a reader that finds this
+// call's token in the word has this call's value, in whatever order the
+// writer's stores landed, so no store needs to be waited for before another
+// workgroup may look.
+__device__ __forceinline__ void store_tagged(uint64_t *p, float v, uint32_t token) {
+    const uint64_t w = ((uint64_t)token << 32) | __float_as_uint(v);
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_tagged(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool has_token(uint64_t w, uint32_t token) {
+    return (uint32_t)(w >> 32) == token;
+}
+__device__ __forceinline__ float tagged_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// (max, sum, O) of the row's two shares merged in share order, then O / sum.
+__device__ __forceinline__ float merge_two(float m0, float l0, float o0, float m1, float l1, float o1) {
+    const float NEG_INF = -__builtin_inff();
+    float M = NEG_INF, L = 0.f, O = 0.f;
+    if (m0 != NEG_INF) { M = m0; L = l0; O = o0; }
+    if (m1 != NEG_INF) {
+        const float Mn = fmaxf(M, m1);
+        const float r_old = M == NEG_INF ? 0.f : exp2f(M - Mn);
+        const float r_new = exp2f(m1 - Mn);
+        L = L * r_old + l1 * r_new;
+        O = O * r_old + o1 * r_new;
+    }
+    return L > 0.f ? O / L : 0.f;
+}
+
+// Waits on another workgroup's published partial end after this many polls
+// (about 4 ms): that workgroup issued its stores before the swap this one has
+// seen, so they land within microseconds; the bound only guarantees that
+// every wave exits.  A row whose partner's words never showed up is written
+// as NaN.
+constexpr int kTaggedPolls = 1 << 16;
+
+// Two workgroups per row, hand-over by tagged partials: each workgroup merges
+// its 8 waves in LDS and publishes its (max, sum, O) as tagged words without
+// waiting for the stores to land, then swaps the tag into the row's flag.
+// The one that gets the tag back arrived second: its partner published
+// before swapping, so it polls the partner's words until every one carries
+// the tag, merges the two in share order and writes the output.  The other
+// leaves.  A workgroup waits only for a partner that has already swapped, so
+// nothing assumes that both are on the GPU at once.
+//
+// The tag of a call's words is its token mixed with the row's epoch, a word
+// of the workspace that each workgroup reads before it publishes and that the
+// merging workgroup advances after it has read both partials.  So the tag
+// changes from call to call even where the token does not (a call replayed
+// from a captured graph keeps the token it was captured with), and words an
+// earlier call or another shape left in the workspace do not carry it.  If a
+// flag happens to hold the tag already, both workgroups take themselves for
+// the second, and both merge the same two partials into the same bits.
+template <int D, int NE, int NW>
+__device__ __forceinline__ void rowsplit_tagged_tail(const AttnArgs &a, int row, int part,
+                                                     const float *red, uint32_t epoch) {
+    constexpr int EPT = (16 * D + NW * kWave - 1) / (NW * kWave);   // elements per thread, at most
+    __shared__ int is_last;
+    const int nrq = a.n_rows_q;
+    const uint32_t tag = a.token + epoch * 0x9E3779B1u;
+    uint64_t *po = reinterpret_cast<uint64_t *>(a.part_o);      // [rows][2][nrq][D]
+    uint64_t *pml = reinterpret_cast<uint64_t *>(a.part_ml);    // [rows][2][nrq][2]
+    const int other = 1 - part;
+    float myM[EPT], myL[EPT], myO[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int idx = threadIdx.x + k * NW * kWave;
+        if (idx < nrq * D) {
+            const int c = idx / D;
+            const int d = idx - c * D;
+            lds_merge_waves<D, NW>(red, nrq, c, d, myM[k], myL[k], myO[k]);
+            const size_t slot = ((size_t)row * 2 + part) * nrq + c;
+            store_tagged(po + slot * D + d, myO[k], tag);
+            if (d == 0) {
+                store_tagged(pml + 2 * slot, myM[k], tag);
+                store_tagged(pml + 2 * slot + 1, myL[k], tag);
+            }
+        }
+    }
+    __syncthreads();                        // every thread's stores are issued
+    if (threadIdx.x == 0) {
+        const uint32_t seen = __hip_atomic_exchange(a.row_flag + row, tag, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        is_last = seen == tag;
+    }
+    __syncthreads();
+    if (!is_last) return;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int idx = threadIdx.x + k * NW * kWave;
+        if (idx < nrq * D) {
+            const int c = idx / D;
+            const int d = idx - c * D;
+            const size_t slot = ((size_t)row * 2 + other) * nrq + c;
+            uint64_t oO = 0, oM = 0, oL = 0;
+            bool ok = false;
+            for (int poll = 0; poll < kTaggedPolls && !ok; ++poll) {
+                if (poll) __builtin_amdgcn_s_sleep(2);
+                oO = load_tagged(po + slot * D + d);
+                oM = load_tagged(pml + 2 * slot);
+                oL = load_tagged(pml + 2 * slot + 1);
+                ok = has_token(oO, tag) && has_token(oM, tag) && has_token(oL, tag);
+            }
+            const float m1 = tagged_value(oM), l1 = tagged_value(oL), o1 = tagged_value(oO);
+            const float res = !ok ? __builtin_nanf("")
+                              : part == 0 ? merge_two(myM[k], myL[k], myO[k], m1, l1, o1)
+                                          : merge_two(m1, l1, o1, myM[k], myL[k], myO[k]);
+            store_out(a, row, c, d, D, res);
+        }
+    }
+    if (threadIdx.x == 0) {
+        // the row's next call gets another tag; its flag no longer matters
+        __hip_atomic_fetch_add(a.row_epoch + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // Two workgroups per row (rows too few to fill the CUs one per row):
 // workgroup s walks entries [s * per_split, (s + 1) * per_split) with 8 waves
 // merged in LDS, and publishes its (max, sum, O) partial with device-scope
@@ -505,8 +648,17 @@ __global__ __launch_bounds__(NW * kWave) void attn_rowsplit_kernel(AttnArgs a) {
     const float NEG_INF = -__builtin_inff();
     const int w_begin = part * a.per_split < a.n_blk ? part * a.per_split : a.n_blk;
     const int w_end = w_begin + a.per_split < a.n_blk ? w_begin + a.per_split : a.n_blk;
+    __shared__ uint32_t epoch;
+    if constexpr (OASIS_ATTN_TAGGED && NT == 1) {
+        if (threadIdx.x == 0)
+            epoch = __hip_atomic_load(a.row_epoch + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     row_waves_to_lds<D, NE, NW, NT>(a, row, w_begin, w_end, red);
     __syncthreads();
+    if constexpr (OASIS_ATTN_TAGGED && NT == 1) {
+        rowsplit_tagged_tail<D, NE, NW>(a, row, part, red, epoch);
+        return;
+    }
     for (int idx = threadIdx.x; idx < nrq * D; idx += NW * kWave) {
         const int c = idx / D;
         const int d = idx - c * D;
@@ -590,8 +742,10 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share
         return hipGetLastError();
     }
     int wg_splits = 0, wg_per = 0;
-    if (row_fits && rowsplit_plan(rows, a.n_blk, &wg_splits, &wg_per) && wg_splits <= a.splits) {
-        // the workspace holds room for a.splits >= wg_splits partials per row
+    if (row_fits && rowsplit_plan(rows, a.n_blk, &wg_splits, &wg_per) &&
+        wg_splits * (OASIS_ATTN_TAGGED ? 2 : 1) <= a.splits) {
+        // the workspace holds room for a.splits partials per row of 4-byte
+        // words; the tagged hand-over stores 8-byte words for its two shares
         AttnArgs r = a;
         r.splits = wg_splits;
         r.per_split = wg_per;

@@ -131,8 +131,9 @@ def test_attn_workspace_and_argument_checks():
     L = ops.lib()
     s = _shape(batch=16, num_q_heads=32, num_kv_heads=8, table_width=2048, num_pages=32768)
     ws = ops.attn_workspace_bytes(s, 1, 128)
-    # 128 rows x 8 splits x 4 query rows x (128 + 2) floats, then 128 row counters
-    assert ws == 128 * 8 * 4 * 130 * 4 + 128 * 4
+    # 128 rows x 8 splits x 4 query rows x (128 + 2) floats, then a flag and an
+    # epoch per row
+    assert ws == 128 * 8 * 4 * 130 * 4 + 128 * 8
     assert ops.attn_workspace_bytes(s, 0, 128) == 0
     assert ops.attn_workspace_bytes(s, 1, 0) == 0
     att = lambda n_q=1, n_blk=128, wsb=ws, wsp=P, blk=P: L.oasis_sparse_decode_attn(

@@ -23,8 +23,9 @@ CASES = {
     "rows4_minmax": (dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 3000)), "minmax", True, True),
     "rows128_exact": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128, ctx=(2048, 3000)), "exact", False, True),
     "rows128_minmax": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128, ctx=(2048, 3000)), "minmax", True, True),
-    # two attention workgroups per row: the hand-over token is fixed in the graph,
-    # and each replay must leave the rows' flags ready for the next
+    # two attention workgroups per row: the call's token is fixed in the graph,
+    # so each replay's hand-over must not take the previous replay's partials
+    # for its own (the rows' epochs change the tag from replay to replay)
     "rows128_minmax_two_workgroups": (dict(batch=16, q_heads=32, kv_heads=8, head_dim=128,
                                            ctx=(2048, 3000)), "minmax", True, False),
 }
