@@ -408,6 +408,11 @@ typedef struct {
     uint16_t *out;
     void *workspace;
     size_t workspace_bytes;
+    const uint16_t *score_k_pool;      /* scoring (and the re-pooling of the last block)
+                                          reads this key pool when set, attention reads
+                                          k_pool: keys kept in two pools by step parity,
+                                          so that one step's keys can be rewritten while
+                                          the step before is attended; NULL: k_pool */
 } oasis_layer;
 
 typedef struct {

@@ -403,11 +403,12 @@ int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const ui
     }
     if (sync->score_after)
         if (int e = check_hip(hipStreamWaitEvent(ss, ev(sync->score_after), 0), fn)) return e;
+    const uint16_t *skp = L->score_k_pool ? L->score_k_pool : L->k_pool;
     int e = L->ck ? oasis_score_blocks_minmax(&L->shape, q_look_next, L->n_look, L->ck,
-                                              L->refresh ? L->k_pool : nullptr,
+                                              L->refresh ? skp : nullptr,
                                               L->refresh ? L->block_table : nullptr, L->ctx_len,
                                               L->scale, scores, ss)
-                  : oasis_score_blocks(&L->shape, q_look_next, L->n_look, L->k_pool, L->block_table,
+                  : oasis_score_blocks(&L->shape, q_look_next, L->n_look, skp, L->block_table,
                                        L->ctx_len, L->scale, scores, ss);
     if (e) return e;
     if ((e = check_hip(hipEventRecord(ev(sync->scored), ss), fn))) return e;

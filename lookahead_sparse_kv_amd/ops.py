@@ -48,7 +48,7 @@ class OasisLayer(ctypes.Structure):
                 ("last_use", ctypes.c_void_p), ("fetch_block", ctypes.c_void_p),
                 ("fetch_slot", ctypes.c_void_p), ("fetch_count", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("score_k_pool", ctypes.c_void_p)]
 
 
 class OasisStepSync(ctypes.Structure):

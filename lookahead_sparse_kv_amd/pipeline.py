@@ -84,18 +84,19 @@ class DecodeLayer:
         return self._fetch_slot_buf[:B * Hkv * self._cap].view(B, Hkv, self._cap)
 
     # individual stages -------------------------------------------------
-    def score(self, q_look, stream=None, scores=None, refresh=False):
+    def score(self, q_look, stream=None, scores=None, refresh=False, k_pool=None):
         """refresh (compressed scorer): in the same launch, first re-pool each
-        sequence's last block from the key pool (see append())."""
+        sequence's last block from the key pool (see append()).  k_pool: read
+        this key pool (same layout and block table) instead of the layer's."""
         out = self.scores if scores is None else scores
+        kp = self.k_pool if k_pool is None else k_pool
         if self.ck is not None:
             ops.score_blocks_minmax(q_look, self.ck, self.ctx_len, out,
-                                    k_pool=self.k_pool if refresh else None,
+                                    k_pool=kp if refresh else None,
                                     block_table=self.block_table if refresh else None,
                                     stream=stream)
         else:
-            ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len, out,
-                             stream=stream)
+            ops.score_blocks(q_look, kp, self.block_table, self.ctx_len, out, stream=stream)
 
     def append(self, stream=None):
         """After the caller has written each sequence's new token into the key
@@ -121,16 +122,20 @@ class DecodeLayer:
                         self.fetch_block, self.fetch_slot, self.fetch_count, stream,
                         step_dev=step_dev)
 
-    def native_desc(self, share_gpu=True, refresh=False):
+    def native_desc(self, share_gpu=True, refresh=False, k_pool=None, score_k_pool=None):
         """oasis_layer descriptor of this layer for oasis_layer_step (built once per
-        setting; every pointer in it is a buffer this layer holds)."""
-        key = (share_gpu, refresh)
+        setting; every pointer in it is a buffer this layer holds, or the key
+        pools given: k_pool for attention, score_k_pool for scoring)."""
+        kp = self.k_pool if k_pool is None else k_pool
+        key = (share_gpu, refresh, kp.data_ptr(),
+               None if score_k_pool is None else score_k_pool.data_ptr())
         cache = self.__dict__.setdefault("_native", {})
         if key not in cache:
             D = self.shape.head_dim
             vp = lambda t: None if t is None else t.data_ptr()
             cache[key] = ops.OasisLayer(
-                shape=self.shape, k_pool=vp(self.k_pool), v_pool=vp(self.v_pool),
+                shape=self.shape, k_pool=vp(kp), v_pool=vp(self.v_pool),
+                score_k_pool=vp(score_k_pool),
                 block_table=vp(self.block_table), ctx_len=vp(self.ctx_len), ck=vp(self.ck),
                 refresh=int(refresh), n_look=self.n_look, n_q=self.n_q, k_blocks=self.k_blocks,
                 cap=self.cap, attn_flags=ops.OASIS_ATTN_SHARE_GPU if share_gpu else 0,
@@ -143,11 +148,13 @@ class DecodeLayer:
         desc.cap = self.cap                     # the one field a caller changes between steps
         return desc
 
-    def attend(self, q, blocks=None, stream=None, share_gpu=False):
-        """share_gpu: another launch (the next step's scoring) runs beside this one."""
+    def attend(self, q, blocks=None, stream=None, share_gpu=False, k_pool=None):
+        """share_gpu: another launch (the next step's scoring) runs beside this one.
+        k_pool: read this key pool instead of the layer's."""
         blocks = self.slot_block if blocks is None else blocks
-        ops.sparse_decode_attn(self.shape, q, self.k_pool, self.v_pool, self.block_table, blocks,
-                               blocks, self.ctx_len, self.out, self.workspace, stream=stream,
+        ops.sparse_decode_attn(self.shape, q, self.k_pool if k_pool is None else k_pool,
+                               self.v_pool, self.block_table, blocks, blocks, self.ctx_len,
+                               self.out, self.workspace, stream=stream,
                                flags=ops.OASIS_ATTN_SHARE_GPU if share_gpu else 0)
 
     def step(self, q_look, q, step, stream=None):
@@ -177,6 +184,17 @@ class PipelinedDecode:
     its own layer's plan.  When several layers (one pipeline each) take turns,
     a layer's plan for t + 1 overlaps the attention of the layers after it.
 
+    With `k_pools` (two key pools of the layer's layout), the keys may change
+    from step to step while the steps overlap: step s is scored and attended
+    from k_pools[s % 2].  The caller brings k_pools[s % 2] to step s's keys on
+    its own stream after step(.., s - 2) has returned and before
+    step(.., s - 1) is called (whose scoring of step s waits for that
+    stream).  The pool's earlier readers, the scoring and the attention of
+    step s - 2, are then ordered before the write (the attention is on the
+    caller's stream and waited for that scoring); attention of step s - 1,
+    beside the scoring of step s, reads the other pool, which nothing writes
+    meanwhile.
+
         pipe = PipelinedDecode(layer)
         pipe.prime(q_look_0, step=0)          # score + select/plan of step 0
         for t in range(T):
@@ -185,7 +203,7 @@ class PipelinedDecode:
     """
 
     def __init__(self, layer: DecodeLayer, side=None, plan_stream=None, native=False,
-                 share_gpu=True):
+                 share_gpu=True, k_pools=None):
         """`side`: the stream the scoring runs on; `plan_stream`: the stream
         select + plan runs on (None: the caller's).  Several pipelines (one per
         layer) may share them, so that each runs layer after layer.  `native`:
@@ -209,6 +227,9 @@ class PipelinedDecode:
         self.i = 0
         self.native = native
         self.share_gpu = share_gpu
+        if k_pools is not None and len(k_pools) != 2:
+            raise ValueError("k_pools: two key pools")
+        self.k_pools = k_pools
         if native:
             # torch creates an event at its first record: create them now, so
             # that their handles can be handed to native code
@@ -216,7 +237,10 @@ class PipelinedDecode:
             for e in (*self.ev_scored, *self.ev_planned, self.ev_attended, self.ev_inputs):
                 e.record(cur)
 
-    def _score_next(self, q_look, main, ev=None, append=False):
+    def _pool(self, step):
+        return None if self.k_pools is None else self.k_pools[step % 2]
+
+    def _score_next(self, q_look, main, ev=None, append=False, step=0):
         b = self.i % 2
         # The caller writes this step's inputs (the lookahead query, ctx_len, an
         # appended key) on its own stream just before the call: scoring waits
@@ -229,7 +253,8 @@ class PipelinedDecode:
         if ev:
             ev[0].record(self.side)
         # append: the compressed keys of the last blocks are refreshed in the launch
-        self.L.score(q_look, stream=self.side, scores=self.buf[b], refresh=append)
+        self.L.score(q_look, stream=self.side, scores=self.buf[b], refresh=append,
+                     k_pool=self._pool(step))
         if ev:
             ev[1].record(self.side)
         self.ev_scored[b].record(self.side)
@@ -252,7 +277,7 @@ class PipelinedDecode:
 
     def prime(self, q_look, step, append=False):
         main = torch.cuda.current_stream()
-        b = self._score_next(q_look, main, append=append)
+        b = self._score_next(q_look, main, append=append, step=step)
         self._plan(b, step, main)
 
     def step(self, q, q_look_next, step, copy_out=True, score_events=None, append=False):
@@ -270,8 +295,8 @@ class PipelinedDecode:
             return None
         if self.plan_stream is not None and self.last_plan is not None:
             main.wait_event(self.last_plan)             # the working set of `step`
-        b = self._score_next(q_look_next, main, score_events, append)
-        self.L.attend(q, stream=main, share_gpu=self.share_gpu)
+        b = self._score_next(q_look_next, main, score_events, append, step=step + 1)
+        self.L.attend(q, stream=main, share_gpu=self.share_gpu, k_pool=self._pool(step))
         out = self.L.out.clone() if copy_out else None
         self._plan(b, step + 1, main, after_attention=True)
         return out
@@ -291,8 +316,9 @@ class PipelinedDecode:
                                  attn_after=h(attn_after), scored=h(self.ev_scored[b]),
                                  attended=h(self.ev_attended), planned=h(self.ev_planned[b]),
                                  inputs=h(self.ev_inputs))
-        ops.layer_step(self.L.native_desc(share_gpu=self.share_gpu, refresh=append), q_look_next, q,
-                       self.buf[b], step + 1, sync)
+        desc = self.L.native_desc(share_gpu=self.share_gpu, refresh=append,
+                                  k_pool=self._pool(step), score_k_pool=self._pool(step + 1))
+        ops.layer_step(desc, q_look_next, q, self.buf[b], step + 1, sync)
         self.last_plan = self.ev_planned[b]
         self.used[b] = True
         self.i += 1

@@ -1241,6 +1241,72 @@ def test_host_tier_matches_full_pool_over_layers_and_steps(scorer):
 
 
 # ---------------------------------------------------------------- multi-step workloads at full size
+def _drift_deltas(wl, d, steps, seed):
+    """Per step t: the key tiles the drift rewrites, (pages, heads, tiles), with
+    the tiles as they are after step t (drift_step applied to d in turn)."""
+    out = []
+    for t in range(steps):
+        pages, heads = wlm.drift_step(wl, d, seed + t)
+        out.append((pages, heads, d["k_pool"][pages, heads].clone()))
+    return out
+
+
+@pytest.mark.parametrize("native", [False, True])
+def test_pipelined_drift_with_two_key_pools_matches_plain_steps(native):
+    """Hot blocks drifting every step, steps overlapped (attention of step t
+    beside the scoring of t + 1) over two key pools by step parity, with the
+    benchmark's schedule: right after step t is enqueued, the caller's stream
+    rewrites the pool step t read into step t + 2's keys.  Outputs, selections
+    and the working-set table equal the plain order with the keys updated in
+    place, bit for bit."""
+    wl = wlm.small_workload(batch=2, q_heads=32, kv_heads=8, head_dim=128, ctx=(8192, 6000),
+                            budget=512, n_hot=16, ratio=0.0625, drift=4, seed=49)
+    d = wlm.make_layer(wl)
+    T = 7
+    k0 = d["k_pool"].clone()                                   # keys before step 0
+    deltas = _drift_deltas(wl, d, T + 1, 900)
+    looks = [dev(wlm.draw_lookahead(wl, d["q32"], 950 + t).to(torch.bfloat16)) for t in range(T + 1)]
+    q = dev(d["q"].unsqueeze(1))
+    sb, lu = (x.numpy() for x in wlm.empty_state(wl))
+    apply = lambda pool, t: pool.index_put_((dev(deltas[t][0]), dev(deltas[t][1])), dev(deltas[t][2]))
+
+    seq = DecodeLayer(k_pool=dev(k0), v_pool=dev(d["v_pool"]), block_table=dev(d["block_table"]),
+                      ctx_len=dev(d["ctx_len"]), num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks,
+                      cap=wl.cap(), slot_block=torch.from_numpy(sb), last_use=torch.from_numpy(lu))
+    want = []
+    for t in range(T):
+        apply(seq.k_pool, t)
+        seq.step(looks[t], q, t)
+        want.append(seq.out.clone())
+    apply(seq.k_pool, T)
+    seq.score(looks[T])
+    seq.select_plan(T)
+
+    pools = [dev(k0), dev(k0)]
+    lay = DecodeLayer(k_pool=pools[0], v_pool=dev(d["v_pool"]), block_table=dev(d["block_table"]),
+                      ctx_len=dev(d["ctx_len"]), num_q_heads=wl.num_q_heads, k_blocks=wl.k_blocks,
+                      cap=wl.cap(), slot_block=torch.from_numpy(sb), last_use=torch.from_numpy(lu))
+    pipe = PipelinedDecode(lay, plan_stream=torch.cuda.Stream(), k_pools=pools, native=native)
+    apply(pools[0], 0)                                         # step 0's keys
+    apply(pools[1], 0)
+    apply(pools[1], 1)                                         # step 1's keys
+    pipe.prime(looks[0], 0)
+    got = []
+    for t in range(T):
+        pipe.step(q, looks[t + 1], t, copy_out=False)
+        got.append(lay.out.clone())
+        if t + 2 <= T:                                         # step t's pool -> step t + 2's keys
+            apply(pools[t % 2], t + 1)
+            apply(pools[t % 2], t + 2)
+    pipe.drain()
+    torch.cuda.synchronize()
+    for t in range(T):
+        assert torch.equal(got[t], want[t]), t
+    for k in ("sel", "slot_block", "last_use", "fetch_count"):
+        assert torch.equal(getattr(lay, k), getattr(seq, k)), k
+    assert torch.equal(pools[T % 2], seq.k_pool)
+
+
 def test_drifting_hot_blocks_131k_every_step_and_row():
     """Llama-3.1-8B-shaped 131K context (4 sequences, 32 rows of 8,192 blocks)
     with hot blocks drifting by up to 4 blocks per step, all 64 steps of the
