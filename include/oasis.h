@@ -231,6 +231,29 @@ int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_
                          void *stream);
 
 /*
+ * Top-K (and the plan) of rows of up to 65,536 blocks and more, with a
+ * workspace.  Rows of at most 8,192 blocks take the one-pass kernels of
+ * oasis_select_plan (the workspace is then not needed; pass NULL).  Wider
+ * rows take two passes: each row is split into chunks of at least 2,048
+ * blocks, one workgroup per chunk writes the chunk's top-K to the workspace
+ * as candidates, then one workgroup per row selects the top-K of its
+ * candidates (every block of the row's top-K is among its chunk's top-K, and
+ * candidates are kept in block order, so ties still go to the lower block)
+ * and plans it.  Results are those of oasis_select_topk / oasis_plan_fetch.
+ * slot_block == NULL selects only (last_use, fetch_block, fetch_slot,
+ * fetch_count and cap are then unused).  Requires 1 <= k_blocks <= 1024,
+ * table_width <= 8192 * (8192 / k_blocks) (65,536 at k_blocks = 1024), and a
+ * workspace of oasis_select_workspace_bytes() bytes, 8-byte aligned, any
+ * contents (OASIS_ERR_NOMEM if smaller).  step_dev as in oasis_select_plan_ex.
+ */
+size_t oasis_select_workspace_bytes(const oasis_shape *s, int32_t k_blocks);
+int oasis_select_plan_ws(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                         int32_t k_blocks, int32_t cap, int32_t step, const int32_t *step_dev,
+                         int32_t *sel, int32_t *slot_block, int32_t *last_use,
+                         int32_t *fetch_block, int32_t *fetch_slot, int32_t *fetch_count,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace oasis_sparse_decode_attn needs for this shape:
  * room for the partial results of a row's shares (per row and share: max,
  * sum and the D-wide output of each query row), then a 32-bit hand-over flag
@@ -392,7 +415,7 @@ int oasis_fetch_blocks(const oasis_shape *s, const uint16_t *host_k, const uint1
  *                 q over the working set slot_block (full-pool mode: the block
  *                 table as page table); record attended if plan_stream differs
  *   plan_stream:  if it differs from attn_stream, wait attended; wait scored;
- *                 oasis_select_plan(step) from scores; record planned
+ *                 oasis_select_plan_ws(step) from scores; record planned
  *
  * and nothing else: the results are those of the three calls in that order.
  * Errors: the first failing call's status; the calls before it stay enqueued.
@@ -413,6 +436,9 @@ typedef struct {
                                           k_pool: keys kept in two pools by step parity,
                                           so that one step's keys can be rewritten while
                                           the step before is attended; NULL: k_pool */
+    void *select_workspace;            /* oasis_select_plan_ws workspace (NULL where the
+                                          table width needs none) */
+    size_t select_workspace_bytes;
 } oasis_layer;
 
 typedef struct {

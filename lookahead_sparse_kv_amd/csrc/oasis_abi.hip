@@ -237,6 +237,62 @@ int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_
     return check_hip(oasis::launch_row_select_plan(a, 2, as_stream(stream)), fn);
 }
 
+size_t oasis_select_workspace_bytes(const oasis_shape *s, int32_t k_blocks) {
+    if (!s || s->batch < 0 || s->num_kv_heads <= 0 || s->table_width < 0 || k_blocks < 1 ||
+        k_blocks > oasis::kMaxKBlocks || (long long)s->batch * s->num_kv_heads > 65535 ||
+        s->table_width <= oasis::kTwoPassMinWidth ||
+        s->table_width > oasis::two_pass_max_width(k_blocks))
+        return 0;
+    int cw = 0, chunks = 0;
+    oasis::two_pass_plan(s->table_width, k_blocks, &cw, &chunks);
+    return (size_t)s->batch * s->num_kv_heads * chunks * k_blocks * 8;
+}
+
+int oasis_select_plan_ws(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                         int32_t k_blocks, int32_t cap, int32_t step, const int32_t *step_dev,
+                         int32_t *sel, int32_t *slot_block, int32_t *last_use,
+                         int32_t *fetch_block, int32_t *fetch_slot, int32_t *fetch_count,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "oasis_select_plan_ws";
+    if (int e = check_shape(s, fn)) return e;
+    if (k_blocks < 1) return fail(OASIS_ERR_INVALID, "%s: k_blocks %d < 1", fn, k_blocks);
+    if (k_blocks > oasis::kMaxKBlocks)
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: k_blocks %d above %d", fn, k_blocks,
+                    oasis::kMaxKBlocks);
+    const bool plan = slot_block != nullptr;
+    if (plan && (cap < 0 || cap > k_blocks))
+        return fail(OASIS_ERR_INVALID, "%s: cap %d outside [0, k_blocks = %d]", fn, cap, k_blocks);
+    if (s->table_width > oasis::two_pass_max_width(k_blocks))
+        return fail(OASIS_ERR_UNSUPPORTED, "%s: table_width %d above %lld for k_blocks %d", fn,
+                    s->table_width, oasis::two_pass_max_width(k_blocks), k_blocks);
+    if (s->batch == 0) return ok();
+    if (!scores || !ctx_len || !sel) return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
+    if (plan && (!last_use || !fetch_count || (cap > 0 && (!fetch_block || !fetch_slot))))
+        return fail(OASIS_ERR_INVALID, "%s: NULL plan buffer", fn);
+    if (s->table_width <= oasis::kTwoPassMinWidth) {      // one pass; no workspace needed
+        if (plan)
+            return oasis_select_plan_ex(s, scores, ctx_len, k_blocks, cap, step, step_dev, sel,
+                                        slot_block, last_use, fetch_block, fetch_slot, fetch_count,
+                                        stream);
+        return oasis_select_topk(s, scores, ctx_len, k_blocks, sel, stream);
+    }
+    const size_t need = oasis_select_workspace_bytes(s, k_blocks);
+    if (!workspace || workspace_bytes < need)
+        return fail(OASIS_ERR_NOMEM, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 8)
+        return fail(OASIS_ERR_INVALID, "%s: workspace must be 8-byte aligned", fn);
+    const int rows = s->batch * s->num_kv_heads;
+    int cw = 0, chunks = 0;
+    oasis::two_pass_plan(s->table_width, k_blocks, &cw, &chunks);
+    uint32_t *cand_key = static_cast<uint32_t *>(workspace);
+    int32_t *cand_idx = reinterpret_cast<int32_t *>(cand_key + (size_t)rows * chunks * k_blocks);
+    oasis::SelectPlanArgs a{scores, ctx_len, sel, slot_block, last_use, fetch_block, fetch_slot,
+                            fetch_count, rows, s->num_kv_heads, s->table_width, k_blocks,
+                            plan ? cap : 0, step, step_dev};
+    return check_hip(oasis::launch_two_pass_select_plan(a, plan ? 3 : 1, cand_key, cand_idx,
+                                                        as_stream(stream)), fn);
+}
+
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk) {
     if (!s || s->batch < 0 || s->num_kv_heads <= 0 || s->num_q_heads <= 0 || s->head_dim <= 0 ||
         n_q < 1 || n_blk < 1 || n_blk > oasis::kMaxAttnBlocks || s->num_q_heads % s->num_kv_heads ||
@@ -424,9 +480,10 @@ int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const ui
         if ((e = check_hip(hipStreamWaitEvent(ps, ev(sync->attended), 0), fn))) return e;
     }
     if ((e = check_hip(hipStreamWaitEvent(ps, ev(sync->scored), 0), fn))) return e;
-    if ((e = oasis_select_plan(&L->shape, scores, L->ctx_len, L->k_blocks, L->cap, step, L->sel,
-                               L->slot_block, L->last_use, L->fetch_block, L->fetch_slot,
-                               L->fetch_count, ps)))
+    if ((e = oasis_select_plan_ws(&L->shape, scores, L->ctx_len, L->k_blocks, L->cap, step,
+                                  nullptr, L->sel, L->slot_block, L->last_use, L->fetch_block,
+                                  L->fetch_slot, L->fetch_count, L->select_workspace,
+                                  L->select_workspace_bytes, ps)))
         return e;
     if (sync->planned)
         if ((e = check_hip(hipEventRecord(ev(sync->planned), ps), fn))) return e;

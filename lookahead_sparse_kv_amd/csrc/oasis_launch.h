@@ -39,6 +39,18 @@ struct SelectPlanArgs {
     const int32_t *step_dev;   // if set, *step_dev is added to step (read on the device)
 };
 
+// Candidates of the two-pass selection of wide rows: each row split into
+// `chunks` chunks of chunk_w blocks; per (row, chunk) the chunk's top-K as
+// order-preserving keys and block indices, in ascending block order, padded
+// with key 0 and index -1.
+struct ChunkArgs {
+    const float *scores;
+    const int32_t *ctx_len;
+    uint32_t *cand_key;    // [rows][chunks][k]
+    int32_t *cand_idx;     // [rows][chunks][k]
+    int rows, hkv, width, k, chunk_w, chunks;
+};
+
 struct FetchArgs {
     const uint16_t *host_k;       // device-mapped pinned host pool, [B][Hkv][host_blocks][bs*D], key tiles in slices
     const uint16_t *host_v;       // [B][Hkv][host_blocks][D][bs]
@@ -118,6 +130,19 @@ constexpr int kWideRowMinWidth = OASIS_WIDE_ROW_MIN_WIDTH;
 namespace wide {
 hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
 }
+// Two-pass selection (and plan) of rows wider than kTwoPassMinWidth blocks:
+// the chunk kernel, then one workgroup per row over the candidates.
+void two_pass_plan(int width, int k, int *chunk_w, int *chunks);
+hipError_t launch_two_pass_select_plan(const SelectPlanArgs &a, int mode, uint32_t *cand_key,
+                                       int32_t *cand_idx, hipStream_t stream);
+namespace wide {
+hipError_t launch_chunk_select(const ChunkArgs &a, hipStream_t stream);
+hipError_t launch_merge_select_plan(const SelectPlanArgs &a, int mode, const uint32_t *cand_key,
+                                    const int32_t *cand_idx, int ncand, hipStream_t stream);
+}
+hipError_t launch_chunk_select(const ChunkArgs &a, hipStream_t stream);
+hipError_t launch_merge_select_plan(const SelectPlanArgs &a, int mode, const uint32_t *cand_key,
+                                    const int32_t *cand_idx, int ncand, hipStream_t stream);
 hipError_t launch_fetch_blocks(const FetchArgs &a, int head_dim, hipStream_t stream);
 hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share_gpu, hipStream_t stream);
 
@@ -133,5 +158,16 @@ constexpr int kRowSelectMaxWidth = 8192;  // widest table the row select keeps i
 constexpr int kFusedMaxWidth = 8192;      // fused select + plan: table width limit (LDS: 61 KiB at K = 512)
 constexpr int kFusedMaxK = 512;           // fused select + plan: K limit
 constexpr int kMaxSelectWidth = 15360;   // keys of a row staged in LDS (60 KiB)
+constexpr int kMaxCandidates = 8192;     // candidates of a row in the two-pass selection (LDS)
+constexpr int kMinChunkWidth = 2048;     // blocks per chunk of the two-pass selection, at least
+// widest row of the two-pass selection: chunks of at most kRowSelectMaxWidth
+// blocks, at most kMaxCandidates / K of them
+__host__ __device__ constexpr long long two_pass_max_width(int k) {
+    return (long long)kRowSelectMaxWidth * (kMaxCandidates / (k > 0 ? k : 1));
+}
+#ifndef OASIS_TWO_PASS_MIN_WIDTH
+#define OASIS_TWO_PASS_MIN_WIDTH 8192    // up to here one fused launch is faster (16.1 against 22 us at 8,192)
+#endif
+constexpr int kTwoPassMinWidth = OASIS_TWO_PASS_MIN_WIDTH;   // rows wider than this: two passes
 
 }  // namespace oasis

@@ -64,12 +64,163 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
     }
 }
 
+// Pass 1 of the two-pass selection: workgroup (row, c) selects the exact
+// top-K of blocks [c * chunk_w, (c + 1) * chunk_w) of the row's valid blocks
+// and writes them as candidates (keys and block indices, ascending, padded).
+__global__ __launch_bounds__(kRowThreads) void row_chunk_select_kernel(ChunkArgs a) {
+    extern __shared__ int dyn[];
+    __shared__ RowShared sh;
+    constexpr int U = 8;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x / a.chunks;
+    const int c = blockIdx.x - row * a.chunks;
+    const int K = a.k;
+    int *sel = dyn;                                               // plan_pad(K)
+    uint32_t *keys = reinterpret_cast<uint32_t *>(dyn + plan_pad(K));   // chunk_w
+    const int n0 = c * a.chunk_w;
+    const float *srow = a.scores + (size_t)row * a.width + n0;
+    const int span = a.width - n0 < a.chunk_w ? a.width - n0 : a.chunk_w;
+    const int ctx_raw = a.ctx_len[row / a.hkv];
+    const int ctx = ctx_raw < 0 ? 0 : ctx_raw;
+    const int cb = ctx / kBlockTokens + (ctx % kBlockTokens != 0);   // ceil, no overflow
+    const int nb = cb > a.width ? a.width : cb;
+    const int len = nb - n0 < 0 ? 0 : (nb - n0 < span ? nb - n0 : span);
+    // the chunk's keys: U loads per thread in flight, from indices clamped
+    // into the chunk
+    for (int i0 = 0; i0 < len; i0 += U * kRowThreads) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kRowThreads + tid;
+            v[u] = srow[i < len ? i : len - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kRowThreads + tid;
+            if (i < len) keys[i] = score_key(v[u]);
+        }
+    }
+    __syncthreads();
+    row_select(keys, len, K, sel, sh);
+    uint32_t *ck = a.cand_key + ((size_t)row * a.chunks + c) * K;
+    int32_t *ci = a.cand_idx + ((size_t)row * a.chunks + c) * K;
+    for (int i = tid; i < K; i += kRowThreads) {
+        const int s = sel[i];
+        ck[i] = s >= 0 ? keys[s] : 0u;
+        ci[i] = s >= 0 ? n0 + s : -1;
+    }
+}
+
+// Pass 2: one workgroup per row selects the top-K of the row's `ncand`
+// candidates (the chunks' top-K sets in chunk order, so positions ascend with
+// block index and the lower position wins a tie exactly when the lower block
+// does) and, with MODE 3, plans it as the fused kernel does.  Every block of
+// the row's top-K is among its chunk's top-K, so the result is the row's.
+template <int MODE>
+__global__ __launch_bounds__(kRowThreads) void row_merge_select_plan_kernel(
+        SelectPlanArgs a, const uint32_t *cand_key, const int32_t *cand_idx, int ncand) {
+    extern __shared__ int dyn[];
+    __shared__ RowShared sh;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const int K = a.k;
+    const int Kp = plan_pad(K);
+    int *sel = dyn;                                               // Kp
+    int *pl = sel + Kp;                                           // 9 Kp (plan)
+    uint32_t *keys = reinterpret_cast<uint32_t *>(MODE & 2 ? pl + 9 * Kp : pl);   // ncand
+    const size_t rk = (size_t)row * K;
+    PlanPrefetch pf;
+    if (MODE & 2) plan_prefetch(a.slot_block + rk, a.last_use + rk, K, pf);
+    const int ctx_raw = a.ctx_len[row / a.hkv];
+    const int ctx = ctx_raw < 0 ? 0 : ctx_raw;
+    const int cb = ctx / kBlockTokens + (ctx % kBlockTokens != 0);
+    const int nb = cb > a.width ? a.width : cb;
+    const uint32_t *rk_key = cand_key + (size_t)row * ncand;
+    const int32_t *rk_idx = cand_idx + (size_t)row * ncand;
+    if (nb <= K) {
+        for (int i = tid; i < K; i += kRowThreads) sel[i] = i < nb ? i : -1;
+        __syncthreads();
+    } else {
+        for (int i = tid; i < ncand; i += kRowThreads) keys[i] = rk_key[i];
+        __syncthreads();
+        row_select(keys, ncand, K, sel, sh);
+        // positions -> blocks (positions ascend with block index; a position
+        // padded with key 0 is never taken: there are at least K valid ones)
+        for (int i = tid; i < K; i += kRowThreads) {
+            const int p = sel[i];
+            sel[i] = p >= 0 ? rk_idx[p] : -1;
+        }
+        __syncthreads();
+    }
+    if (a.sel)
+        for (int i = tid; i < K; i += kRowThreads) a.sel[rk + i] = sel[i];
+    if (MODE & 2) {
+        const int step = a.step + (a.step_dev ? *a.step_dev : 0);
+        const float *srow = a.scores + (size_t)row * a.width;
+        row_plan(sel, [&](int s) { return srow[s]; }, K, a.cap, step, pf, a.slot_block + rk,
+                 a.last_use + rk, a.fetch_block + (size_t)row * a.cap,
+                 a.fetch_slot + (size_t)row * a.cap, a.fetch_count + row, pl, sh);
+    }
+}
+
+hipError_t launch_chunk_select(const ChunkArgs &a, hipStream_t stream) {
+    const size_t lds = (size_t)(plan_pad(a.k) + a.chunk_w) * 4;
+    hipLaunchKernelGGL(row_chunk_select_kernel, dim3(a.rows * a.chunks), dim3(kRowThreads), lds,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_select_plan(const SelectPlanArgs &a, int mode, const uint32_t *cand_key,
+                                    const int32_t *cand_idx, int ncand, hipStream_t stream) {
+    const int Kp = plan_pad(a.k);
+    if (mode == 3)
+        hipLaunchKernelGGL(row_merge_select_plan_kernel<3>, dim3(a.rows), dim3(kRowThreads),
+                           (size_t)(10 * Kp + ncand) * 4, stream, a, cand_key, cand_idx, ncand);
+    else
+        hipLaunchKernelGGL(row_merge_select_plan_kernel<1>, dim3(a.rows), dim3(kRowThreads),
+                           (size_t)(Kp + ncand) * 4, stream, a, cand_key, cand_idx, ncand);
+    return hipGetLastError();
+}
+
 bool row_select_plan_fits(int width, int k, int mode) {
     if (k > kMaxKBlocks) return false;
     if (mode == 1) return width <= kRowSelectMaxWidth;
     if (mode == 2) return true;
     return width <= kFusedMaxWidth && k <= kFusedMaxK;
 }
+
+#ifndef OASIS_ROW_WIDE
+// Chunks of at least kMinChunkWidth blocks, few enough that their K
+// candidates each fit kMaxCandidates; chunk widths a multiple of 64.
+void two_pass_plan(int width, int k, int *chunk_w, int *chunks) {
+    const int cmax = kMaxCandidates / k;
+    int cw = (width + cmax - 1) / cmax;
+    cw = cw < kMinChunkWidth ? kMinChunkWidth : (cw + 63) / 64 * 64;
+    *chunk_w = cw;
+    *chunks = (width + cw - 1) / cw;
+}
+
+// mode 1 = select, 3 = select then plan (the plan in the same launch when
+// its LDS fits beside the candidates, else a plan launch after it).
+hipError_t launch_two_pass_select_plan(const SelectPlanArgs &a, int mode, uint32_t *cand_key,
+                                       int32_t *cand_idx, hipStream_t stream) {
+    if (a.rows == 0) return hipSuccess;
+    int cw = 0, chunks = 0;
+    two_pass_plan(a.width, a.k, &cw, &chunks);
+    const ChunkArgs ca{a.scores, a.ctx_len, cand_key, cand_idx, a.rows, a.hkv, a.width, a.k, cw,
+                       chunks};
+    hipError_t e = cw > kWideRowMinWidth ? wide::launch_chunk_select(ca, stream)
+                                         : launch_chunk_select(ca, stream);
+    if (e != hipSuccess) return e;
+    const int ncand = chunks * a.k;
+    const bool fused = mode == 3 && (size_t)(10 * plan_pad(a.k) + ncand) * 4 <= 65536;
+    const int m = fused ? 3 : 1;
+    e = ncand > kWideRowMinWidth ? wide::launch_merge_select_plan(a, m, cand_key, cand_idx, ncand, stream)
+                                 : launch_merge_select_plan(a, m, cand_key, cand_idx, ncand, stream);
+    if (e != hipSuccess || mode == 1 || fused) return e;
+    return launch_row_select_plan(a, 2, stream);
+}
+#endif
 
 hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream) {
     if (a.rows == 0) return hipSuccess;

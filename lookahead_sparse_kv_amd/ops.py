@@ -22,7 +22,7 @@ OASIS_OK, OASIS_ERR_INVALID, OASIS_ERR_UNSUPPORTED, OASIS_ERR_NOMEM, OASIS_ERR_H
 
 # Every symbol include/oasis.h declares.
 EXPORTS = ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax", "oasis_select_topk", "oasis_plan_fetch", "oasis_select_plan",
-           "oasis_select_plan_ex",
+           "oasis_select_plan_ex", "oasis_select_workspace_bytes", "oasis_select_plan_ws",
            "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_sparse_decode_attn_ex",
            "oasis_sparse_decode_attn_noalloc",
            "oasis_hostpool_create",
@@ -48,7 +48,8 @@ class OasisLayer(ctypes.Structure):
                 ("last_use", ctypes.c_void_p), ("fetch_block", ctypes.c_void_p),
                 ("fetch_slot", ctypes.c_void_p), ("fetch_count", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("score_k_pool", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("score_k_pool", ctypes.c_void_p),
+                ("select_workspace", ctypes.c_void_p), ("select_workspace_bytes", ctypes.c_size_t)]
 
 
 class OasisStepSync(ctypes.Structure):
@@ -84,6 +85,9 @@ def lib() -> ctypes.CDLL:
         L.oasis_plan_fetch.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p]
         L.oasis_select_plan.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p, p]
         L.oasis_select_plan_ex.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p, p, p]
+        L.oasis_select_workspace_bytes.argtypes = [S, i32]
+        L.oasis_select_workspace_bytes.restype = sz
+        L.oasis_select_plan_ws.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p, p, p, sz, p]
         L.oasis_attn_workspace_bytes.argtypes = [S, i32, i32]
         L.oasis_attn_workspace_bytes.restype = sz
         L.oasis_sparse_decode_attn.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz, p]
@@ -99,7 +103,8 @@ def lib() -> ctypes.CDLL:
         L.oasis_fetch_blocks.argtypes = [S, p, p, i32, p, p, p, i32, p, p, p, p]
         for fn in ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax",
                    "oasis_select_topk", "oasis_plan_fetch",
-                   "oasis_select_plan", "oasis_select_plan_ex", "oasis_layer_step",
+                   "oasis_select_plan", "oasis_select_plan_ex", "oasis_select_plan_ws",
+                   "oasis_layer_step",
                    "oasis_sparse_decode_attn",
                    "oasis_sparse_decode_attn_ex", "oasis_sparse_decode_attn_noalloc",
                    "oasis_hostpool_create",
@@ -140,12 +145,16 @@ def _numel(*dims) -> int:
     return n
 
 
-def _check_tensors(*specs):
+def _check_tensors(*specs, enabled=True):
     """The C ABI receives bare pointers and cannot see a buffer's size, layout
     or device: reject, before anything is enqueued, a tensor that is not a
     contiguous tensor of the expected dtype holding at least the elements the
     call will touch, and then one that is not on the GPU.  Each spec is
-    (tensor, name, dtype, numel) or (tensor, name, dtype, numel, optional)."""
+    (tensor, name, dtype, numel) or (tensor, name, dtype, numel, optional).
+    enabled=False: a caller that checked these buffers once (a layer's own
+    buffers, at construction) skips the checks on its hot path."""
+    if not enabled:
+        return
     present = []
     for spec in specs:
         t, name, dtype, numel = spec[:4]
@@ -188,7 +197,7 @@ def _pool_shape(q: torch.Tensor, k_pool: torch.Tensor, table: torch.Tensor) -> O
                       table.shape[1], k_pool.shape[0])
 
 
-def score_blocks(q_look, k_pool, block_table, ctx_len, scores, scale=None, stream=None):
+def score_blocks(q_look, k_pool, block_table, ctx_len, scores, scale=None, stream=None, check=True):
     """q_look [B][n_look][Hq][D] bf16, k_pool [P][Hkv][16][D] bf16 (tiles in 8-dim slices),
     block_table [B][W] i32,
     ctx_len [B] i32 -> scores [B][Hkv][W] f32 (written in place)."""
@@ -201,7 +210,7 @@ def score_blocks(q_look, k_pool, block_table, ctx_len, scores, scale=None, strea
                    (k_pool, "k_pool", _BF16, _numel(s.num_pages, Hkv, BLOCK_SIZE, D)),
                    (block_table, "block_table", _I32, B * W),
                    (ctx_len, "ctx_len", _I32, B),
-                   (scores, "scores", _F32, B * Hkv * W))
+                   (scores, "scores", _F32, B * Hkv * W), enabled=check)
     scale = float(s.head_dim) ** -0.5 if scale is None else scale
     _check(lib().oasis_score_blocks(ctypes.byref(s), _ptr(q_look), q_look.shape[1], _ptr(k_pool),
                                     _ptr(block_table), _ptr(ctx_len), scale, _ptr(scores),
@@ -234,7 +243,7 @@ def pool_keys(k_pool, block_table, ctx_len, ck, num_q_heads=None, last_only=Fals
 
 
 def score_blocks_minmax(q_look, ck, ctx_len, scores, scale=None, k_pool=None, block_table=None,
-                        stream=None):
+                        stream=None, check=True):
     """q_look [B][n_look][Hq][D] bf16, ck (compressed_keys_shape) bf16, ctx_len [B] i32 ->
     scores [B][Hkv][W] f32 (written in place).  With k_pool [P][Hkv][16][D] and
     block_table [B][W], each sequence's last block is re-pooled into ck first."""
@@ -247,7 +256,7 @@ def score_blocks_minmax(q_look, ck, ctx_len, scores, scale=None, k_pool=None, bl
                    (ctx_len, "ctx_len", _I32, B),
                    (scores, "scores", _F32, B * Hkv * W),
                    (k_pool, "k_pool", _BF16, _numel(s.num_pages, Hkv, BLOCK_SIZE, D), True),
-                   (block_table, "block_table", _I32, B * W, True))
+                   (block_table, "block_table", _I32, B * W, True), enabled=check)
     scale = float(D) ** -0.5 if scale is None else scale
     _check(lib().oasis_score_blocks_minmax(ctypes.byref(s), _ptr(q_look), q_look.shape[1],
                                            _ptr(ck), _ptr(k_pool), _ptr(block_table),
@@ -255,12 +264,12 @@ def score_blocks_minmax(q_look, ck, ctx_len, scores, scale=None, k_pool=None, bl
     return scores
 
 
-def select_topk(shape: OasisShape, scores, ctx_len, k_blocks, sel, stream=None):
+def select_topk(shape: OasisShape, scores, ctx_len, k_blocks, sel, stream=None, check=True):
     """scores [B][Hkv][W] f32 -> sel [B][Hkv][K] i32 (ascending, -1 padded)."""
     rows = shape.batch * shape.num_kv_heads
     _check_tensors((scores, "scores", _F32, rows * shape.table_width),
                    (ctx_len, "ctx_len", _I32, shape.batch),
-                   (sel, "sel", _I32, rows * max(k_blocks, 0)))
+                   (sel, "sel", _I32, rows * max(k_blocks, 0)), enabled=check)
     _check(lib().oasis_select_topk(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks,
                                    _ptr(sel), _stream(stream)))
     return sel
@@ -281,24 +290,41 @@ def _plan_specs(shape, k_blocks, cap, sel, slot_block, last_use, fetch_block, fe
 
 
 def plan_fetch(shape: OasisShape, sel, scores, k_blocks, cap, step, slot_block, last_use,
-               fetch_block, fetch_slot, fetch_count, stream=None):
+               fetch_block, fetch_slot, fetch_count, stream=None, check=True):
     """Updates slot_block / last_use [B][Hkv][K] in place; writes the capped fetch list."""
     _check_tensors(*_plan_specs(shape, k_blocks, cap, sel, slot_block, last_use, fetch_block,
-                                fetch_slot, fetch_count, scores))
+                                fetch_slot, fetch_count, scores), enabled=check)
     _check(lib().oasis_plan_fetch(ctypes.byref(shape), _ptr(sel), _ptr(scores), k_blocks, cap,
                                   step, _ptr(slot_block), _ptr(last_use), _ptr(fetch_block),
                                   _ptr(fetch_slot), _ptr(fetch_count), _stream(stream)))
 
 
+def select_workspace_bytes(shape: OasisShape, k_blocks: int) -> int:
+    """Workspace of the two-pass selection of wide rows (0 where none is needed)."""
+    return int(lib().oasis_select_workspace_bytes(ctypes.byref(shape), k_blocks))
+
+
 def select_plan(shape: OasisShape, scores, ctx_len, k_blocks, cap, step, sel, slot_block,
-                last_use, fetch_block, fetch_slot, fetch_count, stream=None, step_dev=None):
+                last_use, fetch_block, fetch_slot, fetch_count, stream=None, step_dev=None,
+                workspace=None, check=True):
     """select_topk then plan_fetch in one launch where the shape allows (same results).
     step_dev (int32 device tensor of one element, or None): the plan's step is
-    step + step_dev[0], read on the device (oasis_select_plan_ex)."""
+    step + step_dev[0], read on the device (oasis_select_plan_ex).  workspace
+    (a device tensor of select_workspace_bytes() bytes): rows wider than 8,192
+    blocks take the two-pass selection (oasis_select_plan_ws)."""
     _check_tensors(*_plan_specs(shape, k_blocks, cap, sel, slot_block, last_use, fetch_block,
                                 fetch_slot, fetch_count, scores),
                    (ctx_len, "ctx_len", _I32, shape.batch),
-                   (step_dev, "step_dev", _I32, 1, True))
+                   (step_dev, "step_dev", _I32, 1, True), enabled=check)
+    if workspace is not None:
+        _check_ws(workspace)
+        _check(lib().oasis_select_plan_ws(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len),
+                                          k_blocks, cap, step, _ptr(step_dev), _ptr(sel),
+                                          _ptr(slot_block), _ptr(last_use), _ptr(fetch_block),
+                                          _ptr(fetch_slot), _ptr(fetch_count), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
+        return
     if step_dev is None:
         _check(lib().oasis_select_plan(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks,
                                        cap, step, _ptr(sel), _ptr(slot_block), _ptr(last_use),
@@ -311,6 +337,28 @@ def select_plan(shape: OasisShape, scores, ctx_len, k_blocks, cap, step, sel, sl
                                           _ptr(fetch_count), _stream(stream)))
 
 
+def _check_ws(workspace):
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous() or \
+            workspace.device.type != "cuda":
+        raise ValueError("workspace: a contiguous GPU tensor is required")
+
+
+def select_topk_ws(shape: OasisShape, scores, ctx_len, k_blocks, sel, workspace, stream=None):
+    """select_topk for rows of any width up to 8192 * (8192 // K) blocks through the
+    two-pass selection (oasis_select_plan_ws, select only)."""
+    rows = shape.batch * shape.num_kv_heads
+    _check_tensors((scores, "scores", _F32, rows * shape.table_width),
+                   (ctx_len, "ctx_len", _I32, shape.batch),
+                   (sel, "sel", _I32, rows * max(k_blocks, 0)))
+    if workspace is not None:
+        _check_ws(workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().oasis_select_plan_ws(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks,
+                                      0, 0, None, _ptr(sel), None, None, None, None, None,
+                                      _ptr(workspace), nbytes, _stream(stream)))
+    return sel
+
+
 def attn_workspace_bytes(shape: OasisShape, n_q: int, n_blk: int) -> int:
     return int(lib().oasis_attn_workspace_bytes(ctypes.byref(shape), n_q, n_blk))
 
@@ -319,7 +367,7 @@ OASIS_ATTN_SHARE_GPU = 1
 
 
 def sparse_decode_attn(shape: OasisShape, q, k_pool, v_pool, page_table, blk, blk_logical,
-                       ctx_len, out, workspace, scale=None, stream=None, flags=0):
+                       ctx_len, out, workspace, scale=None, stream=None, flags=0, check=True):
     """q [B][n_q][Hq][D] bf16 -> out [B][n_q][Hq][D] bf16 over the listed blocks.
     blk / blk_logical [B][Hkv][n_blk] i32 (blk may be None: entry e is index e).
     workspace: any contents (oasis_attn_workspace_bytes() bytes).  flags: OASIS_ATTN_SHARE_GPU when another launch runs
@@ -338,7 +386,7 @@ def sparse_decode_attn(shape: OasisShape, q, k_pool, v_pool, page_table, blk, bl
                    (ctx_len, "ctx_len", _I32, B),
                    (out, "out", _BF16, _numel(B, n_q, shape.num_q_heads, D)),
                    (workspace, "workspace", workspace.dtype if isinstance(workspace, torch.Tensor)
-                    else None, 0))
+                    else None, 0), enabled=check)
     scale = float(shape.head_dim) ** -0.5 if scale is None else scale
     args = (ctypes.byref(shape), _ptr(q), q.shape[1], _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
             _ptr(blk), n_blk, _ptr(blk_logical), _ptr(ctx_len), scale, _ptr(out), _ptr(workspace),
@@ -436,7 +484,7 @@ class HostPool:
 
 def fetch_blocks(ws_shape: OasisShape, host_k_dev: int, host_v_dev: int, host_blocks: int,
                  fetch_block, fetch_slot, fetch_count, cap, ws_page_table, ws_k_pool, ws_v_pool,
-                 stream=None):
+                 stream=None, check=True):
     """Copy the listed blocks from the pinned host pool into working-set slots (device side)."""
     rows = ws_shape.batch * ws_shape.num_kv_heads
     tile = _numel(ws_shape.num_pages, ws_shape.num_kv_heads, BLOCK_SIZE, ws_shape.head_dim)
@@ -446,7 +494,7 @@ def fetch_blocks(ws_shape: OasisShape, host_k_dev: int, host_v_dev: int, host_bl
     if cap > 0:
         specs += [(fetch_block, "fetch_block", _I32, rows * int(cap)),
                   (fetch_slot, "fetch_slot", _I32, rows * int(cap))]
-    _check_tensors(*specs)
+    _check_tensors(*specs, enabled=check)
     _check(lib().oasis_fetch_blocks(ctypes.byref(ws_shape), ctypes.c_void_p(host_k_dev),
                                     ctypes.c_void_p(host_v_dev), host_blocks, _ptr(fetch_block),
                                     _ptr(fetch_slot), _ptr(fetch_count), cap, _ptr(ws_page_table),

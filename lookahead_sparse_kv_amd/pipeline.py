@@ -54,11 +54,40 @@ class DecodeLayer:
         self.out = torch.empty((B, n_q, num_q_heads, D), dtype=torch.bfloat16, device=dev)
         ws = ops.attn_workspace_bytes(self.shape, n_q, k_blocks)
         self.workspace = torch.zeros((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        # rows wider than 8,192 blocks: the two-pass selection's candidates
+        sws = ops.select_workspace_bytes(self.shape, k_blocks)
+        self.select_workspace = (torch.empty(((sws + 7) // 8,), dtype=torch.int64, device=dev)
+                                 if sws else None)
         self.ck = None
         if scorer == "minmax":
             self.ck = torch.empty(ops.compressed_keys_shape(B, Hkv, W, D), dtype=torch.bfloat16,
                                   device=dev)
             ops.pool_keys(k_pool, block_table, ctx_len, self.ck, num_q_heads=num_q_heads)
+        # the caller's buffers are checked once here; the stages then call the
+        # library without re-checking them (the per-step queries are checked)
+        tile = ops._numel(self.shape.num_pages, Hkv, 16, D)
+        ops._check_tensors((k_pool, "k_pool", torch.bfloat16, tile),
+                           (v_pool, "v_pool", torch.bfloat16, tile),
+                           (block_table, "block_table", torch.int32, B * W),
+                           (ctx_len, "ctx_len", torch.int32, B))
+
+    def _check_q(self, q, rows, name):
+        s = self.shape
+        ops._check_tensors((q, name, torch.bfloat16, ops._numel(s.batch, rows, s.num_q_heads,
+                                                                 s.head_dim)))
+
+    def _query_rows(self, q):
+        # attention takes any number of query rows up to the layer's n_q (its
+        # output buffer holds n_q rows per sequence)
+        rows = q.shape[1] if isinstance(q, torch.Tensor) and q.dim() == 4 else 0
+        if not 1 <= rows <= self.n_q:
+            raise ValueError(f"q: [B][n_q][Hq][D] with 1 <= n_q <= {self.n_q} expected, "
+                             f"got shape {tuple(getattr(q, 'shape', ()))}")
+        self._check_q(q, rows, "q")
+
+    def _check_pool(self, k_pool):
+        if k_pool is not None and k_pool is not self.k_pool:
+            ops._check_tensors((k_pool, "k_pool", torch.bfloat16, self.k_pool.numel()))
 
     @property
     def cap(self) -> int:
@@ -90,13 +119,18 @@ class DecodeLayer:
         this key pool (same layout and block table) instead of the layer's."""
         out = self.scores if scores is None else scores
         kp = self.k_pool if k_pool is None else k_pool
+        self._check_q(q_look, self.n_look, "q_look")
+        self._check_pool(k_pool)
+        if scores is not None:
+            ops._check_tensors((scores, "scores", torch.float32, self.scores.numel()))
         if self.ck is not None:
             ops.score_blocks_minmax(q_look, self.ck, self.ctx_len, out,
                                     k_pool=kp if refresh else None,
                                     block_table=self.block_table if refresh else None,
-                                    stream=stream)
+                                    stream=stream, check=False)
         else:
-            ops.score_blocks(q_look, kp, self.block_table, self.ctx_len, out, stream=stream)
+            ops.score_blocks(q_look, kp, self.block_table, self.ctx_len, out, stream=stream,
+                             check=False)
 
     def append(self, stream=None):
         """After the caller has written each sequence's new token into the key
@@ -117,10 +151,14 @@ class DecodeLayer:
 
     def select_plan(self, step, stream=None, scores=None, step_dev=None):
         """step_dev: the plan's step is step + step_dev[0], read on the device."""
+        if scores is not None:
+            ops._check_tensors((scores, "scores", torch.float32, self.scores.numel()))
+        if step_dev is not None:
+            ops._check_tensors((step_dev, "step_dev", torch.int32, 1))
         ops.select_plan(self.shape, self.scores if scores is None else scores, self.ctx_len,
                         self.k_blocks, self.cap, step, self.sel, self.slot_block, self.last_use,
                         self.fetch_block, self.fetch_slot, self.fetch_count, stream,
-                        step_dev=step_dev)
+                        step_dev=step_dev, workspace=self.select_workspace, check=False)
 
     def native_desc(self, share_gpu=True, refresh=False, k_pool=None, score_k_pool=None):
         """oasis_layer descriptor of this layer for oasis_layer_step (built once per
@@ -143,7 +181,10 @@ class DecodeLayer:
                 last_use=vp(self.last_use), fetch_block=vp(self._fetch_block_buf),
                 fetch_slot=vp(self._fetch_slot_buf), fetch_count=vp(self.fetch_count),
                 out=vp(self.out), workspace=vp(self.workspace),
-                workspace_bytes=self.workspace.numel() * self.workspace.element_size())
+                workspace_bytes=self.workspace.numel() * self.workspace.element_size(),
+                select_workspace=vp(self.select_workspace),
+                select_workspace_bytes=(0 if self.select_workspace is None else
+                                        self.select_workspace.numel() * 8))
         desc = cache[key]
         desc.cap = self.cap                     # the one field a caller changes between steps
         return desc
@@ -151,11 +192,16 @@ class DecodeLayer:
     def attend(self, q, blocks=None, stream=None, share_gpu=False, k_pool=None):
         """share_gpu: another launch (the next step's scoring) runs beside this one.
         k_pool: read this key pool instead of the layer's."""
-        blocks = self.slot_block if blocks is None else blocks
+        self._query_rows(q)
+        self._check_pool(k_pool)
+        if blocks is None:
+            blocks = self.slot_block
+        else:
+            ops._check_tensors((blocks, "blocks", torch.int32, self.slot_block.numel()))
         ops.sparse_decode_attn(self.shape, q, self.k_pool if k_pool is None else k_pool,
                                self.v_pool, self.block_table, blocks, blocks, self.ctx_len,
                                self.out, self.workspace, stream=stream,
-                               flags=ops.OASIS_ATTN_SHARE_GPU if share_gpu else 0)
+                               flags=ops.OASIS_ATTN_SHARE_GPU if share_gpu else 0, check=False)
 
     def step(self, q_look, q, step, stream=None):
         self.score(q_look, stream)
@@ -494,30 +540,59 @@ class HostTierLayer:
         self.out = torch.empty((B, n_q, num_q_heads, D), dtype=torch.bfloat16, device=dev)
         ws = ops.attn_workspace_bytes(self.ws_shape, n_q, k_blocks)
         self.workspace = torch.zeros((max(ws, 16) + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        # the caller's buffers are checked once here; the stages then call the
+        # library without re-checking them (the per-step queries are checked)
+        specs = [(block_table, "block_table", torch.int32, B * W),
+                 (ctx_len, "ctx_len", torch.int32, B),
+                 (ws_page_table, "ws_page_table", torch.int32, B * k_blocks)]
+        if k_pool is not None:
+            specs.append((k_pool, "k_pool", torch.bfloat16, ops._numel(k_pool.shape[0], Hkv, 16, D)))
+        else:
+            specs.append((ck, "ck", torch.bfloat16, ops._numel(*ops.compressed_keys_shape(B, Hkv, W, D))))
+        ops._check_tensors(*specs)
+
+    def _check_q(self, q, rows, name):
+        s = self.shape
+        ops._check_tensors((q, name, torch.bfloat16, ops._numel(s.batch, rows, s.num_q_heads,
+                                                                 s.head_dim)))
+
+    def _query_rows(self, q):
+        # attention takes any number of query rows up to the layer's n_q (its
+        # output buffer holds n_q rows per sequence)
+        rows = q.shape[1] if isinstance(q, torch.Tensor) and q.dim() == 4 else 0
+        if not 1 <= rows <= self.n_q:
+            raise ValueError(f"q: [B][n_q][Hq][D] with 1 <= n_q <= {self.n_q} expected, "
+                             f"got shape {tuple(getattr(q, 'shape', ()))}")
+        self._check_q(q, rows, "q")
 
     def score(self, q_look, stream=None):
+        self._check_q(q_look, self.n_look, "q_look")
         if self.ck is not None:
-            ops.score_blocks_minmax(q_look, self.ck, self.ctx_len, self.scores, stream=stream)
+            ops.score_blocks_minmax(q_look, self.ck, self.ctx_len, self.scores, stream=stream,
+                                    check=False)
         else:
             ops.score_blocks(q_look, self.k_pool, self.block_table, self.ctx_len, self.scores,
-                             stream=stream)
+                             stream=stream, check=False)
 
     def select_plan(self, step, cap=None, stream=None):
         cap = self.cap if cap is None else cap
+        if not 0 <= cap <= self.k_blocks:
+            raise ValueError(f"cap {cap} outside [0, k_blocks = {self.k_blocks}]")
         ops.select_plan(self.shape, self.scores, self.ctx_len, self.k_blocks, cap, step, self.sel,
                         self.slot_block, self.last_use, self.fetch_block, self.fetch_slot,
-                        self.fetch_count, stream)
+                        self.fetch_count, stream, check=False)
         self._last_cap = cap
 
     def fetch(self, stream=None):
         ops.fetch_blocks(self.ws_shape, self.host_k, self.host_v, self.host_blocks,
                          self.fetch_block, self.fetch_slot, self.fetch_count, self._last_cap,
-                         self.ws_page_table, self.ws_k, self.ws_v, stream)
+                         self.ws_page_table, self.ws_k, self.ws_v, stream, check=False)
 
     def attend(self, q, stream=None):
+        self._query_rows(q)
         ops.sparse_decode_attn(self.ws_shape, q, self.ws_k, self.ws_v, self.ws_page_table, None,
                                self.slot_block, self.ctx_len, self.out, self.workspace,
-                               stream=stream)
+                               stream=stream, check=False)
 
 
 class HostTierDecode:

@@ -92,6 +92,40 @@ int main(void) {
     EXPECT(oasis_select_plan_ex(&ok, PF, PI, 8, 2, INT32_MIN, PI, NULL, PI, PI, PI, PI, PI, NULL),
            OASIS_ERR_INVALID);
 
+    /* the two-pass selection of wide rows */
+    s = shape(2, 8, 2, 128, 16, 8193, 128);
+    const size_t sws = oasis_select_workspace_bytes(&s, 128);
+    if (sws != (size_t)2 * 2 * 5 * 128 * 8) { fprintf(stderr, "select workspace %zu\n", sws); ++failures; }
+    s.table_width = 8192;
+    if (oasis_select_workspace_bytes(&s, 128) != 0) { fprintf(stderr, "8192 needs none\n"); ++failures; }
+    s.table_width = 8193;
+    if (oasis_select_workspace_bytes(&ok, 128) != 0) { fprintf(stderr, "narrow rows need none\n"); ++failures; }
+    (void)oasis_select_workspace_bytes(&big, INT32_MAX);
+    (void)oasis_select_workspace_bytes(&big, 1);
+    (void)oasis_select_workspace_bytes(NULL, 1);
+    EXPECT(oasis_select_plan_ws(&s, PF, PI, 128, 2, 0, NULL, PI, PI, PI, PI, PI, PI, NULL, 0, NULL),
+           OASIS_ERR_NOMEM);
+    EXPECT(oasis_select_plan_ws(&s, PF, PI, 128, 2, 0, NULL, PI, PI, PI, PI, PI, PI, PV, sws - 1, NULL),
+           OASIS_ERR_NOMEM);
+    EXPECT(oasis_select_plan_ws(&s, PF, PI, 128, 2, 0, NULL, PI, PI, PI, PI, PI, PI,
+                                (void *)(uintptr_t)4100, sws, NULL), OASIS_ERR_INVALID);
+    EXPECT(oasis_select_plan_ws(&s, PF, PI, 0, 2, 0, NULL, PI, PI, PI, PI, PI, PI, PV, sws, NULL),
+           OASIS_ERR_INVALID);
+    EXPECT(oasis_select_plan_ws(&s, PF, PI, 2000, 2, 0, NULL, PI, PI, PI, PI, PI, PI, PV, sws, NULL),
+           OASIS_ERR_UNSUPPORTED);
+    EXPECT(oasis_select_plan_ws(&s, PF, PI, 128, 129, 0, NULL, PI, PI, PI, PI, PI, PI, PV, sws, NULL),
+           OASIS_ERR_INVALID);
+    EXPECT(oasis_select_plan_ws(&s, PF, PI, 128, 2, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, PV,
+                                sws, NULL), OASIS_ERR_INVALID);            /* select only, no sel */
+    EXPECT(oasis_select_plan_ws(&s, PF, PI, 128, 2, 0, NULL, PI, PI, NULL, PI, PI, PI, PV, sws, NULL),
+           OASIS_ERR_INVALID);                                             /* plan without last_use */
+    s = shape(2, 8, 2, 128, 16, 1048577, 128);
+    EXPECT(oasis_select_plan_ws(&s, PF, PI, 128, 2, 0, NULL, PI, PI, PI, PI, PI, PI, PV, (size_t)-1,
+                                NULL), OASIS_ERR_UNSUPPORTED);             /* wider than 8192 * 64 */
+    s = shape(0, 8, 2, 128, 16, 65536, 128);
+    EXPECT(oasis_select_plan_ws(&s, NULL, NULL, 128, 2, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                                NULL, 0, NULL), OASIS_OK);
+
     /* attention: workspace sizes at the extremes must not overflow */
     (void)oasis_attn_workspace_bytes(&big, 1, INT32_MAX);
     (void)oasis_attn_workspace_bytes(&big, INT32_MAX, 1);

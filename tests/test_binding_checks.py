@@ -19,7 +19,17 @@ def _layer(cap=4, K=8):
                        ctx_len=torch.zeros((B,), dtype=I32), num_q_heads=8, k_blocks=K, cap=cap)
 
 
-def test_layer_refuses_a_cap_its_fetch_lists_cannot_hold():
+def test_layer_checks_the_callers_buffers_at_construction():
+    with pytest.raises(ValueError, match="GPU"):
+        _layer()
+
+
+def test_layer_refuses_a_cap_its_fetch_lists_cannot_hold(monkeypatch):
+    # the layer's device check is set aside: the cap logic is host-side
+    real = ops._check_tensors
+    monkeypatch.setattr(ops, "_check_tensors",
+                        lambda *specs, enabled=True: real(*[x for x in specs if x[0] is None or
+                                                           x[0].device.type == "cuda"]))
     L = _layer(cap=4, K=8)
     assert L.fetch_block.shape == (2, 2, 4) and L.fetch_slot.shape == (2, 2, 4)
     L.cap = 8                          # up to K: the storage has room for K entries per row
@@ -33,6 +43,19 @@ def test_layer_refuses_a_cap_its_fetch_lists_cannot_hold():
         L.cap = -1
     with pytest.raises(ValueError):
         _layer(cap=9, K=8)
+
+
+def test_layer_attention_takes_up_to_its_query_rows(monkeypatch):
+    real = ops._check_tensors
+    monkeypatch.setattr(ops, "_check_tensors",
+                        lambda *specs, enabled=True: real(*[x for x in specs if x[0] is None or
+                                                           x[0].device.type == "cuda"]))
+    L = _layer()                                   # n_q = 1
+    for rows in (0, 2):
+        with pytest.raises(ValueError, match="n_q"):
+            L.attend(torch.zeros((2, rows, 8, 64), dtype=BF))
+    with pytest.raises(ValueError, match="n_q"):
+        L.attend(torch.zeros((2 * 8 * 64,), dtype=BF))
 
 
 def test_plan_buffers_too_small_for_the_cap_are_refused():

@@ -6,6 +6,7 @@ fp32 scores, so the integer results must match bit for bit); the step tests
 chain the four stages and apply the near-tie exemption where the fp32 kernel
 scores and the fp64 oracle scores may legitimately order a boundary pair
 differently.  Sizes span several tiles with ragged tails, plus edge cases."""
+import ctypes
 import math
 
 import numpy as np
@@ -274,6 +275,91 @@ def test_select_plan_fused_bit_exact_over_steps(case):
         np.testing.assert_array_equal(fs.cpu().numpy(), ofs)
         np.testing.assert_array_equal(g_sb.cpu().numpy(), sb)
         np.testing.assert_array_equal(g_lu.cpu().numpy(), lu)
+
+
+TWO_PASS_CASES = [
+    # B, Hkv, W, K, cap, mode, contexts (blocks; None = every row full)
+    (2, 2, 8193, 64, 3, "normal", None),               # one block above the one-pass width
+    (2, 8, 9000, 128, 2, "normal", None),              # 5 chunks of 2,048
+    (2, 4, 12000, 128, 6, "ties", (12000, 5000)),
+    (2, 2, 20000, 300, 7, "ties", (20000, 9001)),      # beyond the one-pass limit, ragged
+    (1, 4, 65536, 128, 2, "normal", None),             # 32 chunks
+    (2, 2, 65536, 1024, 25, "narrow", (65536, 40000)), # 8 chunks of 8,192; plan in its own launch
+    (2, 2, 16384, 1024, 9, "outliers", None),
+    (2, 2, 12000, 64, 3, "equal", (12000, 3000)),      # every key equal: lowest indices win
+    (2, 2, 9000, 128, 2, "zeros", (9000, 100)),        # a row with fewer blocks than K
+]
+
+
+@pytest.mark.parametrize("case", TWO_PASS_CASES, ids=lambda c: f"W{c[2]}K{c[3]}{c[5]}")
+def test_two_pass_select_plan_bit_exact_over_steps(case):
+    """Rows wider than 8,192 blocks: the chunks' top-K candidates, then the
+    row's top-K of them and its plan (oasis_select_plan_ws), bit for bit the
+    oracle's selection, fetch list and working-set table over chained steps;
+    the select-only form gives the same selection.  Up to 65,536 blocks."""
+    B, Hkv, W, K, cap, mode, ctx_blocks = case
+    rng = np.random.default_rng(hash(str(case)) % 2 ** 32)
+    nbs = ctx_blocks or (W,) * B
+    ctx_len = np.array([16 * n - (3 if n < W else 0) for n in nbs], np.int32)   # ragged
+    shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
+    need = ops.select_workspace_bytes(shape, K)
+    assert need > 0
+    ws = torch.randint(-2 ** 31, 2 ** 31 - 1, (need // 4 + 2,), dtype=torch.int32,
+                       generator=torch.Generator().manual_seed(3)).to(DEV)      # any contents
+    sb, lu = _random_state(rng, B, Hkv, K, min(nbs), None)
+    g_sb, g_lu = dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))
+    g_ctx = dev(torch.from_numpy(ctx_len))
+    sel = torch.empty((B, Hkv, K), dtype=torch.int32, device=DEV)
+    sel_only = torch.full((B, Hkv, K), -7, dtype=torch.int32, device=DEV)
+    fb = torch.empty((B, Hkv, max(cap, 1)), dtype=torch.int32, device=DEV)
+    fs = torch.empty_like(fb)
+    fc = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    for step in range(3, 6):
+        sc = _random_scores(rng, B, Hkv, W, mode)
+        osel = orc.select(sc.astype(np.float64), ctx_len, 16, K)
+        ofb, ofs, ocnt, sb, lu = orc.plan(osel, sc.astype(np.float64), sb, lu, cap, step)
+        g_s = dev(torch.from_numpy(sc))
+        ops.select_plan(shape, g_s, g_ctx, K, cap, step, sel, g_sb, g_lu, fb, fs, fc,
+                        workspace=ws)
+        ops.select_topk_ws(shape, g_s, g_ctx, K, sel_only, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(sel.cpu().numpy(), osel)
+        np.testing.assert_array_equal(sel_only.cpu().numpy(), osel)
+        np.testing.assert_array_equal(fc.cpu().numpy(), ocnt)
+        np.testing.assert_array_equal(fb.cpu().numpy()[..., :cap], ofb)
+        np.testing.assert_array_equal(fs.cpu().numpy()[..., :cap], ofs)
+        np.testing.assert_array_equal(g_sb.cpu().numpy(), sb)
+        np.testing.assert_array_equal(g_lu.cpu().numpy(), lu)
+
+
+def test_select_plan_ws_without_workspace_at_one_pass_widths():
+    """Up to 8,192 blocks the workspace call needs no workspace and gives the
+    one-pass results."""
+    B, Hkv, W, K, cap = 2, 4, 8192, 128, 2
+    rng = np.random.default_rng(17)
+    ctx_len = np.array([16 * W, 16 * 5000 - 7], np.int32)
+    shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
+    assert ops.select_workspace_bytes(shape, K) == 0
+    sb, lu = _random_state(rng, B, Hkv, K, 5000, None)
+    sc = _random_scores(rng, B, Hkv, W, "normal")
+    osel = orc.select(sc.astype(np.float64), ctx_len, 16, K)
+    ofb, ofs, ocnt, osb, olu = orc.plan(osel, sc.astype(np.float64), sb, lu, cap, 9)
+    g_sb, g_lu = dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))
+    sel = torch.empty((B, Hkv, K), dtype=torch.int32, device=DEV)
+    fb = torch.empty((B, Hkv, cap), dtype=torch.int32, device=DEV)
+    fs, fc = torch.empty_like(fb), torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    status = ops.lib().oasis_select_plan_ws(
+        ctypes.byref(shape), ops._ptr(dev(torch.from_numpy(sc))),
+        ops._ptr(dev(torch.from_numpy(ctx_len))), K, cap, 9, None, ops._ptr(sel),
+        ops._ptr(g_sb), ops._ptr(g_lu), ops._ptr(fb), ops._ptr(fs), ops._ptr(fc), None, 0, None)
+    assert status == ops.OASIS_OK
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), osel)
+    np.testing.assert_array_equal(fc.cpu().numpy(), ocnt)
+    np.testing.assert_array_equal(fb.cpu().numpy(), ofb)
+    np.testing.assert_array_equal(fs.cpu().numpy(), ofs)
+    np.testing.assert_array_equal(g_sb.cpu().numpy(), osb)
+    np.testing.assert_array_equal(g_lu.cpu().numpy(), olu)
 
 
 @pytest.mark.parametrize("W,K", [(300, 32), (3000, 128), (9000, 128), (1000, 600)],
