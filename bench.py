@@ -35,6 +35,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 N_LOOK_DRAWS = 4               # distinct lookahead draws cycled through the steps
+INPUTS_NOTE = {
+    "resident": "resident in HBM before the timed region; the scoring stream waits on the "
+                "caller's stream once",
+    "caller": "each scoring launch ordered after everything enqueued on the caller's stream "
+              "(where a decode loop writes the next lookahead query)",
+}
 KERNEL_SRC = os.path.join(ROOT, "lookahead_sparse_kv_amd", "csrc", "score_blocks.hip")
 
 
@@ -58,6 +64,10 @@ def parse():
     p.add_argument("--native", choices=("on", "off"), default="on",
                    help="enqueue each pipelined layer-step with one oasis_layer_step call "
                         "(on) or with the Python sequence of launches and event calls (off)")
+    p.add_argument("--inputs", choices=("resident", "caller"), default="resident",
+                   help="scoring inputs resident before the timed region (the scoring stream "
+                        "waits on the caller's stream once) or ordered after the caller's "
+                        "stream at every step; the bench line also times the other one")
     p.add_argument("--attn-share", choices=("auto", "on", "off"), default="auto",
                    help="attention in the step launched with the share-GPU hint (one CU per "
                         "row; auto: with exact scoring)")
@@ -657,14 +667,24 @@ def main():
     # longer kernel) one CU per row leaves the other CUs to it; with the
     # compressed scorer attention is the longer kernel and takes every CU
     share_gpu = (wl.scorer == "exact") if args.attn_share == "auto" else args.attn_share == "on"
-    pipes = [PipelinedDecode(L, side=side, plan_stream=plan_stream, native=args.native == "on",
-                             share_gpu=share_gpu)
-             for L in layers]
+    # Every lookahead draw, the context lengths and the pools are in HBM before
+    # the timed region and stay unchanged ("resident"): the scoring stream
+    # waits on the caller's stream once, at prime.  "caller" orders each
+    # scoring launch after everything on the caller's stream, as a decode loop
+    # that writes the next lookahead query there needs; the previous layer's
+    # attention is then always ahead of the scoring.
     # compressed scorer: each scoring launch also re-pools the block a decode
     # step appends to (the pool itself is not written here)
     append = wl.scorer == "minmax"
-    for P in pipes:
-        P.prime(looks[0], 0, append=append)
+
+    def make_pipes(inputs, first_step):
+        ps = [PipelinedDecode(L, side=side, plan_stream=plan_stream, native=args.native == "on",
+                              share_gpu=share_gpu, inputs=inputs) for L in layers]
+        for P in ps:
+            P.prime(looks[0], first_step, append=append)
+        return ps
+
+    pipes = make_pipes(args.inputs, 0)
     for i in range(args.warmup):
         pipes[i % n_rep].step(q, looks[(i // n_rep + 1) % N_LOOK_DRAWS], 1 + i // n_rep,
                               copy_out=False, append=append)
@@ -672,13 +692,14 @@ def main():
         P.drain()
     torch.cuda.synchronize()
 
-    def run_steps(first, events=None):
+    def run_steps(first, events=None, ps=None):
+        ps = pipes if ps is None else ps
         for i in range(args.steps):
             s = first + i
-            pipes[s % n_rep].step(q, looks[(s // n_rep + 1) % N_LOOK_DRAWS], 1 + s // n_rep,
-                                  copy_out=False, append=append,
-                                  score_events=None if events is None else events[i])
-        for P in pipes:
+            ps[s % n_rep].step(q, looks[(s // n_rep + 1) % N_LOOK_DRAWS], 1 + s // n_rep,
+                               copy_out=False, append=append,
+                               score_events=None if events is None else events[i])
+        for P in ps:
             P.drain()
 
     # The timed region: K steps, no events inside (an event pair per launch
@@ -704,6 +725,18 @@ def main():
     ms_per_step_with_events = e_a.elapsed_time(e_b) / args.steps
     # blocks fetched by the plan of the timed loop's last step (all rows)
     fetched = int(pipes[(args.warmup + 2 * args.steps - 1) % n_rep].L.fetch_count.sum().item())
+    # the same K steps with the other ordering of the scoring inputs
+    other_inputs = "caller" if args.inputs == "resident" else "resident"
+    first = args.warmup + 2 * args.steps
+    pipes_other = make_pipes(other_inputs, 1 + first // n_rep)
+    run_steps(first + n_rep, ps=pipes_other)                  # warm-up
+    torch.cuda.synchronize()
+    e_c, e_d = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_c.record()
+    run_steps(first + n_rep + args.steps, ps=pipes_other)
+    e_d.record()
+    torch.cuda.synchronize()
+    ms_per_step_other = e_c.elapsed_time(e_d) / args.steps
     score_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
     mean_ms = {"score": sum(score_ms) / len(score_ms)}
 
@@ -841,7 +874,11 @@ def main():
                    "attn_in_step": ("one workgroup per row (share-GPU hint)" if share_gpu else
                                     "default launch shape"),
                    "replicas": n_rep,
+                   "scoring_inputs": INPUTS_NOTE[args.inputs],
                    "parallelism": "single GPU"},
+        "other_scoring_inputs": {"scoring_inputs": INPUTS_NOTE[other_inputs],
+                                 "value": round(wl.batch / (ms_per_step_other * 1e-3), 1),
+                                 "ms_per_step": round(ms_per_step_other, 4)},
         "roofline": {"bound": "hbm", "kernel": SCORE_KERNELS[wl.scorer][0],
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

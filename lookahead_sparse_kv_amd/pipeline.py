@@ -249,7 +249,7 @@ class PipelinedDecode:
     """
 
     def __init__(self, layer: DecodeLayer, side=None, plan_stream=None, native=False,
-                 share_gpu=True, k_pools=None):
+                 share_gpu=True, k_pools=None, inputs="caller"):
         """`side`: the stream the scoring runs on; `plan_stream`: the stream
         select + plan runs on (None: the caller's).  Several pipelines (one per
         layer) may share them, so that each runs layer after layer.  `native`:
@@ -257,7 +257,20 @@ class PipelinedDecode:
         launches and the same event waits and records from native code.
         `share_gpu`: attention launched with the share-GPU hint (one CU per row
         from 128 rows), which pays when the concurrent scoring is the longer
-        kernel (exact scoring); without it, attention spreads over every CU."""
+        kernel (exact scoring); without it, attention spreads over every CU.
+        `inputs`: "caller" (default): each step's scoring waits for everything
+        enqueued on the caller's stream so far, where the caller writes that
+        step's lookahead query, context lengths and appended keys; since the
+        previous attention is on that stream too, the scoring then starts only
+        after it.  "resident": every buffer the scoring reads was written
+        before prime() (which waits for the caller's stream once) and stays
+        unchanged, so steps add no wait on the caller's stream and the scoring
+        of one layer may start before the attention enqueued ahead of it."""
+        if inputs not in ("caller", "resident"):
+            raise ValueError(f"inputs: 'caller' or 'resident', not {inputs!r}")
+        if inputs == "resident" and k_pools is not None:
+            raise ValueError("inputs='resident' with k_pools: the keys change between steps")
+        self.inputs = inputs
         self.L = layer
         self.buf = [layer.scores, torch.empty_like(layer.scores)]
         if side is None:
@@ -286,15 +299,17 @@ class PipelinedDecode:
     def _pool(self, step):
         return None if self.k_pools is None else self.k_pools[step % 2]
 
-    def _score_next(self, q_look, main, ev=None, append=False, step=0):
+    def _score_next(self, q_look, main, ev=None, append=False, step=0, prime=False):
         b = self.i % 2
         # The caller writes this step's inputs (the lookahead query, ctx_len, an
         # appended key) on its own stream just before the call: scoring waits
         # for everything enqueued there so far.  With select + plan on the
-        # caller's stream that includes the plan that last read buf[b];
-        # otherwise that plan is waited for on its own.
-        self.side.wait_stream(main)
-        if self.used[b] and self.plan_stream is not None:
+        # caller's stream that includes
+        # the plan that last read buf[b]; otherwise that plan is waited for on
+        # its own.  With resident inputs only prime() waits for that stream.
+        if self.inputs == "caller" or prime:
+            self.side.wait_stream(main)
+        if self.used[b] and (self.plan_stream is not None or self.inputs == "resident"):
             self.side.wait_event(self.ev_planned[b])    # the plan that last read buf[b]
         if ev:
             ev[0].record(self.side)
@@ -323,7 +338,7 @@ class PipelinedDecode:
 
     def prime(self, q_look, step, append=False):
         main = torch.cuda.current_stream()
-        b = self._score_next(q_look, main, append=append, step=step)
+        b = self._score_next(q_look, main, append=append, step=step, prime=True)
         self._plan(b, step, main)
 
     def step(self, q, q_look_next, step, copy_out=True, score_events=None, append=False):
@@ -351,9 +366,11 @@ class PipelinedDecode:
         """The same step as the Python path below, through oasis_layer_step."""
         b = self.i % 2
         # as in _score_next: the inputs event orders scoring after the caller's
-        # stream; a plan on another stream that last read buf[b] is waited for
-        score_after = (self.ev_planned[b] if self.used[b] and self.plan_stream is not None
-                       else None)
+        # stream; a plan that last read buf[b] and that the caller's stream
+        # does not order is waited for
+        caller = self.inputs == "caller"
+        score_after = (self.ev_planned[b] if self.used[b] and
+                       (self.plan_stream is not None or not caller) else None)
         ps = main if self.plan_stream is None else self.plan_stream
         attn_after = self.last_plan if self.plan_stream is not None else None
         h = lambda x: None if x is None else x.cuda_event
@@ -361,7 +378,7 @@ class PipelinedDecode:
                                  plan_stream=ps.cuda_stream, score_after=h(score_after),
                                  attn_after=h(attn_after), scored=h(self.ev_scored[b]),
                                  attended=h(self.ev_attended), planned=h(self.ev_planned[b]),
-                                 inputs=h(self.ev_inputs))
+                                 inputs=h(self.ev_inputs) if caller else None)
         desc = self.L.native_desc(share_gpu=self.share_gpu, refresh=append,
                                   k_pool=self._pool(step), score_k_pool=self._pool(step + 1))
         ops.layer_step(desc, q_look_next, q, self.buf[b], step + 1, sync)

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from lookahead_sparse_kv_amd import ops
-from lookahead_sparse_kv_amd.pipeline import DecodeLayer
+from lookahead_sparse_kv_amd.pipeline import DecodeLayer, PipelinedDecode
 
 BF, I32, F32 = torch.bfloat16, torch.int32, torch.float32
 
@@ -117,3 +117,11 @@ def test_wrong_dtype_layout_or_size_is_refused_before_any_launch():
                          torch.zeros(7, dtype=I32), torch.zeros(4, dtype=I32), 2,
                          torch.zeros(16, dtype=I32), torch.zeros((16, Hkv, 16, D), dtype=BF),
                          torch.zeros((16, Hkv, D, 16), dtype=BF))
+
+
+def test_pipeline_input_ordering_modes():
+    with pytest.raises(ValueError, match="inputs"):
+        PipelinedDecode(None, inputs="never")
+    # keys that change between steps must be ordered at every step
+    with pytest.raises(ValueError, match="k_pools"):
+        PipelinedDecode(None, inputs="resident", k_pools=(None, None))

@@ -838,7 +838,9 @@ def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch, s
     """oasis_layer_step enqueues the pipelined step (score, attention, select +
     plan, with the same event waits and records) from native code: per-step
     outputs and the final state are bit-identical to the Python pipeline's,
-    over several layers taking turns on shared streams.  32 and 128 rows."""
+    over several layers taking turns on shared streams, also with resident
+    inputs (scoring not ordered after the caller's stream at each step).
+    32 and 128 rows."""
     wl = wlm.small_workload(batch=batch, q_heads=32, kv_heads=8, head_dim=128,
                             ctx=(4096, 3000, 2500, 4000), budget=512, n_hot=12, ratio=0.125, seed=44,
                             n_look=max(1, drafts))
@@ -851,13 +853,14 @@ def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch, s
               for t in range(T + 1)] for l, d in enumerate(datas)]
     append = scorer == "minmax"
     runs = {}
-    for native in (False, True):
+    for native, inputs in ((False, "caller"), (True, "caller"), (False, "resident"),
+                           (True, "resident")):
         sb, lu = (x.numpy() for x in wlm.empty_state(wl))
         layers = [_gpu_layer(wl, d, wl.cap(), sb, lu, scorer=scorer, n_q=n_q) for d in datas]
         side = torch.cuda.Stream()
         ps = torch.cuda.Stream() if plan_stream else None
-        pipes = [PipelinedDecode(L, side=side, plan_stream=ps, native=native, share_gpu=share)
-                 for L in layers]
+        pipes = [PipelinedDecode(L, side=side, plan_stream=ps, native=native, share_gpu=share,
+                                 inputs=inputs) for L in layers]
         for l, P in enumerate(pipes):
             P.prime(looks[l][0], 0, append=append)
         outs = []
@@ -868,15 +871,17 @@ def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch, s
         for P in pipes:
             P.drain()
         torch.cuda.synchronize()
-        runs[native] = (outs, [{k: getattr(L, k).clone() for k in
-                                ("sel", "slot_block", "last_use", "fetch_count")} for L in layers])
-    (o_py, st_py), (o_nat, st_nat) = runs[False], runs[True]
-    for i, (a, b) in enumerate(zip(o_py, o_nat)):
-        assert torch.equal(a, b), i
-    for a, b in zip(st_py, st_nat):
-        for k in a:
-            assert torch.equal(a[k], b[k]), k
-    assert int(max(x["fetch_count"].max().item() for x in st_nat)) == wl.cap()
+        runs[native, inputs] = (outs, [{k: getattr(L, k).clone() for k in
+                                        ("sel", "slot_block", "last_use", "fetch_count")}
+                                       for L in layers])
+    o_py, st_py = runs[False, "caller"]
+    for key, (o_other, st_other) in runs.items():
+        for i, (a, b) in enumerate(zip(o_py, o_other)):
+            assert torch.equal(a, b), (key, i)
+        for a, b in zip(st_py, st_other):
+            for k in a:
+                assert torch.equal(a[k], b[k]), (key, k)
+    assert int(max(x["fetch_count"].max().item() for x in st_py)) == wl.cap()
 
 
 @pytest.mark.parametrize("native,plan_stream", [(False, False), (False, True), (True, False),
