@@ -386,6 +386,13 @@ int oasis_hostpool_destroy(void *host_ptr);
  * those oasis_plan_fetch writes; the call reads them on the device, so no host
  * synchronisation is needed.  Requires 0 <= cap <= K and the four pools
  * 16-byte aligned.
+ *
+ * This is the path's fetch-issue call: enqueued on a side stream, it issues
+ * the step's capped host -> HBM transfer.  It is a gather kernel rather than
+ * a series of copy-engine copies (hipMemcpyAsync of each listed tile): the
+ * copy engines pay a fixed cost per copy that 4 KiB tiles cannot amortise
+ * (about 1.8 GB/s against 55 GB/s for the gather on MI355X), and a list of
+ * copies would have to come back to the host first.
  */
 int oasis_fetch_blocks(const oasis_shape *s, const uint16_t *host_k, const uint16_t *host_v,
                        int32_t host_blocks, const int32_t *fetch_block, const int32_t *fetch_slot,
