@@ -709,6 +709,7 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     run_steps(args.warmup)
+    host_ms = (time.perf_counter() - t0) * 1e3          # enqueue only (no wait for the GPU)
     ev1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
@@ -911,6 +912,7 @@ def main():
         "topk_agreement": agreement,
         "pool_keys_build": pool_build,
         "wall_ms_timed_region": round(wall_ms, 2),
+        "host_enqueue_us_per_step": round(host_ms * 1e3 / timed_steps, 2),
         "input_generation_s": round(gen_s, 1),
         "cpu_baseline": cpu,
     }

@@ -19,6 +19,11 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// The completion event of the stage oasis_layer_step is enqueueing: the
+// stage's last kernel launch records it (oasis::LaunchStop).  Null outside
+// oasis_layer_step, so the public calls launch as they always do.
+thread_local oasis::LaunchStop *t_stage_stop = nullptr;
+
 int fail(int status, const char *fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
@@ -101,7 +106,7 @@ int oasis_score_blocks(const oasis_shape *s, const uint16_t *q_look, int32_t n_l
     oasis::ScoreArgs a{q_look, k_pool, block_table, ctx_len, scores, scale,
                        s->batch, s->num_q_heads, s->num_kv_heads, G, s->table_width,
                        s->num_pages, n_look, n_look * G};
-    return check_hip(oasis::launch_score_blocks(a, s->head_dim, as_stream(stream)), fn);
+    return check_hip(oasis::launch_score_blocks(a, s->head_dim, as_stream(stream), t_stage_stop), fn);
 }
 
 int oasis_pool_keys(const oasis_shape *s, const uint16_t *k_pool, const int32_t *block_table,
@@ -143,7 +148,7 @@ int oasis_score_blocks_minmax(const oasis_shape *s, const uint16_t *q_look, int3
     oasis::MinmaxArgs a{q_look, ck, k_pool, block_table, ctx_len, scores, scale, s->batch,
                         s->num_q_heads, s->num_kv_heads, G, s->table_width, s->num_pages, n_look,
                         n_look * G};
-    return check_hip(oasis::launch_score_minmax(a, s->head_dim, as_stream(stream)), fn);
+    return check_hip(oasis::launch_score_minmax(a, s->head_dim, as_stream(stream), t_stage_stop), fn);
 }
 
 int oasis_select_topk(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
@@ -163,7 +168,7 @@ int oasis_select_topk(const oasis_shape *s, const float *scores, const int32_t *
     if (oasis::row_select_plan_fits(s->table_width, k_blocks, 1)) {
         oasis::SelectPlanArgs a{scores, ctx_len, sel, nullptr, nullptr, nullptr, nullptr, nullptr,
                                 rows, s->num_kv_heads, s->table_width, k_blocks, 0, 0};
-        return check_hip(oasis::launch_row_select_plan(a, 1, as_stream(stream)), fn);
+        return check_hip(oasis::launch_row_select_plan(a, 1, as_stream(stream), t_stage_stop), fn);
     }
     oasis::SelectArgs a{scores, ctx_len, sel, rows, s->num_kv_heads, s->table_width, k_blocks};
     return check_hip(oasis::launch_select_topk(a, as_stream(stream)), fn);
@@ -190,7 +195,7 @@ int oasis_plan_fetch(const oasis_shape *s, const int32_t *sel, const float *scor
     oasis::SelectPlanArgs a{scores, nullptr, const_cast<int32_t *>(sel), slot_block, last_use,
                             fetch_block, fetch_slot, fetch_count, rows, s->num_kv_heads,
                             s->table_width, k_blocks, cap, step};
-    return check_hip(oasis::launch_row_select_plan(a, 2, as_stream(stream)), fn);
+    return check_hip(oasis::launch_row_select_plan(a, 2, as_stream(stream), t_stage_stop), fn);
 }
 
 int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
@@ -227,14 +232,14 @@ int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_
                             fetch_count, rows, s->num_kv_heads, s->table_width, k_blocks, cap,
                             step, step_dev};
     if (oasis::row_select_plan_fits(s->table_width, k_blocks, 3))
-        return check_hip(oasis::launch_row_select_plan(a, 3, as_stream(stream)), fn);
+        return check_hip(oasis::launch_row_select_plan(a, 3, as_stream(stream), t_stage_stop), fn);
     if (oasis::row_select_plan_fits(s->table_width, k_blocks, 1)) {
         if (int e = check_hip(oasis::launch_row_select_plan(a, 1, as_stream(stream)), fn)) return e;
     } else {
         oasis::SelectArgs sa{scores, ctx_len, sel, rows, s->num_kv_heads, s->table_width, k_blocks};
         if (int e = check_hip(oasis::launch_select_topk(sa, as_stream(stream)), fn)) return e;
     }
-    return check_hip(oasis::launch_row_select_plan(a, 2, as_stream(stream)), fn);
+    return check_hip(oasis::launch_row_select_plan(a, 2, as_stream(stream), t_stage_stop), fn);
 }
 
 size_t oasis_select_workspace_bytes(const oasis_shape *s, int32_t k_blocks) {
@@ -290,7 +295,7 @@ int oasis_select_plan_ws(const oasis_shape *s, const float *scores, const int32_
                             fetch_count, rows, s->num_kv_heads, s->table_width, k_blocks,
                             plan ? cap : 0, step, step_dev};
     return check_hip(oasis::launch_two_pass_select_plan(a, plan ? 3 : 1, cand_key, cand_idx,
-                                                        as_stream(stream)), fn);
+                                                        as_stream(stream), t_stage_stop), fn);
 }
 
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk) {
@@ -376,7 +381,7 @@ int oasis_sparse_decode_attn_ex(const oasis_shape *s, const uint16_t *q, int32_t
                       s->batch, s->num_q_heads, s->num_kv_heads, G, s->table_width,
                       s->num_pages, n_q, nrq, n_blk, splits, per};
     return check_hip(oasis::launch_sparse_decode_attn(a, s->head_dim, (flags & OASIS_ATTN_SHARE_GPU) != 0,
-                                                      as_stream(stream)), fn);
+                                                      as_stream(stream), t_stage_stop), fn);
 }
 
 }  // extern "C"
@@ -453,6 +458,18 @@ int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const ui
     hipStream_t ss = as_stream(sync->score_stream), as = as_stream(sync->attn_stream),
                 ps = as_stream(sync->plan_stream);
     const auto ev = [](void *e) { return reinterpret_cast<hipEvent_t>(e); };
+    // Each stage's completion event is recorded by its last kernel launch;
+    // a stage that launched nothing records it as a command of its own.
+    const auto run_stage = [&](void *event, hipStream_t stream, auto &&enqueue) -> int {
+        oasis::LaunchStop st;
+        st.event = ev(event);
+        t_stage_stop = event ? &st : nullptr;
+        const int e = enqueue();
+        t_stage_stop = nullptr;
+        if (e) return e;
+        if (event && !st.used) return check_hip(hipEventRecord(ev(event), stream), fn);
+        return OASIS_OK;
+    };
     if (sync->inputs) {
         if (int e = check_hip(hipEventRecord(ev(sync->inputs), as), fn)) return e;
         if (int e = check_hip(hipStreamWaitEvent(ss, ev(sync->inputs), 0), fn)) return e;
@@ -460,34 +477,33 @@ int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const ui
     if (sync->score_after)
         if (int e = check_hip(hipStreamWaitEvent(ss, ev(sync->score_after), 0), fn)) return e;
     const uint16_t *skp = L->score_k_pool ? L->score_k_pool : L->k_pool;
-    int e = L->ck ? oasis_score_blocks_minmax(&L->shape, q_look_next, L->n_look, L->ck,
-                                              L->refresh ? skp : nullptr,
-                                              L->refresh ? L->block_table : nullptr, L->ctx_len,
-                                              L->scale, scores, ss)
-                  : oasis_score_blocks(&L->shape, q_look_next, L->n_look, skp, L->block_table,
-                                       L->ctx_len, L->scale, scores, ss);
+    int e = run_stage(sync->scored, ss, [&] {
+        return L->ck ? oasis_score_blocks_minmax(&L->shape, q_look_next, L->n_look, L->ck,
+                                                 L->refresh ? skp : nullptr,
+                                                 L->refresh ? L->block_table : nullptr, L->ctx_len,
+                                                 L->scale, scores, ss)
+                     : oasis_score_blocks(&L->shape, q_look_next, L->n_look, skp, L->block_table,
+                                          L->ctx_len, L->scale, scores, ss);
+    });
     if (e) return e;
-    if ((e = check_hip(hipEventRecord(ev(sync->scored), ss), fn))) return e;
     if (sync->attn_after)
         if ((e = check_hip(hipStreamWaitEvent(as, ev(sync->attn_after), 0), fn))) return e;
-    if ((e = oasis_sparse_decode_attn_ex(&L->shape, q, L->n_q, L->k_pool, L->v_pool, L->block_table,
-                                         L->slot_block, L->k_blocks, L->slot_block, L->ctx_len,
-                                         L->scale, L->out, L->workspace, L->workspace_bytes,
-                                         L->attn_flags, as)))
-        return e;
-    if (ps != as) {
-        if ((e = check_hip(hipEventRecord(ev(sync->attended), as), fn))) return e;
+    e = run_stage(ps != as ? sync->attended : nullptr, as, [&] {
+        return oasis_sparse_decode_attn_ex(&L->shape, q, L->n_q, L->k_pool, L->v_pool,
+                                           L->block_table, L->slot_block, L->k_blocks,
+                                           L->slot_block, L->ctx_len, L->scale, L->out,
+                                           L->workspace, L->workspace_bytes, L->attn_flags, as);
+    });
+    if (e) return e;
+    if (ps != as)
         if ((e = check_hip(hipStreamWaitEvent(ps, ev(sync->attended), 0), fn))) return e;
-    }
     if ((e = check_hip(hipStreamWaitEvent(ps, ev(sync->scored), 0), fn))) return e;
-    if ((e = oasis_select_plan_ws(&L->shape, scores, L->ctx_len, L->k_blocks, L->cap, step,
-                                  nullptr, L->sel, L->slot_block, L->last_use, L->fetch_block,
-                                  L->fetch_slot, L->fetch_count, L->select_workspace,
-                                  L->select_workspace_bytes, ps)))
-        return e;
-    if (sync->planned)
-        if ((e = check_hip(hipEventRecord(ev(sync->planned), ps), fn))) return e;
-    return ok();
+    return run_stage(sync->planned, ps, [&] {
+        return oasis_select_plan_ws(&L->shape, scores, L->ctx_len, L->k_blocks, L->cap, step,
+                                    nullptr, L->sel, L->slot_block, L->last_use, L->fetch_block,
+                                    L->fetch_slot, L->fetch_count, L->select_workspace,
+                                    L->select_workspace_bytes, ps);
+    });
 }
 
 int oasis_hostpool_create(size_t bytes, void **host_ptr) {

@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -113,14 +114,42 @@ __host__ __device__ inline size_t ck_slice_offset(int row, int width, int n, int
     return (((size_t)row * tiles + n / 16) * (size_t)(2 * D / 8) + s) * 128 + (size_t)(n % 16) * 8;
 }
 
-hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t stream);
+// An event recorded by the completion of a stage's last kernel, as part of that
+// launch (hipExtLaunchKernelGGL's stop event) rather than as a separate record
+// command behind it: in a schedule of three streams tied by events, separate
+// record commands doubled the period of a layer-step in a probe.  `used` tells
+// whether a launch took it (a stage that launches nothing leaves it to the
+// caller).
+struct LaunchStop {
+    hipEvent_t event = nullptr;
+    bool used = false;
+};
+
+// Launch `kernel`; with `stop` (not yet used), the launch also records its
+// event when the kernel completes.
+template <typename F, typename... Args>
+inline void launch_k(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                     LaunchStop *stop, Args... args) {
+    if (stop && stop->event && !stop->used) {
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, nullptr, stop->event, 0u,
+                              args...);
+        stop->used = true;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+    }
+}
+
+hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t stream,
+                               LaunchStop *stop = nullptr);
 hipError_t launch_pool_keys(const PoolArgs &a, int head_dim, hipStream_t stream);
-hipError_t launch_score_minmax(const MinmaxArgs &a, int head_dim, hipStream_t stream);
+hipError_t launch_score_minmax(const MinmaxArgs &a, int head_dim, hipStream_t stream,
+                               LaunchStop *stop = nullptr);
 hipError_t launch_select_topk(const SelectArgs &a, hipStream_t stream);
 // One workgroup per row (256 threads; 1024 for rows wider than kWideRowMinWidth);
 // mode 1 = select, 2 = plan, 3 = select then plan.
 bool row_select_plan_fits(int width, int k, int mode);
-hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
+hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream,
+                                  LaunchStop *stop = nullptr);
 // Rows wider than this (in blocks) are selected by a 1024-thread build of the
 // same kernels (select_plan_wide.hip).
 #ifndef OASIS_WIDE_ROW_MIN_WIDTH
@@ -128,23 +157,28 @@ hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t
 #endif
 constexpr int kWideRowMinWidth = OASIS_WIDE_ROW_MIN_WIDTH;
 namespace wide {
-hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream);
+hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream,
+                                  LaunchStop *stop = nullptr);
 }
 // Two-pass selection (and plan) of rows wider than kTwoPassMinWidth blocks:
 // the chunk kernel, then one workgroup per row over the candidates.
 void two_pass_plan(int width, int k, int *chunk_w, int *chunks);
 hipError_t launch_two_pass_select_plan(const SelectPlanArgs &a, int mode, uint32_t *cand_key,
-                                       int32_t *cand_idx, hipStream_t stream);
+                                       int32_t *cand_idx, hipStream_t stream,
+                                       LaunchStop *stop = nullptr);
 namespace wide {
 hipError_t launch_chunk_select(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_merge_select_plan(const SelectPlanArgs &a, int mode, const uint32_t *cand_key,
-                                    const int32_t *cand_idx, int ncand, hipStream_t stream);
+                                    const int32_t *cand_idx, int ncand, hipStream_t stream,
+                                    LaunchStop *stop = nullptr);
 }
 hipError_t launch_chunk_select(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_merge_select_plan(const SelectPlanArgs &a, int mode, const uint32_t *cand_key,
-                                    const int32_t *cand_idx, int ncand, hipStream_t stream);
+                                    const int32_t *cand_idx, int ncand, hipStream_t stream,
+                                    LaunchStop *stop = nullptr);
 hipError_t launch_fetch_blocks(const FetchArgs &a, int head_dim, hipStream_t stream);
-hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share_gpu, hipStream_t stream);
+hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share_gpu, hipStream_t stream,
+                                     LaunchStop *stop = nullptr);
 
 // Split-K plan of the attention kernel: how many splits per row and entries per split.
 void attn_split_plan(int rows, int n_blk, int *splits, int *per_split);

@@ -155,16 +155,17 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_blocks_kernel(Score
     }
 }
 
-hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t stream) {
+hipError_t launch_score_blocks(const ScoreArgs &a, int head_dim, hipStream_t stream,
+                               LaunchStop *stop) {
     const int rows = a.batch * a.hkv;
     if (rows == 0 || a.width == 0) return hipSuccess;
     const int per_wg = kScoreWaves * kScoreChunk;
     dim3 grid((a.width + per_wg - 1) / per_wg, rows);
     dim3 block(kScoreWaves * kWave);
     if (head_dim == 128)
-        hipLaunchKernelGGL(score_blocks_kernel<128>, grid, block, 0, stream, a);
+        launch_k(score_blocks_kernel<128>, grid, block, 0, stream, stop, a);
     else
-        hipLaunchKernelGGL(score_blocks_kernel<64>, grid, block, 0, stream, a);
+        launch_k(score_blocks_kernel<64>, grid, block, 0, stream, stop, a);
     return hipGetLastError();
 }
 

@@ -220,7 +220,8 @@ __global__ __launch_bounds__(kMmWaves * kWave) void score_minmax_kernel(MinmaxAr
     }
 }
 
-hipError_t launch_score_minmax(const MinmaxArgs &a, int head_dim, hipStream_t stream) {
+hipError_t launch_score_minmax(const MinmaxArgs &a, int head_dim, hipStream_t stream,
+                               LaunchStop *stop) {
     const long long rows = (long long)a.batch * a.hkv;
     const long long chunks = (a.width + kMmBlocksPerWave - 1) / kMmBlocksPerWave;
     const long long waves = rows * chunks + (a.k_pool ? rows : 0);
@@ -228,9 +229,9 @@ hipError_t launch_score_minmax(const MinmaxArgs &a, int head_dim, hipStream_t st
     const dim3 grid((unsigned)((waves + kMmWaves - 1) / kMmWaves));
     const dim3 block(kMmWaves * kWave);
     if (head_dim == 128)
-        hipLaunchKernelGGL(score_minmax_kernel<128>, grid, block, 0, stream, a);
+        launch_k(score_minmax_kernel<128>, grid, block, 0, stream, stop, a);
     else
-        hipLaunchKernelGGL(score_minmax_kernel<64>, grid, block, 0, stream, a);
+        launch_k(score_minmax_kernel<64>, grid, block, 0, stream, stop, a);
     return hipGetLastError();
 }
 

@@ -171,14 +171,15 @@ hipError_t launch_chunk_select(const ChunkArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_merge_select_plan(const SelectPlanArgs &a, int mode, const uint32_t *cand_key,
-                                    const int32_t *cand_idx, int ncand, hipStream_t stream) {
+                                    const int32_t *cand_idx, int ncand, hipStream_t stream,
+                                    LaunchStop *stop) {
     const int Kp = plan_pad(a.k);
     if (mode == 3)
-        hipLaunchKernelGGL(row_merge_select_plan_kernel<3>, dim3(a.rows), dim3(kRowThreads),
-                           (size_t)(10 * Kp + ncand) * 4, stream, a, cand_key, cand_idx, ncand);
+        launch_k(row_merge_select_plan_kernel<3>, dim3(a.rows), dim3(kRowThreads),
+                 (size_t)(10 * Kp + ncand) * 4, stream, stop, a, cand_key, cand_idx, ncand);
     else
-        hipLaunchKernelGGL(row_merge_select_plan_kernel<1>, dim3(a.rows), dim3(kRowThreads),
-                           (size_t)(Kp + ncand) * 4, stream, a, cand_key, cand_idx, ncand);
+        launch_k(row_merge_select_plan_kernel<1>, dim3(a.rows), dim3(kRowThreads),
+                 (size_t)(Kp + ncand) * 4, stream, stop, a, cand_key, cand_idx, ncand);
     return hipGetLastError();
 }
 
@@ -203,7 +204,7 @@ void two_pass_plan(int width, int k, int *chunk_w, int *chunks) {
 // mode 1 = select, 3 = select then plan (the plan in the same launch when
 // its LDS fits beside the candidates, else a plan launch after it).
 hipError_t launch_two_pass_select_plan(const SelectPlanArgs &a, int mode, uint32_t *cand_key,
-                                       int32_t *cand_idx, hipStream_t stream) {
+                                       int32_t *cand_idx, hipStream_t stream, LaunchStop *stop) {
     if (a.rows == 0) return hipSuccess;
     int cw = 0, chunks = 0;
     two_pass_plan(a.width, a.k, &cw, &chunks);
@@ -215,27 +216,32 @@ hipError_t launch_two_pass_select_plan(const SelectPlanArgs &a, int mode, uint32
     const int ncand = chunks * a.k;
     const bool fused = mode == 3 && (size_t)(10 * plan_pad(a.k) + ncand) * 4 <= 65536;
     const int m = fused ? 3 : 1;
-    e = ncand > kWideRowMinWidth ? wide::launch_merge_select_plan(a, m, cand_key, cand_idx, ncand, stream)
-                                 : launch_merge_select_plan(a, m, cand_key, cand_idx, ncand, stream);
+    // the stop event goes with the last launch: the merge, or the plan after it
+    LaunchStop *merge_stop = (mode == 1 || fused) ? stop : nullptr;
+    e = ncand > kWideRowMinWidth
+            ? wide::launch_merge_select_plan(a, m, cand_key, cand_idx, ncand, stream, merge_stop)
+            : launch_merge_select_plan(a, m, cand_key, cand_idx, ncand, stream, merge_stop);
     if (e != hipSuccess || mode == 1 || fused) return e;
-    return launch_row_select_plan(a, 2, stream);
+    return launch_row_select_plan(a, 2, stream, stop);
 }
 #endif
 
-hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream) {
+hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream,
+                                  LaunchStop *stop) {
     if (a.rows == 0) return hipSuccess;
 #ifndef OASIS_ROW_WIDE
-    if ((mode & 1) && a.width > kWideRowMinWidth) return wide::launch_row_select_plan(a, mode, stream);
+    if ((mode & 1) && a.width > kWideRowMinWidth)
+        return wide::launch_row_select_plan(a, mode, stream, stop);
 #endif
     const int Kp = plan_pad(a.k);
     const size_t w = (size_t)(a.width > 0 ? a.width : 1);
     const dim3 grid(a.rows), block(kRowThreads);
     if (mode == 1) {
-        hipLaunchKernelGGL(row_select_plan_kernel<1>, grid, block, (Kp + w) * 4, stream, a);
+        launch_k(row_select_plan_kernel<1>, grid, block, (Kp + w) * 4, stream, stop, a);
     } else if (mode == 2) {
-        hipLaunchKernelGGL(row_select_plan_kernel<2>, grid, block, (size_t)10 * Kp * 4, stream, a);
+        launch_k(row_select_plan_kernel<2>, grid, block, (size_t)10 * Kp * 4, stream, stop, a);
     } else {
-        hipLaunchKernelGGL(row_select_plan_kernel<3>, grid, block, (10 * Kp + w) * 4, stream, a);
+        launch_k(row_select_plan_kernel<3>, grid, block, (10 * Kp + w) * 4, stream, stop, a);
     }
     return hipGetLastError();
 }

@@ -712,17 +712,18 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnArgs a) {
 }
 
 template <int D>
-void launch_merge(const AttnArgs &a, int rows, hipStream_t stream) {
+void launch_merge(const AttnArgs &a, int rows, hipStream_t stream, LaunchStop *stop) {
     const dim3 grid(rows * a.n_rows_q), block(D);
     if (a.splits <= 8)
-        hipLaunchKernelGGL((attn_merge_kernel<D, 8>), grid, block, 0, stream, a);
+        launch_k(attn_merge_kernel<D, 8>, grid, block, 0, stream, stop, a);
     else if (a.splits <= 16)
-        hipLaunchKernelGGL((attn_merge_kernel<D, 16>), grid, block, 0, stream, a);
+        launch_k(attn_merge_kernel<D, 16>, grid, block, 0, stream, stop, a);
     else
-        hipLaunchKernelGGL((attn_merge_kernel<D, 32>), grid, block, 0, stream, a);
+        launch_k(attn_merge_kernel<D, 32>, grid, block, 0, stream, stop, a);
 }
 
-hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share_gpu, hipStream_t stream) {
+hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share_gpu, hipStream_t stream,
+                                     LaunchStop *stop) {
     const int rows = a.batch * a.hkv;
     if (rows == 0) return hipSuccess;
     const long long waves = (long long)rows * a.splits;
@@ -736,9 +737,9 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share
     if (rows >= row_min && row_fits) {
         const size_t lds = row_lds;
         if (head_dim == 128)
-            hipLaunchKernelGGL(attn_row_kernel<128>, dim3(rows), dim3(kRowAttnWaves * kWave), lds, stream, a);
+            launch_k(attn_row_kernel<128>, dim3(rows), dim3(kRowAttnWaves * kWave), lds, stream, stop, a);
         else
-            hipLaunchKernelGGL(attn_row_kernel<64>, dim3(rows), dim3(kRowAttnWaves * kWave), lds, stream, a);
+            launch_k(attn_row_kernel<64>, dim3(rows), dim3(kRowAttnWaves * kWave), lds, stream, stop, a);
         return hipGetLastError();
     }
     int wg_splits = 0, wg_per = 0;
@@ -754,13 +755,13 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share
         // a wave share of exactly 8 or 16 entries takes the fully unrolled walk
         const int share = wg_per % kRowSplitWaves == 0 ? wg_per / kRowSplitWaves : 0;
         if (head_dim == 128) {
-            if (share == 8) hipLaunchKernelGGL((attn_rowsplit_kernel<128, 8>), grid2, block2, lds2, stream, r);
-            else if (share == 16) hipLaunchKernelGGL((attn_rowsplit_kernel<128, 16>), grid2, block2, lds2, stream, r);
-            else hipLaunchKernelGGL((attn_rowsplit_kernel<128, 0>), grid2, block2, lds2, stream, r);
+            if (share == 8) launch_k(attn_rowsplit_kernel<128, 8>, grid2, block2, lds2, stream, stop, r);
+            else if (share == 16) launch_k(attn_rowsplit_kernel<128, 16>, grid2, block2, lds2, stream, stop, r);
+            else launch_k(attn_rowsplit_kernel<128, 0>, grid2, block2, lds2, stream, stop, r);
         } else {
-            if (share == 8) hipLaunchKernelGGL((attn_rowsplit_kernel<64, 8>), grid2, block2, lds2, stream, r);
-            else if (share == 16) hipLaunchKernelGGL((attn_rowsplit_kernel<64, 16>), grid2, block2, lds2, stream, r);
-            else hipLaunchKernelGGL((attn_rowsplit_kernel<64, 0>), grid2, block2, lds2, stream, r);
+            if (share == 8) launch_k(attn_rowsplit_kernel<64, 8>, grid2, block2, lds2, stream, stop, r);
+            else if (share == 16) launch_k(attn_rowsplit_kernel<64, 16>, grid2, block2, lds2, stream, stop, r);
+            else launch_k(attn_rowsplit_kernel<64, 0>, grid2, block2, lds2, stream, stop, r);
         }
         return hipGetLastError();
     }
@@ -777,11 +778,11 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share
         const dim3 grid2((unsigned)(rows * wg_splits)), block2(kSplit2Waves * kWave);
         const bool share16 = wg_per == 16 * kSplit2Waves;     // 16 entries per wave: unrolled
         if (head_dim == 128) {
-            if (share16) hipLaunchKernelGGL((attn_rowsplit_kernel<128, 16, 2, kSplit2Waves>), grid2, block2, lds_t2, stream, r);
-            else hipLaunchKernelGGL((attn_rowsplit_kernel<128, 0, 2, kSplit2Waves>), grid2, block2, lds_t2, stream, r);
+            if (share16) launch_k(attn_rowsplit_kernel<128, 16, 2, kSplit2Waves>, grid2, block2, lds_t2, stream, stop, r);
+            else launch_k(attn_rowsplit_kernel<128, 0, 2, kSplit2Waves>, grid2, block2, lds_t2, stream, stop, r);
         } else {
-            if (share16) hipLaunchKernelGGL((attn_rowsplit_kernel<64, 16, 2, kSplit2Waves>), grid2, block2, lds_t2, stream, r);
-            else hipLaunchKernelGGL((attn_rowsplit_kernel<64, 0, 2, kSplit2Waves>), grid2, block2, lds_t2, stream, r);
+            if (share16) launch_k(attn_rowsplit_kernel<64, 16, 2, kSplit2Waves>, grid2, block2, lds_t2, stream, stop, r);
+            else launch_k(attn_rowsplit_kernel<64, 0, 2, kSplit2Waves>, grid2, block2, lds_t2, stream, stop, r);
         }
         return hipGetLastError();
     }
@@ -789,11 +790,11 @@ hipError_t launch_sparse_decode_attn(const AttnArgs &a, int head_dim, bool share
     if (head_dim == 128) {
         if (two) hipLaunchKernelGGL((attn_partial_kernel<128, 2>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_partial_kernel<128, 1>), grid, block, 0, stream, a);
-        launch_merge<128>(a, rows, stream);
+        launch_merge<128>(a, rows, stream, stop);
     } else {
         if (two) hipLaunchKernelGGL((attn_partial_kernel<64, 2>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_partial_kernel<64, 1>), grid, block, 0, stream, a);
-        launch_merge<64>(a, rows, stream);
+        launch_merge<64>(a, rows, stream, stop);
     }
     return hipGetLastError();
 }
