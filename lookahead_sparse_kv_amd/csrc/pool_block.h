@@ -41,23 +41,44 @@ __device__ __forceinline__ void pool_load(rsrc_t r, uint32_t lane_off,
         v[i] = buf_load16<CPOL>(r, lane_off, i * PoolGeom<D>::kLanes * 16);
 }
 
+// One token group (16 bytes: eight dimensions of one token) into the lane's
+// running min/max, if `ok`.
+__device__ __forceinline__ void pool_fold_tokens(const u32x4 &v, bool ok, float (&mn)[8],
+                                                 float (&mx)[8]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float lo = bf16_bits_to_float(v[w] & 0xffffu);
+        const float hi = bf16_bits_to_float(v[w] >> 16);
+        mn[2 * w] = ok ? fminf(mn[2 * w], lo) : mn[2 * w];
+        mx[2 * w] = ok ? fmaxf(mx[2 * w], lo) : mx[2 * w];
+        mn[2 * w + 1] = ok ? fminf(mn[2 * w + 1], hi) : mn[2 * w + 1];
+        mx[2 * w + 1] = ok ? fmaxf(mx[2 * w + 1], hi) : mx[2 * w + 1];
+    }
+}
+
+// The lanes of a slice's group folded together: every lane of the group ends
+// with the group's min/max.
+template <int D>
+__device__ __forceinline__ void pool_fold_lanes(float (&mn)[8], float (&mx)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        mn[e] = fminf(mn[e], dpp_f<kDppQuadXor1>(mn[e]));
+        mx[e] = fmaxf(mx[e], dpp_f<kDppQuadXor1>(mx[e]));
+        mn[e] = fminf(mn[e], dpp_f<kDppQuadXor2>(mn[e]));
+        mx[e] = fmaxf(mx[e], dpp_f<kDppQuadXor2>(mx[e]));
+        if (PoolGeom<D>::kLanes == 8) {
+            mn[e] = fminf(mn[e], dpp_f<kDppHalfMirror>(mn[e]));
+            mx[e] = fmaxf(mx[e], dpp_f<kDppHalfMirror>(mx[e]));
+        }
+    }
+}
+
 template <int D, bool FULL>
 __device__ __forceinline__ void pool_slice_tokens(const u32x4 (&v)[PoolGeom<D>::kLoads], int nt,
                                                   int t0, float (&mn)[8], float (&mx)[8]) {
     using G = PoolGeom<D>;
 #pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
-        const bool ok = FULL || t0 + G::kLanes * i < nt;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float lo = bf16_bits_to_float(v[i][w] & 0xffffu);
-            const float hi = bf16_bits_to_float(v[i][w] >> 16);
-            mn[2 * w] = ok ? fminf(mn[2 * w], lo) : mn[2 * w];
-            mx[2 * w] = ok ? fmaxf(mx[2 * w], lo) : mx[2 * w];
-            mn[2 * w + 1] = ok ? fminf(mn[2 * w + 1], hi) : mn[2 * w + 1];
-            mx[2 * w + 1] = ok ? fmaxf(mx[2 * w + 1], hi) : mx[2 * w + 1];
-        }
-    }
+    for (int i = 0; i < G::kLoads; ++i) pool_fold_tokens(v[i], FULL || t0 + G::kLanes * i < nt, mn, mx);
 }
 
 // (mn, mx) of slice lane / kLanes over its tokens t < nt (1 <= nt <= 16), in
@@ -74,17 +95,7 @@ __device__ __forceinline__ void pool_slice(const u32x4 (&v)[PoolGeom<D>::kLoads]
         pool_slice_tokens<D, true>(v, nt, t0, mn, mx);
     else
         pool_slice_tokens<D, false>(v, nt, t0, mn, mx);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        mn[e] = fminf(mn[e], dpp_f<kDppQuadXor1>(mn[e]));
-        mx[e] = fmaxf(mx[e], dpp_f<kDppQuadXor1>(mx[e]));
-        mn[e] = fminf(mn[e], dpp_f<kDppQuadXor2>(mn[e]));
-        mx[e] = fmaxf(mx[e], dpp_f<kDppQuadXor2>(mx[e]));
-        if (G::kLanes == 8) {
-            mn[e] = fminf(mn[e], dpp_f<kDppHalfMirror>(mn[e]));
-            mx[e] = fmaxf(mx[e], dpp_f<kDppHalfMirror>(mx[e]));
-        }
-    }
+    pool_fold_lanes<D>(mn, mx);
 }
 
 // Eight widened bf16 values back to their bit patterns (exact: each one is a
