@@ -71,6 +71,11 @@ def parse():
     p.add_argument("--attn-share", choices=("auto", "on", "off"), default="auto",
                    help="attention in the step launched with the share-GPU hint (one CU per "
                         "row; auto: with exact scoring)")
+    p.add_argument("--tables", choices=("auto", "one", "two"), default="auto",
+                   help="the working-set table in one copy, planned in place (the plan of t + 1 "
+                        "waits for the attention of t), or in two, planned from one into the "
+                        "other (it waits for the attention of t - 1); auto: two with the "
+                        "compressed scorer")
     p.add_argument("--detail", action="store_true",
                    help="also time the steps without overlap and each stage alone")
     return p.parse_args()
@@ -667,6 +672,7 @@ def main():
     # longer kernel) one CU per row leaves the other CUs to it; with the
     # compressed scorer attention is the longer kernel and takes every CU
     share_gpu = (wl.scorer == "exact") if args.attn_share == "auto" else args.attn_share == "on"
+    two_tables = (wl.scorer == "minmax") if args.tables == "auto" else args.tables == "two"
     # Every lookahead draw, the context lengths and the pools are in HBM before
     # the timed region and stay unchanged ("resident"): the scoring stream
     # waits on the caller's stream once, at prime.  "caller" orders each
@@ -679,7 +685,8 @@ def main():
 
     def make_pipes(inputs, first_step):
         ps = [PipelinedDecode(L, side=side, plan_stream=plan_stream, native=args.native == "on",
-                              share_gpu=share_gpu, inputs=inputs) for L in layers]
+                              share_gpu=share_gpu, inputs=inputs, double_tables=two_tables)
+              for L in layers]
         for P in ps:
             P.prime(looks[0], first_step, append=append)
         return ps
@@ -879,6 +886,7 @@ def main():
                    "attn_in_step": ("one workgroup per row (share-GPU hint)" if share_gpu else
                                     "default launch shape"),
                    "replicas": n_rep,
+                   "working_set_tables": 2 if two_tables else 1,
                    "scoring_inputs": INPUTS_NOTE[args.inputs],
                    "parallelism": "single GPU"},
         "other_scoring_inputs": {"scoring_inputs": INPUTS_NOTE[other_inputs],

@@ -254,6 +254,26 @@ int oasis_select_plan_ws(const oasis_shape *s, const float *scores, const int32_
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * oasis_select_plan_ws with the plan starting from the working-set table
+ * (slot_block_in, last_use_in) and writing the planned table to (slot_block,
+ * last_use).  An output array is either its input array itself (in place,
+ * as oasis_select_plan_ws) or shares no entry with either input array; the
+ * inputs are only read.  Keeping two copies of the table and planning from
+ * one into the other lets the plan of step t + 1 run while the attention of
+ * step t still reads the table of step t (flow step 4 and Figure 8 caption:
+ * the next step's prediction overlaps the current step's attention), instead
+ * of waiting for it.  Results are those of oasis_select_plan_ws on a copy of
+ * the input table.  Same requirements and errors, plus OASIS_ERR_INVALID for
+ * NULL table arrays or for tables that overlap otherwise than in place.
+ */
+int oasis_select_plan_next(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                           int32_t k_blocks, int32_t cap, int32_t step, const int32_t *step_dev,
+                           int32_t *sel, const int32_t *slot_block_in, const int32_t *last_use_in,
+                           int32_t *slot_block, int32_t *last_use, int32_t *fetch_block,
+                           int32_t *fetch_slot, int32_t *fetch_count, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace oasis_sparse_decode_attn needs for this shape:
  * room for the partial results of a row's shares (per row and share: max,
  * sum and the D-wide output of each query row), then a 32-bit hand-over flag
@@ -421,8 +441,11 @@ int oasis_fetch_blocks(const oasis_shape *s, const uint16_t *host_k, const uint1
  *   attn_stream:  wait attn_after; oasis_sparse_decode_attn_ex(attn_flags) of
  *                 q over the working set slot_block (full-pool mode: the block
  *                 table as page table); record attended if plan_stream differs
- *   plan_stream:  if it differs from attn_stream, wait attended; wait scored;
- *                 oasis_select_plan_ws(step) from scores; record planned
+ *   plan_stream:  if it differs from attn_stream, wait attended (plan_after
+ *                 with two table copies); if it differs from score_stream,
+ *                 wait scored; oasis_select_plan_next(step) from scores, the
+ *                 table read and written in place (slot_block / last_use) or,
+ *                 with two copies, from one copy into the other; record planned
  *
  * and nothing else: the results are those of the three calls in that order.
  * Errors: the first failing call's status; the calls before it stay enqueued.
@@ -446,6 +469,15 @@ typedef struct {
     void *select_workspace;            /* oasis_select_plan_ws workspace (NULL where the
                                           table width needs none) */
     size_t select_workspace_bytes;
+    int32_t *slot_block_next, *last_use_next;
+                                       /* a second copy of the working-set table, or both
+                                          NULL: the plan of step s writes copy s & 1 (copy 1
+                                          = these arrays, copy 0 = slot_block / last_use)
+                                          from copy (s - 1) & 1, which the attention of the
+                                          call reads; so the next step's plan need not wait
+                                          for this step's attention.  Both copies must hold
+                                          the table before the first call; steps of
+                                          consecutive calls must be consecutive */
 } oasis_layer;
 
 typedef struct {
@@ -457,6 +489,11 @@ typedef struct {
                                           ctx_len and appended keys written on attn_stream
                                           (the caller's stream) before the call; NULL: the
                                           caller orders those writes itself */
+    void *plan_after;                  /* with two table copies: the event the previous
+                                          call's attention recorded (`attended` then), which
+                                          the plan waits for instead of this call's
+                                          `attended`: that attention last read the copy the
+                                          plan writes.  NULL: this call's `attended` */
 } oasis_step_sync;
 
 int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const uint16_t *q,

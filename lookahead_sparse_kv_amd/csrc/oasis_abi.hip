@@ -194,7 +194,7 @@ int oasis_plan_fetch(const oasis_shape *s, const int32_t *sel, const float *scor
     const int rows = s->batch * s->num_kv_heads;
     oasis::SelectPlanArgs a{scores, nullptr, const_cast<int32_t *>(sel), slot_block, last_use,
                             fetch_block, fetch_slot, fetch_count, rows, s->num_kv_heads,
-                            s->table_width, k_blocks, cap, step};
+                            s->table_width, k_blocks, cap, step, nullptr, slot_block, last_use};
     return check_hip(oasis::launch_row_select_plan(a, 2, as_stream(stream), t_stage_stop), fn);
 }
 
@@ -206,12 +206,14 @@ int oasis_select_plan(const oasis_shape *s, const float *scores, const int32_t *
                                 last_use, fetch_block, fetch_slot, fetch_count, stream);
 }
 
-int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
-                         int32_t k_blocks, int32_t cap, int32_t step, const int32_t *step_dev,
-                         int32_t *sel, int32_t *slot_block, int32_t *last_use,
-                         int32_t *fetch_block, int32_t *fetch_slot, int32_t *fetch_count,
-                         void *stream) {
-    const char *fn = "oasis_select_plan";
+// Select + plan where the plan starts from the table (sb_in, lu_in) and
+// writes (slot_block, last_use): the same arrays when planning in place.
+static int select_plan_one_pass(const char *fn, const oasis_shape *s, const float *scores,
+                                const int32_t *ctx_len, int32_t k_blocks, int32_t cap, int32_t step,
+                                const int32_t *step_dev, int32_t *sel, const int32_t *sb_in,
+                                const int32_t *lu_in, int32_t *slot_block, int32_t *last_use,
+                                int32_t *fetch_block, int32_t *fetch_slot, int32_t *fetch_count,
+                                void *stream) {
     if (int e = check_shape(s, fn)) return e;
     if (k_blocks < 1) return fail(OASIS_ERR_INVALID, "%s: k_blocks %d < 1", fn, k_blocks);
     if (k_blocks > oasis::kMaxKBlocks)
@@ -223,14 +225,14 @@ int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_
     if (cap < 0 || cap > k_blocks)
         return fail(OASIS_ERR_INVALID, "%s: cap %d outside [0, k_blocks = %d]", fn, cap, k_blocks);
     if (s->batch == 0) return ok();
-    if (!scores || !ctx_len || !sel || !slot_block || !last_use || !fetch_count)
+    if (!scores || !ctx_len || !sel || !slot_block || !last_use || !fetch_count || !sb_in || !lu_in)
         return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
     if (cap > 0 && (!fetch_block || !fetch_slot))
         return fail(OASIS_ERR_INVALID, "%s: NULL fetch list with cap %d", fn, cap);
     const int rows = s->batch * s->num_kv_heads;
     oasis::SelectPlanArgs a{scores, ctx_len, sel, slot_block, last_use, fetch_block, fetch_slot,
                             fetch_count, rows, s->num_kv_heads, s->table_width, k_blocks, cap,
-                            step, step_dev};
+                            step, step_dev, sb_in, lu_in};
     if (oasis::row_select_plan_fits(s->table_width, k_blocks, 3))
         return check_hip(oasis::launch_row_select_plan(a, 3, as_stream(stream), t_stage_stop), fn);
     if (oasis::row_select_plan_fits(s->table_width, k_blocks, 1)) {
@@ -240,6 +242,16 @@ int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_
         if (int e = check_hip(oasis::launch_select_topk(sa, as_stream(stream)), fn)) return e;
     }
     return check_hip(oasis::launch_row_select_plan(a, 2, as_stream(stream), t_stage_stop), fn);
+}
+
+int oasis_select_plan_ex(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                         int32_t k_blocks, int32_t cap, int32_t step, const int32_t *step_dev,
+                         int32_t *sel, int32_t *slot_block, int32_t *last_use,
+                         int32_t *fetch_block, int32_t *fetch_slot, int32_t *fetch_count,
+                         void *stream) {
+    return select_plan_one_pass("oasis_select_plan", s, scores, ctx_len, k_blocks, cap, step,
+                                step_dev, sel, slot_block, last_use, slot_block, last_use,
+                                fetch_block, fetch_slot, fetch_count, stream);
 }
 
 size_t oasis_select_workspace_bytes(const oasis_shape *s, int32_t k_blocks) {
@@ -253,12 +265,14 @@ size_t oasis_select_workspace_bytes(const oasis_shape *s, int32_t k_blocks) {
     return (size_t)s->batch * s->num_kv_heads * chunks * k_blocks * 8;
 }
 
-int oasis_select_plan_ws(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
-                         int32_t k_blocks, int32_t cap, int32_t step, const int32_t *step_dev,
-                         int32_t *sel, int32_t *slot_block, int32_t *last_use,
-                         int32_t *fetch_block, int32_t *fetch_slot, int32_t *fetch_count,
-                         void *workspace, size_t workspace_bytes, void *stream) {
-    const char *fn = "oasis_select_plan_ws";
+// oasis_select_plan_ws with the plan starting from (sb_in, lu_in).
+static int select_plan_any_width(const char *fn, const oasis_shape *s, const float *scores,
+                                 const int32_t *ctx_len, int32_t k_blocks, int32_t cap,
+                                 int32_t step, const int32_t *step_dev, int32_t *sel,
+                                 const int32_t *sb_in, const int32_t *lu_in, int32_t *slot_block,
+                                 int32_t *last_use, int32_t *fetch_block, int32_t *fetch_slot,
+                                 int32_t *fetch_count, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
     if (int e = check_shape(s, fn)) return e;
     if (k_blocks < 1) return fail(OASIS_ERR_INVALID, "%s: k_blocks %d < 1", fn, k_blocks);
     if (k_blocks > oasis::kMaxKBlocks)
@@ -272,13 +286,14 @@ int oasis_select_plan_ws(const oasis_shape *s, const float *scores, const int32_
                     s->table_width, oasis::two_pass_max_width(k_blocks), k_blocks);
     if (s->batch == 0) return ok();
     if (!scores || !ctx_len || !sel) return fail(OASIS_ERR_INVALID, "%s: NULL pointer argument", fn);
-    if (plan && (!last_use || !fetch_count || (cap > 0 && (!fetch_block || !fetch_slot))))
+    if (plan && (!last_use || !fetch_count || !sb_in || !lu_in ||
+                 (cap > 0 && (!fetch_block || !fetch_slot))))
         return fail(OASIS_ERR_INVALID, "%s: NULL plan buffer", fn);
     if (s->table_width <= oasis::kTwoPassMinWidth) {      // one pass; no workspace needed
         if (plan)
-            return oasis_select_plan_ex(s, scores, ctx_len, k_blocks, cap, step, step_dev, sel,
-                                        slot_block, last_use, fetch_block, fetch_slot, fetch_count,
-                                        stream);
+            return select_plan_one_pass(fn, s, scores, ctx_len, k_blocks, cap, step, step_dev,
+                                        sel, sb_in, lu_in, slot_block, last_use, fetch_block,
+                                        fetch_slot, fetch_count, stream);
         return oasis_select_topk(s, scores, ctx_len, k_blocks, sel, stream);
     }
     const size_t need = oasis_select_workspace_bytes(s, k_blocks);
@@ -293,9 +308,54 @@ int oasis_select_plan_ws(const oasis_shape *s, const float *scores, const int32_
     int32_t *cand_idx = reinterpret_cast<int32_t *>(cand_key + (size_t)rows * chunks * k_blocks);
     oasis::SelectPlanArgs a{scores, ctx_len, sel, slot_block, last_use, fetch_block, fetch_slot,
                             fetch_count, rows, s->num_kv_heads, s->table_width, k_blocks,
-                            plan ? cap : 0, step, step_dev};
+                            plan ? cap : 0, step, step_dev, sb_in, lu_in};
     return check_hip(oasis::launch_two_pass_select_plan(a, plan ? 3 : 1, cand_key, cand_idx,
                                                         as_stream(stream), t_stage_stop), fn);
+}
+
+int oasis_select_plan_ws(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                         int32_t k_blocks, int32_t cap, int32_t step, const int32_t *step_dev,
+                         int32_t *sel, int32_t *slot_block, int32_t *last_use,
+                         int32_t *fetch_block, int32_t *fetch_slot, int32_t *fetch_count,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    return select_plan_any_width("oasis_select_plan_ws", s, scores, ctx_len, k_blocks, cap, step,
+                                 step_dev, sel, slot_block, last_use, slot_block, last_use,
+                                 fetch_block, fetch_slot, fetch_count, workspace,
+                                 workspace_bytes, stream);
+}
+
+// [a, a + n) and [b, b + n) (int32 entries) share an entry
+static bool overlap(const int32_t *a, const int32_t *b, size_t n) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + n * sizeof(int32_t) && y < x + n * sizeof(int32_t);
+}
+
+int oasis_select_plan_next(const oasis_shape *s, const float *scores, const int32_t *ctx_len,
+                           int32_t k_blocks, int32_t cap, int32_t step, const int32_t *step_dev,
+                           int32_t *sel, const int32_t *slot_block_in, const int32_t *last_use_in,
+                           int32_t *slot_block, int32_t *last_use, int32_t *fetch_block,
+                           int32_t *fetch_slot, int32_t *fetch_count, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    const char *fn = "oasis_select_plan_next";
+    if (int e = check_shape(s, fn)) return e;
+    if (!slot_block || !last_use || !slot_block_in || !last_use_in)
+        return fail(OASIS_ERR_INVALID, "%s: NULL working-set table", fn);
+    if (k_blocks >= 1) {
+        // each output array is either the matching input array itself (in
+        // place) or shares no entry with any input array
+        const size_t n = (size_t)(s->batch < 0 ? 0 : s->batch) * s->num_kv_heads * k_blocks;
+        const int32_t *outs[2] = {slot_block, last_use}, *ins[2] = {slot_block_in, last_use_in};
+        for (int o = 0; o < 2; ++o)
+            for (int i = 0; i < 2; ++i)
+                if (!(o == i && outs[o] == ins[i]) && overlap(outs[o], ins[i], n))
+                    return fail(OASIS_ERR_INVALID,
+                                "%s: an output table overlaps an input table without being it", fn);
+        if (overlap(slot_block, last_use, n))
+            return fail(OASIS_ERR_INVALID, "%s: slot_block and last_use overlap", fn);
+    }
+    return select_plan_any_width(fn, s, scores, ctx_len, k_blocks, cap, step, step_dev, sel,
+                                 slot_block_in, last_use_in, slot_block, last_use, fetch_block,
+                                 fetch_slot, fetch_count, workspace, workspace_bytes, stream);
 }
 
 size_t oasis_attn_workspace_bytes(const oasis_shape *s, int32_t n_q, int32_t n_blk) {
@@ -477,6 +537,17 @@ int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const ui
     if (sync->score_after)
         if (int e = check_hip(hipStreamWaitEvent(ss, ev(sync->score_after), 0), fn)) return e;
     const uint16_t *skp = L->score_k_pool ? L->score_k_pool : L->k_pool;
+    // Two copies of the working-set table (slot_block_next set): the plan of
+    // step s writes copy s & 1 (copy 1 = the *_next arrays) from copy
+    // (s - 1) & 1, which this call's attention (of step s - 1) reads.
+    const bool two = L->slot_block_next != nullptr;
+    if (two != (L->last_use_next != nullptr))
+        return fail(OASIS_ERR_INVALID, "%s: slot_block_next and last_use_next go together", fn);
+    const bool odd = (step & 1) != 0;
+    int32_t *sb_out = two && odd ? L->slot_block_next : L->slot_block;
+    int32_t *lu_out = two && odd ? L->last_use_next : L->last_use;
+    int32_t *sb_cur = two && !odd ? L->slot_block_next : L->slot_block;
+    int32_t *lu_cur = two && !odd ? L->last_use_next : L->last_use;
     int e = run_stage(sync->scored, ss, [&] {
         return L->ck ? oasis_score_blocks_minmax(&L->shape, q_look_next, L->n_look, L->ck,
                                                  L->refresh ? skp : nullptr,
@@ -490,19 +561,25 @@ int oasis_layer_step(const oasis_layer *L, const uint16_t *q_look_next, const ui
         if ((e = check_hip(hipStreamWaitEvent(as, ev(sync->attn_after), 0), fn))) return e;
     e = run_stage(ps != as ? sync->attended : nullptr, as, [&] {
         return oasis_sparse_decode_attn_ex(&L->shape, q, L->n_q, L->k_pool, L->v_pool,
-                                           L->block_table, L->slot_block, L->k_blocks,
-                                           L->slot_block, L->ctx_len, L->scale, L->out,
-                                           L->workspace, L->workspace_bytes, L->attn_flags, as);
+                                           L->block_table, sb_cur, L->k_blocks, sb_cur, L->ctx_len,
+                                           L->scale, L->out, L->workspace, L->workspace_bytes,
+                                           L->attn_flags, as);
     });
     if (e) return e;
-    if (ps != as)
-        if ((e = check_hip(hipStreamWaitEvent(ps, ev(sync->attended), 0), fn))) return e;
-    if ((e = check_hip(hipStreamWaitEvent(ps, ev(sync->scored), 0), fn))) return e;
+    // the plan rewrites the table copy that the attention waited for here
+    // last read: this call's attention, or with two copies (plan_after set)
+    // the attention of the call before
+    if (ps != as) {
+        void *after = two && sync->plan_after ? sync->plan_after : sync->attended;
+        if ((e = check_hip(hipStreamWaitEvent(ps, ev(after), 0), fn))) return e;
+    }
+    if (ps != ss)
+        if ((e = check_hip(hipStreamWaitEvent(ps, ev(sync->scored), 0), fn))) return e;
     return run_stage(sync->planned, ps, [&] {
-        return oasis_select_plan_ws(&L->shape, scores, L->ctx_len, L->k_blocks, L->cap, step,
-                                    nullptr, L->sel, L->slot_block, L->last_use, L->fetch_block,
-                                    L->fetch_slot, L->fetch_count, L->select_workspace,
-                                    L->select_workspace_bytes, ps);
+        return oasis_select_plan_next(&L->shape, scores, L->ctx_len, L->k_blocks, L->cap, step,
+                                      nullptr, L->sel, sb_cur, lu_cur, sb_out, lu_out,
+                                      L->fetch_block, L->fetch_slot, L->fetch_count,
+                                      L->select_workspace, L->select_workspace_bytes, ps);
     });
 }
 

@@ -38,6 +38,10 @@ struct SelectPlanArgs {
     int32_t *fetch_count;
     int rows, hkv, width, k, cap, step;
     const int32_t *step_dev;   // if set, *step_dev is added to step (read on the device)
+    // the working-set table the plan starts from (the plan writes slot_block /
+    // last_use): the same arrays when planning in place
+    const int32_t *slot_block_in;
+    const int32_t *last_use_in;
 };
 
 // Candidates of the two-pass selection of wide rows: each row split into

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
     const size_t rk = (size_t)row * K;
 
     PlanPrefetch pf;
-    if (MODE & 2) plan_prefetch(a.slot_block + rk, a.last_use + rk, K, pf);   // in flight during the select
+    if (MODE & 2) plan_prefetch(a.slot_block_in + rk, a.last_use_in + rk, K, pf);   // in flight during the select
     if (MODE & 1) {
         const int nb = load_row_keys(srow, a.width, a.ctx_len + row / a.hkv, keys);
         __syncthreads();
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kRowThreads) void row_merge_select_plan_kernel(
     uint32_t *keys = reinterpret_cast<uint32_t *>(MODE & 2 ? pl + 9 * Kp : pl);   // ncand
     const size_t rk = (size_t)row * K;
     PlanPrefetch pf;
-    if (MODE & 2) plan_prefetch(a.slot_block + rk, a.last_use + rk, K, pf);
+    if (MODE & 2) plan_prefetch(a.slot_block_in + rk, a.last_use_in + rk, K, pf);
     const int ctx_raw = a.ctx_len[row / a.hkv];
     const int ctx = ctx_raw < 0 ? 0 : ctx_raw;
     const int cb = ctx / kBlockTokens + (ctx % kBlockTokens != 0);

@@ -23,7 +23,7 @@ OASIS_OK, OASIS_ERR_INVALID, OASIS_ERR_UNSUPPORTED, OASIS_ERR_NOMEM, OASIS_ERR_H
 # Every symbol include/oasis.h declares.
 EXPORTS = ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax", "oasis_select_topk", "oasis_plan_fetch", "oasis_select_plan",
            "oasis_select_plan_ex", "oasis_select_workspace_bytes", "oasis_select_plan_ws",
-           "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_sparse_decode_attn_ex",
+           "oasis_select_plan_next", "oasis_attn_workspace_bytes", "oasis_sparse_decode_attn", "oasis_sparse_decode_attn_ex",
            "oasis_sparse_decode_attn_noalloc",
            "oasis_hostpool_create",
            "oasis_hostpool_device_pointer", "oasis_hostpool_destroy", "oasis_fetch_blocks",
@@ -49,14 +49,16 @@ class OasisLayer(ctypes.Structure):
                 ("fetch_slot", ctypes.c_void_p), ("fetch_count", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("score_k_pool", ctypes.c_void_p),
-                ("select_workspace", ctypes.c_void_p), ("select_workspace_bytes", ctypes.c_size_t)]
+                ("select_workspace", ctypes.c_void_p), ("select_workspace_bytes", ctypes.c_size_t),
+                ("slot_block_next", ctypes.c_void_p), ("last_use_next", ctypes.c_void_p)]
 
 
 class OasisStepSync(ctypes.Structure):
     """oasis_step_sync: streams and events (raw handles) of one oasis_layer_step."""
     _fields_ = [(n, ctypes.c_void_p) for n in ("score_stream", "attn_stream", "plan_stream",
                                                 "score_after", "attn_after", "scored",
-                                                "attended", "planned", "inputs")]
+                                                "attended", "planned", "inputs",
+                                                "plan_after")]
 
 
 class OasisError(RuntimeError):
@@ -88,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.oasis_select_workspace_bytes.argtypes = [S, i32]
         L.oasis_select_workspace_bytes.restype = sz
         L.oasis_select_plan_ws.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p, p, p, sz, p]
+        L.oasis_select_plan_next.argtypes = [S, p, p, i32, i32, i32, p, p, p, p, p, p, p, p, p, p,
+                                             sz, p]
         L.oasis_attn_workspace_bytes.argtypes = [S, i32, i32]
         L.oasis_attn_workspace_bytes.restype = sz
         L.oasis_sparse_decode_attn.argtypes = [S, p, i32, p, p, p, p, i32, p, p, f32, p, p, sz, p]
@@ -104,7 +108,7 @@ def lib() -> ctypes.CDLL:
         for fn in ("oasis_score_blocks", "oasis_pool_keys", "oasis_score_blocks_minmax",
                    "oasis_select_topk", "oasis_plan_fetch",
                    "oasis_select_plan", "oasis_select_plan_ex", "oasis_select_plan_ws",
-                   "oasis_layer_step",
+                   "oasis_select_plan_next", "oasis_layer_step",
                    "oasis_sparse_decode_attn",
                    "oasis_sparse_decode_attn_ex", "oasis_sparse_decode_attn_noalloc",
                    "oasis_hostpool_create",
@@ -306,16 +310,32 @@ def select_workspace_bytes(shape: OasisShape, k_blocks: int) -> int:
 
 def select_plan(shape: OasisShape, scores, ctx_len, k_blocks, cap, step, sel, slot_block,
                 last_use, fetch_block, fetch_slot, fetch_count, stream=None, step_dev=None,
-                workspace=None, check=True):
+                workspace=None, check=True, table_in=None):
     """select_topk then plan_fetch in one launch where the shape allows (same results).
     step_dev (int32 device tensor of one element, or None): the plan's step is
     step + step_dev[0], read on the device (oasis_select_plan_ex).  workspace
     (a device tensor of select_workspace_bytes() bytes): rows wider than 8,192
-    blocks take the two-pass selection (oasis_select_plan_ws)."""
+    blocks take the two-pass selection (oasis_select_plan_ws).  table_in
+    ((slot_block_in, last_use_in) or None): the plan starts from that table and
+    writes slot_block / last_use (oasis_select_plan_next); None: in place."""
     _check_tensors(*_plan_specs(shape, k_blocks, cap, sel, slot_block, last_use, fetch_block,
                                 fetch_slot, fetch_count, scores),
                    (ctx_len, "ctx_len", _I32, shape.batch),
                    (step_dev, "step_dev", _I32, 1, True), enabled=check)
+    if table_in is not None:
+        sb_in, lu_in = table_in
+        n = shape.batch * shape.num_kv_heads * k_blocks
+        _check_tensors((sb_in, "slot_block_in", _I32, n), (lu_in, "last_use_in", _I32, n),
+                       enabled=check)
+        if workspace is not None:
+            _check_ws(workspace)
+        _check(lib().oasis_select_plan_next(
+            ctypes.byref(shape), _ptr(scores), _ptr(ctx_len), k_blocks, cap, step, _ptr(step_dev),
+            _ptr(sel), _ptr(sb_in), _ptr(lu_in), _ptr(slot_block), _ptr(last_use),
+            _ptr(fetch_block), _ptr(fetch_slot), _ptr(fetch_count), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream(stream)))
+        return
     if workspace is not None:
         _check_ws(workspace)
         _check(lib().oasis_select_plan_ws(ctypes.byref(shape), _ptr(scores), _ptr(ctx_len),
@@ -426,18 +446,21 @@ def sparse_decode_attn_noalloc(shape: OasisShape, q, k_pool, v_pool, page_table,
     return out
 
 
-def layer_step(layer: OasisLayer, q_look_next, q, scores, step: int, sync: OasisStepSync):
+def layer_step(layer: OasisLayer, q_look_next, q, scores, step: int, sync: OasisStepSync,
+               check=True):
     """oasis_layer_step: score (q_look_next -> scores), attention (q), select + plan (step),
     ordered across the streams of `sync` by its events.  The layer's own buffers were
-    checked when its descriptor was built (DecodeLayer)."""
-    s = layer.shape
-    rows = s.batch * s.num_kv_heads
-    _check_tensors((q_look_next, "q_look_next", _BF16,
-                    _numel(s.batch, layer.n_look, s.num_q_heads, s.head_dim)),
-                   (q, "q", _BF16, _numel(s.batch, layer.n_q, s.num_q_heads, s.head_dim)),
-                   (scores, "scores", _F32, rows * s.table_width))
-    _check(lib().oasis_layer_step(ctypes.byref(layer), _ptr(q_look_next), _ptr(q), _ptr(scores),
-                                  step, ctypes.byref(sync)))
+    checked when its descriptor was built (DecodeLayer); check=False skips the checks of
+    the three tensors here, for a caller that has checked these very tensors before."""
+    if check:
+        s = layer.shape
+        rows = s.batch * s.num_kv_heads
+        _check_tensors((q_look_next, "q_look_next", _BF16,
+                        _numel(s.batch, layer.n_look, s.num_q_heads, s.head_dim)),
+                       (q, "q", _BF16, _numel(s.batch, layer.n_q, s.num_q_heads, s.head_dim)),
+                       (scores, "scores", _F32, rows * s.table_width))
+    _check(lib().oasis_layer_step(ctypes.byref(layer), q_look_next.data_ptr(), q.data_ptr(),
+                                  scores.data_ptr(), step, ctypes.byref(sync)))
 
 
 class HostPool:

@@ -149,8 +149,10 @@ class DecodeLayer:
                        self.k_blocks, self.cap, step, self.slot_block, self.last_use,
                        self.fetch_block, self.fetch_slot, self.fetch_count, stream)
 
-    def select_plan(self, step, stream=None, scores=None, step_dev=None):
-        """step_dev: the plan's step is step + step_dev[0], read on the device."""
+    def select_plan(self, step, stream=None, scores=None, step_dev=None, table_in=None):
+        """step_dev: the plan's step is step + step_dev[0], read on the device.
+        table_in: (slot_block, last_use) the plan starts from, written into this
+        layer's slot_block / last_use (None: planned in place)."""
         if scores is not None:
             ops._check_tensors((scores, "scores", torch.float32, self.scores.numel()))
         if step_dev is not None:
@@ -158,15 +160,21 @@ class DecodeLayer:
         ops.select_plan(self.shape, self.scores if scores is None else scores, self.ctx_len,
                         self.k_blocks, self.cap, step, self.sel, self.slot_block, self.last_use,
                         self.fetch_block, self.fetch_slot, self.fetch_count, stream,
-                        step_dev=step_dev, workspace=self.select_workspace, check=False)
+                        step_dev=step_dev, workspace=self.select_workspace, check=False,
+                        table_in=table_in)
 
-    def native_desc(self, share_gpu=True, refresh=False, k_pool=None, score_k_pool=None):
+    def native_desc(self, share_gpu=True, refresh=False, k_pool=None, score_k_pool=None,
+                    tables=None):
         """oasis_layer descriptor of this layer for oasis_layer_step (built once per
         setting; every pointer in it is a buffer this layer holds, or the key
-        pools given: k_pool for attention, score_k_pool for scoring)."""
+        pools given: k_pool for attention, score_k_pool for scoring).  tables:
+        two copies of the working-set table, ((slot_block, last_use), (slot_block,
+        last_use)), planned from one into the other by step parity; None: this
+        layer's table, planned in place."""
         kp = self.k_pool if k_pool is None else k_pool
+        tkey = None if tables is None else tuple(t.data_ptr() for pair in tables for t in pair)
         key = (share_gpu, refresh, kp.data_ptr(),
-               None if score_k_pool is None else score_k_pool.data_ptr())
+               None if score_k_pool is None else score_k_pool.data_ptr(), tkey)
         cache = self.__dict__.setdefault("_native", {})
         if key not in cache:
             D = self.shape.head_dim
@@ -177,8 +185,12 @@ class DecodeLayer:
                 block_table=vp(self.block_table), ctx_len=vp(self.ctx_len), ck=vp(self.ck),
                 refresh=int(refresh), n_look=self.n_look, n_q=self.n_q, k_blocks=self.k_blocks,
                 cap=self.cap, attn_flags=ops.OASIS_ATTN_SHARE_GPU if share_gpu else 0,
-                scale=float(D) ** -0.5, sel=vp(self.sel), slot_block=vp(self.slot_block),
-                last_use=vp(self.last_use), fetch_block=vp(self._fetch_block_buf),
+                scale=float(D) ** -0.5, sel=vp(self.sel),
+                slot_block=vp(self.slot_block if tables is None else tables[0][0]),
+                last_use=vp(self.last_use if tables is None else tables[0][1]),
+                slot_block_next=None if tables is None else vp(tables[1][0]),
+                last_use_next=None if tables is None else vp(tables[1][1]),
+                fetch_block=vp(self._fetch_block_buf),
                 fetch_slot=vp(self._fetch_slot_buf), fetch_count=vp(self.fetch_count),
                 out=vp(self.out), workspace=vp(self.workspace),
                 workspace_bytes=self.workspace.numel() * self.workspace.element_size(),
@@ -249,7 +261,7 @@ class PipelinedDecode:
     """
 
     def __init__(self, layer: DecodeLayer, side=None, plan_stream=None, native=False,
-                 share_gpu=True, k_pools=None, inputs="caller"):
+                 share_gpu=True, k_pools=None, inputs="caller", double_tables=False):
         """`side`: the stream the scoring runs on; `plan_stream`: the stream
         select + plan runs on (None: the caller's).  Several pipelines (one per
         layer) may share them, so that each runs layer after layer.  `native`:
@@ -265,7 +277,13 @@ class PipelinedDecode:
         after it.  "resident": every buffer the scoring reads was written
         before prime() (which waits for the caller's stream once) and stays
         unchanged, so steps add no wait on the caller's stream and the scoring
-        of one layer may start before the attention enqueued ahead of it."""
+        of one layer may start before the attention enqueued ahead of it.
+        `double_tables`: the working-set table is kept in two copies and the
+        plan of step s writes copy s % 2 from copy (s - 1) % 2, so the plan of
+        t + 1 waits for the attention of t - 1 (the last reader of the copy it
+        writes) instead of the attention of t; the layer's slot_block /
+        last_use attributes name the copy of the latest plan.  Steps must be
+        consecutive."""
         if inputs not in ("caller", "resident"):
             raise ValueError(f"inputs: 'caller' or 'resident', not {inputs!r}")
         if inputs == "resident" and k_pools is not None:
@@ -289,10 +307,19 @@ class PipelinedDecode:
         if k_pools is not None and len(k_pools) != 2:
             raise ValueError("k_pools: two key pools")
         self.k_pools = k_pools
+        self.tables = None
+        if double_tables:
+            # both copies start as the layer's table (the first plan may read either)
+            self.tables = ((layer.slot_block, layer.last_use),
+                           (layer.slot_block.clone(), layer.last_use.clone()))
+        self.ev_att = [torch.cuda.Event(), torch.cuda.Event()]   # attention of even / odd steps
+        self._syncs, self._descs, self._checked = {}, {}, {}     # native step: built once each
+        cur = torch.cuda.current_stream()
+        for e in self.ev_att:
+            e.record(cur)
         if native:
             # torch creates an event at its first record: create them now, so
             # that their handles can be handed to native code
-            cur = torch.cuda.current_stream()
             for e in (*self.ev_scored, *self.ev_planned, self.ev_attended, self.ev_inputs):
                 e.record(cur)
 
@@ -324,13 +351,21 @@ class PipelinedDecode:
     def _plan(self, b, step, main, after_attention=False):
         ps = main if self.plan_stream is None else self.plan_stream
         if ps is not main:
-            if after_attention:
+            if not after_attention:
+                ps.wait_stream(main)                    # inputs written on the caller's stream
+            elif self.tables is not None:
+                # the copy this plan writes was last read by the attention of step - 2
+                ps.wait_event(self.ev_att[step % 2])
+            else:
                 self.ev_attended.record(main)            # the plan rewrites what it read
                 ps.wait_event(self.ev_attended)
-            else:
-                ps.wait_stream(main)                    # inputs written on the caller's stream
         ps.wait_event(self.ev_scored[b])
-        self.L.select_plan(step, stream=ps, scores=self.buf[b])
+        if self.tables is not None:
+            table_in = self.tables[(step - 1) % 2]
+            self.L.slot_block, self.L.last_use = self.tables[step % 2]
+            self.L.select_plan(step, stream=ps, scores=self.buf[b], table_in=table_in)
+        else:
+            self.L.select_plan(step, stream=ps, scores=self.buf[b])
         self.ev_planned[b].record(ps)
         self.last_plan = self.ev_planned[b]
         self.used[b] = True
@@ -358,30 +393,60 @@ class PipelinedDecode:
             main.wait_event(self.last_plan)             # the working set of `step`
         b = self._score_next(q_look_next, main, score_events, append, step=step + 1)
         self.L.attend(q, stream=main, share_gpu=self.share_gpu, k_pool=self._pool(step))
+        if self.tables is not None:
+            self.ev_att[step % 2].record(main)
         out = self.L.out.clone() if copy_out else None
         self._plan(b, step + 1, main, after_attention=True)
         return out
 
     def _native_step(self, q, q_look_next, step, main, append):
-        """The same step as the Python path below, through oasis_layer_step."""
+        """The same step as the Python path below, through oasis_layer_step.
+        The call's stream/event set and layer descriptor take a few distinct
+        values (by score buffer, step parity and the caller's stream), so each
+        is built once and reused: the host time per step is then the native
+        call's."""
         b = self.i % 2
-        # as in _score_next: the inputs event orders scoring after the caller's
-        # stream; a plan that last read buf[b] and that the caller's stream
-        # does not order is waited for
-        caller = self.inputs == "caller"
-        score_after = (self.ev_planned[b] if self.used[b] and
-                       (self.plan_stream is not None or not caller) else None)
-        ps = main if self.plan_stream is None else self.plan_stream
-        attn_after = self.last_plan if self.plan_stream is not None else None
-        h = lambda x: None if x is None else x.cuda_event
-        sync = ops.OasisStepSync(score_stream=self.side.cuda_stream, attn_stream=main.cuda_stream,
-                                 plan_stream=ps.cuda_stream, score_after=h(score_after),
-                                 attn_after=h(attn_after), scored=h(self.ev_scored[b]),
-                                 attended=h(self.ev_attended), planned=h(self.ev_planned[b]),
-                                 inputs=h(self.ev_inputs) if caller else None)
-        desc = self.L.native_desc(share_gpu=self.share_gpu, refresh=append,
-                                  k_pool=self._pool(step), score_k_pool=self._pool(step + 1))
-        ops.layer_step(desc, q_look_next, q, self.buf[b], step + 1, sync)
+        two = self.tables is not None
+        parity = step % 2
+        key = (b, self.used[b], id(self.last_plan), parity if two else 0, main.cuda_stream)
+        sync = self._syncs.get(key)
+        if sync is None:
+            # as in _score_next: the inputs event orders scoring after the
+            # caller's stream; a plan that last read buf[b] and that the
+            # caller's stream does not order is waited for
+            caller = self.inputs == "caller"
+            score_after = (self.ev_planned[b] if self.used[b] and
+                           (self.plan_stream is not None or not caller) else None)
+            ps = main if self.plan_stream is None else self.plan_stream
+            attn_after = self.last_plan if self.plan_stream is not None else None
+            h = lambda x: None if x is None else x.cuda_event
+            sync = ops.OasisStepSync(
+                score_stream=self.side.cuda_stream, attn_stream=main.cuda_stream,
+                plan_stream=ps.cuda_stream, score_after=h(score_after), attn_after=h(attn_after),
+                scored=h(self.ev_scored[b]),
+                attended=h(self.ev_att[parity] if two else self.ev_attended),
+                planned=h(self.ev_planned[b]), inputs=h(self.ev_inputs) if caller else None,
+                plan_after=h(self.ev_att[1 - parity]) if two else None)
+            self._syncs[key] = sync
+        dkey = (append, parity if self.k_pools is not None else 0)
+        desc = self._descs.get(dkey)
+        if desc is None:
+            desc = self.L.native_desc(share_gpu=self.share_gpu, refresh=append,
+                                      k_pool=self._pool(step), score_k_pool=self._pool(step + 1),
+                                      tables=self.tables)
+            self._descs[dkey] = desc
+        desc.cap = self.L.cap               # the one field a caller changes between steps
+        # the per-step tensors are checked the first time each is seen (held
+        # here, so that an id is not reused by another tensor meanwhile)
+        seen = self._checked
+        fresh = id(q) not in seen or id(q_look_next) not in seen
+        if fresh and len(seen) > 64:
+            seen.clear()
+        ops.layer_step(desc, q_look_next, q, self.buf[b], step + 1, sync, check=fresh)
+        if fresh:
+            seen[id(q)], seen[id(q_look_next)] = q, q_look_next
+        if two:
+            self.L.slot_block, self.L.last_use = self.tables[(step + 1) % 2]
         self.last_plan = self.ev_planned[b]
         self.used[b] = True
         self.i += 1

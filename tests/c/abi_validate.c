@@ -126,6 +126,27 @@ int main(void) {
     EXPECT(oasis_select_plan_ws(&s, NULL, NULL, 128, 2, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
                                 NULL, 0, NULL), OASIS_OK);
 
+    /* planning from one table copy into another: the tables are required, and
+       an output array is its input array or shares no entry with the inputs
+       (ok: 4 rows x 8 entries = 32 per array) */
+    EXPECT(oasis_select_plan_next(&ok, PF, PI, 8, 2, 0, NULL, PI, NULL, PI + 100, PI + 200, PI + 300,
+                                  PI, PI, PI, NULL, 0, NULL), OASIS_ERR_INVALID);
+    EXPECT(oasis_select_plan_next(&ok, PF, PI, 8, 2, 0, NULL, PI, PI + 100, PI + 200, NULL, PI + 300,
+                                  PI, PI, PI, NULL, 0, NULL), OASIS_ERR_INVALID);
+    EXPECT(oasis_select_plan_next(&ok, PF, PI, 8, 2, 0, NULL, PI, PI + 100, PI + 200, PI + 101,
+                                  PI + 300, PI, PI, PI, NULL, 0, NULL), OASIS_ERR_INVALID);
+    EXPECT(oasis_select_plan_next(&ok, PF, PI, 8, 2, 0, NULL, PI, PI + 100, PI + 200, PI + 231,
+                                  PI + 300, PI, PI, PI, NULL, 0, NULL), OASIS_ERR_INVALID);
+    EXPECT(oasis_select_plan_next(&ok, PF, PI, 8, 2, 0, NULL, PI, PI + 100, PI + 200, PI + 100,
+                                  PI + 116, PI, PI, PI, NULL, 0, NULL), OASIS_ERR_INVALID);
+    EXPECT(oasis_select_plan_next(&ok, PF, PI, 8, 2, 0, NULL, PI, PI + 100, PI + 200, PI + 300,
+                                  PI + 300, PI, PI, PI, NULL, 0, NULL), OASIS_ERR_INVALID);
+    EXPECT(oasis_select_plan_next(&ok, PF, PI, 8, 9, 0, NULL, PI, PI + 100, PI + 200, PI + 300,
+                                  PI + 400, PI, PI, PI, NULL, 0, NULL), OASIS_ERR_INVALID);
+    s = shape(0, 8, 2, 128, 16, 64, 128);
+    EXPECT(oasis_select_plan_next(&s, NULL, NULL, 8, 2, 0, NULL, NULL, PI, PI + 100, PI, PI + 100,
+                                  NULL, NULL, NULL, NULL, 0, NULL), OASIS_OK);   /* in place, no rows */
+
     /* attention: workspace sizes at the extremes must not overflow */
     (void)oasis_attn_workspace_bytes(&big, 1, INT32_MAX);
     (void)oasis_attn_workspace_bytes(&big, INT32_MAX, 1);
@@ -191,6 +212,10 @@ int main(void) {
     EXPECT(oasis_layer_step(NULL, P16, P16, PF, 0, &sync), OASIS_ERR_INVALID);
     EXPECT(oasis_layer_step(&layer, P16, P16, PF, 0, NULL), OASIS_ERR_INVALID);
     EXPECT(oasis_layer_step(&layer, P16, P16, PF, 0, &sync), OASIS_ERR_INVALID);   /* no events */
+    sync.scored = PV;
+    sync.attended = PV;
+    layer.slot_block_next = PI;                                        /* without last_use_next */
+    EXPECT(oasis_layer_step(&layer, P16, P16, PF, 0, &sync), OASIS_ERR_INVALID);
 
     /* status text */
     if (strcmp(oasis_status_string(OASIS_ERR_NOMEM), "OASIS_ERR_NOMEM") != 0 ||

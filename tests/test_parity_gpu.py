@@ -332,6 +332,46 @@ def test_two_pass_select_plan_bit_exact_over_steps(case):
         np.testing.assert_array_equal(g_lu.cpu().numpy(), lu)
 
 
+@pytest.mark.parametrize("case", [(2, 4, 2048, 128, 2), (2, 2, 8192, 1024, 9),
+                                  (2, 2, 12000, 128, 6)], ids=lambda c: f"W{c[2]}K{c[3]}")
+def test_select_plan_next_plans_from_one_table_copy_into_the_other(case):
+    """oasis_select_plan_next: the plan starts from one copy of the working-set
+    table and writes the other, over chained steps with the copies swapping
+    roles; the written copy is the oracle's new table, bit for bit, and the
+    copy read is left as it was.  One pass fused, one pass with a separate
+    plan launch (K = 1,024) and two passes (12,000 blocks)."""
+    B, Hkv, W, K, cap = case
+    rng = np.random.default_rng(W + K)
+    ctx_len = np.array([16 * W - 5, 16 * (W // 2) + 3], np.int32)
+    shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
+    need = ops.select_workspace_bytes(shape, K)
+    ws = torch.empty((need // 8 + 1,), dtype=torch.int64, device=DEV) if need else None
+    sb, lu = _random_state(rng, B, Hkv, K, W // 2, None)
+    copies = [(dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))),
+              (torch.full((B, Hkv, K), -9, dtype=torch.int32, device=DEV),
+               torch.full((B, Hkv, K), -9, dtype=torch.int32, device=DEV))]
+    g_ctx = dev(torch.from_numpy(ctx_len))
+    sel = torch.empty((B, Hkv, K), dtype=torch.int32, device=DEV)
+    fb = torch.empty((B, Hkv, cap), dtype=torch.int32, device=DEV)
+    fs, fc = torch.empty_like(fb), torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    for step in range(4):
+        src, dst = copies[step % 2], copies[(step + 1) % 2]
+        before = [t.clone() for t in src]
+        sc = _random_scores(rng, B, Hkv, W, "ties" if step % 2 else "normal")
+        osel = orc.select(sc.astype(np.float64), ctx_len, 16, K)
+        ofb, ofs, ocnt, sb, lu = orc.plan(osel, sc.astype(np.float64), sb, lu, cap, 10 + step)
+        ops.select_plan(shape, dev(torch.from_numpy(sc)), g_ctx, K, cap, 10 + step, sel,
+                        dst[0], dst[1], fb, fs, fc, workspace=ws, table_in=src)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(sel.cpu().numpy(), osel)
+        np.testing.assert_array_equal(fc.cpu().numpy(), ocnt)
+        np.testing.assert_array_equal(fb.cpu().numpy(), ofb)
+        np.testing.assert_array_equal(fs.cpu().numpy(), ofs)
+        np.testing.assert_array_equal(dst[0].cpu().numpy(), sb)
+        np.testing.assert_array_equal(dst[1].cpu().numpy(), lu)
+        assert all(torch.equal(x, y) for x, y in zip(before, src))
+
+
 def test_select_plan_ws_without_workspace_at_one_pass_widths():
     """Up to 8,192 blocks the workspace call needs no workspace and gives the
     one-pass results."""
@@ -798,11 +838,14 @@ def test_decode_steps_mid_size_with_lru(n_look):
     assert exempt <= len(rows) * 6 // 4
 
 
-@pytest.mark.parametrize("plan_stream", [False, True])
-def test_pipelined_decode_matches_sequential_steps(plan_stream):
+@pytest.mark.parametrize("plan_stream,double", [(False, False), (True, False), (True, True),
+                                                (False, True)])
+def test_pipelined_decode_matches_sequential_steps(plan_stream, double):
     """Scoring of step t + 1 on a side stream, overlapped with attention of
     step t (and, with plan_stream, select + plan on a third stream), gives
-    bit-identical outputs and state to the plain step order."""
+    bit-identical outputs and state to the plain step order; also with the
+    working-set table in two copies (the plan of t + 1 written beside the
+    table attention of t reads)."""
     wl = wlm.small_workload(batch=4, q_heads=32, kv_heads=8, head_dim=128,
                             ctx=(8192, 6000, 4096, 7000), budget=1024, n_hot=24, ratio=0.05, seed=43)
     d = wlm.make_layer(wl)
@@ -818,7 +861,8 @@ def test_pipelined_decode_matches_sequential_steps(plan_stream):
     seq.score(looks[T])
     seq.select_plan(T)
     pipe_layer = _gpu_layer(wl, d, wl.cap(), sb, lu)
-    pipe = PipelinedDecode(pipe_layer, plan_stream=torch.cuda.Stream() if plan_stream else None)
+    pipe = PipelinedDecode(pipe_layer, plan_stream=torch.cuda.Stream() if plan_stream else None,
+                           double_tables=double)
     pipe.prime(looks[0], 0)
     got = [pipe.step(q, looks[t + 1], t) for t in range(T)]
     pipe.drain()
@@ -839,8 +883,8 @@ def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch, s
     plan, with the same event waits and records) from native code: per-step
     outputs and the final state are bit-identical to the Python pipeline's,
     over several layers taking turns on shared streams, also with resident
-    inputs (scoring not ordered after the caller's stream at each step).
-    32 and 128 rows."""
+    inputs (scoring not ordered after the caller's stream at each step) and
+    with the working-set table in two copies.  32 and 128 rows."""
     wl = wlm.small_workload(batch=batch, q_heads=32, kv_heads=8, head_dim=128,
                             ctx=(4096, 3000, 2500, 4000), budget=512, n_hot=12, ratio=0.125, seed=44,
                             n_look=max(1, drafts))
@@ -853,14 +897,16 @@ def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch, s
               for t in range(T + 1)] for l, d in enumerate(datas)]
     append = scorer == "minmax"
     runs = {}
-    for native, inputs in ((False, "caller"), (True, "caller"), (False, "resident"),
-                           (True, "resident")):
+    for native, inputs, double in ((False, "caller", False), (True, "caller", False),
+                                   (False, "resident", False), (True, "resident", False),
+                                   (False, "resident", True), (True, "resident", True),
+                                   (True, "caller", True)):
         sb, lu = (x.numpy() for x in wlm.empty_state(wl))
         layers = [_gpu_layer(wl, d, wl.cap(), sb, lu, scorer=scorer, n_q=n_q) for d in datas]
         side = torch.cuda.Stream()
         ps = torch.cuda.Stream() if plan_stream else None
         pipes = [PipelinedDecode(L, side=side, plan_stream=ps, native=native, share_gpu=share,
-                                 inputs=inputs) for L in layers]
+                                 inputs=inputs, double_tables=double) for L in layers]
         for l, P in enumerate(pipes):
             P.prime(looks[l][0], 0, append=append)
         outs = []
@@ -871,10 +917,10 @@ def test_native_layer_step_matches_python_pipeline(scorer, plan_stream, batch, s
         for P in pipes:
             P.drain()
         torch.cuda.synchronize()
-        runs[native, inputs] = (outs, [{k: getattr(L, k).clone() for k in
-                                        ("sel", "slot_block", "last_use", "fetch_count")}
-                                       for L in layers])
-    o_py, st_py = runs[False, "caller"]
+        runs[native, inputs, double] = (outs, [{k: getattr(L, k).clone() for k in
+                                                ("sel", "slot_block", "last_use", "fetch_count")}
+                                               for L in layers])
+    o_py, st_py = runs[False, "caller", False]
     for key, (o_other, st_other) in runs.items():
         for i, (a, b) in enumerate(zip(o_py, o_other)):
             assert torch.equal(a, b), (key, i)
