@@ -787,9 +787,32 @@ def main():
             L.score(looks[(r + j) % N_LOOK_DRAWS], scores=buf, refresh=append)
             pair.append(buf)
         alt.append(pair)
+    # Select + plan takes about 13 us of GPU time, close to the Python cost of
+    # a layer's select_plan() call, so the loop calls the library entry point
+    # with its arguments marshalled once per replica and score buffer: the
+    # loop then measures the kernel, not the interpreter.
+    import ctypes
+    lib = ops.lib()
+
+    def sp_args(L, buf):
+        ws = L.select_workspace
+        return (ctypes.byref(L.shape), buf.data_ptr(), L.ctx_len.data_ptr(), L.k_blocks, L.cap,
+                L.sel.data_ptr(), L.slot_block.data_ptr(), L.last_use.data_ptr(),
+                L.fetch_block.data_ptr(), L.fetch_slot.data_ptr(), L.fetch_count.data_ptr(),
+                None if ws is None else ws.data_ptr(),
+                0 if ws is None else ws.numel() * ws.element_size(),
+                torch.cuda.current_stream().cuda_stream)
+    sp = [[sp_args(L, buf) for buf in alt[r]] for r, L in enumerate(layers)]
+
+    def select_plan_raw(i):
+        sh, sc, ctx, k, c, sel, sb, lu, fb, fs, fc, ws, wsb, st = sp[i % n_rep][(i // n_rep) % 2]
+        status = lib.oasis_select_plan_ws(sh, sc, ctx, k, c, 3000 + i, None, sel, sb, lu, fb, fs,
+                                          fc, ws, wsb, st)
+        if status:
+            raise ops.OasisError(status, ops.last_error())
+
     stages = [("score", lambda i, L: L.score(draw(i), refresh=append)),
-              ("select_plan", lambda i, L: L.select_plan(3000 + i,
-                                                         scores=alt[i % n_rep][(i // n_rep) % 2])),
+              ("select_plan", lambda i, L: select_plan_raw(i)),
               ("attn", lambda i, L: L.attend(q))]
     if share_gpu:
         # the launch shape the timed step uses for attention (one CU per row)

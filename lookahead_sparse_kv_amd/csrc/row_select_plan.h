@@ -53,9 +53,12 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // bounds of the [B][Hkv][W] scores, with no branch around the loads), so the
 // first round does not wait for the context length, which is loaded beside it
 // and applied when the keys are written.
+constexpr int kKeyRegs = 8;              // keys a thread holds in registers: n = u * kRowThreads + tid
+
+
 __device__ __forceinline__ int load_row_keys(const float *srow, int width, const int32_t *ctx_p,
-                                             uint32_t *keys) {
-    constexpr int U = 8;
+                                             uint32_t *keys, uint32_t (&kr)[kKeyRegs]) {
+    constexpr int U = kKeyRegs;
     constexpr int kRound = kRowThreads * U;
     if (width <= 0) return 0;
     const int ctx_raw = *ctx_p;
@@ -72,7 +75,8 @@ __device__ __forceinline__ int load_row_keys(const float *srow, int width, const
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int n = u * kRowThreads + (int)threadIdx.x;
-        if (n < nb) keys[n] = score_key(v[u]);
+        kr[u] = score_key(v[u]);
+        if (n < nb) keys[n] = kr[u];
     }
     for (int n0 = kRound; n0 < nb; n0 += kRound) {      // rows longer than one round
 #pragma unroll
@@ -110,14 +114,17 @@ struct RowShared {
     int wave_sums[kRowWaves];
     uint32_t wave_min[kRowWaves], wave_max[kRowWaves];
     int digit, above, count;
-    uint32_t gkey[kRankMax];                // keys of a small threshold bin
-    int gidx[kRankMax];
+    alignas(16) uint32_t gkey[kRankMax];    // keys of a small threshold bin
+    int rank_acc[kRankMax];                 // per gathered key: (keys above) | (keys at or above) << 16
     int ngather, gt_in_bin;
     uint32_t tau;
 };
 
 // Top-K of `nb` keys (keys[0..nb), already in LDS) into sel[0..K): ascending,
 // -1 padded.  Ends with a barrier; sel may then be read by every thread.
+// REGS: every key of the row is also in the calling thread's registers, kr[u]
+// = keys[u * kRowThreads + tid] (nb <= kKeyRegs * kRowThreads), so the passes
+// over all keys read registers instead of LDS.
 //
 // The radix digits are taken from u - kmin over the row's own key range
 // [kmin, kmax], the first one being the top 11 bits of that span: block scores
@@ -126,10 +133,12 @@ struct RowShared {
 // that finds the threshold bin holding exactly the keys still to take ends the
 // search: every key from that bin's base up is taken, with no tie to split.
 // A threshold bin of at most kRankMax keys ends it too: those keys are
-// gathered and ranked against each other (key descending, then block index
-// ascending), which gives the K-th largest key exactly.
+// gathered and counted against each other, which gives the K-th largest key
+// exactly (the key tau with fewer than krem keys above it in the bin and at
+// least krem at or above it).
+template <bool REGS>
 __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, int *sel,
-                                           RowShared &sh) {
+                                           RowShared &sh, const uint32_t (&kr)[kKeyRegs]) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -138,13 +147,24 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
         __syncthreads();
         return;
     }
+    // f(u, n) over every key u = keys[n], n < nb, of this thread
+    const auto each_key = [&](auto &&f) {
+        if constexpr (REGS) {
+#pragma unroll
+            for (int u = 0; u < kKeyRegs; ++u) {
+                const int n = u * kRowThreads + tid;
+                if (n < nb) f(kr[u], n);
+            }
+        } else {
+            for (int n = tid; n < nb; n += kRowThreads) f(keys[n], n);
+        }
+    };
     // the row's key range (and the first histogram cleared)
     uint32_t kmn = 0xffffffffu, kmx = 0u;
-    for (int n = tid; n < nb; n += kRowThreads) {
-        const uint32_t u = keys[n];
+    each_key([&](uint32_t u, int) {
         kmn = u < kmn ? u : kmn;
         kmx = u > kmx ? u : kmx;
-    }
+    });
     kmn = wave_min_u32(kmn);
     kmx = wave_max_u32(kmx);
     if (lane == 0) { sh.wave_min[wave] = kmn; sh.wave_max[wave] = kmx; }
@@ -171,10 +191,10 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
             for (int i = tid; i < sbins; i += kRowThreads) sh.hist[i] = 0;
             __syncthreads();
         }
-        for (int n = tid; n < nb; n += kRowThreads) {
-            const uint32_t d = keys[n] - kmin;
+        each_key([&](uint32_t u, int) {
+            const uint32_t d = u - kmin;
             if ((d & pmask) == prefix) atomicAdd(&sh.hist[(d >> shift) & (uint32_t)(nbins - 1)], 1);
-        }
+        });
         __syncthreads();
         // thread t owns `per` bins counted from the top: bins hi, hi-1, .., lo
         // (its counts held in registers for the search below)
@@ -211,26 +231,76 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
         __syncthreads();                          // digit / above / count are rewritten next pass
         if (whole || shift == 0) break;
         if (cnt <= kRankMax) {
-            // the cnt keys left in the threshold bin, ranked directly
-            for (int n = tid; n < nb; n += kRowThreads) {
-                const uint32_t u = keys[n];
-                if (((u - kmin) & pmask) == prefix) {
-                    const int slot = atomicAdd(&sh.ngather, 1);
-                    sh.gkey[slot] = u;
-                    sh.gidx[slot] = n;
+            // the cnt keys left in the threshold bin, gathered: a ballot of
+            // the matching lanes per round, one slot reservation per wave
+            if (tid < kRankMax) sh.rank_acc[tid] = 0;
+            const auto below = [](uint64_t bal) {
+                return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            };
+            if constexpr (REGS) {
+                uint64_t bal[kKeyRegs];
+                int total = 0;
+#pragma unroll
+                for (int u = 0; u < kKeyRegs; ++u) {
+                    const int n = u * kRowThreads + tid;
+                    bal[u] = __ballot(n < nb && ((kr[u] - kmin) & pmask) == prefix);
+                    total += __popcll(bal[u]);
+                }
+                if (total) {
+                    int base = 0;
+                    if (lane == 0) base = atomicAdd(&sh.ngather, total);
+                    base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+                    for (int u = 0; u < kKeyRegs; ++u) {
+                        if ((bal[u] >> lane) & 1) sh.gkey[base + below(bal[u])] = kr[u];
+                        base += __popcll(bal[u]);
+                    }
+                }
+            } else {
+                for (int n0 = 0; n0 < nb; n0 += kRowThreads) {     // uniform trip count
+                    const int n = n0 + tid;
+                    const uint32_t u = n < nb ? keys[n] : 0u;
+                    const bool m = n < nb && ((u - kmin) & pmask) == prefix;
+                    const uint64_t bal = __ballot(m);
+                    if (bal) {
+                        int base = 0;
+                        if (lane == 0) base = atomicAdd(&sh.ngather, __popcll(bal));
+                        base = __builtin_amdgcn_readfirstlane(base);
+                        if (m) sh.gkey[base + below(bal)] = u;
+                    }
                 }
             }
             __syncthreads();
-            if (tid < cnt) {
-                const uint32_t kj = sh.gkey[tid];
-                const int ij = sh.gidx[tid];
-                int rank = 0, gt = 0;
-                for (int i = 0; i < cnt; ++i) {
-                    const uint32_t ki = sh.gkey[i];
-                    rank += (ki > kj) | ((ki == kj) & (sh.gidx[i] < ij));
-                    gt += ki > kj;
+            // the bin's keys counted against each other, the comparisons
+            // spread over every wave: wave w compares key j (lane j) with
+            // keys [w * S, w * S + S) and adds (above, at or above) to key j's
+            // tally.  Key j is tau when fewer than krem keys lie above it
+            // and at least krem at or above it (every copy of tau agrees).
+            constexpr int S = kRankMax / kRowWaves;
+            if (lane < cnt) {
+                const uint32_t kj = sh.gkey[lane];
+                int gt = 0, ge = 0;
+#pragma unroll
+                for (int c0 = 0; c0 < S; c0 += 4) {
+                    const int i0 = wave * S + c0;
+                    if (i0 >= cnt) break;
+                    const uint4 k4 = *reinterpret_cast<const uint4 *>(&sh.gkey[i0]);
+                    const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const bool in = i0 + c < cnt;
+                        gt += in && kk[c] > kj;
+                        ge += in && kk[c] >= kj;
+                    }
                 }
-                if (rank == krem - 1) { sh.tau = kj; sh.gt_in_bin = gt; }
+                if (gt | ge) atomicAdd(&sh.rank_acc[lane], gt | (ge << 16));
+            }
+            __syncthreads();
+            if (tid < cnt) {
+                const int t = sh.rank_acc[tid];
+                const int gt = t & 0xffff, ge = t >> 16;
+                if (gt < krem && krem <= ge) { sh.tau = sh.gkey[tid]; sh.gt_in_bin = gt; }
             }
             __syncthreads();
             prefix = sh.tau - kmin;                // tau = kmin + prefix, exactly
@@ -248,10 +318,22 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
     const int lo = tid * E;
     const int hi = lo + E < nb ? lo + E : nb;
     int c_gt = 0, c_eq = 0;
-    for (int n = lo; n < hi; ++n) {
-        const uint32_t u = keys[n];
-        c_gt += whole ? u >= tau : u > tau;
-        c_eq += !whole && u == tau;
+    uint32_t ck[kKeyRegs];                        // this thread's chunk, when it fits
+    if (E <= kKeyRegs) {
+#pragma unroll
+        for (int i = 0; i < kKeyRegs; ++i) ck[i] = lo + i < hi ? keys[lo + i] : 0u;
+#pragma unroll
+        for (int i = 0; i < kKeyRegs; ++i) {
+            const bool in = lo + i < hi;
+            c_gt += in && (whole ? ck[i] >= tau : ck[i] > tau);
+            c_eq += in && !whole && ck[i] == tau;
+        }
+    } else {
+        for (int n = lo; n < hi; ++n) {
+            const uint32_t u = keys[n];
+            c_gt += whole ? u >= tau : u > tau;
+            c_eq += !whole && u == tau;
+        }
     }
     // one scan of both counts (each < 2^16): the keys taken before this
     // thread's chunk are all the larger ones and the first krem copies of tau
@@ -261,13 +343,31 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
     const int eq_before = before >> 16;
     int pos = gt_before + (eq_before < krem ? eq_before : krem);
     int er = eq_before;
-    for (int n = lo; n < hi; ++n) {
-        const uint32_t u = keys[n];
-        bool take = whole ? u >= tau : u > tau;
-        if (!whole && u == tau) { take = er < krem; ++er; }
-        if (take) sel[pos++] = n;
+    if (E <= kKeyRegs) {
+#pragma unroll
+        for (int i = 0; i < kKeyRegs; ++i) {
+            if (lo + i >= hi) break;
+            const uint32_t u = ck[i];
+            bool take = whole ? u >= tau : u > tau;
+            if (!whole && u == tau) { take = er < krem; ++er; }
+            if (take) sel[pos++] = lo + i;
+        }
+    } else {
+        for (int n = lo; n < hi; ++n) {
+            const uint32_t u = keys[n];
+            bool take = whole ? u >= tau : u > tau;
+            if (!whole && u == tau) { take = er < krem; ++er; }
+            if (take) sel[pos++] = n;
+        }
     }
     __syncthreads();
+}
+
+// Without the keys in registers.
+__device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, int *sel,
+                                           RowShared &sh) {
+    const uint32_t none[kKeyRegs] = {};
+    row_select<false>(keys, nb, K, sel, sh, none);
 }
 
 __device__ __forceinline__ int4 ld_i4(const int *p) { return *reinterpret_cast<const int4 *>(p); }
@@ -494,9 +594,15 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
                 const float sc = m_score[mp[u]];
                 const int blk = m_block[mp[u]];
                 int rank = 0;
-                for (int q = 0; q < M; ++q) {
-                    const float s2 = m_score[q];
-                    rank += (s2 > sc) | ((s2 == sc) & (m_block[q] < blk));
+#pragma unroll 2
+                for (int q0 = 0; q0 < M; q0 += 4) {      // four misses per 16-byte read
+                    const float4 s4 = ld_f4(m_score + q0);
+                    const int4 b4 = ld_i4(m_block + q0);
+                    const float ss[4] = {s4.x, s4.y, s4.z, s4.w};
+                    const int bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        rank += (q0 + c < M) & ((ss[c] > sc) | ((ss[c] == sc) & (bb[c] < blk)));
                 }
                 fetched[u] = rank < cap;
                 m_rank[mp[u]] = rank;
@@ -509,9 +615,15 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
         if (cand[u] && n_victims > 0) {
             const int l0 = lu[lo + u], b0 = sb[lo + u];
             int rank = 0;
-            for (int q = 0; q < C; ++q) {
-                const int l2 = c_lu[q];
-                rank += (l2 < l0) | ((l2 == l0) & (c_block[q] < b0));
+#pragma unroll 2
+            for (int q0 = 0; q0 < C; q0 += 4) {          // four candidates per 16-byte read
+                const int4 l4 = ld_i4(c_lu + q0);
+                const int4 b4 = ld_i4(c_block + q0);
+                const int ll[4] = {l4.x, l4.y, l4.z, l4.w};
+                const int bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    rank += (q0 + c < C) & ((ll[c] < l0) | ((ll[c] == l0) & (bb[c] < b0)));
             }
             if (rank < n_victims) dest[nfree + rank] = lo + u;
         }
@@ -525,7 +637,13 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
             int fpos = mp[u];
             if (M > cap) {
                 fpos = 0;
-                for (int q = 0; q < mp[u]; ++q) fpos += m_rank[q] < cap;
+#pragma unroll 2
+                for (int q0 = 0; q0 < mp[u]; q0 += 4) {
+                    const int4 r4 = ld_i4(m_rank + q0);
+                    const int rr[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) fpos += (q0 + c < mp[u]) & (rr[c] < cap);
+                }
             }
             if (fpos >= nF) continue;   // only a selection with repeated blocks gets here
             const int blk = sel[lo + u];

@@ -24,7 +24,7 @@ __device__ __forceinline__ float key_to_score(uint32_t k) {
 // MODE 1 = select, 2 = plan (selection read from a.sel), 3 = select then plan.
 template <int MODE>
 __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlanArgs a) {
-    extern __shared__ int dyn[];
+    extern __shared__ __attribute__((aligned(16))) int dyn[];   // 16-byte vector reads
     __shared__ RowShared sh;
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
@@ -39,9 +39,13 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
     PlanPrefetch pf;
     if (MODE & 2) plan_prefetch(a.slot_block_in + rk, a.last_use_in + rk, K, pf);   // in flight during the select
     if (MODE & 1) {
-        const int nb = load_row_keys(srow, a.width, a.ctx_len + row / a.hkv, keys);
+        uint32_t kr[kKeyRegs];
+        const int nb = load_row_keys(srow, a.width, a.ctx_len + row / a.hkv, keys, kr);
         __syncthreads();
-        row_select(keys, nb, K, sel, sh);
+        if (nb <= kKeyRegs * kRowThreads)
+            row_select<true>(keys, nb, K, sel, sh, kr);
+        else
+            row_select(keys, nb, K, sel, sh);
         if (a.sel)
             for (int i = tid; i < K; i += kRowThreads) a.sel[rk + i] = sel[i];
     } else {
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
 // top-K of blocks [c * chunk_w, (c + 1) * chunk_w) of the row's valid blocks
 // and writes them as candidates (keys and block indices, ascending, padded).
 __global__ __launch_bounds__(kRowThreads) void row_chunk_select_kernel(ChunkArgs a) {
-    extern __shared__ int dyn[];
+    extern __shared__ __attribute__((aligned(16))) int dyn[];   // 16-byte vector reads
     __shared__ RowShared sh;
     constexpr int U = 8;
     const int tid = threadIdx.x;
@@ -86,7 +90,9 @@ __global__ __launch_bounds__(kRowThreads) void row_chunk_select_kernel(ChunkArgs
     const int nb = cb > a.width ? a.width : cb;
     const int len = nb - n0 < 0 ? 0 : (nb - n0 < span ? nb - n0 : span);
     // the chunk's keys: U loads per thread in flight, from indices clamped
-    // into the chunk
+    // into the chunk; the first round also stays in registers
+    static_assert(U == kKeyRegs, "the first round of keys is the register set");
+    uint32_t kr[kKeyRegs];
     for (int i0 = 0; i0 < len; i0 += U * kRowThreads) {
         float v[U];
 #pragma unroll
@@ -97,11 +103,16 @@ __global__ __launch_bounds__(kRowThreads) void row_chunk_select_kernel(ChunkArgs
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = i0 + u * kRowThreads + tid;
-            if (i < len) keys[i] = score_key(v[u]);
+            const uint32_t k = score_key(v[u]);
+            if (i0 == 0) kr[u] = k;
+            if (i < len) keys[i] = k;
         }
     }
     __syncthreads();
-    row_select(keys, len, K, sel, sh);
+    if (len <= kKeyRegs * kRowThreads)
+        row_select<true>(keys, len, K, sel, sh, kr);
+    else
+        row_select(keys, len, K, sel, sh);
     uint32_t *ck = a.cand_key + ((size_t)row * a.chunks + c) * K;
     int32_t *ci = a.cand_idx + ((size_t)row * a.chunks + c) * K;
     for (int i = tid; i < K; i += kRowThreads) {
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(kRowThreads) void row_chunk_select_kernel(ChunkArgs
 template <int MODE>
 __global__ __launch_bounds__(kRowThreads) void row_merge_select_plan_kernel(
         SelectPlanArgs a, const uint32_t *cand_key, const int32_t *cand_idx, int ncand) {
-    extern __shared__ int dyn[];
+    extern __shared__ __attribute__((aligned(16))) int dyn[];   // 16-byte vector reads
     __shared__ RowShared sh;
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
