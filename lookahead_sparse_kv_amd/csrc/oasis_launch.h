@@ -193,7 +193,7 @@ constexpr int kMaxAttnRowsQ = 32; // query rows per KV head in attention (two MF
 constexpr int kMaxAttnBlocks = 65536;  // list entries per row in attention (keeps the split plan's int sums in range)
 constexpr int kMaxKBlocks = 1024; // K limit of select / plan
 constexpr int kRowSelectMaxWidth = 8192;  // widest table the row select keeps in LDS
-constexpr int kFusedMaxWidth = 8192;      // fused select + plan: table width limit (LDS: 61 KiB at K = 512)
+constexpr int kFusedMaxWidth = 8192;      // fused select + plan: table width limit (and the LDS bound of row_select_plan_fits)
 constexpr int kFusedMaxK = 512;           // fused select + plan: K limit
 constexpr int kMaxSelectWidth = 15360;   // keys of a row staged in LDS (60 KiB)
 constexpr int kMaxCandidates = 8192;     // candidates of a row in the two-pass selection (LDS)

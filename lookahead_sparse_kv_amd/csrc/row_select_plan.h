@@ -320,8 +320,15 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
     int c_gt = 0, c_eq = 0;
     uint32_t ck[kKeyRegs];                        // this thread's chunk, when it fits
     if (E <= kKeyRegs) {
+        if (E == kKeyRegs && lo + kKeyRegs <= nb) {       // 32-byte aligned: two 16-byte reads
+            const uint4 a = *reinterpret_cast<const uint4 *>(keys + lo);
+            const uint4 b = *reinterpret_cast<const uint4 *>(keys + lo + 4);
+            ck[0] = a.x; ck[1] = a.y; ck[2] = a.z; ck[3] = a.w;
+            ck[4] = b.x; ck[5] = b.y; ck[6] = b.z; ck[7] = b.w;
+        } else {                                          // read together, indices clamped (nb > K >= 1)
 #pragma unroll
-        for (int i = 0; i < kKeyRegs; ++i) ck[i] = lo + i < hi ? keys[lo + i] : 0u;
+            for (int i = 0; i < kKeyRegs; ++i) ck[i] = keys[lo + i < nb ? lo + i : nb - 1];
+        }
 #pragma unroll
         for (int i = 0; i < kKeyRegs; ++i) {
             const bool in = lo + i < hi;
@@ -425,7 +432,7 @@ __device__ __forceinline__ void plan_prefetch(const int32_t *slot_block, const i
 // The plan of one row.  sel[0..K) (LDS) holds the selection; sel_score_of(s)
 // gives the fp32 score of block s; pf holds this thread's part of the slot
 // table (plan_prefetch); slot_block / last_use / fetch_* point at this row's
-// part of the global arrays.  `pl` is 9 * Kp ints of LDS.
+// part of the global arrays.  `pl` is 11 * Kp ints of LDS.
 //
 // Each thread owns a contiguous chunk of selection entries and of slots, so
 // every position (the p-th miss or fetched block in ascending order, the p-th
@@ -441,7 +448,9 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
                                          const PlanPrefetch &pf,
                                          int32_t *slot_block, int32_t *last_use,
                                          int32_t *fetch_block, int32_t *fetch_slot,
-                                         int32_t *fetch_count, int *pl, RowShared &sh) {
+                                         int32_t *fetch_count, int *pl, RowShared &sh,
+                                         bool ascending = false, int *map = nullptr,
+                                         int map_len = 0) {
     const int tid = threadIdx.x;
     const int Kp = plan_pad(K);
     const int E = (K + kRowThreads - 1) / kRowThreads;
@@ -456,13 +465,16 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
     int *m_block = pl + 7 * Kp;
     int *c_lu = pl + 8 * Kp;       // eviction candidates, compacted: last use
     int *c_block = hit_sel;        //   ... and block (hit_sel is dead by then)
-    int *m_rank = reinterpret_cast<int *>(sel_score);   // per miss: rank (sel_score dead by then)
+    int *m_rank = pl + 9 * Kp;     // per compacted miss: its rank (a tally)
+    int *c_rank = pl + 10 * Kp;    // per compacted eviction candidate: its rank (a tally)
 
     for (int i = tid; i < Kp; i += kRowThreads) {
         if (i >= K) sel[i] = -1;
         hit_sel[i] = 0;
         fill[i] = -1;
         dest[i] = -1;
+        m_rank[i] = 0;
+        c_rank[i] = 0;
     }
     bool unsorted = false;
 #pragma unroll
@@ -471,13 +483,14 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
         if (u < E && j < K) {
             sb[j] = pf.sb[u] < 0 ? -1 : pf.sb[u];
             lu[j] = pf.lu[u];
-            if (j + 1 < K) {
+            if (!ascending && j + 1 < K) {
                 const int x = sel[j], y = sel[j + 1];
                 unsorted |= (x < 0 && y >= 0) || (x >= 0 && y >= 0 && x >= y);
             }
         }
     }
-    if (__syncthreads_or(unsorted)) {
+    // a selection from the row select is ascending by construction
+    if (!ascending && __syncthreads_or(unsorted)) {
         // not ascending: order by (valid first, block, entry) into fill / dest, then back
         int key_s[kPlanMaxPer];
 #pragma unroll
@@ -509,6 +522,10 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
     for (int i = tid; i < Kp; i += kRowThreads) {
         const int x = sel[i];
         sel_score[i] = (i < K && x >= 0) ? sel_score_of(x) : 0.f;
+        // map (where given): block -> selection entry, over the row's keys,
+        // which are dead once read here (a block's key is read and its map
+        // entry written by the thread of the one entry selecting it)
+        if (map && i < K && x >= 0 && x < map_len) map[x] = i;
     }
     // one scan: valid selection entries (an ascending prefix) | empty slots
     bool empty[kPlanMaxPer];
@@ -535,10 +552,19 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
         if (u < E && j < K) {
             const int blk = sb[j];
             if (blk >= 0) {
-                int l = 0, h = m_valid;                    // first entry >= blk
-                while (l < h) {
-                    const int mid = (l + h) >> 1;
-                    if (sel[mid] < blk) l = mid + 1; else h = mid;
+                int l;
+                if (map) {
+                    // the map entry of an unselected block holds anything:
+                    // it is a hit only if the entry it names selects blk
+                    l = blk < map_len ? map[blk] : -1;
+                    if ((unsigned)l >= (unsigned)m_valid) l = m_valid;
+                } else {
+                    int h = m_valid;                       // first entry >= blk
+                    l = 0;
+                    while (l < h) {
+                        const int mid = (l + h) >> 1;
+                        if (sel[mid] < blk) l = mid + 1; else h = mid;
+                    }
                 }
                 if (l < m_valid && sel[l] == blk) { hit[u] = true; hit_sel[l] = 1; }
                 cand[u] = !hit[u];
@@ -563,10 +589,10 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
     const int nF = M < cap ? M : cap;                      // the first min(M, cap) misses are fetched
     const int n_victims = nF > nfree ? nF - nfree : 0;     // (C >= n_victims always)
     int mpos = pos_b & 0xffff, cpos = pos_b >> 16;
-    int mp[kPlanMaxPer];
+    int mp[kPlanMaxPer], cp[kPlanMaxPer];
 #pragma unroll
     for (int u = 0; u < kPlanMaxPer; ++u) {
-        mp[u] = -1;
+        mp[u] = cp[u] = -1;
         if (miss[u]) {
             mp[u] = mpos;
             m_score[mpos] = sel_score[lo + u];
@@ -574,6 +600,7 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
             ++mpos;
         }
         if (cand[u] && n_victims > 0) {
+            cp[u] = cpos;
             c_lu[cpos] = lu[lo + u];
             c_block[cpos] = sb[lo + u];
             ++cpos;
@@ -582,49 +609,59 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
     __syncthreads();
     // ranks: misses by (score desc, block asc); candidates by (last use asc,
     // block asc), the first n_victims of them evicted in that order, after the
-    // free slots (ascending)
-    bool fetched[kPlanMaxPer];
+    // free slots (ascending).  Each rank is a tally of the entries ahead of
+    // it, the comparisons spread over the workgroup: wave w compares entry i
+    // (lane i, i + 64, ...) with a slice of the others, four per 16-byte LDS
+    // read, and adds its count to i's tally.
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    if (M > cap) {
+        const int S = ((M + kRowWaves - 1) / kRowWaves + 3) & ~3;
+        const int q_lo = wave * S, q_hi = q_lo + S < M ? q_lo + S : M;
+        for (int i = lane; i < M && q_lo < q_hi; i += kWave) {
+            const float sc = m_score[i];
+            const int blk = m_block[i];
+            int r = 0;
+            for (int q0 = q_lo; q0 < q_hi; q0 += 4) {
+                const float4 s4 = ld_f4(m_score + q0);
+                const int4 b4 = ld_i4(m_block + q0);
+                const float ss[4] = {s4.x, s4.y, s4.z, s4.w};
+                const int bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-    for (int u = 0; u < kPlanMaxPer; ++u) {
-        fetched[u] = false;
-        if (miss[u]) {
-            if (M <= cap) {
-                fetched[u] = true;
-            } else {
-                const float sc = m_score[mp[u]];
-                const int blk = m_block[mp[u]];
-                int rank = 0;
-#pragma unroll 2
-                for (int q0 = 0; q0 < M; q0 += 4) {      // four misses per 16-byte read
-                    const float4 s4 = ld_f4(m_score + q0);
-                    const int4 b4 = ld_i4(m_block + q0);
-                    const float ss[4] = {s4.x, s4.y, s4.z, s4.w};
-                    const int bb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        rank += (q0 + c < M) & ((ss[c] > sc) | ((ss[c] == sc) & (bb[c] < blk)));
-                }
-                fetched[u] = rank < cap;
-                m_rank[mp[u]] = rank;
+                for (int c = 0; c < 4; ++c)
+                    r += (q0 + c < q_hi) & ((ss[c] > sc) | ((ss[c] == sc) & (bb[c] < blk)));
             }
+            if (r) atomicAdd(&m_rank[i], r);
         }
-        if (empty[u]) {
-            if (epos < nF) dest[epos] = lo + u;
-            ++epos;
-        }
-        if (cand[u] && n_victims > 0) {
-            const int l0 = lu[lo + u], b0 = sb[lo + u];
-            int rank = 0;
-#pragma unroll 2
-            for (int q0 = 0; q0 < C; q0 += 4) {          // four candidates per 16-byte read
+    }
+    if (n_victims > 0) {
+        const int S = ((C + kRowWaves - 1) / kRowWaves + 3) & ~3;
+        const int q_lo = wave * S, q_hi = q_lo + S < C ? q_lo + S : C;
+        for (int i = lane; i < C && q_lo < q_hi; i += kWave) {
+            const int l0 = c_lu[i], b0 = c_block[i];
+            int r = 0;
+            for (int q0 = q_lo; q0 < q_hi; q0 += 4) {
                 const int4 l4 = ld_i4(c_lu + q0);
                 const int4 b4 = ld_i4(c_block + q0);
                 const int ll[4] = {l4.x, l4.y, l4.z, l4.w};
                 const int bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    rank += (q0 + c < C) & ((ll[c] < l0) | ((ll[c] == l0) & (bb[c] < b0)));
+                    r += (q0 + c < q_hi) & ((ll[c] < l0) | ((ll[c] == l0) & (bb[c] < b0)));
             }
+            if (r) atomicAdd(&c_rank[i], r);
+        }
+    }
+    __syncthreads();
+    bool fetched[kPlanMaxPer];
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        fetched[u] = miss[u] && (M <= cap || m_rank[mp[u]] < cap);
+        if (empty[u]) {
+            if (epos < nF) dest[epos] = lo + u;
+            ++epos;
+        }
+        if (cp[u] >= 0) {
+            const int rank = c_rank[cp[u]];
             if (rank < n_victims) dest[nfree + rank] = lo + u;
         }
     }

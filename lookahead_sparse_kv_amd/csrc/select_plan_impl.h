@@ -31,8 +31,8 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
     const int K = a.k;
     const int Kp = plan_pad(K);
     int *sel = dyn;                                               // Kp
-    int *pl = sel + Kp;                                           // 9 Kp (plan)
-    uint32_t *keys = reinterpret_cast<uint32_t *>(MODE & 2 ? pl + 9 * Kp : pl);   // width
+    int *pl = sel + Kp;                                           // 11 Kp (plan)
+    uint32_t *keys = reinterpret_cast<uint32_t *>(MODE & 2 ? pl + 11 * Kp : pl);   // width
     const float *srow = a.scores + (size_t)row * a.width;
     const size_t rk = (size_t)row * K;
 
@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
         int32_t *fs = a.fetch_slot + (size_t)row * a.cap;
         if (MODE & 1)
             row_plan(sel, [&](int s) { return key_to_score(keys[s]); }, K, a.cap, step, pf,
-                     a.slot_block + rk, a.last_use + rk, fb, fs, a.fetch_count + row, pl, sh);
+                     a.slot_block + rk, a.last_use + rk, fb, fs, a.fetch_count + row, pl, sh,
+                     true, reinterpret_cast<int *>(keys), a.width);
         else
             row_plan(sel, [&](int s) { return srow[s]; }, K, a.cap, step, pf, a.slot_block + rk,
                      a.last_use + rk, fb, fs, a.fetch_count + row, pl, sh);
@@ -137,8 +138,8 @@ __global__ __launch_bounds__(kRowThreads) void row_merge_select_plan_kernel(
     const int K = a.k;
     const int Kp = plan_pad(K);
     int *sel = dyn;                                               // Kp
-    int *pl = sel + Kp;                                           // 9 Kp (plan)
-    uint32_t *keys = reinterpret_cast<uint32_t *>(MODE & 2 ? pl + 9 * Kp : pl);   // ncand
+    int *pl = sel + Kp;                                           // 11 Kp (plan)
+    uint32_t *keys = reinterpret_cast<uint32_t *>(MODE & 2 ? pl + 11 * Kp : pl);   // ncand
     const size_t rk = (size_t)row * K;
     PlanPrefetch pf;
     if (MODE & 2) plan_prefetch(a.slot_block_in + rk, a.last_use_in + rk, K, pf);
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kRowThreads) void row_merge_select_plan_kernel(
         const float *srow = a.scores + (size_t)row * a.width;
         row_plan(sel, [&](int s) { return srow[s]; }, K, a.cap, step, pf, a.slot_block + rk,
                  a.last_use + rk, a.fetch_block + (size_t)row * a.cap,
-                 a.fetch_slot + (size_t)row * a.cap, a.fetch_count + row, pl, sh);
+                 a.fetch_slot + (size_t)row * a.cap, a.fetch_count + row, pl, sh, true);
     }
 }
 
@@ -187,7 +188,7 @@ hipError_t launch_merge_select_plan(const SelectPlanArgs &a, int mode, const uin
     const int Kp = plan_pad(a.k);
     if (mode == 3)
         launch_k(row_merge_select_plan_kernel<3>, dim3(a.rows), dim3(kRowThreads),
-                 (size_t)(10 * Kp + ncand) * 4, stream, stop, a, cand_key, cand_idx, ncand);
+                 (size_t)(12 * Kp + ncand) * 4, stream, stop, a, cand_key, cand_idx, ncand);
     else
         launch_k(row_merge_select_plan_kernel<1>, dim3(a.rows), dim3(kRowThreads),
                  (size_t)(Kp + ncand) * 4, stream, stop, a, cand_key, cand_idx, ncand);
@@ -198,7 +199,10 @@ bool row_select_plan_fits(int width, int k, int mode) {
     if (k > kMaxKBlocks) return false;
     if (mode == 1) return width <= kRowSelectMaxWidth;
     if (mode == 2) return true;
-    return width <= kFusedMaxWidth && k <= kFusedMaxK;
+    // the fused launch's LDS: the selection, the plan's arrays and the keys,
+    // beside the static row state, within 64 KiB
+    return width <= kFusedMaxWidth && k <= kFusedMaxK &&
+           (size_t)(12 * plan_pad(k) + width) * 4 + sizeof(RowShared) <= 65536;
 }
 
 #ifndef OASIS_ROW_WIDE
@@ -225,7 +229,7 @@ hipError_t launch_two_pass_select_plan(const SelectPlanArgs &a, int mode, uint32
                                          : launch_chunk_select(ca, stream);
     if (e != hipSuccess) return e;
     const int ncand = chunks * a.k;
-    const bool fused = mode == 3 && (size_t)(10 * plan_pad(a.k) + ncand) * 4 <= 65536;
+    const bool fused = mode == 3 && (size_t)(12 * plan_pad(a.k) + ncand) * 4 + sizeof(RowShared) <= 65536;
     const int m = fused ? 3 : 1;
     // the stop event goes with the last launch: the merge, or the plan after it
     LaunchStop *merge_stop = (mode == 1 || fused) ? stop : nullptr;
@@ -250,9 +254,9 @@ hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t
     if (mode == 1) {
         launch_k(row_select_plan_kernel<1>, grid, block, (Kp + w) * 4, stream, stop, a);
     } else if (mode == 2) {
-        launch_k(row_select_plan_kernel<2>, grid, block, (size_t)10 * Kp * 4, stream, stop, a);
+        launch_k(row_select_plan_kernel<2>, grid, block, (size_t)12 * Kp * 4, stream, stop, a);
     } else {
-        launch_k(row_select_plan_kernel<3>, grid, block, (10 * Kp + w) * 4, stream, stop, a);
+        launch_k(row_select_plan_kernel<3>, grid, block, (12 * Kp + w) * 4, stream, stop, a);
     }
     return hipGetLastError();
 }
