@@ -93,8 +93,10 @@ __device__ __forceinline__ int load_row_keys(const float *srow, int width, const
     return nb;
 }
 
-// Inclusive scan of one int per thread over the workgroup (two barriers).
-__device__ __forceinline__ int row_inclusive_scan(int v, int *wave_sums) {
+// Inclusive scan of one int per thread over the workgroup.  trailing: end
+// with a barrier, so that wave_sums may be written again at once; a caller
+// that reaches another barrier before the next scan passes false.
+__device__ __forceinline__ int row_inclusive_scan(int v, int *wave_sums, bool trailing = true) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     v = wave_inclusive_scan(v);
@@ -103,7 +105,7 @@ __device__ __forceinline__ int row_inclusive_scan(int v, int *wave_sums) {
     int off = 0;
 #pragma unroll
     for (int w = 0; w < kRowWaves; ++w) off += (w < wave) ? wave_sums[w] : 0;
-    __syncthreads();
+    if (trailing) __syncthreads();
     return v + off;
 }
 
@@ -207,7 +209,7 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
             h[j] = j < per ? sh.hist[hi - j >= 0 ? hi - j : 0] : 0;
             local += h[j];
         }
-        const int incl = row_inclusive_scan(local, sh.wave_sums);
+        const int incl = row_inclusive_scan(local, sh.wave_sums, false);   // a barrier follows
         int acc = incl - local;                   // keys in bins above hi
         if (acc < krem && krem <= incl) {
             bool found = false;
@@ -345,7 +347,7 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
     // one scan of both counts (each < 2^16): the keys taken before this
     // thread's chunk are all the larger ones and the first krem copies of tau
     const int packed = (c_eq << 16) | c_gt;
-    const int before = row_inclusive_scan(packed, sh.wave_sums) - packed;
+    const int before = row_inclusive_scan(packed, sh.wave_sums, false) - packed;   // (barrier at the end)
     const int gt_before = before & 0xffff;
     const int eq_before = before >> 16;
     int pos = gt_before + (eq_before < krem ? eq_before : krem);
@@ -386,7 +388,9 @@ __host__ __device__ __forceinline__ int plan_pad(int K) {
 }
 
 // Exclusive scan of one int per thread; `total` gets the workgroup sum.
-__device__ __forceinline__ int row_exclusive_scan(int v, int *wave_sums, int &total) {
+// trailing as in row_inclusive_scan.
+__device__ __forceinline__ int row_exclusive_scan(int v, int *wave_sums, int &total,
+                                                  bool trailing = true) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int x = wave_inclusive_scan(v);
@@ -399,7 +403,7 @@ __device__ __forceinline__ int row_exclusive_scan(int v, int *wave_sums, int &to
         off += (w < wave) ? ws : 0;
         tot += ws;
     }
-    __syncthreads();
+    if (trailing) __syncthreads();
     total = tot;
     return x - v + off;
 }
@@ -583,7 +587,8 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
         my_cand += cand[u];
     }
     int tot_b;
-    const int pos_b = row_exclusive_scan(my_miss | (my_cand << 16), sh.wave_sums, tot_b);
+    const int pos_b = row_exclusive_scan(my_miss | (my_cand << 16), sh.wave_sums, tot_b,
+                                         false);                 // a barrier follows the compaction
     const int M = tot_b & 0xffff;
     const int C = tot_b >> 16;
     const int nF = M < cap ? M : cap;                      // the first min(M, cap) misses are fetched
