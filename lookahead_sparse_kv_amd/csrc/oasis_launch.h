@@ -204,7 +204,7 @@ __host__ __device__ constexpr long long two_pass_max_width(int k) {
     return (long long)kRowSelectMaxWidth * (kMaxCandidates / (k > 0 ? k : 1));
 }
 #ifndef OASIS_TWO_PASS_MIN_WIDTH
-#define OASIS_TWO_PASS_MIN_WIDTH 8192    // up to here one fused launch is faster (16.1 against 22 us at 8,192)
+#define OASIS_TWO_PASS_MIN_WIDTH 8192    // up to here one fused launch is faster (13.1 against 17.8 us at 8,192)
 #endif
 constexpr int kTwoPassMinWidth = OASIS_TWO_PASS_MIN_WIDTH;   // rows wider than this: two passes
 

@@ -53,7 +53,10 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // bounds of the [B][Hkv][W] scores, with no branch around the loads), so the
 // first round does not wait for the context length, which is loaded beside it
 // and applied when the keys are written.
-constexpr int kKeyRegs = 8;              // keys a thread holds in registers: n = u * kRowThreads + tid
+// keys a thread holds in registers, n = u * kRowThreads + tid: rows of up to
+// 2,048 blocks at 256 threads, 8,192 at 512 or 1,024
+constexpr int kKeyRegs = kRowThreads == 512 ? 16 : 8;
+static_assert(kKeyRegs % 4 == 0, "a thread's chunk is read 16 bytes at a time");
 
 
 __device__ __forceinline__ int load_row_keys(const float *srow, int width, const int32_t *ctx_p,
@@ -322,11 +325,12 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
     int c_gt = 0, c_eq = 0;
     uint32_t ck[kKeyRegs];                        // this thread's chunk, when it fits
     if (E <= kKeyRegs) {
-        if (E == kKeyRegs && lo + kKeyRegs <= nb) {       // 32-byte aligned: two 16-byte reads
-            const uint4 a = *reinterpret_cast<const uint4 *>(keys + lo);
-            const uint4 b = *reinterpret_cast<const uint4 *>(keys + lo + 4);
-            ck[0] = a.x; ck[1] = a.y; ck[2] = a.z; ck[3] = a.w;
-            ck[4] = b.x; ck[5] = b.y; ck[6] = b.z; ck[7] = b.w;
+        if (E == kKeyRegs && lo + kKeyRegs <= nb) {       // 16-byte aligned chunk: 16-byte reads
+#pragma unroll
+            for (int i = 0; i < kKeyRegs; i += 4) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(keys + lo + i);
+                ck[i] = a.x; ck[i + 1] = a.y; ck[i + 2] = a.z; ck[i + 3] = a.w;
+            }
         } else {                                          // read together, indices clamped (nb > K >= 1)
 #pragma unroll
             for (int i = 0; i < kKeyRegs; ++i) ck[i] = keys[lo + i < nb ? lo + i : nb - 1];

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
 __global__ __launch_bounds__(kRowThreads) void row_chunk_select_kernel(ChunkArgs a) {
     extern __shared__ __attribute__((aligned(16))) int dyn[];   // 16-byte vector reads
     __shared__ RowShared sh;
-    constexpr int U = 8;
+    constexpr int U = kKeyRegs;
     const int tid = threadIdx.x;
     const int row = blockIdx.x / a.chunks;
     const int c = blockIdx.x - row * a.chunks;
