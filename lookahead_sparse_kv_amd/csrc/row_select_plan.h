@@ -13,8 +13,9 @@
 // range): an LDS histogram of the keys that still match the prefix, a
 // workgroup scan over the bins from the top, and the bin where the count
 // crosses the remaining K.  Keys above tau are taken, and copies of tau fill
-// the rest in ascending block order (ordered scans over index-contiguous
-// chunks), so ties go to the lower index and the set comes out ascending.
+// the rest in ascending block order (ordered scans: over the ballots of the
+// keys a thread holds in registers, or over index-contiguous chunks), so ties
+// go to the lower index and the set comes out ascending.
 //
 // Plan: each thread owns contiguous chunks of the selection and of the slot
 // table, so positions are exclusive scans; hits are binary searches in the
@@ -123,13 +124,19 @@ struct RowShared {
     int rank_acc[kRankMax];                 // per gathered key: (keys above) | (keys at or above) << 16
     int ngather, gt_in_bin;
     uint32_t tau;
+    int reg_cnt[kKeyRegs * kRowWaves];      // per (register, wave): taken keys | copies of tau << 16
 };
+
+// Lanes below this one whose bit is set in a wave-wide mask.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 // Top-K of `nb` keys (keys[0..nb), already in LDS) into sel[0..K): ascending,
 // -1 padded.  Ends with a barrier; sel may then be read by every thread.
-// REGS: every key of the row is also in the calling thread's registers, kr[u]
-// = keys[u * kRowThreads + tid] (nb <= kKeyRegs * kRowThreads), so the passes
-// over all keys read registers instead of LDS.
+// REGS: every key of the row is in the calling thread's registers instead,
+// kr[u] = key u * kRowThreads + tid (nb <= kKeyRegs * kRowThreads); the
+// passes over all keys read those registers, and `keys` is not read.
 //
 // The radix digits are taken from u - kmin over the row's own key range
 // [kmin, kmax], the first one being the top 11 bits of that span: block scores
@@ -239,10 +246,6 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
             // the cnt keys left in the threshold bin, gathered: a ballot of
             // the matching lanes per round, one slot reservation per wave
             if (tid < kRankMax) sh.rank_acc[tid] = 0;
-            const auto below = [](uint64_t bal) {
-                return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            };
             if constexpr (REGS) {
                 uint64_t bal[kKeyRegs];
                 int total = 0;
@@ -258,7 +261,7 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
                     base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
                     for (int u = 0; u < kKeyRegs; ++u) {
-                        if ((bal[u] >> lane) & 1) sh.gkey[base + below(bal[u])] = kr[u];
+                        if ((bal[u] >> lane) & 1) sh.gkey[base + lanes_below(bal[u])] = kr[u];
                         base += __popcll(bal[u]);
                     }
                 }
@@ -272,7 +275,7 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
                         int base = 0;
                         if (lane == 0) base = atomicAdd(&sh.ngather, __popcll(bal));
                         base = __builtin_amdgcn_readfirstlane(base);
-                        if (m) sh.gkey[base + below(bal)] = u;
+                        if (m) sh.gkey[base + lanes_below(bal)] = u;
                     }
                 }
             }
@@ -319,6 +322,47 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
     // largest key, and keys above it plus its first krem copies are taken.
     const uint32_t tau = kmin + prefix;
 
+    if constexpr (REGS) {
+        // Ordered compaction from the registers: key n = u * kRowThreads + tid,
+        // so index order is (u, wave, lane).  Per register, a ballot of the
+        // keys taken outright (above tau; at or above it when whole) and one
+        // of the copies of tau; their counts per (u, wave) slot, scanned in
+        // slot order, give each taken key its position: the taken keys before
+        // it plus the copies of tau before it, at most krem.
+        constexpr int NS = kKeyRegs * kRowWaves;
+        static_assert(NS <= 2 * kWave && kRowWaves % 2 == 0, "two (register, wave) slots per lane");
+        uint64_t bg[kKeyRegs], be[kKeyRegs];
+        int mine = 0;
+#pragma unroll
+        for (int u = 0; u < kKeyRegs; ++u) {
+            // bitwise, not short-circuit, so that no compare is branched around
+            const bool in = u * kRowThreads + tid < nb;
+            const bool eq = kr[u] == tau;
+            bg[u] = __ballot(in & ((kr[u] > tau) | (whole & eq)));
+            be[u] = __ballot(in & !whole & eq);
+            const int packed = __popcll(bg[u]) | (__popcll(be[u]) << 16);
+            mine = lane == u ? packed : mine;
+        }
+        if (lane < kKeyRegs) sh.reg_cnt[lane * kRowWaves + wave] = mine;
+        __syncthreads();
+        // every wave scans the slots itself, lane l holding slots 2l and 2l + 1;
+        // slot u * kRowWaves + wave has this wave's parity (kRowWaves is even)
+        const int c0 = 2 * lane < NS ? sh.reg_cnt[2 * lane] : 0;
+        const int c1 = 2 * lane + 1 < NS ? sh.reg_cnt[2 * lane + 1] : 0;
+        const int ex0 = wave_inclusive_scan(c0 + c1) - c0 - c1;
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const int ex = (wv & 1) ? ex0 + c0 : ex0;
+#pragma unroll
+        for (int u = 0; u < kKeyRegs; ++u) {
+            const int before = __builtin_amdgcn_readlane(ex, (u * kRowWaves + wv) >> 1);
+            const int gt_b = (before & 0xffff) + lanes_below(bg[u]);
+            const int eq_b = (before >> 16) + lanes_below(be[u]);
+            const bool take = (bool)((bg[u] >> lane) & 1) | ((bool)((be[u] >> lane) & 1) & (eq_b < krem));
+            if (take) sel[gt_b + (eq_b < krem ? eq_b : krem)] = u * kRowThreads + tid;
+        }
+        __syncthreads();
+        return;
+    }
     const int E = (nb + kRowThreads - 1) / kRowThreads;
     const int lo = tid * E;
     const int hi = lo + E < nb ? lo + E : nb;

@@ -153,9 +153,21 @@ __global__ __launch_bounds__(kRowThreads) void row_merge_select_plan_kernel(
         for (int i = tid; i < K; i += kRowThreads) sel[i] = i < nb ? i : -1;
         __syncthreads();
     } else {
-        for (int i = tid; i < ncand; i += kRowThreads) keys[i] = rk_key[i];
-        __syncthreads();
-        row_select(keys, ncand, K, sel, sh);
+        if (ncand <= kKeyRegs * kRowThreads) {
+            // the candidates in registers only, key n = u * kRowThreads + tid
+            // (the register select reads no key from LDS)
+            uint32_t kr[kKeyRegs];
+#pragma unroll
+            for (int u = 0; u < kKeyRegs; ++u) {
+                const int n = u * kRowThreads + tid;
+                kr[u] = rk_key[n < ncand ? n : ncand - 1];
+            }
+            row_select<true>(keys, ncand, K, sel, sh, kr);
+        } else {
+            for (int i = tid; i < ncand; i += kRowThreads) keys[i] = rk_key[i];
+            __syncthreads();
+            row_select(keys, ncand, K, sel, sh);
+        }
         // positions -> blocks (positions ascend with block index; a position
         // padded with key 0 is never taken: there are at least K valid ones)
         for (int i = tid; i < K; i += kRowThreads) {
