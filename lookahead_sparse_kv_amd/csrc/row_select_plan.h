@@ -48,6 +48,10 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
 // Scores of one row into LDS as keys, for the row's valid blocks n < nb;
 // returns nb.  A thread's loads (8 per round of 8 * kRowThreads blocks) are all issued
 // before the first is used, from indices clamped into the row (always in
@@ -122,7 +126,7 @@ struct RowShared {
     int digit, above, count;
     alignas(16) uint32_t gkey[kRankMax];    // keys of a small threshold bin
     int rank_acc[kRankMax];                 // per gathered key: (keys above) | (keys at or above) << 16
-    int ngather, gt_in_bin;
+    int ngather, gt_in_bin, ge_in_bin;
     uint32_t tau;
     int reg_cnt[kKeyRegs * kRowWaves];      // per (register, wave): taken keys | copies of tau << 16
 };
@@ -132,11 +136,26 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Top-K of `nb` keys (keys[0..nb), already in LDS) into sel[0..K): ascending,
-// -1 padded.  Ends with a barrier; sel may then be read by every thread.
-// REGS: every key of the row is in the calling thread's registers instead,
-// kr[u] = key u * kRowThreads + tid (nb <= kKeyRegs * kRowThreads); the
-// passes over all keys read those registers, and `keys` is not read.
+// Where the K-th largest key lies: the keys taken are those above tau and,
+// unless whole, the first krem copies of tau in index order (whole: every key
+// >= tau, exactly K of them).  all_ties: every copy of tau is taken as well,
+// so the keys taken are exactly the keys >= tau.
+struct RowCut {
+    uint32_t tau;
+    int krem;
+    bool whole;
+    bool all_ties;
+};
+
+// Hooks of row_find_cut for work that needs the same two barriers:
+// clear() runs before the first, mark() before the second.
+struct NoMarks {
+    __device__ void clear() const {}
+    __device__ void mark() const {}
+};
+
+// The cut of `nb` > K keys (keys[0..nb) in LDS; REGS: in registers instead,
+// as row_select takes them).
 //
 // The radix digits are taken from u - kmin over the row's own key range
 // [kmin, kmax], the first one being the top 11 bits of that span: block scores
@@ -148,17 +167,13 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // gathered and counted against each other, which gives the K-th largest key
 // exactly (the key tau with fewer than krem keys above it in the bin and at
 // least krem at or above it).
-template <bool REGS>
-__device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, int *sel,
-                                           RowShared &sh, const uint32_t (&kr)[kKeyRegs]) {
+template <bool REGS, class Marks = NoMarks>
+__device__ __forceinline__ RowCut row_find_cut(const uint32_t *keys, int nb, int K, RowShared &sh,
+                                               const uint32_t (&kr)[kKeyRegs],
+                                               const Marks &marks = Marks()) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    if (nb <= K) {
-        for (int i = tid; i < K; i += kRowThreads) sel[i] = i < nb ? i : -1;
-        __syncthreads();
-        return;
-    }
     // f(u, n) over every key u = keys[n], n < nb, of this thread
     const auto each_key = [&](auto &&f) {
         if constexpr (REGS) {
@@ -181,6 +196,7 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
     kmx = wave_max_u32(kmx);
     if (lane == 0) { sh.wave_min[wave] = kmn; sh.wave_max[wave] = kmx; }
     for (int i = tid; i < kHistBins; i += kRowThreads) sh.hist[i] = 0;
+    marks.clear();
     __syncthreads();
     uint32_t kmin = sh.wave_min[0], kmax = sh.wave_max[0];
 #pragma unroll
@@ -207,6 +223,7 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
             const uint32_t d = u - kmin;
             if ((d & pmask) == prefix) atomicAdd(&sh.hist[(d >> shift) & (uint32_t)(nbins - 1)], 1);
         });
+        if (pass == 0) marks.mark();
         __syncthreads();
         // thread t owns `per` bins counted from the top: bins hi, hi-1, .., lo
         // (its counts held in registers for the search below)
@@ -308,20 +325,34 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
             if (tid < cnt) {
                 const int t = sh.rank_acc[tid];
                 const int gt = t & 0xffff, ge = t >> 16;
-                if (gt < krem && krem <= ge) { sh.tau = sh.gkey[tid]; sh.gt_in_bin = gt; }
+                if (gt < krem && krem <= ge) {
+                    sh.tau = sh.gkey[tid]; sh.gt_in_bin = gt; sh.ge_in_bin = ge;
+                }
             }
             __syncthreads();
             prefix = sh.tau - kmin;                // tau = kmin + prefix, exactly
             krem -= sh.gt_in_bin;                  // copies of tau still to take
-            break;
+            return RowCut{sh.tau, krem, false, sh.ge_in_bin - sh.gt_in_bin == krem};
         }
         width = shift < 11 ? shift : 11;
         shift -= width;
     }
-    // whole: every key >= tau is taken (exactly K); otherwise tau is the K-th
-    // largest key, and keys above it plus its first krem copies are taken.
-    const uint32_t tau = kmin + prefix;
+    // whole: every key >= tau is taken (exactly K); otherwise the last digit
+    // was resolved (the bin holds the copies of tau alone) and its first krem
+    // copies are taken.
+    return RowCut{kmin + prefix, krem, whole, whole};
+}
 
+// The K keys of a cut into sel[0..K), ascending.  Ends with a barrier.
+template <bool REGS>
+__device__ __forceinline__ void row_compact(const uint32_t *keys, int nb, int *sel, RowShared &sh,
+                                            const uint32_t (&kr)[kKeyRegs], const RowCut &cut) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const uint32_t tau = cut.tau;
+    const int krem = cut.krem;
+    const bool whole = cut.whole;
     if constexpr (REGS) {
         // Ordered compaction from the registers: key n = u * kRowThreads + tid,
         // so index order is (u, wave, lane).  Per register, a ballot of the
@@ -420,6 +451,22 @@ __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, 
     __syncthreads();
 }
 
+// Top-K of `nb` keys (keys[0..nb), already in LDS) into sel[0..K): ascending,
+// -1 padded.  Ends with a barrier; sel may then be read by every thread.
+// REGS: every key of the row is in the calling thread's registers instead,
+// kr[u] = key u * kRowThreads + tid (nb <= kKeyRegs * kRowThreads); the
+// passes over all keys read those registers, and `keys` is not read.
+template <bool REGS>
+__device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, int *sel,
+                                           RowShared &sh, const uint32_t (&kr)[kKeyRegs]) {
+    if (nb <= K) {
+        for (int i = threadIdx.x; i < K; i += kRowThreads) sel[i] = i < nb ? i : -1;
+        __syncthreads();
+        return;
+    }
+    row_compact<REGS>(keys, nb, sel, sh, kr, row_find_cut<REGS>(keys, nb, K, sh, kr));
+}
+
 // Without the keys in registers.
 __device__ __forceinline__ void row_select(const uint32_t *keys, int nb, int K, int *sel,
                                            RowShared &sh) {
@@ -479,6 +526,70 @@ __device__ __forceinline__ void plan_prefetch(const int32_t *slot_block, const i
         pf.sb[u] = slot_block[jc];
         pf.lu[u] = last_use[jc];
     }
+}
+
+// Ranks of the compacted misses by (score desc, block asc) when more than
+// cap of them, and of the compacted eviction candidates by (last use asc,
+// block asc) when any is evicted, into m_rank / c_rank (zeroed by the
+// caller).  Each rank is a tally of the entries ahead of it, the comparisons
+// spread over the workgroup: wave w compares entry i (lane i, i + 64, ...)
+// with a slice of the others, four per 16-byte LDS read, and adds its count
+// to i's tally.  The caller's barrier follows.
+__device__ __forceinline__ void plan_ranks(const float *m_score, const int *m_block, int *m_rank,
+                                           int M, int cap, const int *c_lu, const int *c_block,
+                                           int *c_rank, int C, int n_victims) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    if (M > cap) {
+        const int S = ((M + kRowWaves - 1) / kRowWaves + 3) & ~3;
+        const int q_lo = wave * S, q_hi = q_lo + S < M ? q_lo + S : M;
+        for (int i = lane; i < M && q_lo < q_hi; i += kWave) {
+            const float sc = m_score[i];
+            const int blk = m_block[i];
+            int r = 0;
+            for (int q0 = q_lo; q0 < q_hi; q0 += 4) {
+                const float4 s4 = ld_f4(m_score + q0);
+                const int4 b4 = ld_i4(m_block + q0);
+                const float ss[4] = {s4.x, s4.y, s4.z, s4.w};
+                const int bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    r += (q0 + c < q_hi) & ((ss[c] > sc) | ((ss[c] == sc) & (bb[c] < blk)));
+            }
+            if (r) atomicAdd(&m_rank[i], r);
+        }
+    }
+    if (n_victims > 0) {
+        const int S = ((C + kRowWaves - 1) / kRowWaves + 3) & ~3;
+        const int q_lo = wave * S, q_hi = q_lo + S < C ? q_lo + S : C;
+        for (int i = lane; i < C && q_lo < q_hi; i += kWave) {
+            const int l0 = c_lu[i], b0 = c_block[i];
+            int r = 0;
+            for (int q0 = q_lo; q0 < q_hi; q0 += 4) {
+                const int4 l4 = ld_i4(c_lu + q0);
+                const int4 b4 = ld_i4(c_block + q0);
+                const int ll[4] = {l4.x, l4.y, l4.z, l4.w};
+                const int bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    r += (q0 + c < q_hi) & ((ll[c] < l0) | ((ll[c] == l0) & (bb[c] < b0)));
+            }
+            if (r) atomicAdd(&c_rank[i], r);
+        }
+    }
+}
+
+// Fetched misses before compacted miss i (those ranked below cap).
+__device__ __forceinline__ int fetched_before(const int *m_rank, int i, int cap) {
+    int f = 0;
+#pragma unroll 2
+    for (int q0 = 0; q0 < i; q0 += 4) {
+        const int4 r4 = ld_i4(m_rank + q0);
+        const int rr[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) f += (q0 + c < i) & (rr[c] < cap);
+    }
+    return f;
 }
 
 // The plan of one row.  sel[0..K) (LDS) holds the selection; sel_score_of(s)
@@ -660,50 +771,9 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
         }
     }
     __syncthreads();
-    // ranks: misses by (score desc, block asc); candidates by (last use asc,
-    // block asc), the first n_victims of them evicted in that order, after the
-    // free slots (ascending).  Each rank is a tally of the entries ahead of
-    // it, the comparisons spread over the workgroup: wave w compares entry i
-    // (lane i, i + 64, ...) with a slice of the others, four per 16-byte LDS
-    // read, and adds its count to i's tally.
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    if (M > cap) {
-        const int S = ((M + kRowWaves - 1) / kRowWaves + 3) & ~3;
-        const int q_lo = wave * S, q_hi = q_lo + S < M ? q_lo + S : M;
-        for (int i = lane; i < M && q_lo < q_hi; i += kWave) {
-            const float sc = m_score[i];
-            const int blk = m_block[i];
-            int r = 0;
-            for (int q0 = q_lo; q0 < q_hi; q0 += 4) {
-                const float4 s4 = ld_f4(m_score + q0);
-                const int4 b4 = ld_i4(m_block + q0);
-                const float ss[4] = {s4.x, s4.y, s4.z, s4.w};
-                const int bb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    r += (q0 + c < q_hi) & ((ss[c] > sc) | ((ss[c] == sc) & (bb[c] < blk)));
-            }
-            if (r) atomicAdd(&m_rank[i], r);
-        }
-    }
-    if (n_victims > 0) {
-        const int S = ((C + kRowWaves - 1) / kRowWaves + 3) & ~3;
-        const int q_lo = wave * S, q_hi = q_lo + S < C ? q_lo + S : C;
-        for (int i = lane; i < C && q_lo < q_hi; i += kWave) {
-            const int l0 = c_lu[i], b0 = c_block[i];
-            int r = 0;
-            for (int q0 = q_lo; q0 < q_hi; q0 += 4) {
-                const int4 l4 = ld_i4(c_lu + q0);
-                const int4 b4 = ld_i4(c_block + q0);
-                const int ll[4] = {l4.x, l4.y, l4.z, l4.w};
-                const int bb[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    r += (q0 + c < q_hi) & ((ll[c] < l0) | ((ll[c] == l0) & (bb[c] < b0)));
-            }
-            if (r) atomicAdd(&c_rank[i], r);
-        }
-    }
+    // ranks: the first cap misses are fetched; the first n_victims candidates
+    // are evicted in rank order, after the free slots (ascending)
+    plan_ranks(m_score, m_block, m_rank, M, cap, c_lu, c_block, c_rank, C, n_victims);
     __syncthreads();
     bool fetched[kPlanMaxPer];
 #pragma unroll
@@ -724,17 +794,7 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
 #pragma unroll
     for (int u = 0; u < kPlanMaxPer; ++u) {
         if (fetched[u]) {
-            int fpos = mp[u];
-            if (M > cap) {
-                fpos = 0;
-#pragma unroll 2
-                for (int q0 = 0; q0 < mp[u]; q0 += 4) {
-                    const int4 r4 = ld_i4(m_rank + q0);
-                    const int rr[4] = {r4.x, r4.y, r4.z, r4.w};
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) fpos += (q0 + c < mp[u]) & (rr[c] < cap);
-                }
-            }
+            const int fpos = M > cap ? fetched_before(m_rank, mp[u], cap) : mp[u];
             if (fpos >= nF) continue;   // only a selection with repeated blocks gets here
             const int blk = sel[lo + u];
             const int d = dest[fpos];
@@ -756,6 +816,200 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
             const int f = fill[j];
             slot_block[j] = f >= 0 ? f : sb[j];
             last_use[j] = (f >= 0 || hit[u]) ? step : lu[j];
+        }
+    }
+}
+
+
+// Resident marks of the threshold plan: one bit per block of the row, cleared
+// while the selection starts and set from this thread's prefetched slots in
+// its first histogram pass (row_find_cut's hooks), so the barriers the
+// selection takes anyway order both.
+struct ResidentMarks {
+    uint32_t *bits;          // (width + 31) / 32 words of LDS
+    int width;
+    int K;
+    const PlanPrefetch *pf;
+    __device__ void clear() const {
+        for (int i = threadIdx.x; i < (width + 31) / 32; i += kRowThreads) bits[i] = 0u;
+    }
+    __device__ void mark() const {
+        const int E = (K + kRowThreads - 1) / kRowThreads;
+        const int lo = threadIdx.x * E;
+#pragma unroll
+        for (int u = 0; u < kPlanMaxPer; ++u) {
+            const int blk = pf->sb[u];
+            if (u < E && lo + u < K && blk >= 0 && blk < width)
+                atomicOr(&bits[blk >> 5], 1u << (blk & 31));
+        }
+    }
+};
+
+// The plan of a row whose selection is a threshold: the blocks taken are
+// exactly the valid ones with key >= T (K of them), every key in this
+// thread's registers (kr[u] = key of block u * kRowThreads + tid, n < nb), the
+// resident blocks marked in res_bits (ResidentMarks).  The selection is never
+// compacted on its own: one exchange of counts places the selected blocks
+// (written to sel_out, when given), the misses (selected, not resident: block
+// order), the eviction candidates (resident, not selected: slot order) and
+// the free slots, and a slot's block is a hit when its key is at or above T.
+// The rest is row_plan's: ranks, the first cap misses fetched into the free
+// slots and then the least recently used candidates, the table rewritten.
+// The same result as row_select followed by row_plan.  `pl` is 8 * Kp ints.
+__device__ __forceinline__ void row_threshold_plan(
+        const uint32_t (&kr)[kKeyRegs], int nb, uint32_t T, const uint32_t *keys,
+        const uint32_t *res_bits, int K, int cap, int step, const PlanPrefetch &pf,
+        int32_t *sel_out, int32_t *slot_block, int32_t *last_use, int32_t *fetch_block,
+        int32_t *fetch_slot, int32_t *fetch_count, int *pl, RowShared &sh) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int Kp = plan_pad(K);
+    const int E = (K + kRowThreads - 1) / kRowThreads;
+    const int lo = tid * E;
+    float *m_score = reinterpret_cast<float *>(pl);   // misses, compacted
+    int *m_block = pl + Kp;
+    int *m_rank = pl + 2 * Kp;
+    int *c_lu = pl + 3 * Kp;                          // eviction candidates, compacted
+    int *c_block = pl + 4 * Kp;
+    int *c_rank = pl + 5 * Kp;
+    int *dest = pl + 6 * Kp;                          // destination slot of the p-th fetched block
+    int *fill = pl + 7 * Kp;                          // per slot: block fetched into it, -1
+    for (int i = tid; i < Kp; i += kRowThreads) {
+        m_rank[i] = 0;
+        c_rank[i] = 0;
+        dest[i] = -1;
+        fill[i] = -1;
+    }
+    // blocks: selected, and selected but not resident, one ballot each per
+    // register; counts per (register, wave) slot
+    constexpr int NS = kKeyRegs * kRowWaves;
+    static_assert(NS <= 2 * kWave && kRowWaves % 2 == 0, "two (register, wave) slots per lane");
+    uint64_t bt[kKeyRegs], bm[kKeyRegs];
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < kKeyRegs; ++u) {
+        const int n = u * kRowThreads + tid;
+        const bool in = n < nb;
+        const uint32_t word = res_bits[in ? n >> 5 : 0];
+        const bool taken = in & (kr[u] >= T);
+        bt[u] = __ballot(taken);
+        bm[u] = __ballot(taken & !((word >> (n & 31)) & 1u));
+        const int packed = __popcll(bt[u]) | (__popcll(bm[u]) << 16);
+        mine = lane == u ? packed : mine;
+    }
+    if (lane < kKeyRegs) sh.reg_cnt[lane * kRowWaves + wave] = mine;
+    // slots (this thread's contiguous chunk): hits, eviction candidates, free
+    bool hit[kPlanMaxPer], cand[kPlanMaxPer], empty[kPlanMaxPer];
+    int my_ce = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        const int blk = pf.sb[u];
+        const bool ok = u < E && lo + u < K;
+        hit[u] = ok && blk >= 0 && blk < nb && keys[blk] >= T;
+        cand[u] = ok && blk >= 0 && !hit[u];
+        empty[u] = ok && blk < 0;
+        my_ce += (int)cand[u] | ((int)empty[u] << 16);
+    }
+    const int ce_incl = wave_inclusive_scan(my_ce);
+    if (lane == kWave - 1) sh.wave_sums[wave] = ce_incl;
+    __syncthreads();
+    // block slots scanned by every wave, lane l holding slots 2l and 2l + 1;
+    // slot u * kRowWaves + wave has this wave's parity (kRowWaves is even)
+    const int c0 = 2 * lane < NS ? sh.reg_cnt[2 * lane] : 0;
+    const int c1 = 2 * lane + 1 < NS ? sh.reg_cnt[2 * lane + 1] : 0;
+    const int incl = wave_inclusive_scan(c0 + c1);
+    const int tm_total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    const int n_taken = tm_total & 0xffff;
+    const int M = tm_total >> 16;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int ex = (wv & 1) ? incl - c1 : incl - c0 - c1;
+    int off = 0, ce_total = 0;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+        const int ws = sh.wave_sums[w];
+        off += (w < wv) ? ws : 0;
+        ce_total += ws;
+    }
+    const int C = ce_total & 0xffff;
+    const int nfree = ce_total >> 16;
+    const int nF = M < cap ? M : cap;                      // the first min(M, cap) misses are fetched
+    const int n_victims = nF > nfree ? nF - nfree : 0;     // (C >= n_victims always)
+    int mp[kKeyRegs];
+#pragma unroll
+    for (int u = 0; u < kKeyRegs; ++u) {
+        const int before = __builtin_amdgcn_readlane(ex, (u * kRowWaves + wv) >> 1);
+        const int n = u * kRowThreads + tid;
+        mp[u] = -1;
+        if ((bt[u] >> lane) & 1) {
+            if (sel_out) sel_out[(before & 0xffff) + lanes_below(bt[u])] = n;
+            if ((bm[u] >> lane) & 1) {
+                const int q = (before >> 16) + lanes_below(bm[u]);
+                m_score[q] = key_to_score(kr[u]);
+                m_block[q] = n;
+                mp[u] = q;
+            }
+        }
+    }
+    if (sel_out)
+        for (int i = n_taken + tid; i < K; i += kRowThreads) sel_out[i] = -1;
+    const int ce_before = ce_incl - my_ce + off;
+    int cpos = ce_before & 0xffff, epos = ce_before >> 16;
+    int cp[kPlanMaxPer];
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        cp[u] = -1;
+        if (empty[u]) {
+            if (epos < nF) dest[epos] = lo + u;
+            ++epos;
+        }
+        if (cand[u] && n_victims > 0) {
+            cp[u] = cpos;
+            c_lu[cpos] = pf.lu[u];
+            c_block[cpos] = pf.sb[u];
+            ++cpos;
+        }
+    }
+    __syncthreads();
+    plan_ranks(m_score, m_block, m_rank, M, cap, c_lu, c_block, c_rank, C, n_victims);
+    __syncthreads();
+    bool fetched[kKeyRegs];
+#pragma unroll
+    for (int u = 0; u < kKeyRegs; ++u) fetched[u] = mp[u] >= 0 && (M <= cap || m_rank[mp[u]] < cap);
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        if (cp[u] >= 0) {
+            const int rank = c_rank[cp[u]];
+            if (rank < n_victims) dest[nfree + rank] = lo + u;
+        }
+    }
+    __syncthreads();
+    // the p-th fetched block (ascending) goes to dest[p]
+#pragma unroll
+    for (int u = 0; u < kKeyRegs; ++u) {
+        if (fetched[u]) {
+            const int fpos = M > cap ? fetched_before(m_rank, mp[u], cap) : mp[u];
+            if (fpos >= nF) continue;   // (cannot happen: the ranks of distinct blocks are distinct)
+            const int blk = u * kRowThreads + tid;
+            const int d = dest[fpos];
+            fetch_block[fpos] = blk;
+            fetch_slot[fpos] = d;
+            if (d >= 0) fill[d] = blk;
+        }
+    }
+    for (int p = nF + tid; p < cap; p += kRowThreads) {
+        fetch_block[p] = -1;
+        fetch_slot[p] = -1;
+    }
+    if (tid == 0) *fetch_count = nF;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPlanMaxPer; ++u) {
+        const int j = lo + u;
+        if (u < E && j < K) {
+            const int f = fill[j];
+            slot_block[j] = f >= 0 ? f : (pf.sb[u] < 0 ? -1 : pf.sb[u]);
+            last_use[j] = (f >= 0 || hit[u]) ? step : pf.lu[u];
         }
     }
 }

@@ -17,10 +17,6 @@ namespace wide {
 #endif
 
 
-__device__ __forceinline__ float key_to_score(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
-}
-
 // MODE 1 = select, 2 = plan (selection read from a.sel), 3 = select then plan.
 template <int MODE>
 __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlanArgs a) {
@@ -38,14 +34,30 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
 
     PlanPrefetch pf;
     if (MODE & 2) plan_prefetch(a.slot_block_in + rk, a.last_use_in + rk, K, pf);   // in flight during the select
+    const int step = (MODE & 2) ? a.step + (a.step_dev ? *a.step_dev : 0) : 0;
+    int32_t *fb = a.fetch_block + (size_t)row * a.cap;
+    int32_t *fs = a.fetch_slot + (size_t)row * a.cap;
     if (MODE & 1) {
         uint32_t kr[kKeyRegs];
         const int nb = load_row_keys(srow, a.width, a.ctx_len + row / a.hkv, keys, kr);
         __syncthreads();
-        if (nb <= kKeyRegs * kRowThreads)
+        if (MODE == 3 && nb > K && nb <= kKeyRegs * kRowThreads) {
+            // the resident marks follow the keys
+            uint32_t *res_bits = keys + (a.width > 0 ? a.width : 1);
+            const RowCut cut = row_find_cut<true>(keys, nb, K, sh, kr,
+                                                  ResidentMarks{res_bits, a.width, K, &pf});
+            if (cut.all_ties) {
+                row_threshold_plan(kr, nb, cut.tau, keys, res_bits, K, a.cap, step, pf,
+                                   a.sel ? a.sel + rk : nullptr, a.slot_block + rk, a.last_use + rk,
+                                   fb, fs, a.fetch_count + row, pl, sh);
+                return;
+            }
+            row_compact<true>(keys, nb, sel, sh, kr, cut);
+        } else if (nb <= kKeyRegs * kRowThreads) {
             row_select<true>(keys, nb, K, sel, sh, kr);
-        else
+        } else {
             row_select(keys, nb, K, sel, sh);
+        }
         if (a.sel)
             for (int i = tid; i < K; i += kRowThreads) a.sel[rk + i] = sel[i];
     } else {
@@ -56,9 +68,6 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
         __syncthreads();
     }
     if (MODE & 2) {
-        const int step = a.step + (a.step_dev ? *a.step_dev : 0);
-        int32_t *fb = a.fetch_block + (size_t)row * a.cap;
-        int32_t *fs = a.fetch_slot + (size_t)row * a.cap;
         if (MODE & 1)
             row_plan(sel, [&](int s) { return key_to_score(keys[s]); }, K, a.cap, step, pf,
                      a.slot_block + rk, a.last_use + rk, fb, fs, a.fetch_count + row, pl, sh,
@@ -214,7 +223,7 @@ bool row_select_plan_fits(int width, int k, int mode) {
     // the fused launch's LDS: the selection, the plan's arrays and the keys,
     // beside the static row state, within 64 KiB
     return width <= kFusedMaxWidth && k <= kFusedMaxK &&
-           (size_t)(12 * plan_pad(k) + width) * 4 + sizeof(RowShared) <= 65536;
+           (size_t)(12 * plan_pad(k) + width + (width + 31) / 32) * 4 + sizeof(RowShared) <= 65536;
 }
 
 #ifndef OASIS_ROW_WIDE
@@ -268,7 +277,7 @@ hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t
     } else if (mode == 2) {
         launch_k(row_select_plan_kernel<2>, grid, block, (size_t)12 * Kp * 4, stream, stop, a);
     } else {
-        launch_k(row_select_plan_kernel<3>, grid, block, (12 * Kp + w) * 4, stream, stop, a);
+        launch_k(row_select_plan_kernel<3>, grid, block, (12 * Kp + w + (w + 31) / 32) * 4, stream, stop, a);
     }
     return hipGetLastError();
 }
