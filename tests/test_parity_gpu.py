@@ -277,6 +277,52 @@ def test_select_plan_fused_bit_exact_over_steps(case):
         np.testing.assert_array_equal(g_lu.cpu().numpy(), lu)
 
 
+@pytest.mark.parametrize("mode", ["normal", "ties"])
+def test_select_plan_with_stale_and_repeated_resident_blocks(mode):
+    """Working-set tables holding blocks past the row's context (a shrunk or
+    stale row), the same block in two slots, and free slots: the fused launch
+    (whose threshold path marks resident blocks in a bitmap and finds hits
+    from the keys) and the plan-only launch on the oracle's selection both
+    give the oracle's fetch list and table, bit for bit, over chained steps."""
+    B, Hkv, W, K, cap = 2, 2, 2048, 128, 4
+    rng = np.random.default_rng(11 if mode == "normal" else 12)
+    ctx_len = np.array([W * 16, 1000 * 16 - 7], np.int32)
+    sb = np.full((B, Hkv, K), -1, np.int32)
+    lu = np.full((B, Hkv, K), NEG, np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            slots = rng.choice(K, size=100, replace=False)
+            sb[b, g, slots] = rng.integers(0, W, size=100)          # any block of the table
+            sb[b, g, slots[1]] = sb[b, g, slots[0]]                 # one block in two slots
+            lu[b, g, slots] = rng.integers(0, 3, size=100)
+    shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
+    g_ctx = dev(torch.from_numpy(ctx_len))
+    tabs = {k: (dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))) for k in ("fused", "plan")}
+    sel = torch.empty((B, Hkv, K), dtype=torch.int32, device=DEV)
+    fb = torch.empty((B, Hkv, cap), dtype=torch.int32, device=DEV)
+    fs = torch.empty_like(fb)
+    fc = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    for step in range(3, 9):
+        s = _random_scores(rng, B, Hkv, W, mode)
+        osel = orc.select(s.astype(np.float64), ctx_len, 16, K)
+        ofb, ofs, ocnt, sb, lu = orc.plan(osel, s.astype(np.float64), sb, lu, cap, step)
+        for kind, (g_sb, g_lu) in tabs.items():
+            if kind == "fused":
+                ops.select_plan(shape, dev(torch.from_numpy(s)), g_ctx, K, cap, step, sel, g_sb,
+                                g_lu, fb, fs, fc)
+            else:
+                ops.plan_fetch(shape, dev(torch.from_numpy(osel)), dev(torch.from_numpy(s)), K,
+                               cap, step, g_sb, g_lu, fb, fs, fc)
+            torch.cuda.synchronize()
+            if kind == "fused":
+                np.testing.assert_array_equal(sel.cpu().numpy(), osel)
+            np.testing.assert_array_equal(fc.cpu().numpy(), ocnt, err_msg=kind)
+            np.testing.assert_array_equal(fb.cpu().numpy(), ofb, err_msg=kind)
+            np.testing.assert_array_equal(fs.cpu().numpy(), ofs, err_msg=kind)
+            np.testing.assert_array_equal(g_sb.cpu().numpy(), sb, err_msg=kind)
+            np.testing.assert_array_equal(g_lu.cpu().numpy(), lu, err_msg=kind)
+
+
 TWO_PASS_CASES = [
     # B, Hkv, W, K, cap, mode, contexts (blocks; None = every row full)
     (2, 2, 8193, 64, 3, "normal", None),               # one block above the one-pass width
