@@ -850,16 +850,17 @@ struct ResidentMarks {
 // thread's registers (kr[u] = key of block u * kRowThreads + tid, n < nb), the
 // resident blocks marked in res_bits (ResidentMarks).  The selection is never
 // compacted on its own: one exchange of counts places the selected blocks
-// (written to sel_out, when given), the misses (selected, not resident: block
-// order), the eviction candidates (resident, not selected: slot order) and
-// the free slots, and a slot's block is a hit when its key is at or above T.
+// (staged in `sel`, Kp ints of LDS, for sel_out when given), the misses
+// (selected, not resident: block order), the eviction candidates (resident,
+// not selected: slot order) and the free slots, and a slot's block is a hit
+// when its key is at or above T.
 // The rest is row_plan's: ranks, the first cap misses fetched into the free
 // slots and then the least recently used candidates, the table rewritten.
 // The same result as row_select followed by row_plan.  `pl` is 8 * Kp ints.
 __device__ __forceinline__ void row_threshold_plan(
         const uint32_t (&kr)[kKeyRegs], int nb, uint32_t T, const uint32_t *keys,
         const uint32_t *res_bits, int K, int cap, int step, const PlanPrefetch &pf,
-        int32_t *sel_out, int32_t *slot_block, int32_t *last_use, int32_t *fetch_block,
+        int32_t *sel_out, int *sel, int32_t *slot_block, int32_t *last_use, int32_t *fetch_block,
         int32_t *fetch_slot, int32_t *fetch_count, int *pl, RowShared &sh) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -942,7 +943,7 @@ __device__ __forceinline__ void row_threshold_plan(
         const int n = u * kRowThreads + tid;
         mp[u] = -1;
         if ((bt[u] >> lane) & 1) {
-            if (sel_out) sel_out[(before & 0xffff) + lanes_below(bt[u])] = n;
+            if (sel_out) sel[(before & 0xffff) + lanes_below(bt[u])] = n;
             if ((bm[u] >> lane) & 1) {
                 const int q = (before >> 16) + lanes_below(bm[u]);
                 m_score[q] = key_to_score(kr[u]);
@@ -951,8 +952,6 @@ __device__ __forceinline__ void row_threshold_plan(
             }
         }
     }
-    if (sel_out)
-        for (int i = n_taken + tid; i < K; i += kRowThreads) sel_out[i] = -1;
     const int ce_before = ce_incl - my_ce + off;
     int cpos = ce_before & 0xffff, epos = ce_before >> 16;
     int cp[kPlanMaxPer];
@@ -971,6 +970,10 @@ __device__ __forceinline__ void row_threshold_plan(
         }
     }
     __syncthreads();
+    // the selection leaves in one coalesced pass (scattered stores from the
+    // registers would issue a store per register and wave)
+    if (sel_out)
+        for (int i = tid; i < K; i += kRowThreads) sel_out[i] = i < n_taken ? sel[i] : -1;
     plan_ranks(m_score, m_block, m_rank, M, cap, c_lu, c_block, c_rank, C, n_victims);
     __syncthreads();
     bool fetched[kKeyRegs];

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kRowThreads) void row_select_plan_kernel(SelectPlan
                                                   ResidentMarks{res_bits, a.width, K, &pf});
             if (cut.all_ties) {
                 row_threshold_plan(kr, nb, cut.tau, keys, res_bits, K, a.cap, step, pf,
-                                   a.sel ? a.sel + rk : nullptr, a.slot_block + rk, a.last_use + rk,
+                                   a.sel ? a.sel + rk : nullptr, sel, a.slot_block + rk, a.last_use + rk,
                                    fb, fs, a.fetch_count + row, pl, sh);
                 return;
             }
