@@ -247,6 +247,9 @@ def test_plan_fetch_bit_exact_when_stored_last_use_is_later_than_the_step():
     (2, 4, 2048, 128, 6, "outliers"),
     (2, 2, 2048, 128, 2, "equal"),
     (2, 2, 1500, 64, 3, "narrow"),
+    (2, 2, 135, 128, 3, "normal"),              # one valid block more than K (the last row: fewer)
+    (2, 3, 500, 1, 1, "normal"),                # K = 1
+    (2, 2, 700, 64, 0, "normal"),               # cap 0: only the hits' last use moves
 ], ids=lambda c: f"nb{c[2]}K{c[3]}cap{c[4]}{c[5]}")
 def test_select_plan_fused_bit_exact_over_steps(case):
     B, Hkv, nb, K, cap, mode = case
