@@ -20,7 +20,10 @@
 // Plan: each thread owns contiguous chunks of the selection and of the slot
 // table, so positions are exclusive scans; hits are binary searches in the
 // ascending selection; only misses (among misses) and eviction candidates
-// (among candidates) are ranked by counting.  Exact and deterministic.
+// (among candidates) are ranked by counting.  When the selection is a
+// threshold (every key at or above the K-th is taken) the fused launch plans
+// straight from the keys instead, without compacting the selection first
+// (row_threshold_plan).  Exact and deterministic.
 #pragma once
 
 #include "oasis_device.h"
@@ -819,7 +822,6 @@ __device__ __forceinline__ void row_plan(int *sel, ScoreOf sel_score_of, int K, 
         }
     }
 }
-
 
 // Resident marks of the threshold plan: one bit per block of the row, cleared
 // while the selection starts and set from this thread's prefetched slots in
