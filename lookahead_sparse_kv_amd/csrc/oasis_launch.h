@@ -163,7 +163,9 @@ constexpr int kWideRowMinWidth = OASIS_WIDE_ROW_MIN_WIDTH;
 namespace wide {
 hipError_t launch_row_select_plan(const SelectPlanArgs &a, int mode, hipStream_t stream,
                                   LaunchStop *stop = nullptr);
+size_t row_shared_bytes();       // static LDS of the 1024-thread build's row state
 }
+size_t row_shared_bytes();       // the same for the 256-thread build
 // Two-pass selection (and plan) of rows wider than kTwoPassMinWidth blocks:
 // the chunk kernel, then one workgroup per row over the candidates.
 void two_pass_plan(int width, int k, int *chunk_w, int *chunks);

@@ -216,15 +216,21 @@ hipError_t launch_merge_select_plan(const SelectPlanArgs &a, int mode, const uin
     return hipGetLastError();
 }
 
+size_t row_shared_bytes() { return sizeof(RowShared); }
+
+#ifndef OASIS_ROW_WIDE
 bool row_select_plan_fits(int width, int k, int mode) {
     if (k > kMaxKBlocks) return false;
     if (mode == 1) return width <= kRowSelectMaxWidth;
     if (mode == 2) return true;
-    // the fused launch's LDS: the selection, the plan's arrays and the keys,
-    // beside the static row state, within 64 KiB
+    // the fused launch's LDS: the selection, the plan's arrays, the keys and
+    // their resident marks, beside the static row state of the build that
+    // takes the row, within 64 KiB
+    const size_t shared = width > kWideRowMinWidth ? wide::row_shared_bytes() : sizeof(RowShared);
     return width <= kFusedMaxWidth && k <= kFusedMaxK &&
-           (size_t)(12 * plan_pad(k) + width + (width + 31) / 32) * 4 + sizeof(RowShared) <= 65536;
+           (size_t)(12 * plan_pad(k) + width + (width + 31) / 32) * 4 + shared <= 65536;
 }
+#endif
 
 #ifndef OASIS_ROW_WIDE
 // Chunks of at least kMinChunkWidth blocks, few enough that their K
@@ -250,7 +256,8 @@ hipError_t launch_two_pass_select_plan(const SelectPlanArgs &a, int mode, uint32
                                          : launch_chunk_select(ca, stream);
     if (e != hipSuccess) return e;
     const int ncand = chunks * a.k;
-    const bool fused = mode == 3 && (size_t)(12 * plan_pad(a.k) + ncand) * 4 + sizeof(RowShared) <= 65536;
+    const size_t shared = ncand > kWideRowMinWidth ? wide::row_shared_bytes() : sizeof(RowShared);
+    const bool fused = mode == 3 && (size_t)(12 * plan_pad(a.k) + ncand) * 4 + shared <= 65536;
     const int m = fused ? 3 : 1;
     // the stop event goes with the last launch: the merge, or the plan after it
     LaunchStop *merge_stop = (mode == 1 || fused) ? stop : nullptr;

@@ -250,6 +250,8 @@ def test_plan_fetch_bit_exact_when_stored_last_use_is_later_than_the_step():
     (2, 2, 135, 128, 3, "normal"),              # one valid block more than K (the last row: fewer)
     (2, 3, 500, 1, 1, "normal"),                # K = 1
     (2, 2, 700, 64, 0, "normal"),               # cap 0: only the hits' last use moves
+    (1, 2, 7600, 512, 9, "normal"),             # the 1,024-thread build's LDS just fits: one launch
+    (1, 2, 7700, 512, 9, "normal"),             # just past it: select, then plan
 ], ids=lambda c: f"nb{c[2]}K{c[3]}cap{c[4]}{c[5]}")
 def test_select_plan_fused_bit_exact_over_steps(case):
     B, Hkv, nb, K, cap, mode = case
