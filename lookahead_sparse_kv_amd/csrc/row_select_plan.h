@@ -333,7 +333,6 @@ __device__ __forceinline__ RowCut row_find_cut(const uint32_t *keys, int nb, int
                 }
             }
             __syncthreads();
-            prefix = sh.tau - kmin;                // tau = kmin + prefix, exactly
             krem -= sh.gt_in_bin;                  // copies of tau still to take
             return RowCut{sh.tau, krem, false, sh.ge_in_bin - sh.gt_in_bin == krem};
         }
