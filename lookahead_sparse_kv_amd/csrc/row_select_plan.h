@@ -533,7 +533,10 @@ __device__ __forceinline__ void plan_prefetch(const int32_t *slot_block, const i
 // Ranks of the compacted misses by (score desc, block asc) when more than
 // cap of them, and of the compacted eviction candidates by (last use asc,
 // block asc) when any is evicted, into m_rank / c_rank (zeroed by the
-// caller).  Each rank is a tally of the entries ahead of it, the comparisons
+// caller).  Candidates with equal keys (one block resident in two slots: a
+// table no plan produces, but one a caller may pass) go by compacted
+// position, i.e. slot order, so that every victim rank is distinct; misses
+// are distinct blocks.  Each rank is a tally of the entries ahead of it, the comparisons
 // spread over the workgroup: wave w compares entry i (lane i, i + 64, ...)
 // with a slice of the others, four per 16-byte LDS read, and adds its count
 // to i's tally.  The caller's barrier follows.
@@ -572,9 +575,13 @@ __device__ __forceinline__ void plan_ranks(const float *m_score, const int *m_bl
                 const int4 b4 = ld_i4(c_block + q0);
                 const int ll[4] = {l4.x, l4.y, l4.z, l4.w};
                 const int bb[4] = {b4.x, b4.y, b4.z, b4.w};
+                // (block, position) below (b0, i): a block below b0, or b0
+                // itself at an earlier position (blocks are >= 0, so the
+                // subtraction cannot wrap)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    r += (q0 + c < q_hi) & ((ll[c] < l0) | ((ll[c] == l0) & (bb[c] < b0)));
+                    r += (q0 + c < q_hi) &
+                         ((ll[c] < l0) | ((ll[c] == l0) & (bb[c] - (int)(q0 + c < i) < b0)));
             }
             if (r) atomicAdd(&c_rank[i], r);
         }

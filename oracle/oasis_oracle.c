@@ -134,7 +134,8 @@ int oracle_select_row(int nb, int K, const double *scores, int *sel)
  *   - the fetched set F goes out in ascending block order;
  *   - destinations: empty slots in ascending order first; if F needs more,
  *     evict exactly that many resident blocks that are NOT selected, least
- *     recently used first (ties to the lower block index), in that order;
+ *     recently used first (ties to the lower block index, then to the lower
+ *     slot), in that order;
  *   - a selected block is never evicted.
  * Outputs fetch_block[i] = F[i], fetch_slot[i] = its slot, -1 padded to cap.
  * Returns |F| through *count.                                               */
@@ -144,7 +145,10 @@ static int cmp_lru(const void *a, const void *b)
 {
     const lru_cand *x = (const lru_cand *)a, *y = (const lru_cand *)b;
     if (x->key != y->key) return (x->key > y->key) - (x->key < y->key);
-    return (x->n > y->n) - (x->n < y->n);
+    if (x->n != y->n) return (x->n > y->n) - (x->n < y->n);
+    /* one block resident in two slots (a table no plan produces, but one a
+       caller may pass): the lower slot goes first */
+    return (x->slot > y->slot) - (x->slot < y->slot);
 }
 
 static int in_list(int v, const int *list, int len)

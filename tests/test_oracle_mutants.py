@@ -49,10 +49,11 @@ MUTANTS = [
      "if (x->key != y->key) return (x->key > y->key) - (x->key < y->key);",
      "if (x->key != y->key) return (x->key < y->key) - (x->key > y->key);"),
     ("plan: LRU ties to the higher block",
-     "    if (x->key != y->key) return (x->key > y->key) - (x->key < y->key);\n"
-     "    return (x->n > y->n) - (x->n < y->n);",
-     "    if (x->key != y->key) return (x->key > y->key) - (x->key < y->key);\n"
-     "    return (x->n < y->n) - (x->n > y->n);"),
+     "    if (x->n != y->n) return (x->n > y->n) - (x->n < y->n);",
+     "    if (x->n != y->n) return (x->n < y->n) - (x->n > y->n);"),
+    ("plan: a block resident in two slots leaves the higher slot first",
+     "return (x->slot > y->slot) - (x->slot < y->slot);",
+     "return (x->slot < y->slot) - (x->slot > y->slot);"),
     ("plan: free slots taken from the top",
      "for (int j = 0; j < K && nd < nF; ++j) if (slot_block[j] < 0) dest[nd++] = j;",
      "for (int j = K - 1; j >= 0 && nd < nF; --j) if (slot_block[j] < 0) dest[nd++] = j;"),
@@ -115,4 +116,4 @@ def test_every_planted_mistake_fails_a_pin(tmp_path):
         results = list(ex.map(lambda j: (j[2], _build_and_run(tmp_path, j[0], j[1])), jobs))
     survived = [name for name, (rc, _) in results if rc == 0]
     assert not survived, f"mistakes no pin catches: {survived}"
-    assert len(results) == len(MUTANTS) == 30
+    assert len(results) == len(MUTANTS) == 31

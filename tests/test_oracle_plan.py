@@ -41,6 +41,21 @@ def test_plan_hand_worked_lru_tie_and_score_tie(orc):
     assert sb.tolist() == [6, 3, 11] and lu.tolist() == [4, 6, 6]
 
 
+def test_plan_block_resident_in_two_slots_leaves_lower_slot_first(orc):
+    # A table no plan produces, but one a caller may pass: block 5 sits in
+    # slots 0 and 1 with the same last use.  Three misses, one free slot
+    # (3), two victims: block 7 (last use 0) first, then the copy of 5 in
+    # the lower slot (0); the copy in slot 1 stays.
+    slot_block = [5, 5, 7, -1]
+    last_use = [1, 1, 0, NEG]
+    sel = [10, 11, 12, -1]
+    scores = np.zeros(16)
+    scores[[10, 11, 12]] = [0.3, 0.2, 0.1]
+    fb, fs, cnt, sb, lu = orc.plan_row(sel, scores, slot_block, last_use, cap=3, step=4)
+    assert cnt == 3 and fb.tolist() == [10, 11, 12] and fs.tolist() == [3, 2, 0]
+    assert sb.tolist() == [12, 5, 11, 10] and lu.tolist() == [4, 1, 4, 4]
+
+
 def test_plan_empty_start_full_cap_fills_slots_ascending(orc):
     sel = [1, 4, 9, 30, -1]
     scores = np.linspace(0, 1, 40)

@@ -282,24 +282,27 @@ def test_select_plan_fused_bit_exact_over_steps(case):
         np.testing.assert_array_equal(g_lu.cpu().numpy(), lu)
 
 
-@pytest.mark.parametrize("mode", ["normal", "ties"])
-def test_select_plan_with_stale_and_repeated_resident_blocks(mode):
+@pytest.mark.parametrize("mode,filled", [("normal", 100), ("ties", 100), ("normal", 128)])
+def test_select_plan_with_stale_and_repeated_resident_blocks(mode, filled):
     """Working-set tables holding blocks past the row's context (a shrunk or
-    stale row), the same block in two slots, and free slots: the fused launch
-    (whose threshold path marks resident blocks in a bitmap and finds hits
-    from the keys) and the plan-only launch on the oracle's selection both
-    give the oracle's fetch list and table, bit for bit, over chained steps."""
+    stale row), the same block in two slots with the same last use, and free
+    slots or none (then every fetch evicts, the repeated block first while it
+    is not selected): the fused launch (whose threshold path marks resident
+    blocks in a bitmap and finds hits from the keys) and the plan-only launch
+    on the oracle's selection both give the oracle's fetch list and table, bit
+    for bit, over chained steps."""
     B, Hkv, W, K, cap = 2, 2, 2048, 128, 4
-    rng = np.random.default_rng(11 if mode == "normal" else 12)
+    rng = np.random.default_rng({("normal", 100): 11, ("ties", 100): 12}.get((mode, filled), 13))
     ctx_len = np.array([W * 16, 1000 * 16 - 7], np.int32)
     sb = np.full((B, Hkv, K), -1, np.int32)
     lu = np.full((B, Hkv, K), NEG, np.int32)
     for b in range(B):
         for g in range(Hkv):
-            slots = rng.choice(K, size=100, replace=False)
-            sb[b, g, slots] = rng.integers(0, W, size=100)          # any block of the table
-            sb[b, g, slots[1]] = sb[b, g, slots[0]]                 # one block in two slots
-            lu[b, g, slots] = rng.integers(0, 3, size=100)
+            slots = rng.choice(K, size=filled, replace=False)
+            sb[b, g, slots] = rng.integers(0, W, size=filled)       # any block of the table
+            lu[b, g, slots] = rng.integers(0, 3, size=filled)
+            sb[b, g, slots[1]] = sb[b, g, slots[0]]                 # one block in two slots,
+            lu[b, g, slots[:2]] = -1                                # the least recently used
     shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
     g_ctx = dev(torch.from_numpy(ctx_len))
     tabs = {k: (dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))) for k in ("fused", "plan")}
