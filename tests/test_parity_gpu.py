@@ -331,6 +331,72 @@ def test_select_plan_with_stale_and_repeated_resident_blocks(mode, filled):
             np.testing.assert_array_equal(g_lu.cpu().numpy(), lu, err_msg=kind)
 
 
+def test_select_plan_random_configurations_against_the_oracle():
+    """Seeded random shapes (widths across the one-pass builds and the two
+    passes, K, cap, score distributions with ties, -inf and narrow ranges,
+    ragged and empty contexts) and working-set tables (free slots, stale
+    blocks, a block in two slots): the fused launch and the plan-only launch
+    on the oracle's selection give the oracle's selection, fetch list and
+    table, bit for bit, over chained steps.  A table the oracle refuses (too
+    few blocks to evict, which only a repeated block can cause) is skipped."""
+    rng = np.random.default_rng(2024)
+    checked = 0
+    for _ in range(40):
+        B, Hkv = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        W = int(rng.choice([64, 300, 1000, 2048, 2049, 3000, 5000, 8192, 9000, 12000]))
+        K = int(rng.choice([1, 8, 64, 128, 200, 512, 1000]))
+        cap = min(K, int(rng.choice([0, 1, 2, 5, 25, K])))
+        mode = str(rng.choice(["normal", "ties", "zeros", "inf", "narrow"]))
+        ctx = rng.integers(0, W * 16 + 1, size=B).astype(np.int32)
+        ctx[0] = W * 16 if rng.random() < 0.5 else ctx[0]
+        sb = np.full((B, Hkv, K), -1, np.int32)
+        lu = np.full((B, Hkv, K), NEG, np.int32)
+        for b in range(B):
+            for g in range(Hkv):
+                n = int(rng.integers(0, K + 1))
+                sl = rng.choice(K, size=n, replace=False)
+                sb[b, g, sl] = rng.integers(0, W, size=n)
+                lu[b, g, sl] = rng.integers(0, 5, size=n)
+                if n >= 2 and rng.random() < 0.3:
+                    sb[b, g, sl[1]] = sb[b, g, sl[0]]
+        shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
+        nws = ops.select_workspace_bytes(shape, K)
+        ws = torch.empty((nws // 8 + 1,), dtype=torch.int64, device=DEV) if nws else None
+        tabs = {k: (dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))) for k in ("fused", "plan")}
+        sel = torch.empty((B, Hkv, K), dtype=torch.int32, device=DEV)
+        fb = torch.empty((B, Hkv, cap), dtype=torch.int32, device=DEV)
+        fs = torch.empty_like(fb)
+        fc = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+        g_ctx = dev(torch.from_numpy(ctx))
+        o_sb, o_lu = sb.copy(), lu.copy()
+        for step in range(2, 4):
+            s = _random_scores(rng, B, Hkv, W, mode)
+            osel = orc.select(s.astype(np.float64), ctx, 16, K)
+            try:
+                ofb, ofs, ocnt, o_sb, o_lu = orc.plan(osel, s.astype(np.float64), o_sb, o_lu, cap, step)
+            except RuntimeError:
+                break
+            g_s = dev(torch.from_numpy(s))
+            for kind, (g_sb, g_lu) in tabs.items():
+                if kind == "fused":
+                    ops.select_plan(shape, g_s, g_ctx, K, cap, step, sel, g_sb, g_lu, fb, fs, fc,
+                                    workspace=ws)
+                else:
+                    ops.plan_fetch(shape, dev(torch.from_numpy(osel)), g_s, K, cap, step, g_sb,
+                                   g_lu, fb, fs, fc)
+                torch.cuda.synchronize()
+                what = f"{kind} B{B} H{Hkv} W{W} K{K} cap{cap} {mode} step {step}"
+                if kind == "fused":
+                    np.testing.assert_array_equal(sel.cpu().numpy(), osel, err_msg=what)
+                np.testing.assert_array_equal(fc.cpu().numpy(), ocnt, err_msg=what)
+                np.testing.assert_array_equal(fb.cpu().numpy(), ofb, err_msg=what)
+                np.testing.assert_array_equal(fs.cpu().numpy(), ofs, err_msg=what)
+                np.testing.assert_array_equal(g_sb.cpu().numpy(), o_sb, err_msg=what)
+                np.testing.assert_array_equal(g_lu.cpu().numpy(), o_lu, err_msg=what)
+            checked += 1
+    assert checked >= 60
+
+
 TWO_PASS_CASES = [
     # B, Hkv, W, K, cap, mode, contexts (blocks; None = every row full)
     (2, 2, 8193, 64, 3, "normal", None),               # one block above the one-pass width
