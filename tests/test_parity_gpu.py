@@ -335,9 +335,10 @@ def test_select_plan_random_configurations_against_the_oracle():
     """Seeded random shapes (widths across the one-pass builds and the two
     passes, K, cap, score distributions with ties, -inf and narrow ranges,
     ragged and empty contexts) and working-set tables (free slots, stale
-    blocks, a block in two slots): the fused launch and the plan-only launch
-    on the oracle's selection give the oracle's selection, fetch list and
-    table, bit for bit, over chained steps.  A table the oracle refuses (too
+    blocks, a block in two slots): the fused launch, the same launch planning
+    from one table copy into another, and the plan-only launch on the
+    oracle's selection give the oracle's selection, fetch list and table, bit
+    for bit, over chained steps.  A table the oracle refuses (too
     few blocks to evict, which only a repeated block can cause) is skipped."""
     rng = np.random.default_rng(2024)
     checked = 0
@@ -362,7 +363,10 @@ def test_select_plan_random_configurations_against_the_oracle():
         shape = ops.make_shape(B, Hkv, Hkv, 128, W, 1)
         nws = ops.select_workspace_bytes(shape, K)
         ws = torch.empty((nws // 8 + 1,), dtype=torch.int64, device=DEV) if nws else None
-        tabs = {k: (dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu))) for k in ("fused", "plan")}
+        tabs = {k: (dev(torch.from_numpy(sb)), dev(torch.from_numpy(lu)))
+                for k in ("fused", "plan", "next")}
+        spare = (torch.full((B, Hkv, K), -9, dtype=torch.int32, device=DEV),
+                 torch.full((B, Hkv, K), -9, dtype=torch.int32, device=DEV))
         sel = torch.empty((B, Hkv, K), dtype=torch.int32, device=DEV)
         fb = torch.empty((B, Hkv, cap), dtype=torch.int32, device=DEV)
         fs = torch.empty_like(fb)
@@ -377,8 +381,17 @@ def test_select_plan_random_configurations_against_the_oracle():
             except RuntimeError:
                 break
             g_s = dev(torch.from_numpy(s))
-            for kind, (g_sb, g_lu) in tabs.items():
-                if kind == "fused":
+            for kind in ("fused", "plan", "next"):
+                g_sb, g_lu = tabs[kind]
+                if kind == "next":                   # planned from one copy into the other
+                    src, before = (g_sb, g_lu), (g_sb.clone(), g_lu.clone())
+                    ops.select_plan(shape, g_s, g_ctx, K, cap, step, sel, spare[0], spare[1], fb,
+                                    fs, fc, workspace=ws, table_in=src)
+                    torch.cuda.synchronize()
+                    assert torch.equal(src[0], before[0]) and torch.equal(src[1], before[1])
+                    tabs[kind], spare = spare, src
+                    g_sb, g_lu = tabs[kind]
+                elif kind == "fused":
                     ops.select_plan(shape, g_s, g_ctx, K, cap, step, sel, g_sb, g_lu, fb, fs, fc,
                                     workspace=ws)
                 else:
@@ -386,7 +399,7 @@ def test_select_plan_random_configurations_against_the_oracle():
                                    g_lu, fb, fs, fc)
                 torch.cuda.synchronize()
                 what = f"{kind} B{B} H{Hkv} W{W} K{K} cap{cap} {mode} step {step}"
-                if kind == "fused":
+                if kind != "plan":
                     np.testing.assert_array_equal(sel.cpu().numpy(), osel, err_msg=what)
                 np.testing.assert_array_equal(fc.cpu().numpy(), ocnt, err_msg=what)
                 np.testing.assert_array_equal(fb.cpu().numpy(), ofb, err_msg=what)
