@@ -661,6 +661,28 @@ def test_sparse_attention_matches_oracle(name):
     assert np.all(np.isfinite(got))
 
 
+def test_sparse_attention_longest_list():
+    """The longest list the ABI takes (65,536 entries, a 1M-token context,
+    10% of the entries empty, in random order) against the oracle."""
+    n_blk = 65536
+    wl = wlm.small_workload(batch=1, q_heads=4, kv_heads=1, head_dim=64, ctx=(n_blk * 16 - 5,),
+                            budget=n_blk * 16, n_hot=0, seed=77)
+    d = wlm.make_layer(wl)
+    rng = np.random.default_rng(78)
+    lists = rng.permutation(n_blk).astype(np.int32).reshape(1, 1, n_blk)
+    lists[0, 0, rng.random(n_blk) < 0.1] = -1
+    q = (torch.randn((1, 1, 4, 64), generator=torch.Generator().manual_seed(79)) * 2).to(torch.bfloat16)
+    shape = ops.make_shape(1, 4, 1, 64, wl.table_width, wl.num_pages)
+    ws = torch.empty(ops.attn_workspace_bytes(shape, 1, n_blk) // 4 + 4, device=DEV)
+    out = torch.empty((1, 1, 4, 64), dtype=torch.bfloat16, device=DEV)
+    g = dev(torch.from_numpy(lists))
+    ops.sparse_decode_attn(shape, dev(q), dev(d["k_pool"]), dev(d["v_pool"]), dev(d["block_table"]),
+                           g, g, dev(d["ctx_len"]), out, ws)
+    got = out.float().cpu().numpy()[:, 0]
+    want = orc.attn(q[:, 0], d["K"], d["V"], d["ctx_len"], 16, lists)
+    check_attention_batch(got, want, q[:, 0], d["K"], d["V"], d["ctx_len"], lists, "65,536 entries")
+
+
 # split-K (2 and 128 rows, short lists); two workgroups per row (128 rows);
 # one workgroup per row (256 rows)
 @pytest.mark.parametrize("batch,kv_heads,K", [(2, 2, 24), (32, 4, 24), (32, 4, 128), (64, 4, 24)])
