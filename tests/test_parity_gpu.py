@@ -421,6 +421,7 @@ TWO_PASS_CASES = [
     (2, 2, 16384, 1024, 9, "outliers", None),
     (2, 2, 12000, 64, 3, "equal", (12000, 3000)),      # every key equal: lowest indices win
     (2, 2, 9000, 128, 2, "zeros", (9000, 100)),        # a row with fewer blocks than K
+    (1, 2, 524288, 128, 2, "normal", None),            # the widest row at K = 128 (64 chunks)
 ]
 
 
