@@ -1467,16 +1467,21 @@ def test_fetch_blocks_copies_listed_tiles_and_skips_bad_entries():
     del pool
 
 
-@pytest.mark.parametrize("scorer", ["exact", "minmax"])
-def test_host_tier_matches_full_pool_over_layers_and_steps(scorer):
+@pytest.mark.parametrize("scorer,shape", [("exact", "d128"), ("minmax", "d128"), ("exact", "d64"),
+                                          ("minmax", "d64")])
+def test_host_tier_matches_full_pool_over_layers_and_steps(scorer, shape):
     """Four steps of two layers with the full KV in pinned host pools, the
     capped fetch on a side stream overlapped with the next layer: outputs and
     plans are bit-identical to the full-pool path, and every resident slot
     holds its block's K and V.  With the compressed scorer the host-tier
     layers hold no device copy of the keys, only the pooled ones."""
     from lookahead_sparse_kv_amd.pipeline import HostTierDecode, HostTierLayer
-    wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 3000),
-                            budget=512, n_hot=10, ratio=0.125, seed=51)
+    if shape == "d128":
+        wl = wlm.small_workload(batch=2, q_heads=8, kv_heads=2, head_dim=128, ctx=(4096, 3000),
+                                budget=512, n_hot=10, ratio=0.125, seed=51)
+    else:       # D 64, four KV heads, a ragged third sequence, a looser cap
+        wl = wlm.small_workload(batch=3, q_heads=16, kv_heads=4, head_dim=64,
+                                ctx=(4096, 2500, 1001), budget=256, n_hot=6, ratio=0.25, seed=52)
     K, cap, W, B, Hkv = wl.k_blocks, wl.cap(), wl.table_width, wl.batch, wl.num_kv_heads
     n_layers, T = 2, 4
     datas = [wlm.make_layer(wl, seed=51 + 7 * l) for l in range(n_layers)]
