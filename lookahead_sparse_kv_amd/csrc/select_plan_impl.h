@@ -4,10 +4,12 @@
 // by select_plan_wide.hip (OASIS_ROW_WIDE: 1024 threads per row, namespace
 // oasis::wide, for rows of more than kWideRowMinWidth blocks).
 //
-// The fused kernel keeps the row's keys, its selection and its slot table in
-// LDS from start to end: the selection never goes back to HBM before it is
-// planned, the slot table is read while the selection runs, and the launch
-// between the two steps disappears.
+// The fused kernel keeps the row's keys, its selection and its slot table on
+// chip (LDS and registers) from start to end: the selection never goes back
+// to HBM before it is planned, the slot table is read while the selection
+// runs, and the launch between the two steps disappears.  When the selection
+// is a threshold (no tie to split) it is planned without being compacted
+// first (row_threshold_plan).
 #pragma once
 #include "row_select_plan.h"
 
