@@ -197,7 +197,9 @@ int oasis_select_topk(const oasis_shape *s, const float *scores, const int32_t *
  * their slots, -1 padded up to cap.  `scores` is the scoring output [B][Hkv][W].
  * Requires 1 <= k_blocks <= 1024, 0 <= cap <= k_blocks; when cap == 0 the
  * fetch_block / fetch_slot pointers may be NULL.  Precondition: no row of
- * slot_block holds a block twice.
+ * slot_block holds a block twice (no plan produces such a row).  Where one
+ * does and enough blocks can still be evicted, the plan is still the one
+ * above, the copies of a block ranked for eviction by slot (lower first).
  */
 int oasis_plan_fetch(const oasis_shape *s, const int32_t *sel, const float *scores,
                      int32_t k_blocks, int32_t cap, int32_t step, int32_t *slot_block,
